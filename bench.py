@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""CSA2 decode benchmark on one MI355X.
+
+Workload (the 128K decode configuration): a Full -> Reindex -> Reuse layer group over one
+shared cache, 16 sequences x 131072 cached entries.  Indexer: 32 heads x 64 dims, E4M3
+keys with a per-token fp32 scale, bf16 queries, head weights U(0,1); Top-512; main KV
+512-dim FP4 E2M1 with per-channel fp32 scales (values N(0,1) plus 1 % of channels x 8);
+64 attention heads, bf16 query and output.  Every layer draws its own queries/weights.
+
+A step is one pass of the whole decode path of the group (indexer scores, Top-K, gather +
+FP4 dequant + attention, for all three layers) through `csa2_layer_group`.  The cache is
+built once (FP4 / E4M3 quantisation on the GPU) and several copies are rotated between
+steps so that every step starts with its cache in HBM rather than in the 256 MB
+Infinity Cache.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import compressed_sparse_attention_csa2_amd as csa2  # noqa: E402
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "CSA2 decode queries/s + achieved HBM GB/s (% of peak) at 128K context"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_device_cache(wl, copies):
+    """Quantise the workload's cache on the GPU (one sequence at a time) and clone it."""
+    B, N, D, dk = wl.B, wl.N, wl.D, wl.dk
+    codes = torch.empty((B, N, D // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    k8 = torch.empty((B, N, dk), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    for b in range(B):
+        x = torch.from_numpy(wl.main_kv(b)).to("cuda")
+        csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, x[None], codes[b:b + 1], scales[b:b + 1])
+        kf = torch.from_numpy(wl.index_keys(b)).to("cuda")
+        csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, kf[None], k8[b:b + 1], ks[b:b + 1])
+        torch.cuda.synchronize()
+        del x, kf
+    n_keys = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    caches = [dict(codes=codes, scales=scales, k8=k8, ks=ks, n_keys=n_keys)]
+    for _ in range(copies - 1):
+        caches.append({k: v.clone() for k, v in caches[0].items()})
+    return caches
+
+
+def layer_inputs(wl):
+    layers = []
+    for i, m in enumerate(wl.modes):
+        layers.append(dict(mode=m,
+                           q_idx=torch.from_numpy(wl.index_query(i)).to(torch.bfloat16).cuda(),
+                           w=torch.from_numpy(wl.head_weights(i)).cuda(),
+                           q_attn=torch.from_numpy(wl.attn_query(i)).to(torch.bfloat16).cuda()))
+    return layers
+
+
+def algorithmic_bytes(wl):
+    """Bytes the group must move at least once: per indexing layer the key
+    scan (64 B key + 4 B scale per entry) and per layer the gathered FP4 rows, their
+    scales, the query, the output and the indices."""
+    B, N, K, D, Hq = wl.B, wl.N, wl.K, wl.D, wl.Hq
+    n_index = sum(1 for m in wl.modes if m != "reuse")
+    scan = B * N * (wl.dk + 4)
+    q_idx = B * wl.H * wl.dk * 2 + B * wl.H * 4
+    per_layer_attend = B * K * (D // 2) + B * D * 4 + B * Hq * D * 2 * 2 + B * K * 4 + B * Hq * 4
+    return n_index * (scan + q_idx + B * K * 4) + len(wl.modes) * per_layer_attend
+
+
+def time_score_kernel(wl, caches, layers, reps):
+    """Average duration of the indexer-score kernel (one launch per csa2_index_score call),
+    with HIP events on the launching stream; launches alternate over the rotated caches
+    and the indexing layers' queries exactly as the timed steps do."""
+    idx_layers = [L for L in layers if L["mode"] != "reuse"]
+    out = torch.empty((wl.B, 1, wl.N), dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    seq = []
+    for r in range(reps):
+        c = caches[(r // len(idx_layers)) % len(caches)]
+        L = idx_layers[r % len(idx_layers)]
+        seq.append((c, L))
+    for c, L in seq[: min(4, reps)]:  # warm-up
+        csa2.index_score(csa2.PREC_FP8, L["q_idx"], L["w"], c["k8"], c["ks"], c["n_keys"], scores=out)
+    torch.cuda.synchronize()
+    for (c, L), (e0, e1) in zip(seq, evs):
+        e0.record()
+        csa2.index_score(csa2.PREC_FP8, L["q_idx"], L["w"], c["k8"], c["ks"], c["n_keys"], scores=out)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    return float(np.mean(ms)), float(np.median(ms))
+
+
+def cpu_baseline(wl, seqs):
+    """The CPU oracle, as it stands, on the same workload restricted to `seqs` sequences
+    (the cache build is setup; the timed part is the group's decode path)."""
+    import oracle
+    sub = workloads.workload(wl.name, B=seqs)
+    ks, k8s, codes, scales = [], [], [], []
+    for b in range(seqs):
+        c, s = oracle.quantize_fp4(sub.main_kv(b)[None])
+        codes.append(c[0]); scales.append(s[0])
+        k8, kss = oracle.quantize_fp8(sub.index_keys(b)[None])
+        k8s.append(k8[0]); ks.append(kss[0])
+    cache = dict(k=np.stack(k8s), k_scale=np.stack(ks), n_keys=np.full(seqs, sub.N, np.int32),
+                 codes=np.stack(codes), scales=np.stack(scales))
+    layers = [dict(mode=m, q_idx=sub.index_query(i), w=sub.head_weights(i), q_attn=sub.attn_query(i))
+              for i, m in enumerate(sub.modes)]
+    t0 = time.perf_counter()
+    oracle.layer_group(layers, cache, oracle.PREC_FP8, sub.K, sub.softmax_scale)
+    dt = time.perf_counter() - t0
+    return dict(value=seqs / dt, unit="queries/s", cores=oracle.num_threads(), kind="oracle",
+                sample="%d of %d sequences of the same workload (N=%d, all %d layers); %.2f s" %
+                       (seqs, wl.B, wl.N, len(wl.modes), dt))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=3, help="cache copies rotated between steps")
+    ap.add_argument("--score-reps", type=int, default=60)
+    ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the CSA2 decode path runs per sequence with no exchange between GPUs, "
+              "and this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if csa2.device_check() != 0:
+        print("not a gfx950 device", file=sys.stderr)
+        sys.exit(1)
+    wl = workloads.WORKLOADS["group128k"]
+    log("building cache (%d copies) ..." % args.copies)
+    caches = build_device_cache(wl, args.copies)
+    layers = layer_inputs(wl)
+    plans = []
+    for c in caches:
+        cache = csa2.GroupCache(c["n_keys"], c["codes"], c["scales"], c["k8"], c["ks"], wl.K, wl.softmax_scale)
+        ls = [dict(L) for L in layers]
+        plans.append(csa2.GroupPlan(ls, cache, out_dtype=torch.bfloat16))
+    log("warmup %d steps" % args.warmup)
+    for s in range(args.warmup):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt / args.steps * 1e3
+    qps = wl.B / (ms_step / 1e3)
+    alg = algorithmic_bytes(wl)
+    step_gbs = alg / (ms_step / 1e3) / 1e9
+
+    log("timing the score kernel")
+    mean_ms, med_ms = time_score_kernel(wl, caches, layers, args.score_reps)
+    # algorithmic bytes of one score launch: per scored key 64 B key + 4 B scale read and
+    # 4 B score written; plus the query and weights
+    score_bytes = wl.B * wl.N * (wl.dk + 4 + 4) + wl.B * wl.H * (wl.dk * 2 + 4)
+    achieved = score_bytes / (mean_ms / 1e3) / 1e9
+
+    res = {
+        "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": "group128k: Full->Reindex->Reuse decode, B=16, N=131072, indexer 32x64 E4M3, "
+                               "Top-512, FP4 E2M1 main KV D=512, 64 heads bf16",
+                   "global_batch": wl.B, "seq_len": wl.N, "layers": list(wl.modes), "cache_copies": args.copies},
+        "step_algorithmic_bytes": alg, "step_achieved_GBps": round(step_gbs, 1),
+        "step_pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_score_fp8 (indexer score, one launch per indexing layer)",
+                     "kernel_ms_mean": round(mean_ms, 5), "kernel_ms_median": round(med_ms, 5),
+                     "bytes_per_launch": score_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

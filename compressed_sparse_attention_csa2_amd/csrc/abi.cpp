@@ -1,0 +1,430 @@
+// C ABI of the CSA2 library: host-side validation, workspace layout and launch order.
+// Every entry point validates all arguments before launching anything; nothing here
+// synchronises with the device, allocates device memory or keeps state beyond the cached
+// device check.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "../../include/csa2.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace csa2;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_dev_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+std::mutex g_dev_mu;
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CSA2_ERR_DEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return CSA2_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return CSA2_ERR_DEVICE;
+    g_dev_ok[dev] = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  return g_dev_ok[dev] == 1 ? CSA2_OK : CSA2_ERR_UNSUPPORTED;
+}
+
+inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline int dev_status(int rc) { return rc ? CSA2_ERR_DEVICE : CSA2_OK; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Bump allocator over the caller's workspace.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* p) : base(static_cast<char*>(p)) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+    off += align256(count * sizeof(T));
+    return p;
+  }
+};
+
+// ---- Top-K workspace: hist [R][bins] u32 | ctl [R] | candbuf [R][ncols] (key,pos)
+size_t topk_ws(int64_t R, int64_t ncols) {
+  return align256((size_t)R * kHistBins * 4) + align256((size_t)R * sizeof(RowCtl)) +
+         align256((size_t)R * ncols * sizeof(uint2));
+}
+struct TopkWs {
+  uint32_t* hist;
+  RowCtl* ctl;
+  uint2* cand;
+};
+TopkWs carve_topk(Carve& c, int64_t R, int64_t ncols) {
+  TopkWs t;
+  t.hist = c.take<uint32_t>((size_t)R * kHistBins);
+  t.ctl = c.take<RowCtl>((size_t)R);
+  t.cand = c.take<uint2>((size_t)R * ncols);
+  return t;
+}
+// zero the histogram and control words (they are contiguous at the start)
+int zero_topk(const TopkWs& t, int64_t R, hipStream_t st) {
+  const size_t bytes = (size_t)((char*)t.cand - (char*)t.hist);
+  return launch_fill_u32(t.hist, (int64_t)(bytes / 4), 0u, st);
+}
+
+// ---- attention workspace: counters | part_ml | part_o
+int attend_splits(int K, int num_splits) {
+  const int per = attend_entries_per_split();
+  const int minimum = (K + per - 1) / per;
+  if (num_splits <= 0) return minimum;
+  return num_splits;
+}
+size_t attend_ws(int64_t R, int Hq, int D, int splits, bool bf16) {
+  if (!bf16 || splits <= 1) return 0;
+  return align256((size_t)R * (Hq / 16) * 4) + align256((size_t)R * splits * Hq * 2 * 4) +
+         align256((size_t)R * splits * Hq * D * 4);
+}
+
+bool valid_dtype(int d) { return d == CSA2_F32 || d == CSA2_BF16; }
+
+int check_attend_shape(int B, int T, int Hq, int D, int K, int q_dtype, int out_dtype, int num_splits) {
+  if (B < 1 || T < 1 || Hq < 1 || Hq > CSA2_MAX_HQ || D < 2 || D > CSA2_MAX_D || K < 1 || K > CSA2_MAX_K)
+    return CSA2_ERR_SHAPE;
+  if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return CSA2_ERR_DTYPE;
+  if (D % 2) return CSA2_ERR_SHAPE;
+  if (q_dtype == CSA2_F32) {
+    if (out_dtype != CSA2_F32) return CSA2_ERR_DTYPE;
+  } else {
+    if (Hq % 16 || D % 128) return CSA2_ERR_UNSUPPORTED;
+    const int splits = attend_splits(K, num_splits);
+    if (num_splits < 0 || (K + splits - 1) / splits > attend_entries_per_split()) return CSA2_ERR_SHAPE;
+  }
+  if ((int64_t)B * T > 65535) return CSA2_ERR_SHAPE;
+  return CSA2_OK;
+}
+
+int check_index_shape(int prec, int B, int T, int H, int dk, int q_dtype, const void* k_scale, int64_t ncols) {
+  if (B < 1 || T < 1 || ncols < 1) return CSA2_ERR_SHAPE;
+  if ((int64_t)B * T > 65535) return CSA2_ERR_SHAPE;
+  if (!valid_dtype(q_dtype)) return CSA2_ERR_DTYPE;
+  if (prec == CSA2_PREC_FP32) {
+    if (q_dtype != CSA2_F32) return CSA2_ERR_DTYPE;
+    if (H < 1 || H > CSA2_MAX_H || dk < 1 || dk > CSA2_MAX_DK || (int64_t)H * dk > 8192) return CSA2_ERR_SHAPE;
+  } else if (prec == CSA2_PREC_FP8) {
+    if (H != 32 || dk != 64) return CSA2_ERR_UNSUPPORTED;
+    if (!k_scale) return CSA2_ERR_NULL;
+  } else {
+    return CSA2_ERR_DTYPE;
+  }
+  return CSA2_OK;
+}
+
+ScoreArgs score_args(int prec, int B, int T, int H, int dk, const void* q, int q_dtype, const float* w, const void* k,
+                     const float* k_scale, int64_t n_max, const int32_t* n_keys, const int32_t* q_limit,
+                     const int32_t* cand, int64_t ncols, float* scores, uint32_t* hist, int key_div) {
+  ScoreArgs a;
+  a.prec = prec;
+  a.q_bf16 = (q_dtype == CSA2_BF16);
+  a.B = B; a.T = T; a.H = H; a.dk = dk;
+  a.q = q; a.w = w; a.k = k; a.k_scale = k_scale;
+  a.n_max = n_max; a.n_keys = n_keys; a.q_limit = q_limit; a.cand = cand;
+  a.ncols = ncols; a.scores = scores; a.hist = hist; a.key_div = key_div;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(int status) {
+  switch (status) {
+    case CSA2_OK: return "CSA2_OK";
+    case CSA2_ERR_NULL: return "CSA2_ERR_NULL: a required pointer is NULL";
+    case CSA2_ERR_SHAPE: return "CSA2_ERR_SHAPE: a size is out of range or inconsistent";
+    case CSA2_ERR_DTYPE: return "CSA2_ERR_DTYPE: unsupported dtype, format or precision";
+    case CSA2_ERR_MODE: return "CSA2_ERR_MODE: invalid layer-mode schedule";
+    case CSA2_ERR_WORKSPACE: return "CSA2_ERR_WORKSPACE: workspace missing or too small";
+    case CSA2_ERR_UNSUPPORTED: return "CSA2_ERR_UNSUPPORTED: device or shape not supported";
+    case CSA2_ERR_DEVICE: return "CSA2_ERR_DEVICE: HIP runtime or launch failure";
+    default: return "unknown csa2 status";
+  }
+}
+
+int csa2_device_check(void) { return check_device(); }
+
+int csa2_quantize_kv(int fmt, int scale_policy, int B, int T, int D, const void* x, int x_dtype, int64_t x_stride_b,
+                     int64_t x_stride_t, const int32_t* n0, int64_t n_max, uint8_t* codes, float* scales,
+                     void* stream) {
+  if (!x || !codes || !scales) return CSA2_ERR_NULL;
+  if (!valid_dtype(x_dtype)) return CSA2_ERR_DTYPE;
+  if (B < 1 || T < 1 || D < 1 || n_max < 1 || x_stride_t < D || x_stride_b < 0 || B > 65535) return CSA2_ERR_SHAPE;
+  const bool bf16 = (x_dtype == CSA2_BF16);
+  if (fmt == CSA2_FMT_FP4_PER_CHANNEL) {
+    if (D % 2) return CSA2_ERR_SHAPE;
+    if (scale_policy != CSA2_SCALE_COMPUTE && scale_policy != CSA2_SCALE_GIVEN) return CSA2_ERR_DTYPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return dev_status(launch_quantize_fp4(scale_policy == CSA2_SCALE_COMPUTE, bf16, B, T, D, x, x_stride_b,
+                                          x_stride_t, n0, n_max, codes, scales, S(stream)));
+  }
+  if (fmt == CSA2_FMT_FP8_PER_TOKEN) {
+    if (scale_policy != CSA2_SCALE_COMPUTE) return CSA2_ERR_DTYPE;
+    if (D > 4096) return CSA2_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return dev_status(launch_quantize_fp8(bf16, B, T, D, x, x_stride_b, x_stride_t, n0, n_max, codes, scales,
+                                          S(stream)));
+  }
+  return CSA2_ERR_DTYPE;
+}
+
+int csa2_gather_dequant(int B, int T, int K, int D, const uint8_t* codes, const float* scales, int64_t n_max,
+                        const int32_t* idx, float* out, void* stream) {
+  if (!codes || !scales || !idx || !out) return CSA2_ERR_NULL;
+  if (B < 1 || T < 1 || K < 1 || D < 8 || D % 8 || n_max < 1) return CSA2_ERR_SHAPE;
+  int rc = check_device();
+  if (rc) return rc;
+  return dev_status(launch_gather_dequant(B, T, K, D, codes, scales, n_max, idx, out, S(stream)));
+}
+
+size_t csa2_index_score_workspace_size(int, int, int64_t) { return 0; }
+
+int csa2_index_score(int prec, int B, int T, int H, int dk, const void* q, int q_dtype, const float* w, const void* k,
+                     const float* k_scale, int64_t n_max, const int32_t* n_keys, const int32_t* q_limit,
+                     const int32_t* cand, int C, float* scores, void*, size_t, void* stream) {
+  if (!q || !w || !k || !n_keys || !scores) return CSA2_ERR_NULL;
+  if (n_max < 1 || (cand && C < 1)) return CSA2_ERR_SHAPE;
+  const int64_t ncols = cand ? C : n_max;
+  int rc = check_index_shape(prec, B, T, H, dk, q_dtype, k_scale, ncols);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  ScoreArgs a = score_args(prec, B, T, H, dk, q, q_dtype, w, k, k_scale, n_max, n_keys, q_limit, cand, ncols, scores,
+                           nullptr, 1);
+  return dev_status(launch_score(a, S(stream)));
+}
+
+size_t csa2_topk_workspace_size(int B, int T, int64_t ncols, int) { return topk_ws((int64_t)B * T, ncols); }
+
+int csa2_topk(int B, int T, int64_t ncols, const float* scores, const int32_t* cand, int K, int32_t* idx_out,
+              float* val_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!scores || !idx_out) return CSA2_ERR_NULL;
+  if (B < 1 || T < 1 || ncols < 1 || ncols > INT32_MAX || K < 1 || K > CSA2_MAX_K || (int64_t)B * T > 65535)
+    return CSA2_ERR_SHAPE;
+  const int64_t R = (int64_t)B * T;
+  if (!ws || ws_bytes < topk_ws(R, ncols)) return CSA2_ERR_WORKSPACE;
+  int rc = check_device();
+  if (rc) return rc;
+  Carve c(ws);
+  TopkWs t = carve_topk(c, R, ncols);
+  hipStream_t st = S(stream);
+  if (zero_topk(t, R, st)) return CSA2_ERR_DEVICE;
+  if (launch_topk_hist((int)R, ncols, scores, cand, t.hist, st)) return CSA2_ERR_DEVICE;
+  return dev_status(launch_topk_select((int)R, ncols, scores, cand, K, t.hist, t.ctl, t.cand, idx_out, val_out, st));
+}
+
+size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int) {
+  const int64_t R = (int64_t)B * T;
+  return align256((size_t)R * ncols * 4) + topk_ws(R, ncols);
+}
+
+int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_dtype, const float* w, const void* k,
+                    const float* k_scale, int64_t n_max, const int32_t* n_keys, const int32_t* q_limit,
+                    const int32_t* cand, int C, int K, int32_t* idx_out, float* val_out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (!q || !w || !k || !n_keys || !idx_out) return CSA2_ERR_NULL;
+  if (n_max < 1 || (cand && C < 1) || K < 1 || K > CSA2_MAX_K) return CSA2_ERR_SHAPE;
+  const int64_t ncols = cand ? C : n_max;
+  if (ncols > INT32_MAX) return CSA2_ERR_SHAPE;
+  int rc = check_index_shape(prec, B, T, H, dk, q_dtype, k_scale, ncols);
+  if (rc) return rc;
+  const int64_t R = (int64_t)B * T;
+  if (!ws || ws_bytes < csa2_index_topk_workspace_size(B, T, ncols, K)) return CSA2_ERR_WORKSPACE;
+  rc = check_device();
+  if (rc) return rc;
+  Carve c(ws);
+  float* scores = c.take<float>((size_t)R * ncols);
+  TopkWs t = carve_topk(c, R, ncols);
+  hipStream_t st = S(stream);
+  if (zero_topk(t, R, st)) return CSA2_ERR_DEVICE;
+  ScoreArgs a = score_args(prec, B, T, H, dk, q, q_dtype, w, k, k_scale, n_max, n_keys, q_limit, cand, ncols, scores,
+                           t.hist, 1);
+  if (launch_score(a, st)) return CSA2_ERR_DEVICE;
+  return dev_status(launch_topk_select((int)R, ncols, scores, cand, K, t.hist, t.ctl, t.cand, idx_out, val_out, st));
+}
+
+size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype, int num_splits) {
+  return attend_ws((int64_t)B * T, Hq, D, attend_splits(K, num_splits), q_dtype == CSA2_BF16);
+}
+
+int csa2_sparse_attend(int B, int T, int Hq, int D, const void* q, int q_dtype, const uint8_t* kv_codes,
+                       const float* kv_scales, int64_t n_max, const int32_t* idx, int K, float softmax_scale,
+                       void* out, int out_dtype, float* lse, int num_splits, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!q || !kv_codes || !kv_scales || !idx || !out) return CSA2_ERR_NULL;
+  if (n_max < 1) return CSA2_ERR_SHAPE;
+  int rc = check_attend_shape(B, T, Hq, D, K, q_dtype, out_dtype, num_splits);
+  if (rc) return rc;
+  const int splits = attend_splits(K, num_splits);
+  const size_t need = csa2_sparse_attend_workspace_size(B, T, Hq, D, K, q_dtype, num_splits);
+  if (need && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
+  rc = check_device();
+  if (rc) return rc;
+  AttendArgs a;
+  a.B = B; a.T = T; a.Hq = Hq; a.D = D; a.K = K;
+  a.q = q; a.q_bf16 = (q_dtype == CSA2_BF16);
+  a.codes = kv_codes; a.scales = kv_scales; a.n_max = n_max; a.idx = idx;
+  a.softmax_scale = softmax_scale; a.out = out; a.out_bf16 = (out_dtype == CSA2_BF16); a.lse = lse;
+  a.splits = a.q_bf16 ? splits : 1;
+  a.counters = nullptr; a.part_ml = nullptr; a.part_o = nullptr;
+  if (need) {
+    Carve c(ws);
+    const int64_t R = (int64_t)B * T;
+    a.counters = c.take<uint32_t>((size_t)R * (Hq / 16));
+    a.part_ml = c.take<float>((size_t)R * splits * Hq * 2);
+    a.part_o = c.take<float>((size_t)R * splits * Hq * D);
+  }
+  return dev_status(launch_attend(a, S(stream)));
+}
+
+// ---------------------------------------------------------------------------- layer group
+static int check_schedule(const csa2_layer* layers, int n) {
+  bool seen_full = false, seen_index = false;
+  for (int i = 0; i < n; ++i) {
+    switch (layers[i].mode) {
+      case CSA2_FULL: seen_full = seen_index = true; break;
+      case CSA2_REINDEX:
+        if (!seen_full) return CSA2_ERR_MODE;
+        seen_index = true;
+        break;
+      case CSA2_REUSE:
+        if (!seen_index) return CSA2_ERR_MODE;
+        break;
+      default: return CSA2_ERR_MODE;
+    }
+  }
+  return n > 0 ? CSA2_OK : CSA2_ERR_MODE;
+}
+
+size_t csa2_layer_group_workspace_size(const csa2_group_cache* c, int) {
+  if (!c) return 0;
+  const int64_t R = c->B;
+  const size_t att = attend_ws(R, c->Hq, c->D, attend_splits(c->K, 0), c->q_dtype == CSA2_BF16);
+  return align256((size_t)R * c->n_max * 4) + topk_ws(R, c->n_max) + att;
+}
+
+int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_cache* c, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (!layers || !c) return CSA2_ERR_NULL;
+  if (n_layers < 1) return CSA2_ERR_MODE;
+  int rc = check_schedule(layers, n_layers);
+  if (rc) return rc;
+  if (!c->n_keys || !c->kv_codes || !c->kv_scales || !c->k) return CSA2_ERR_NULL;
+  if (c->n_max < 1 || c->n_max > INT32_MAX || c->K < 1 || c->K > CSA2_MAX_K) return CSA2_ERR_SHAPE;
+  rc = check_index_shape(c->prec, c->B, 1, c->H, c->dk, c->q_dtype, c->k_scale, c->n_max);
+  if (rc) return rc;
+  rc = check_attend_shape(c->B, 1, c->Hq, c->D, c->K, c->q_dtype, c->out_dtype, 0);
+  if (rc) return rc;
+  for (int i = 0; i < n_layers; ++i) {
+    const csa2_layer& L = layers[i];
+    if (!L.q_attn || !L.out) return CSA2_ERR_NULL;
+    if (L.mode != CSA2_REUSE && (!L.q_idx || !L.w || !L.idx)) return CSA2_ERR_NULL;
+  }
+  if (!ws || ws_bytes < csa2_layer_group_workspace_size(c, n_layers)) return CSA2_ERR_WORKSPACE;
+  rc = check_device();
+  if (rc) return rc;
+
+  const int64_t R = c->B;
+  Carve cv(ws);
+  float* scores = cv.take<float>((size_t)R * c->n_max);
+  TopkWs t = carve_topk(cv, R, c->n_max);
+  const int splits = attend_splits(c->K, 0);
+  AttendArgs a;
+  a.B = c->B; a.T = 1; a.Hq = c->Hq; a.D = c->D; a.K = c->K;
+  a.q_bf16 = (c->q_dtype == CSA2_BF16);
+  a.codes = c->kv_codes; a.scales = c->kv_scales; a.n_max = c->n_max;
+  a.softmax_scale = c->softmax_scale; a.out_bf16 = (c->out_dtype == CSA2_BF16);
+  a.splits = a.q_bf16 ? splits : 1;
+  a.counters = nullptr; a.part_ml = nullptr; a.part_o = nullptr;
+  if (a.q_bf16 && splits > 1) {
+    a.counters = cv.take<uint32_t>((size_t)R * (c->Hq / 16));
+    a.part_ml = cv.take<float>((size_t)R * splits * c->Hq * 2);
+    a.part_o = cv.take<float>((size_t)R * splits * c->Hq * c->D);
+  }
+  hipStream_t st = S(stream);
+  const int32_t* last_idx = nullptr;
+  for (int i = 0; i < n_layers; ++i) {
+    const csa2_layer& L = layers[i];
+    if (L.mode != CSA2_REUSE) {
+      if (zero_topk(t, R, st)) return CSA2_ERR_DEVICE;
+      ScoreArgs sa = score_args(c->prec, c->B, 1, c->H, c->dk, L.q_idx, c->q_dtype, L.w, c->k, c->k_scale, c->n_max,
+                                c->n_keys, nullptr, nullptr, c->n_max, scores, t.hist, 1);
+      if (launch_score(sa, st)) return CSA2_ERR_DEVICE;
+      if (launch_topk_select((int)R, c->n_max, scores, nullptr, c->K, t.hist, t.ctl, t.cand, L.idx, nullptr, st))
+        return CSA2_ERR_DEVICE;
+      last_idx = L.idx;
+    }
+    a.q = L.q_attn;
+    a.idx = last_idx;
+    a.out = L.out;
+    a.lse = L.lse;
+    if (launch_attend(a, st)) return CSA2_ERR_DEVICE;
+  }
+  return CSA2_OK;
+}
+
+// ---------------------------------------------------------------------------- two-level indexer
+int csa2_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int block, const uint8_t* k8,
+                     const float* k_scale, uint8_t* kb8, float* kb_scale, void* stream) {
+  if (!n_keys || !k8 || !k_scale || !kb8 || !kb_scale) return CSA2_ERR_NULL;
+  if (B < 1 || B > 65535 || n_max < 1 || dk < 1 || dk > CSA2_MAX_DK || block < 1) return CSA2_ERR_SHAPE;
+  int rc = check_device();
+  if (rc) return rc;
+  return dev_status(launch_coarse_keys(B, n_max, n_keys, dk, block, k8, k_scale, kb8, kb_scale, S(stream)));
+}
+
+size_t csa2_hier_select_workspace_size(int B, int64_t n_max, int block, int block_topk, int) {
+  const int64_t nb = (n_max + block - 1) / block;
+  const int64_t C = (int64_t)block_topk * block;
+  return align256((size_t)B * nb * 4) + topk_ws(B, nb) + align256((size_t)B * block_topk * 4) +
+         align256((size_t)B * C * 4) + align256((size_t)B * C * 4) + topk_ws(B, C);
+}
+
+int csa2_hier_select(int B, int H, int dk, const void* q, int q_dtype, const float* w, const uint8_t* k8,
+                     const float* k_scale, const uint8_t* kb8, const float* kb_scale, int64_t n_max,
+                     const int32_t* n_keys, int block, int block_topk, int K, int32_t* idx_out, int32_t* block_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !w || !k8 || !k_scale || !kb8 || !kb_scale || !n_keys || !idx_out) return CSA2_ERR_NULL;
+  if (block < 1 || block_topk < 1 || block_topk > CSA2_MAX_K || K < 1 || K > CSA2_MAX_K || n_max < 1)
+    return CSA2_ERR_SHAPE;
+  const int64_t nb = (n_max + block - 1) / block;
+  const int64_t C = (int64_t)block_topk * block;
+  if (C > INT32_MAX || n_max > INT32_MAX) return CSA2_ERR_SHAPE;
+  int rc = check_index_shape(CSA2_PREC_FP8, B, 1, H, dk, q_dtype, k_scale, nb);
+  if (rc) return rc;
+  if (!ws || ws_bytes < csa2_hier_select_workspace_size(B, n_max, block, block_topk, K)) return CSA2_ERR_WORKSPACE;
+  rc = check_device();
+  if (rc) return rc;
+  Carve cv(ws);
+  float* cscores = cv.take<float>((size_t)B * nb);
+  TopkWs t1 = carve_topk(cv, B, nb);
+  int32_t* blocks = cv.take<int32_t>((size_t)B * block_topk);
+  int32_t* cand = cv.take<int32_t>((size_t)B * C);
+  float* fscores = cv.take<float>((size_t)B * C);
+  TopkWs t2 = carve_topk(cv, B, C);
+  hipStream_t st = S(stream);
+  if (zero_topk(t1, B, st) || zero_topk(t2, B, st)) return CSA2_ERR_DEVICE;
+  ScoreArgs a1 = score_args(CSA2_PREC_FP8, B, 1, H, dk, q, q_dtype, w, kb8, kb_scale, nb, n_keys, nullptr, nullptr,
+                            nb, cscores, t1.hist, block);
+  if (launch_score(a1, st)) return CSA2_ERR_DEVICE;
+  int32_t* bout = block_out ? block_out : blocks;
+  if (launch_topk_select(B, nb, cscores, nullptr, block_topk, t1.hist, t1.ctl, t1.cand, bout, nullptr, st))
+    return CSA2_ERR_DEVICE;
+  if (launch_expand_blocks(B, block_topk, block, bout, n_keys, cand, st)) return CSA2_ERR_DEVICE;
+  ScoreArgs a2 = score_args(CSA2_PREC_FP8, B, 1, H, dk, q, q_dtype, w, k8, k_scale, n_max, n_keys, nullptr, cand, C,
+                            fscores, t2.hist, 1);
+  if (launch_score(a2, st)) return CSA2_ERR_DEVICE;
+  return dev_status(launch_topk_select(B, C, fscores, cand, K, t2.hist, t2.ctl, t2.cand, idx_out, nullptr, st));
+}
+
+}  // extern "C"

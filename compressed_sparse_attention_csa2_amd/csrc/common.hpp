@@ -1,0 +1,115 @@
+// Device-side helpers shared by the CSA2 kernels (gfx950 / CDNA4, wave64).
+//
+// Number formats follow "FP4 Main KV Cache To Halve Storage Again" (E2M1 main KV) in the
+// DeepSeek V4.1 Flash paper notes and 3.5 of the Chinese reading (E4M3 scales); the
+// indexer's fp8 keys are OCP E4M3 ("FN").  Every codec here is exact: the tests compare
+// its bytes with an independent host implementation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+#define CSA2_MAX_D_DEV 512
+#define CSA2_MAX_K_DEV 2048
+#define CSA2_MAX_DK_DEV 256
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------- formats
+// E2M1 magnitude of y by round-to-nearest, ties to the even code, saturating at 6:
+// the seven decision points sit halfway between consecutive magnitudes
+// (0 .5 1 1.5 2 3 4 6); at a tie the comparison picks the even code.
+__device__ __forceinline__ uint32_t e2m1_encode(float y) {
+  const float a = fabsf(y);
+  uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+               (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return m | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+  // magnitudes by code: 0 .5 1 1.5 2 3 4 6 (exact in fp32)
+  const uint32_t m = code & 7u;
+  float mag = (m < 2u) ? 0.5f * (float)m : __uint_as_float(((m >> 1) + 126u) << 23 | (m & 1u) << 22);
+  return (code & 8u) ? -mag : mag;
+}
+
+// OCP E4M3 of y: round-to-nearest-even on the 3-bit mantissa, saturating at 448.
+// Normal range (|y| >= 2^-6): round the fp32 mantissa at bit 20 and rebias the exponent
+// (a mantissa carry moves into the exponent).  Below 2^-6 the grid is uniform with step
+// 2^-9, so the code is rint(|y| * 512) (exact scaling; rint is ties-to-even).
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t code;
+  if (!(a <= 448.0f)) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);
+    code = (u >> 20) - (120u << 3);
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = (e == 0u) ? (float)m * 0.001953125f : __uint_as_float((e + 120u) << 23 | m << 20);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// ---------------------------------------------------------------------------- ordering
+// Order-preserving 32-bit key of a visible score (larger score -> larger key); -0 and +0
+// map to the same key so that equal scores tie exactly as real numbers do.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = (f == 0.0f) ? 0u : __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ bool visible(float s) { return s > kNegInf; }  // false for NaN
+
+constexpr int kHistBits = 11;
+constexpr int kHistBins = 1 << kHistBits;
+__device__ __forceinline__ uint32_t hist_bin(uint32_t key) { return key >> (32 - kHistBits); }
+
+// ---------------------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace csa2

@@ -58,6 +58,7 @@ def _load():
         L.orc_topk.argtypes = [i, i, i64, p, p, i, p, p]
         L.orc_sparse_attend.argtypes = [i, i, i, i, p, p, p, i64, p, i, d, p, p]
         L.orc_coarse_keys.argtypes = [i, i64, p, i, i, p, p, p, p]
+        L.orc_num_threads.argtypes, L.orc_num_threads.restype = [], i
         for fn in ("orc_quantize_fp4", "orc_quantize_fp8", "orc_quantize_index_query", "orc_gather_dequant",
                    "orc_index_score", "orc_topk", "orc_sparse_attend", "orc_coarse_keys"):
             getattr(L, fn).restype = None
@@ -71,6 +72,10 @@ def _c(a, dtype):
 
 def _p(a):
     return None if a is None else a.ctypes.data
+
+
+def num_threads() -> int:
+    return _load().orc_num_threads()
 
 
 # ---------------------------------------------------------------------------- codecs

@@ -26,6 +26,7 @@
  * on the thread count.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -393,3 +394,6 @@ void orc_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int bl
     }
   }
 }
+
+/* Threads the oracle's parallel loops use (for reporting the CPU baseline). */
+int orc_num_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,301 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Bars: codec bytes, dequantised values, Top-K on given scores and coarse keys are
+bit-exact; fp32 indexer scores within 1e-5 of the fp64 reference relative to the
+per-element sum of |terms|; fp8 indexer scores within 1e-5 of that sum (fp32 accumulation
+of exact fp8 products); Top-K from GPU-computed scores by the near-tie rule (K-th and
+(K+1)-th within 1e-3 relative); attention max-abs-relative error <= 1e-5 (fp32 path) and
+<= 2e-3 (bf16 path, fp32 output), bf16 output per element within
+2e-3*max|ref| + half a bf16 ulp of the reference.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import (DEV, build_cache, check_topk_near_tie, e4m3_to_f64, fp8_score_bound, max_abs_rel, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+csa2 = pytest.importorskip("compressed_sparse_attention_csa2_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert csa2.device_check() == 0, "not a gfx950 device"
+
+
+# ------------------------------------------------------------------------------ codecs
+@pytest.mark.parametrize("name,n", [("tiny", 4096), ("full64k", 3001)])
+def test_quantize_fp4_bitexact(name, n):
+    wl = workloads.workload(name, B=2)
+    c = build_cache(wl, n_rows=n)
+    assert np.array_equal(c["scales"].cpu().numpy(), c["scales_ref"])
+    assert np.array_equal(c["codes"].cpu().numpy(), c["codes_ref"])
+
+
+def test_quantize_fp4_bf16_input_and_append_given_scales():
+    wl = workloads.workload("prefill", N=1000, T=333)
+    x = np.stack([wl.main_kv(0, rows=1000)])
+    codes_ref, s_ref = oracle.quantize_fp4(x, n_max=1333)
+    new = wl.new_kv()                                           # bf16 values [1][333][512]
+    oracle.quantize_fp4(new, n_max=1333, n0=np.array([1000], np.int32), scales=s_ref, codes=codes_ref)
+    codes = torch.zeros((1, 1333, 256), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((1, 512), dtype=torch.float32, device=DEV)
+    csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, to_dev(x), codes, scales)       # rows [0, 1000), COMPUTE
+    csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, to_dev(new, torch.bfloat16), codes, scales,
+                     scale_policy=csa2.SCALE_GIVEN, n0=to_dev(np.array([1000], np.int32)))
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), codes_ref)
+
+
+def test_quantize_fp4_strided_and_special_values():
+    x = np.zeros((1, 6, 64), np.float32)
+    x[0, 0, :16] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, -0.1, -0.0, 1e-30, -6.0, 3.0, 0.5, 1e4, -1e4]
+    x[0, 1:, :] = np.linspace(-3, 3, 5 * 64, dtype=np.float32).reshape(5, 64)
+    x[0, :, 20] = 0.0                                            # a zero channel -> scale 0, codes +0
+    s = np.ones((1, 64), np.float32)
+    s[0, 20] = 0.0
+    ref, _ = oracle.quantize_fp4(x, scales=s)
+    big = np.zeros((1, 6, 80), np.float32)                       # row stride 80 > D
+    big[:, :, :64] = x
+    xd = to_dev(big)[:, :, :64]
+    codes = torch.empty((1, 6, 32), dtype=torch.uint8, device=DEV)
+    sd = to_dev(s)
+    csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, xd, codes, sd, scale_policy=csa2.SCALE_GIVEN)
+    assert np.array_equal(codes.cpu().numpy(), ref)
+
+
+def test_quantize_fp8_bitexact_and_special_values():
+    wl = workloads.workload("full64k")
+    k = np.stack([wl.index_keys(b, rows=2500) for b in range(2)])
+    k[0, 0, :8] = [448.0, 0.0, -0.0, 1e-6, -1e-6, 2 ** -10, 3 * 2 ** -10, 100.0]
+    k[0, 1, :] = 0.0                                             # zero row -> scale 0
+    k8_ref, ks_ref = oracle.quantize_fp8(k)
+    k8 = torch.empty((2, 2500, 64), dtype=torch.uint8, device=DEV)
+    ks = torch.empty((2, 2500), dtype=torch.float32, device=DEV)
+    csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(k), k8, ks)
+    assert np.array_equal(ks.cpu().numpy(), ks_ref)
+    assert np.array_equal(k8.cpu().numpy(), k8_ref)
+
+
+def test_gather_dequant_bitexact():
+    wl = workloads.workload("full64k", B=2)
+    c = build_cache(wl, n_rows=777)
+    rng = np.random.default_rng(5)
+    idx = rng.integers(-1, 777, size=(2, 3, 40)).astype(np.int32)
+    idx[0, 0, 0] = 900                                           # out of range -> 0
+    ref = oracle.gather_dequant(c["codes_ref"], c["scales_ref"], idx)
+    got = csa2.gather_dequant(c["codes"], c["scales"], to_dev(idx)).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------------------ indexer
+def test_index_score_fp32_tiny():
+    wl = workloads.WORKLOADS["tiny"]
+    c = build_cache(wl)
+    q, w = wl.index_query(), wl.head_weights()
+    nk = np.array([4000], np.int32)
+    ref = oracle.index_score(oracle.PREC_FP32, q, w, c["kf"], None, nk)
+    got = csa2.index_score(csa2.PREC_FP32, to_dev(q), to_dev(w), c["kdev"], None, to_dev(nk)).cpu().numpy()
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    bound = np.einsum("bthd,bjd,bth->btj", np.abs(q.astype(np.float64)), np.abs(c["kf"].astype(np.float64)),
+                      np.abs(w.astype(np.float64)))
+    assert np.all(np.abs(got[fin] - ref[fin]) <= 1e-5 * bound[fin] + 1e-30)
+
+
+@pytest.mark.parametrize("T,causal", [(1, False), (3, True)])
+def test_index_score_fp8(T, causal):
+    wl = workloads.workload("full64k", B=3, T=T)
+    n = 20000
+    c = build_cache(wl, n_rows=n)
+    q, w = wl.index_query(), wl.head_weights()
+    nk = np.array([20000, 13001, 777], np.int32)
+    ql = np.array([[19990 + t * 3 for t in range(T)], [5000, 13000, 20000][:T], [0, 100, 776][:T]],
+                  np.int32) if causal else None
+    ref = oracle.index_score(oracle.PREC_FP8, q, w, c["k8_ref"], c["ks_ref"], nk, q_limit=ql)
+    got = csa2.index_score(csa2.PREC_FP8, to_dev(q, torch.bfloat16), to_dev(w), c["k8"], c["ks"], to_dev(nk),
+                           q_limit=None if ql is None else to_dev(ql)).cpu().numpy()
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    bound = fp8_score_bound(q, w, c["k8_ref"], c["ks_ref"])
+    err = np.abs(got[fin] - ref[fin])
+    assert np.all(err <= 1e-5 * bound[fin] + 1e-30), float(np.max(err / bound[fin]))
+
+
+def test_index_score_fp8_candidates():
+    wl = workloads.workload("full64k", B=2)
+    c = build_cache(wl, n_rows=5000)
+    q, w = wl.index_query(), wl.head_weights()
+    nk = np.array([5000, 4000], np.int32)
+    rng = np.random.default_rng(9)
+    cand = rng.integers(-1, 5000, size=(2, 1, 1111)).astype(np.int32)
+    ref = oracle.index_score(oracle.PREC_FP8, q, w, c["k8_ref"], c["ks_ref"], nk, cand=cand)
+    got = csa2.index_score(csa2.PREC_FP8, to_dev(q, torch.bfloat16), to_dev(w), c["k8"], c["ks"], to_dev(nk),
+                           cand=to_dev(cand)).cpu().numpy()
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    assert np.allclose(got[fin], ref[fin], rtol=1e-4, atol=1e-4 * np.abs(ref[fin]).max())
+
+
+# ------------------------------------------------------------------------------ Top-K
+@pytest.mark.parametrize("seed,n,K", [(0, 5000, 64), (1, 131072, 512), (2, 300, 512), (3, 70000, 2048),
+                                      (4, 4096, 1)])
+def test_topk_given_scores_exact(seed, n, K):
+    rng = np.random.default_rng(seed)
+    s = rng.normal(size=(3, 2, n)).astype(np.float32) * 30
+    s[0, 0, ::7] = np.round(s[0, 0, ::7])                        # ties
+    s[0, 1, :] = 1.0                                             # all equal: lowest positions win
+    s[1, 0, rng.random(n) < 0.3] = -np.inf                       # invisible columns
+    s[1, 1, :] = -np.inf                                         # nothing visible
+    s[2, 0, : n // 2] = -0.0                                     # -0 ties +0
+    s[2, 0, n // 2:] = 0.0
+    ref = oracle.topk(s.astype(np.float64), K)
+    got_i, got_v = csa2.topk(to_dev(s), K, want_values=True)
+    assert np.array_equal(got_i.cpu().numpy(), ref)
+    ref_v = np.where(ref >= 0, np.take_along_axis(s, np.maximum(ref, 0), axis=2), -np.inf)
+    assert np.array_equal(got_v.cpu().numpy(), ref_v.astype(np.float32))
+
+
+def test_topk_given_scores_with_candidates():
+    rng = np.random.default_rng(11)
+    cand = rng.permutation(100000)[:16384].astype(np.int32).reshape(1, 1, 16384)
+    cand[0, 0, rng.random(16384) < 0.05] = -1
+    s = rng.normal(size=(1, 1, 16384)).astype(np.float32)
+    ref = oracle.topk(s.astype(np.float64), 1024, cand=cand)
+    got = csa2.topk(to_dev(s), 1024, cand=to_dev(cand)).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_index_topk_fp8_near_tie():
+    wl = workloads.workload("full64k", B=4)
+    c = build_cache(wl, n_rows=30000)
+    q, w = wl.index_query(), wl.head_weights()
+    nk = np.array([30000, 29999, 1000, 300], np.int32)
+    ref_s = oracle.index_score(oracle.PREC_FP8, q, w, c["k8_ref"], c["ks_ref"], nk)
+    got = csa2.index_topk(csa2.PREC_FP8, to_dev(q, torch.bfloat16), to_dev(w), c["k8"], c["ks"], to_dev(nk),
+                          512).cpu().numpy()
+    exact = check_topk_near_tie(got, ref_s, 512)
+    assert exact >= 3
+
+
+# ------------------------------------------------------------------------------ attention
+def test_sparse_attend_fp32_tiny():
+    wl = workloads.WORKLOADS["tiny"]
+    c = build_cache(wl)
+    q = wl.attn_query()
+    rng = np.random.default_rng(2)
+    idx = np.sort(rng.choice(4096, 64, replace=False)).astype(np.int32)[None, None]
+    idx[0, 0, -3:] = -1
+    ref_o, ref_l = oracle.sparse_attend(q, c["codes_ref"], c["scales_ref"], idx, wl.softmax_scale)
+    out, lse = csa2.sparse_attend(to_dev(q), c["codes"], c["scales"], to_dev(idx), wl.softmax_scale)
+    assert max_abs_rel(out.cpu().numpy(), ref_o) <= 1e-5
+    assert np.allclose(lse.cpu().numpy(), ref_l, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("K,splits", [(512, 0), (512, 8), (100, 1), (1024, 0), (37, 0)])
+def test_sparse_attend_bf16(K, splits):
+    wl = workloads.workload("full64k", B=2, K=K)
+    c = build_cache(wl, n_rows=3000)
+    q = wl.attn_query()
+    rng = np.random.default_rng(K)
+    idx = np.stack([np.sort(rng.choice(3000, K, replace=False)) for _ in range(2)]).astype(np.int32)[:, None]
+    idx[1, 0, ::5] = -1                                          # skipped entries
+    ref_o, ref_l = oracle.sparse_attend(q, c["codes_ref"], c["scales_ref"], idx, wl.softmax_scale)
+    qd = to_dev(q, torch.bfloat16)
+    out, lse = csa2.sparse_attend(qd, c["codes"], c["scales"], to_dev(idx), wl.softmax_scale,
+                                  out_dtype=torch.float32, num_splits=splits)
+    assert max_abs_rel(out.cpu().numpy(), ref_o) <= 2e-3
+    assert np.allclose(lse.cpu().numpy(), ref_l, rtol=2e-3, atol=2e-3)
+    ob, _ = csa2.sparse_attend(qd, c["codes"], c["scales"], to_dev(idx), wl.softmax_scale, out_dtype=torch.bfloat16,
+                               num_splits=splits)
+    ob = ob.float().cpu().numpy()
+    half_ulp = np.abs(ref_o) * 2.0 ** -8
+    assert np.all(np.abs(ob - ref_o) <= 2e-3 * np.abs(ref_o).max() + half_ulp)
+
+
+def test_sparse_attend_bf16_empty_rows():
+    wl = workloads.workload("full64k", B=1, K=512)
+    c = build_cache(wl, n_rows=600)
+    q = wl.attn_query()
+    idx = np.full((1, 1, 512), -1, np.int32)
+    out, lse = csa2.sparse_attend(to_dev(q, torch.bfloat16), c["codes"], c["scales"], to_dev(idx), wl.softmax_scale,
+                                  out_dtype=torch.float32)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+# ------------------------------------------------------------------------------ layer group
+def test_layer_group_modes():
+    wl = workloads.workload("group128k", B=3, N=20000)
+    c = build_cache(wl)
+    nk = np.array([20000, 19000, 2000], np.int32)
+    layers, ref_layers = [], []
+    for i, m in enumerate(["full", "reindex", "reuse", "reuse"]):
+        qi, w, qa = wl.index_query(i), wl.head_weights(i), wl.attn_query(i)
+        ref_layers.append(dict(mode=m, q_idx=qi, w=w, q_attn=qa))
+        layers.append(dict(mode=m, q_idx=to_dev(qi, torch.bfloat16), w=to_dev(w), q_attn=to_dev(qa, torch.bfloat16)))
+    cache = csa2.GroupCache(to_dev(nk), c["codes"], c["scales"], c["k8"], c["ks"], wl.K, wl.softmax_scale)
+    csa2.layer_group(layers, cache, out_dtype=torch.float32)
+    rc = dict(k=c["k8_ref"], k_scale=c["ks_ref"], n_keys=nk, codes=c["codes_ref"], scales=c["scales_ref"])
+    ref = oracle.layer_group(ref_layers, rc, oracle.PREC_FP8, wl.K, wl.softmax_scale)
+    idx_last = None
+    for i, (L, R) in enumerate(zip(layers, ref)):
+        if L["mode"] != "reuse":
+            s = oracle.index_score(oracle.PREC_FP8, ref_layers[i]["q_idx"], ref_layers[i]["w"], c["k8_ref"],
+                                   c["ks_ref"], nk)
+            g = L["idx"].cpu().numpy()
+            check_topk_near_tie(g, s, wl.K)
+            idx_last = g
+        out = L["out"].cpu().numpy()
+        for b in range(3):
+            if np.array_equal(idx_last[b], R["idx"][b]):
+                assert max_abs_rel(out[b], R["out"][b]) <= 2e-3
+    # Reuse consumed the Reindex layer's indices unchanged: recompute it standalone
+    o3, _ = csa2.sparse_attend(layers[3]["q_attn"], c["codes"], c["scales"], layers[1]["idx"], wl.softmax_scale,
+                               out_dtype=torch.float32)
+    assert torch.equal(o3, layers[3]["out"])
+
+
+# ------------------------------------------------------------------------------ two-level indexer
+def test_coarse_keys_bitexact():
+    wl = workloads.workload("hier1m")
+    n = 64 * 300 + 17
+    k = wl.index_keys(0, rows=n)[None]
+    k8r, ksr = oracle.quantize_fp8(k)
+    nk = np.array([n - 5], np.int32)
+    kb_ref, kbs_ref = oracle.coarse_keys(k8r, ksr, nk, 64)
+    k8 = torch.empty((1, n, 64), dtype=torch.uint8, device=DEV)
+    ks = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(k), k8, ks)
+    kb, kbs = csa2.coarse_keys(k8, ks, to_dev(nk), 64)
+    assert np.array_equal(kbs.cpu().numpy(), kbs_ref)
+    assert np.array_equal(kb.cpu().numpy(), kb_ref)
+
+
+def test_hier_select_matches_oracle():
+    wl = workloads.workload("hier1m", N=64 * 2048)
+    n = wl.N
+    k = wl.index_keys(0)[None]
+    k8r, ksr = oracle.quantize_fp8(k)
+    nk = np.array([n - 100], np.int32)
+    kb_ref, kbs_ref = oracle.coarse_keys(k8r, ksr, nk, 64)
+    q, w = wl.index_query(), wl.head_weights()
+    ref_idx, ref_blk = oracle.hier_select(q, w, k8r, ksr, kb_ref, kbs_ref, nk, 64, 256, 1024)
+    k8 = torch.empty((1, n, 64), dtype=torch.uint8, device=DEV)
+    ks = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(k), k8, ks)
+    kb, kbs = csa2.coarse_keys(k8, ks, to_dev(nk), 64)
+    idx, blk = csa2.hier_select(to_dev(q, torch.bfloat16), to_dev(w), k8, ks, kb, kbs, to_dev(nk), 64, 256, 1024,
+                                want_blocks=True)
+    cs = oracle.index_score(oracle.PREC_FP8, q, w, kb_ref, kbs_ref, (nk + 63) // 64)
+    check_topk_near_tie(blk.cpu().numpy(), cs, 256)
+    if np.array_equal(blk.cpu().numpy(), ref_blk):
+        cand = oracle.expand_blocks(ref_blk, 64, nk)
+        fs = oracle.index_score(oracle.PREC_FP8, q, w, k8r, ksr, nk, cand=cand)
+        full = np.full((1, 1, n), -np.inf)
+        full[0, 0, cand[0, 0][cand[0, 0] >= 0]] = fs[0, 0][cand[0, 0] >= 0]
+        check_topk_near_tie(idx.cpu().numpy(), full, 1024)
