@@ -83,8 +83,8 @@ def lib() -> ctypes.CDLL:
             "csa2_topk_workspace_size": ([i, i, i64, i], sz),
             "csa2_index_topk": ([i, i, i, i, i, p, i, p, p, p, i64, p, p, p, i, i, p, p, p, sz, p], i),
             "csa2_index_topk_workspace_size": ([i, i, i64, i], sz),
-            "csa2_sparse_attend": ([i, i, i, i, p, i, p, p, i64, p, i, f, p, i, p, i, p, sz, p], i),
-            "csa2_sparse_attend_workspace_size": ([i, i, i, i, i, i, i], sz),
+            "csa2_sparse_attend": ([i, i, i, i, p, i, p, p, i64, p, i, f, p, i, p, p, sz, p], i),
+            "csa2_sparse_attend_workspace_size": ([i, i, i, i, i, i], sz),
             "csa2_layer_group": ([p, i, p, p, sz, p], i),
             "csa2_layer_group_workspace_size": ([p, i], sz),
             "csa2_coarse_keys": ([i, i64, p, i, i, p, p, p, p, p], i),
@@ -221,7 +221,7 @@ def index_topk(prec: int, q: torch.Tensor, w: torch.Tensor, k: torch.Tensor, k_s
 # ------------------------------------------------------------------------------ attention
 def sparse_attend(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, idx: torch.Tensor,
                   softmax_scale: float, out_dtype: Optional[torch.dtype] = None, want_lse: bool = True,
-                  num_splits: int = 0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
     B, T, Hq, D = q.shape
     n_max = codes.shape[1]
     K = idx.shape[-1]
@@ -230,11 +230,11 @@ def sparse_attend(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, id
     if lse is None and want_lse:
         lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
     qd = _dtype_code(q)
-    nb = lib().csa2_sparse_attend_workspace_size(B, T, Hq, D, K, qd, num_splits)
+    nb = lib().csa2_sparse_attend_workspace_size(B, T, Hq, D, K, qd)
     ws = _workspace(nb, q.device)
     _check(lib().csa2_sparse_attend(B, T, Hq, D, _ptr(q), qd, _ptr(codes), _ptr(scales), n_max, _ptr(idx), K,
-                                    float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse), num_splits,
-                                    _ptr(ws), nb, _stream()), "csa2_sparse_attend")
+                                    float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws), nb,
+                                    _stream()), "csa2_sparse_attend")
     return out, lse
 
 

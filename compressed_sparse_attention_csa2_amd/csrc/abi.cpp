@@ -10,6 +10,7 @@
 #include "../../include/csa2.h"
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_dev.hpp"
 
 using namespace csa2;
 
@@ -35,6 +36,8 @@ int check_device() {
 inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int dev_status(int rc) { return rc ? CSA2_ERR_DEVICE : CSA2_OK; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+// Top-K columns per row this build handles (the finaliser keeps per-region counts in LDS)
+constexpr int64_t kMaxTopkCols = (int64_t)kFinMaxRegions * kFilterColsPerBlock;
 
 // Bump allocator over the caller's workspace.
 struct Carve {
@@ -49,45 +52,58 @@ struct Carve {
   }
 };
 
-// ---- Top-K workspace: hist [R][bins] u32 | ctl [R] | candbuf [R][ncols] (key,pos)
-size_t topk_ws(int64_t R, int64_t ncols) {
-  return align256((size_t)R * kHistBins * 4) + align256((size_t)R * sizeof(RowCtl)) +
-         align256((size_t)R * ncols * sizeof(uint2));
+// ---- Top-K workspace: hist [R][bins] | hist2 [R][bins] | ctl [R] (zeroed per use) |
+//      candidate regions [R][regions][kFilterColsPerBlock] | counts [R][regions]
+size_t topk_zero_bytes(int64_t R) {
+  return 2 * align256((size_t)R * kHistBins * 4) + align256((size_t)R * sizeof(RowCtl));
 }
+size_t cand_bytes(int64_t R, int64_t ncols) {
+  const int64_t nreg = topk_regions(ncols);
+  return align256((size_t)R * nreg * kFilterColsPerBlock * sizeof(uint2)) + align256((size_t)R * nreg * 4);
+}
+size_t topk_ws(int64_t R, int64_t ncols) { return topk_zero_bytes(R) + cand_bytes(R, ncols); }
 struct TopkWs {
   uint32_t* hist;
+  uint32_t* hist2;
   RowCtl* ctl;
   uint2* cand;
+  uint32_t* cnt;
 };
-TopkWs carve_topk(Carve& c, int64_t R, int64_t ncols) {
+struct CandWs {
+  uint2* cand;
+  uint32_t* cnt;
+};
+CandWs carve_cand(Carve& c, int64_t R, int64_t ncols) {
+  const int64_t nreg = topk_regions(ncols);
+  CandWs w;
+  w.cand = c.take<uint2>((size_t)R * nreg * kFilterColsPerBlock);
+  w.cnt = c.take<uint32_t>((size_t)R * nreg);
+  return w;
+}
+TopkWs carve_topk_zero(Carve& c, int64_t R) {
   TopkWs t;
   t.hist = c.take<uint32_t>((size_t)R * kHistBins);
+  t.hist2 = c.take<uint32_t>((size_t)R * kHistBins);
   t.ctl = c.take<RowCtl>((size_t)R);
-  t.cand = c.take<uint2>((size_t)R * ncols);
+  t.cand = nullptr;
+  t.cnt = nullptr;
   return t;
 }
-// zero the histogram and control words (they are contiguous at the start)
+TopkWs carve_topk(Carve& c, int64_t R, int64_t ncols) {
+  TopkWs t = carve_topk_zero(c, R);
+  CandWs w = carve_cand(c, R, ncols);
+  t.cand = w.cand;
+  t.cnt = w.cnt;
+  return t;
+}
+// zero the histograms and control words (contiguous at the start of the Top-K workspace)
 int zero_topk(const TopkWs& t, int64_t R, hipStream_t st) {
-  const size_t bytes = (size_t)((char*)t.cand - (char*)t.hist);
-  return launch_fill_u32(t.hist, (int64_t)(bytes / 4), 0u, st);
-}
-
-// ---- attention workspace: counters | part_ml | part_o
-int attend_splits(int K, int num_splits) {
-  const int per = attend_entries_per_split();
-  const int minimum = (K + per - 1) / per;
-  if (num_splits <= 0) return minimum;
-  return num_splits;
-}
-size_t attend_ws(int64_t R, int Hq, int D, int splits, bool bf16) {
-  if (!bf16 || splits <= 1) return 0;
-  return align256((size_t)R * (Hq / 16) * 4) + align256((size_t)R * splits * Hq * 2 * 4) +
-         align256((size_t)R * splits * Hq * D * 4);
+  return launch_fill_u32(t.hist, (int64_t)(topk_zero_bytes(R) / 4), 0u, st);
 }
 
 bool valid_dtype(int d) { return d == CSA2_F32 || d == CSA2_BF16; }
 
-int check_attend_shape(int B, int T, int Hq, int D, int K, int q_dtype, int out_dtype, int num_splits) {
+int check_attend_shape(int B, int T, int Hq, int D, int K, int q_dtype, int out_dtype) {
   if (B < 1 || T < 1 || Hq < 1 || Hq > CSA2_MAX_HQ || D < 2 || D > CSA2_MAX_D || K < 1 || K > CSA2_MAX_K)
     return CSA2_ERR_SHAPE;
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return CSA2_ERR_DTYPE;
@@ -95,12 +111,23 @@ int check_attend_shape(int B, int T, int Hq, int D, int K, int q_dtype, int out_
   if (q_dtype == CSA2_F32) {
     if (out_dtype != CSA2_F32) return CSA2_ERR_DTYPE;
   } else {
-    if (Hq % 16 || D % 128) return CSA2_ERR_UNSUPPORTED;
-    const int splits = attend_splits(K, num_splits);
-    if (num_splits < 0 || (K + splits - 1) / splits > attend_entries_per_split()) return CSA2_ERR_SHAPE;
+    if (Hq % 16 || (D != 128 && D != 256 && D != 512)) return CSA2_ERR_UNSUPPORTED;
   }
   if ((int64_t)B * T > 65535) return CSA2_ERR_SHAPE;
   return CSA2_OK;
+}
+
+AttendArgs attend_args(int B, int T, int Hq, int D, int K, const void* q, int q_dtype, const uint8_t* codes,
+                       const float* scales, int64_t n_max, const int32_t* idx, float softmax_scale, void* out,
+                       int out_dtype, float* lse) {
+  AttendArgs a;
+  a.B = B; a.T = T; a.Hq = Hq; a.D = D; a.K = K;
+  a.q = q; a.q_bf16 = (q_dtype == CSA2_BF16);
+  a.codes = codes; a.scales = scales; a.n_max = n_max; a.idx = idx;
+  a.softmax_scale = softmax_scale; a.out = out; a.out_bf16 = (out_dtype == CSA2_BF16); a.lse = lse;
+  a.ctl = nullptr; a.hist2 = nullptr; a.candbuf = nullptr; a.cnt = nullptr; a.nreg = 0; a.idx_out = nullptr;
+  a.part = nullptr;
+  return a;
 }
 
 int check_index_shape(int prec, int B, int T, int H, int dk, int q_dtype, const void* k_scale, int64_t ncols) {
@@ -209,7 +236,7 @@ size_t csa2_topk_workspace_size(int B, int T, int64_t ncols, int) { return topk_
 int csa2_topk(int B, int T, int64_t ncols, const float* scores, const int32_t* cand, int K, int32_t* idx_out,
               float* val_out, void* ws, size_t ws_bytes, void* stream) {
   if (!scores || !idx_out) return CSA2_ERR_NULL;
-  if (B < 1 || T < 1 || ncols < 1 || ncols > INT32_MAX || K < 1 || K > CSA2_MAX_K || (int64_t)B * T > 65535)
+  if (B < 1 || T < 1 || ncols < 1 || ncols > kMaxTopkCols || K < 1 || K > CSA2_MAX_K || (int64_t)B * T > 65535)
     return CSA2_ERR_SHAPE;
   const int64_t R = (int64_t)B * T;
   if (!ws || ws_bytes < topk_ws(R, ncols)) return CSA2_ERR_WORKSPACE;
@@ -220,7 +247,9 @@ int csa2_topk(int B, int T, int64_t ncols, const float* scores, const int32_t* c
   hipStream_t st = S(stream);
   if (zero_topk(t, R, st)) return CSA2_ERR_DEVICE;
   if (launch_topk_hist((int)R, ncols, scores, cand, t.hist, st)) return CSA2_ERR_DEVICE;
-  return dev_status(launch_topk_select((int)R, ncols, scores, cand, K, t.hist, t.ctl, t.cand, idx_out, val_out, st));
+  if (launch_topk_filter((int)R, ncols, scores, cand, K, t.hist, t.hist2, t.ctl, t.cand, t.cnt, st))
+    return CSA2_ERR_DEVICE;
+  return dev_status(launch_topk_finalize((int)R, ncols, K, t.ctl, t.hist2, t.cand, t.cnt, idx_out, val_out, st));
 }
 
 size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int) {
@@ -235,7 +264,7 @@ int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_
   if (!q || !w || !k || !n_keys || !idx_out) return CSA2_ERR_NULL;
   if (n_max < 1 || (cand && C < 1) || K < 1 || K > CSA2_MAX_K) return CSA2_ERR_SHAPE;
   const int64_t ncols = cand ? C : n_max;
-  if (ncols > INT32_MAX) return CSA2_ERR_SHAPE;
+  if (ncols > kMaxTopkCols) return CSA2_ERR_SHAPE;
   int rc = check_index_shape(prec, B, T, H, dk, q_dtype, k_scale, ncols);
   if (rc) return rc;
   const int64_t R = (int64_t)B * T;
@@ -250,40 +279,30 @@ int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_
   ScoreArgs a = score_args(prec, B, T, H, dk, q, q_dtype, w, k, k_scale, n_max, n_keys, q_limit, cand, ncols, scores,
                            t.hist, 1);
   if (launch_score(a, st)) return CSA2_ERR_DEVICE;
-  return dev_status(launch_topk_select((int)R, ncols, scores, cand, K, t.hist, t.ctl, t.cand, idx_out, val_out, st));
+  if (launch_topk_filter((int)R, ncols, scores, cand, K, t.hist, t.hist2, t.ctl, t.cand, t.cnt, st))
+    return CSA2_ERR_DEVICE;
+  return dev_status(launch_topk_finalize((int)R, ncols, K, t.ctl, t.hist2, t.cand, t.cnt, idx_out, val_out, st));
 }
 
-size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype, int num_splits) {
-  return attend_ws((int64_t)B * T, Hq, D, attend_splits(K, num_splits), q_dtype == CSA2_BF16);
+size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype) {
+  if (q_dtype != CSA2_BF16) return 0;
+  return align256(attend_ws_floats(B * T, Hq, D, K) * 4);
 }
 
 int csa2_sparse_attend(int B, int T, int Hq, int D, const void* q, int q_dtype, const uint8_t* kv_codes,
                        const float* kv_scales, int64_t n_max, const int32_t* idx, int K, float softmax_scale,
-                       void* out, int out_dtype, float* lse, int num_splits, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !kv_codes || !kv_scales || !idx || !out) return CSA2_ERR_NULL;
   if (n_max < 1) return CSA2_ERR_SHAPE;
-  int rc = check_attend_shape(B, T, Hq, D, K, q_dtype, out_dtype, num_splits);
+  int rc = check_attend_shape(B, T, Hq, D, K, q_dtype, out_dtype);
   if (rc) return rc;
-  const int splits = attend_splits(K, num_splits);
-  const size_t need = csa2_sparse_attend_workspace_size(B, T, Hq, D, K, q_dtype, num_splits);
+  const size_t need = csa2_sparse_attend_workspace_size(B, T, Hq, D, K, q_dtype);
   if (need && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   rc = check_device();
   if (rc) return rc;
-  AttendArgs a;
-  a.B = B; a.T = T; a.Hq = Hq; a.D = D; a.K = K;
-  a.q = q; a.q_bf16 = (q_dtype == CSA2_BF16);
-  a.codes = kv_codes; a.scales = kv_scales; a.n_max = n_max; a.idx = idx;
-  a.softmax_scale = softmax_scale; a.out = out; a.out_bf16 = (out_dtype == CSA2_BF16); a.lse = lse;
-  a.splits = a.q_bf16 ? splits : 1;
-  a.counters = nullptr; a.part_ml = nullptr; a.part_o = nullptr;
-  if (need) {
-    Carve c(ws);
-    const int64_t R = (int64_t)B * T;
-    a.counters = c.take<uint32_t>((size_t)R * (Hq / 16));
-    a.part_ml = c.take<float>((size_t)R * splits * Hq * 2);
-    a.part_o = c.take<float>((size_t)R * splits * Hq * D);
-  }
+  AttendArgs a = attend_args(B, T, Hq, D, K, q, q_dtype, kv_codes, kv_scales, n_max, idx, softmax_scale, out,
+                             out_dtype, lse);
+  a.part = need ? static_cast<float*>(ws) : nullptr;
   return dev_status(launch_attend(a, S(stream)));
 }
 
@@ -306,11 +325,20 @@ static int check_schedule(const csa2_layer* layers, int n) {
   return n > 0 ? CSA2_OK : CSA2_ERR_MODE;
 }
 
-size_t csa2_layer_group_workspace_size(const csa2_group_cache* c, int) {
-  if (!c) return 0;
+static int count_index_layers(const csa2_layer* layers, int n) {
+  int c = 0;
+  for (int i = 0; i < n; ++i) c += (layers[i].mode != CSA2_REUSE);
+  return c;
+}
+
+// workspace: [hist, hist2, ctl per indexing layer (zeroed once per call)] [scores]
+//            [candidates] [attention partials]
+size_t csa2_layer_group_workspace_size(const csa2_group_cache* c, int n_layers) {
+  if (!c || n_layers < 1) return 0;
   const int64_t R = c->B;
-  const size_t att = attend_ws(R, c->Hq, c->D, attend_splits(c->K, 0), c->q_dtype == CSA2_BF16);
-  return align256((size_t)R * c->n_max * 4) + topk_ws(R, c->n_max) + att;
+  const int slots = n_layers < 64 ? n_layers : 64;
+  const size_t att = (c->q_dtype == CSA2_BF16) ? align256(attend_ws_floats((int)R, c->Hq, c->D, c->K) * 4) : 0;
+  return topk_zero_bytes(R) * (size_t)slots + align256((size_t)R * c->n_max * 4) + cand_bytes(R, c->n_max) + att;
 }
 
 int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_cache* c, void* ws, size_t ws_bytes,
@@ -320,10 +348,10 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   int rc = check_schedule(layers, n_layers);
   if (rc) return rc;
   if (!c->n_keys || !c->kv_codes || !c->kv_scales || !c->k) return CSA2_ERR_NULL;
-  if (c->n_max < 1 || c->n_max > INT32_MAX || c->K < 1 || c->K > CSA2_MAX_K) return CSA2_ERR_SHAPE;
+  if (c->n_max < 1 || c->n_max > kMaxTopkCols || c->K < 1 || c->K > CSA2_MAX_K) return CSA2_ERR_SHAPE;
   rc = check_index_shape(c->prec, c->B, 1, c->H, c->dk, c->q_dtype, c->k_scale, c->n_max);
   if (rc) return rc;
-  rc = check_attend_shape(c->B, 1, c->Hq, c->D, c->K, c->q_dtype, c->out_dtype, 0);
+  rc = check_attend_shape(c->B, 1, c->Hq, c->D, c->K, c->q_dtype, c->out_dtype);
   if (rc) return rc;
   for (int i = 0; i < n_layers; ++i) {
     const csa2_layer& L = layers[i];
@@ -335,39 +363,50 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   if (rc) return rc;
 
   const int64_t R = c->B;
+  const int n_index = count_index_layers(layers, n_layers);
+  const int slots = n_index < 64 ? n_index : 64;
   Carve cv(ws);
+  TopkWs tz[64];
+  for (int i = 0; i < slots; ++i) tz[i] = carve_topk_zero(cv, R);
+  const size_t zero_bytes = cv.off;
   float* scores = cv.take<float>((size_t)R * c->n_max);
-  TopkWs t = carve_topk(cv, R, c->n_max);
-  const int splits = attend_splits(c->K, 0);
-  AttendArgs a;
-  a.B = c->B; a.T = 1; a.Hq = c->Hq; a.D = c->D; a.K = c->K;
-  a.q_bf16 = (c->q_dtype == CSA2_BF16);
-  a.codes = c->kv_codes; a.scales = c->kv_scales; a.n_max = c->n_max;
-  a.softmax_scale = c->softmax_scale; a.out_bf16 = (c->out_dtype == CSA2_BF16);
-  a.splits = a.q_bf16 ? splits : 1;
-  a.counters = nullptr; a.part_ml = nullptr; a.part_o = nullptr;
-  if (a.q_bf16 && splits > 1) {
-    a.counters = cv.take<uint32_t>((size_t)R * (c->Hq / 16));
-    a.part_ml = cv.take<float>((size_t)R * splits * c->Hq * 2);
-    a.part_o = cv.take<float>((size_t)R * splits * c->Hq * c->D);
-  }
+  CandWs cw = carve_cand(cv, R, c->n_max);
+  float* part = (c->q_dtype == CSA2_BF16) ? cv.take<float>(attend_ws_floats((int)R, c->Hq, c->D, c->K)) : nullptr;
   hipStream_t st = S(stream);
+  // one fill clears every indexing layer's histograms and control words (more than 64
+  // indexing layers reuse the last slot, cleared again before each reuse)
+  if (slots > 0 && launch_fill_u32(tz[0].hist, (int64_t)(zero_bytes / 4), 0u, st)) return CSA2_ERR_DEVICE;
+
+  AttendArgs a = attend_args(c->B, 1, c->Hq, c->D, c->K, nullptr, c->q_dtype, c->kv_codes, c->kv_scales, c->n_max,
+                             nullptr, c->softmax_scale, nullptr, c->out_dtype, nullptr);
+  a.part = part;
   const int32_t* last_idx = nullptr;
+  int li = 0;
   for (int i = 0; i < n_layers; ++i) {
     const csa2_layer& L = layers[i];
+    a.q = L.q_attn;
+    a.out = L.out;
+    a.lse = L.lse;
+    a.ctl = nullptr; a.hist2 = nullptr; a.candbuf = nullptr; a.idx_out = nullptr; a.idx = last_idx;
     if (L.mode != CSA2_REUSE) {
-      if (zero_topk(t, R, st)) return CSA2_ERR_DEVICE;
+      TopkWs t = tz[li < slots ? li : slots - 1];
+      if (li >= slots && zero_topk(t, R, st)) return CSA2_ERR_DEVICE;
+      ++li;
       ScoreArgs sa = score_args(c->prec, c->B, 1, c->H, c->dk, L.q_idx, c->q_dtype, L.w, c->k, c->k_scale, c->n_max,
                                 c->n_keys, nullptr, nullptr, c->n_max, scores, t.hist, 1);
       if (launch_score(sa, st)) return CSA2_ERR_DEVICE;
-      if (launch_topk_select((int)R, c->n_max, scores, nullptr, c->K, t.hist, t.ctl, t.cand, L.idx, nullptr, st))
+      if (launch_topk_filter((int)R, c->n_max, scores, nullptr, c->K, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st))
         return CSA2_ERR_DEVICE;
+      if (a.q_bf16) {
+        a.ctl = t.ctl; a.hist2 = t.hist2; a.candbuf = cw.cand; a.cnt = cw.cnt; a.nreg = topk_regions(c->n_max);
+        a.idx_out = L.idx;
+      } else {
+        if (launch_topk_finalize((int)R, c->n_max, c->K, t.ctl, t.hist2, cw.cand, cw.cnt, L.idx, nullptr, st))
+          return CSA2_ERR_DEVICE;
+        a.idx = L.idx;
+      }
       last_idx = L.idx;
     }
-    a.q = L.q_attn;
-    a.idx = last_idx;
-    a.out = L.out;
-    a.lse = L.lse;
     if (launch_attend(a, st)) return CSA2_ERR_DEVICE;
   }
   return CSA2_OK;
@@ -399,7 +438,7 @@ int csa2_hier_select(int B, int H, int dk, const void* q, int q_dtype, const flo
     return CSA2_ERR_SHAPE;
   const int64_t nb = (n_max + block - 1) / block;
   const int64_t C = (int64_t)block_topk * block;
-  if (C > INT32_MAX || n_max > INT32_MAX) return CSA2_ERR_SHAPE;
+  if (C > kMaxTopkCols || nb > kMaxTopkCols || n_max > INT32_MAX) return CSA2_ERR_SHAPE;
   int rc = check_index_shape(CSA2_PREC_FP8, B, 1, H, dk, q_dtype, k_scale, nb);
   if (rc) return rc;
   if (!ws || ws_bytes < csa2_hier_select_workspace_size(B, n_max, block, block_topk, K)) return CSA2_ERR_WORKSPACE;
@@ -418,13 +457,17 @@ int csa2_hier_select(int B, int H, int dk, const void* q, int q_dtype, const flo
                             nb, cscores, t1.hist, block);
   if (launch_score(a1, st)) return CSA2_ERR_DEVICE;
   int32_t* bout = block_out ? block_out : blocks;
-  if (launch_topk_select(B, nb, cscores, nullptr, block_topk, t1.hist, t1.ctl, t1.cand, bout, nullptr, st))
+  if (launch_topk_filter(B, nb, cscores, nullptr, block_topk, t1.hist, t1.hist2, t1.ctl, t1.cand, t1.cnt, st))
+    return CSA2_ERR_DEVICE;
+  if (launch_topk_finalize(B, nb, block_topk, t1.ctl, t1.hist2, t1.cand, t1.cnt, bout, nullptr, st))
     return CSA2_ERR_DEVICE;
   if (launch_expand_blocks(B, block_topk, block, bout, n_keys, cand, st)) return CSA2_ERR_DEVICE;
   ScoreArgs a2 = score_args(CSA2_PREC_FP8, B, 1, H, dk, q, q_dtype, w, k8, k_scale, n_max, n_keys, nullptr, cand, C,
                             fscores, t2.hist, 1);
   if (launch_score(a2, st)) return CSA2_ERR_DEVICE;
-  return dev_status(launch_topk_select(B, C, fscores, cand, K, t2.hist, t2.ctl, t2.cand, idx_out, nullptr, st));
+  if (launch_topk_filter(B, C, fscores, cand, K, t2.hist, t2.hist2, t2.ctl, t2.cand, t2.cnt, st))
+    return CSA2_ERR_DEVICE;
+  return dev_status(launch_topk_finalize(B, C, K, t2.ctl, t2.hist2, t2.cand, t2.cnt, idx_out, nullptr, st));
 }
 
 }  // extern "C"

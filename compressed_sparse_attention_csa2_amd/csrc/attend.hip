@@ -4,290 +4,415 @@
 // before attention; "Model Setup Numbers Without Jargon": 64 heads of dim 512.  The whole
 // dequantised entry is both key and value.
 //
-// MFMA path (bf16 queries, Hq % 16 == 0, D % 128 == 0).  One block = 16 heads x up to
-// 128 selected entries (4 waves x 32).  The per-channel scale s_c factors out of both
-// contractions: logits use q' = q * s (fp32, split into bf16 hi + lo so that q' keeps
-// ~16 significant bits) against the exact E2M1 values e (bf16); the output is
-// s_c * sum_j p_j e_jc, with p in fp16 and e exact in fp16.  Each FP4 row is read
-// straight from HBM into MFMA operand layout (no LDS staging): for QK lane (entry n,
-// group g) takes 16 contiguous bytes per 128 channels; for PV lane (channel block n,
-// entry group g) takes one 32-bit word (8 channels) of each of 8 entries, so the 8
-// MFMAs of a k-step cover 8 interleaved channel sets.  Entries are split over blocks
-// (split-K); the last block of a (row, head group) to finish merges the partial results
-// by log-sum-exp.
+// MFMA path (bf16 queries, Hq % 16 == 0, D in {128, 256, 512}).  One block = one query
+// row x 16 heads (the MFMA M dimension) over all K selected entries, 16 waves, processed
+// in chunks of 512 entries with an online softmax.  The per-channel scale s_c factors
+// out of both contractions: logits use q'' = q * s * 2^k in fp16 (2^k an exact prescale
+// keeping |q''| below 2^15, undone in the softmax scale; ~2^-12 relative error) against
+// the exact E2M1 values e in fp16; the output is s_c * sum_j p_j e_jc / l with p in fp16.
+// FP4 rows go straight from HBM into MFMA operand layout (no LDS staging): for QK lane
+// (entry n, group g) reads 16 contiguous bytes per 128 channels; for PV lane (channel
+// block n, entry group g) reads one 32-bit word (8 channels) of each of 8 entries, so the
+// 8 MFMAs of a k-step cover 8 interleaved channel sets.  PV is split over waves by
+// (channel tile, entry group) and the entry groups are summed in LDS in a fixed order
+// (deterministic).  There is no split over blocks: merging partial softmaxes across blocks
+// needs either another launch or an in-kernel release fence, both slower here than the
+// extra per-block work.
 //
 // fp32 path (fp32 queries): plain VALU, one block per (row, head), fp32 throughout.
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_dev.hpp"
 
 namespace csa2 {
 
-constexpr int kAttHeads = 16;    // heads per block (MFMA M)
-constexpr int kAttEntries = 128; // entries per block (4 waves x 32)
+constexpr int kAttHeads = 16;      // heads per block (MFMA M)
+constexpr int kAttWaves = 8;       // two waves per SIMD, so that each SIMD interleaves two streams
+constexpr int kAttThreads = 64 * kAttWaves;
+constexpr int kAttSplit = 16 * kAttWaves;  // entries per block (one 16-entry tile per wave in QK)
+
+// partials: part_o [R][S][Hq][D] normalised outputs, part_ml [R][S][Hq][2] (max, sum)
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xFFFFu) | (hi16 << 16); }
 
-// E2M1 pair in byte BS of `word` -> two fp16 / bf16 values (exact; scale 1).
+// E2M1 pair in byte BS of `word` -> two fp16 values (exact; scale 1), low nibble first.
 template <int BS>
 __device__ __forceinline__ uint32_t cvt_pair_f16(uint32_t word) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, BS));
 }
-template <int BS>
-__device__ __forceinline__ uint32_t cvt_pair_bf16(uint32_t word) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, BS));
-}
 
-// 8 E2M1 codes of one 32-bit word -> 8 bf16 values (exact), in nibble order.
-__device__ __forceinline__ v8bf decode8_bf16(uint32_t word) {
-  const uint4 u = make_uint4(cvt_pair_bf16<0>(word), cvt_pair_bf16<1>(word), cvt_pair_bf16<2>(word),
-                             cvt_pair_bf16<3>(word));
-  return __builtin_bit_cast(v8bf, u);
+// 8 E2M1 codes of one 32-bit word -> 8 fp16 values (exact), in nibble order.
+__device__ __forceinline__ v8h decode8_f16(uint32_t word) {
+  const uint4 u = make_uint4(cvt_pair_f16<0>(word), cvt_pair_f16<1>(word), cvt_pair_f16<2>(word),
+                             cvt_pair_f16<3>(word));
+  return __builtin_bit_cast(v8h, u);
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_attend_mfma(int T, int Hq, int K, int splits, const uint16_t* __restrict__ q,
-                                                     const uint8_t* __restrict__ codes,
-                                                     const float* __restrict__ scales, int64_t n_max,
-                                                     const int32_t* __restrict__ idx, float softmax_scale,
-                                                     void* __restrict__ out, int out_bf16, float* __restrict__ lse,
-                                                     float* __restrict__ part_o, float* __restrict__ part_ml,
-                                                     uint32_t* __restrict__ counters) {
+struct AttLds {
+  static constexpr int kApad = D + 8;           // fp16 per A row (padding against bank conflicts)
+  static constexpr int kPpad = kAttSplit + 8;
+  static constexpr size_t kA = (size_t)kAttHeads * kApad * 2;
+  static constexpr size_t kP = (size_t)kAttHeads * kPpad * 2;
+  static constexpr size_t kO = (size_t)kAttHeads * D * 4;
+  static constexpr size_t kWork = kA + kP + kO;
+  static constexpr size_t kUnion = kWork > sizeof(FinalizeSmem) ? kWork : sizeof(FinalizeSmem);
+};
+
+// One block = one query row x 16 heads x one split of up to kAttSplit selected entries.
+// FROM_CAND: the block first derives the row's whole Top-K from the candidate list (every
+// block of the row does this identically; block (split 0, head group 0) writes idx_out).
+// With one split the block writes the final output; otherwise it writes its partial
+// (normalised output, running max, sum) for k_attend_combine.
+template <int D, bool FROM_CAND>
+__global__ __launch_bounds__(kAttThreads) void k_attend_part(
+    int T, int Hq, int K, int S, const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scales, int64_t n_max, const int32_t* __restrict__ idx, const RowCtl* __restrict__ ctl,
+    const uint32_t* __restrict__ hist2, const uint2* __restrict__ candbuf, const uint32_t* __restrict__ cnt, int nreg,
+    int32_t* __restrict__ idx_out, float softmax_scale, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
+    float* __restrict__ part, float* __restrict__ part_ml) {
+  using L = AttLds<D>;
   constexpr int kRowBytes = D / 2;
-  constexpr int kChunks = D / 128;
-  constexpr int kApad = D + 8;         // bf16 elements per A row (pad against bank conflicts)
-  constexpr int kPpad = kAttEntries + 8;
+  constexpr int kCT = D / 128;                 // 128-channel tiles
+  constexpr int kWPT = (kAttWaves / kCT < kAttSplit / 32) ? kAttWaves / kCT : kAttSplit / 32;  // waves per tile in PV
+  constexpr int kEPW = kAttSplit / kWPT;       // entries per wave in PV (a multiple of 32)
   __shared__ float s_scale[D];
-  __shared__ uint16_t s_ahi[kAttHeads * kApad];
-  __shared__ uint16_t s_alo[kAttHeads * kApad];
-  __shared__ uint16_t s_p[kAttHeads * kPpad];
-  __shared__ int32_t s_idx[kAttEntries];
-  __shared__ float s_red[4][kAttHeads];
+  __shared__ int32_t s_idx[FROM_CAND ? CSA2_MAX_K_DEV : kAttSplit];
+  __shared__ float s_red[kAttWaves][kAttHeads];
   __shared__ float s_m[kAttHeads], s_l[kAttHeads];
-  __shared__ uint32_t s_last;
+  __shared__ float s_qmax[kAttWaves];
+  __shared__ __align__(16) unsigned char s_u[L::kUnion];
+  uint16_t* sA = reinterpret_cast<uint16_t*>(s_u);
+  uint16_t* sP = reinterpret_cast<uint16_t*>(s_u + L::kA);
+  float* sO = reinterpret_cast<float*>(s_u + L::kA + L::kP);
 
   const int split = blockIdx.x, hg = blockIdx.y, r = blockIdx.z;
   const int b = r / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, g = lane >> 4;
-  const int per_split = (K + splits - 1) / splits;
-  const int e0 = split * per_split;
-  const int ecount = max(0, min(per_split, K - e0));
+  const int e0 = split * kAttSplit;            // first entry of this split
 
-  // ---- phase 0: scales, indices, q' = q * s split into bf16 hi + lo
-  for (int i = tid; i < D; i += 256) s_scale[i] = scales[(int64_t)b * D + i];
-  for (int i = tid; i < kAttEntries; i += 256) {
-    int32_t j = (i < ecount) ? idx[(int64_t)r * K + e0 + i] : -1;
-    s_idx[i] = (j >= 0 && j < n_max) ? j : -1;
+  // ---- phase 0: scales, the split's entries, q'' = q * s * 2^k in fp16
+  for (int i = tid; i < D; i += kAttThreads) s_scale[i] = scales[(int64_t)b * D + i];
+  const int32_t* sel;                           // the split's entries (LDS)
+  if (FROM_CAND) {
+    FinalizeSmem& fs = *reinterpret_cast<FinalizeSmem*>(s_u);
+    const RowCtl c = ctl[r];
+    const int keff = finalize_row<kAttThreads>(candbuf + (int64_t)r * nreg * kFilterColsPerBlock,
+                                               cnt + (int64_t)r * nreg, nreg, hist2 + (int64_t)r * kHistBins, c.beta,
+                                               c.above, c.keff, fs, s_idx, nullptr);
+    for (int i = keff + tid; i < K; i += kAttThreads) s_idx[i] = -1;
+    __syncthreads();
+    if (split == 0 && hg == 0 && idx_out)
+      for (int i = tid; i < K; i += kAttThreads) idx_out[(int64_t)r * K + i] = s_idx[i];
+    sel = s_idx + e0;
+  } else {
+    for (int i = tid; i < kAttSplit; i += kAttThreads) {
+      const int e = e0 + i;
+      const int32_t j = (e < K) ? idx[(int64_t)r * K + e] : -1;
+      s_idx[i] = (j >= 0 && j < n_max) ? j : -1;
+    }
+    sel = s_idx;
   }
-  __syncthreads();
+  const int ecount = min(kAttSplit, K - e0);
+
   const uint16_t* qb = q + ((int64_t)r * Hq + hg * kAttHeads) * D;
-  for (int i = tid; i < kAttHeads * D / 8; i += 256) {
-    const int h = i / (D / 8), c = (i % (D / 8)) * 8;
+  constexpr int kQItems = kAttHeads * D / 8;       // 8 channels per item
+  constexpr int kQPer = (kQItems + kAttThreads - 1) / kAttThreads;
+  float qv[kQPer][8];
+  float qmax = 0.0f;
+  __syncthreads();  // s_scale
+#pragma unroll
+  for (int it = 0; it < kQPer; ++it) {
+    const int i = tid + it * kAttThreads;
+    const int ic = i < kQItems ? i : kQItems - 1;
+    const int h = ic / (D / 8), c = (ic % (D / 8)) * 8;
     const uint4 raw = *reinterpret_cast<const uint4*>(qb + (int64_t)h * D + c);
     const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[it][e] = bf16_to_f32((uint16_t)(wds[e >> 1] >> (16 * (e & 1)))) * s_scale[c + e];
+      qmax = fmaxf(qmax, fabsf(qv[it][e]));
+    }
+  }
+  qmax = wave_max(qmax);
+  if (lane == 0) s_qmax[wave] = qmax;
+  if (tid < kAttHeads) {
+    s_m[tid] = kNegInf;
+    s_l[tid] = 0.0f;
+  }
+  __syncthreads();
+  qmax = s_qmax[0];
+#pragma unroll
+  for (int w2 = 1; w2 < kAttWaves; ++w2) qmax = fmaxf(qmax, s_qmax[w2]);
+  // power-of-two prescale so that |q''| < 2^15 (fp16 max 65504); exact, undone in the logits
+  int qexp = 0;
+  if (qmax > 0.0f) qexp = (int)((__float_as_uint(qmax) >> 23) & 255u) - 126;
+  const float up = __uint_as_float((uint32_t)(127 + 15 - qexp) << 23);
+  const float down = __uint_as_float((uint32_t)(127 - 15 + qexp) << 23);
+  const float lscale = softmax_scale * down;
+#pragma unroll
+  for (int it = 0; it < kQPer; ++it) {
+    const int i = tid + it * kAttThreads;
+    if (i >= kQItems) break;
+    const int h = i / (D / 8), c = (i % (D / 8)) * 8;
+    uint32_t wv[4];
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
-      uint32_t hh[2], ll[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float qv = bf16_to_f32((uint16_t)(wds[k2] >> (16 * e)));
-        const float qs = qv * s_scale[c + 2 * k2 + e];
-        const uint16_t h16 = bf16_rne(qs);
-        hh[e] = h16;
-        ll[e] = bf16_rne(qs - bf16_to_f32(h16));
-      }
-      hi[k2] = pack2(hh[0], hh[1]);
-      lo[k2] = pack2(ll[0], ll[1]);
+      const _Float16 a0 = (_Float16)(qv[it][2 * k2] * up), a1 = (_Float16)(qv[it][2 * k2 + 1] * up);
+      wv[k2] = pack2(__builtin_bit_cast(uint16_t, a0), __builtin_bit_cast(uint16_t, a1));
     }
-    *reinterpret_cast<uint4*>(&s_ahi[h * kApad + c]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    *reinterpret_cast<uint4*>(&s_alo[h * kApad + c]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(&sA[h * L::kApad + c]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
   __syncthreads();
 
-  // ---- phase 1: logits for this wave's 32 entries (two 16-entry tiles)
-  float logit[2][4];
+  // ---- phase 1: logits of this wave's 16 entries
   const uint8_t* cb = codes + (int64_t)b * n_max * kRowBytes;
+  float logit[4];
+  {
+    const int e = wave * 16 + n16;
+    const int32_t j = (e < ecount) ? sel[e] : -1;
+    // unconditional loads from a valid row (row 0 for skipped entries) keep the loads
+    // branch-free so that they pipeline; skipped entries are masked in the logits
+    const uint8_t* rowp = cb + (int64_t)(j >= 0 ? j : 0) * kRowBytes + 16 * g;
+    uint4 kw[kCT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int el = wave * 32 + nt * 16 + n16;
-    const int32_t j = s_idx[el];
-    uint4 kw[kChunks];
+    for (int i = 0; i < kCT; ++i) kw[i] = *reinterpret_cast<const uint4*>(rowp + 64 * i);
+    v4f a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i)
-      kw[i] = (j >= 0) ? *reinterpret_cast<const uint4*>(cb + (int64_t)j * kRowBytes + 64 * i + 16 * g)
-                       : make_uint4(0, 0, 0, 0);
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
+    for (int i = 0; i < kCT; ++i) {
       const uint32_t wd[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
-        const v8bf bv = decode8_bf16(wd[sub]);
-        const int c = 128 * i + 32 * g + 8 * sub;
-        const v8bf ah = *reinterpret_cast<const v8bf*>(&s_ahi[n16 * kApad + c]);
-        const v8bf al = *reinterpret_cast<const v8bf*>(&s_alo[n16 * kApad + c]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc, 0, 0, 0);
+        const v8h bv = decode8_f16(wd[sub]);
+        const v8h av = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, a, 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) logit[nt][rr] = (j >= 0) ? acc[rr] * softmax_scale : kNegInf;
+    for (int rr = 0; rr < 4; ++rr) logit[rr] = (j >= 0) ? a[rr] * lscale : kNegInf;
   }
 
-  // ---- phase 2: softmax statistics over the block's entries (heads 4g + rr of this lane)
-  float mx[4];
+  // ---- phase 2: softmax statistics of the split (heads 4g + rr of this lane)
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    float v = fmaxf(logit[0][rr], logit[1][rr]);
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-    mx[rr] = v;
+    const float v = row16_max(logit[rr]);
+    if (n16 == 0) s_red[wave][4 * g + rr] = v;
   }
-  if (n16 == 0)
+  __syncthreads();
+  if (tid < kAttHeads) {
+    float mc = s_red[0][tid];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) s_red[wave][4 * g + rr] = mx[rr];
+    for (int w2 = 1; w2 < kAttWaves; ++w2) mc = fmaxf(mc, s_red[w2][tid]);
+    s_m[tid] = mc;
+  }
   __syncthreads();
-  if (tid < kAttHeads) s_m[tid] = fmaxf(fmaxf(s_red[0][tid], s_red[1][tid]), fmaxf(s_red[2][tid], s_red[3][tid]));
-  __syncthreads();
-  float psum[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int h = 4 * g + rr;
     const float m = s_m[h];
-    float v = 0.0f;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float p = (m == kNegInf) ? 0.0f : __expf(logit[nt][rr] - m);
-      const _Float16 ph = (_Float16)p;
-      s_p[h * kPpad + wave * 32 + nt * 16 + n16] = __builtin_bit_cast(uint16_t, ph);
-      v += p;
-    }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
-    psum[rr] = v;
+    const float p = (m == kNegInf) ? 0.0f : __expf(logit[rr] - m);
+    const _Float16 ph = (_Float16)p;
+    sP[h * L::kPpad + wave * 16 + n16] = __builtin_bit_cast(uint16_t, ph);
+    const float v = row16_sum(p);
+    if (n16 == 0) s_red[wave][h] = v;
   }
   __syncthreads();
-  if (n16 == 0)
+  if (tid < kAttHeads) {
+    float sum = 0.0f;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) s_red[wave][4 * g + rr] = psum[rr];
-  __syncthreads();
-  if (tid < kAttHeads) s_l[tid] = (s_red[0][tid] + s_red[1][tid]) + (s_red[2][tid] + s_red[3][tid]);
-  __syncthreads();
+    for (int w2 = 0; w2 < kAttWaves; ++w2) sum += s_red[w2][tid];
+    s_l[tid] = sum;
+  }
 
-  // ---- phase 3: o[h][c] = sum_j p[h][j] e[j][c]; wave w covers channel tiles w, w+4, ...
-  const bool single = (splits == 1);
-  for (int ct = wave; ct < kChunks; ct += 4) {
-    v4f acc[8];
+  // ---- phase 3: o[h][c] = sum_j p[h][j] e[j][c] over this wave's entries and channel tile.
+  //      B operands: for each pair of entries the two code words are nibble-interleaved
+  //      so that one byte holds the same channel of both entries; one fp4->fp16 pair
+  //      conversion then yields the (entry 2p, entry 2p+1) dword the MFMA k-order wants.
+  const int ct = wave % kCT, eq = wave / kCT;
+  const bool pv_active = eq < kWPT;
+  v4f acc[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < 8; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
+  if (pv_active) {
 #pragma unroll
-    for (int ks = 0; ks < kAttEntries / 32; ++ks) {
-      const v8h pa = *reinterpret_cast<const v8h*>(&s_p[n16 * kPpad + 32 * ks + 8 * g]);
+    for (int ks = 0; ks < kEPW / 32; ++ks) {
+      const int el = eq * kEPW + 32 * ks + 8 * g;  // first of this lane's 8 entries
+      const v8h pa = *reinterpret_cast<const v8h*>(&sP[n16 * L::kPpad + el]);
       uint32_t wd[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        const int32_t j = s_idx[32 * ks + 8 * g + jj];
-        wd[jj] = (j >= 0) ? *reinterpret_cast<const uint32_t*>(cb + (int64_t)j * kRowBytes + 64 * ct + 4 * n16) : 0u;
+        const int e = el + jj;
+        const int32_t j = (e < ecount) ? sel[e] : -1;
+        // p is 0 for skipped entries, so any valid row may stand in for them
+        wd[jj] = *reinterpret_cast<const uint32_t*>(cb + (int64_t)(j >= 0 ? j : 0) * kRowBytes + 64 * ct + 4 * n16);
       }
-      // cv[jj][bsel] = channels (2 bsel, 2 bsel + 1) of entry jj as two fp16
-      uint32_t cv[8][4];
+      uint32_t xe[4], xo[4];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        cv[jj][0] = cvt_pair_f16<0>(wd[jj]);
-        cv[jj][1] = cvt_pair_f16<1>(wd[jj]);
-        cv[jj][2] = cvt_pair_f16<2>(wd[jj]);
-        cv[jj][3] = cvt_pair_f16<3>(wd[jj]);
+      for (int p2 = 0; p2 < 4; ++p2) {
+        const uint32_t w0 = wd[2 * p2], w1 = wd[2 * p2 + 1];
+        xe[p2] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);  // channels 0,2,4,6
+        xo[p2] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);  // channels 1,3,5,7
       }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int bs = m >> 1, hi = m & 1;
-        uint32_t bw[4];
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const uint32_t x0 = hi ? (cv[2 * q2][bs] >> 16) : cv[2 * q2][bs];
-          const uint32_t x1 = hi ? (cv[2 * q2 + 1][bs] >> 16) : cv[2 * q2 + 1][bs];
-          bw[q2] = pack2(x0, x1);
-        }
-        const v8h bv = __builtin_bit_cast(v8h, make_uint4(bw[0], bw[1], bw[2], bw[3]));
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, acc[m], 0, 0, 0);
-      }
-    }
-    // lane holds heads 4g + rr, channel 128 ct + 8 n16 + m
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int h = 4 * g + rr;
-      const float l = s_l[h];
-      const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int c = 128 * ct + 8 * n16 + m;
-        const float o = acc[m][rr] * inv * s_scale[c];
-        const int64_t oh = (int64_t)r * Hq + hg * kAttHeads + h;
-        if (single) {
-          if (out_bf16)
-            reinterpret_cast<uint16_t*>(out)[oh * D + c] = bf16_rne(o);
-          else
-            reinterpret_cast<float*>(out)[oh * D + c] = o;
-        } else {
-          part_o[(((int64_t)r * splits + split) * Hq + hg * kAttHeads + h) * D + c] = o;
-        }
-      }
-    }
+#define CSA2_PV_MFMA(M, X, BS)                                                                                  \
+  {                                                                                                          \
+    const uint4 bw = make_uint4(cvt_pair_f16<BS>(X[0]), cvt_pair_f16<BS>(X[1]), cvt_pair_f16<BS>(X[2]),      \
+                                cvt_pair_f16<BS>(X[3]));                                                     \
+    acc[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(v8h, bw), acc[M], 0, 0, 0);       \
   }
-  if (single) {
-    if (lse && tid < kAttHeads) {
-      const float l = s_l[tid];
-      lse[(int64_t)r * Hq + hg * kAttHeads + tid] = (l > 0.0f) ? s_m[tid] + __logf(l) : kNegInf;
+      CSA2_PV_MFMA(0, xe, 0) CSA2_PV_MFMA(1, xo, 0) CSA2_PV_MFMA(2, xe, 1) CSA2_PV_MFMA(3, xo, 1)
+      CSA2_PV_MFMA(4, xe, 2) CSA2_PV_MFMA(5, xo, 2) CSA2_PV_MFMA(6, xe, 3) CSA2_PV_MFMA(7, xo, 3)
+#undef CSA2_PV_MFMA
     }
-    return;
-  }
-  if (tid < kAttHeads) {
-    float* ml = part_ml + (((int64_t)r * splits + split) * Hq + hg * kAttHeads + tid) * 2;
-    ml[0] = s_m[tid];
-    ml[1] = s_l[tid];
   }
 
-  // ---- phase 4: the last split block of (r, hg) merges all splits by log-sum-exp
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&counters[(int64_t)r * (Hq / kAttHeads) + hg], 1u) == (uint32_t)splits - 1) ? 1u : 0u;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid < kAttHeads) {
-    const int h = tid;
-    float M = kNegInf;
-    for (int s = 0; s < splits; ++s) {
-      const float* ml = part_ml + (((int64_t)r * splits + s) * Hq + hg * kAttHeads + h) * 2;
-      if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
-    }
-    float Z = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-      const float* ml = part_ml + (((int64_t)r * splits + s) * Hq + hg * kAttHeads + h) * 2;
-      if (ml[1] > 0.0f) Z += ml[1] * __expf(ml[0] - M);
-    }
-    s_m[h] = M;
-    s_l[h] = Z;
-    if (lse) lse[(int64_t)r * Hq + hg * kAttHeads + h] = (Z > 0.0f) ? M + __logf(Z) : kNegInf;
+  // ---- phase 4: normalise and store.  With one wave per channel tile (D = 512) each lane
+  //      stores its own results (8 consecutive channels per head); otherwise the entry
+  //      groups of a tile are first summed in LDS in a fixed order.
+  __syncthreads();  // s_l
+  float inv_l[4], m_h[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const float l = s_l[4 * g + rr];
+    inv_l[rr] = (l > 0.0f) ? 1.0f / l : 0.0f;
+    m_h[rr] = s_m[4 * g + rr];
   }
-  __syncthreads();
-  for (int i = tid; i < kAttHeads * D; i += 256) {
-    const int h = i / D, c = i % D;
-    const float M = s_m[h], Z = s_l[h];
-    float o = 0.0f;
-    if (Z > 0.0f) {
-      for (int s = 0; s < splits; ++s) {
-        const int64_t base = ((int64_t)r * splits + s) * Hq + hg * kAttHeads + h;
-        const float* ml = part_ml + base * 2;
-        if (ml[1] > 0.0f) o = fmaf(ml[1] * __expf(ml[0] - M) / Z, part_o[base * D + c], o);
+  if (kWPT > 1) {
+    for (int round = 0; round < kWPT; ++round) {
+      if (eq == round) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            float* o = &sO[(4 * g + rr) * D + 128 * ct + 8 * n16 + m];
+            *o = (round == 0) ? acc[m][rr] : *o + acc[m][rr];
+          }
+      }
+      __syncthreads();
+    }
+    if (eq == 0) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m][rr] = sO[(4 * g + rr) * D + 128 * ct + 8 * n16 + m];
+    }
+  }
+  if (eq == 0) {
+    const int c = 128 * ct + 8 * n16;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int h = hg * kAttHeads + 4 * g + rr;
+      float o[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) o[m] = acc[m][rr] * inv_l[rr];
+      if (S == 1) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) o[m] *= s_scale[c + m];
+        const int64_t oi = ((int64_t)r * Hq + h) * D + c;
+        if (out_bf16) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int k2 = 0; k2 < 4; ++k2) w4[k2] = pack2(bf16_rne(o[2 * k2]), bf16_rne(o[2 * k2 + 1]));
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + oi) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        } else {
+          float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi);
+          dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+          dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        }
+      } else {
+        float4* dst = reinterpret_cast<float4*>(part + (((int64_t)r * S + split) * Hq + h) * D + c);
+        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
       }
     }
-    const int64_t oh = (int64_t)r * Hq + hg * kAttHeads + h;
-    if (out_bf16)
-      reinterpret_cast<uint16_t*>(out)[oh * D + c] = bf16_rne(o);
-    else
-      reinterpret_cast<float*>(out)[oh * D + c] = o;
+  }
+  if (tid < kAttHeads) {
+    const float l = s_l[tid];
+    if (S == 1) {
+      if (lse) lse[(int64_t)r * Hq + hg * kAttHeads + tid] = (l > 0.0f) ? s_m[tid] + __logf(l) : kNegInf;
+    } else {
+      float* ml = part_ml + (((int64_t)r * S + split) * Hq + hg * kAttHeads + tid) * 2;
+      ml[0] = s_m[tid];
+      ml[1] = l;
+    }
+  }
+}
+
+// Merge the splits of (row, head group, channel tile) by log-sum-exp and scale by s_c.
+// Thread t: head t / 16 of the group, channels 128 ct + 8 (t % 16) + [0, 8); all split
+// loads are issued before any is used.
+template <int D>
+__global__ __launch_bounds__(256) void k_attend_combine(int T, int Hq, int S, const float* __restrict__ scales,
+                                                        const float* __restrict__ part,
+                                                        const float* __restrict__ part_ml, void* __restrict__ out,
+                                                        int out_bf16, float* __restrict__ lse) {
+  constexpr int kCT = D / 128;
+  constexpr int kMaxS = CSA2_MAX_K_DEV / kAttSplit;
+  __shared__ float s_w[kMaxS][kAttHeads];
+  const int hg = blockIdx.x / kCT, ct = blockIdx.x % kCT, r = blockIdx.y;
+  const int b = r / T;
+  const int tid = threadIdx.x;
+  const int hl = tid >> 4, c = 128 * ct + 8 * (tid & 15);
+  const int h = hg * kAttHeads + hl;
+  // issue the partial loads first (up to kMaxS splits, 2 x 16 B each)
+  float4 pv[kMaxS][2];
+#pragma unroll
+  for (int s = 0; s < kMaxS; ++s) {
+    if (s < S) {
+      const float4* src = reinterpret_cast<const float4*>(part + (((int64_t)r * S + s) * Hq + h) * D + c);
+      pv[s][0] = src[0];
+      pv[s][1] = src[1];
+    }
+  }
+  const float4 sc0 = *reinterpret_cast<const float4*>(scales + (int64_t)b * D + c);
+  const float4 sc1 = *reinterpret_cast<const float4*>(scales + (int64_t)b * D + c + 4);
+  if (tid < kAttHeads) {
+    const float* ml = part_ml + ((int64_t)r * S) * Hq * 2;
+    const int hh = hg * kAttHeads + tid;
+    float mv[kMaxS], lv[kMaxS];
+    float M = kNegInf;
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s) {
+      mv[s] = (s < S) ? ml[((int64_t)s * Hq + hh) * 2] : kNegInf;
+      lv[s] = (s < S) ? ml[((int64_t)s * Hq + hh) * 2 + 1] : 0.0f;
+      if (lv[s] > 0.0f) M = fmaxf(M, mv[s]);
+    }
+    float Z = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s) {
+      const float wgt = (lv[s] > 0.0f) ? lv[s] * __expf(mv[s] - M) : 0.0f;
+      s_w[s][tid] = wgt;
+      Z += wgt;
+    }
+    const float inv = (Z > 0.0f) ? 1.0f / Z : 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s) s_w[s][tid] *= inv;
+    if (lse && ct == 0) lse[(int64_t)r * Hq + hh] = (Z > 0.0f) ? M + __logf(Z) : kNegInf;
+  }
+  __syncthreads();
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxS; ++s) {
+    if (s < S) {
+      const float wgt = s_w[s][hl];
+      o[0] = fmaf(wgt, pv[s][0].x, o[0]); o[1] = fmaf(wgt, pv[s][0].y, o[1]);
+      o[2] = fmaf(wgt, pv[s][0].z, o[2]); o[3] = fmaf(wgt, pv[s][0].w, o[3]);
+      o[4] = fmaf(wgt, pv[s][1].x, o[4]); o[5] = fmaf(wgt, pv[s][1].y, o[5]);
+      o[6] = fmaf(wgt, pv[s][1].z, o[6]); o[7] = fmaf(wgt, pv[s][1].w, o[7]);
+    }
+  }
+  o[0] *= sc0.x; o[1] *= sc0.y; o[2] *= sc0.z; o[3] *= sc0.w;
+  o[4] *= sc1.x; o[5] *= sc1.y; o[6] *= sc1.z; o[7] *= sc1.w;
+  const int64_t oi = ((int64_t)r * Hq + h) * D + c;
+  if (out_bf16) {
+    uint32_t w4[4];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) w4[k2] = pack2(bf16_rne(o[2 * k2]), bf16_rne(o[2 * k2 + 1]));
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + oi) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  } else {
+    float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi);
+    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
   }
 }
 
@@ -362,29 +487,43 @@ __global__ __launch_bounds__(256) void k_attend_f32(int T, int Hq, int D, int K,
   if (lse && tid == 0) lse[(int64_t)r * Hq + h] = (z > 0.0f) ? m + logf(z) : kNegInf;
 }
 
-int attend_entries_per_split() { return kAttEntries; }
+int attend_splits(int K) { return (K + kAttSplit - 1) / kAttSplit; }
+
+size_t attend_ws_floats(int R, int Hq, int D, int K) {
+  const int S = attend_splits(K);
+  if (S <= 1) return 0;
+  return (size_t)R * S * Hq * D + (size_t)R * S * Hq * 2;
+}
+
+template <int D, bool FC>
+static void launch_mfma(const AttendArgs& a, int S, hipStream_t st) {
+  dim3 g(S, a.Hq / kAttHeads, a.B * a.T);
+  float* part_ml = a.part ? a.part + (size_t)a.B * a.T * S * a.Hq * D : nullptr;
+  hipLaunchKernelGGL((k_attend_part<D, FC>), g, dim3(kAttThreads), 0, st, a.T, a.Hq, a.K, S, (const uint16_t*)a.q,
+                     a.codes, a.scales, a.n_max, a.idx, a.ctl, a.hist2, a.candbuf, a.cnt, a.nreg, a.idx_out,
+                     a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml);
+  if (S > 1)
+    hipLaunchKernelGGL(k_attend_combine<D>, dim3(a.Hq / kAttHeads * (D / 128), a.B * a.T), dim3(256), 0, st, a.T,
+                       a.Hq, S, a.scales, (const float*)a.part, (const float*)part_ml, a.out, (int)a.out_bf16, a.lse);
+}
 
 int launch_attend(const AttendArgs& a, hipStream_t st) {
   const int R = a.B * a.T;
   if (!a.q_bf16) {
+    if (a.candbuf) return -1;  // the fp32 path takes given indices
     hipLaunchKernelGGL(k_attend_f32, dim3(a.Hq, R), dim3(256), 0, st, a.T, a.Hq, a.D, a.K, (const float*)a.q,
                        a.codes, a.scales, a.n_max, a.idx, a.softmax_scale, (float*)a.out, a.lse);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  if (a.splits > 1 && launch_fill_u32(a.counters, (int64_t)R * (a.Hq / kAttHeads), 0u, st)) return -1;
-  dim3 g(a.splits, a.Hq / kAttHeads, R);
-#define CSA2_ATT(DD)                                                                                               \
-  hipLaunchKernelGGL(k_attend_mfma<DD>, g, dim3(256), 0, st, a.T, a.Hq, a.K, a.splits, (const uint16_t*)a.q,     \
-                     a.codes, a.scales, a.n_max, a.idx, a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part_o, \
-                     a.part_ml, a.counters)
+  const int S = attend_splits(a.K);
+  if (S > 1 && !a.part) return -1;
+  const bool fc = a.candbuf != nullptr;
   switch (a.D) {
-    case 128: CSA2_ATT(128); break;
-    case 256: CSA2_ATT(256); break;
-    case 384: CSA2_ATT(384); break;
-    case 512: CSA2_ATT(512); break;
+    case 128: fc ? launch_mfma<128, true>(a, S, st) : launch_mfma<128, false>(a, S, st); break;
+    case 256: fc ? launch_mfma<256, true>(a, S, st) : launch_mfma<256, false>(a, S, st); break;
+    case 512: fc ? launch_mfma<512, true>(a, S, st) : launch_mfma<512, false>(a, S, st); break;
     default: return -1;
   }
-#undef CSA2_ATT
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -101,15 +101,79 @@ constexpr int kHistBins = 1 << kHistBits;
 __device__ __forceinline__ uint32_t hist_bin(uint32_t key) { return key >> (32 - kHistBits); }
 
 // ---------------------------------------------------------------------------- reductions
+// Cross-lane reductions with DPP (a few cycles each) instead of LDS permutes (~100+
+// cycles each, and chained).  A DPP row is 16 lanes; after the quad swaps (xor 1, xor 2),
+// the half-row mirror and the row mirror every lane of the row holds the row's total,
+// combined in the same order on every lane.  Whole-wave results combine the four row
+// totals read back as scalars.  Call from wave-uniform control flow only.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_mov<kDppMirror>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<kDppXor1>(v);
+  v += dpp_mov<kDppXor2>(v);
+  v += dpp_mov<kDppHalfMirror>(v);
+  return v + dpp_mov<kDppMirror>(v);
+}
+// inclusive suffix sum within each 16-lane row (lane i: lanes i..15 of its row), by
+// Hillis-Steele steps with DPP row shifts toward lower lanes (lanes past the row end add 0)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_shift_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t row16_suffix(uint32_t x) {
+  x += dpp_shift_u<0x101>(x);  // row_shl:1
+  x += dpp_shift_u<0x102>(x);  // row_shl:2
+  x += dpp_shift_u<0x104>(x);  // row_shl:4
+  x += dpp_shift_u<0x108>(x);  // row_shl:8
+  return x;
+}
+// inclusive suffix sum over the 64 lanes of the wave
+__device__ __forceinline__ uint32_t wave_suffix(uint32_t x) {
+  x = row16_suffix(x);
+  const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t t3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  const int row = (threadIdx.x & 63) >> 4;
+  const uint32_t add = (row == 0) ? t1 + t2 + t3 : (row == 1) ? t2 + t3 : (row == 2) ? t3 : 0u;
+  return x + add;
+}
+// Reserve consecutive slots of an LDS counter for the lanes whose pred is set: one atomic
+// per wave (lanes keep their order); returns this lane's slot (meaningful where pred).
+// Every lane of the wave must call it.
+__device__ __forceinline__ uint32_t wave_reserve(uint32_t* counter, bool pred) {
+  const uint64_t mask = __ballot(pred);
+  if (mask == 0) return 0;
+  const int lane = threadIdx.x & 63;
+  const int leader = __builtin_ctzll(mask);
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(counter, (uint32_t)__builtin_popcountll(mask));
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+  const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+  return base + below;
+}
+__device__ __forceinline__ float lane_read(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = row16_sum(v);
+  return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
 }
 
 }  // namespace csa2

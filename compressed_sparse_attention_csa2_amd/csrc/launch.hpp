@@ -9,9 +9,10 @@ namespace csa2 {
 
 // per-row state of the distributed Top-K select (zeroed before each use)
 struct RowCtl {
-  uint32_t ncand;  // candidates appended so far
-  uint32_t done;   // blocks of the select kernel finished
-  uint32_t pad[2];
+  uint32_t pad;
+  uint32_t beta;   // first-level bin holding the K-th largest score (written by the filter)
+  uint32_t above;  // visible scores in first-level bins above beta
+  uint32_t keff;   // min(K, visible scores)
 };
 
 int launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
@@ -41,10 +42,16 @@ struct ScoreArgs {
 int launch_score(const ScoreArgs& a, hipStream_t st);
 int score_cols_per_block(int64_t ncols);
 
-// Top-K select from scores whose histogram is in `hist`; ctl zeroed on entry.
+// Top-K: histogram (zeroed on entry) -> filter into candidates (ctl zeroed on entry)
+// -> finalize (here, or fused into the attention kernel).
 int launch_topk_hist(int R, int64_t ncols, const float* scores, const int32_t* cand, uint32_t* hist, hipStream_t st);
-int launch_topk_select(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const uint32_t* hist,
-                       RowCtl* ctl, uint2* candbuf, int32_t* idx_out, float* val_out, hipStream_t st);
+// hist2 [R][kHistBins]: second-level histogram of the threshold bin (zeroed on entry).
+// candbuf [R][regions][kFilterColsPerBlock] and cnt [R][regions], regions = topk_regions.
+int topk_regions(int64_t ncols);
+int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const uint32_t* hist,
+                       uint32_t* hist2, RowCtl* ctl, uint2* candbuf, uint32_t* cnt, hipStream_t st);
+int launch_topk_finalize(int R, int64_t ncols, int K, const RowCtl* ctl, const uint32_t* hist2, const uint2* candbuf,
+                         const uint32_t* cnt, int32_t* idx_out, float* val_out, hipStream_t st);
 
 struct AttendArgs {
   int B, T, Hq, D, K;
@@ -58,13 +65,18 @@ struct AttendArgs {
   void* out;
   bool out_bf16;
   float* lse;
-  int splits;         // MFMA path: number of entry groups
-  float* part_o;      // [R][splits][Hq][D]
-  float* part_ml;     // [R][splits][Hq][2]
-  uint32_t* counters; // [R][Hq/16], zeroed on entry
+  // MFMA path only: take the Top-K from the candidate list (candbuf != nullptr) instead of idx
+  const RowCtl* ctl;
+  const uint32_t* hist2;
+  const uint2* candbuf;   // [R][nreg][kFilterColsPerBlock]
+  const uint32_t* cnt;    // [R][nreg]
+  int nreg;
+  int32_t* idx_out;   // written when taking the Top-K from candidates (nullable)
+  float* part;        // MFMA path with more than one entry split: partial results (attend_ws_floats)
 };
 int launch_attend(const AttendArgs& a, hipStream_t st);
-int attend_entries_per_split();
+int attend_splits(int K);
+size_t attend_ws_floats(int R, int Hq, int D, int K);
 
 int launch_gather_dequant(int B, int T, int K, int D, const uint8_t* codes, const float* scales, int64_t n_max,
                           const int32_t* idx, float* out, hipStream_t st);

@@ -3,40 +3,33 @@
 // the lower position (a strict total order, so the selected set is unique); the result is
 // written in ascending position order, -1 padded.
 //
-// Distributed radix select, no grid-wide barrier:
+// Distributed radix select over three launches, no fence or grid-wide wait inside a
+// kernel (on MI355X an agent-scope release writes back the XCD's whole L2, which made
+// in-kernel hand-offs between blocks cost tens of microseconds):
 //   1. the score kernel (or k_topk_hist) adds every visible score's top 11 key bits to a
-//      per-row histogram;
-//   2. every block of k_topk_select derives from the histogram the bin that holds the
-//      K-th largest score, and appends the (key, position) pairs of its column chunk that
-//      fall in that bin or above to a per-row candidate list (one atomic per block);
-//   3. the last block of a row to finish (atomic counter after a release fence) runs an
-//      exact 8-bit-digit radix select over the candidates on the 64-bit composite
-//      key = (score key << 32) | ~position, then sorts the winners by position.
-// Candidates per row are typically ~2K for K = 512 of 131072; all-equal scores degrade to
-// every visible column (correct, slower).
+//      per-row histogram (LDS histogram per block, then one atomic per non-empty bin);
+//   2. k_topk_filter: every block derives from the complete histogram the bin holding the
+//      K-th largest score and writes the (key, position) pairs of its column chunk in
+//      that bin or above to its own region of the row's candidate list, plus their count
+//      (no cross-block reservation, so no atomic round trip on the critical path); scores
+//      in the threshold bin also feed a second-level histogram of the next 11 key bits;
+//   3. finalize_row (topk_dev.hpp) selects the exact K among the candidates - in
+//      k_topk_finalize, or inside the attention kernel of an indexing layer.
+// Candidates per row are typically ~1K for K = 512 of 131072 N(0,1)-like scores; all-equal
+// scores degrade to every visible column (correct, slower).
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_dev.hpp"
 
 namespace csa2 {
 
 constexpr int kSelThreads = 256;
-constexpr int kSelColsPerBlock = 2048;
+constexpr int kHistColsPerBlock = 2048;
+constexpr int kFinThreads = 1024;
 
 // inclusive suffix sum over the 256 threads of a block: sum of v over threads >= tid
 __device__ __forceinline__ uint32_t block_suffix_sum(uint32_t v, uint32_t* sh4) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_down(x, o);
-    if (lane + o < 64) x += y;
-  }
-  if (lane == 0) sh4[wave] = x;
-  __syncthreads();
-  uint32_t add = 0;
-  for (int w2 = wave + 1; w2 < kSelThreads / 64; ++w2) add += sh4[w2];
-  __syncthreads();
-  return x + add;
+  return block_suffix<kSelThreads, kSelThreads>(v, sh4);
 }
 
 template <bool CAND>
@@ -46,8 +39,8 @@ __global__ __launch_bounds__(256) void k_topk_hist(int64_t ncols, const float* _
   const int r = blockIdx.y;
   for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
   __syncthreads();
-  const int64_t c0 = (int64_t)blockIdx.x * kSelColsPerBlock;
-  for (int64_t c = c0 + threadIdx.x; c < c0 + kSelColsPerBlock && c < ncols; c += 256) {
+  const int64_t c0 = (int64_t)blockIdx.x * kHistColsPerBlock;
+  for (int64_t c = c0 + threadIdx.x; c < c0 + kHistColsPerBlock && c < ncols; c += 256) {
     const float s = scores[(int64_t)r * ncols + c];
     const bool ok = visible(s) && (!CAND || cand[(int64_t)r * ncols + c] >= 0);
     if (ok) atomicAdd(&lhist[hist_bin(order_key(s))], 1u);
@@ -60,19 +53,35 @@ __global__ __launch_bounds__(256) void k_topk_hist(int64_t ncols, const float* _
 }
 
 template <bool CAND>
-__global__ __launch_bounds__(256) void k_topk_select(int64_t ncols, const float* __restrict__ scores,
+__global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float* __restrict__ scores,
                                                      const int32_t* __restrict__ cand, int K,
-                                                     const uint32_t* __restrict__ hist, RowCtl* __restrict__ ctl,
-                                                     uint2* __restrict__ candbuf, int32_t* __restrict__ idx_out,
-                                                     float* __restrict__ val_out) {
-  __shared__ uint2 stage[kSelColsPerBlock];  // candidates of this block; reused by the final sort
+                                                     const uint32_t* __restrict__ hist, uint32_t* __restrict__ hist2,
+                                                     RowCtl* __restrict__ ctl, uint2* __restrict__ candbuf,
+                                                     uint32_t* __restrict__ cnt) {
+  __shared__ uint2 stage[kFilterColsPerBlock];
+  __shared__ uint32_t lhist2[kHistBins];
   __shared__ uint32_t sh4[4];
   __shared__ uint32_t s_misc[8];
-  __shared__ uint32_t h256[256];
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
 
-  // ---- 1. threshold bin from the row histogram (thread t owns bins 8t .. 8t+7)
+  // the scores of this block's columns (all loads first, branch-free, clamped)
+  const int64_t c0 = (int64_t)blockIdx.x * kFilterColsPerBlock;
+  const float* srow = scores + (int64_t)r * ncols;
+  const int32_t* prow = CAND ? cand + (int64_t)r * ncols : nullptr;
+  constexpr int kPer = kFilterColsPerBlock / kSelThreads;  // 16 columns per thread
+  float sv[kPer];
+  int32_t pv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t c = c0 + tid + (int64_t)i * kSelThreads;
+    const int64_t cc = c < ncols ? c : ncols - 1;
+    sv[i] = srow[cc];
+    pv[i] = CAND ? prow[cc] : (int32_t)cc;
+    if (c >= ncols) sv[i] = kNegInf;
+  }
+
+  // threshold bin (thread t owns bins 8t .. 8t+7)
   const uint32_t* hrow = hist + (int64_t)r * kHistBins;
   uint32_t hb[8];
   uint32_t local = 0;
@@ -81,132 +90,89 @@ __global__ __launch_bounds__(256) void k_topk_select(int64_t ncols, const float*
     hb[i] = hrow[tid * 8 + i];
     local += hb[i];
   }
+  for (int i = tid; i < kHistBins; i += kSelThreads) lhist2[i] = 0;
   const uint32_t suf = block_suffix_sum(local, sh4);  // visible scores in bins >= 8*tid
-  if (tid == 0) s_misc[0] = suf;                      // total visible
+  if (tid == 0) {
+    s_misc[0] = suf;
+    s_misc[1] = kHistBins;
+    s_misc[2] = 0;
+    s_misc[4] = 0;
+  }
   __syncthreads();
   const uint32_t total = s_misc[0];
   const uint32_t keff = total < (uint32_t)K ? total : (uint32_t)K;
-  if (tid == 0) s_misc[1] = kHistBins;  // no candidates unless set below
-  __syncthreads();
   if (keff > 0 && suf >= keff && suf - local < keff) {
-    // the K-th largest lies in one of this thread's bins; walk them from the top
     uint32_t acc = suf - local;
     for (int i = 7; i >= 0; --i) {
-      acc += hb[i];
-      if (acc >= keff) {
+      if (acc + hb[i] >= keff) {
         s_misc[1] = tid * 8 + i;
+        s_misc[4] = acc;  // visible scores in bins above beta
         break;
       }
+      acc += hb[i];
     }
   }
-  if (tid == 0) s_misc[2] = 0;
   __syncthreads();
   const uint32_t beta = s_misc[1];
+  const int nreg = (int)gridDim.x;
+  if (blockIdx.x == 0 && tid == 0) {
+    ctl[r].beta = beta;
+    ctl[r].above = s_misc[4];
+    ctl[r].keff = keff;
+  }
+  if (beta >= (uint32_t)kHistBins) {  // nothing visible in this row (uniform per block)
+    if (tid == 0) cnt[(int64_t)r * nreg + blockIdx.x] = 0;
+    return;
+  }
 
-  // ---- 2. append this block's candidates (bin >= beta)
-  const int64_t c0 = (int64_t)blockIdx.x * kSelColsPerBlock;
-  if (beta < (uint32_t)kHistBins) {
-    for (int64_t c = c0 + tid; c < c0 + kSelColsPerBlock && c < ncols; c += kSelThreads) {
-      const float s = scores[(int64_t)r * ncols + c];
-      const int32_t pos = CAND ? cand[(int64_t)r * ncols + c] : (int32_t)c;
-      if (visible(s) && pos >= 0) {
-        const uint32_t key = order_key(s);
-        if (hist_bin(key) >= beta) {
-          const uint32_t slot = atomicAdd(&s_misc[2], 1u);
-          stage[slot] = make_uint2(key, (uint32_t)pos);
-        }
-      }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const bool vis = visible(sv[i]) && pv[i] >= 0;
+    const uint32_t key = order_key(sv[i]);
+    const uint32_t b1 = hist_bin(key);
+    const bool take = vis && b1 >= beta;
+    const uint32_t slot = wave_reserve(&s_misc[2], take);
+    if (take) {
+      stage[slot] = make_uint2(key, (uint32_t)pv[i]);
+      if (b1 == beta) atomicAdd(&lhist2[hist2_bin(key)], 1u);
     }
   }
   __syncthreads();
+  // this block's candidates go to its own region: no cross-block reservation
   const uint32_t nloc = s_misc[2];
-  if (tid == 0) s_misc[3] = nloc ? atomicAdd(&ctl[r].ncand, nloc) : 0u;
-  __syncthreads();
-  uint2* crow = candbuf + (int64_t)r * ncols;
-  for (uint32_t i = tid; i < nloc; i += kSelThreads) crow[s_misc[3] + i] = stage[i];
-
-  // ---- 3. the last block of the row finishes the selection
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_misc[4] = (atomicAdd(&ctl[r].done, 1u) == gridDim.x - 1) ? 1u : 0u;
-  __syncthreads();
-  if (!s_misc[4]) return;
-  __threadfence();
-  const uint32_t M = __hip_atomic_load(&ctl[r].ncand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-  // radix select of the keff-th largest composite over 8-bit digits, most significant first
-  uint64_t prefix = 0, mask = 0;
-  uint32_t need = keff;
-  for (int shift = 56; shift >= 0 && need > 0; shift -= 8) {
-    h256[tid] = 0;
-    __syncthreads();
-    for (uint32_t i = tid; i < M; i += kSelThreads) {
-      const uint2 c = crow[i];
-      const uint64_t comp = ((uint64_t)c.x << 32) | (uint32_t)(~c.y);
-      if ((comp & mask) == prefix) atomicAdd(&h256[(comp >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    const uint32_t mine = h256[tid];
-    const uint32_t sfx = block_suffix_sum(mine, sh4);
-    if (sfx >= need && sfx - mine < need) {
-      s_misc[5] = tid;
-      s_misc[6] = sfx - mine;  // strictly above this digit
-      s_misc[7] = mine;
-    }
-    __syncthreads();
-    const uint32_t v = s_misc[5];
-    need -= s_misc[6];
-    prefix |= (uint64_t)v << shift;
-    mask |= (uint64_t)255u << shift;
-    const bool done = (s_misc[7] == need);
-    __syncthreads();
-    if (done) break;
+  if (tid == 0) cnt[(int64_t)r * nreg + blockIdx.x] = nloc;
+  if (nloc == 0) return;
+  for (int i = tid; i < kHistBins; i += kSelThreads) {
+    const uint32_t v = lhist2[i];
+    if (v) atomicAdd(&hist2[(int64_t)r * kHistBins + i], v);
   }
+  uint2* creg = candbuf + ((int64_t)r * nreg + blockIdx.x) * kFilterColsPerBlock;
+  for (uint32_t i = tid; i < nloc; i += kSelThreads) creg[i] = stage[i];
+}
 
-  // winners: (comp & mask) >= prefix
-  if (tid == 0) s_misc[2] = 0;
-  __syncthreads();
-  if (keff > 0) {
-    for (uint32_t i = tid; i < M; i += kSelThreads) {
-      const uint2 c = crow[i];
-      const uint64_t comp = ((uint64_t)c.x << 32) | (uint32_t)(~c.y);
-      if ((comp & mask) >= prefix) {
-        const uint32_t slot = atomicAdd(&s_misc[2], 1u);
-        if (slot < (uint32_t)K) stage[slot] = make_uint2(c.y, c.x);  // (position, key)
-      }
-    }
-  }
-  __syncthreads();
-  // bitonic sort of the winners by position (padding sorts last)
-  int P = 1;
-  while (P < (int)keff) P <<= 1;
-  for (int i = (int)keff + tid; i < P; i += kSelThreads) stage[i] = make_uint2(0x7FFFFFFFu, 0u);
-  __syncthreads();
-  for (int kk = 2; kk <= P; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += kSelThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint2 x = stage[i], y = stage[ixj];
-          const bool up = (i & kk) == 0;
-          if (((int)x.x > (int)y.x) == up) {
-            stage[i] = y;
-            stage[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = tid; i < K; i += kSelThreads) {
-    const bool have = i < (int)keff;
-    idx_out[(int64_t)r * K + i] = have ? (int32_t)stage[i].x : -1;
-    if (val_out) val_out[(int64_t)r * K + i] = have ? key_to_float(stage[i].y) : kNegInf;
+__global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, const RowCtl* __restrict__ ctl,
+                                                               const uint32_t* __restrict__ hist2,
+                                                               const uint2* __restrict__ candbuf,
+                                                               const uint32_t* __restrict__ cnt,
+                                                               int32_t* __restrict__ idx_out,
+                                                               float* __restrict__ val_out) {
+  __shared__ FinalizeSmem sm;
+  __shared__ int32_t s_pos[CSA2_MAX_K_DEV];
+  __shared__ uint32_t s_key[CSA2_MAX_K_DEV];
+  const int r = blockIdx.x;
+  const RowCtl c = ctl[r];
+  const int keff = finalize_row<kFinThreads>(candbuf + (int64_t)r * nreg * kFilterColsPerBlock, cnt + (int64_t)r * nreg,
+                                             nreg, hist2 + (int64_t)r * kHistBins, c.beta, c.above, c.keff, sm,
+                                             s_pos, s_key);
+  for (int i = threadIdx.x; i < K; i += kFinThreads) {
+    const bool have = i < keff;
+    idx_out[(int64_t)r * K + i] = have ? s_pos[i] : -1;
+    if (val_out) val_out[(int64_t)r * K + i] = have ? key_to_float(s_key[i]) : kNegInf;
   }
 }
 
 int launch_topk_hist(int R, int64_t ncols, const float* scores, const int32_t* cand, uint32_t* hist, hipStream_t st) {
-  dim3 g((unsigned)((ncols + kSelColsPerBlock - 1) / kSelColsPerBlock), R);
+  dim3 g((unsigned)((ncols + kHistColsPerBlock - 1) / kHistColsPerBlock), R);
   if (cand)
     hipLaunchKernelGGL(k_topk_hist<true>, g, dim3(256), 0, st, ncols, scores, cand, hist);
   else
@@ -214,15 +180,24 @@ int launch_topk_hist(int R, int64_t ncols, const float* scores, const int32_t* c
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_topk_select(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const uint32_t* hist,
-                       RowCtl* ctl, uint2* candbuf, int32_t* idx_out, float* val_out, hipStream_t st) {
-  dim3 g((unsigned)((ncols + kSelColsPerBlock - 1) / kSelColsPerBlock), R);
+int topk_regions(int64_t ncols) { return (int)((ncols + kFilterColsPerBlock - 1) / kFilterColsPerBlock); }
+
+int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const uint32_t* hist,
+                       uint32_t* hist2, RowCtl* ctl, uint2* candbuf, uint32_t* cnt, hipStream_t st) {
+  dim3 g((unsigned)topk_regions(ncols), R);
   if (cand)
-    hipLaunchKernelGGL(k_topk_select<true>, g, dim3(kSelThreads), 0, st, ncols, scores, cand, K, hist, ctl, candbuf,
-                       idx_out, val_out);
+    hipLaunchKernelGGL(k_topk_filter<true>, g, dim3(kSelThreads), 0, st, ncols, scores, cand, K, hist, hist2, ctl,
+                       candbuf, cnt);
   else
-    hipLaunchKernelGGL(k_topk_select<false>, g, dim3(kSelThreads), 0, st, ncols, scores, cand, K, hist, ctl,
-                       candbuf, idx_out, val_out);
+    hipLaunchKernelGGL(k_topk_filter<false>, g, dim3(kSelThreads), 0, st, ncols, scores, cand, K, hist, hist2, ctl,
+                       candbuf, cnt);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_topk_finalize(int R, int64_t ncols, int K, const RowCtl* ctl, const uint32_t* hist2, const uint2* candbuf,
+                         const uint32_t* cnt, int32_t* idx_out, float* val_out, hipStream_t st) {
+  hipLaunchKernelGGL(k_topk_finalize, dim3(R), dim3(kFinThreads), 0, st, topk_regions(ncols), K, ctl, hist2, candbuf,
+                     cnt, idx_out, val_out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -164,16 +164,17 @@ size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int K);
  *   No selected entry: out = 0, lse = -inf.
  *   q: [B][T][Hq][D] of q_dtype; kv_codes [B][n_max][D/2]; kv_scales [B][D];
  *   idx [B][T][K]; out [B][T][Hq][D] of out_dtype; lse [B][T][Hq] fp32 (nullable).
- *   q_dtype CSA2_F32: fp32 arithmetic throughout.  q_dtype CSA2_BF16: bf16/fp16 MFMA with
- *   fp32 accumulation (needs Hq % 16 == 0 and D a multiple of 128).  num_splits: entries
- *   are split into that many groups whose partial results are merged by log-sum-exp
- *   (0 = automatic).  ws: csa2_sparse_attend_workspace_size() bytes.
+ *   q_dtype CSA2_F32: fp32 arithmetic throughout (out_dtype must be CSA2_F32).
+ *   q_dtype CSA2_BF16: fp16 MFMA with fp32 accumulation, the per-channel scale folded into
+ *   the query (exact power-of-two prescale) and into the output; needs Hq % 16 == 0 and
+ *   D in {128, 256, 512}.  Entries are processed in groups of 128 whose partial softmax
+ *   results are merged by log-sum-exp.  ws: csa2_sparse_attend_workspace_size() bytes
+ *   (0 when K <= 128 or q is fp32; then ws may be NULL).
  */
 int csa2_sparse_attend(int B, int T, int Hq, int D, const void* q, int q_dtype, const uint8_t* kv_codes,
                        const float* kv_scales, int64_t n_max, const int32_t* idx, int K, float softmax_scale,
-                       void* out, int out_dtype, float* lse, int num_splits, void* ws, size_t ws_bytes,
-                       void* stream);
-size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype, int num_splits);
+                       void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
+size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype);
 
 /*
  * Layer group: Full / Reindex / Reuse layers over one shared cache, run strictly in order.

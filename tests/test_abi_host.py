@@ -62,16 +62,15 @@ def test_errors_before_any_launch():
                               None) == -1
     assert L.csa2_index_score(7, 1, 1, 32, 64, _p(), 1, _p(), _p(), _p(), 100, _p(), None, None, 0, _p(), None, 0,
                               None) == -3
-    # attention: bf16 path needs Hq % 16 == 0 and D % 128 == 0; fp32 query needs fp32 output
-    assert L.csa2_sparse_attend(1, 1, 8, 512, _p(), 1, _p(), _p(), 10, _p(), 8, 1.0, _p(), 1, None, 0, None, 0,
+    # attention: bf16 path needs Hq % 16 == 0 and D in {128, 256, 512}; fp32 query needs fp32 output
+    assert L.csa2_sparse_attend(1, 1, 8, 512, _p(), 1, _p(), _p(), 10, _p(), 8, 1.0, _p(), 1, None, None, 0,
                                 None) == -6
-    assert L.csa2_sparse_attend(1, 1, 8, 128, _p(), 0, _p(), _p(), 10, _p(), 8, 1.0, _p(), 1, None, 0, None, 0,
+    assert L.csa2_sparse_attend(1, 1, 16, 384, _p(), 1, _p(), _p(), 10, _p(), 8, 1.0, _p(), 1, None, None, 0,
+                                None) == -6
+    assert L.csa2_sparse_attend(1, 1, 8, 128, _p(), 0, _p(), _p(), 10, _p(), 8, 1.0, _p(), 1, None, None, 0,
                                 None) == -3
-    assert L.csa2_sparse_attend(1, 1, 16, 512, _p(), 1, _p(), _p(), 10, _p(), 4096, 1.0, _p(), 1, None, 0, None, 0,
+    assert L.csa2_sparse_attend(1, 1, 16, 512, _p(), 1, _p(), _p(), 10, _p(), 4096, 1.0, _p(), 1, None, None, 0,
                                 None) == -2
-    # too few splits for the entries per block
-    assert L.csa2_sparse_attend(1, 1, 16, 512, _p(), 1, _p(), _p(), 10, _p(), 512, 1.0, _p(), 1, None, 2, _p(),
-                                1 << 30, None) == -2
 
 
 @pytest.mark.parametrize("modes,code", [

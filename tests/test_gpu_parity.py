@@ -197,9 +197,10 @@ def test_sparse_attend_fp32_tiny():
     assert np.allclose(lse.cpu().numpy(), ref_l, rtol=1e-5, atol=1e-5)
 
 
-@pytest.mark.parametrize("K,splits", [(512, 0), (512, 8), (100, 1), (1024, 0), (37, 0)])
-def test_sparse_attend_bf16(K, splits):
-    wl = workloads.workload("full64k", B=2, K=K)
+@pytest.mark.parametrize("K,D", [(512, 512), (100, 512), (1024, 512), (37, 512), (2048, 512), (600, 256),
+                                 (512, 128)])
+def test_sparse_attend_bf16(K, D):
+    wl = workloads.workload("full64k", B=2, K=K, D=D)
     c = build_cache(wl, n_rows=3000)
     q = wl.attn_query()
     rng = np.random.default_rng(K)
@@ -208,11 +209,10 @@ def test_sparse_attend_bf16(K, splits):
     ref_o, ref_l = oracle.sparse_attend(q, c["codes_ref"], c["scales_ref"], idx, wl.softmax_scale)
     qd = to_dev(q, torch.bfloat16)
     out, lse = csa2.sparse_attend(qd, c["codes"], c["scales"], to_dev(idx), wl.softmax_scale,
-                                  out_dtype=torch.float32, num_splits=splits)
+                                  out_dtype=torch.float32)
     assert max_abs_rel(out.cpu().numpy(), ref_o) <= 2e-3
     assert np.allclose(lse.cpu().numpy(), ref_l, rtol=2e-3, atol=2e-3)
-    ob, _ = csa2.sparse_attend(qd, c["codes"], c["scales"], to_dev(idx), wl.softmax_scale, out_dtype=torch.bfloat16,
-                               num_splits=splits)
+    ob, _ = csa2.sparse_attend(qd, c["codes"], c["scales"], to_dev(idx), wl.softmax_scale, out_dtype=torch.bfloat16)
     ob = ob.float().cpu().numpy()
     half_ulp = np.abs(ref_o) * 2.0 ** -8
     assert np.all(np.abs(ob - ref_o) <= 2e-3 * np.abs(ref_o).max() + half_ulp)
