@@ -31,6 +31,9 @@ import compressed_sparse_attention_csa2_amd as csa2  # noqa: E402
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+SCORE_SOURCES = ("compressed_sparse_attention_csa2_amd/csrc/score.hip", "compressed_sparse_attention_csa2_amd/csrc/common.hpp",
+                 "compressed_sparse_attention_csa2_amd/csrc/launch.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_fp8_group128k_hbm_traffic.md")
 METRIC = "CSA2 decode queries/s + achieved HBM GB/s (% of peak) at 128K context"
 
 
@@ -83,26 +86,81 @@ def algorithmic_bytes(wl):
 
 def time_score_kernel(wl, caches, layers, reps):
     """Average duration of the indexer-score kernel (one launch per csa2_index_score call),
-    with HIP events on the launching stream; launches alternate over the rotated caches
-    and the indexing layers' queries exactly as the timed steps do."""
+    from HIP events on the launching stream around `reps` back-to-back launches (so the
+    per-event overhead is not counted); launches alternate over the rotated caches and the
+    indexing layers' queries exactly as the timed steps do.  Also returns the median of
+    single launches each bracketed by its own events."""
     idx_layers = [L for L in layers if L["mode"] != "reuse"]
     out = torch.empty((wl.B, 1, wl.N), dtype=torch.float32, device="cuda")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     seq = []
     for r in range(reps):
         c = caches[(r // len(idx_layers)) % len(caches)]
         L = idx_layers[r % len(idx_layers)]
         seq.append((c, L))
+
+    def launch(c, L):
+        csa2.index_score(csa2.PREC_FP8, L["q_idx"], L["w"], c["k8"], c["ks"], c["n_keys"], scores=out)
+
     for c, L in seq[: min(4, reps)]:  # warm-up
-        csa2.index_score(csa2.PREC_FP8, L["q_idx"], L["w"], c["k8"], c["ks"], c["n_keys"], scores=out)
+        launch(c, L)
     torch.cuda.synchronize()
-    for (c, L), (e0, e1) in zip(seq, evs):
-        e0.record()
-        csa2.index_score(csa2.PREC_FP8, L["q_idx"], L["w"], c["k8"], c["ks"], c["n_keys"], scores=out)
-        e1.record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for c, L in seq:
+        launch(c, L)
+    e1.record()
     torch.cuda.synchronize()
-    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    return float(np.mean(ms)), float(np.median(ms))
+    mean_ms = e0.elapsed_time(e1) / reps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for (c, L), (a, b) in zip(seq, evs):
+        a.record()
+        launch(c, L)
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return float(mean_ms), float(np.median(ms))
+
+
+def score_sources_sha256():
+    """Digest of the sources the score kernel is built from (the HBM-traffic figures below
+    hold only for the kernel they were counted on)."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in SCORE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counted_traffic():
+    """HBM bytes per score launch from the committed rocprofv3 --pmc summary (FETCH_SIZE +
+    WRITE_SIZE, each scaled by the same counter's reading on a copy of known size), or
+    None when the summary is absent or the kernel's sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_sources_sha256") != score_sources_sha256():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(nbytes, reps=5):
+    """A plain device copy of known size (read nbytes, write nbytes): the calibration
+    kernel for the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def cpu_baseline(wl, seqs):
@@ -135,8 +193,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated between steps")
     ap.add_argument("--score-reps", type=int, default=60)
-    ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--cpu-seqs", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the CSA2 decode path runs per sequence with no exchange between GPUs, "
@@ -146,6 +206,9 @@ def main():
     if csa2.device_check() != 0:
         print("not a gfx950 device", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     wl = workloads.WORKLOADS["group128k"]
     log("building cache (%d copies) ..." % args.copies)
     caches = build_device_cache(wl, args.copies)
@@ -188,10 +251,10 @@ def main():
         "step_algorithmic_bytes": alg, "step_achieved_GBps": round(step_gbs, 1),
         "step_pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counted_traffic(),
                      "kernel": "k_score_fp8 (indexer score, one launch per indexing layer)",
                      "kernel_ms_mean": round(mean_ms, 5), "kernel_ms_median": round(med_ms, 5),
-                     "bytes_per_launch": score_bytes},
+                     "bytes_per_launch": score_bytes, "traffic_unit": "bytes per launch"},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -249,7 +249,8 @@ int csa2_topk(int B, int T, int64_t ncols, const float* scores, const int32_t* c
   if (launch_topk_hist((int)R, ncols, scores, cand, t.hist, st)) return CSA2_ERR_DEVICE;
   if (launch_topk_filter((int)R, ncols, scores, cand, K, t.hist, t.hist2, t.ctl, t.cand, t.cnt, st))
     return CSA2_ERR_DEVICE;
-  return dev_status(launch_topk_finalize((int)R, ncols, K, t.ctl, t.hist2, t.cand, t.cnt, idx_out, val_out, st));
+  return dev_status(
+      launch_topk_finalize((int)R, ncols, K, cand == nullptr, t.ctl, t.hist2, t.cand, t.cnt, idx_out, val_out, st));
 }
 
 size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int) {
@@ -281,7 +282,8 @@ int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_
   if (launch_score(a, st)) return CSA2_ERR_DEVICE;
   if (launch_topk_filter((int)R, ncols, scores, cand, K, t.hist, t.hist2, t.ctl, t.cand, t.cnt, st))
     return CSA2_ERR_DEVICE;
-  return dev_status(launch_topk_finalize((int)R, ncols, K, t.ctl, t.hist2, t.cand, t.cnt, idx_out, val_out, st));
+  return dev_status(
+      launch_topk_finalize((int)R, ncols, K, cand == nullptr, t.ctl, t.hist2, t.cand, t.cnt, idx_out, val_out, st));
 }
 
 size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype) {
@@ -401,7 +403,7 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
         a.ctl = t.ctl; a.hist2 = t.hist2; a.candbuf = cw.cand; a.cnt = cw.cnt; a.nreg = topk_regions(c->n_max);
         a.idx_out = L.idx;
       } else {
-        if (launch_topk_finalize((int)R, c->n_max, c->K, t.ctl, t.hist2, cw.cand, cw.cnt, L.idx, nullptr, st))
+        if (launch_topk_finalize((int)R, c->n_max, c->K, true, t.ctl, t.hist2, cw.cand, cw.cnt, L.idx, nullptr, st))
           return CSA2_ERR_DEVICE;
         a.idx = L.idx;
       }
@@ -459,7 +461,7 @@ int csa2_hier_select(int B, int H, int dk, const void* q, int q_dtype, const flo
   int32_t* bout = block_out ? block_out : blocks;
   if (launch_topk_filter(B, nb, cscores, nullptr, block_topk, t1.hist, t1.hist2, t1.ctl, t1.cand, t1.cnt, st))
     return CSA2_ERR_DEVICE;
-  if (launch_topk_finalize(B, nb, block_topk, t1.ctl, t1.hist2, t1.cand, t1.cnt, bout, nullptr, st))
+  if (launch_topk_finalize(B, nb, block_topk, true, t1.ctl, t1.hist2, t1.cand, t1.cnt, bout, nullptr, st))
     return CSA2_ERR_DEVICE;
   if (launch_expand_blocks(B, block_topk, block, bout, n_keys, cand, st)) return CSA2_ERR_DEVICE;
   ScoreArgs a2 = score_args(CSA2_PREC_FP8, B, 1, H, dk, q, q_dtype, w, k8, k_scale, n_max, n_keys, nullptr, cand, C,
@@ -467,7 +469,7 @@ int csa2_hier_select(int B, int H, int dk, const void* q, int q_dtype, const flo
   if (launch_score(a2, st)) return CSA2_ERR_DEVICE;
   if (launch_topk_filter(B, C, fscores, cand, K, t2.hist, t2.hist2, t2.ctl, t2.cand, t2.cnt, st))
     return CSA2_ERR_DEVICE;
-  return dev_status(launch_topk_finalize(B, C, K, t2.ctl, t2.hist2, t2.cand, t2.cnt, idx_out, nullptr, st));
+  return dev_status(launch_topk_finalize(B, C, K, false, t2.ctl, t2.hist2, t2.cand, t2.cnt, idx_out, nullptr, st));
 }
 
 }  // extern "C"

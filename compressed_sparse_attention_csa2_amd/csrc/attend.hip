@@ -5,19 +5,18 @@
 // dequantised entry is both key and value.
 //
 // MFMA path (bf16 queries, Hq % 16 == 0, D in {128, 256, 512}).  One block = one query
-// row x 16 heads (the MFMA M dimension) over all K selected entries, 16 waves, processed
-// in chunks of 512 entries with an online softmax.  The per-channel scale s_c factors
-// out of both contractions: logits use q'' = q * s * 2^k in fp16 (2^k an exact prescale
-// keeping |q''| below 2^15, undone in the softmax scale; ~2^-12 relative error) against
-// the exact E2M1 values e in fp16; the output is s_c * sum_j p_j e_jc / l with p in fp16.
-// FP4 rows go straight from HBM into MFMA operand layout (no LDS staging): for QK lane
+// row x 16 heads (the MFMA M dimension) x one split of up to 128 selected entries, 8
+// waves; with more than one split a second kernel merges the splits' partial softmaxes
+// by log-sum-exp (a kernel boundary: merging inside the kernel would need a device-scope
+// release fence, which costs more here).  The per-channel scale s_c factors out of both
+// contractions: logits use q'' = q * s * 2^k in fp16 (2^k an exact prescale keeping
+// |q''| below 2^15, undone in the softmax scale; ~2^-12 relative error) against the exact
+// E2M1 values e in fp16; the output is s_c * sum_j p_j e_jc / l with p in fp16.  FP4
+// rows go straight from HBM into MFMA operand layout (no LDS staging): for QK lane
 // (entry n, group g) reads 16 contiguous bytes per 128 channels; for PV lane (channel
-// block n, entry group g) reads one 32-bit word (8 channels) of each of 8 entries, so the
-// 8 MFMAs of a k-step cover 8 interleaved channel sets.  PV is split over waves by
-// (channel tile, entry group) and the entry groups are summed in LDS in a fixed order
-// (deterministic).  There is no split over blocks: merging partial softmaxes across blocks
-// needs either another launch or an in-kernel release fence, both slower here than the
-// extra per-block work.
+// block n, entry group g) reads one 32-bit word (8 channels) of each of 8 entries.  PV is
+// split over waves by (channel tile, entry group) and the entry groups are summed in LDS
+// in a fixed order (deterministic).
 //
 // fp32 path (fp32 queries): plain VALU, one block per (row, head), fp32 throughout.
 #include "common.hpp"
@@ -92,13 +91,24 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   const int n16 = lane & 15, g = lane >> 4;
   const int e0 = split * kAttSplit;            // first entry of this split
 
-  // ---- phase 0: scales, the split's entries, q'' = q * s * 2^k in fp16
+  // ---- phase 0: scales, the split's entries, q'' = q * s * 2^k in fp16.  The query
+  //      loads are issued first so that their latency overlaps the entry selection.
+  const uint16_t* qb = q + ((int64_t)r * Hq + hg * kAttHeads) * D;
+  constexpr int kQItems = kAttHeads * D / 8;       // 8 channels per item
+  constexpr int kQPer = (kQItems + kAttThreads - 1) / kAttThreads;
+  uint4 qraw[kQPer];
+#pragma unroll
+  for (int it = 0; it < kQPer; ++it) {
+    const int i = tid + it * kAttThreads;
+    const int ic = i < kQItems ? i : kQItems - 1;
+    qraw[it] = *reinterpret_cast<const uint4*>(qb + (int64_t)(ic / (D / 8)) * D + (ic % (D / 8)) * 8);
+  }
   for (int i = tid; i < D; i += kAttThreads) s_scale[i] = scales[(int64_t)b * D + i];
   const int32_t* sel;                           // the split's entries (LDS)
   if (FROM_CAND) {
     FinalizeSmem& fs = *reinterpret_cast<FinalizeSmem*>(s_u);
     const RowCtl c = ctl[r];
-    const int keff = finalize_row<kAttThreads>(candbuf + (int64_t)r * nreg * kFilterColsPerBlock,
+    const int keff = finalize_row<kAttThreads, true>(candbuf + (int64_t)r * nreg * kFilterColsPerBlock,
                                                cnt + (int64_t)r * nreg, nreg, hist2 + (int64_t)r * kHistBins, c.beta,
                                                c.above, c.keff, fs, s_idx, nullptr);
     for (int i = keff + tid; i < K; i += kAttThreads) s_idx[i] = -1;
@@ -116,9 +126,6 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   }
   const int ecount = min(kAttSplit, K - e0);
 
-  const uint16_t* qb = q + ((int64_t)r * Hq + hg * kAttHeads) * D;
-  constexpr int kQItems = kAttHeads * D / 8;       // 8 channels per item
-  constexpr int kQPer = (kQItems + kAttThreads - 1) / kAttThreads;
   float qv[kQPer][8];
   float qmax = 0.0f;
   __syncthreads();  // s_scale
@@ -126,9 +133,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   for (int it = 0; it < kQPer; ++it) {
     const int i = tid + it * kAttThreads;
     const int ic = i < kQItems ? i : kQItems - 1;
-    const int h = ic / (D / 8), c = (ic % (D / 8)) * 8;
-    const uint4 raw = *reinterpret_cast<const uint4*>(qb + (int64_t)h * D + c);
-    const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+    const int c = (ic % (D / 8)) * 8;
+    const uint32_t wds[4] = {qraw[it].x, qraw[it].y, qraw[it].z, qraw[it].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       qv[it][e] = bf16_to_f32((uint16_t)(wds[e >> 1] >> (16 * (e & 1)))) * s_scale[c + e];

@@ -150,6 +150,10 @@ __device__ __forceinline__ uint32_t wave_suffix(uint32_t x) {
   const uint32_t add = (row == 0) ? t1 + t2 + t3 : (row == 1) ? t2 + t3 : (row == 2) ? t3 : 0u;
   return x + add;
 }
+// number of lanes below this one whose bit is set in mask
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
 // Reserve consecutive slots of an LDS counter for the lanes whose pred is set: one atomic
 // per wave (lanes keep their order); returns this lane's slot (meaningful where pred).
 // Every lane of the wave must call it.
@@ -161,8 +165,7 @@ __device__ __forceinline__ uint32_t wave_reserve(uint32_t* counter, bool pred) {
   uint32_t base = 0;
   if (lane == leader) base = atomicAdd(counter, (uint32_t)__builtin_popcountll(mask));
   base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
-  const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-  return base + below;
+  return base + lanes_below(mask);
 }
 __device__ __forceinline__ float lane_read(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));

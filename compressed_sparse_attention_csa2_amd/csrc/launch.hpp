@@ -50,8 +50,9 @@ int launch_topk_hist(int R, int64_t ncols, const float* scores, const int32_t* c
 int topk_regions(int64_t ncols);
 int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const uint32_t* hist,
                        uint32_t* hist2, RowCtl* ctl, uint2* candbuf, uint32_t* cnt, hipStream_t st);
-int launch_topk_finalize(int R, int64_t ncols, int K, const RowCtl* ctl, const uint32_t* hist2, const uint2* candbuf,
-                         const uint32_t* cnt, int32_t* idx_out, float* val_out, hipStream_t st);
+// sorted: the candidates were filtered without a candidate map (list in position order)
+int launch_topk_finalize(int R, int64_t ncols, int K, bool sorted, const RowCtl* ctl, const uint32_t* hist2,
+                         const uint2* candbuf, const uint32_t* cnt, int32_t* idx_out, float* val_out, hipStream_t st);
 
 struct AttendArgs {
   int B, T, Hq, D, K;

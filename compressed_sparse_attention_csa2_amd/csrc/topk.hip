@@ -58,18 +58,21 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
                                                      const uint32_t* __restrict__ hist, uint32_t* __restrict__ hist2,
                                                      RowCtl* __restrict__ ctl, uint2* __restrict__ candbuf,
                                                      uint32_t* __restrict__ cnt) {
-  __shared__ uint2 stage[kFilterColsPerBlock];
+  constexpr int kWaves = kSelThreads / 64;
+  constexpr int kPer = kFilterColsPerBlock / kSelThreads;  // 16 columns per thread
   __shared__ uint32_t lhist2[kHistBins];
-  __shared__ uint32_t sh4[4];
+  __shared__ uint32_t sh4[kWaves];
   __shared__ uint32_t s_misc[8];
+  __shared__ uint32_t s_off[kPer * kWaves];  // candidates before (column pass i, wave w)
+  static_assert(kPer * kWaves == 64, "one wave scans the (pass, wave) counts");
   const int r = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // the scores of this block's columns (all loads first, branch-free, clamped)
+  // the scores of this block's columns (all loads first, branch-free, clamped); pass i,
+  // wave w, lane l holds column c0 + 256 i + 64 w + l, so (i, w, l) order is column order
   const int64_t c0 = (int64_t)blockIdx.x * kFilterColsPerBlock;
   const float* srow = scores + (int64_t)r * ncols;
   const int32_t* prow = CAND ? cand + (int64_t)r * ncols : nullptr;
-  constexpr int kPer = kFilterColsPerBlock / kSelThreads;  // 16 columns per thread
   float sv[kPer];
   int32_t pv[kPer];
 #pragma unroll
@@ -95,7 +98,6 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
   if (tid == 0) {
     s_misc[0] = suf;
     s_misc[1] = kHistBins;
-    s_misc[2] = 0;
     s_misc[4] = 0;
   }
   __syncthreads();
@@ -125,31 +127,53 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
     return;
   }
 
+  // candidates: visible, first-level bin >= beta.  Compacted in column order (ballot
+  // counts per (pass, wave), an exclusive scan over them, then each lane's rank in its
+  // ballot), so that without a candidate map a row's list is sorted by position.
+  uint64_t bal[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const bool vis = visible(sv[i]) && pv[i] >= 0;
     const uint32_t key = order_key(sv[i]);
     const uint32_t b1 = hist_bin(key);
     const bool take = vis && b1 >= beta;
-    const uint32_t slot = wave_reserve(&s_misc[2], take);
-    if (take) {
-      stage[slot] = make_uint2(key, (uint32_t)pv[i]);
-      if (b1 == beta) atomicAdd(&lhist2[hist2_bin(key)], 1u);
-    }
+    bal[i] = __ballot(take);
+    if (take && b1 == beta) atomicAdd(&lhist2[hist2_bin(key)], 1u);
+  }
+  if (lane < kPer) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (i == lane) n = (uint32_t)__builtin_popcountll(bal[i]);
+    s_off[lane * kWaves + wave] = n;
   }
   __syncthreads();
-  // this block's candidates go to its own region: no cross-block reservation
+  if (wave == 0) {  // exclusive scan over the kPer * kWaves (= 64) counts in (pass, wave) order
+    const uint32_t v = s_off[lane];
+    const uint32_t sfx = wave_suffix(v);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 0);
+    s_off[lane] = tot - sfx;
+    if (lane == 0) s_misc[2] = tot;
+  }
+  __syncthreads();
   const uint32_t nloc = s_misc[2];
   if (tid == 0) cnt[(int64_t)r * nreg + blockIdx.x] = nloc;
   if (nloc == 0) return;
+  uint2* creg = candbuf + ((int64_t)r * nreg + blockIdx.x) * kFilterColsPerBlock;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if ((bal[i] >> lane) & 1ull) {
+      const uint32_t slot = s_off[i * kWaves + wave] + lanes_below(bal[i]);
+      creg[slot] = make_uint2(order_key(sv[i]), (uint32_t)pv[i]);
+    }
+  }
   for (int i = tid; i < kHistBins; i += kSelThreads) {
     const uint32_t v = lhist2[i];
     if (v) atomicAdd(&hist2[(int64_t)r * kHistBins + i], v);
   }
-  uint2* creg = candbuf + ((int64_t)r * nreg + blockIdx.x) * kFilterColsPerBlock;
-  for (uint32_t i = tid; i < nloc; i += kSelThreads) creg[i] = stage[i];
 }
 
+template <bool SORTED>
 __global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, const RowCtl* __restrict__ ctl,
                                                                const uint32_t* __restrict__ hist2,
                                                                const uint2* __restrict__ candbuf,
@@ -161,9 +185,9 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, 
   __shared__ uint32_t s_key[CSA2_MAX_K_DEV];
   const int r = blockIdx.x;
   const RowCtl c = ctl[r];
-  const int keff = finalize_row<kFinThreads>(candbuf + (int64_t)r * nreg * kFilterColsPerBlock, cnt + (int64_t)r * nreg,
-                                             nreg, hist2 + (int64_t)r * kHistBins, c.beta, c.above, c.keff, sm,
-                                             s_pos, s_key);
+  const int keff = finalize_row<kFinThreads, SORTED>(candbuf + (int64_t)r * nreg * kFilterColsPerBlock,
+                                                     cnt + (int64_t)r * nreg, nreg, hist2 + (int64_t)r * kHistBins,
+                                                     c.beta, c.above, c.keff, sm, s_pos, s_key);
   for (int i = threadIdx.x; i < K; i += kFinThreads) {
     const bool have = i < keff;
     idx_out[(int64_t)r * K + i] = have ? s_pos[i] : -1;
@@ -194,10 +218,14 @@ int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t*
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_topk_finalize(int R, int64_t ncols, int K, const RowCtl* ctl, const uint32_t* hist2, const uint2* candbuf,
-                         const uint32_t* cnt, int32_t* idx_out, float* val_out, hipStream_t st) {
-  hipLaunchKernelGGL(k_topk_finalize, dim3(R), dim3(kFinThreads), 0, st, topk_regions(ncols), K, ctl, hist2, candbuf,
-                     cnt, idx_out, val_out);
+int launch_topk_finalize(int R, int64_t ncols, int K, bool sorted, const RowCtl* ctl, const uint32_t* hist2,
+                         const uint2* candbuf, const uint32_t* cnt, int32_t* idx_out, float* val_out, hipStream_t st) {
+  if (sorted)
+    hipLaunchKernelGGL(k_topk_finalize<true>, dim3(R), dim3(kFinThreads), 0, st, topk_regions(ncols), K, ctl, hist2,
+                       candbuf, cnt, idx_out, val_out);
+  else
+    hipLaunchKernelGGL(k_topk_finalize<false>, dim3(R), dim3(kFinThreads), 0, st, topk_regions(ncols), K, ctl, hist2,
+                       candbuf, cnt, idx_out, val_out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -7,11 +7,14 @@
 // bins > beta and are winners; inside bin beta the filter built a second-level histogram
 // of the next 11 key bits.  The finaliser
 //   1. finds in that histogram the second-level bin beta2 holding the remaining need,
-//   2. keeps every candidate above (beta, beta2) and collects the few tied at (beta, beta2),
-//   3. picks the remaining need among the tied ones by the exact order (score desc,
-//      position asc) - rank counting when few, an MSB-first radix select on the 64-bit
-//      composite (key << 32 | ~position) otherwise (e.g. many equal scores),
-//   4. ranks the winners by position (ascending output).
+//   2. collects the few candidates tied at (beta, beta2),
+//   3. finds among them the threshold of the exact order (score desc, position asc) on
+//      the 64-bit composite (key << 32 | ~position): rank counting when few, an MSB-first
+//      radix select otherwise (e.g. many equal scores),
+//   4. compacts the winners (above (beta, beta2), or tied with composite >= threshold)
+//      in list order.  The filter writes the list in position order when there is no
+//      candidate map, so the winners come out ascending; with a candidate map they are
+//      ranked by position afterwards.
 #pragma once
 
 #include "common.hpp"
@@ -72,16 +75,16 @@ __device__ __forceinline__ bool is_tied(uint32_t key, uint32_t beta, uint32_t be
   return hist_bin(key) == beta && hist2_bin(key) == beta2;
 }
 
-// Select `need` of the tied candidates by the exact order and append them to the winner
-// list (slot counter misc[3]).  src[0..n) holds the tied candidates (FILTERED = false), or
-// is the row's whole candidate list from which the tied ones are picked by is_tied.
+// The composite threshold among the tied candidates: exactly `need` (>= 1) of them have
+// composite >= the returned value.  src[0..n) holds the tied candidates (FILTERED =
+// false), or is the row's whole candidate list from which the tied ones are picked by
+// is_tied.  Ends with a block barrier; every thread gets the value.
 template <int NT, bool FILTERED, typename SRC>
-__device__ void select_tied(const SRC& src, uint32_t n, uint32_t need, uint32_t beta, uint32_t beta2,
-                            FinalizeSmem& sm) {
+__device__ uint64_t tied_threshold(const SRC& src, uint32_t n, uint32_t need, uint32_t beta, uint32_t beta2,
+                                   FinalizeSmem& sm) {
   const int tid = threadIdx.x;
-  if (need == 0) return;
   if (!FILTERED && n <= (uint32_t)kFinRankMax) {
-    for (uint32_t i = tid; i < n; i += NT) {
+    for (uint32_t i = tid; i < n; i += NT) {  // ranks are distinct: positions are
       const uint2 c = src(i);
       const uint64_t ci = ((uint64_t)c.x << 32) | (uint32_t)(~c.y);
       uint32_t rank = 0;
@@ -90,18 +93,16 @@ __device__ void select_tied(const SRC& src, uint32_t n, uint32_t need, uint32_t 
         const uint64_t cj = ((uint64_t)d.x << 32) | (uint32_t)(~d.y);
         rank += (cj > ci) ? 1u : 0u;
       }
-      if (rank < need) {
-        const uint32_t slot = atomicAdd(&sm.misc[3], 1u);
-        if (slot < (uint32_t)CSA2_MAX_K_DEV) {
-          sm.win_pos[slot] = c.y;
-          sm.win_key[slot] = c.x;
-        }
+      if (rank == need - 1) {
+        sm.misc[12] = (uint32_t)ci;
+        sm.misc[13] = (uint32_t)(ci >> 32);
       }
     }
     __syncthreads();
-    return;
+    return ((uint64_t)sm.misc[13] << 32) | sm.misc[12];
   }
-  // radix select over 8-bit digits of the composite, most significant first
+  // radix select over 8-bit digits of the composite, most significant first; the
+  // selected ones are those with (comp & mask) >= prefix, i.e. comp >= prefix
   uint64_t prefix = 0, mask = 0;
   uint32_t rem = need;
   for (int shift = 56; shift >= 0; shift -= 8) {
@@ -129,30 +130,28 @@ __device__ void select_tied(const SRC& src, uint32_t n, uint32_t need, uint32_t 
     __syncthreads();
     if (done) break;
   }
-  for (uint32_t i = tid; i < n; i += NT) {
-    const uint2 c = src(i);
-    if (FILTERED && !is_tied(c.x, beta, beta2)) continue;
-    const uint64_t comp = ((uint64_t)c.x << 32) | (uint32_t)(~c.y);
-    if ((comp & mask) >= prefix) {
-      const uint32_t slot = atomicAdd(&sm.misc[3], 1u);
-      if (slot < (uint32_t)CSA2_MAX_K_DEV) {
-        sm.win_pos[slot] = c.y;
-        sm.win_key[slot] = c.x;
-      }
-    }
-  }
-  __syncthreads();
+  return prefix;
 }
 
 // Writes the keff winners' positions (ascending) to out_pos[0..keff) and, if out_key !=
 // nullptr, their order keys; returns keff.  All threads of the block must call it.
-// The candidates are in `nreg` regions of kFilterColsPerBlock pairs (counts in cnt).
-template <int NT>
+// The candidates are in `nreg` regions of kFilterColsPerBlock pairs (counts in cnt);
+// SORTED: the list is in ascending position order (no candidate map).
+template <int NT, bool SORTED>
 __device__ int finalize_row(const uint2* __restrict__ regions, const uint32_t* __restrict__ cnt, int nreg,
                             const uint32_t* __restrict__ h2row, uint32_t beta, uint32_t above, uint32_t keff,
                             FinalizeSmem& sm, int32_t* out_pos, uint32_t* out_key) {
-  const int tid = threadIdx.x;
+  constexpr int kWaves = NT / 64;
+  constexpr int kCompPer = 64 / kWaves;  // list items per thread and compaction pass
+  static_assert(kCompPer * kWaves == 64 && kCompPer >= 1, "one wave scans the (pass, wave) counts");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (keff == 0) return 0;
+  // the second-level histogram is loaded first: its latency overlaps the count prefix
+  constexpr int kPer = (kHistBins / NT > 0) ? kHistBins / NT : 1;  // bins per thread
+  constexpr int kT = kHistBins / kPer;                               // threads holding bins
+  uint32_t hb[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) hb[i] = (tid < kT) ? h2row[tid * kPer + i] : 0u;
   // 0. region starts: exclusive prefix of the per-region counts (one load per thread per
   //    pass; nreg <= kFinMaxRegions)
   {
@@ -192,20 +191,13 @@ __device__ int finalize_row(const uint2* __restrict__ regions, const uint32_t* _
   }
   // 2. second-level threshold inside bin beta
   const uint32_t need1 = keff - above;
-  constexpr int kPer = (kHistBins / NT > 0) ? kHistBins / NT : 1;  // bins per thread
-  constexpr int kT = kHistBins / kPer;                               // threads holding bins
-  uint32_t hb[kPer];
   uint32_t local = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    hb[i] = (tid < kT) ? h2row[tid * kPer + i] : 0u;
-    local += hb[i];
-  }
+  for (int i = 0; i < kPer; ++i) local += hb[i];
   if (tid == 0) {
     sm.misc[0] = 0;  // beta2
     sm.misc[1] = 0;  // candidates of bin beta above beta2
     sm.misc[2] = 0;  // tied count
-    sm.misc[3] = 0;  // winner count
   }
   const uint32_t suf = block_suffix<NT, kT>(local, sm.wsum);
   if (tid < kT && suf >= need1 && suf - local < need1) {
@@ -221,53 +213,96 @@ __device__ int finalize_row(const uint2* __restrict__ regions, const uint32_t* _
   }
   __syncthreads();
   const uint32_t beta2 = sm.misc[0];
-  const uint32_t need3 = need1 - sm.misc[1];
-  // 3. classify: winners above (beta, beta2), tied at (beta, beta2)
+  const uint32_t need3 = need1 - sm.misc[1];  // >= 1: bin (beta, beta2) holds the K-th
+  // 3. collect the candidates tied at (beta, beta2)
   for (uint32_t base = 0; base < M; base += NT) {  // uniform trip count: wave_reserve needs every lane
     const uint32_t i = base + tid;
     const bool valid = i < M;
     const uint2 c = valid ? (staged ? sm.stage[i] : list.get(i)) : make_uint2(0u, 0u);
-    const uint32_t b1 = hist_bin(c.x);
-    const uint32_t b2 = hist2_bin(c.x);
-    const bool win = valid && (b1 > beta || (b1 == beta && b2 > beta2));
-    const bool tie = valid && b1 == beta && b2 == beta2;
-    const uint32_t ws = wave_reserve(&sm.misc[3], win);
+    const bool tie = valid && is_tied(c.x, beta, beta2);
     const uint32_t ts = wave_reserve(&sm.misc[2], tie);
-    if (win && ws < (uint32_t)CSA2_MAX_K_DEV) {
-      sm.win_pos[ws] = c.y;
-      sm.win_key[ws] = c.x;
-    }
     if (tie && ts < (uint32_t)kFinCap) sm.tied[ts] = c;
   }
   __syncthreads();
-  // 4. the remaining need among the tied candidates (held in LDS, or - rare, e.g. many
-  //    equal scores - picked out of the whole candidate list again)
+  // 4. the composite threshold among them (held in LDS, or - rare, e.g. many equal
+  //    scores - picked out of the whole candidate list again)
   const uint32_t ntied = sm.misc[2];
+  uint64_t thr;
   if (ntied <= (uint32_t)kFinCap) {
     const uint2* tl = sm.tied;
-    select_tied<NT, false>([tl](uint32_t i) { return tl[i]; }, ntied, need3, beta, beta2, sm);
+    thr = tied_threshold<NT, false>([tl](uint32_t i) { return tl[i]; }, ntied, need3, beta, beta2, sm);
   } else if (staged) {
     const uint2* st = sm.stage;
-    select_tied<NT, true>([st](uint32_t i) { return st[i]; }, M, need3, beta, beta2, sm);
+    thr = tied_threshold<NT, true>([st](uint32_t i) { return st[i]; }, M, need3, beta, beta2, sm);
   } else {
-    select_tied<NT, true>([list](uint32_t i) { return list.get(i); }, M, need3, beta, beta2, sm);
+    thr = tied_threshold<NT, true>([list](uint32_t i) { return list.get(i); }, M, need3, beta, beta2, sm);
   }
-  // 5. rank the winners by position (distinct positions): each counts the smaller ones,
-  //    reading the list four at a time (broadcast LDS reads)
-  for (uint32_t i = tid; i < keff; i += NT) {
-    const uint32_t p = sm.win_pos[i];
-    uint32_t rank = 0;
-    const uint32_t k4 = keff & ~3u;
-#pragma unroll 8
-    for (uint32_t j = 0; j < k4; j += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&sm.win_pos[j]);
-      rank += (v.x < p) + (v.y < p) + (v.z < p) + (v.w < p);
+  // 5. compact the winners in list order: item base + 64 (kWaves u + wave) + lane goes to
+  //    its (pass u, wave) count's exclusive prefix plus its rank in the ballot
+  int32_t* dst_pos = SORTED ? out_pos : reinterpret_cast<int32_t*>(sm.win_pos);
+  uint32_t* dst_key = SORTED ? out_key : sm.win_key;
+  uint32_t carry = 0;
+  for (uint32_t base = 0; base < M; base += 64 * 64) {
+    uint64_t bal[kCompPer];
+    uint2 cv[kCompPer];
+#pragma unroll
+    for (int u = 0; u < kCompPer; ++u) {
+      const uint32_t i = base + 64 * (kWaves * u + wave) + lane;
+      const bool valid = i < M;
+      const uint2 c = valid ? (staged ? sm.stage[i] : list.get(i)) : make_uint2(0u, 0u);
+      const uint32_t b1 = hist_bin(c.x), b2 = hist2_bin(c.x);
+      const uint64_t comp = ((uint64_t)c.x << 32) | (uint32_t)(~c.y);
+      const bool win = valid && (b1 > beta || (b1 == beta && (b2 > beta2 || (b2 == beta2 && comp >= thr))));
+      bal[u] = __ballot(win);
+      cv[u] = c;
     }
-    for (uint32_t j = k4; j < keff; ++j) rank += (sm.win_pos[j] < p) ? 1u : 0u;
-    out_pos[rank] = (int32_t)p;
-    if (out_key) out_key[rank] = sm.win_key[i];
+    if (lane < kCompPer) {
+      uint32_t n = 0;
+#pragma unroll
+      for (int u = 0; u < kCompPer; ++u)
+        if (u == lane) n = (uint32_t)__builtin_popcountll(bal[u]);
+      sm.h256[lane * kWaves + wave] = n;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t v = sm.h256[lane];
+      const uint32_t sfx = wave_suffix(v);
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 0);
+      sm.h256[64 + lane] = carry + tot - sfx;
+      if (lane == 0) sm.misc[5] = tot;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kCompPer; ++u) {
+      if ((bal[u] >> lane) & 1ull) {
+        const uint32_t slot = sm.h256[64 + u * kWaves + wave] + lanes_below(bal[u]);
+        if (slot < (uint32_t)CSA2_MAX_K_DEV) {
+          dst_pos[slot] = (int32_t)cv[u].y;
+          if (!SORTED || out_key) dst_key[slot] = cv[u].x;
+        }
+      }
+    }
+    carry += sm.misc[5];
+    __syncthreads();
   }
-  __syncthreads();
+  if (!SORTED) {
+    // rank the winners by position (distinct positions): each counts the smaller ones,
+    // reading the list four at a time (broadcast LDS reads)
+    for (uint32_t i = tid; i < keff; i += NT) {
+      const uint32_t p = sm.win_pos[i];
+      uint32_t rank = 0;
+      const uint32_t k4 = keff & ~3u;
+#pragma unroll 8
+      for (uint32_t j = 0; j < k4; j += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&sm.win_pos[j]);
+        rank += (v.x < p) + (v.y < p) + (v.z < p) + (v.w < p);
+      }
+      for (uint32_t j = k4; j < keff; ++j) rank += (sm.win_pos[j] < p) ? 1u : 0u;
+      out_pos[rank] = (int32_t)p;
+      if (out_key) out_key[rank] = sm.win_key[i];
+    }
+    __syncthreads();
+  }
   return (int)keff;
 }
 
