@@ -5,10 +5,10 @@
 // dequantised entry is both key and value.
 //
 // MFMA path (bf16 queries, Hq % 16 == 0, D in {128, 256, 512}).  One block = one query
-// row x 16 heads (the MFMA M dimension) x one split of up to 128 selected entries, 8
-// waves; with more than one split a second kernel merges the splits' partial softmaxes
-// by log-sum-exp (a kernel boundary: merging inside the kernel would need a device-scope
-// release fence, which costs more here).  The per-channel scale s_c factors out of both
+// row x 16 heads (the MFMA M dimension) x one split of up to 512 selected entries, 16
+// waves, so the pages' Top-512 needs no merge; larger K runs several splits and a second
+// kernel merges their partial softmaxes by log-sum-exp (a kernel boundary: merging inside
+// the kernel would need a device-scope release fence, which costs more here).  The per-channel scale s_c factors out of both
 // contractions: logits use q'' = q * s * 2^k in fp16 (2^k an exact prescale keeping
 // |q''| below 2^15, undone in the softmax scale; ~2^-12 relative error) against the exact
 // E2M1 values e in fp16; the output is s_c * sum_j p_j e_jc / l with p in fp16.  FP4
@@ -26,9 +26,11 @@
 namespace csa2 {
 
 constexpr int kAttHeads = 16;      // heads per block (MFMA M)
-constexpr int kAttWaves = 8;       // two waves per SIMD, so that each SIMD interleaves two streams
+constexpr int kAttWaves = 16;      // four waves per SIMD
 constexpr int kAttThreads = 64 * kAttWaves;
-constexpr int kAttSplit = 16 * kAttWaves;  // entries per block (one 16-entry tile per wave in QK)
+constexpr int kAttSplit = 512;     // entries per block: the pages' Top-512 in one block, no merge
+constexpr int kAttTPW = kAttSplit / 16 / kAttWaves;  // 16-entry QK tiles per wave
+static_assert(kAttTPW * 16 * kAttWaves == kAttSplit, "QK tiles cover the split");
 
 // partials: part_o [R][S][Hq][D] normalised outputs, part_ml [R][S][Hq][2] (max, sum)
 
@@ -174,35 +176,45 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
 
   // ---- phase 1: logits of this wave's 16 entries
   const uint8_t* cb = codes + (int64_t)b * n_max * kRowBytes;
-  float logit[4];
+  float logit[kAttTPW][4];
   {
-    const int e = wave * 16 + n16;
-    const int32_t j = (e < ecount) ? sel[e] : -1;
-    // unconditional loads from a valid row (row 0 for skipped entries) keep the loads
-    // branch-free so that they pipeline; skipped entries are masked in the logits
-    const uint8_t* rowp = cb + (int64_t)(j >= 0 ? j : 0) * kRowBytes + 16 * g;
-    uint4 kw[kCT];
+    // all row loads first: unconditional loads from a valid row (row 0 for skipped
+    // entries) keep them branch-free so that they pipeline; skipped entries are masked
+    uint4 kw[kAttTPW][kCT];
+    int32_t jt[kAttTPW];
 #pragma unroll
-    for (int i = 0; i < kCT; ++i) kw[i] = *reinterpret_cast<const uint4*>(rowp + 64 * i);
-    v4f a = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kAttTPW; ++t) {
+      const int e = (wave * kAttTPW + t) * 16 + n16;
+      jt[t] = (e < ecount) ? sel[e] : -1;
+      const uint8_t* rowp = cb + (int64_t)(jt[t] >= 0 ? jt[t] : 0) * kRowBytes + 16 * g;
 #pragma unroll
-    for (int i = 0; i < kCT; ++i) {
-      const uint32_t wd[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        const v8h bv = decode8_f16(wd[sub]);
-        const v8h av = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, a, 0, 0, 0);
-      }
+      for (int i = 0; i < kCT; ++i) kw[t][i] = *reinterpret_cast<const uint4*>(rowp + 64 * i);
     }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) logit[rr] = (j >= 0) ? a[rr] * lscale : kNegInf;
+    for (int t = 0; t < kAttTPW; ++t) {
+      v4f a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kCT; ++i) {
+        const uint32_t wd[4] = {kw[t][i].x, kw[t][i].y, kw[t][i].z, kw[t][i].w};
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+          const v8h bv = decode8_f16(wd[sub]);
+          const v8h av = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, a, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (jt[t] >= 0) ? a[rr] * lscale : kNegInf;
+    }
   }
 
   // ---- phase 2: softmax statistics of the split (heads 4g + rr of this lane)
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    const float v = row16_max(logit[rr]);
+    float v = logit[0][rr];
+#pragma unroll
+    for (int t = 1; t < kAttTPW; ++t) v = fmaxf(v, logit[t][rr]);
+    v = row16_max(v);
     if (n16 == 0) s_red[wave][4 * g + rr] = v;
   }
   __syncthreads();
@@ -217,10 +229,15 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   for (int rr = 0; rr < 4; ++rr) {
     const int h = 4 * g + rr;
     const float m = s_m[h];
-    const float p = (m == kNegInf) ? 0.0f : __expf(logit[rr] - m);
-    const _Float16 ph = (_Float16)p;
-    sP[h * L::kPpad + wave * 16 + n16] = __builtin_bit_cast(uint16_t, ph);
-    const float v = row16_sum(p);
+    float v = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kAttTPW; ++t) {
+      const float p = (m == kNegInf) ? 0.0f : __expf(logit[t][rr] - m);
+      const _Float16 ph = (_Float16)p;
+      sP[h * L::kPpad + (wave * kAttTPW + t) * 16 + n16] = __builtin_bit_cast(uint16_t, ph);
+      v += p;
+    }
+    v = row16_sum(v);
     if (n16 == 0) s_red[wave][h] = v;
   }
   __syncthreads();
