@@ -49,14 +49,15 @@ __device__ __forceinline__ v8h decode8_f16(uint32_t word) {
   return __builtin_bit_cast(v8h, u);
 }
 
-template <int D>
+template <int D, int WPT>
 struct AttLds {
   static constexpr int kApad = D + 8;           // fp16 per A row (padding against bank conflicts)
   static constexpr int kPpad = kAttSplit + 8;
   static constexpr size_t kA = (size_t)kAttHeads * kApad * 2;
   static constexpr size_t kP = (size_t)kAttHeads * kPpad * 2;
-  static constexpr size_t kO = (size_t)kAttHeads * D * 4;
-  static constexpr size_t kWork = kA + kP + kO;
+  static constexpr size_t kO = (size_t)WPT * kAttHeads * D * 4;  // per entry group, after sA/sP are dead
+  static constexpr size_t kAP = kA + kP;
+  static constexpr size_t kWork = kAP > kO ? kAP : kO;
   static constexpr size_t kUnion = kWork > sizeof(FinalizeSmem) ? kWork : sizeof(FinalizeSmem);
 };
 
@@ -72,11 +73,11 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     const uint32_t* __restrict__ hist2, const uint2* __restrict__ candbuf, const uint32_t* __restrict__ cnt, int nreg,
     int32_t* __restrict__ idx_out, float softmax_scale, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
     float* __restrict__ part, float* __restrict__ part_ml) {
-  using L = AttLds<D>;
   constexpr int kRowBytes = D / 2;
   constexpr int kCT = D / 128;                 // 128-channel tiles
   constexpr int kWPT = (kAttWaves / kCT < kAttSplit / 32) ? kAttWaves / kCT : kAttSplit / 32;  // waves per tile in PV
   constexpr int kEPW = kAttSplit / kWPT;       // entries per wave in PV (a multiple of 32)
+  using L = AttLds<D, kWPT>;
   __shared__ float s_scale[D];
   __shared__ int32_t s_idx[FROM_CAND ? CSA2_MAX_K_DEV : kAttSplit];
   __shared__ float s_red[kAttWaves][kAttHeads];
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   __shared__ __align__(16) unsigned char s_u[L::kUnion];
   uint16_t* sA = reinterpret_cast<uint16_t*>(s_u);
   uint16_t* sP = reinterpret_cast<uint16_t*>(s_u + L::kA);
-  float* sO = reinterpret_cast<float*>(s_u + L::kA + L::kP);
+  float* sO = reinterpret_cast<float*>(s_u);  // [kWPT][16][D], used once sA and sP are dead
 
   const int split = blockIdx.x, hg = blockIdx.y, r = blockIdx.z;
   const int b = r / T;
@@ -113,11 +114,9 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     const int keff = finalize_row<kAttThreads, true>(candbuf + (int64_t)r * nreg * kFilterColsPerBlock,
                                                cnt + (int64_t)r * nreg, nreg, hist2 + (int64_t)r * kHistBins, c.beta,
                                                c.above, c.keff, fs, s_idx, nullptr);
-    for (int i = keff + tid; i < K; i += kAttThreads) s_idx[i] = -1;
-    __syncthreads();
-    if (split == 0 && hg == 0 && idx_out)
-      for (int i = tid; i < K; i += kAttThreads) idx_out[(int64_t)r * K + i] = s_idx[i];
-    sel = s_idx + e0;
+    for (int i = keff + tid; i < S * kAttSplit; i += kAttThreads) s_idx[i] = -1;  // pad to whole splits
+    sel = s_idx + e0;  // the row's indices are stored at the end (a global store before a
+                       // barrier would make that barrier wait for every load in flight)
   } else {
     for (int i = tid; i < kAttSplit; i += kAttThreads) {
       const int e = e0 + i;
@@ -126,11 +125,26 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     }
     sel = s_idx;
   }
-  const int ecount = min(kAttSplit, K - e0);
+  __syncthreads();  // s_scale, s_idx
 
+  // ---- phase 1a: issue this wave's QK row loads now, so that their latency overlaps the
+  //      query preparation.  Unconditional loads from a valid row (row 0 for skipped
+  //      entries) keep them branch-free; skipped entries are masked in the logits.
+  const uint8_t* cb = codes + (int64_t)b * n_max * kRowBytes;
+  uint4 kw[kAttTPW][kCT];
+  int32_t jt[kAttTPW];
+#pragma unroll
+  for (int t = 0; t < kAttTPW; ++t) {
+    const int e = (wave * kAttTPW + t) * 16 + n16;
+    jt[t] = sel[e];  // -1 past K
+    const uint8_t* rowp = cb + (int64_t)(jt[t] >= 0 ? jt[t] : 0) * kRowBytes + 16 * g;
+#pragma unroll
+    for (int i = 0; i < kCT; ++i) kw[t][i] = *reinterpret_cast<const uint4*>(rowp + 64 * i);
+  }
+
+  // ---- phase 0b: q'' = q * s * 2^k in fp16 into LDS (A operand of QK)
   float qv[kQPer][8];
   float qmax = 0.0f;
-  __syncthreads();  // s_scale
 #pragma unroll
   for (int it = 0; it < kQPer; ++it) {
     const int i = tid + it * kAttThreads;
@@ -145,14 +159,15 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   }
   qmax = wave_max(qmax);
   if (lane == 0) s_qmax[wave] = qmax;
-  if (tid < kAttHeads) {
-    s_m[tid] = kNegInf;
-    s_l[tid] = 0.0f;
-  }
   __syncthreads();
-  qmax = s_qmax[0];
+  {
+    float t4[kAttWaves];
 #pragma unroll
-  for (int w2 = 1; w2 < kAttWaves; ++w2) qmax = fmaxf(qmax, s_qmax[w2]);
+    for (int w2 = 0; w2 < kAttWaves; ++w2) t4[w2] = s_qmax[w2];
+    qmax = t4[0];
+#pragma unroll
+    for (int w2 = 1; w2 < kAttWaves; ++w2) qmax = fmaxf(qmax, t4[w2]);
+  }
   // power-of-two prescale so that |q''| < 2^15 (fp16 max 65504); exact, undone in the logits
   int qexp = 0;
   if (qmax > 0.0f) qexp = (int)((__float_as_uint(qmax) >> 23) & 255u) - 126;
@@ -174,41 +189,46 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   }
   __syncthreads();
 
-  // ---- phase 1: logits of this wave's 16 entries
-  const uint8_t* cb = codes + (int64_t)b * n_max * kRowBytes;
+  // ---- phase 1b: logits of this wave's kAttTPW tiles of 16 entries
   float logit[kAttTPW][4];
-  {
-    // all row loads first: unconditional loads from a valid row (row 0 for skipped
-    // entries) keep them branch-free so that they pipeline; skipped entries are masked
-    uint4 kw[kAttTPW][kCT];
-    int32_t jt[kAttTPW];
 #pragma unroll
-    for (int t = 0; t < kAttTPW; ++t) {
-      const int e = (wave * kAttTPW + t) * 16 + n16;
-      jt[t] = (e < ecount) ? sel[e] : -1;
-      const uint8_t* rowp = cb + (int64_t)(jt[t] >= 0 ? jt[t] : 0) * kRowBytes + 16 * g;
+  for (int t = 0; t < kAttTPW; ++t) {
+    v4f a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < kCT; ++i) kw[t][i] = *reinterpret_cast<const uint4*>(rowp + 64 * i);
+    for (int i = 0; i < kCT; ++i) {
+      const uint32_t wd[4] = {kw[t][i].x, kw[t][i].y, kw[t][i].z, kw[t][i].w};
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const v8h bv = decode8_f16(wd[sub]);
+        const v8h av = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, a, 0, 0, 0);
+      }
     }
 #pragma unroll
-    for (int t = 0; t < kAttTPW; ++t) {
-      v4f a = {0.f, 0.f, 0.f, 0.f};
+    for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (jt[t] >= 0) ? a[rr] * lscale : kNegInf;
+  }
+
+  // ---- phase 3a: issue the PV code-word loads (cache hits: the rows were just read) so
+  //      that they are in flight during the softmax.  Wave (channel tile ct, entry group
+  //      eq); lane (channel block n16, group g) takes one 32-bit word (8 channels) of each
+  //      of the 8 entries el..el+7 of every 32-entry k-step.
+  const int ct = wave % kCT, eq = wave / kCT;
+  const bool pv_active = eq < kWPT;
+  uint32_t pw[kEPW / 32][8];
 #pragma unroll
-      for (int i = 0; i < kCT; ++i) {
-        const uint32_t wd[4] = {kw[t][i].x, kw[t][i].y, kw[t][i].z, kw[t][i].w};
+  for (int ks = 0; ks < kEPW / 32; ++ks) {
+    const int el = eq * kEPW + 32 * ks + 8 * g;
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-          const v8h bv = decode8_f16(wd[sub]);
-          const v8h av = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
-          a = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, a, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (jt[t] >= 0) ? a[rr] * lscale : kNegInf;
+    for (int jj = 0; jj < 8; ++jj) {
+      const int e = el + jj;
+      const int32_t j = sel[e];  // -1 past K (read unconditionally: no branch per load)
+      // p is 0 for skipped entries, so any valid row may stand in for them
+      pw[ks][jj] = *reinterpret_cast<const uint32_t*>(cb + (int64_t)(j >= 0 ? j : 0) * kRowBytes + 64 * ct + 4 * n16);
     }
   }
 
-  // ---- phase 2: softmax statistics of the split (heads 4g + rr of this lane)
+  // ---- phase 2: softmax statistics of the split (heads 4g + rr of this lane).  Per-wave
+  //      partials go to LDS; 256 threads (one 16-lane row per head) reduce them by DPP.
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     float v = logit[0][rr];
@@ -218,11 +238,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     if (n16 == 0) s_red[wave][4 * g + rr] = v;
   }
   __syncthreads();
-  if (tid < kAttHeads) {
-    float mc = s_red[0][tid];
-#pragma unroll
-    for (int w2 = 1; w2 < kAttWaves; ++w2) mc = fmaxf(mc, s_red[w2][tid]);
-    s_m[tid] = mc;
+  static_assert(kAttWaves == 16 && kAttHeads == 16, "one 16-lane row per head reduces the 16 waves");
+  if (tid < 256) {
+    const float v = row16_max(s_red[tid & 15][tid >> 4]);
+    if ((tid & 15) == 0) s_m[tid >> 4] = v;
   }
   __syncthreads();
 #pragma unroll
@@ -241,19 +260,15 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     if (n16 == 0) s_red[wave][h] = v;
   }
   __syncthreads();
-  if (tid < kAttHeads) {
-    float sum = 0.0f;
-#pragma unroll
-    for (int w2 = 0; w2 < kAttWaves; ++w2) sum += s_red[w2][tid];
-    s_l[tid] = sum;
+  if (tid < 256) {
+    const float v = row16_sum(s_red[tid & 15][tid >> 4]);
+    if ((tid & 15) == 0) s_l[tid >> 4] = v;
   }
 
-  // ---- phase 3: o[h][c] = sum_j p[h][j] e[j][c] over this wave's entries and channel tile.
-  //      B operands: for each pair of entries the two code words are nibble-interleaved
-  //      so that one byte holds the same channel of both entries; one fp4->fp16 pair
-  //      conversion then yields the (entry 2p, entry 2p+1) dword the MFMA k-order wants.
-  const int ct = wave % kCT, eq = wave / kCT;
-  const bool pv_active = eq < kWPT;
+  // ---- phase 3b: o[h][c] = sum_j p[h][j] e[j][c] over this wave's entries and channel
+  //      tile.  For each pair of entries the two code words are nibble-interleaved so that
+  //      one byte holds the same channel of both entries; one fp4->fp16 pair conversion
+  //      then yields the (entry 2p, entry 2p+1) dword the MFMA k-order wants.
   v4f acc[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -262,18 +277,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     for (int ks = 0; ks < kEPW / 32; ++ks) {
       const int el = eq * kEPW + 32 * ks + 8 * g;  // first of this lane's 8 entries
       const v8h pa = *reinterpret_cast<const v8h*>(&sP[n16 * L::kPpad + el]);
-      uint32_t wd[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int e = el + jj;
-        const int32_t j = (e < ecount) ? sel[e] : -1;
-        // p is 0 for skipped entries, so any valid row may stand in for them
-        wd[jj] = *reinterpret_cast<const uint32_t*>(cb + (int64_t)(j >= 0 ? j : 0) * kRowBytes + 64 * ct + 4 * n16);
-      }
       uint32_t xe[4], xo[4];
 #pragma unroll
       for (int p2 = 0; p2 < 4; ++p2) {
-        const uint32_t w0 = wd[2 * p2], w1 = wd[2 * p2 + 1];
+        const uint32_t w0 = pw[ks][2 * p2], w1 = pw[ks][2 * p2 + 1];
         xe[p2] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);  // channels 0,2,4,6
         xo[p2] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);  // channels 1,3,5,7
       }
@@ -289,64 +296,55 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     }
   }
 
-  // ---- phase 4: normalise and store.  With one wave per channel tile (D = 512) each lane
-  //      stores its own results (8 consecutive channels per head); otherwise the entry
-  //      groups of a tile are first summed in LDS in a fixed order.
-  __syncthreads();  // s_l
-  float inv_l[4], m_h[4];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const float l = s_l[4 * g + rr];
-    inv_l[rr] = (l > 0.0f) ? 1.0f / l : 0.0f;
-    m_h[rr] = s_m[4 * g + rr];
-  }
-  if (kWPT > 1) {
-    for (int round = 0; round < kWPT; ++round) {
-      if (eq == round) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            float* o = &sO[(4 * g + rr) * D + 128 * ct + 8 * n16 + m];
-            *o = (round == 0) ? acc[m][rr] : *o + acc[m][rr];
-          }
-      }
-      __syncthreads();
-    }
-    if (eq == 0) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int m = 0; m < 8; ++m) acc[m][rr] = sO[(4 * g + rr) * D + 128 * ct + 8 * n16 + m];
-    }
-  }
-  if (eq == 0) {
+  // ---- phase 4: every entry group writes its partial sums to its own LDS slice (sA and
+  //      sP are dead once all waves are past PV); then each thread sums the kWPT slices of
+  //      8 channels of one head in a fixed order (deterministic), normalises and stores.
+  __syncthreads();
+  if (pv_active) {
     const int c = 128 * ct + 8 * n16;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int h = hg * kAttHeads + 4 * g + rr;
-      float o[8];
+      float4* o = reinterpret_cast<float4*>(&sO[((size_t)eq * kAttHeads + 4 * g + rr) * D + c]);
+      o[0] = make_float4(acc[0][rr], acc[1][rr], acc[2][rr], acc[3][rr]);
+      o[1] = make_float4(acc[4][rr], acc[5][rr], acc[6][rr], acc[7][rr]);
+    }
+  }
+  __syncthreads();
+  constexpr int kOItems = kAttHeads * D / 8;
+  for (int i = tid; i < kOItems; i += kAttThreads) {
+    const int hl = i / (D / 8), c = (i % (D / 8)) * 8;
+    float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) o[m] = acc[m][rr] * inv_l[rr];
-      if (S == 1) {
+    for (int gq = 0; gq < kWPT; ++gq) {
+      const float4* src = reinterpret_cast<const float4*>(&sO[((size_t)gq * kAttHeads + hl) * D + c]);
+      const float4 a0 = src[0], a1 = src[1];
+      o0.x += a0.x; o0.y += a0.y; o0.z += a0.z; o0.w += a0.w;
+      o1.x += a1.x; o1.y += a1.y; o1.z += a1.z; o1.w += a1.w;
+    }
+    const float l = s_l[hl];
+    const float inv_l = (l > 0.0f) ? 1.0f / l : 0.0f;
+    float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
 #pragma unroll
-        for (int m = 0; m < 8; ++m) o[m] *= s_scale[c + m];
-        const int64_t oi = ((int64_t)r * Hq + h) * D + c;
-        if (out_bf16) {
-          uint32_t w4[4];
+    for (int m = 0; m < 8; ++m) o[m] *= inv_l;
+    const int h = hg * kAttHeads + hl;
+    if (S == 1) {
 #pragma unroll
-          for (int k2 = 0; k2 < 4; ++k2) w4[k2] = pack2(bf16_rne(o[2 * k2]), bf16_rne(o[2 * k2 + 1]));
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + oi) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-        } else {
-          float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi);
-          dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-          dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-        }
+      for (int m = 0; m < 8; ++m) o[m] *= s_scale[c + m];
+      const int64_t oi = ((int64_t)r * Hq + h) * D + c;
+      if (out_bf16) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) w4[k2] = pack2(bf16_rne(o[2 * k2]), bf16_rne(o[2 * k2 + 1]));
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + oi) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
       } else {
-        float4* dst = reinterpret_cast<float4*>(part + (((int64_t)r * S + split) * Hq + h) * D + c);
+        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi);
         dst[0] = make_float4(o[0], o[1], o[2], o[3]);
         dst[1] = make_float4(o[4], o[5], o[6], o[7]);
       }
+    } else {
+      float4* dst = reinterpret_cast<float4*>(part + (((int64_t)r * S + split) * Hq + h) * D + c);
+      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
     }
   }
   if (tid < kAttHeads) {
@@ -359,6 +357,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
       ml[1] = l;
     }
   }
+  if (FROM_CAND && split == 0 && hg == 0 && idx_out)
+    for (int i = tid; i < K; i += kAttThreads) idx_out[(int64_t)r * K + i] = s_idx[i];
 }
 
 // Merge the splits of (row, head group, channel tile) by log-sum-exp and scale by s_c.

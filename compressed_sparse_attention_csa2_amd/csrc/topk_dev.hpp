@@ -65,7 +65,8 @@ __device__ __forceinline__ uint32_t block_suffix(uint32_t v, uint32_t* wsum) {
   if (lane == 0) wsum[wave] = x;
   __syncthreads();
   uint32_t add = 0;
-  for (int w2 = wave + 1; w2 < T / 64; ++w2) add += wsum[w2];
+#pragma unroll
+  for (int w2 = 1; w2 < T / 64; ++w2) add += (w2 > wave) ? wsum[w2] : 0u;  // independent reads
   __syncthreads();
   return (tid < T) ? x + add : 0u;
 }
@@ -172,21 +173,16 @@ __device__ int finalize_row(const uint2* __restrict__ regions, const uint32_t* _
   }
   const uint32_t M = sm.misc[4];
   const CandList list{regions, sm.start, nreg};
-  // 1. stage the candidates in LDS (four loads in flight per thread, clamped, branch-free)
+  // 1. issue the loads that stage the candidates in LDS (all in flight, clamped,
+  //    branch-free); they are stored after the second-level scan, which hides them
+  constexpr int kStagePer = kFinStage / NT;
   const bool staged = M <= (uint32_t)kFinStage;
+  uint2 sv[kStagePer];
   if (staged) {
-    for (uint32_t base = tid; base < M; base += 4 * NT) {
-      uint2 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t i = base + u * NT;
-        v[u] = list.get(i < M ? i : M - 1);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t i = base + u * NT;
-        if (i < M) sm.stage[i] = v[u];
-      }
+    for (int u = 0; u < kStagePer; ++u) {
+      const uint32_t i = tid + u * NT;
+      if (u * NT < (int)M) sv[u] = list.get(i < M ? i : M - 1);  // uniform guard
     }
   }
   // 2. second-level threshold inside bin beta
@@ -209,6 +205,13 @@ __device__ int finalize_row(const uint2* __restrict__ regions, const uint32_t* _
         break;
       }
       acc += hb[i];
+    }
+  }
+  if (staged) {
+#pragma unroll
+    for (int u = 0; u < kStagePer; ++u) {
+      const uint32_t i = tid + u * NT;
+      if (i < M) sm.stage[i] = sv[u];
     }
   }
   __syncthreads();

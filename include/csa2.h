@@ -167,9 +167,9 @@ size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int K);
  *   q_dtype CSA2_F32: fp32 arithmetic throughout (out_dtype must be CSA2_F32).
  *   q_dtype CSA2_BF16: fp16 MFMA with fp32 accumulation, the per-channel scale folded into
  *   the query (exact power-of-two prescale) and into the output; needs Hq % 16 == 0 and
- *   D in {128, 256, 512}.  Entries are processed in groups of 128 whose partial softmax
+ *   D in {128, 256, 512}.  Entries are processed in groups of 512 whose partial softmax
  *   results are merged by log-sum-exp.  ws: csa2_sparse_attend_workspace_size() bytes
- *   (0 when K <= 128 or q is fp32; then ws may be NULL).
+ *   (0 when K <= 512 or q is fp32; then ws may be NULL).
  */
 int csa2_sparse_attend(int B, int T, int Hq, int D, const void* q, int q_dtype, const uint8_t* kv_codes,
                        const float* kv_scales, int64_t n_max, const int32_t* idx, int K, float softmax_scale,
