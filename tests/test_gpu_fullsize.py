@@ -1,0 +1,160 @@
+"""GPU parity at the full sizes of the measured configurations, in the launch
+configuration bench.py times.
+
+The whole batch runs on the GPU. The oracle recomputes a sample of sequences (or query
+rows) one by one: the cache bytes of the sampled sequences bit-exact, the Top-K sets
+under the near-tie rule, and the attention outputs under the bf16 rule. A second run of
+the same call must reproduce every output bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_attention_csa2_amd as csa2
+import oracle
+import workloads
+from helpers import DEV, check_topk_near_tie, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_ok(out, ref):
+    """bf16-written output: per element within 2e-3 * max|ref| plus half a bf16 ulp."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return bool(np.all(np.abs(out - ref) <= 2e-3 * np.abs(ref).max() + np.abs(ref) * 2.0 ** -8))
+
+
+def _device_cache_with_samples(wl, sample):
+    """Quantise every sequence on the GPU, one at a time, as bench.py does; the sampled
+    sequences are also quantised by the oracle and compared byte for byte."""
+    B, N, D, dk = wl.B, wl.N, wl.D, wl.dk
+    codes = torch.empty((B, N, D // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((B, D), dtype=torch.float32, device=DEV)
+    k8 = torch.empty((B, N, dk), dtype=torch.uint8, device=DEV)
+    ks = torch.empty((B, N), dtype=torch.float32, device=DEV)
+    ref = {}
+    for b in range(B):
+        x = wl.main_kv(b)
+        kf = wl.index_keys(b)
+        csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, to_dev(x)[None], codes[b:b + 1], scales[b:b + 1])
+        csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(kf)[None], k8[b:b + 1], ks[b:b + 1])
+        if b in sample:
+            cr, sr = oracle.quantize_fp4(x[None])
+            kr, ksr = oracle.quantize_fp8(kf[None])
+            torch.cuda.synchronize()
+            assert np.array_equal(codes[b].cpu().numpy(), cr[0]), b
+            assert np.array_equal(scales[b].cpu().numpy(), sr[0]), b
+            assert np.array_equal(k8[b].cpu().numpy(), kr[0]), b
+            assert np.array_equal(ks[b].cpu().numpy(), ksr[0]), b
+            ref[b] = (cr[0], sr[0], kr[0], ksr[0])
+    torch.cuda.synchronize()
+    return dict(codes=codes, scales=scales, k8=k8, ks=ks), ref
+
+
+def _check_group_against_oracle(wl, modes, dev_layers, ref_cache, sample, q_in):
+    ref_layers = [dict(mode=m, q_idx=q_in[i][0][sample], w=q_in[i][1][sample], q_attn=q_in[i][2][sample])
+                  for i, m in enumerate(modes)]
+    R = oracle.layer_group(ref_layers, ref_cache, oracle.PREC_FP8, wl.K, wl.softmax_scale)
+    idx_last = None
+    exact = 0
+    for i, (L, Rl) in enumerate(zip(dev_layers, R)):
+        if L["mode"] != "reuse":
+            s = oracle.index_score(oracle.PREC_FP8, ref_layers[i]["q_idx"], ref_layers[i]["w"], ref_cache["k"],
+                                   ref_cache["k_scale"], ref_cache["n_keys"])
+            idx_last = L["idx"].cpu().numpy()[sample]
+            exact += check_topk_near_tie(idx_last, s, wl.K)
+        out = L["out"].float().cpu().numpy()[sample]
+        for j in range(len(sample)):
+            if np.array_equal(idx_last[j], Rl["idx"][j]):
+                assert _bf16_ok(out[j], Rl["out"][j]), (i, sample[j])
+    return exact
+
+
+def test_group128k_full_size_sampled_sequences():
+    """The 128K decode configuration: Full -> Reindex -> Reuse, 16 sequences x 131072."""
+    wl = workloads.WORKLOADS["group128k"]
+    sample = [0, 9, 15]
+    c, ref = _device_cache_with_samples(wl, sample)
+    n_keys = torch.full((wl.B,), wl.N, dtype=torch.int32, device=DEV)
+    q_in, layers = [], []
+    for i, m in enumerate(wl.modes):
+        qi, w, qa = wl.index_query(i), wl.head_weights(i), wl.attn_query(i)
+        q_in.append((qi, w, qa))
+        layers.append(dict(mode=m, q_idx=to_dev(qi, torch.bfloat16), w=to_dev(w), q_attn=to_dev(qa, torch.bfloat16)))
+    cache = csa2.GroupCache(n_keys, c["codes"], c["scales"], c["k8"], c["ks"], wl.K, wl.softmax_scale)
+    plan = csa2.GroupPlan(layers, cache, out_dtype=torch.bfloat16)
+    plan.run()
+    torch.cuda.synchronize()
+    first = [(L["out"].clone(), L["lse"].clone(), L.get("idx").clone() if L.get("idx") is not None else None)
+             for L in layers]
+    ref_cache = dict(k=np.stack([ref[b][2] for b in sample]), k_scale=np.stack([ref[b][3] for b in sample]),
+                     n_keys=np.full(len(sample), wl.N, np.int32), codes=np.stack([ref[b][0] for b in sample]),
+                     scales=np.stack([ref[b][1] for b in sample]))
+    _check_group_against_oracle(wl, wl.modes, layers, ref_cache, sample, q_in)
+    # determinism: the same call again gives the same bits
+    plan.run()
+    torch.cuda.synchronize()
+    for L, (o, l, ix) in zip(layers, first):
+        assert torch.equal(L["out"], o) and torch.equal(L["lse"], l)
+        if ix is not None:
+            assert torch.equal(L["idx"], ix)
+
+
+def test_full64k_full_size_sampled_sequences():
+    """The single-layer 64K decode configuration: Full, 16 sequences x 65536."""
+    wl = workloads.WORKLOADS["full64k"]
+    sample = [3, 12]
+    c, ref = _device_cache_with_samples(wl, sample)
+    n_keys = torch.full((wl.B,), wl.N, dtype=torch.int32, device=DEV)
+    qi, w, qa = wl.index_query(0), wl.head_weights(0), wl.attn_query(0)
+    layers = [dict(mode="full", q_idx=to_dev(qi, torch.bfloat16), w=to_dev(w), q_attn=to_dev(qa, torch.bfloat16))]
+    cache = csa2.GroupCache(n_keys, c["codes"], c["scales"], c["k8"], c["ks"], wl.K, wl.softmax_scale)
+    csa2.layer_group(layers, cache, out_dtype=torch.bfloat16)
+    ref_cache = dict(k=np.stack([ref[b][2] for b in sample]), k_scale=np.stack([ref[b][3] for b in sample]),
+                     n_keys=np.full(len(sample), wl.N, np.int32), codes=np.stack([ref[b][0] for b in sample]),
+                     scales=np.stack([ref[b][1] for b in sample]))
+    _check_group_against_oracle(wl, ["full"], layers, ref_cache, sample, [(qi, w, qa)])
+
+
+def test_hier1m_full_size():
+    """The 1M-entry two-level configuration: coarse keys of 64-entry blocks, top-256 blocks,
+    Top-1024 inside them, then attention over the 1024 entries (two splits merged)."""
+    wl = workloads.WORKLOADS["hier1m"]
+    n = wl.N
+    x = wl.main_kv(0)
+    kf = wl.index_keys(0)
+    kr, ksr = oracle.quantize_fp8(kf[None])
+    nk = np.array([n], np.int32)
+    kb_ref, kbs_ref = oracle.coarse_keys(kr, ksr, nk, wl.coarse_block)
+    k8 = torch.empty((1, n, wl.dk), dtype=torch.uint8, device=DEV)
+    ks = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(kf)[None], k8, ks)
+    codes = torch.empty((1, n, wl.D // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((1, wl.D), dtype=torch.float32, device=DEV)
+    csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, to_dev(x)[None], codes, scales)
+    kb, kbs = csa2.coarse_keys(k8, ks, to_dev(nk), wl.coarse_block)
+    assert np.array_equal(kb.cpu().numpy(), kb_ref) and np.array_equal(kbs.cpu().numpy(), kbs_ref)
+    q, w = wl.index_query(), wl.head_weights()
+    idx, blk = csa2.hier_select(to_dev(q, torch.bfloat16), to_dev(w), k8, ks, kb, kbs, to_dev(nk), wl.coarse_block,
+                                wl.coarse_topk, wl.K, want_blocks=True)
+    cs = oracle.index_score(oracle.PREC_FP8, q, w, kb_ref, kbs_ref, (nk + wl.coarse_block - 1) // wl.coarse_block)
+    check_topk_near_tie(blk.cpu().numpy(), cs, wl.coarse_topk)
+    ref_idx, ref_blk = oracle.hier_select(q, w, kr, ksr, kb_ref, kbs_ref, nk, wl.coarse_block, wl.coarse_topk, wl.K)
+    g_idx = idx.cpu().numpy()
+    if np.array_equal(blk.cpu().numpy(), ref_blk):
+        cand = oracle.expand_blocks(ref_blk, wl.coarse_block, nk)
+        fs = oracle.index_score(oracle.PREC_FP8, q, w, kr, ksr, nk, cand=cand)
+        full = np.full((1, 1, n), -np.inf)
+        c0 = cand[0, 0]
+        full[0, 0, c0[c0 >= 0]] = fs[0, 0][c0 >= 0]
+        check_topk_near_tie(g_idx, full, wl.K)
+    # attention over the GPU's selection on both sides
+    qa = wl.attn_query()
+    cr, sr = oracle.quantize_fp4(x[None])
+    assert np.array_equal(codes.cpu().numpy(), cr)
+    out, lse = csa2.sparse_attend(to_dev(qa, torch.bfloat16), codes, scales, idx, wl.softmax_scale,
+                                  out_dtype=torch.bfloat16)
+    ro, rl = oracle.sparse_attend(qa, cr, sr, g_idx, wl.softmax_scale)
+    assert _bf16_ok(out.float().cpu().numpy(), ro)
+    assert np.allclose(lse.cpu().numpy(), rl, rtol=0, atol=2e-3 * max(1.0, np.abs(rl).max()))
