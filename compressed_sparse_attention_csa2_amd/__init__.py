@@ -183,8 +183,10 @@ def index_score(prec: int, q: torch.Tensor, w: torch.Tensor, k: torch.Tensor, k_
     ncols = C if cand is not None else n_max
     if scores is None:
         scores = torch.empty((B, T, ncols), dtype=torch.float32, device=q.device)
+    nb = lib().csa2_index_score_workspace_size(B, T, ncols)
+    ws = _workspace(nb, q.device)
     _check(lib().csa2_index_score(prec, B, T, H, dk, _ptr(q), _dtype_code(q), _ptr(w), _ptr(k), _ptr(k_scale),
-                                  n_max, _ptr(n_keys), _ptr(q_limit), _ptr(cand), C, _ptr(scores), None, 0,
+                                  n_max, _ptr(n_keys), _ptr(q_limit), _ptr(cand), C, _ptr(scores), _ptr(ws), nb,
                                   _stream()), "csa2_index_score")
     return scores
 

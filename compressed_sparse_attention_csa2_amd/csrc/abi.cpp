@@ -156,6 +156,7 @@ ScoreArgs score_args(int prec, int B, int T, int H, int dk, const void* q, int q
   a.q = q; a.w = w; a.k = k; a.k_scale = k_scale;
   a.n_max = n_max; a.n_keys = n_keys; a.q_limit = q_limit; a.cand = cand;
   a.ncols = ncols; a.scores = scores; a.hist = hist; a.key_div = key_div;
+  a.qstage = nullptr;
   return a;
 }
 
@@ -214,20 +215,25 @@ int csa2_gather_dequant(int B, int T, int K, int D, const uint8_t* codes, const 
   return dev_status(launch_gather_dequant(B, T, K, D, codes, scales, n_max, idx, out, S(stream)));
 }
 
-size_t csa2_index_score_workspace_size(int, int, int64_t) { return 0; }
+size_t csa2_index_score_workspace_size(int B, int T, int64_t) {
+  return T >= score_tiled_min_rows() ? align256(score_stage_bytes((int64_t)B * T)) : 0;
+}
 
 int csa2_index_score(int prec, int B, int T, int H, int dk, const void* q, int q_dtype, const float* w, const void* k,
                      const float* k_scale, int64_t n_max, const int32_t* n_keys, const int32_t* q_limit,
-                     const int32_t* cand, int C, float* scores, void*, size_t, void* stream) {
+                     const int32_t* cand, int C, float* scores, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !w || !k || !n_keys || !scores) return CSA2_ERR_NULL;
   if (n_max < 1 || (cand && C < 1)) return CSA2_ERR_SHAPE;
   const int64_t ncols = cand ? C : n_max;
   int rc = check_index_shape(prec, B, T, H, dk, q_dtype, k_scale, ncols);
   if (rc) return rc;
+  const size_t need = csa2_index_score_workspace_size(B, T, ncols);
+  if (need && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   rc = check_device();
   if (rc) return rc;
   ScoreArgs a = score_args(prec, B, T, H, dk, q, q_dtype, w, k, k_scale, n_max, n_keys, q_limit, cand, ncols, scores,
                            nullptr, 1);
+  if (need) a.qstage = static_cast<uint8_t*>(ws);
   return dev_status(launch_score(a, S(stream)));
 }
 
@@ -255,7 +261,7 @@ int csa2_topk(int B, int T, int64_t ncols, const float* scores, const int32_t* c
 
 size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int) {
   const int64_t R = (int64_t)B * T;
-  return align256((size_t)R * ncols * 4) + topk_ws(R, ncols);
+  return align256((size_t)R * ncols * 4) + topk_ws(R, ncols) + csa2_index_score_workspace_size(B, T, ncols);
 }
 
 int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_dtype, const float* w, const void* k,
@@ -275,10 +281,13 @@ int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_
   Carve c(ws);
   float* scores = c.take<float>((size_t)R * ncols);
   TopkWs t = carve_topk(c, R, ncols);
+  const size_t stage = csa2_index_score_workspace_size(B, T, ncols);
+  uint8_t* qstage = stage ? c.take<uint8_t>(stage) : nullptr;
   hipStream_t st = S(stream);
   if (zero_topk(t, R, st)) return CSA2_ERR_DEVICE;
   ScoreArgs a = score_args(prec, B, T, H, dk, q, q_dtype, w, k, k_scale, n_max, n_keys, q_limit, cand, ncols, scores,
                            t.hist, 1);
+  a.qstage = qstage;
   if (launch_score(a, st)) return CSA2_ERR_DEVICE;
   if (launch_topk_filter((int)R, ncols, scores, cand, K, t.hist, t.hist2, t.ctl, t.cand, t.cnt, st))
     return CSA2_ERR_DEVICE;

@@ -38,8 +38,13 @@ struct ScoreArgs {
   float* scores;
   uint32_t* hist;     // nullable: [R][kHistBins], must be zero on entry
   int key_div;        // 1, or the coarse block size when columns are blocks
+  uint8_t* qstage;    // nullable: score_stage_bytes(R) of scratch for the many-row fp8 path
 };
 int launch_score(const ScoreArgs& a, hipStream_t st);
+// Many-row fp8 scoring (chunked prefill) stages the quantised query rows: E4M3 codes and
+// head factors, R * (2048 + 128) bytes; used when T >= score_tiled_min_rows().
+inline size_t score_stage_bytes(int64_t R) { return (size_t)R * (32 * 64 + 32 * 4); }
+inline int score_tiled_min_rows() { return 8; }
 int score_cols_per_block(int64_t ncols);
 
 // Top-K: histogram (zeroed on entry) -> filter into candidates (ctl zeroed on entry)

@@ -214,6 +214,148 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
   }
 }
 
+// ------------------------------------------------------------------ fp8 path, many rows
+// Chunked prefill scores many query rows of one sequence against the same keys: a dense
+// fp8 contraction (rows x heads) x (keys), where re-streaming the keys once per row (as
+// the decode kernel does) would move ~T times the key bytes.  Here a block takes a tile
+// of kRowTile rows x (4 waves x NKT x 32) keys: the rows' E4M3 operands (quantised once
+// per row by k_quant_query) sit in LDS, each wave keeps 4 key tiles in registers and
+// runs all rows of the tile against them, so every key tile is read once per row tile.
+// The per-row first-level Top-K histogram is kept in LDS with 16-bit counters packed in
+// pairs (a block adds at most 128 x NKT <= 4096 to one bin of one row).
+constexpr int kRowTile = 8;
+
+// q [R][32][64] -> E4M3 codes q8 [R][32][64] and c [R][32] = w * sq, with sq = absmax/448
+// over the head's 64 values: the same arithmetic as quantize_query_operand.
+template <typename QT>
+__global__ __launch_bounds__(256) void k_quant_query(const QT* __restrict__ q, const float* __restrict__ w,
+                                                     uint8_t* __restrict__ q8, float* __restrict__ c) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int h = tid >> 3, d0 = (tid & 7) * 8;  // 8 lanes per head, 8 dims per lane
+  const QT* p = q + ((int64_t)r * 32 + h) * 64 + d0;
+  float v[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = load_as_f32(p + i);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  const float sq = amax / 448.0f;
+  uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t code = (sq != 0.0f) ? e4m3_encode(v[i] / sq) : 0u;
+    wd[i >> 2] |= code << (8 * (i & 3));
+  }
+  *reinterpret_cast<uint2*>(q8 + ((int64_t)r * 32 + h) * 64 + d0) = make_uint2(wd[0], wd[1]);
+  if ((tid & 7) == 0) c[(int64_t)r * 32 + h] = w[(int64_t)r * 32 + h] * sq;
+}
+
+template <int NKT>
+__global__ __launch_bounds__(256) void k_score_fp8_rows(int T, int64_t ncols, const uint8_t* __restrict__ q8,
+                                                        const float* __restrict__ cst, const uint8_t* __restrict__ k8,
+                                                        const float* __restrict__ ks, int64_t n_max,
+                                                        const int32_t* __restrict__ n_keys,
+                                                        const int32_t* __restrict__ q_limit,
+                                                        float* __restrict__ scores, uint32_t* __restrict__ hist) {
+  static_assert(NKT % 4 == 0, "key tiles come in groups of 4");
+  __shared__ __align__(16) uint8_t s_q8[kRowTile * 32 * 64];
+  __shared__ __align__(16) float s_c[kRowTile * 32];
+  __shared__ int64_t s_lim[kRowTile];
+  __shared__ uint32_t s_h[kRowTile * kHistBins / 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int tiles_per_seq = (T + kRowTile - 1) / kRowTile;
+  const int b = blockIdx.y / tiles_per_seq;
+  const int t0 = (blockIdx.y % tiles_per_seq) * kRowTile;
+  const int nrows = (T - t0 < kRowTile) ? T - t0 : kRowTile;  // uniform per block
+  const int64_t r0 = (int64_t)b * T + t0;
+  const int64_t c0 = (int64_t)blockIdx.x * (kScoreWaves * NKT * 32);
+
+  // rows' operands and limits into LDS (rows past T are never used)
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(q8 + r0 * 32 * 64);
+    for (int i = tid; i < nrows * 32 * 64 / 16; i += 256) reinterpret_cast<uint4*>(s_q8)[i] = src[i];
+    for (int i = tid; i < nrows * 32; i += 256) s_c[i] = cst[r0 * 32 + i];
+    if (tid < nrows) {
+      int64_t nk = n_keys[b];
+      int64_t lim = (nk < n_max ? nk : n_max) - 1;
+      if (q_limit && q_limit[r0 + tid] < lim) lim = q_limit[r0 + tid];
+      s_lim[tid] = lim;
+    }
+    if (hist)
+      for (int i = tid; i < kRowTile * kHistBins / 2; i += 256) s_h[i] = 0;
+  }
+  __syncthreads();
+
+  const uint8_t* kb = k8 + (int64_t)b * n_max * 64 + half * 32;
+  const float* ksb = ks + (int64_t)b * n_max;
+  for (int g = 0; g < NKT / 4; ++g) {
+    v8i Bt[4];
+    float skv[4];
+    int64_t col[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      col[u] = c0 + (int64_t)(wave + kScoreWaves * (4 * g + u)) * 32 + (lane & 31);
+      const int64_t rr = col[u] < ncols ? col[u] : 0;  // clamped, masked below
+      const v4i* src = reinterpret_cast<const v4i*>(kb + rr * 64);
+      const v4i x0 = src[0], x1 = src[1];
+      Bt[u][0] = x0[0]; Bt[u][1] = x0[1]; Bt[u][2] = x0[2]; Bt[u][3] = x0[3];
+      Bt[u][4] = x1[0]; Bt[u][5] = x1[1]; Bt[u][6] = x1[2]; Bt[u][7] = x1[3];
+      skv[u] = ksb[rr];
+    }
+    for (int t = 0; t < nrows; ++t) {
+      const uint4* qa = reinterpret_cast<const uint4*>(s_q8 + (t * 32 + (lane & 31)) * 64 + half * 32);
+      const uint4 a0 = qa[0], a1 = qa[1];
+      v8i A;
+      A[0] = a0.x; A[1] = a0.y; A[2] = a0.z; A[3] = a0.w; A[4] = a1.x; A[5] = a1.y; A[6] = a1.z; A[7] = a1.w;
+      float cvec[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 cc = *reinterpret_cast<const float4*>(&s_c[t * 32 + 8 * j + 4 * half]);
+        cvec[4 * j] = cc.x; cvec[4 * j + 1] = cc.y; cvec[4 * j + 2] = cc.z; cvec[4 * j + 3] = cc.w;
+      }
+      const int64_t lim = s_lim[t];
+      float* srow = scores + (r0 + t) * ncols;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v16f acc = {};
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bt[u], acc, 0, 0, 0, 0, 0, 0);
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) part = fmaf(cvec[j], acc[j], part);
+        const float total = part + __shfl_xor(part, 32);
+        const float sc = (col[u] <= lim) ? total * skv[u] : kNegInf;
+        if (half == 0 && col[u] < ncols) {
+          srow[col[u]] = sc;
+          if (hist && visible(sc)) {
+            const uint32_t bin = hist_bin(order_key(sc));
+            atomicAdd(&s_h[t * (kHistBins / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
+          }
+        }
+      }
+    }
+  }
+  if (hist) {
+    __syncthreads();
+    for (int i = tid; i < nrows * (kHistBins / 2); i += 256) {
+      const uint32_t v = s_h[i];
+      if (v) {
+        const int t = i / (kHistBins / 2), bp = i % (kHistBins / 2);
+        uint32_t* hrow = hist + (r0 + t) * kHistBins;
+        if (v & 0xFFFFu) atomicAdd(&hrow[2 * bp], v & 0xFFFFu);
+        if (v >> 16) atomicAdd(&hrow[2 * bp + 1], v >> 16);
+      }
+    }
+  }
+}
+
+int score_rows_tiled(const ScoreArgs& a) {
+  return a.prec == 1 && a.cand == nullptr && a.key_div == 1 && a.T >= kRowTile && a.qstage != nullptr;
+}
+
 int score_cols_per_block(int64_t ncols) {
   // tiles per wave: long rows stream 2048 keys per block (128 KB of keys), short rows
   // use smaller blocks so that the chip still fills
@@ -241,6 +383,21 @@ static void launch_fp8_tpw(const ScoreArgs& a, hipStream_t st) {
 
 int launch_score(const ScoreArgs& a, hipStream_t st) {
   const int R = a.B * a.T;
+  if (score_rows_tiled(a)) {
+    uint8_t* q8 = a.qstage;
+    float* cst = reinterpret_cast<float*>(a.qstage + (size_t)R * 32 * 64);
+    if (a.q_bf16)
+      hipLaunchKernelGGL(k_quant_query<uint16_t>, dim3(R), dim3(256), 0, st, (const uint16_t*)a.q, a.w, q8, cst);
+    else
+      hipLaunchKernelGGL(k_quant_query<float>, dim3(R), dim3(256), 0, st, (const float*)a.q, a.w, q8, cst);
+    constexpr int kNKT = 32;
+    const int64_t cpb = kScoreWaves * kNKT * 32;
+    dim3 g((unsigned)((a.ncols + cpb - 1) / cpb), (unsigned)(a.B * ((a.T + kRowTile - 1) / kRowTile)));
+    hipLaunchKernelGGL(k_score_fp8_rows<kNKT>, g, dim3(256), 0, st, a.T, a.ncols, (const uint8_t*)q8,
+                       (const float*)cst, (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.scores,
+                       a.hist);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   if (a.prec == 0) {
     dim3 g((unsigned)((a.ncols + 255) / 256), R);
     const size_t sh = sizeof(float) * ((size_t)a.H * a.dk + a.H);
