@@ -186,6 +186,77 @@ def cpu_baseline(wl, seqs):
                        (seqs, wl.B, wl.N, len(wl.modes), dt))
 
 
+def run_prefill(args):
+    """Chunked prefill (262144 cached entries + 4096 new tokens, one sequence): a step is
+    the whole path for the new tokens - FP4 (GIVEN scales) and E4M3 append of their main KV
+    and indexer keys, causal fp8 scoring of every new token against all visible entries,
+    Top-512 per token, sparse attention of 64 bf16 heads per token."""
+    wl = workloads.WORKLOADS["prefill"]
+    Nc, T, D, dk = wl.N, wl.T, wl.D, wl.dk
+    n_max = Nc + T
+    log("building the cached part (%d entries) ..." % Nc)
+    codes = torch.zeros((1, n_max, D // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((1, D), dtype=torch.float32, device="cuda")
+    k8 = torch.zeros((1, n_max, dk), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((1, n_max), dtype=torch.float32, device="cuda")
+    csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, torch.from_numpy(wl.main_kv(0)[None]).cuda(), codes, scales)
+    csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, torch.from_numpy(wl.index_keys(0)[None]).cuda(), k8, ks)
+    new = torch.from_numpy(wl.new_kv()).to(torch.bfloat16).cuda()
+    newk = torch.from_numpy(wl.new_index_keys()).cuda()
+    n0 = torch.tensor([Nc], dtype=torch.int32, device="cuda")
+    n_keys = torch.tensor([n_max], dtype=torch.int32, device="cuda")
+    q_limit = (Nc + torch.arange(T, dtype=torch.int32, device="cuda"))[None].contiguous()
+    q = torch.from_numpy(wl.index_query()).to(torch.bfloat16).cuda()
+    w = torch.from_numpy(wl.head_weights()).cuda()
+    qa = torch.from_numpy(wl.attn_query()).to(torch.bfloat16).cuda()
+    idx = torch.empty((1, T, wl.K), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, T, wl.Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, T, wl.Hq), dtype=torch.float32, device="cuda")
+
+    def step():
+        csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, new, codes, scales, scale_policy=csa2.SCALE_GIVEN, n0=n0)
+        csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, newk, k8, ks, n0=n0)
+        csa2.index_topk(csa2.PREC_FP8, q, w, k8, ks, n_keys, wl.K, q_limit=q_limit, idx=idx)
+        csa2.sparse_attend(qa, codes, scales, idx, wl.softmax_scale, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    # the scoring kernel alone: events around back-to-back csa2_index_score calls (each is
+    # the per-row query quantisation plus the many-row score kernel)
+    sc = torch.empty((1, T, n_max), dtype=torch.float32, device="cuda")
+    reps = 5
+    csa2.index_score(csa2.PREC_FP8, q, w, k8, ks, n_keys, q_limit=q_limit, scores=sc)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        csa2.index_score(csa2.PREC_FP8, q, w, k8, ks, n_keys, q_limit=q_limit, scores=sc)
+    e1.record()
+    torch.cuda.synchronize()
+    score_ms = e0.elapsed_time(e1) / reps
+    pairs = sum(Nc + t + 1 for t in range(T))
+    flops = 2 * wl.H * dk * pairs
+    tflops = flops / (score_ms / 1e3) / 1e12
+    res = {
+        "metric": "CSA2 chunked-prefill new tokens/s", "value": round(T / (ms_step / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": "prefill: 262144 cached + 4096 new tokens, causal, indexer 32x64 E4M3, Top-512, "
+                               "FP4 E2M1 main KV D=512, 64 heads bf16", "global_batch": 1, "seq_len": n_max},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 5000.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 5000.0, 4), "traffic": None,
+                     "kernel": "k_quant_query + k_score_fp8_rows (one csa2_index_score call)",
+                     "kernel_ms_mean": round(score_ms, 4), "flops_per_launch": flops},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +266,8 @@ def main():
     ap.add_argument("--score-reps", type=int, default=60)
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="group128k", choices=["group128k", "prefill"],
+                    help="group128k: the 128K decode group (the headline); prefill: the chunked-prefill path")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -208,6 +281,9 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.workload == "prefill":
+        run_prefill(args)
         return
     wl = workloads.WORKLOADS["group128k"]
     log("building cache (%d copies) ..." % args.copies)

@@ -20,7 +20,10 @@ HEADERS = ["common.hpp", "launch.hpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(HERE, "..", "include")]
-DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA results in ordinary VGPRs: the epilogues read every accumulator with VALU ops, and
+# accumulators in AGPRs would cost one v_accvgpr_read per element first.
+DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str) -> str:

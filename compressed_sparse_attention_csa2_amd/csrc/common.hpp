@@ -167,6 +167,13 @@ __device__ __forceinline__ uint32_t wave_reserve(uint32_t* counter, bool pred) {
   base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
   return base + lanes_below(mask);
 }
+// the value of lane l ^ 32 (v_permlane32_swap exchanges the two 32-lane halves; a VALU
+// op, unlike a shuffle through LDS)
+__device__ __forceinline__ float swap_halves(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  const auto pr = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? pr[0] : pr[1]);
+}
 __device__ __forceinline__ float lane_read(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }

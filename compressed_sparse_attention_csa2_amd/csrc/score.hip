@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
 // runs all rows of the tile against them, so every key tile is read once per row tile.
 // The per-row first-level Top-K histogram is kept in LDS with 16-bit counters packed in
 // pairs (a block adds at most 128 x NKT <= 4096 to one bin of one row).
-constexpr int kRowTile = 8;
+constexpr int kRowTile = 8;  // rows per tile of the many-row path (minimum T)
 
 // q [R][32][64] -> E4M3 codes q8 [R][32][64] and c [R][32] = w * sq, with sq = absmax/448
 // over the head's 64 values: the same arithmetic as quantize_query_operand.
@@ -254,31 +254,44 @@ __global__ __launch_bounds__(256) void k_quant_query(const QT* __restrict__ q, c
   if ((tid & 7) == 0) c[(int64_t)r * 32 + h] = w[(int64_t)r * 32 + h] * sq;
 }
 
-template <int NKT>
-__global__ __launch_bounds__(256) void k_score_fp8_rows(int T, int64_t ncols, const uint8_t* __restrict__ q8,
-                                                        const float* __restrict__ cst, const uint8_t* __restrict__ k8,
-                                                        const float* __restrict__ ks, int64_t n_max,
-                                                        const int32_t* __restrict__ n_keys,
-                                                        const int32_t* __restrict__ q_limit,
-                                                        float* __restrict__ scores, uint32_t* __restrict__ hist) {
-  static_assert(NKT % 4 == 0, "key tiles come in groups of 4");
-  __shared__ __align__(16) uint8_t s_q8[kRowTile * 32 * 64];
-  __shared__ __align__(16) float s_c[kRowTile * 32];
-  __shared__ int64_t s_lim[kRowTile];
-  __shared__ uint32_t s_h[kRowTile * kHistBins / 2];
+// TT rows per tile, NW waves per block, NKT key tiles of 32 per wave (groups of 4 tiles;
+// with DB the next group's keys are loaded while the current one runs).
+template <int TT, int NW, int NKT, bool DB>
+__global__ __launch_bounds__(64 * NW) void k_score_fp8_rows(int T, int64_t ncols, const uint8_t* __restrict__ q8,
+                                                            const float* __restrict__ cst,
+                                                            const uint8_t* __restrict__ k8,
+                                                            const float* __restrict__ ks, int64_t n_max,
+                                                            const int32_t* __restrict__ n_keys,
+                                                            const int32_t* __restrict__ q_limit,
+                                                            float* __restrict__ scores, uint32_t* __restrict__ hist) {
+  static_assert(NKT % 4 == 0 && (!DB || (NKT / 4) % 2 == 0), "key tiles come in (pairs of) groups of 4");
+  constexpr int NT = 64 * NW;
+  constexpr int kQRow = 80;  // bytes per head row in LDS: 64 + 16 padding, so that the 16-byte
+                             // operand reads of 16 lanes fall on distinct banks
+  __shared__ __align__(16) uint8_t s_q8[TT * 32 * kQRow];
+  __shared__ __align__(16) float s_c[TT * 32];
+  __shared__ int64_t s_lim[TT];
+  __shared__ uint32_t s_h[TT * kHistBins / 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-  const int tiles_per_seq = (T + kRowTile - 1) / kRowTile;
-  const int b = blockIdx.y / tiles_per_seq;
-  const int t0 = (blockIdx.y % tiles_per_seq) * kRowTile;
-  const int nrows = (T - t0 < kRowTile) ? T - t0 : kRowTile;  // uniform per block
+  // grid x = row tiles (fastest), y = key ranges: the blocks in flight at once share a few
+  // key ranges, which stay in L2 while every row tile reads them
+  const int tiles_per_seq = (T + TT - 1) / TT;
+  const int b = blockIdx.x / tiles_per_seq;
+  const int t0 = (blockIdx.x % tiles_per_seq) * TT;
+  const int nrows = (T - t0 < TT) ? T - t0 : TT;  // uniform per block
   const int64_t r0 = (int64_t)b * T + t0;
-  const int64_t c0 = (int64_t)blockIdx.x * (kScoreWaves * NKT * 32);
+  const int64_t c0 = (int64_t)blockIdx.y * (NW * NKT * 32);
 
-  // rows' operands and limits into LDS (rows past T are never used)
+  // rows' operands and limits into LDS (rows past T: zero operands, never stored)
   {
     const uint4* src = reinterpret_cast<const uint4*>(q8 + r0 * 32 * 64);
-    for (int i = tid; i < nrows * 32 * 64 / 16; i += 256) reinterpret_cast<uint4*>(s_q8)[i] = src[i];
-    for (int i = tid; i < nrows * 32; i += 256) s_c[i] = cst[r0 * 32 + i];
+    for (int i = tid; i < TT * 32 * 64 / 16; i += NT) {
+      const int hr = i >> 2, part = i & 3;  // head row (t * 32 + h), 16-byte piece
+      reinterpret_cast<uint4*>(s_q8 + hr * kQRow)[part] =
+          (i < nrows * 32 * 64 / 16) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    for (int i = tid; i < TT * 32; i += NT) s_c[i] = (i < nrows * 32) ? cst[r0 * 32 + i] : 0.0f;
+    if (tid < TT && tid >= nrows) s_lim[tid] = -1;
     if (tid < nrows) {
       int64_t nk = n_keys[b];
       int64_t lim = (nk < n_max ? nk : n_max) - 1;
@@ -286,28 +299,32 @@ __global__ __launch_bounds__(256) void k_score_fp8_rows(int T, int64_t ncols, co
       s_lim[tid] = lim;
     }
     if (hist)
-      for (int i = tid; i < kRowTile * kHistBins / 2; i += 256) s_h[i] = 0;
+      for (int i = tid; i < TT * kHistBins / 2; i += NT) s_h[i] = 0;
   }
   __syncthreads();
 
   const uint8_t* kb = k8 + (int64_t)b * n_max * 64 + half * 32;
   const float* ksb = ks + (int64_t)b * n_max;
-  for (int g = 0; g < NKT / 4; ++g) {
-    v8i Bt[4];
-    float skv[4];
+  struct KeyGroup {
+    v8i B[4];
+    float sk[4];
     int64_t col[4];
+  };
+  auto load_group = [&](int g, KeyGroup& kg) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      col[u] = c0 + (int64_t)(wave + kScoreWaves * (4 * g + u)) * 32 + (lane & 31);
-      const int64_t rr = col[u] < ncols ? col[u] : 0;  // clamped, masked below
+      kg.col[u] = c0 + (int64_t)(wave + NW * (4 * g + u)) * 32 + (lane & 31);
+      const int64_t rr = kg.col[u] < ncols ? kg.col[u] : 0;  // clamped, masked below
       const v4i* src = reinterpret_cast<const v4i*>(kb + rr * 64);
       const v4i x0 = src[0], x1 = src[1];
-      Bt[u][0] = x0[0]; Bt[u][1] = x0[1]; Bt[u][2] = x0[2]; Bt[u][3] = x0[3];
-      Bt[u][4] = x1[0]; Bt[u][5] = x1[1]; Bt[u][6] = x1[2]; Bt[u][7] = x1[3];
-      skv[u] = ksb[rr];
+      kg.B[u][0] = x0[0]; kg.B[u][1] = x0[1]; kg.B[u][2] = x0[2]; kg.B[u][3] = x0[3];
+      kg.B[u][4] = x1[0]; kg.B[u][5] = x1[1]; kg.B[u][6] = x1[2]; kg.B[u][7] = x1[3];
+      kg.sk[u] = ksb[rr];
     }
+  };
+  auto run_group = [&](const KeyGroup& kg) {
     for (int t = 0; t < nrows; ++t) {
-      const uint4* qa = reinterpret_cast<const uint4*>(s_q8 + (t * 32 + (lane & 31)) * 64 + half * 32);
+      const uint4* qa = reinterpret_cast<const uint4*>(s_q8 + (t * 32 + (lane & 31)) * kQRow + half * 32);
       const uint4 a0 = qa[0], a1 = qa[1];
       v8i A;
       A[0] = a0.x; A[1] = a0.y; A[2] = a0.z; A[3] = a0.w; A[4] = a1.x; A[5] = a1.y; A[6] = a1.z; A[7] = a1.w;
@@ -319,17 +336,23 @@ __global__ __launch_bounds__(256) void k_score_fp8_rows(int T, int64_t ncols, co
       }
       const int64_t lim = s_lim[t];
       float* srow = scores + (r0 + t) * ncols;
+      // the four contractions first (independent accumulators, so they issue back to
+      // back), then their epilogues
+      v16f acc[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        v16f acc = {};
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bt[u], acc, 0, 0, 0, 0, 0, 0);
+        acc[u] = (v16f){};
+        acc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, kg.B[u], acc[u], 0, 0, 0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
         float part = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) part = fmaf(cvec[j], acc[j], part);
-        const float total = part + __shfl_xor(part, 32);
-        const float sc = (col[u] <= lim) ? total * skv[u] : kNegInf;
-        if (half == 0 && col[u] < ncols) {
-          srow[col[u]] = sc;
+        for (int j = 0; j < 16; ++j) part = fmaf(cvec[j], acc[u][j], part);
+        const float total = part + swap_halves(part);
+        const float sc = (kg.col[u] <= lim) ? total * kg.sk[u] : kNegInf;
+        if (half == 0 && kg.col[u] < ncols) {
+          srow[kg.col[u]] = sc;
           if (hist && visible(sc)) {
             const uint32_t bin = hist_bin(order_key(sc));
             atomicAdd(&s_h[t * (kHistBins / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
@@ -337,10 +360,26 @@ __global__ __launch_bounds__(256) void k_score_fp8_rows(int T, int64_t ncols, co
         }
       }
     }
+  };
+  if (DB) {
+    KeyGroup g0, g1;
+    load_group(0, g0);
+    for (int g = 0; g < NKT / 4; g += 2) {
+      load_group(g + 1, g1);
+      run_group(g0);
+      if (g + 2 < NKT / 4) load_group(g + 2, g0);
+      run_group(g1);
+    }
+  } else {
+    for (int g = 0; g < NKT / 4; ++g) {
+      KeyGroup kg;
+      load_group(g, kg);
+      run_group(kg);
+    }
   }
   if (hist) {
     __syncthreads();
-    for (int i = tid; i < nrows * (kHistBins / 2); i += 256) {
+    for (int i = tid; i < nrows * (kHistBins / 2); i += NT) {
       const uint32_t v = s_h[i];
       if (v) {
         const int t = i / (kHistBins / 2), bp = i % (kHistBins / 2);
@@ -350,6 +389,14 @@ __global__ __launch_bounds__(256) void k_score_fp8_rows(int T, int64_t ncols, co
       }
     }
   }
+}
+
+template <int TT, int NW, int NKT, bool DB>
+static void launch_rows(const ScoreArgs& a, const uint8_t* q8, const float* cst, hipStream_t st) {
+  const int64_t cpb = NW * NKT * 32;
+  dim3 g((unsigned)(a.B * ((a.T + TT - 1) / TT)), (unsigned)((a.ncols + cpb - 1) / cpb));
+  hipLaunchKernelGGL((k_score_fp8_rows<TT, NW, NKT, DB>), g, dim3(64 * NW), 0, st, a.T, a.ncols, q8, cst,
+                     (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.scores, a.hist);
 }
 
 int score_rows_tiled(const ScoreArgs& a) {
@@ -390,12 +437,9 @@ int launch_score(const ScoreArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(k_quant_query<uint16_t>, dim3(R), dim3(256), 0, st, (const uint16_t*)a.q, a.w, q8, cst);
     else
       hipLaunchKernelGGL(k_quant_query<float>, dim3(R), dim3(256), 0, st, (const float*)a.q, a.w, q8, cst);
-    constexpr int kNKT = 32;
-    const int64_t cpb = kScoreWaves * kNKT * 32;
-    dim3 g((unsigned)((a.ncols + cpb - 1) / cpb), (unsigned)(a.B * ((a.T + kRowTile - 1) / kRowTile)));
-    hipLaunchKernelGGL(k_score_fp8_rows<kNKT>, g, dim3(256), 0, st, a.T, a.ncols, (const uint8_t*)q8,
-                       (const float*)cst, (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.scores,
-                       a.hist);
+    // 8 rows x 4096 keys per block, single-buffered key groups: the variant measured
+    // fastest (double buffering or 16-row tiles cost occupancy and ran slower)
+    launch_rows<kRowTile, 4, 32, false>(a, q8, cst, st);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   if (a.prec == 0) {

@@ -52,7 +52,62 @@ __global__ __launch_bounds__(256) void k_topk_hist(int64_t ncols, const float* _
   }
 }
 
-template <bool CAND>
+// The threshold bin of a row from its first-level histogram: beta, the visible scores
+// above it, keff = min(K, visible).  Block-wide (256 threads, thread t owns bins 8t..8t+7);
+// result in s_misc[0] (visible total), [1] (beta; kHistBins if nothing is visible),
+// [4] (above).
+__device__ __forceinline__ void row_threshold(const uint32_t* __restrict__ hrow, int K, uint32_t* sh4,
+                                              uint32_t* s_misc) {
+  const int tid = threadIdx.x;
+  uint32_t hb[8];
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hb[i] = hrow[tid * 8 + i];
+    local += hb[i];
+  }
+  const uint32_t suf = block_suffix_sum(local, sh4);  // visible scores in bins >= 8*tid
+  if (tid == 0) {
+    s_misc[0] = suf;
+    s_misc[1] = kHistBins;
+    s_misc[4] = 0;
+  }
+  __syncthreads();
+  const uint32_t total = s_misc[0];
+  const uint32_t keff = total < (uint32_t)K ? total : (uint32_t)K;
+  if (keff > 0 && suf >= keff && suf - local < keff) {
+    uint32_t acc = suf - local;
+    for (int i = 7; i >= 0; --i) {
+      if (acc + hb[i] >= keff) {
+        s_misc[1] = tid * 8 + i;
+        s_misc[4] = acc;  // visible scores in bins above beta
+        break;
+      }
+      acc += hb[i];
+    }
+  }
+  __syncthreads();
+}
+
+// Many rows (chunked prefill): one block per row derives the row's threshold once, so
+// that the filter blocks read 16 bytes of it instead of the 8 KB histogram each.
+__global__ __launch_bounds__(kSelThreads) void k_topk_threshold(int K, const uint32_t* __restrict__ hist,
+                                                                RowCtl* __restrict__ ctl) {
+  __shared__ uint32_t sh4[4];
+  __shared__ uint32_t s_misc[8];
+  const int r = blockIdx.x;
+  row_threshold(hist + (int64_t)r * kHistBins, K, sh4, s_misc);
+  if (threadIdx.x == 0) {
+    const uint32_t total = s_misc[0];
+    ctl[r].beta = s_misc[1];
+    ctl[r].above = s_misc[4];
+    ctl[r].keff = total < (uint32_t)K ? total : (uint32_t)K;
+  }
+}
+
+// CTL: the row's threshold was computed by k_topk_threshold (read ctl); otherwise every
+// block derives it from the histogram and block 0 of the row writes ctl.
+template <bool CAND, bool CTL>
 __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float* __restrict__ scores,
                                                      const int32_t* __restrict__ cand, int K,
                                                      const uint32_t* __restrict__ hist, uint32_t* __restrict__ hist2,
@@ -84,44 +139,23 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
     if (c >= ncols) sv[i] = kNegInf;
   }
 
-  // threshold bin (thread t owns bins 8t .. 8t+7)
-  const uint32_t* hrow = hist + (int64_t)r * kHistBins;
-  uint32_t hb[8];
-  uint32_t local = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    hb[i] = hrow[tid * 8 + i];
-    local += hb[i];
-  }
+  // threshold bin
   for (int i = tid; i < kHistBins; i += kSelThreads) lhist2[i] = 0;
-  const uint32_t suf = block_suffix_sum(local, sh4);  // visible scores in bins >= 8*tid
-  if (tid == 0) {
-    s_misc[0] = suf;
-    s_misc[1] = kHistBins;
-    s_misc[4] = 0;
-  }
-  __syncthreads();
-  const uint32_t total = s_misc[0];
-  const uint32_t keff = total < (uint32_t)K ? total : (uint32_t)K;
-  if (keff > 0 && suf >= keff && suf - local < keff) {
-    uint32_t acc = suf - local;
-    for (int i = 7; i >= 0; --i) {
-      if (acc + hb[i] >= keff) {
-        s_misc[1] = tid * 8 + i;
-        s_misc[4] = acc;  // visible scores in bins above beta
-        break;
-      }
-      acc += hb[i];
+  uint32_t beta;
+  if (CTL) {
+    beta = ctl[r].beta;
+    __syncthreads();  // lhist2 zeroed before any block thread adds to it
+  } else {
+    row_threshold(hist + (int64_t)r * kHistBins, K, sh4, s_misc);
+    beta = s_misc[1];
+    if (blockIdx.x == 0 && tid == 0) {
+      const uint32_t total = s_misc[0];
+      ctl[r].beta = beta;
+      ctl[r].above = s_misc[4];
+      ctl[r].keff = total < (uint32_t)K ? total : (uint32_t)K;
     }
   }
-  __syncthreads();
-  const uint32_t beta = s_misc[1];
   const int nreg = (int)gridDim.x;
-  if (blockIdx.x == 0 && tid == 0) {
-    ctl[r].beta = beta;
-    ctl[r].above = s_misc[4];
-    ctl[r].keff = keff;
-  }
   if (beta >= (uint32_t)kHistBins) {  // nothing visible in this row (uniform per block)
     if (tid == 0) cnt[(int64_t)r * nreg + blockIdx.x] = 0;
     return;
@@ -206,15 +240,24 @@ int launch_topk_hist(int R, int64_t ncols, const float* scores, const int32_t* c
 
 int topk_regions(int64_t ncols) { return (int)((ncols + kFilterColsPerBlock - 1) / kFilterColsPerBlock); }
 
+// Rows from which the threshold is computed once per row in its own kernel rather than
+// in every filter block (many rows: the histogram re-reads would cost more than a launch).
+constexpr int kThresholdKernelRows = 64;
+
 int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const uint32_t* hist,
                        uint32_t* hist2, RowCtl* ctl, uint2* candbuf, uint32_t* cnt, hipStream_t st) {
   dim3 g((unsigned)topk_regions(ncols), R);
-  if (cand)
-    hipLaunchKernelGGL(k_topk_filter<true>, g, dim3(kSelThreads), 0, st, ncols, scores, cand, K, hist, hist2, ctl,
-                       candbuf, cnt);
-  else
-    hipLaunchKernelGGL(k_topk_filter<false>, g, dim3(kSelThreads), 0, st, ncols, scores, cand, K, hist, hist2, ctl,
-                       candbuf, cnt);
+  const bool pre = R >= kThresholdKernelRows;
+  if (pre) hipLaunchKernelGGL(k_topk_threshold, dim3(R), dim3(kSelThreads), 0, st, K, hist, ctl);
+#define CSA2_FILTER(C, P)                                                                                      \
+  hipLaunchKernelGGL((k_topk_filter<C, P>), g, dim3(kSelThreads), 0, st, ncols, scores, cand, K, hist, hist2, ctl, \
+                     candbuf, cnt)
+  if (cand) {
+    if (pre) CSA2_FILTER(true, true); else CSA2_FILTER(true, false);
+  } else {
+    if (pre) CSA2_FILTER(false, true); else CSA2_FILTER(false, false);
+  }
+#undef CSA2_FILTER
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
