@@ -73,7 +73,7 @@ def layer_inputs(wl):
 
 
 def algorithmic_bytes(wl):
-    """Bytes the group must move at least once (see DESIGN.md): per indexing layer the key
+    """Bytes the group must move at least once: per indexing layer the key
     scan (64 B key + 4 B scale per entry) and per layer the gathered FP4 rows, their
     scales, the query, the output and the indices."""
     B, N, K, D, Hq = wl.B, wl.N, wl.K, wl.D, wl.Hq
@@ -257,6 +257,108 @@ def run_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+def run_full64k(args):
+    """The single-layer 64K decode configuration: a Full layer over 16 sequences x 65536
+    entries (score, Top-512, FP4 gather + attention), with 3 rotated cache copies."""
+    wl = workloads.WORKLOADS["full64k"]
+    log("building cache (%d copies) ..." % args.copies)
+    caches = build_device_cache(wl, args.copies)
+    layers = layer_inputs(wl)
+    plans = [csa2.GroupPlan([dict(L) for L in layers],
+                            csa2.GroupCache(c["n_keys"], c["codes"], c["scales"], c["k8"], c["ks"], wl.K,
+                                            wl.softmax_scale), out_dtype=torch.bfloat16) for c in caches]
+    for s in range(args.warmup):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    alg = algorithmic_bytes(wl)
+    gbs = alg / (ms_step / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "CSA2 decode queries/s at 64K context (single Full layer)", "value": round(wl.B / (ms_step / 1e3), 1),
+        "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": "full64k: Full decode, B=16, N=65536, indexer 32x64 E4M3, Top-512, FP4 E2M1 main KV "
+                               "D=512, 64 heads bf16", "global_batch": wl.B, "seq_len": wl.N},
+        "step_algorithmic_bytes": alg, "step_achieved_GBps": round(gbs, 1),
+        "step_pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
+
+
+def run_hier1m(args):
+    """The 1M-entry two-level configuration (one sequence): coarse keys (64-entry block
+    means, built once, not timed) -> score 16384 coarse keys -> top-256 blocks -> exact
+    scores of their 16384 entries -> Top-1024 -> attention over the 1024 entries."""
+    wl = workloads.WORKLOADS["hier1m"]
+    n = wl.N
+    k8 = torch.empty((1, n, wl.dk), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    codes = torch.empty((1, n, wl.D // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((1, wl.D), dtype=torch.float32, device="cuda")
+    csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, torch.from_numpy(wl.index_keys(0)[None]).cuda(), k8, ks)
+    csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, torch.from_numpy(wl.main_kv(0)[None]).cuda(), codes, scales)
+    nk = torch.tensor([n], dtype=torch.int32, device="cuda")
+    kb, kbs = csa2.coarse_keys(k8, ks, nk, wl.coarse_block)
+    q = torch.from_numpy(wl.index_query()).to(torch.bfloat16).cuda()
+    w = torch.from_numpy(wl.head_weights()).cuda()
+    qa = torch.from_numpy(wl.attn_query()).to(torch.bfloat16).cuda()
+    out = torch.empty((1, 1, wl.Hq, wl.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, 1, wl.Hq), dtype=torch.float32, device="cuda")
+
+    def step():
+        idx = csa2.hier_select(q, w, k8, ks, kb, kbs, nk, wl.coarse_block, wl.coarse_topk, wl.K)
+        csa2.sparse_attend(qa, codes, scales, idx, wl.softmax_scale, out=out, lse=lse)
+
+    # one query's step is ~11 short launches: the host's launch rate, not the GPU, would
+    # set the pace, so the step is captured once into a HIP graph and replayed
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    # the flat alternative on the same cache: one Full layer (scan all 2^20 keys, Top-1024,
+    # attention), also graph-replayed
+    layer = dict(mode="full", q_idx=q, w=w, q_attn=qa)
+    plan = csa2.GroupPlan([layer], csa2.GroupCache(nk, codes, scales, k8, ks, wl.K, wl.softmax_scale),
+                          out_dtype=torch.bfloat16)
+    for _ in range(2):
+        plan.run()
+    torch.cuda.synchronize()
+    gflat = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gflat):
+        plan.run()
+    for _ in range(args.warmup):
+        gflat.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        gflat.replay()
+    torch.cuda.synchronize()
+    flat_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    nb = n // wl.coarse_block
+    alg = nb * (wl.dk + 4) + wl.coarse_topk * wl.coarse_block * (wl.dk + 4) + wl.K * (wl.D // 2 + 4) + \
+        wl.Hq * wl.D * 2 * 2
+    print(json.dumps({
+        "metric": "CSA2 decode queries/s at 1M context (two-level indexer)", "value": round(1.0 / (ms_step / 1e3), 1),
+        "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": "hier1m: B=1, N=2^20, coarse blocks of 64, top-256 blocks, Top-1024, FP4 E2M1 main KV "
+                               "D=512, 64 heads bf16", "global_batch": 1, "seq_len": n, "launch": "hip graph replay"},
+        "step_algorithmic_bytes": alg, "flat_full_layer_ms_per_step": round(flat_ms, 5),
+        "flat_scan_at_hbm_peak_ms": round(n * (wl.dk + 4) / (HBM_PEAK_GBS * 1e9) * 1e3, 5)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,8 +368,9 @@ def main():
     ap.add_argument("--score-reps", type=int, default=60)
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="group128k", choices=["group128k", "prefill"],
-                    help="group128k: the 128K decode group (the headline); prefill: the chunked-prefill path")
+    ap.add_argument("--workload", default="group128k", choices=["group128k", "prefill", "full64k", "hier1m"],
+                    help="group128k: the 128K decode group (the headline; default); prefill: the chunked-prefill "
+                         "path; full64k: one Full layer at 64K; hier1m: the two-level indexer at 1M")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -284,6 +387,12 @@ def main():
         return
     if args.workload == "prefill":
         run_prefill(args)
+        return
+    if args.workload == "full64k":
+        run_full64k(args)
+        return
+    if args.workload == "hier1m":
+        run_hier1m(args)
         return
     wl = workloads.WORKLOADS["group128k"]
     log("building cache (%d copies) ..." % args.copies)

@@ -160,6 +160,13 @@ ScoreArgs score_args(int prec, int B, int T, int H, int dk, const void* q, int q
   return a;
 }
 
+// filter + finalize
+int select_topk(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const TopkWs& t,
+                int32_t* idx_out, float* val_out, hipStream_t st) {
+  if (launch_topk_filter(R, ncols, scores, cand, K, t.hist, t.hist2, t.ctl, t.cand, t.cnt, st)) return -1;
+  return launch_topk_finalize(R, ncols, K, cand == nullptr, t.ctl, t.hist2, t.cand, t.cnt, idx_out, val_out, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -253,10 +260,7 @@ int csa2_topk(int B, int T, int64_t ncols, const float* scores, const int32_t* c
   hipStream_t st = S(stream);
   if (zero_topk(t, R, st)) return CSA2_ERR_DEVICE;
   if (launch_topk_hist((int)R, ncols, scores, cand, t.hist, st)) return CSA2_ERR_DEVICE;
-  if (launch_topk_filter((int)R, ncols, scores, cand, K, t.hist, t.hist2, t.ctl, t.cand, t.cnt, st))
-    return CSA2_ERR_DEVICE;
-  return dev_status(
-      launch_topk_finalize((int)R, ncols, K, cand == nullptr, t.ctl, t.hist2, t.cand, t.cnt, idx_out, val_out, st));
+  return dev_status(select_topk((int)R, ncols, scores, cand, K, t, idx_out, val_out, st));
 }
 
 size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int) {
@@ -289,10 +293,7 @@ int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_
                            t.hist, 1);
   a.qstage = qstage;
   if (launch_score(a, st)) return CSA2_ERR_DEVICE;
-  if (launch_topk_filter((int)R, ncols, scores, cand, K, t.hist, t.hist2, t.ctl, t.cand, t.cnt, st))
-    return CSA2_ERR_DEVICE;
-  return dev_status(
-      launch_topk_finalize((int)R, ncols, K, cand == nullptr, t.ctl, t.hist2, t.cand, t.cnt, idx_out, val_out, st));
+  return dev_status(select_topk((int)R, ncols, scores, cand, K, t, idx_out, val_out, st));
 }
 
 size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype) {
@@ -456,29 +457,37 @@ int csa2_hier_select(int B, int H, int dk, const void* q, int q_dtype, const flo
   rc = check_device();
   if (rc) return rc;
   Carve cv(ws);
+  // both selections' zeroed state first (one fill), then their candidate lists
+  TopkWs t1 = carve_topk_zero(cv, B);
+  TopkWs t2 = carve_topk_zero(cv, B);
+  const CandWs w1 = carve_cand(cv, B, nb);
+  const CandWs w2 = carve_cand(cv, B, C);
+  t1.cand = w1.cand; t1.cnt = w1.cnt;
+  t2.cand = w2.cand; t2.cnt = w2.cnt;
   float* cscores = cv.take<float>((size_t)B * nb);
-  TopkWs t1 = carve_topk(cv, B, nb);
   int32_t* blocks = cv.take<int32_t>((size_t)B * block_topk);
   int32_t* cand = cv.take<int32_t>((size_t)B * C);
   float* fscores = cv.take<float>((size_t)B * C);
-  TopkWs t2 = carve_topk(cv, B, C);
   hipStream_t st = S(stream);
-  if (zero_topk(t1, B, st) || zero_topk(t2, B, st)) return CSA2_ERR_DEVICE;
+  if (launch_fill_u32(t1.hist, (int64_t)(2 * topk_zero_bytes(B) / 4), 0u, st)) return CSA2_ERR_DEVICE;
   ScoreArgs a1 = score_args(CSA2_PREC_FP8, B, 1, H, dk, q, q_dtype, w, kb8, kb_scale, nb, n_keys, nullptr, nullptr,
                             nb, cscores, t1.hist, block);
   if (launch_score(a1, st)) return CSA2_ERR_DEVICE;
   int32_t* bout = block_out ? block_out : blocks;
+  // the block selection also writes the selected blocks' positions (the fine candidates)
   if (launch_topk_filter(B, nb, cscores, nullptr, block_topk, t1.hist, t1.hist2, t1.ctl, t1.cand, t1.cnt, st))
     return CSA2_ERR_DEVICE;
-  if (launch_topk_finalize(B, nb, block_topk, true, t1.ctl, t1.hist2, t1.cand, t1.cnt, bout, nullptr, st))
+  if (launch_topk_finalize(B, nb, block_topk, true, t1.ctl, t1.hist2, t1.cand, t1.cnt, bout, nullptr, st, block,
+                           n_keys, cand))
     return CSA2_ERR_DEVICE;
-  if (launch_expand_blocks(B, block_topk, block, bout, n_keys, cand, st)) return CSA2_ERR_DEVICE;
   ScoreArgs a2 = score_args(CSA2_PREC_FP8, B, 1, H, dk, q, q_dtype, w, k8, k_scale, n_max, n_keys, nullptr, cand, C,
                             fscores, t2.hist, 1);
   if (launch_score(a2, st)) return CSA2_ERR_DEVICE;
+  // the expanded candidates ascend (blocks ascending, positions within a block ascending,
+  // -1 for none), so the filtered list is in position order
   if (launch_topk_filter(B, C, fscores, cand, K, t2.hist, t2.hist2, t2.ctl, t2.cand, t2.cnt, st))
     return CSA2_ERR_DEVICE;
-  return dev_status(launch_topk_finalize(B, C, K, false, t2.ctl, t2.hist2, t2.cand, t2.cnt, idx_out, nullptr, st));
+  return dev_status(launch_topk_finalize(B, C, K, true, t2.ctl, t2.hist2, t2.cand, t2.cnt, idx_out, nullptr, st));
 }
 
 }  // extern "C"

@@ -45,7 +45,7 @@ int launch_score(const ScoreArgs& a, hipStream_t st);
 // head factors, R * (2048 + 128) bytes; used when T >= score_tiled_min_rows().
 inline size_t score_stage_bytes(int64_t R) { return (size_t)R * (32 * 64 + 32 * 4); }
 inline int score_tiled_min_rows() { return 8; }
-int score_cols_per_block(int64_t ncols);
+int score_cols_per_block(int64_t rows, int64_t ncols);
 
 // Top-K: histogram (zeroed on entry) -> filter into candidates (ctl zeroed on entry)
 // -> finalize (here, or fused into the attention kernel).
@@ -56,8 +56,11 @@ int topk_regions(int64_t ncols);
 int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const uint32_t* hist,
                        uint32_t* hist2, RowCtl* ctl, uint2* candbuf, uint32_t* cnt, hipStream_t st);
 // sorted: the candidates were filtered without a candidate map (list in position order)
+// expand_out (nullable, needs sorted): also write the selected blocks' positions (block
+// positions per selected column, -1 past n_keys[r] or for padding), [R][K * block]
 int launch_topk_finalize(int R, int64_t ncols, int K, bool sorted, const RowCtl* ctl, const uint32_t* hist2,
-                         const uint2* candbuf, const uint32_t* cnt, int32_t* idx_out, float* val_out, hipStream_t st);
+                         const uint2* candbuf, const uint32_t* cnt, int32_t* idx_out, float* val_out, hipStream_t st,
+                         int block = 0, const int32_t* n_keys = nullptr, int32_t* expand_out = nullptr);
 
 struct AttendArgs {
   int B, T, Hq, D, K;
@@ -88,7 +91,4 @@ int launch_gather_dequant(int B, int T, int K, int D, const uint8_t* codes, cons
                           const int32_t* idx, float* out, hipStream_t st);
 int launch_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int block, const uint8_t* k8,
                        const float* k_scale, uint8_t* kb8, float* kb_scale, hipStream_t st);
-int launch_expand_blocks(int B, int KB, int block, const int32_t* blocks, const int32_t* n_keys, int32_t* cand,
-                         hipStream_t st);
-
 }  // namespace csa2

@@ -78,17 +78,6 @@ __global__ __launch_bounds__(256) void k_coarse_keys(int64_t n_max, const int32_
   if (lane == 0) kb_scale[orow] = s;
 }
 
-// cand[b][i*block + o] = blocks[b][i]*block + o, or -1 past n_keys[b] / for padded blocks
-__global__ void k_expand_blocks(int KB, int block, const int32_t* __restrict__ blocks,
-                                const int32_t* __restrict__ n_keys, int32_t* __restrict__ cand) {
-  const int b = blockIdx.y;
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= (int64_t)KB * block) return;
-  const int32_t blk = blocks[(int64_t)b * KB + i / block];
-  const int64_t pos = (int64_t)blk * block + i % block;
-  cand[(int64_t)b * KB * block + i] = (blk >= 0 && pos < n_keys[b]) ? (int32_t)pos : -1;
-}
-
 int launch_gather_dequant(int B, int T, int K, int D, const uint8_t* codes, const float* scales, int64_t n_max,
                           const int32_t* idx, float* out, hipStream_t st) {
   const int64_t total = (int64_t)B * T * K * (D / 8);
@@ -103,14 +92,6 @@ int launch_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int 
   const int64_t nb = (n_max + block - 1) / block;
   hipLaunchKernelGGL(k_coarse_keys, dim3((unsigned)((nb + 3) / 4), B), dim3(256), 0, st, n_max, n_keys, dk, block, nb,
                      k8, k_scale, kb8, kb_scale);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-int launch_expand_blocks(int B, int KB, int block, const int32_t* blocks, const int32_t* n_keys, int32_t* cand,
-                         hipStream_t st) {
-  const int64_t n = (int64_t)KB * block;
-  hipLaunchKernelGGL(k_expand_blocks, dim3((unsigned)((n + 255) / 256), B), dim3(256), 0, st, KB, block, blocks,
-                     n_keys, cand);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

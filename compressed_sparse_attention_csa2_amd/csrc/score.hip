@@ -403,12 +403,15 @@ int score_rows_tiled(const ScoreArgs& a) {
   return a.prec == 1 && a.cand == nullptr && a.key_div == 1 && a.T >= kRowTile && a.qstage != nullptr;
 }
 
-int score_cols_per_block(int64_t ncols) {
-  // tiles per wave: long rows stream 2048 keys per block (128 KB of keys), short rows
-  // use smaller blocks so that the chip still fills
-  if (ncols >= 65536) return kScoreWaves * 16 * 32;
-  if (ncols >= 8192) return kScoreWaves * 8 * 32;
-  return kScoreWaves * 4 * 32;
+int score_cols_per_block(int64_t rows, int64_t ncols) {
+  // tiles per wave: the largest of 16 / 8 / 4 / 2 that still gives >= 512 blocks (two per
+  // CU), so that long scans stream 2048 keys per block and short ones (few rows, small N)
+  // spread over the chip
+  for (int tpw = 16; tpw > 2; tpw >>= 1) {
+    const int64_t cpb = kScoreWaves * tpw * 32;
+    if (rows * ((ncols + cpb - 1) / cpb) >= 512) return (int)cpb;
+  }
+  return kScoreWaves * 2 * 32;
 }
 
 template <typename QT, bool CAND, int TPW>
@@ -422,10 +425,11 @@ static void launch_fp8(const ScoreArgs& a, hipStream_t st) {
 
 template <typename QT, bool CAND>
 static void launch_fp8_tpw(const ScoreArgs& a, hipStream_t st) {
-  const int cpb = score_cols_per_block(a.ncols);
+  const int cpb = score_cols_per_block((int64_t)a.B * a.T, a.ncols);
   if (cpb == kScoreWaves * 16 * 32) launch_fp8<QT, CAND, 16>(a, st);
   else if (cpb == kScoreWaves * 8 * 32) launch_fp8<QT, CAND, 8>(a, st);
-  else launch_fp8<QT, CAND, 4>(a, st);
+  else if (cpb == kScoreWaves * 4 * 32) launch_fp8<QT, CAND, 4>(a, st);
+  else launch_fp8<QT, CAND, 2>(a, st);
 }
 
 int launch_score(const ScoreArgs& a, hipStream_t st) {

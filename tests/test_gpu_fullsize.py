@@ -158,3 +158,47 @@ def test_hier1m_full_size():
     ro, rl = oracle.sparse_attend(qa, cr, sr, g_idx, wl.softmax_scale)
     assert _bf16_ok(out.float().cpu().numpy(), ro)
     assert np.allclose(lse.cpu().numpy(), rl, rtol=0, atol=2e-3 * max(1.0, np.abs(rl).max()))
+
+
+def test_hier_step_graph_replay_matches_eager():
+    """The two-level select + attention captured into a HIP graph: every replay (with eager
+    work and synchronisation between replays) reproduces the eager result bit for bit."""
+    wl = workloads.workload("hier1m", N=64 * 4096)
+    n = wl.N
+    k8 = torch.empty((1, n, wl.dk), dtype=torch.uint8, device=DEV)
+    ks = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    codes = torch.empty((1, n, wl.D // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((1, wl.D), dtype=torch.float32, device=DEV)
+    csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(wl.index_keys(0))[None], k8, ks)
+    csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, to_dev(wl.main_kv(0))[None], codes, scales)
+    nk = torch.tensor([n - 77], dtype=torch.int32, device=DEV)
+    kb, kbs = csa2.coarse_keys(k8, ks, nk, wl.coarse_block)
+    q = to_dev(wl.index_query(), torch.bfloat16)
+    w = to_dev(wl.head_weights())
+    qa = to_dev(wl.attn_query(), torch.bfloat16)
+    out = torch.empty((1, 1, wl.Hq, wl.D), dtype=torch.float32, device=DEV)
+    lse = torch.empty((1, 1, wl.Hq), dtype=torch.float32, device=DEV)
+    holder = {}
+
+    def step():
+        holder["idx"] = csa2.hier_select(q, w, k8, ks, kb, kbs, nk, wl.coarse_block, wl.coarse_topk, wl.K)
+        csa2.sparse_attend(qa, codes, scales, holder["idx"], wl.softmax_scale, out=out, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (holder["idx"].clone(), out.clone(), lse.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    g_idx = holder["idx"]  # the index tensor the graph writes
+    for rep in range(4):
+        out.zero_()
+        lse.zero_()
+        g_idx.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g_idx, ref[0]), rep
+        assert torch.equal(out, ref[1]) and torch.equal(lse, ref[2]), rep
+        step()  # eager work between replays
+        torch.cuda.synchronize()
