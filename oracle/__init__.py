@@ -216,24 +216,55 @@ def check_schedule(modes):
     return len(modes) > 0
 
 
-def layer_group(layers, cache, prec, K, softmax_scale):
+def block_max(scores, block):
+    """[B][T][n] scores -> [B][T][ceil(n / block)]: the largest score in each block of
+    `block` consecutive positions, -inf where the block holds no visible score.
+    "Hierarchical Sparse Indexer In Simple Terms": a block is represented by its best
+    entry's score."""
+    s = np.asarray(scores, np.float64)
+    B, T, n = s.shape
+    nb = (n + block - 1) // block
+    pad = np.full((B, T, nb * block), -np.inf)
+    pad[..., :n] = s
+    return pad.reshape(B, T, nb, block).max(axis=3)
+
+
+def pool_positions(scores, block, pool_blocks, n_keys):
+    """The candidate pool a Full layer leaves for later Reindex layers: the `pool_blocks`
+    blocks with the largest block maxima (lowest block index on ties), expanded to their
+    positions in ascending order (-1 past n_keys or for missing blocks).  Same source."""
+    blocks = topk(block_max(scores, block), pool_blocks)
+    return expand_blocks(blocks, block, n_keys)
+
+
+def layer_group(layers, cache, prec, K, softmax_scale, pool=None):
     """Run the layers in order over one shared cache.
 
     layers: list of dicts {mode, q_idx, w, q_attn}; cache: dict {k, k_scale, n_keys, codes,
     scales}.  Full and Reindex score the shared indexer keys with their own query and
     take a fresh Top-K; Reuse takes the most recent indexing layer's Top-K unchanged.
     Every mode then attends over the shared main KV with its own attention query.
-    Returns a list of dicts {idx, out, lse}."""
+    pool = (block, pool_blocks): every Full layer also leaves the pool of its best blocks
+    (pool_positions) and the Reindex layers after it score only the pool's positions.
+    Returns a list of dicts {idx, out, lse} (plus 'pool' for Full layers with a pool)."""
     modes = [L["mode"] for L in layers]
     if not check_schedule(modes):
         raise ValueError("invalid mode schedule %r" % (modes,))
-    results, last_idx = [], None
+    results, last_idx, cand = [], None, None
     for L in layers:
-        if L["mode"] in (FULL, REINDEX):
+        res = {}
+        if L["mode"] == FULL or (L["mode"] == REINDEX and cand is None):
             s = index_score(prec, L["q_idx"], L["w"], cache["k"], cache["k_scale"], cache["n_keys"])
             last_idx = topk(s, K)
+            if L["mode"] == FULL and pool is not None:
+                cand = pool_positions(s, pool[0], pool[1], cache["n_keys"])
+                res["pool"] = cand
+        elif L["mode"] == REINDEX:
+            s = index_score(prec, L["q_idx"], L["w"], cache["k"], cache["k_scale"], cache["n_keys"], cand=cand)
+            last_idx = topk(s, K, cand=cand)
         out, lse = sparse_attend(L["q_attn"], cache["codes"], cache["scales"], last_idx, softmax_scale)
-        results.append({"idx": last_idx, "out": out, "lse": lse})
+        res.update({"idx": last_idx, "out": out, "lse": lse})
+        results.append(res)
     return results
 
 
