@@ -287,6 +287,65 @@ def run_full64k(args):
         "step_pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
 
 
+DECODER_MODES = ["full"] + ["reuse"] * 3 + (["reindex"] + ["reuse"] * 3) * 4
+DECODER_POOL = (8, 2048)
+
+
+def run_decoder128k(args):
+    """The decoder's layer schedule (Full, 3 Reuse, then 4 x [Reindex, 3 Reuse]; 20 layers)
+    at 128K context, 16 sequences: the Full layer scans all 131072 entries and also keeps its
+    best 2048 blocks of 8 entries (by block maximum) as the candidate pool; every Reindex
+    layer scores only the pool's 16384 positions.  The same schedule without the pool (every
+    Reindex layer scans everything) is timed beside it."""
+    wl = workloads.WORKLOADS["group128k"]
+    log("building cache (%d copies) ..." % args.copies)
+    caches = build_device_cache(wl, args.copies)
+    layers = []
+    for i, m in enumerate(DECODER_MODES):
+        layers.append(dict(mode=m, q_idx=torch.from_numpy(wl.index_query(i)).to(torch.bfloat16).cuda(),
+                           w=torch.from_numpy(wl.head_weights(i)).cuda(),
+                           q_attn=torch.from_numpy(wl.attn_query(i)).to(torch.bfloat16).cuda()))
+
+    def timed(pool):
+        plans = [csa2.GroupPlan([dict(L) for L in layers],
+                                csa2.GroupCache(c["n_keys"], c["codes"], c["scales"], c["k8"], c["ks"], wl.K,
+                                                wl.softmax_scale, pool=pool), out_dtype=torch.bfloat16)
+                 for c in caches]
+        for s in range(args.warmup):
+            plans[s % len(plans)].run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            plans[s % len(plans)].run()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps * 1e3
+
+    ms_step = timed(DECODER_POOL)
+    flat_ms = timed(None)
+    B, N, K, D, Hq = wl.B, wl.N, wl.K, wl.D, wl.Hq
+    C = DECODER_POOL[0] * DECODER_POOL[1]
+    n_reindex = DECODER_MODES.count("reindex")
+    q_idx = B * wl.H * wl.dk * 2 + B * wl.H * 4
+    attend = B * K * (D // 2) + B * D * 4 + B * Hq * D * 2 * 2 + B * K * 4 + B * Hq * 4
+    # Full: the scan, its scores' block maxima (read back once) and the pool written; Reindex:
+    # the pool read and its entries' keys and scales
+    alg = (B * N * (wl.dk + 4) + B * N * 4 + B * C * 4 + q_idx + B * K * 4) + \
+        n_reindex * (B * C * (4 + wl.dk + 4) + q_idx + B * K * 4) + len(DECODER_MODES) * attend
+    gbs = alg / (ms_step / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "CSA2 decode queries/s at 128K context (decoder schedule with the candidate pool)",
+        "value": round(B / (ms_step / 1e3), 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": "decoder128k: Full, 3 Reuse, 4 x [Reindex, 3 Reuse] (20 layers), B=16, N=131072, "
+                               "pool of 2048 blocks x 8, indexer 32x64 E4M3, Top-512, FP4 E2M1 main KV D=512, "
+                               "64 heads bf16", "global_batch": B, "seq_len": N, "layers": DECODER_MODES,
+                   "pool": list(DECODER_POOL), "cache_copies": args.copies},
+        "step_algorithmic_bytes": alg, "step_achieved_GBps": round(gbs, 1),
+        "step_pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "no_pool_ms_per_step": round(flat_ms, 5)}), flush=True)
+
+
 def run_hier1m(args):
     """The 1M-entry two-level configuration (one sequence): coarse keys (64-entry block
     means, built once, not timed) -> score 16384 coarse keys -> top-256 blocks -> exact
@@ -368,9 +427,11 @@ def main():
     ap.add_argument("--score-reps", type=int, default=60)
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="group128k", choices=["group128k", "prefill", "full64k", "hier1m"],
+    ap.add_argument("--workload", default="group128k",
+                    choices=["group128k", "prefill", "full64k", "hier1m", "decoder128k"],
                     help="group128k: the 128K decode group (the headline; default); prefill: the chunked-prefill "
-                         "path; full64k: one Full layer at 64K; hier1m: the two-level indexer at 1M")
+                         "path; full64k: one Full layer at 64K; hier1m: the two-level indexer at 1M; decoder128k: "
+                         "the 20-layer decoder schedule at 128K with the candidate pool")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -393,6 +454,9 @@ def main():
         return
     if args.workload == "hier1m":
         run_hier1m(args)
+        return
+    if args.workload == "decoder128k":
+        run_decoder128k(args)
         return
     wl = workloads.WORKLOADS["group128k"]
     log("building cache (%d copies) ..." % args.copies)

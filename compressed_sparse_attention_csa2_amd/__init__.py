@@ -49,7 +49,7 @@ class Csa2Error(RuntimeError):
 class _Layer(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int), ("q_idx", ctypes.c_void_p), ("w", ctypes.c_void_p),
                 ("q_attn", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
-                ("idx", ctypes.c_void_p)]
+                ("idx", ctypes.c_void_p), ("pool", ctypes.c_void_p)]
 
 
 class _GroupCache(ctypes.Structure):
@@ -57,7 +57,8 @@ class _GroupCache(ctypes.Structure):
                 ("D", ctypes.c_int), ("K", ctypes.c_int), ("n_max", ctypes.c_int64), ("n_keys", ctypes.c_void_p),
                 ("kv_codes", ctypes.c_void_p), ("kv_scales", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("prec", ctypes.c_int), ("q_dtype", ctypes.c_int),
-                ("out_dtype", ctypes.c_int), ("softmax_scale", ctypes.c_float)]
+                ("out_dtype", ctypes.c_int), ("softmax_scale", ctypes.c_float), ("pool_block", ctypes.c_int),
+                ("pool_blocks", ctypes.c_int)]
 
 
 _lib = None
@@ -244,15 +245,19 @@ def sparse_attend(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, id
 class GroupCache:
     """The shared cache of a layer group (all device tensors)."""
 
-    def __init__(self, n_keys, kv_codes, kv_scales, k, k_scale, K, softmax_scale, prec=PREC_FP8):
+    def __init__(self, n_keys, kv_codes, kv_scales, k, k_scale, K, softmax_scale, prec=PREC_FP8, pool=None):
+        """pool: None, or (block, blocks): Full layers leave the positions of their `blocks`
+        best blocks of `block` positions (by block maximum) to the later Reindex layers."""
         self.n_keys, self.kv_codes, self.kv_scales, self.k, self.k_scale = n_keys, kv_codes, kv_scales, k, k_scale
         self.K, self.softmax_scale, self.prec = K, softmax_scale, prec
+        self.pool = pool
 
     def struct(self, H, dk, Hq, q_dtype, out_dtype):
         B, n_max, Dh = self.kv_codes.shape
+        pb, pn = self.pool if self.pool else (0, 0)
         return _GroupCache(B, H, dk, Hq, 2 * Dh, self.K, n_max, _ptr(self.n_keys), _ptr(self.kv_codes),
                            _ptr(self.kv_scales), _ptr(self.k), _ptr(self.k_scale), self.prec, q_dtype, out_dtype,
-                           float(self.softmax_scale))
+                           float(self.softmax_scale), pb, pn)
 
 
 class GroupPlan:
@@ -272,8 +277,9 @@ def layer_group(layers: Sequence[dict], cache: GroupCache, out_dtype: Optional[t
     """Run Full/Reindex/Reuse layers in order over one shared cache.
 
     layers: dicts with mode ('full'|'reindex'|'reuse'), q_idx [B][1][H][dk], w [B][1][H],
-    q_attn [B][1][Hq][D] and optionally out, lse, idx tensors.  Returns the layer dicts
-    with 'out', 'lse' and (Full/Reindex) 'idx' filled."""
+    q_attn [B][1][Hq][D] and optionally out, lse, idx tensors, and for Full layers of a
+    cache with a pool a 'pool' int32 tensor [B][blocks*block] that receives the pool's
+    positions.  Returns the layer dicts with 'out', 'lse' and (Full/Reindex) 'idx' filled."""
     return GroupPlan(layers, cache, out_dtype).run()
 
 
@@ -292,8 +298,15 @@ def _marshal_group(layers, cache, out_dtype):
             L["lse"] = torch.empty((B, 1, Hq), dtype=torch.float32, device=q_attn.device)
         if mode != REUSE and L.get("idx") is None:
             L["idx"] = torch.empty((B, 1, cache.K), dtype=torch.int32, device=q_attn.device)
+        p = L.get("pool")
+        if p is not None and mode == FULL:
+            if not cache.pool:
+                raise ValueError("a pool output was given but the cache has no pool")
+            if p.dtype != torch.int32 or not p.is_contiguous() or p.numel() != B * cache.pool[0] * cache.pool[1]:
+                raise ValueError("pool must be a contiguous int32 tensor of B * block * blocks elements")
         arr[i] = _Layer(mode, _ptr(L.get("q_idx")), _ptr(L.get("w")), _ptr(L["q_attn"]), _ptr(L["out"]),
-                        _ptr(L["lse"]), _ptr(L.get("idx")) if mode != REUSE else None)
+                        _ptr(L["lse"]), _ptr(L.get("idx")) if mode != REUSE else None,
+                        _ptr(L.get("pool")) if mode == FULL else None)
     qd = _dtype_code(q_attn)
     gc = cache.struct(H, dk, Hq, qd, _dtype_code(torch.empty(0, dtype=odt)))
     nb = lib().csa2_layer_group_workspace_size(ctypes.byref(gc), len(layers))

@@ -343,14 +343,28 @@ static int count_index_layers(const csa2_layer* layers, int n) {
   return c;
 }
 
-// workspace: [hist, hist2, ctl per indexing layer (zeroed once per call)] [scores]
-//            [candidates] [attention partials]
+static bool pool_on(const csa2_group_cache* c) { return c->pool_blocks > 0; }
+static int64_t pool_cols(const csa2_group_cache* c) { return pool_on(c) ? (int64_t)c->pool_blocks * c->pool_block : 0; }
+static int64_t pool_nb(const csa2_group_cache* c) {
+  return pool_on(c) ? (c->n_max + c->pool_block - 1) / c->pool_block : 0;
+}
+// columns the scores and candidate regions are sized for (the full scan or the pool)
+static int64_t group_cols(const csa2_group_cache* c) {
+  const int64_t pc = pool_cols(c);
+  return pc > c->n_max ? pc : c->n_max;
+}
+
+// workspace: [hist, hist2, ctl per Top-K selection (zeroed once per call)] [scores]
+//            [candidates] [attention partials] [pool positions, block maxima]
 size_t csa2_layer_group_workspace_size(const csa2_group_cache* c, int n_layers) {
   if (!c || n_layers < 1) return 0;
   const int64_t R = c->B;
-  const int slots = n_layers < 64 ? n_layers : 64;
+  const int sel = pool_on(c) ? 2 * n_layers : n_layers;  // a pooled Full layer makes two selections
+  const int slots = sel < 64 ? sel : 64;
   const size_t att = (c->q_dtype == CSA2_BF16) ? align256(attend_ws_floats((int)R, c->Hq, c->D, c->K) * 4) : 0;
-  return topk_zero_bytes(R) * (size_t)slots + align256((size_t)R * c->n_max * 4) + cand_bytes(R, c->n_max) + att;
+  const size_t pool = pool_on(c) ? align256((size_t)R * pool_cols(c) * 4) + align256((size_t)R * pool_nb(c) * 4) : 0;
+  return topk_zero_bytes(R) * (size_t)slots + align256((size_t)R * group_cols(c) * 4) + cand_bytes(R, group_cols(c)) +
+         att + pool;
 }
 
 int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_cache* c, void* ws, size_t ws_bytes,
@@ -361,6 +375,8 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   if (rc) return rc;
   if (!c->n_keys || !c->kv_codes || !c->kv_scales || !c->k) return CSA2_ERR_NULL;
   if (c->n_max < 1 || c->n_max > kMaxTopkCols || c->K < 1 || c->K > CSA2_MAX_K) return CSA2_ERR_SHAPE;
+  if (c->pool_blocks < 0 || c->pool_blocks > CSA2_MAX_K || (pool_on(c) && c->pool_block < 1)) return CSA2_ERR_SHAPE;
+  if (pool_cols(c) > kMaxTopkCols || c->n_max > INT32_MAX) return CSA2_ERR_SHAPE;
   rc = check_index_shape(c->prec, c->B, 1, c->H, c->dk, c->q_dtype, c->k_scale, c->n_max);
   if (rc) return rc;
   rc = check_attend_shape(c->B, 1, c->Hq, c->D, c->K, c->q_dtype, c->out_dtype);
@@ -375,25 +391,38 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   if (rc) return rc;
 
   const int64_t R = c->B;
-  const int n_index = count_index_layers(layers, n_layers);
-  const int slots = n_index < 64 ? n_index : 64;
+  const bool pooled = pool_on(c);
+  int n_sel = count_index_layers(layers, n_layers);
+  if (pooled)
+    for (int i = 0; i < n_layers; ++i) n_sel += (layers[i].mode == CSA2_FULL);
+  const int slots = n_sel < 64 ? n_sel : 64;
   Carve cv(ws);
   TopkWs tz[64];
   for (int i = 0; i < slots; ++i) tz[i] = carve_topk_zero(cv, R);
   const size_t zero_bytes = cv.off;
-  float* scores = cv.take<float>((size_t)R * c->n_max);
-  CandWs cw = carve_cand(cv, R, c->n_max);
+  float* scores = cv.take<float>((size_t)R * group_cols(c));
+  CandWs cw = carve_cand(cv, R, group_cols(c));
   float* part = (c->q_dtype == CSA2_BF16) ? cv.take<float>(attend_ws_floats((int)R, c->Hq, c->D, c->K)) : nullptr;
+  const int64_t pc = pool_cols(c), nb = pool_nb(c);
+  int32_t* pool = pooled ? cv.take<int32_t>((size_t)R * pc) : nullptr;
+  float* bmax = pooled ? cv.take<float>((size_t)R * nb) : nullptr;
   hipStream_t st = S(stream);
-  // one fill clears every indexing layer's histograms and control words (more than 64
-  // indexing layers reuse the last slot, cleared again before each reuse)
+  // one fill clears every selection's histograms and control words (more than 64 selections
+  // reuse the last slot, cleared again before each reuse)
   if (slots > 0 && launch_fill_u32(tz[0].hist, (int64_t)(zero_bytes / 4), 0u, st)) return CSA2_ERR_DEVICE;
+  int si = 0;
+  auto next_slot = [&](TopkWs& t) -> int {
+    t = tz[si < slots ? si : slots - 1];
+    const bool reuse = si >= slots;
+    ++si;
+    return reuse ? zero_topk(t, R, st) : 0;
+  };
+  const int32_t* cur_pool = nullptr;  // the pool of the most recent Full layer
 
   AttendArgs a = attend_args(c->B, 1, c->Hq, c->D, c->K, nullptr, c->q_dtype, c->kv_codes, c->kv_scales, c->n_max,
                              nullptr, c->softmax_scale, nullptr, c->out_dtype, nullptr);
   a.part = part;
   const int32_t* last_idx = nullptr;
-  int li = 0;
   for (int i = 0; i < n_layers; ++i) {
     const csa2_layer& L = layers[i];
     a.q = L.q_attn;
@@ -401,25 +430,44 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
     a.lse = L.lse;
     a.ctl = nullptr; a.hist2 = nullptr; a.candbuf = nullptr; a.idx_out = nullptr; a.idx = last_idx;
     if (L.mode != CSA2_REUSE) {
-      TopkWs t = tz[li < slots ? li : slots - 1];
-      if (li >= slots && zero_topk(t, R, st)) return CSA2_ERR_DEVICE;
-      ++li;
+      TopkWs t;
+      if (next_slot(t)) return CSA2_ERR_DEVICE;
+      // a Reindex layer after a pooled Full layer scores only the pool's positions; the pool
+      // ascends, so its filtered candidates are in position order like a full scan's
+      const bool use_pool = (L.mode == CSA2_REINDEX) && cur_pool;
+      const int64_t ncols = use_pool ? pc : c->n_max;
+      const int32_t* cand = use_pool ? cur_pool : nullptr;
       ScoreArgs sa = score_args(c->prec, c->B, 1, c->H, c->dk, L.q_idx, c->q_dtype, L.w, c->k, c->k_scale, c->n_max,
-                                c->n_keys, nullptr, nullptr, c->n_max, scores, t.hist, 1);
+                                c->n_keys, nullptr, cand, ncols, scores, t.hist, 1);
       if (launch_score(sa, st)) return CSA2_ERR_DEVICE;
-      if (launch_topk_filter((int)R, c->n_max, scores, nullptr, c->K, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st))
+      if (launch_topk_filter((int)R, ncols, scores, cand, c->K, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st))
         return CSA2_ERR_DEVICE;
       if (a.q_bf16) {
-        a.ctl = t.ctl; a.hist2 = t.hist2; a.candbuf = cw.cand; a.cnt = cw.cnt; a.nreg = topk_regions(c->n_max);
+        a.ctl = t.ctl; a.hist2 = t.hist2; a.candbuf = cw.cand; a.cnt = cw.cnt; a.nreg = topk_regions(ncols);
         a.idx_out = L.idx;
       } else {
-        if (launch_topk_finalize((int)R, c->n_max, c->K, true, t.ctl, t.hist2, cw.cand, cw.cnt, L.idx, nullptr, st))
+        if (launch_topk_finalize((int)R, ncols, c->K, true, t.ctl, t.hist2, cw.cand, cw.cnt, L.idx, nullptr, st))
           return CSA2_ERR_DEVICE;
         a.idx = L.idx;
       }
       last_idx = L.idx;
     }
     if (launch_attend(a, st)) return CSA2_ERR_DEVICE;
+    if (pooled && L.mode == CSA2_FULL) {
+      // the pool: block maxima of this layer's scores, their best pool_blocks blocks (lowest
+      // block on ties), expanded to positions (-1 past n_keys).  Runs after the attention,
+      // which has finished reading the candidate regions this selection reuses.
+      TopkWs t;
+      if (next_slot(t)) return CSA2_ERR_DEVICE;
+      int32_t* dst = L.pool ? L.pool : pool;
+      if (launch_block_max((int)R, c->n_max, c->pool_block, scores, bmax, t.hist, st)) return CSA2_ERR_DEVICE;
+      if (launch_topk_filter((int)R, nb, bmax, nullptr, c->pool_blocks, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st))
+        return CSA2_ERR_DEVICE;
+      if (launch_topk_finalize((int)R, nb, c->pool_blocks, true, t.ctl, t.hist2, cw.cand, cw.cnt, nullptr, nullptr, st,
+                               c->pool_block, c->n_keys, dst))
+        return CSA2_ERR_DEVICE;
+      cur_pool = dst;
+    }
   }
   return CSA2_OK;
 }

@@ -50,6 +50,10 @@ int score_cols_per_block(int64_t rows, int64_t ncols);
 // Top-K: histogram (zeroed on entry) -> filter into candidates (ctl zeroed on entry)
 // -> finalize (here, or fused into the attention kernel).
 int launch_topk_hist(int R, int64_t ncols, const float* scores, const int32_t* cand, uint32_t* hist, hipStream_t st);
+// bmax [R][ceil(ncols / block)]: block maxima of the scores; hist (zeroed on entry): their
+// first-level histogram
+int launch_block_max(int R, int64_t ncols, int block, const float* scores, float* bmax, uint32_t* hist,
+                     hipStream_t st);
 // hist2 [R][kHistBins]: second-level histogram of the threshold bin (zeroed on entry).
 // candbuf [R][regions][kFilterColsPerBlock] and cnt [R][regions], regions = topk_regions.
 int topk_regions(int64_t ncols);

@@ -207,9 +207,10 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
   }
 }
 
-// EXPAND (two-level select): the selected columns are blocks of `block` positions; the
-// kernel also writes the blocks' positions in order, -1 past a sequence's n_keys or for
-// padding (the candidate list of the fine stage).
+// EXPAND (two-level select, candidate pool): the selected columns are blocks of `block`
+// positions; the kernel also writes the blocks' positions in order, -1 past a sequence's
+// n_keys or for padding (the candidate list of the fine stage).  idx_out and val_out may be
+// null.
 template <bool SORTED, bool EXPAND>
 __global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, const RowCtl* __restrict__ ctl,
                                                                const uint32_t* __restrict__ hist2,
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, 
                                                      c.beta, c.above, c.keff, sm, s_pos, s_key);
   for (int i = threadIdx.x; i < K; i += kFinThreads) {
     const bool have = i < keff;
-    idx_out[(int64_t)r * K + i] = have ? s_pos[i] : -1;
+    if (idx_out) idx_out[(int64_t)r * K + i] = have ? s_pos[i] : -1;
     if (val_out) val_out[(int64_t)r * K + i] = have ? key_to_float(s_key[i]) : kNegInf;
   }
   if (EXPAND) {
@@ -240,6 +241,40 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, 
       expand_out[(int64_t)r * K * block + i] = (pos >= 0 && pos < nk) ? (int32_t)pos : -1;
     }
   }
+}
+
+// Candidate pool of a Full layer: the largest score of every block of `block` consecutive
+// positions (-inf where none is visible), plus the first-level histogram of those maxima
+// for the pool's Top-K.  One thread per block of positions, 256 blocks per workgroup.
+__global__ __launch_bounds__(256) void k_block_max(int64_t ncols, int block, int64_t nb,
+                                                   const float* __restrict__ scores, float* __restrict__ bmax,
+                                                   uint32_t* __restrict__ hist) {
+  __shared__ uint32_t lhist[kHistBins];
+  const int r = blockIdx.y;
+  for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
+  __syncthreads();
+  const int64_t k = blockIdx.x * 256LL + threadIdx.x;
+  if (k < nb) {
+    const float* s = scores + (int64_t)r * ncols + k * block;
+    const int64_t n = (ncols - k * block < block) ? ncols - k * block : block;
+    float m = kNegInf;
+    for (int64_t i = 0; i < n; ++i) m = fmaxf(m, s[i]);  // -inf stays -inf; scores are never NaN
+    bmax[(int64_t)r * nb + k] = m;
+    if (visible(m)) atomicAdd(&lhist[hist_bin(order_key(m))], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kHistBins; i += 256) {
+    const uint32_t v = lhist[i];
+    if (v) atomicAdd(&hist[(int64_t)r * kHistBins + i], v);
+  }
+}
+
+int launch_block_max(int R, int64_t ncols, int block, const float* scores, float* bmax, uint32_t* hist,
+                     hipStream_t st) {
+  const int64_t nb = (ncols + block - 1) / block;
+  hipLaunchKernelGGL(k_block_max, dim3((unsigned)((nb + 255) / 256), R), dim3(256), 0, st, ncols, block, nb, scores,
+                     bmax, hist);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_topk_hist(int R, int64_t ncols, const float* scores, const int32_t* cand, uint32_t* hist, hipStream_t st) {

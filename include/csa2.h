@@ -190,6 +190,11 @@ size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int
  * (q_dtype), w [B][1][H], q_attn [B][1][Hq][D] (q_dtype), out [B][1][Hq][D] (out_dtype),
  * lse [B][1][Hq] (nullable), idx [B][1][K] written by FULL/REINDEX, ignored by REUSE
  * (may be NULL there).  Decode only (one query token per sequence).
+ * With a candidate pool (csa2_group_cache.pool_blocks > 0), a REINDEX layer after a FULL
+ * layer scores only the pool that the most recent FULL layer left; pool [B][pool_blocks *
+ * pool_block] (nullable, FULL only) receives that pool's positions: selected blocks
+ * ascending, positions ascending inside a block, -1 at or past n_keys and for blocks
+ * missing when fewer than pool_blocks blocks hold a visible position.
  */
 typedef struct {
   int mode;              /* csa2_mode */
@@ -199,6 +204,7 @@ typedef struct {
   void* out;
   float* lse;
   int32_t* idx;          /* FULL/REINDEX: output; REUSE: ignored */
+  int32_t* pool;         /* FULL with a pool: optional output; otherwise ignored */
 } csa2_layer;
 
 typedef struct {
@@ -212,6 +218,13 @@ typedef struct {
   int prec;                /* csa2_index_prec */
   int q_dtype, out_dtype;  /* csa2_dtype */
   float softmax_scale;
+  /* Candidate pool ("Hierarchical Sparse Indexer In Simple Terms"): with pool_blocks > 0,
+   * every Full layer also reduces its scores over blocks of pool_block consecutive positions
+   * to the block maximum, keeps the pool_blocks best blocks (lowest block index on ties) and
+   * the Reindex layers after it score only those blocks' positions.  0 = no pool (every
+   * Reindex layer scores all n_keys entries).  1 <= pool_blocks <= CSA2_MAX_K. */
+  int pool_block;
+  int pool_blocks;
 } csa2_group_cache;
 
 int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_cache* cache, void* ws,

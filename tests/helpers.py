@@ -97,3 +97,31 @@ def build_cache(wl, n_rows=None, seqs=None):
     else:
         res["kdev"] = kd
     return res
+
+
+def check_pool(gpool, s_ref, block, blocks, nk):
+    """A candidate pool gpool [B][blocks*block] from the GPU against the oracle's Full scores
+    s_ref [B][1][n]: its block list by the near-tie rule on the block maxima, its positions
+    exactly the expansion of that list."""
+    bm = oracle.block_max(s_ref, block)
+    for b in range(gpool.shape[0]):
+        p = gpool[b]
+        first = p[::block]
+        blk = np.where(first >= 0, first // block, -1).astype(np.int32)
+        assert np.array_equal(oracle.expand_blocks(blk[None, None], block, nk[b:b + 1])[0, 0], p), b
+        check_topk_near_tie(blk[None, None], bm[b:b + 1], blocks)
+
+
+def check_pooled_reindex(g_idx, q, w, k8, ks, nk, gpool, K):
+    """A Reindex selection against the oracle's scores of the GPU's pool positions (near-tie
+    rule on the pool), and inside the pool."""
+    n = k8.shape[1]
+    fs = oracle.index_score(oracle.PREC_FP8, q, w, k8, ks, nk, cand=gpool[:, None])
+    full = np.full((len(nk), 1, n), -np.inf)
+    for b in range(len(nk)):
+        ok = gpool[b] >= 0
+        full[b, 0, gpool[b][ok]] = fs[b, 0][ok]
+    check_topk_near_tie(g_idx, full, K)
+    for b in range(len(nk)):
+        sel = g_idx[b, 0]
+        assert np.all(np.isin(sel[sel >= 0], gpool[b])), b

@@ -100,6 +100,29 @@ def test_pages_schedule_passes_validation():
     assert L.csa2_layer_group(arr, len(modes), ctypes.byref(gc), None, 0, None) == -5
 
 
+@pytest.mark.parametrize("block,blocks,code", [(8, -1, -2), (8, 2049, -2), (0, 16, -2), (8, 2048, -5), (0, 0, -5)])
+def test_layer_group_pool_validation(block, blocks, code):
+    L = csa2.lib()
+    arr = (csa2._Layer * 2)()
+    for i, m in enumerate([0, 1]):
+        arr[i] = csa2._Layer(m, _p(), _p(), _p(), _p(), None, _p(), None)
+    gc = csa2._GroupCache(1, 32, 64, 64, 512, 512, 1000, _p(), _p(), _p(), _p(), _p(), 1, 1, 1, 0.04, block, blocks)
+    assert L.csa2_layer_group(arr, 2, ctypes.byref(gc), None, 0, None) == code
+
+
+def test_layer_group_pool_workspace_grows():
+    L = csa2.lib()
+    base = csa2._GroupCache(4, 32, 64, 64, 512, 512, 131072, _p(), _p(), _p(), _p(), _p(), 1, 1, 1, 0.04)
+    pooled = csa2._GroupCache(4, 32, 64, 64, 512, 512, 131072, _p(), _p(), _p(), _p(), _p(), 1, 1, 1, 0.04, 8, 2048)
+    big = csa2._GroupCache(4, 32, 64, 64, 512, 512, 1000, _p(), _p(), _p(), _p(), _p(), 1, 1, 1, 0.04, 16, 2048)
+    a = L.csa2_layer_group_workspace_size(ctypes.byref(base), 4)
+    b = L.csa2_layer_group_workspace_size(ctypes.byref(pooled), 4)
+    # pool positions and block maxima, plus one more selection per layer
+    assert b >= a + 4 * 16384 * 4 + 4 * 16384 * 4
+    # a pool wider than the cache sizes the scores and candidates for the pool
+    assert L.csa2_layer_group_workspace_size(ctypes.byref(big), 4) >= 4 * 32768 * 4 * 2
+
+
 def test_product_path_does_not_import_oracle():
     pkg = os.path.join(ROOT, "compressed_sparse_attention_csa2_amd")
     for dirpath, _, files in os.walk(pkg):

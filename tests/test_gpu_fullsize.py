@@ -13,7 +13,7 @@ import torch
 import compressed_sparse_attention_csa2_amd as csa2
 import oracle
 import workloads
-from helpers import DEV, check_topk_near_tie, to_dev
+from helpers import DEV, check_pool, check_pooled_reindex, check_topk_near_tie, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -99,6 +99,55 @@ def test_group128k_full_size_sampled_sequences():
         assert torch.equal(L["out"], o) and torch.equal(L["lse"], l)
         if ix is not None:
             assert torch.equal(L["idx"], ix)
+
+
+def test_decoder128k_pool_full_size_sampled_sequences():
+    """The 128K decode configuration with the candidate pool of the pages' decoder: the Full
+    layer keeps its best 2048 blocks of 8 (16384 positions) and the Reindex layers score only
+    those.  16 sequences x 131072, schedule Full, Reuse, Reindex, Reuse, Reindex."""
+    wl = workloads.WORKLOADS["group128k"]
+    sample = [0, 9, 15]
+    pool = (8, 2048)
+    modes = ["full", "reuse", "reindex", "reuse", "reindex"]
+    c, ref = _device_cache_with_samples(wl, sample)
+    n_keys = torch.full((wl.B,), wl.N, dtype=torch.int32, device=DEV)
+    q_in, layers = [], []
+    for i, m in enumerate(modes):
+        qi, w, qa = wl.index_query(i), wl.head_weights(i), wl.attn_query(i)
+        q_in.append((qi, w, qa))
+        L = dict(mode=m, q_idx=to_dev(qi, torch.bfloat16), w=to_dev(w), q_attn=to_dev(qa, torch.bfloat16))
+        if m == "full":
+            L["pool"] = torch.full((wl.B, pool[0] * pool[1]), -7, dtype=torch.int32, device=DEV)
+        layers.append(L)
+    cache = csa2.GroupCache(n_keys, c["codes"], c["scales"], c["k8"], c["ks"], wl.K, wl.softmax_scale, pool=pool)
+    plan = csa2.GroupPlan(layers, cache, out_dtype=torch.bfloat16)
+    plan.run()
+    torch.cuda.synchronize()
+    first = [L["out"].clone() for L in layers]
+    k8 = np.stack([ref[b][2] for b in sample])
+    ks = np.stack([ref[b][3] for b in sample])
+    codes = np.stack([ref[b][0] for b in sample])
+    scales = np.stack([ref[b][1] for b in sample])
+    nk = np.full(len(sample), wl.N, np.int32)
+    gpool = g_idx = None
+    for i, (L, m) in enumerate(zip(layers, modes)):
+        qi, w, qa = (x[sample] for x in q_in[i])
+        if m == "full":
+            s = oracle.index_score(oracle.PREC_FP8, qi, w, k8, ks, nk)
+            g_idx = L["idx"].cpu().numpy()[sample]
+            check_topk_near_tie(g_idx, s, wl.K)
+            gpool = L["pool"].cpu().numpy()[sample]
+            check_pool(gpool, s, pool[0], pool[1], nk)
+            assert np.all(gpool >= 0)  # 16384 blocks to choose 2048 from: every slot filled
+        elif m == "reindex":
+            g_idx = L["idx"].cpu().numpy()[sample]
+            check_pooled_reindex(g_idx, qi, w, k8, ks, nk, gpool, wl.K)
+        ro, _ = oracle.sparse_attend(qa, codes, scales, g_idx, wl.softmax_scale)
+        assert _bf16_ok(L["out"].float().cpu().numpy()[sample], ro), i
+    plan.run()
+    torch.cuda.synchronize()
+    for L, o in zip(layers, first):
+        assert torch.equal(L["out"], o)
 
 
 def test_full64k_full_size_sampled_sequences():
