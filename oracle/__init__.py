@@ -29,6 +29,7 @@ _LIB_PATH = os.path.join(_HERE, "libcsa2_oracle.so")
 _lib = None
 
 PREC_FP32, PREC_FP8 = 0, 1
+FMT_FP4_PER_CHANNEL, FMT_FP4_G16 = 0, 2
 
 
 def build(force: bool = False) -> str:
@@ -53,14 +54,15 @@ def _load():
         L.orc_quantize_fp4.argtypes = [i, i, i, p, i64, i64, p, i64, p, p, i]
         L.orc_quantize_fp8.argtypes = [i, i, i, p, i64, i64, p, i64, p, p]
         L.orc_quantize_index_query.argtypes = [i, i, p, p, p]
-        L.orc_gather_dequant.argtypes = [i, i, i, i, p, p, i64, p, p]
+        L.orc_quantize_fp4_g16.argtypes = [i, i, i, p, i64, i64, p, i64, p, p]
+        L.orc_gather_dequant.argtypes = [i, i, i, i, i, p, p, i64, p, p]
         L.orc_index_score.argtypes = [i, i, i, i, i, p, p, p, p, i64, p, p, p, i, p]
         L.orc_topk.argtypes = [i, i, i64, p, p, i, p, p]
-        L.orc_sparse_attend.argtypes = [i, i, i, i, p, p, p, i64, p, i, d, p, p]
+        L.orc_sparse_attend.argtypes = [i, i, i, i, i, p, p, p, i64, p, i, d, p, p]
         L.orc_coarse_keys.argtypes = [i, i64, p, i, i, p, p, p, p]
         L.orc_num_threads.argtypes, L.orc_num_threads.restype = [], i
-        for fn in ("orc_quantize_fp4", "orc_quantize_fp8", "orc_quantize_index_query", "orc_gather_dequant",
-                   "orc_index_score", "orc_topk", "orc_sparse_attend", "orc_coarse_keys"):
+        for fn in ("orc_quantize_fp4", "orc_quantize_fp4_g16", "orc_quantize_fp8", "orc_quantize_index_query",
+                   "orc_gather_dequant", "orc_index_score", "orc_topk", "orc_sparse_attend", "orc_coarse_keys"):
             getattr(L, fn).restype = None
         _lib = L
     return _lib
@@ -112,6 +114,30 @@ def quantize_fp4(x, n_max=None, n0=None, scales=None, codes=None):
     return codes, scales
 
 
+def quantize_fp4_g16(x, n_max=None, n0=None, codes=None, gscales=None):
+    """x [B][T][D] -> (codes [B][n_max][D/2] u8, gscales [B][n_max][D/16] u8): the pages'
+    layout, one E4M3 scale per 16 channels of each entry (see orc_quantize_fp4_g16)."""
+    x = _c(x, np.float32)
+    B, T, D = x.shape
+    assert D % 16 == 0
+    n_max = T if n_max is None else n_max
+    codes = np.zeros((B, n_max, D // 2), np.uint8) if codes is None else codes
+    gscales = np.zeros((B, n_max, D // 16), np.uint8) if gscales is None else gscales
+    assert codes.flags["C_CONTIGUOUS"] and gscales.flags["C_CONTIGUOUS"]
+    n0a = None if n0 is None else _c(n0, np.int32)
+    _load().orc_quantize_fp4_g16(B, T, D, _p(x), T * D, D, _p(n0a), n_max, _p(codes), _p(gscales))
+    return codes, gscales
+
+
+def _kv_scales(scales):
+    """(format, contiguous scales): uint8 scales are the per-16-channel E4M3 layout
+    [B][n_max][D/16], anything else the per-channel fp32 scales [B][D]."""
+    a = np.asarray(scales)
+    if a.dtype == np.uint8:
+        return FMT_FP4_G16, _c(a, np.uint8)
+    return FMT_FP4_PER_CHANNEL, _c(a, np.float32)
+
+
 def quantize_fp8(x, n_max=None, n0=None, codes=None, scales=None):
     """x [B][T][D] -> (codes [B][n_max][D] u8, scales [B][n_max] f32); per-row absmax/448."""
     x = _c(x, np.float32)
@@ -137,11 +163,12 @@ def quantize_index_query(q):
 
 
 def gather_dequant(codes, scales, idx):
-    codes, scales, idx = _c(codes, np.uint8), _c(scales, np.float32), _c(idx, np.int32)
+    fmt, scales = _kv_scales(scales)
+    codes, idx = _c(codes, np.uint8), _c(idx, np.int32)
     B, n_max, Dh = codes.shape
     _, T, K = idx.shape
     out = np.zeros((B, T, K, 2 * Dh), np.float32)
-    _load().orc_gather_dequant(B, T, K, 2 * Dh, _p(codes), _p(scales), n_max, _p(idx), _p(out))
+    _load().orc_gather_dequant(fmt, B, T, K, 2 * Dh, _p(codes), _p(scales), n_max, _p(idx), _p(out))
     return out
 
 
@@ -179,15 +206,17 @@ def topk(scores, K, cand=None, want_values=False):
 
 # ---------------------------------------------------------------------------- attention
 def sparse_attend(q, codes, scales, idx, softmax_scale):
-    """(out [B][T][Hq][D] float64, lse [B][T][Hq] float64)."""
+    """(out [B][T][Hq][D] float64, lse [B][T][Hq] float64).  scales: fp32 [B][D] (one per
+    channel) or uint8 [B][n_max][D/16] (E4M3 per 16 channels of each entry)."""
     q = _c(q, np.float32)
     B, T, Hq, D = q.shape
-    codes, scales, idx = _c(codes, np.uint8), _c(scales, np.float32), _c(idx, np.int32)
+    fmt, scales = _kv_scales(scales)
+    codes, idx = _c(codes, np.uint8), _c(idx, np.int32)
     n_max = codes.shape[1]
     K = idx.shape[-1]
     out = np.empty((B, T, Hq, D), np.float64)
     lse = np.empty((B, T, Hq), np.float64)
-    _load().orc_sparse_attend(B, T, Hq, D, _p(q), _p(codes), _p(scales), n_max, _p(idx), K,
+    _load().orc_sparse_attend(fmt, B, T, Hq, D, _p(q), _p(codes), _p(scales), n_max, _p(idx), K,
                               float(softmax_scale), _p(out), _p(lse))
     return out, lse
 

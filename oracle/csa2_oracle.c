@@ -126,6 +126,48 @@ void orc_quantize_fp4(int B, int T, int D, const float* x, int64_t xsb, int64_t 
   }
 }
 
+/* FP4 main-KV quantisation in the pages' own layout: E2M1 values with one E4M3 scale per
+ * 16 consecutive channels of each entry and no second-level (global) scale.
+ * [N] "FP4 Main KV Cache To Halve Storage Again" (one scale per 16 channels, no global
+ * scale).  The pages do not say how the scale is chosen or rounded; reading (the plainest
+ * one): the group's absmax divided by 6 (the largest E2M1 magnitude), rounded to E4M3 like
+ * any other value (nearest, ties to even, saturating at 448), and the values divided by
+ * that rounded scale:
+ *   amax = max_{c in group} |x_c|;  sc = E4M3(fl32(amax / 6));  sv = value(sc)
+ *   code_c = E2M1(fl32(x_c / sv)) (sv == 0 gives code +0)
+ * A value can land above 6 after the division when the scale rounded down; E2M1 then
+ * saturates it to 6.  codes [B][n_max][D/2] as in orc_quantize_fp4; gscales
+ * [B][n_max][D/16] holds the E4M3 scale bytes.  D % 16 == 0. */
+void orc_quantize_fp4_g16(int B, int T, int D, const float* x, int64_t xsb, int64_t xst, const int32_t* n0,
+                          int64_t n_max, uint8_t* codes, uint8_t* gscales) {
+  const int G = D / 16;
+  for (int b = 0; b < B; ++b) {
+    int64_t base = n0 ? n0[b] : 0;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+      const float* xr = x + b * xsb + t * xst;
+      int64_t row = (int64_t)b * n_max + base + t;
+      uint8_t* crow = codes + row * (D / 2);
+      for (int g = 0; g < G; ++g) {
+        float amax = 0.0f;
+        for (int c = 16 * g; c < 16 * g + 16; ++c)
+          if (fabsf(xr[c]) > amax) amax = fabsf(xr[c]);
+        int sc = orc_e4m3_encode(amax / 6.0f);
+        float sv = (float)orc_e4m3_value(sc);
+        gscales[row * G + g] = (uint8_t)sc;
+        for (int c = 16 * g; c < 16 * g + 16; c += 2) {
+          int lo = 0, hi = 0;
+          if (sv != 0.0f) {
+            lo = orc_e2m1_encode(xr[c] / sv);
+            hi = orc_e2m1_encode(xr[c + 1] / sv);
+          }
+          crow[c / 2] = (uint8_t)(lo | (hi << 4));
+        }
+      }
+    }
+  }
+}
+
 /* E4M3 quantisation with one fp32 scale per row (indexer keys, per token):
  *   s = fl32(max_d |x_d| / 448); code_d = E4M3(fl32(x_d / s)); s == 0 gives code +0.
  * Reading: the pages keep the indexer low-bit ([N] "FP4 Main KV Cache": indexer q/k
@@ -149,23 +191,34 @@ void orc_quantize_fp8(int B, int T, int D, const float* x, int64_t xsb, int64_t 
   }
 }
 
-/* Dequantised value of channel c of an FP4 row: fl32(E2M1(code) * s_c). */
-static float fp4_dequant(const uint8_t* row, const float* s, int c) {
+/* Main-KV formats: 0 = one fp32 scale per (sequence, channel), scales [B][D];
+ *                  2 = one E4M3 scale per 16 channels of each entry, scales [B][n_max][D/16]. */
+enum { ORC_FMT_FP4_PER_CHANNEL = 0, ORC_FMT_FP4_G16 = 2 };
+
+/* Dequantised value of channel c of FP4 cache row j of sequence b:
+ *   per channel: fl32(E2M1(code) * s[b][c]);
+ *   per 16 channels: E2M1(code) * E4M3(gs[b][j][c / 16]) (exact in fp32). */
+static float fp4_dequant(int fmt, const uint8_t* codes, const void* scales, int b, int64_t n_max, int64_t j, int D,
+                         int c) {
+  const uint8_t* row = codes + ((int64_t)b * n_max + j) * (D / 2);
   int code = (c & 1) ? (row[c / 2] >> 4) : (row[c / 2] & 15);
-  return (float)(orc_e2m1_value(code) * (double)s[c]);
+  double s;
+  if (fmt == ORC_FMT_FP4_G16)
+    s = orc_e4m3_value(((const uint8_t*)scales)[((int64_t)b * n_max + j) * (D / 16) + c / 16]);
+  else
+    s = ((const float*)scales)[(int64_t)b * D + c];
+  return (float)(orc_e2m1_value(code) * s);
 }
 
 /* Gather + dequantise: out[b][t][k][c] = dequantised channel c of cache row idx[b][t][k];
  * rows with idx outside [0, n_max) (including the -1 padding) give 0. */
-void orc_gather_dequant(int B, int T, int K, int D, const uint8_t* codes, const float* scales, int64_t n_max,
+void orc_gather_dequant(int fmt, int B, int T, int K, int D, const uint8_t* codes, const void* scales, int64_t n_max,
                         const int32_t* idx, float* out) {
   for (int64_t r = 0; r < (int64_t)B * T * K; ++r) {
     int b = (int)(r / ((int64_t)T * K));
     int32_t j = idx[r];
     for (int c = 0; c < D; ++c)
-      out[r * D + c] = (j >= 0 && j < n_max)
-                           ? fp4_dequant(codes + ((int64_t)b * n_max + j) * (D / 2), scales + (int64_t)b * D, c)
-                           : 0.0f;
+      out[r * D + c] = (j >= 0 && j < n_max) ? fp4_dequant(fmt, codes, scales, b, n_max, j, D, c) : 0.0f;
   }
 }
 
@@ -308,9 +361,10 @@ void orc_topk(int B, int T, int64_t ncols, const double* scores, const int32_t* 
  *   l_hj = scale * q_h . v_j;  m_h = max_j l_hj;  Z_h = sum_j exp(l_hj - m_h)
  *   o_h  = sum_j exp(l_hj - m_h) v_j / Z_h;   lse_h = m_h + ln Z_h
  * An empty S gives o = 0, lse = -inf.  q is [B][T][Hq][D]; out [B][T][Hq][D]; lse
- * [B][T][Hq] (nullable). */
-void orc_sparse_attend(int B, int T, int Hq, int D, const float* q, const uint8_t* codes, const float* scales,
-                       int64_t n_max, const int32_t* idx, int K, double scale, double* out, double* lse) {
+ * [B][T][Hq] (nullable); fmt and scales as for fp4_dequant. */
+void orc_sparse_attend(int fmt, int B, int T, int Hq, int D, const float* q, const uint8_t* codes,
+                       const void* scales, int64_t n_max, const int32_t* idx, int K, double scale, double* out,
+                       double* lse) {
 #pragma omp parallel for schedule(dynamic)
   for (int64_t r = 0; r < (int64_t)B * T; ++r) {
     int b = (int)(r / T);
@@ -320,8 +374,7 @@ void orc_sparse_attend(int B, int T, int Hq, int D, const float* q, const uint8_
     for (int k = 0; k < K; ++k) {
       int32_t j = idx[r * K + k];
       if (j < 0 || j >= n_max) continue;
-      const uint8_t* row = codes + ((int64_t)b * n_max + j) * (D / 2);
-      for (int c = 0; c < D; ++c) v[(int64_t)n * D + c] = fp4_dequant(row, scales + (int64_t)b * D, c);
+      for (int c = 0; c < D; ++c) v[(int64_t)n * D + c] = fp4_dequant(fmt, codes, scales, b, n_max, j, D, c);
       ++n;
     }
     for (int h = 0; h < Hq; ++h) {
