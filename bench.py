@@ -41,16 +41,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_device_cache(wl, copies):
-    """Quantise the workload's cache on the GPU (one sequence at a time) and clone it."""
+def build_device_cache(wl, copies, kv_fmt=csa2.FMT_FP4_PER_CHANNEL):
+    """Quantise the workload's cache on the GPU (one sequence at a time) and clone it.  The
+    main KV takes one fp32 scale per channel, or (FMT_FP4_G16) one E4M3 scale per 16
+    channels of each entry."""
     B, N, D, dk = wl.B, wl.N, wl.D, wl.dk
     codes = torch.empty((B, N, D // 2), dtype=torch.uint8, device="cuda")
-    scales = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    if kv_fmt == csa2.FMT_FP4_G16:
+        scales = torch.empty((B, N, D // 16), dtype=torch.uint8, device="cuda")
+    else:
+        scales = torch.empty((B, D), dtype=torch.float32, device="cuda")
     k8 = torch.empty((B, N, dk), dtype=torch.uint8, device="cuda")
     ks = torch.empty((B, N), dtype=torch.float32, device="cuda")
     for b in range(B):
         x = torch.from_numpy(wl.main_kv(b)).to("cuda")
-        csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, x[None], codes[b:b + 1], scales[b:b + 1])
+        csa2.quantize_kv(kv_fmt, x[None], codes[b:b + 1], scales[b:b + 1])
         kf = torch.from_numpy(wl.index_keys(b)).to("cuda")
         csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, kf[None], k8[b:b + 1], ks[b:b + 1])
         torch.cuda.synchronize()
@@ -346,6 +351,43 @@ def run_decoder128k(args):
         "no_pool_ms_per_step": round(flat_ms, 5)}), flush=True)
 
 
+def run_group128k_g16(args):
+    """The 128K decode group (Full -> Reindex -> Reuse, 16 x 131072, Top-512) with the
+    pages' FP4 layout: one E4M3 scale per 16 channels of each entry (288 B per entry
+    instead of 256 B plus a per-sequence scale row)."""
+    wl = workloads.WORKLOADS["group128k"]
+    log("building cache (%d copies) ..." % args.copies)
+    caches = build_device_cache(wl, args.copies, csa2.FMT_FP4_G16)
+    layers = layer_inputs(wl)
+    plans = [csa2.GroupPlan([dict(L) for L in layers],
+                            csa2.GroupCache(c["n_keys"], c["codes"], c["scales"], c["k8"], c["ks"], wl.K,
+                                            wl.softmax_scale), out_dtype=torch.bfloat16) for c in caches]
+    for s in range(args.warmup):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    # as algorithmic_bytes, with 32 B of group scales gathered per entry instead of the
+    # per-sequence scale row
+    B, K, D = wl.B, wl.K, wl.D
+    alg = algorithmic_bytes(wl) + len(wl.modes) * (B * K * (D // 16) - B * D * 4)
+    gbs = alg / (ms_step / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "CSA2 decode queries/s at 128K context (FP4 with one E4M3 scale per 16 channels)",
+        "value": round(B / (ms_step / 1e3), 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": "group128k_g16: Full->Reindex->Reuse decode, B=16, N=131072, indexer 32x64 E4M3, "
+                               "Top-512, FP4 E2M1 main KV D=512 with one E4M3 scale per 16 channels (288 B/entry), "
+                               "64 heads bf16", "global_batch": B, "seq_len": wl.N, "layers": list(wl.modes),
+                   "cache_copies": args.copies},
+        "step_algorithmic_bytes": alg, "step_achieved_GBps": round(gbs, 1),
+        "step_pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
+
+
 def run_hier1m(args):
     """The 1M-entry two-level configuration (one sequence): coarse keys (64-entry block
     means, built once, not timed) -> score 16384 coarse keys -> top-256 blocks -> exact
@@ -428,10 +470,11 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="group128k",
-                    choices=["group128k", "prefill", "full64k", "hier1m", "decoder128k"],
+                    choices=["group128k", "prefill", "full64k", "hier1m", "decoder128k", "group128k_g16"],
                     help="group128k: the 128K decode group (the headline; default); prefill: the chunked-prefill "
                          "path; full64k: one Full layer at 64K; hier1m: the two-level indexer at 1M; decoder128k: "
-                         "the 20-layer decoder schedule at 128K with the candidate pool")
+                         "the 20-layer decoder schedule at 128K with the candidate pool; group128k_g16: the 128K group with "
+                         "the per-16-channel E4M3-scaled FP4 layout")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -457,6 +500,9 @@ def main():
         return
     if args.workload == "decoder128k":
         run_decoder128k(args)
+        return
+    if args.workload == "group128k_g16":
+        run_group128k_g16(args)
         return
     wl = workloads.WORKLOADS["group128k"]
     log("building cache (%d copies) ..." % args.copies)

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 # enums of include/csa2.h
 OK = 0
 F32, BF16 = 0, 1
-FMT_FP4_PER_CHANNEL, FMT_FP8_PER_TOKEN = 0, 1
+FMT_FP4_PER_CHANNEL, FMT_FP8_PER_TOKEN, FMT_FP4_G16 = 0, 1, 2
 SCALE_COMPUTE, SCALE_GIVEN = 0, 1
 PREC_FP32, PREC_FP8 = 0, 1
 FULL, REINDEX, REUSE = 0, 1, 2
@@ -58,7 +58,7 @@ class _GroupCache(ctypes.Structure):
                 ("kv_codes", ctypes.c_void_p), ("kv_scales", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("prec", ctypes.c_int), ("q_dtype", ctypes.c_int),
                 ("out_dtype", ctypes.c_int), ("softmax_scale", ctypes.c_float), ("pool_block", ctypes.c_int),
-                ("pool_blocks", ctypes.c_int)]
+                ("pool_blocks", ctypes.c_int), ("kv_fmt", ctypes.c_int)]
 
 
 _lib = None
@@ -77,14 +77,14 @@ def lib() -> ctypes.CDLL:
             "csa2_status_string": ([i], ctypes.c_char_p),
             "csa2_device_check": ([], i),
             "csa2_quantize_kv": ([i, i, i, i, i, p, i, i64, i64, p, i64, p, p, p], i),
-            "csa2_gather_dequant": ([i, i, i, i, p, p, i64, p, p, p], i),
+            "csa2_gather_dequant": ([i, i, i, i, i, p, p, i64, p, p, p], i),
             "csa2_index_score": ([i, i, i, i, i, p, i, p, p, p, i64, p, p, p, i, p, p, sz, p], i),
             "csa2_index_score_workspace_size": ([i, i, i64], sz),
             "csa2_topk": ([i, i, i64, p, p, i, p, p, p, sz, p], i),
             "csa2_topk_workspace_size": ([i, i, i64, i], sz),
             "csa2_index_topk": ([i, i, i, i, i, p, i, p, p, p, i64, p, p, p, i, i, p, p, p, sz, p], i),
             "csa2_index_topk_workspace_size": ([i, i, i64, i], sz),
-            "csa2_sparse_attend": ([i, i, i, i, p, i, p, p, i64, p, i, f, p, i, p, p, sz, p], i),
+            "csa2_sparse_attend": ([i, i, i, i, p, i, i, p, p, i64, p, i, f, p, i, p, p, sz, p], i),
             "csa2_sparse_attend_workspace_size": ([i, i, i, i, i, i], sz),
             "csa2_layer_group": ([p, i, p, p, sz, p], i),
             "csa2_layer_group_workspace_size": ([p, i], sz),
@@ -163,14 +163,20 @@ def quantize_kv(fmt: int, x: torch.Tensor, codes: torch.Tensor, scales: torch.Te
            "csa2_quantize_kv")
 
 
+def kv_format(scales: torch.Tensor) -> int:
+    """The main-KV layout a scales tensor belongs to: uint8 [B][n_max][D/16] E4M3 bytes is
+    the per-16-channel layout (FMT_FP4_G16), fp32 [B][D] the per-channel one."""
+    return FMT_FP4_G16 if scales.dtype == torch.uint8 else FMT_FP4_PER_CHANNEL
+
+
 def gather_dequant(codes: torch.Tensor, scales: torch.Tensor, idx: torch.Tensor,
                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
     B, n_max, Dh = codes.shape
     _, T, K = idx.shape
     if out is None:
         out = torch.empty((B, T, K, 2 * Dh), dtype=torch.float32, device=codes.device)
-    _check(lib().csa2_gather_dequant(B, T, K, 2 * Dh, _ptr(codes), _ptr(scales), n_max, _ptr(idx), _ptr(out),
-                                     _stream()), "csa2_gather_dequant")
+    _check(lib().csa2_gather_dequant(kv_format(scales), B, T, K, 2 * Dh, _ptr(codes), _ptr(scales), n_max, _ptr(idx),
+                                     _ptr(out), _stream()), "csa2_gather_dequant")
     return out
 
 
@@ -235,15 +241,17 @@ def sparse_attend(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, id
     qd = _dtype_code(q)
     nb = lib().csa2_sparse_attend_workspace_size(B, T, Hq, D, K, qd)
     ws = _workspace(nb, q.device)
-    _check(lib().csa2_sparse_attend(B, T, Hq, D, _ptr(q), qd, _ptr(codes), _ptr(scales), n_max, _ptr(idx), K,
-                                    float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws), nb,
-                                    _stream()), "csa2_sparse_attend")
+    _check(lib().csa2_sparse_attend(B, T, Hq, D, _ptr(q), qd, kv_format(scales), _ptr(codes), _ptr(scales), n_max,
+                                    _ptr(idx), K, float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse),
+                                    _ptr(ws), nb, _stream()), "csa2_sparse_attend")
     return out, lse
 
 
 # ------------------------------------------------------------------------------ layer group
 class GroupCache:
-    """The shared cache of a layer group (all device tensors)."""
+    """The shared cache of a layer group (all device tensors).  kv_scales: fp32 [B][D]
+    (one scale per channel) or uint8 [B][n_max][D/16] (one E4M3 scale per 16 channels of
+    each entry)."""
 
     def __init__(self, n_keys, kv_codes, kv_scales, k, k_scale, K, softmax_scale, prec=PREC_FP8, pool=None):
         """pool: None, or (block, blocks): Full layers leave the positions of their `blocks`
@@ -257,7 +265,7 @@ class GroupCache:
         pb, pn = self.pool if self.pool else (0, 0)
         return _GroupCache(B, H, dk, Hq, 2 * Dh, self.K, n_max, _ptr(self.n_keys), _ptr(self.kv_codes),
                            _ptr(self.kv_scales), _ptr(self.k), _ptr(self.k_scale), self.prec, q_dtype, out_dtype,
-                           float(self.softmax_scale), pb, pn)
+                           float(self.softmax_scale), pb, pn, kv_format(self.kv_scales))
 
 
 class GroupPlan:

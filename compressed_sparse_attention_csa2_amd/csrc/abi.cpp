@@ -103,6 +103,13 @@ int zero_topk(const TopkWs& t, int64_t R, hipStream_t st) {
 
 bool valid_dtype(int d) { return d == CSA2_F32 || d == CSA2_BF16; }
 
+// main-KV layouts the attention reads
+int check_kv_fmt(int kv_fmt, int D) {
+  if (kv_fmt != CSA2_FMT_FP4_PER_CHANNEL && kv_fmt != CSA2_FMT_FP4_G16) return CSA2_ERR_DTYPE;
+  if (kv_fmt == CSA2_FMT_FP4_G16 && D % 16) return CSA2_ERR_SHAPE;
+  return CSA2_OK;
+}
+
 int check_attend_shape(int B, int T, int Hq, int D, int K, int q_dtype, int out_dtype) {
   if (B < 1 || T < 1 || Hq < 1 || Hq > CSA2_MAX_HQ || D < 2 || D > CSA2_MAX_D || K < 1 || K > CSA2_MAX_K)
     return CSA2_ERR_SHAPE;
@@ -117,13 +124,13 @@ int check_attend_shape(int B, int T, int Hq, int D, int K, int q_dtype, int out_
   return CSA2_OK;
 }
 
-AttendArgs attend_args(int B, int T, int Hq, int D, int K, const void* q, int q_dtype, const uint8_t* codes,
-                       const float* scales, int64_t n_max, const int32_t* idx, float softmax_scale, void* out,
-                       int out_dtype, float* lse) {
+AttendArgs attend_args(int B, int T, int Hq, int D, int K, const void* q, int q_dtype, int kv_fmt,
+                       const uint8_t* codes, const void* scales, int64_t n_max, const int32_t* idx,
+                       float softmax_scale, void* out, int out_dtype, float* lse) {
   AttendArgs a;
   a.B = B; a.T = T; a.Hq = Hq; a.D = D; a.K = K;
   a.q = q; a.q_bf16 = (q_dtype == CSA2_BF16);
-  a.codes = codes; a.scales = scales; a.n_max = n_max; a.idx = idx;
+  a.codes = codes; a.scales = scales; a.g16 = (kv_fmt == CSA2_FMT_FP4_G16); a.n_max = n_max; a.idx = idx;
   a.softmax_scale = softmax_scale; a.out = out; a.out_bf16 = (out_dtype == CSA2_BF16); a.lse = lse;
   a.ctl = nullptr; a.hist2 = nullptr; a.candbuf = nullptr; a.cnt = nullptr; a.nreg = 0; a.idx_out = nullptr;
   a.part = nullptr;
@@ -188,8 +195,9 @@ const char* csa2_status_string(int status) {
 int csa2_device_check(void) { return check_device(); }
 
 int csa2_quantize_kv(int fmt, int scale_policy, int B, int T, int D, const void* x, int x_dtype, int64_t x_stride_b,
-                     int64_t x_stride_t, const int32_t* n0, int64_t n_max, uint8_t* codes, float* scales,
+                     int64_t x_stride_t, const int32_t* n0, int64_t n_max, uint8_t* codes, void* scales_v,
                      void* stream) {
+  float* scales = static_cast<float*>(scales_v);
   if (!x || !codes || !scales) return CSA2_ERR_NULL;
   if (!valid_dtype(x_dtype)) return CSA2_ERR_DTYPE;
   if (B < 1 || T < 1 || D < 1 || n_max < 1 || x_stride_t < D || x_stride_b < 0 || B > 65535) return CSA2_ERR_SHAPE;
@@ -210,16 +218,26 @@ int csa2_quantize_kv(int fmt, int scale_policy, int B, int T, int D, const void*
     return dev_status(launch_quantize_fp8(bf16, B, T, D, x, x_stride_b, x_stride_t, n0, n_max, codes, scales,
                                           S(stream)));
   }
+  if (fmt == CSA2_FMT_FP4_G16) {
+    if (D % 16) return CSA2_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return dev_status(launch_quantize_fp4_g16(bf16, B, T, D, x, x_stride_b, x_stride_t, n0, n_max, codes,
+                                              static_cast<uint8_t*>(scales_v), S(stream)));
+  }
   return CSA2_ERR_DTYPE;
 }
 
-int csa2_gather_dequant(int B, int T, int K, int D, const uint8_t* codes, const float* scales, int64_t n_max,
-                        const int32_t* idx, float* out, void* stream) {
+int csa2_gather_dequant(int kv_fmt, int B, int T, int K, int D, const uint8_t* codes, const void* scales,
+                        int64_t n_max, const int32_t* idx, float* out, void* stream) {
   if (!codes || !scales || !idx || !out) return CSA2_ERR_NULL;
+  if (kv_fmt != CSA2_FMT_FP4_PER_CHANNEL && kv_fmt != CSA2_FMT_FP4_G16) return CSA2_ERR_DTYPE;
   if (B < 1 || T < 1 || K < 1 || D < 8 || D % 8 || n_max < 1) return CSA2_ERR_SHAPE;
+  if (kv_fmt == CSA2_FMT_FP4_G16 && D % 16) return CSA2_ERR_SHAPE;
   int rc = check_device();
   if (rc) return rc;
-  return dev_status(launch_gather_dequant(B, T, K, D, codes, scales, n_max, idx, out, S(stream)));
+  return dev_status(
+      launch_gather_dequant(kv_fmt == CSA2_FMT_FP4_G16, B, T, K, D, codes, scales, n_max, idx, out, S(stream)));
 }
 
 size_t csa2_index_score_workspace_size(int B, int T, int64_t) {
@@ -301,19 +319,21 @@ size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int
   return align256(attend_ws_floats(B * T, Hq, D, K) * 4);
 }
 
-int csa2_sparse_attend(int B, int T, int Hq, int D, const void* q, int q_dtype, const uint8_t* kv_codes,
-                       const float* kv_scales, int64_t n_max, const int32_t* idx, int K, float softmax_scale,
+int csa2_sparse_attend(int B, int T, int Hq, int D, const void* q, int q_dtype, int kv_fmt, const uint8_t* kv_codes,
+                       const void* kv_scales, int64_t n_max, const int32_t* idx, int K, float softmax_scale,
                        void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !kv_codes || !kv_scales || !idx || !out) return CSA2_ERR_NULL;
   if (n_max < 1) return CSA2_ERR_SHAPE;
-  int rc = check_attend_shape(B, T, Hq, D, K, q_dtype, out_dtype);
+  int rc = check_kv_fmt(kv_fmt, D);
+  if (rc) return rc;
+  rc = check_attend_shape(B, T, Hq, D, K, q_dtype, out_dtype);
   if (rc) return rc;
   const size_t need = csa2_sparse_attend_workspace_size(B, T, Hq, D, K, q_dtype);
   if (need && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   rc = check_device();
   if (rc) return rc;
-  AttendArgs a = attend_args(B, T, Hq, D, K, q, q_dtype, kv_codes, kv_scales, n_max, idx, softmax_scale, out,
-                             out_dtype, lse);
+  AttendArgs a = attend_args(B, T, Hq, D, K, q, q_dtype, kv_fmt, kv_codes, kv_scales, n_max, idx, softmax_scale,
+                             out, out_dtype, lse);
   a.part = need ? static_cast<float*>(ws) : nullptr;
   return dev_status(launch_attend(a, S(stream)));
 }
@@ -379,6 +399,8 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   if (pool_cols(c) > kMaxTopkCols || c->n_max > INT32_MAX) return CSA2_ERR_SHAPE;
   rc = check_index_shape(c->prec, c->B, 1, c->H, c->dk, c->q_dtype, c->k_scale, c->n_max);
   if (rc) return rc;
+  rc = check_kv_fmt(c->kv_fmt, c->D);
+  if (rc) return rc;
   rc = check_attend_shape(c->B, 1, c->Hq, c->D, c->K, c->q_dtype, c->out_dtype);
   if (rc) return rc;
   for (int i = 0; i < n_layers; ++i) {
@@ -419,7 +441,8 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   };
   const int32_t* cur_pool = nullptr;  // the pool of the most recent Full layer
 
-  AttendArgs a = attend_args(c->B, 1, c->Hq, c->D, c->K, nullptr, c->q_dtype, c->kv_codes, c->kv_scales, c->n_max,
+  AttendArgs a = attend_args(c->B, 1, c->Hq, c->D, c->K, nullptr, c->q_dtype, c->kv_fmt, c->kv_codes, c->kv_scales,
+                             c->n_max,
                              nullptr, c->softmax_scale, nullptr, c->out_dtype, nullptr);
   a.part = part;
   const int32_t* last_idx = nullptr;

@@ -4,6 +4,9 @@
 // before attention; "Model Setup Numbers Without Jargon": 64 heads of dim 512.  The whole
 // dequantised entry is both key and value.
 //
+// Two main-KV layouts: one fp32 scale per (sequence, channel), and the pages' own one E4M3
+// scale per 16 channels of each entry (G16, see k_attend_part).
+//
 // MFMA path (bf16 queries, Hq % 16 == 0, D in {128, 256, 512}).  One block = one query
 // row x 16 heads (the MFMA M dimension) x one split of up to 512 selected entries, 16
 // waves, so the pages' Top-512 needs no merge; larger K runs several splits and a second
@@ -34,6 +37,18 @@ static_assert(kAttTPW * 16 * kAttWaves == kAttSplit, "QK tiles cover the split")
 
 // partials: part_o [R][S][Hq][D] normalised outputs, part_ml [R][S][Hq][2] (max, sum)
 
+// Two E4M3 codes (bytes 0 and 1 of w) -> two fp16 values (exact), low byte in the low half.
+// Placing the code's exponent and mantissa bits at the top of an fp16 gives the value times
+// 2^-8 (the exponent biases are 7 and 15), subnormal codes included; one packed multiply
+// by 256 restores it.
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+  const uint32_t sp = (w & 0xFFu) | ((w & 0xFF00u) << 8);
+  const uint32_t bits = ((sp & 0x007F007Fu) << 7) | ((sp & 0x00800080u) << 8);
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 v = __builtin_bit_cast(h2, bits) * (h2){(_Float16)256.0f, (_Float16)256.0f};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xFFFFu) | (hi16 << 16); }
 
 // E2M1 pair in byte BS of `word` -> two fp16 values (exact; scale 1), low nibble first.
@@ -49,14 +64,16 @@ __device__ __forceinline__ v8h decode8_f16(uint32_t word) {
   return __builtin_bit_cast(v8h, u);
 }
 
-template <int D, int WPT>
+template <int D, int WPT, bool G16>
 struct AttLds {
   static constexpr int kApad = D + 8;           // fp16 per A row (padding against bank conflicts)
   static constexpr int kPpad = kAttSplit + 8;
+  static constexpr int kSpad = kAttSplit + 8;   // fp16 per group row of the entry scales (G16)
   static constexpr size_t kA = (size_t)kAttHeads * kApad * 2;
   static constexpr size_t kP = (size_t)kAttHeads * kPpad * 2;
-  static constexpr size_t kO = (size_t)WPT * kAttHeads * D * 4;  // per entry group, after sA/sP are dead
-  static constexpr size_t kAP = kA + kP;
+  static constexpr size_t kS = G16 ? (size_t)(D / 16) * kSpad * 2 : 0;  // [group][entry] fp16 scales
+  static constexpr size_t kO = (size_t)WPT * kAttHeads * D * 4;  // per entry group, after sA/sP/sS are dead
+  static constexpr size_t kAP = kA + kP + kS;
   static constexpr size_t kWork = kAP > kO ? kAP : kO;
   static constexpr size_t kUnion = kWork > sizeof(FinalizeSmem) ? kWork : sizeof(FinalizeSmem);
 };
@@ -66,10 +83,14 @@ struct AttLds {
 // block of the row does this identically; block (split 0, head group 0) writes idx_out).
 // With one split the block writes the final output; otherwise it writes its partial
 // (normalised output, running max, sum) for k_attend_combine.
-template <int D, bool FROM_CAND>
+// G16: the cache holds one E4M3 scale per 16 channels of each entry (the pages' layout).
+// The scale no longer factors out of the contractions; instead the split's scales are
+// staged in LDS as fp16, [group][entry], and multiply the fp16 key / value operands after
+// the E2M1 conversion (E2M1 * E4M3 is exact in fp16, so the operands stay exact).
+template <int D, bool FROM_CAND, bool G16>
 __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     int T, int Hq, int K, int S, const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
-    const float* __restrict__ scales, int64_t n_max, const int32_t* __restrict__ idx, const RowCtl* __restrict__ ctl,
+    const void* __restrict__ scales_v, int64_t n_max, const int32_t* __restrict__ idx, const RowCtl* __restrict__ ctl,
     const uint32_t* __restrict__ hist2, const uint2* __restrict__ candbuf, const uint32_t* __restrict__ cnt, int nreg,
     int32_t* __restrict__ idx_out, float softmax_scale, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
     float* __restrict__ part, float* __restrict__ part_ml) {
@@ -77,8 +98,9 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   constexpr int kCT = D / 128;                 // 128-channel tiles
   constexpr int kWPT = (kAttWaves / kCT < kAttSplit / 32) ? kAttWaves / kCT : kAttSplit / 32;  // waves per tile in PV
   constexpr int kEPW = kAttSplit / kWPT;       // entries per wave in PV (a multiple of 32)
-  using L = AttLds<D, kWPT>;
-  __shared__ float s_scale[D];
+  using L = AttLds<D, kWPT, G16>;
+  constexpr int kNG = D / 16;                  // scale groups per entry (G16)
+  __shared__ float s_scale[G16 ? 1 : D];
   __shared__ int32_t s_idx[FROM_CAND ? CSA2_MAX_K_DEV : kAttSplit];
   __shared__ float s_red[kAttWaves][kAttHeads];
   __shared__ float s_m[kAttHeads], s_l[kAttHeads];
@@ -86,7 +108,9 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   __shared__ __align__(16) unsigned char s_u[L::kUnion];
   uint16_t* sA = reinterpret_cast<uint16_t*>(s_u);
   uint16_t* sP = reinterpret_cast<uint16_t*>(s_u + L::kA);
-  float* sO = reinterpret_cast<float*>(s_u);  // [kWPT][16][D], used once sA and sP are dead
+  uint16_t* sS = reinterpret_cast<uint16_t*>(s_u + L::kA + L::kP);  // G16: [kNG][kSpad] fp16
+  float* sO = reinterpret_cast<float*>(s_u);  // [kWPT][16][D], used once sA, sP, sS are dead
+  const float* scales = static_cast<const float*>(scales_v);
 
   const int split = blockIdx.x, hg = blockIdx.y, r = blockIdx.z;
   const int b = r / T;
@@ -106,7 +130,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     const int ic = i < kQItems ? i : kQItems - 1;
     qraw[it] = *reinterpret_cast<const uint4*>(qb + (int64_t)(ic / (D / 8)) * D + (ic % (D / 8)) * 8);
   }
-  for (int i = tid; i < D; i += kAttThreads) s_scale[i] = scales[(int64_t)b * D + i];
+  if (!G16)
+    for (int i = tid; i < D; i += kAttThreads) s_scale[i] = scales[(int64_t)b * D + i];
   const int32_t* sel;                           // the split's entries (LDS)
   if (FROM_CAND) {
     FinalizeSmem& fs = *reinterpret_cast<FinalizeSmem*>(s_u);
@@ -131,6 +156,32 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   //      query preparation.  Unconditional loads from a valid row (row 0 for skipped
   //      entries) keep them branch-free; skipped entries are masked in the logits.
   const uint8_t* cb = codes + (int64_t)b * n_max * kRowBytes;
+  // G16: the split's entry scales in chunks of 16 (8 when D = 128) groups of one entry,
+  // issued before the rows so that waiting for them (to stage them in LDS) does not wait
+  // for the rows; the lanes of a wave take consecutive entries of one chunk column.
+  // Skipped entries get scale 0 (their logits are masked and their p is 0 anyway).
+  constexpr int kCB = kNG < 16 ? kNG : 16;     // scale bytes per chunk
+  constexpr int kGC = kNG / kCB;               // chunks per entry
+  constexpr int kScChunks = kAttSplit * kGC;
+  constexpr int kScPer = G16 ? (kScChunks + kAttThreads - 1) / kAttThreads : 1;
+  uint4 gsw[kScPer];
+  if (G16) {
+    const uint8_t* gsb = static_cast<const uint8_t*>(scales_v) + (int64_t)b * n_max * kNG;
+#pragma unroll
+    for (int it = 0; it < kScPer; ++it) {
+      const int i = tid + it * kAttThreads;
+      const int ic = i < kScChunks ? i : kScChunks - 1;
+      const int32_t j = sel[ic % kAttSplit];
+      const uint8_t* src = gsb + (int64_t)(j >= 0 ? j : 0) * kNG + kCB * (ic / kAttSplit);
+      if (kCB == 16) {
+        gsw[it] = *reinterpret_cast<const uint4*>(src);
+      } else {
+        const uint2 h = *reinterpret_cast<const uint2*>(src);
+        gsw[it] = make_uint4(h.x, h.y, 0u, 0u);
+      }
+      if (j < 0) gsw[it] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
   uint4 kw[kAttTPW][kCT];
   int32_t jt[kAttTPW];
 #pragma unroll
@@ -153,7 +204,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     const uint32_t wds[4] = {qraw[it].x, qraw[it].y, qraw[it].z, qraw[it].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      qv[it][e] = bf16_to_f32((uint16_t)(wds[e >> 1] >> (16 * (e & 1)))) * s_scale[c + e];
+      qv[it][e] = bf16_to_f32((uint16_t)(wds[e >> 1] >> (16 * (e & 1)))) * (G16 ? 1.0f : s_scale[c + e]);
       qmax = fmaxf(qmax, fabsf(qv[it][e]));
     }
   }
@@ -187,6 +238,21 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     }
     *reinterpret_cast<uint4*>(&sA[h * L::kApad + c]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
+  if (G16) {  // the scales as fp16, [group][entry]
+#pragma unroll
+    for (int it = 0; it < kScPer; ++it) {
+      const int i = tid + it * kAttThreads;
+      if (i >= kScChunks) break;
+      const int e = i % kAttSplit, grp0 = kCB * (i / kAttSplit);
+      const uint32_t wd[4] = {gsw[it].x, gsw[it].y, gsw[it].z, gsw[it].w};
+#pragma unroll
+      for (int k2 = 0; k2 < kCB / 2; ++k2) {
+        const uint32_t s2 = e4m3x2_to_f16x2(wd[k2 >> 1] >> (16 * (k2 & 1)));
+        sS[(grp0 + 2 * k2) * L::kSpad + e] = (uint16_t)(s2 & 0xFFFFu);
+        sS[(grp0 + 2 * k2 + 1) * L::kSpad + e] = (uint16_t)(s2 >> 16);
+      }
+    }
+  }
   __syncthreads();
 
   // ---- phase 1b: logits of this wave's kAttTPW tiles of 16 entries
@@ -194,12 +260,19 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
 #pragma unroll
   for (int t = 0; t < kAttTPW; ++t) {
     v4f a = {0.f, 0.f, 0.f, 0.f};
+    const int el = (wave * kAttTPW + t) * 16 + n16;  // this lane's entry in the split
 #pragma unroll
     for (int i = 0; i < kCT; ++i) {
       const uint32_t wd[4] = {kw[t][i].x, kw[t][i].y, kw[t][i].z, kw[t][i].w};
+      _Float16 gs[2] = {(_Float16)1.0f, (_Float16)1.0f};
+      if (G16) {  // channels 128 i + 32 g + [0, 32): groups 8 i + 2 g and 8 i + 2 g + 1
+        gs[0] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g) * L::kSpad + el]);
+        gs[1] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g + 1) * L::kSpad + el]);
+      }
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
-        const v8h bv = decode8_f16(wd[sub]);
+        v8h bv = decode8_f16(wd[sub]);
+        if (G16) bv = bv * gs[sub >> 1];
         const v8h av = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
         a = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, a, 0, 0, 0);
       }
@@ -277,6 +350,9 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     for (int ks = 0; ks < kEPW / 32; ++ks) {
       const int el = eq * kEPW + 32 * ks + 8 * g;  // first of this lane's 8 entries
       const v8h pa = *reinterpret_cast<const v8h*>(&sP[n16 * L::kPpad + el]);
+      // G16: the scales of entries el..el+7 in this lane's group (channels 128 ct + 8 n16 ..)
+      v8h sc = {};
+      if (G16) sc = *reinterpret_cast<const v8h*>(&sS[(8 * ct + (n16 >> 1)) * L::kSpad + el]);
       uint32_t xe[4], xo[4];
 #pragma unroll
       for (int p2 = 0; p2 < 4; ++p2) {
@@ -288,7 +364,9 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   {                                                                                                          \
     const uint4 bw = make_uint4(cvt_pair_f16<BS>(X[0]), cvt_pair_f16<BS>(X[1]), cvt_pair_f16<BS>(X[2]),      \
                                 cvt_pair_f16<BS>(X[3]));                                                     \
-    acc[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(v8h, bw), acc[M], 0, 0, 0);       \
+    v8h bv = __builtin_bit_cast(v8h, bw);                                                                    \
+    if (G16) bv = bv * sc;                                                                                   \
+    acc[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, acc[M], 0, 0, 0);                                \
   }
       CSA2_PV_MFMA(0, xe, 0) CSA2_PV_MFMA(1, xo, 0) CSA2_PV_MFMA(2, xe, 1) CSA2_PV_MFMA(3, xo, 1)
       CSA2_PV_MFMA(4, xe, 2) CSA2_PV_MFMA(5, xo, 2) CSA2_PV_MFMA(6, xe, 3) CSA2_PV_MFMA(7, xo, 3)
@@ -328,8 +406,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     for (int m = 0; m < 8; ++m) o[m] *= inv_l;
     const int h = hg * kAttHeads + hl;
     if (S == 1) {
+      if (!G16) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) o[m] *= s_scale[c + m];
+        for (int m = 0; m < 8; ++m) o[m] *= s_scale[c + m];
+      }
       const int64_t oi = ((int64_t)r * Hq + h) * D + c;
       if (out_bf16) {
         uint32_t w4[4];
@@ -361,7 +441,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     for (int i = tid; i < K; i += kAttThreads) idx_out[(int64_t)r * K + i] = s_idx[i];
 }
 
-// Merge the splits of (row, head group, channel tile) by log-sum-exp and scale by s_c.
+// Merge the splits of (row, head group, channel tile) by log-sum-exp and scale by s_c
+// (scales null: the G16 layout, whose scales were applied inside the splits).
 // Thread t: head t / 16 of the group, channels 128 ct + 8 (t % 16) + [0, 8); all split
 // loads are issued before any is used.
 template <int D>
@@ -387,8 +468,11 @@ __global__ __launch_bounds__(256) void k_attend_combine(int T, int Hq, int S, co
       pv[s][1] = src[1];
     }
   }
-  const float4 sc0 = *reinterpret_cast<const float4*>(scales + (int64_t)b * D + c);
-  const float4 sc1 = *reinterpret_cast<const float4*>(scales + (int64_t)b * D + c + 4);
+  float4 sc0 = make_float4(1.f, 1.f, 1.f, 1.f), sc1 = sc0;
+  if (scales) {
+    sc0 = *reinterpret_cast<const float4*>(scales + (int64_t)b * D + c);
+    sc1 = *reinterpret_cast<const float4*>(scales + (int64_t)b * D + c + 4);
+  }
   if (tid < kAttHeads) {
     const float* ml = part_ml + ((int64_t)r * S) * Hq * 2;
     const int hh = hg * kAttHeads + tid;
@@ -439,10 +523,20 @@ __global__ __launch_bounds__(256) void k_attend_combine(int T, int Hq, int S, co
   }
 }
 
-// fp32 path: one block per (row, head)
+// fp32 path: one block per (row, head).  Dequantised value of channel c of cache row j of
+// sequence b: E2M1 * s_c (per channel) or E2M1 * E4M3 group scale (G16).
+template <bool G16>
+__device__ __forceinline__ float deq_f32(const uint8_t* cb, const uint8_t* gsb, const float* s_scale, int D,
+                                         int32_t j, int c) {
+  const uint32_t byte = cb[(int64_t)j * (D / 2) + c / 2];
+  const float e = e2m1_value((c & 1) ? (byte >> 4) : (byte & 15u));
+  return G16 ? e * e4m3_value(gsb[(int64_t)j * (D / 16) + c / 16]) : e * s_scale[c];
+}
+
+template <bool G16>
 __global__ __launch_bounds__(256) void k_attend_f32(int T, int Hq, int D, int K, const float* __restrict__ q,
                                                     const uint8_t* __restrict__ codes,
-                                                    const float* __restrict__ scales, int64_t n_max,
+                                                    const void* __restrict__ scales_v, int64_t n_max,
                                                     const int32_t* __restrict__ idx, float softmax_scale,
                                                     float* __restrict__ out, float* __restrict__ lse) {
   __shared__ float s_q[CSA2_MAX_D_DEV];
@@ -455,24 +549,20 @@ __global__ __launch_bounds__(256) void k_attend_f32(int T, int Hq, int D, int K,
   const float* qh = q + ((int64_t)r * Hq + h) * D;
   for (int c = tid; c < D; c += 256) {
     s_q[c] = qh[c];
-    s_scale[c] = scales[(int64_t)b * D + c];
+    if (!G16) s_scale[c] = static_cast<const float*>(scales_v)[(int64_t)b * D + c];
   }
   for (int e = tid; e < K; e += 256) {
     const int32_t j = idx[(int64_t)r * K + e];
     s_idx[e] = (j >= 0 && j < n_max) ? j : -1;
   }
   __syncthreads();
-  const int rowb = D / 2;
-  const uint8_t* cb = codes + (int64_t)b * n_max * rowb;
+  const uint8_t* cb = codes + (int64_t)b * n_max * (D / 2);
+  const uint8_t* gsb = G16 ? static_cast<const uint8_t*>(scales_v) + (int64_t)b * n_max * (D / 16) : nullptr;
   for (int e = wave; e < K; e += 4) {
     const int32_t j = s_idx[e];
     float dot = 0.0f;
     if (j >= 0) {
-      for (int c = lane; c < D; c += 64) {
-        const uint32_t byte = cb[(int64_t)j * rowb + c / 2];
-        const float v = e2m1_value((c & 1) ? (byte >> 4) : (byte & 15u)) * s_scale[c];
-        dot = fmaf(s_q[c], v, dot);
-      }
+      for (int c = lane; c < D; c += 64) dot = fmaf(s_q[c], deq_f32<G16>(cb, gsb, s_scale, D, j, c), dot);
     }
     dot = wave_sum(dot);
     if (lane == 0) s_logit[e] = (j >= 0) ? dot * softmax_scale : kNegInf;
@@ -501,9 +591,7 @@ __global__ __launch_bounds__(256) void k_attend_f32(int T, int Hq, int D, int K,
     for (int e = 0; e < K; ++e) {
       const int32_t j = s_idx[e];
       if (j < 0) continue;
-      const uint32_t byte = cb[(int64_t)j * rowb + c / 2];
-      const float v = e2m1_value((c & 1) ? (byte >> 4) : (byte & 15u)) * s_scale[c];
-      o = fmaf(s_logit[e], v, o);
+      o = fmaf(s_logit[e], deq_f32<G16>(cb, gsb, s_scale, D, j, c), o);
     }
     out[((int64_t)r * Hq + h) * D + c] = o * inv;
   }
@@ -518,33 +606,48 @@ size_t attend_ws_floats(int R, int Hq, int D, int K) {
   return (size_t)R * S * Hq * D + (size_t)R * S * Hq * 2;
 }
 
-template <int D, bool FC>
+template <int D, bool FC, bool G16>
 static void launch_mfma(const AttendArgs& a, int S, hipStream_t st) {
   dim3 g(S, a.Hq / kAttHeads, a.B * a.T);
   float* part_ml = a.part ? a.part + (size_t)a.B * a.T * S * a.Hq * D : nullptr;
-  hipLaunchKernelGGL((k_attend_part<D, FC>), g, dim3(kAttThreads), 0, st, a.T, a.Hq, a.K, S, (const uint16_t*)a.q,
-                     a.codes, a.scales, a.n_max, a.idx, a.ctl, a.hist2, a.candbuf, a.cnt, a.nreg, a.idx_out,
-                     a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml);
+  hipLaunchKernelGGL((k_attend_part<D, FC, G16>), g, dim3(kAttThreads), 0, st, a.T, a.Hq, a.K, S,
+                     (const uint16_t*)a.q, a.codes, a.scales, a.n_max, a.idx, a.ctl, a.hist2, a.candbuf, a.cnt,
+                     a.nreg, a.idx_out, a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml);
   if (S > 1)
     hipLaunchKernelGGL(k_attend_combine<D>, dim3(a.Hq / kAttHeads * (D / 128), a.B * a.T), dim3(256), 0, st, a.T,
-                       a.Hq, S, a.scales, (const float*)a.part, (const float*)part_ml, a.out, (int)a.out_bf16, a.lse);
+                       a.Hq, S, G16 ? nullptr : static_cast<const float*>(a.scales), (const float*)a.part,
+                       (const float*)part_ml, a.out, (int)a.out_bf16, a.lse);
+}
+
+template <int D>
+static void launch_mfma_d(const AttendArgs& a, int S, hipStream_t st) {
+  const bool fc = a.candbuf != nullptr;
+  if (a.g16)
+    fc ? launch_mfma<D, true, true>(a, S, st) : launch_mfma<D, false, true>(a, S, st);
+  else
+    fc ? launch_mfma<D, true, false>(a, S, st) : launch_mfma<D, false, false>(a, S, st);
 }
 
 int launch_attend(const AttendArgs& a, hipStream_t st) {
   const int R = a.B * a.T;
   if (!a.q_bf16) {
     if (a.candbuf) return -1;  // the fp32 path takes given indices
-    hipLaunchKernelGGL(k_attend_f32, dim3(a.Hq, R), dim3(256), 0, st, a.T, a.Hq, a.D, a.K, (const float*)a.q,
-                       a.codes, a.scales, a.n_max, a.idx, a.softmax_scale, (float*)a.out, a.lse);
+    if (a.g16)
+      hipLaunchKernelGGL(k_attend_f32<true>, dim3(a.Hq, R), dim3(256), 0, st, a.T, a.Hq, a.D, a.K,
+                         (const float*)a.q, a.codes, a.scales, a.n_max, a.idx, a.softmax_scale, (float*)a.out,
+                         a.lse);
+    else
+      hipLaunchKernelGGL(k_attend_f32<false>, dim3(a.Hq, R), dim3(256), 0, st, a.T, a.Hq, a.D, a.K,
+                         (const float*)a.q, a.codes, a.scales, a.n_max, a.idx, a.softmax_scale, (float*)a.out,
+                         a.lse);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   const int S = attend_splits(a.K);
   if (S > 1 && !a.part) return -1;
-  const bool fc = a.candbuf != nullptr;
   switch (a.D) {
-    case 128: fc ? launch_mfma<128, true>(a, S, st) : launch_mfma<128, false>(a, S, st); break;
-    case 256: fc ? launch_mfma<256, true>(a, S, st) : launch_mfma<256, false>(a, S, st); break;
-    case 512: fc ? launch_mfma<512, true>(a, S, st) : launch_mfma<512, false>(a, S, st); break;
+    case 128: launch_mfma_d<128>(a, S, st); break;
+    case 256: launch_mfma_d<256>(a, S, st); break;
+    case 512: launch_mfma_d<512>(a, S, st); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -19,6 +19,9 @@ int launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
 
 int launch_quantize_fp4(bool compute, bool bf16, int B, int T, int D, const void* x, int64_t xsb, int64_t xst,
                         const int32_t* n0, int64_t n_max, uint8_t* codes, float* scales, hipStream_t st);
+// the pages' layout: codes [B][n_max][D/2], gscales [B][n_max][D/16] E4M3 bytes (D % 16 == 0)
+int launch_quantize_fp4_g16(bool bf16, int B, int T, int D, const void* x, int64_t xsb, int64_t xst,
+                            const int32_t* n0, int64_t n_max, uint8_t* codes, uint8_t* gscales, hipStream_t st);
 int launch_quantize_fp8(bool bf16, int B, int T, int D, const void* x, int64_t xsb, int64_t xst, const int32_t* n0,
                         int64_t n_max, uint8_t* codes, float* scales, hipStream_t st);
 
@@ -71,7 +74,8 @@ struct AttendArgs {
   const void* q;
   bool q_bf16;
   const uint8_t* codes;
-  const float* scales;
+  const void* scales;     // fp32 [B][D] (per channel) or E4M3 bytes [B][n_max][D/16] (g16)
+  bool g16;
   int64_t n_max;
   const int32_t* idx;
   float softmax_scale;
@@ -91,8 +95,8 @@ int launch_attend(const AttendArgs& a, hipStream_t st);
 int attend_splits(int K);
 size_t attend_ws_floats(int R, int Hq, int D, int K);
 
-int launch_gather_dequant(int B, int T, int K, int D, const uint8_t* codes, const float* scales, int64_t n_max,
-                          const int32_t* idx, float* out, hipStream_t st);
+int launch_gather_dequant(bool g16, int B, int T, int K, int D, const uint8_t* codes, const void* scales,
+                          int64_t n_max, const int32_t* idx, float* out, hipStream_t st);
 int launch_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int block, const uint8_t* k8,
                        const float* k_scale, uint8_t* kb8, float* kb_scale, hipStream_t st);
 }  // namespace csa2

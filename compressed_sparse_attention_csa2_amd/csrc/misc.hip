@@ -4,11 +4,13 @@
 
 namespace csa2 {
 
-// out[r][k][c] = fl32(E2M1(code) * s_c) of cache row idx[r][k]; 0 for rows outside
-// [0, n_max).  One thread per 8 channels.  ("values are dequantized back before
-// attention": "FP4 Main KV Cache To Halve Storage Again", paper notes.)
+// out[r][k][c] = fl32(E2M1(code) * s_c) of cache row idx[r][k] (G16: the scale of the
+// entry's 16-channel group, E4M3); 0 for rows outside [0, n_max).  One thread per 8
+// channels.  ("values are dequantized back before attention": "FP4 Main KV Cache To
+// Halve Storage Again", paper notes.)
+template <bool G16>
 __global__ __launch_bounds__(256) void k_gather_dequant(int T, int K, int D, const uint8_t* __restrict__ codes,
-                                                        const float* __restrict__ scales, int64_t n_max,
+                                                        const void* __restrict__ scales_v, int64_t n_max,
                                                         const int32_t* __restrict__ idx, float* __restrict__ out,
                                                         int64_t total_words) {
   const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -20,10 +22,17 @@ __global__ __launch_bounds__(256) void k_gather_dequant(int T, int K, int D, con
   const int32_t j = idx[rk];
   float v[8];
   if (j >= 0 && j < n_max) {
-    const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + ((int64_t)b * n_max + j) * (D / 2) + w8 * 4);
-    const float* s = scales + (int64_t)b * D + w8 * 8;
+    const int64_t row = (int64_t)b * n_max + j;
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + row * (D / 2) + w8 * 4);
+    if (G16) {
+      const float s = e4m3_value(static_cast<const uint8_t*>(scales_v)[row * (D / 16) + w8 / 2]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = e2m1_value((word >> (4 * i)) & 15u) * s[i];
+      for (int i = 0; i < 8; ++i) v[i] = e2m1_value((word >> (4 * i)) & 15u) * s;
+    } else {
+      const float* s = static_cast<const float*>(scales_v) + (int64_t)b * D + w8 * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = e2m1_value((word >> (4 * i)) & 15u) * s[i];
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = 0.0f;
@@ -78,12 +87,15 @@ __global__ __launch_bounds__(256) void k_coarse_keys(int64_t n_max, const int32_
   if (lane == 0) kb_scale[orow] = s;
 }
 
-int launch_gather_dequant(int B, int T, int K, int D, const uint8_t* codes, const float* scales, int64_t n_max,
-                          const int32_t* idx, float* out, hipStream_t st) {
+int launch_gather_dequant(bool g16, int B, int T, int K, int D, const uint8_t* codes, const void* scales,
+                          int64_t n_max, const int32_t* idx, float* out, hipStream_t st) {
   const int64_t total = (int64_t)B * T * K * (D / 8);
   if (total == 0) return 0;
-  hipLaunchKernelGGL(k_gather_dequant, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, T, K, D, codes,
-                     scales, n_max, idx, out, total);
+  const dim3 g((unsigned)((total + 255) / 256));
+  if (g16)
+    hipLaunchKernelGGL(k_gather_dequant<true>, g, dim3(256), 0, st, T, K, D, codes, scales, n_max, idx, out, total);
+  else
+    hipLaunchKernelGGL(k_gather_dequant<false>, g, dim3(256), 0, st, T, K, D, codes, scales, n_max, idx, out, total);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -1,4 +1,5 @@
-// Write side: FP4 (E2M1, per-channel fp32 scale) main-KV pack and E4M3 per-row quantise.
+// Write side: FP4 (E2M1, per-channel fp32 scale, or one E4M3 scale per 16 channels of each
+// entry) main-KV pack and E4M3 per-row quantise.
 // "FP4 Main KV Cache To Halve Storage Again" (paper notes) / 3.5 of the Chinese reading:
 // the main KV is stored as E2M1 and dequantised before attention.  The per-channel scale
 // is the absmax over the sequence's rows divided by 6 (the largest E2M1 magnitude).
@@ -79,6 +80,41 @@ __global__ __launch_bounds__(256) void k_fp4_pack_bytes(int T, int D, const XT* 
   codes[((int64_t)b * n_max + row) * bytes + i] = (uint8_t)(lo | hi << 4);
 }
 
+// The pages' layout: one E4M3 scale per 16 channels of each entry, no global scale.  One
+// thread per (row, group of 16 channels): sc = E4M3(fl32(amax / 6)), codes E2M1(fl32(x /
+// value(sc))).  Consecutive threads take consecutive groups, so the 64 B reads and the 8 B
+// code writes are contiguous across a wave.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_fp4g16_pack(int T, int D, const XT* __restrict__ x, int64_t xsb, int64_t xst,
+                                                     const int32_t* __restrict__ n0, int64_t n_max,
+                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ gscales) {
+  const int groups = D / 16;
+  const int64_t gi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int b = blockIdx.y;
+  if (gi >= (int64_t)T * groups) return;
+  const int t = (int)(gi / groups), g = (int)(gi % groups);
+  const int64_t row = (int64_t)(n0 ? n0[b] : 0) + t;
+  if (row < 0 || row >= n_max) return;
+  const XT* xr = x + b * xsb + t * xst + 16 * g;
+  float v[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = load_as_f32(xr + i);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const uint32_t sc = e4m3_encode(amax / 6.0f);
+  const float sv = e4m3_value(sc);
+  uint32_t w[2] = {0u, 0u};
+  if (sv != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i >> 3] |= e2m1_encode(v[i] / sv) << (4 * (i & 7));
+  }
+  const int64_t orow = (int64_t)b * n_max + row;
+  *reinterpret_cast<uint2*>(codes + orow * (D / 2) + 8 * g) = make_uint2(w[0], w[1]);
+  gscales[orow * groups + g] = (uint8_t)sc;
+}
+
 // E4M3 per row: one wave per row, lanes stride over the row's D values.
 template <typename XT>
 __global__ __launch_bounds__(256) void k_fp8_rows(int T, int D, const XT* __restrict__ x, int64_t xsb, int64_t xst,
@@ -137,6 +173,19 @@ int launch_quantize_fp4(bool compute, bool bf16, int B, int T, int D, const void
   if (bf16)
     return quantize_fp4_t(compute, B, T, D, (const uint16_t*)x, xsb, xst, n0, n_max, codes, scales, st);
   return quantize_fp4_t(compute, B, T, D, (const float*)x, xsb, xst, n0, n_max, codes, scales, st);
+}
+
+int launch_quantize_fp4_g16(bool bf16, int B, int T, int D, const void* x, int64_t xsb, int64_t xst,
+                            const int32_t* n0, int64_t n_max, uint8_t* codes, uint8_t* gscales, hipStream_t st) {
+  const int64_t work = (int64_t)T * (D / 16);
+  dim3 g((unsigned)((work + 255) / 256), B);
+  if (bf16)
+    hipLaunchKernelGGL(k_fp4g16_pack<uint16_t>, g, dim3(256), 0, st, T, D, (const uint16_t*)x, xsb, xst, n0, n_max,
+                       codes, gscales);
+  else
+    hipLaunchKernelGGL(k_fp4g16_pack<float>, g, dim3(256), 0, st, T, D, (const float*)x, xsb, xst, n0, n_max, codes,
+                       gscales);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_quantize_fp8(bool bf16, int B, int T, int D, const void* x, int64_t xsb, int64_t xst, const int32_t* n0,

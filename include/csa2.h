@@ -56,14 +56,14 @@ typedef enum {
 } csa2_status;
 
 typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
-typedef enum { CSA2_FMT_FP4_PER_CHANNEL = 0, CSA2_FMT_FP8_PER_TOKEN = 1 } csa2_fmt;
+typedef enum { CSA2_FMT_FP4_PER_CHANNEL = 0, CSA2_FMT_FP8_PER_TOKEN = 1, CSA2_FMT_FP4_G16 = 2 } csa2_fmt;
 typedef enum { CSA2_SCALE_COMPUTE = 0, CSA2_SCALE_GIVEN = 1 } csa2_scale_policy;
 typedef enum { CSA2_PREC_FP32 = 0, CSA2_PREC_FP8 = 1 } csa2_index_prec;
 typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
 
 /* Limits of this build. */
 #define CSA2_MAX_K 2048      /* Top-K */
-#define CSA2_MAX_D 512       /* main-KV dim (multiple of 32) */
+#define CSA2_MAX_D 512       /* main-KV dim */
 #define CSA2_MAX_HQ 128      /* attention heads */
 #define CSA2_MAX_DK 256      /* indexer dim (fp32 indexer); the fp8 indexer needs dk == 64 */
 #define CSA2_MAX_H 64        /* indexer heads (fp32 indexer); the fp8 indexer needs H == 32 */
@@ -91,20 +91,30 @@ int csa2_device_check(void);
  *     +-6 s saturate).  D even, 2 <= D.
  *   CSA2_FMT_FP8_PER_TOKEN: codes [B][n_max][D] (E4M3), scales [B][n_max] fp32, one scale
  *     per row: s = fl32(max_c |x| / 448) (scale_policy must be COMPUTE).  D <= 4096.
+ *   CSA2_FMT_FP4_G16 (the pages' layout: one E4M3 scale per 16 channels of each entry, no
+ *     global scale; "FP4 Main KV Cache To Halve Storage Again"): codes [B][n_max][D/2] as
+ *     above, scales [B][n_max][D/16] uint8 (E4M3 bytes).  Per group of 16 channels of a row:
+ *     sc = E4M3(fl32(max |x| / 6)) (nearest, ties to even, saturating at 448), code =
+ *     E2M1(fl32(x / value(sc))) (values beyond 6 after the division saturate; sc = 0 gives
+ *     code +0).  Every entry's scales come from the entry itself, so scale_policy is
+ *     ignored.  D % 16 == 0.  288 B per entry at D = 512.
  */
 int csa2_quantize_kv(int fmt, int scale_policy, int B, int T, int D, const void* x, int x_dtype,
                      int64_t x_stride_b, int64_t x_stride_t, const int32_t* n0, int64_t n_max, uint8_t* codes,
-                     float* scales, void* stream);
+                     void* scales, void* stream);
 
 /*
  * Gather + dequantise selected FP4 rows (the step before attention; "values are
  * dequantized back before attention" in "FP4 Main KV Cache To Halve Storage Again").
- *   out[b][t][k][c] = fl32(E2M1(code) * scales[b][c]) of cache row idx[b][t][k]; rows
- *   with idx outside [0, n_max) (e.g. the -1 padding) give 0.  out is fp32
- *   [B][T][K][D].  Bit-exact.
+ *   kv_fmt CSA2_FMT_FP4_PER_CHANNEL: out[b][t][k][c] = fl32(E2M1(code) * scales[b][c]),
+ *     scales fp32 [B][D];
+ *   kv_fmt CSA2_FMT_FP4_G16: out = E2M1(code) * E4M3(scales[b][j][c / 16]) (exact), scales
+ *     uint8 [B][n_max][D/16], D % 16 == 0;
+ *   of cache row j = idx[b][t][k]; rows with idx outside [0, n_max) (e.g. the -1 padding)
+ *   give 0.  out is fp32 [B][T][K][D].  Bit-exact.
  */
-int csa2_gather_dequant(int B, int T, int K, int D, const uint8_t* codes, const float* scales, int64_t n_max,
-                        const int32_t* idx, float* out, void* stream);
+int csa2_gather_dequant(int kv_fmt, int B, int T, int K, int D, const uint8_t* codes, const void* scales,
+                        int64_t n_max, const int32_t* idx, float* out, void* stream);
 
 /*
  * Indexer scores (Full / Reindex layers).  Source: "Compressed Sparse Attention 2 Or CSA2
@@ -162,17 +172,21 @@ size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int K);
  *   l_hj = softmax_scale * q_h . v_j over j in idx[b][t][*] (entries outside [0, n_max)
  *   skipped);  out_h = sum_j softmax(l_h)_j v_j;  lse_h = log sum_j exp(l_hj).
  *   No selected entry: out = 0, lse = -inf.
- *   q: [B][T][Hq][D] of q_dtype; kv_codes [B][n_max][D/2]; kv_scales [B][D];
- *   idx [B][T][K]; out [B][T][Hq][D] of out_dtype; lse [B][T][Hq] fp32 (nullable).
+ *   q: [B][T][Hq][D] of q_dtype; kv_codes [B][n_max][D/2]; kv_scales as for
+ *   csa2_gather_dequant of kv_fmt (fp32 [B][D] per channel, or uint8 [B][n_max][D/16] E4M3
+ *   per 16 channels of each entry); idx [B][T][K]; out [B][T][Hq][D] of out_dtype; lse
+ *   [B][T][Hq] fp32 (nullable).
  *   q_dtype CSA2_F32: fp32 arithmetic throughout (out_dtype must be CSA2_F32).
- *   q_dtype CSA2_BF16: fp16 MFMA with fp32 accumulation, the per-channel scale folded into
- *   the query (exact power-of-two prescale) and into the output; needs Hq % 16 == 0 and
- *   D in {128, 256, 512}.  Entries are processed in groups of 512 whose partial softmax
- *   results are merged by log-sum-exp.  ws: csa2_sparse_attend_workspace_size() bytes
- *   (0 when K <= 512 or q is fp32; then ws may be NULL).
+ *   q_dtype CSA2_BF16: fp16 MFMA with fp32 accumulation; needs Hq % 16 == 0 and D in
+ *   {128, 256, 512}.  Per-channel scales are folded into the query (with an exact
+ *   power-of-two prescale) and into the output; per-16-channel scales multiply the fp16
+ *   key/value operands (E2M1 * E4M3 is exact in fp16).  Entries are processed in groups of
+ *   512 whose partial softmax results are merged by log-sum-exp.
+ *   ws: csa2_sparse_attend_workspace_size() bytes (0 when K <= 512 or q is fp32; then ws
+ *   may be NULL).
  */
-int csa2_sparse_attend(int B, int T, int Hq, int D, const void* q, int q_dtype, const uint8_t* kv_codes,
-                       const float* kv_scales, int64_t n_max, const int32_t* idx, int K, float softmax_scale,
+int csa2_sparse_attend(int B, int T, int Hq, int D, const void* q, int q_dtype, int kv_fmt, const uint8_t* kv_codes,
+                       const void* kv_scales, int64_t n_max, const int32_t* idx, int K, float softmax_scale,
                        void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype);
 
@@ -212,7 +226,7 @@ typedef struct {
   int64_t n_max;
   const int32_t* n_keys;   /* [B] */
   const uint8_t* kv_codes; /* [B][n_max][D/2] */
-  const float* kv_scales;  /* [B][D] */
+  const void* kv_scales;   /* fp32 [B][D], or uint8 [B][n_max][D/16] with kv_fmt CSA2_FMT_FP4_G16 */
   const void* k;           /* [B][n_max][dk] E4M3 codes (FP8) or fp32 (FP32) */
   const float* k_scale;    /* [B][n_max] (FP8) or NULL */
   int prec;                /* csa2_index_prec */
@@ -225,6 +239,7 @@ typedef struct {
    * Reindex layer scores all n_keys entries).  1 <= pool_blocks <= CSA2_MAX_K. */
   int pool_block;
   int pool_blocks;
+  int kv_fmt;              /* CSA2_FMT_FP4_PER_CHANNEL (0) or CSA2_FMT_FP4_G16 */
 } csa2_group_cache;
 
 int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_cache* cache, void* ws,

@@ -150,6 +150,53 @@ def test_decoder128k_pool_full_size_sampled_sequences():
         assert torch.equal(L["out"], o)
 
 
+def test_group128k_g16_full_size_sampled_sequences():
+    """The 128K decode group with the pages' FP4 layout (one E4M3 scale per 16 channels of
+    each entry, 288 B per entry): Full -> Reindex -> Reuse, 16 sequences x 131072."""
+    wl = workloads.WORKLOADS["group128k"]
+    sample = [2, 13]
+    B, N, D, dk = wl.B, wl.N, wl.D, wl.dk
+    codes = torch.empty((B, N, D // 2), dtype=torch.uint8, device=DEV)
+    gs = torch.empty((B, N, D // 16), dtype=torch.uint8, device=DEV)
+    k8 = torch.empty((B, N, dk), dtype=torch.uint8, device=DEV)
+    ks = torch.empty((B, N), dtype=torch.float32, device=DEV)
+    ref = {}
+    for b in range(B):
+        x, kf = wl.main_kv(b), wl.index_keys(b)
+        csa2.quantize_kv(csa2.FMT_FP4_G16, to_dev(x)[None], codes[b:b + 1], gs[b:b + 1])
+        csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(kf)[None], k8[b:b + 1], ks[b:b + 1])
+        if b in sample:
+            cr, gr = oracle.quantize_fp4_g16(x[None])
+            kr, ksr = oracle.quantize_fp8(kf[None])
+            torch.cuda.synchronize()
+            assert np.array_equal(codes[b].cpu().numpy(), cr[0]) and np.array_equal(gs[b].cpu().numpy(), gr[0]), b
+            assert np.array_equal(k8[b].cpu().numpy(), kr[0]) and np.array_equal(ks[b].cpu().numpy(), ksr[0]), b
+            ref[b] = (cr[0], gr[0], kr[0], ksr[0])
+    n_keys = torch.full((B,), N, dtype=torch.int32, device=DEV)
+    q_in, layers = [], []
+    for i, m in enumerate(wl.modes):
+        qi, w, qa = wl.index_query(i), wl.head_weights(i), wl.attn_query(i)
+        q_in.append((qi, w, qa))
+        layers.append(dict(mode=m, q_idx=to_dev(qi, torch.bfloat16), w=to_dev(w), q_attn=to_dev(qa, torch.bfloat16)))
+    cache = csa2.GroupCache(n_keys, codes, gs, k8, ks, wl.K, wl.softmax_scale)
+    csa2.layer_group(layers, cache, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    cr = np.stack([ref[b][0] for b in sample])
+    gr = np.stack([ref[b][1] for b in sample])
+    kr = np.stack([ref[b][2] for b in sample])
+    ksr = np.stack([ref[b][3] for b in sample])
+    nk = np.full(len(sample), N, np.int32)
+    g_idx = None
+    for i, (L, m) in enumerate(zip(layers, wl.modes)):
+        qi, w, qa = (x[sample] for x in q_in[i])
+        if m != "reuse":
+            s = oracle.index_score(oracle.PREC_FP8, qi, w, kr, ksr, nk)
+            g_idx = L["idx"].cpu().numpy()[sample]
+            check_topk_near_tie(g_idx, s, wl.K)
+        ro, _ = oracle.sparse_attend(qa, cr, gr, g_idx, wl.softmax_scale)
+        assert _bf16_ok(L["out"].float().cpu().numpy()[sample], ro), i
+
+
 def test_full64k_full_size_sampled_sequences():
     """The single-layer 64K decode configuration: Full, 16 sequences x 65536."""
     wl = workloads.WORKLOADS["full64k"]
