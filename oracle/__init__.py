@@ -58,7 +58,7 @@ def _load():
         L.orc_gather_dequant.argtypes = [i, i, i, i, i, p, p, i64, p, p]
         L.orc_index_score.argtypes = [i, i, i, i, i, p, p, p, p, i64, p, p, p, i, p]
         L.orc_topk.argtypes = [i, i, i64, p, p, i, p, p]
-        L.orc_sparse_attend.argtypes = [i, i, i, i, i, p, p, p, i64, p, i, d, p, p]
+        L.orc_sparse_attend.argtypes = [i, i, i, i, i, p, p, p, i64, p, i, p, p, i64, p, i, d, p, p]
         L.orc_coarse_keys.argtypes = [i, i64, p, i, i, p, p, p, p]
         L.orc_num_threads.argtypes, L.orc_num_threads.restype = [], i
         for fn in ("orc_quantize_fp4", "orc_quantize_fp4_g16", "orc_quantize_fp8", "orc_quantize_index_query",
@@ -205,9 +205,11 @@ def topk(scores, K, cand=None, want_values=False):
 
 
 # ---------------------------------------------------------------------------- attention
-def sparse_attend(q, codes, scales, idx, softmax_scale):
+def sparse_attend(q, codes, scales, idx, softmax_scale, swa=None):
     """(out [B][T][Hq][D] float64, lse [B][T][Hq] float64).  scales: fp32 [B][D] (one per
-    channel) or uint8 [B][n_max][D/16] (E4M3 per 16 channels of each entry)."""
+    channel) or uint8 [B][n_max][D/16] (E4M3 per 16 channels of each entry).
+    swa: None, or (swa_codes [B][n][D] u8, swa_scales [B][n] f32, swa_end [B][T] i32,
+    window): the layer's sliding-window entries, attended in the same softmax."""
     q = _c(q, np.float32)
     B, T, Hq, D = q.shape
     fmt, scales = _kv_scales(scales)
@@ -216,8 +218,14 @@ def sparse_attend(q, codes, scales, idx, softmax_scale):
     K = idx.shape[-1]
     out = np.empty((B, T, Hq, D), np.float64)
     lse = np.empty((B, T, Hq), np.float64)
-    _load().orc_sparse_attend(fmt, B, T, Hq, D, _p(q), _p(codes), _p(scales), n_max, _p(idx), K,
-                              float(softmax_scale), _p(out), _p(lse))
+    sc = ss = se = None
+    sn, win = 0, 0
+    if swa is not None:
+        sc, ss, se, win = _c(swa[0], np.uint8), _c(swa[1], np.float32), _c(swa[2], np.int32), int(swa[3])
+        assert sc.shape[0] == B and sc.shape[2] == D and se.shape == (B, T)
+        sn = sc.shape[1]
+    _load().orc_sparse_attend(fmt, B, T, Hq, D, _p(q), _p(codes), _p(scales), n_max, _p(idx), K, _p(sc), _p(ss),
+                              sn, _p(se), win, float(softmax_scale), _p(out), _p(lse))
     return out, lse
 
 
@@ -269,7 +277,8 @@ def pool_positions(scores, block, pool_blocks, n_keys):
 def layer_group(layers, cache, prec, K, softmax_scale, pool=None):
     """Run the layers in order over one shared cache.
 
-    layers: list of dicts {mode, q_idx, w, q_attn}; cache: dict {k, k_scale, n_keys, codes,
+    layers: list of dicts {mode, q_idx, w, q_attn} and optionally swa (the layer's own
+    sliding-window cache, as for sparse_attend); cache: dict {k, k_scale, n_keys, codes,
     scales}.  Full and Reindex score the shared indexer keys with their own query and
     take a fresh Top-K; Reuse takes the most recent indexing layer's Top-K unchanged.
     Every mode then attends over the shared main KV with its own attention query.
@@ -291,7 +300,8 @@ def layer_group(layers, cache, prec, K, softmax_scale, pool=None):
         elif L["mode"] == REINDEX:
             s = index_score(prec, L["q_idx"], L["w"], cache["k"], cache["k_scale"], cache["n_keys"], cand=cand)
             last_idx = topk(s, K, cand=cand)
-        out, lse = sparse_attend(L["q_attn"], cache["codes"], cache["scales"], last_idx, softmax_scale)
+        out, lse = sparse_attend(L["q_attn"], cache["codes"], cache["scales"], last_idx, softmax_scale,
+                                 swa=L.get("swa"))
         res.update({"idx": last_idx, "out": out, "lse": lse})
         results.append(res)
     return results

@@ -361,21 +361,43 @@ void orc_topk(int B, int T, int64_t ncols, const double* scores, const int32_t* 
  *   l_hj = scale * q_h . v_j;  m_h = max_j l_hj;  Z_h = sum_j exp(l_hj - m_h)
  *   o_h  = sum_j exp(l_hj - m_h) v_j / Z_h;   lse_h = m_h + ln Z_h
  * An empty S gives o = 0, lse = -inf.  q is [B][T][Hq][D]; out [B][T][Hq][D]; lse
- * [B][T][Hq] (nullable); fmt and scales as for fp4_dequant. */
+ * [B][T][Hq] (nullable); fmt and scales as for fp4_dequant.
+ * Sliding window (swa_codes != NULL): [N] "CSA2 In Simple Terms" (every layer also looks
+ * at recent tokens through sliding window attention), "Model Setup Numbers" (window 128),
+ * "FP4 Main KV Cache" (the window cache stays 8-bit), 3.3 of the Chinese reading (each
+ * layer keeps its own window KV).  Reading: the window's entries join S in one softmax
+ * (the whole entry again both key and value); the window cache is E4M3 with one fp32
+ * scale per row (swa_codes [B][swa_n_max][D], swa_scales [B][swa_n_max]); row (b,t)
+ * sees window rows [max(0, e - window), e) with e = min(swa_end[b][t], swa_n_max). */
 void orc_sparse_attend(int fmt, int B, int T, int Hq, int D, const float* q, const uint8_t* codes,
-                       const void* scales, int64_t n_max, const int32_t* idx, int K, double scale, double* out,
-                       double* lse) {
+                       const void* scales, int64_t n_max, const int32_t* idx, int K, const uint8_t* swa_codes,
+                       const float* swa_scales, int64_t swa_n_max, const int32_t* swa_end, int window,
+                       double scale, double* out, double* lse) {
+  const int W = swa_codes ? window : 0;
 #pragma omp parallel for schedule(dynamic)
   for (int64_t r = 0; r < (int64_t)B * T; ++r) {
     int b = (int)(r / T);
-    double* v = (double*)malloc(sizeof(double) * (size_t)K * D);
-    double* l = (double*)malloc(sizeof(double) * (size_t)K);
+    double* v = (double*)malloc(sizeof(double) * (size_t)(K + W) * D);
+    double* l = (double*)malloc(sizeof(double) * (size_t)(K + W));
     int n = 0;
     for (int k = 0; k < K; ++k) {
       int32_t j = idx[r * K + k];
       if (j < 0 || j >= n_max) continue;
       for (int c = 0; c < D; ++c) v[(int64_t)n * D + c] = fp4_dequant(fmt, codes, scales, b, n_max, j, D, c);
       ++n;
+    }
+    /* the sliding window: the last `window` entries before swa_end[b][t] of this layer's
+     * own cache, dequantised as E4M3(code) * s_row, joining the same softmax */
+    if (W > 0) {
+      int64_t end = swa_end[r];
+      if (end > swa_n_max) end = swa_n_max;
+      int64_t start = end - W < 0 ? 0 : end - W;
+      for (int64_t j = start; j < end; ++j) {
+        const int64_t row = (int64_t)b * swa_n_max + j;
+        for (int c = 0; c < D; ++c)
+          v[(int64_t)n * D + c] = orc_e4m3_value(swa_codes[row * D + c]) * (double)swa_scales[row];
+        ++n;
+      }
     }
     for (int h = 0; h < Hq; ++h) {
       const float* qh = q + (r * Hq + h) * D;
