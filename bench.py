@@ -388,6 +388,50 @@ def run_group128k_g16(args):
         "step_pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
 
 
+def run_group128k_swa(args):
+    """The 128K decode group (Full -> Reindex -> Reuse, 16 x 131072, Top-512) where every
+    layer also attends to its own sliding window of the last 128 tokens (E4M3 rows with one
+    fp32 scale each) in the same softmax as its selected entries."""
+    wl = workloads.WORKLOADS["group128k"]
+    W = 128
+    log("building cache (%d copies) ..." % args.copies)
+    caches = build_device_cache(wl, args.copies)
+    layers = layer_inputs(wl)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    end = torch.full((wl.B, 1), W, dtype=torch.int32, device="cuda")
+    for i, L in enumerate(layers):   # every layer its own window cache
+        x = torch.randn((wl.B, W, wl.D), generator=gen, device="cuda")
+        wc = torch.empty((wl.B, W, wl.D), dtype=torch.uint8, device="cuda")
+        ws = torch.empty((wl.B, W), dtype=torch.float32, device="cuda")
+        csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, x, wc, ws)
+        L["swa"] = csa2.Swa(wc, ws, end, W)
+    plans = [csa2.GroupPlan([dict(L) for L in layers],
+                            csa2.GroupCache(c["n_keys"], c["codes"], c["scales"], c["k8"], c["ks"], wl.K,
+                                            wl.softmax_scale), out_dtype=torch.bfloat16) for c in caches]
+    for s in range(args.warmup):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    B, D = wl.B, wl.D
+    alg = algorithmic_bytes(wl) + len(wl.modes) * B * W * (D + 4)
+    gbs = alg / (ms_step / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "CSA2 decode queries/s at 128K context (Top-512 plus a 128-token sliding window per layer)",
+        "value": round(B / (ms_step / 1e3), 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": "group128k_swa: Full->Reindex->Reuse decode, B=16, N=131072, indexer 32x64 E4M3, "
+                               "Top-512 + a 128-entry E4M3 sliding window per layer in one softmax, FP4 E2M1 main "
+                               "KV D=512, 64 heads bf16", "global_batch": B, "seq_len": wl.N,
+                   "layers": list(wl.modes), "window": W, "cache_copies": args.copies},
+        "step_algorithmic_bytes": alg, "step_achieved_GBps": round(gbs, 1),
+        "step_pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
+
+
 def run_hier1m(args):
     """The 1M-entry two-level configuration (one sequence): coarse keys (64-entry block
     means, built once, not timed) -> score 16384 coarse keys -> top-256 blocks -> exact
@@ -470,11 +514,13 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="group128k",
-                    choices=["group128k", "prefill", "full64k", "hier1m", "decoder128k", "group128k_g16"],
+                    choices=["group128k", "prefill", "full64k", "hier1m", "decoder128k", "group128k_g16",
+                             "group128k_swa"],
                     help="group128k: the 128K decode group (the headline; default); prefill: the chunked-prefill "
                          "path; full64k: one Full layer at 64K; hier1m: the two-level indexer at 1M; decoder128k: "
                          "the 20-layer decoder schedule at 128K with the candidate pool; group128k_g16: the 128K group with "
-                         "the per-16-channel E4M3-scaled FP4 layout")
+                         "the per-16-channel E4M3-scaled FP4 layout; group128k_swa: the 128K group with a 128-token sliding "
+                         "window per layer")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -503,6 +549,9 @@ def main():
         return
     if args.workload == "group128k_g16":
         run_group128k_g16(args)
+        return
+    if args.workload == "group128k_swa":
+        run_group128k_swa(args)
         return
     wl = workloads.WORKLOADS["group128k"]
     log("building cache (%d copies) ..." % args.copies)

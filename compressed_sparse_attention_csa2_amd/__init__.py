@@ -46,10 +46,15 @@ class Csa2Error(RuntimeError):
         super().__init__("%s failed: %s" % (where, status_string(status)))
 
 
+class _Swa(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("n_max", ctypes.c_int64),
+                ("end", ctypes.c_void_p), ("window", ctypes.c_int)]
+
+
 class _Layer(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int), ("q_idx", ctypes.c_void_p), ("w", ctypes.c_void_p),
                 ("q_attn", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
-                ("idx", ctypes.c_void_p), ("pool", ctypes.c_void_p)]
+                ("idx", ctypes.c_void_p), ("pool", ctypes.c_void_p), ("swa", ctypes.POINTER(_Swa))]
 
 
 class _GroupCache(ctypes.Structure):
@@ -58,7 +63,7 @@ class _GroupCache(ctypes.Structure):
                 ("kv_codes", ctypes.c_void_p), ("kv_scales", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("prec", ctypes.c_int), ("q_dtype", ctypes.c_int),
                 ("out_dtype", ctypes.c_int), ("softmax_scale", ctypes.c_float), ("pool_block", ctypes.c_int),
-                ("pool_blocks", ctypes.c_int), ("kv_fmt", ctypes.c_int)]
+                ("pool_blocks", ctypes.c_int), ("kv_fmt", ctypes.c_int), ("window", ctypes.c_int)]
 
 
 _lib = None
@@ -84,8 +89,8 @@ def lib() -> ctypes.CDLL:
             "csa2_topk_workspace_size": ([i, i, i64, i], sz),
             "csa2_index_topk": ([i, i, i, i, i, p, i, p, p, p, i64, p, p, p, i, i, p, p, p, sz, p], i),
             "csa2_index_topk_workspace_size": ([i, i, i64, i], sz),
-            "csa2_sparse_attend": ([i, i, i, i, p, i, i, p, p, i64, p, i, f, p, i, p, p, sz, p], i),
-            "csa2_sparse_attend_workspace_size": ([i, i, i, i, i, i], sz),
+            "csa2_sparse_attend": ([i, i, i, i, p, i, i, p, p, i64, p, i, p, f, p, i, p, p, sz, p], i),
+            "csa2_sparse_attend_workspace_size": ([i, i, i, i, i, i, i], sz),
             "csa2_layer_group": ([p, i, p, p, sz, p], i),
             "csa2_layer_group_workspace_size": ([p, i], sz),
             "csa2_coarse_keys": ([i, i64, p, i, i, p, p, p, p, p], i),
@@ -228,9 +233,22 @@ def index_topk(prec: int, q: torch.Tensor, w: torch.Tensor, k: torch.Tensor, k_s
 
 
 # ------------------------------------------------------------------------------ attention
+class Swa:
+    """A layer's own sliding-window cache: codes [B][n_max][D] uint8 (E4M3) and scales
+    [B][n_max] fp32 (as quantize_kv writes them with FMT_FP8_PER_TOKEN), end [B][T] int32:
+    query row (b, t) attends to rows [max(0, end - window), end)."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, end: torch.Tensor, window: int):
+        self.codes, self.scales, self.end, self.window = codes, scales, end, int(window)
+
+    def struct(self) -> _Swa:
+        return _Swa(_ptr(self.codes), _ptr(self.scales), self.codes.shape[1], _ptr(self.end), self.window)
+
+
 def sparse_attend(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, idx: torch.Tensor,
                   softmax_scale: float, out_dtype: Optional[torch.dtype] = None, want_lse: bool = True,
-                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  swa: Optional[Swa] = None):
     B, T, Hq, D = q.shape
     n_max = codes.shape[1]
     K = idx.shape[-1]
@@ -239,11 +257,12 @@ def sparse_attend(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, id
     if lse is None and want_lse:
         lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
     qd = _dtype_code(q)
-    nb = lib().csa2_sparse_attend_workspace_size(B, T, Hq, D, K, qd)
+    nb = lib().csa2_sparse_attend_workspace_size(B, T, Hq, D, K, qd, swa.window if swa else 0)
     ws = _workspace(nb, q.device)
+    sw = swa.struct() if swa else None
     _check(lib().csa2_sparse_attend(B, T, Hq, D, _ptr(q), qd, kv_format(scales), _ptr(codes), _ptr(scales), n_max,
-                                    _ptr(idx), K, float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse),
-                                    _ptr(ws), nb, _stream()), "csa2_sparse_attend")
+                                    _ptr(idx), K, ctypes.byref(sw) if sw else None, float(softmax_scale), _ptr(out),
+                                    _dtype_code(out), _ptr(lse), _ptr(ws), nb, _stream()), "csa2_sparse_attend")
     return out, lse
 
 
@@ -260,12 +279,12 @@ class GroupCache:
         self.K, self.softmax_scale, self.prec = K, softmax_scale, prec
         self.pool = pool
 
-    def struct(self, H, dk, Hq, q_dtype, out_dtype):
+    def struct(self, H, dk, Hq, q_dtype, out_dtype, window=0):
         B, n_max, Dh = self.kv_codes.shape
         pb, pn = self.pool if self.pool else (0, 0)
         return _GroupCache(B, H, dk, Hq, 2 * Dh, self.K, n_max, _ptr(self.n_keys), _ptr(self.kv_codes),
                            _ptr(self.kv_scales), _ptr(self.k), _ptr(self.k_scale), self.prec, q_dtype, out_dtype,
-                           float(self.softmax_scale), pb, pn, kv_format(self.kv_scales))
+                           float(self.softmax_scale), pb, pn, kv_format(self.kv_scales), window)
 
 
 class GroupPlan:
@@ -273,7 +292,7 @@ class GroupPlan:
 
     def __init__(self, layers: Sequence[dict], cache: GroupCache, out_dtype: Optional[torch.dtype] = None):
         self.layers = list(layers)
-        self._arr, self._gc, self._ws, self._nb = _marshal_group(self.layers, cache, out_dtype)
+        self._arr, self._gc, self._ws, self._nb, self._swa = _marshal_group(self.layers, cache, out_dtype)
 
     def run(self):
         _check(lib().csa2_layer_group(self._arr, len(self.layers), ctypes.byref(self._gc), _ptr(self._ws), self._nb,
@@ -285,9 +304,9 @@ def layer_group(layers: Sequence[dict], cache: GroupCache, out_dtype: Optional[t
     """Run Full/Reindex/Reuse layers in order over one shared cache.
 
     layers: dicts with mode ('full'|'reindex'|'reuse'), q_idx [B][1][H][dk], w [B][1][H],
-    q_attn [B][1][Hq][D] and optionally out, lse, idx tensors, and for Full layers of a
-    cache with a pool a 'pool' int32 tensor [B][blocks*block] that receives the pool's
-    positions.  Returns the layer dicts with 'out', 'lse' and (Full/Reindex) 'idx' filled."""
+    q_attn [B][1][Hq][D] and optionally out, lse, idx tensors, 'swa' (the layer's own
+    sliding-window cache, a Swa), and for Full layers of a cache with a pool a 'pool' int32
+    tensor [B][blocks*block] that receives the pool's positions.  Returns the layer dicts with 'out', 'lse' and (Full/Reindex) 'idx' filled."""
     return GroupPlan(layers, cache, out_dtype).run()
 
 
@@ -298,6 +317,8 @@ def _marshal_group(layers, cache, out_dtype):
     H, dk = (first["q_idx"].shape[2], first["q_idx"].shape[3]) if first.get("q_idx") is not None else (32, 64)
     odt = out_dtype or q_attn.dtype
     arr = (_Layer * len(layers))()
+    swas = [L["swa"].struct() if L.get("swa") is not None else None for L in layers]  # kept alive by the plan
+    window = max([sw.window for sw in swas if sw is not None], default=0)
     for i, L in enumerate(layers):
         mode = MODE_NAMES[L["mode"]] if isinstance(L["mode"], str) else int(L["mode"])
         if L.get("out") is None:
@@ -314,12 +335,13 @@ def _marshal_group(layers, cache, out_dtype):
                 raise ValueError("pool must be a contiguous int32 tensor of B * block * blocks elements")
         arr[i] = _Layer(mode, _ptr(L.get("q_idx")), _ptr(L.get("w")), _ptr(L["q_attn"]), _ptr(L["out"]),
                         _ptr(L["lse"]), _ptr(L.get("idx")) if mode != REUSE else None,
-                        _ptr(L.get("pool")) if mode == FULL else None)
+                        _ptr(L.get("pool")) if mode == FULL else None,
+                        ctypes.pointer(swas[i]) if swas[i] is not None else None)
     qd = _dtype_code(q_attn)
-    gc = cache.struct(H, dk, Hq, qd, _dtype_code(torch.empty(0, dtype=odt)))
+    gc = cache.struct(H, dk, Hq, qd, _dtype_code(torch.empty(0, dtype=odt)), window)
     nb = lib().csa2_layer_group_workspace_size(ctypes.byref(gc), len(layers))
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=q_attn.device)
-    return arr, gc, ws, nb
+    return arr, gc, ws, nb, swas
 
 
 # ------------------------------------------------------------------------------ two-level indexer

@@ -134,7 +134,24 @@ AttendArgs attend_args(int B, int T, int Hq, int D, int K, const void* q, int q_
   a.softmax_scale = softmax_scale; a.out = out; a.out_bf16 = (out_dtype == CSA2_BF16); a.lse = lse;
   a.ctl = nullptr; a.hist2 = nullptr; a.candbuf = nullptr; a.cnt = nullptr; a.nreg = 0; a.idx_out = nullptr;
   a.part = nullptr;
+  a.swa_codes = nullptr; a.swa_scales = nullptr; a.swa_n_max = 0; a.swa_end = nullptr; a.window = 0;
   return a;
+}
+
+// a layer's sliding-window cache
+int check_swa(const csa2_swa* w, int max_window) {
+  if (!w) return CSA2_OK;
+  if (!w->codes || !w->scales || !w->end) return CSA2_ERR_NULL;
+  if (w->window < 1 || w->window > CSA2_MAX_WINDOW || w->window > max_window || w->n_max < 1) return CSA2_ERR_SHAPE;
+  return CSA2_OK;
+}
+
+void set_swa(AttendArgs& a, const csa2_swa* w) {
+  a.swa_codes = w ? w->codes : nullptr;
+  a.swa_scales = w ? w->scales : nullptr;
+  a.swa_n_max = w ? w->n_max : 0;
+  a.swa_end = w ? w->end : nullptr;
+  a.window = w ? w->window : 0;
 }
 
 int check_index_shape(int prec, int B, int T, int H, int dk, int q_dtype, const void* k_scale, int64_t ncols) {
@@ -314,27 +331,31 @@ int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_
   return dev_status(select_topk((int)R, ncols, scores, cand, K, t, idx_out, val_out, st));
 }
 
-size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype) {
+size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype, int window) {
   if (q_dtype != CSA2_BF16) return 0;
-  return align256(attend_ws_floats(B * T, Hq, D, K) * 4);
+  return align256(attend_ws_floats(B * T, Hq, D, K, window) * 4);
 }
 
 int csa2_sparse_attend(int B, int T, int Hq, int D, const void* q, int q_dtype, int kv_fmt, const uint8_t* kv_codes,
-                       const void* kv_scales, int64_t n_max, const int32_t* idx, int K, float softmax_scale,
-                       void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                       const void* kv_scales, int64_t n_max, const int32_t* idx, int K, const csa2_swa* swa,
+                       float softmax_scale, void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes,
+                       void* stream) {
   if (!q || !kv_codes || !kv_scales || !idx || !out) return CSA2_ERR_NULL;
   if (n_max < 1) return CSA2_ERR_SHAPE;
   int rc = check_kv_fmt(kv_fmt, D);
   if (rc) return rc;
   rc = check_attend_shape(B, T, Hq, D, K, q_dtype, out_dtype);
   if (rc) return rc;
-  const size_t need = csa2_sparse_attend_workspace_size(B, T, Hq, D, K, q_dtype);
+  rc = check_swa(swa, CSA2_MAX_WINDOW);
+  if (rc) return rc;
+  const size_t need = csa2_sparse_attend_workspace_size(B, T, Hq, D, K, q_dtype, swa ? swa->window : 0);
   if (need && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   rc = check_device();
   if (rc) return rc;
   AttendArgs a = attend_args(B, T, Hq, D, K, q, q_dtype, kv_fmt, kv_codes, kv_scales, n_max, idx, softmax_scale,
                              out, out_dtype, lse);
   a.part = need ? static_cast<float*>(ws) : nullptr;
+  set_swa(a, swa);
   return dev_status(launch_attend(a, S(stream)));
 }
 
@@ -381,7 +402,8 @@ size_t csa2_layer_group_workspace_size(const csa2_group_cache* c, int n_layers) 
   const int64_t R = c->B;
   const int sel = pool_on(c) ? 2 * n_layers : n_layers;  // a pooled Full layer makes two selections
   const int slots = sel < 64 ? sel : 64;
-  const size_t att = (c->q_dtype == CSA2_BF16) ? align256(attend_ws_floats((int)R, c->Hq, c->D, c->K) * 4) : 0;
+  const size_t att =
+      (c->q_dtype == CSA2_BF16) ? align256(attend_ws_floats((int)R, c->Hq, c->D, c->K, c->window) * 4) : 0;
   const size_t pool = pool_on(c) ? align256((size_t)R * pool_cols(c) * 4) + align256((size_t)R * pool_nb(c) * 4) : 0;
   return topk_zero_bytes(R) * (size_t)slots + align256((size_t)R * group_cols(c) * 4) + cand_bytes(R, group_cols(c)) +
          att + pool;
@@ -396,6 +418,7 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   if (!c->n_keys || !c->kv_codes || !c->kv_scales || !c->k) return CSA2_ERR_NULL;
   if (c->n_max < 1 || c->n_max > kMaxTopkCols || c->K < 1 || c->K > CSA2_MAX_K) return CSA2_ERR_SHAPE;
   if (c->pool_blocks < 0 || c->pool_blocks > CSA2_MAX_K || (pool_on(c) && c->pool_block < 1)) return CSA2_ERR_SHAPE;
+  if (c->window < 0 || c->window > CSA2_MAX_WINDOW) return CSA2_ERR_SHAPE;
   if (pool_cols(c) > kMaxTopkCols || c->n_max > INT32_MAX) return CSA2_ERR_SHAPE;
   rc = check_index_shape(c->prec, c->B, 1, c->H, c->dk, c->q_dtype, c->k_scale, c->n_max);
   if (rc) return rc;
@@ -407,6 +430,8 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
     const csa2_layer& L = layers[i];
     if (!L.q_attn || !L.out) return CSA2_ERR_NULL;
     if (L.mode != CSA2_REUSE && (!L.q_idx || !L.w || !L.idx)) return CSA2_ERR_NULL;
+    rc = check_swa(L.swa, c->window);
+    if (rc) return rc;
   }
   if (!ws || ws_bytes < csa2_layer_group_workspace_size(c, n_layers)) return CSA2_ERR_WORKSPACE;
   rc = check_device();
@@ -424,7 +449,8 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   const size_t zero_bytes = cv.off;
   float* scores = cv.take<float>((size_t)R * group_cols(c));
   CandWs cw = carve_cand(cv, R, group_cols(c));
-  float* part = (c->q_dtype == CSA2_BF16) ? cv.take<float>(attend_ws_floats((int)R, c->Hq, c->D, c->K)) : nullptr;
+  float* part =
+      (c->q_dtype == CSA2_BF16) ? cv.take<float>(attend_ws_floats((int)R, c->Hq, c->D, c->K, c->window)) : nullptr;
   const int64_t pc = pool_cols(c), nb = pool_nb(c);
   int32_t* pool = pooled ? cv.take<int32_t>((size_t)R * pc) : nullptr;
   float* bmax = pooled ? cv.take<float>((size_t)R * nb) : nullptr;
@@ -451,6 +477,7 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
     a.q = L.q_attn;
     a.out = L.out;
     a.lse = L.lse;
+    set_swa(a, L.swa);
     a.ctl = nullptr; a.hist2 = nullptr; a.candbuf = nullptr; a.idx_out = nullptr; a.idx = last_idx;
     if (L.mode != CSA2_REUSE) {
       TopkWs t;

@@ -35,7 +35,8 @@ constexpr int kAttSplit = 512;     // entries per block: the pages' Top-512 in o
 constexpr int kAttTPW = kAttSplit / 16 / kAttWaves;  // 16-entry QK tiles per wave
 static_assert(kAttTPW * 16 * kAttWaves == kAttSplit, "QK tiles cover the split");
 
-// partials: part_o [R][S][Hq][D] normalised outputs, part_ml [R][S][Hq][2] (max, sum)
+// partials: part_o [R][P][Hq][D] normalised outputs, part_ml [R][P][Hq][2] (max, sum); P
+// = the splits of the selected entries, plus one slot for the sliding window
 
 // Two E4M3 codes (bytes 0 and 1 of w) -> two fp16 values (exact), low byte in the low half.
 // Placing the code's exponent and mantissa bits at the top of an fp16 gives the value times
@@ -64,6 +65,267 @@ __device__ __forceinline__ v8h decode8_f16(uint32_t word) {
   return __builtin_bit_cast(v8h, u);
 }
 
+// Sliding window of a layer: one block = one query row x 16 heads (8 working waves), up to
+// kWinMax entries (the window rows [max(0, end - window), end) of the layer's own E4M3
+// cache with one fp32 scale per row), written as partial slot `slot` for the merge with
+// the selected entries ("CSA2 In Simple Terms": every layer also attends to recent tokens;
+// the window cache stays 8-bit in "FP4 Main KV Cache To Halve Storage Again").
+//   QK: wave w takes entries 16 w .. 16 w + 15; lane (entry n16, group g) reads 32 bytes
+//       per 128-channel tile, converted exactly to fp16; the row scale multiplies the logit.
+//   PV: wave w takes channels [w D / 8, (w + 1) D / 8) over all entries, so no cross-wave
+//       sum is needed; lane (n16, g) reads D / 128 bytes of each of 8 entries and byte-
+//       transposes them into the (entry 2p, entry 2p + 1) fp16 pairs the MFMA k-order
+//       wants.  The row scales go into p (with one power-of-two normalisation 2^k so that
+//       p * s * 2^k stays in fp16's normal range), undone after the sum.
+constexpr int kWinMax = 128;
+constexpr int kWinWaves = 8;
+
+// two E4M3 codes (low 16 bits of w, first code in the low byte) -> two fp16 (exact)
+__device__ __forceinline__ uint32_t e4m3x2_f16(uint32_t w) { return e4m3x2_to_f16x2(w); }
+
+// LDS of the window path (carved from the attention block's shared union)
+template <int D>
+struct WinLds {
+  static constexpr int kApad = D + 8;
+  static constexpr int kPpad = kWinMax + 8;
+  static constexpr size_t kA = (size_t)kAttHeads * kApad * 2;
+  static constexpr size_t kP = (size_t)kAttHeads * kPpad * 2;
+  static constexpr size_t kRed = (size_t)kWinWaves * kAttHeads * 4;
+  static constexpr size_t kBytes = kA + kP + kRed + 2 * kAttHeads * 4 + (kAttWaves + kWinWaves) * 4;
+};
+
+// Runs on a whole attention block (kAttThreads threads): waves 0..kWinWaves-1 do the work,
+// every wave takes part in the barriers.  `lds` holds WinLds<D>::kBytes (16-B aligned).
+template <int D>
+__device__ __forceinline__ void attend_window_block(
+    int hg, int r, int T, int Hq, const uint16_t* __restrict__ q, const uint8_t* __restrict__ wcodes,
+    const float* __restrict__ wscales, int64_t wn_max, const int32_t* __restrict__ wend, int window,
+    float softmax_scale, int P, int slot, float* __restrict__ part, float* __restrict__ part_ml,
+    unsigned char* lds) {
+  constexpr int kCT = D / 128;
+  constexpr int kApad = D + 8;
+  constexpr int kPpad = kWinMax + 8;
+  constexpr int kCPL = D / 128;                 // PV: channels per lane (bytes per entry)
+  using WL = WinLds<D>;
+  uint16_t* sA = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* sP = reinterpret_cast<uint16_t*>(lds + WL::kA);
+  float (*s_red)[kAttHeads] = reinterpret_cast<float (*)[kAttHeads]>(lds + WL::kA + WL::kP);
+  float* s_m = reinterpret_cast<float*>(lds + WL::kA + WL::kP + WL::kRed);
+  float* s_l = s_m + kAttHeads;
+  float* s_qmax = s_l + kAttHeads;
+  float* s_smax = s_qmax + kAttWaves;
+  const int b = r / T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool act = wave < kWinWaves;           // waves past kWinWaves only join the barriers
+  const int n16 = lane & 15, g = lane >> 4;
+  int64_t e_end = wend[r];
+  if (e_end > wn_max) e_end = wn_max;
+  const int64_t e_start = e_end - window > 0 ? e_end - window : 0;
+  const int nw = e_end > e_start ? (int)(e_end - e_start) : 0;  // entries in the window
+  float* ml = part_ml + (((int64_t)r * P + slot) * Hq + hg * kAttHeads) * 2;
+  float* po = part + (((int64_t)r * P + slot) * Hq + hg * kAttHeads) * (int64_t)D;
+  if (nw == 0) {  // empty window: an empty partial (l = 0 drops it from the merge)
+    for (int i = tid; i < kAttHeads * D; i += kAttThreads) po[i] = 0.0f;
+    if (tid < kAttHeads) {
+      ml[2 * tid] = kNegInf;
+      ml[2 * tid + 1] = 0.0f;
+    }
+    return;
+  }
+  const uint8_t* wb = wcodes + ((int64_t)b * wn_max + e_start) * D;
+  const float* wsb = wscales + (int64_t)b * wn_max + e_start;
+
+  // ---- query loads, then this wave's QK rows (entries past the window read row 0 of it)
+  const uint16_t* qb = q + ((int64_t)r * Hq + hg * kAttHeads) * D;
+  constexpr int kQItems = kAttHeads * D / 8;
+  constexpr int kQPer = (kQItems + kAttThreads - 1) / kAttThreads;
+  uint4 qraw[kQPer];
+#pragma unroll
+  for (int it = 0; it < kQPer; ++it) {
+    const int i = tid + it * kAttThreads;
+    const int ic = i < kQItems ? i : kQItems - 1;
+    qraw[it] = *reinterpret_cast<const uint4*>(qb + (int64_t)(ic / (D / 8)) * D + (ic % (D / 8)) * 8);
+  }
+  const int eq = wave * 16 + n16;                // this lane's QK entry (active waves)
+  const bool q_ok = act && eq < nw;
+  const uint8_t* rowq = wb + (int64_t)(q_ok ? eq : 0) * D + 32 * g;
+  uint4 kw[kCT][2];
+  if (act) {
+#pragma unroll
+    for (int i = 0; i < kCT; ++i) {
+      kw[i][0] = *reinterpret_cast<const uint4*>(rowq + 128 * i);
+      kw[i][1] = *reinterpret_cast<const uint4*>(rowq + 128 * i + 16);
+    }
+  }
+  const float sq = q_ok ? wsb[eq] : 0.0f;
+
+  // ---- q'' = q * 2^k in fp16 (exact power-of-two prescale, undone in the logits)
+  float qmax = 0.0f;
+  float qv[kQPer][8];
+#pragma unroll
+  for (int it = 0; it < kQPer; ++it) {
+    const uint32_t wds[4] = {qraw[it].x, qraw[it].y, qraw[it].z, qraw[it].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[it][e] = bf16_to_f32((uint16_t)(wds[e >> 1] >> (16 * (e & 1))));
+      qmax = fmaxf(qmax, fabsf(qv[it][e]));
+    }
+  }
+  qmax = wave_max(qmax);
+  if (lane == 0) s_qmax[wave] = qmax;
+  __syncthreads();
+  qmax = s_qmax[0];
+#pragma unroll
+  for (int w2 = 1; w2 < kAttWaves; ++w2) qmax = fmaxf(qmax, s_qmax[w2]);
+  int qexp = 0;
+  if (qmax > 0.0f) qexp = (int)((__float_as_uint(qmax) >> 23) & 255u) - 126;
+  const float up = __uint_as_float((uint32_t)(127 + 15 - qexp) << 23);
+  const float down = __uint_as_float((uint32_t)(127 - 15 + qexp) << 23);
+#pragma unroll
+  for (int it = 0; it < kQPer; ++it) {
+    const int i = tid + it * kAttThreads;
+    if (i >= kQItems) break;
+    const int h = i / (D / 8), c = (i % (D / 8)) * 8;
+    uint32_t wv[4];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const _Float16 a0 = (_Float16)(qv[it][2 * k2] * up), a1 = (_Float16)(qv[it][2 * k2 + 1] * up);
+      wv[k2] = pack2(__builtin_bit_cast(uint16_t, a0), __builtin_bit_cast(uint16_t, a1));
+    }
+    *reinterpret_cast<uint4*>(&sA[h * kApad + c]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+  __syncthreads();
+
+  // ---- logits of this wave's 16 entries (lane: entry n16, heads 4 g + rr)
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < (act ? kCT : 0); ++i) {
+    const uint32_t wd[8] = {kw[i][0].x, kw[i][0].y, kw[i][0].z, kw[i][0].w,
+                            kw[i][1].x, kw[i][1].y, kw[i][1].z, kw[i][1].w};
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {  // channels 128 i + 32 g + 8 sub + [0, 8)
+      const uint4 bw = make_uint4(e4m3x2_f16(wd[2 * sub]), e4m3x2_f16(wd[2 * sub] >> 16),
+                                  e4m3x2_f16(wd[2 * sub + 1]), e4m3x2_f16(wd[2 * sub + 1] >> 16));
+      const v8h av = *reinterpret_cast<const v8h*>(&sA[n16 * kApad + 128 * i + 32 * g + 8 * sub]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(v8h, bw), acc, 0, 0, 0);
+    }
+  }
+  const float lscale = softmax_scale * down * sq;
+  float logit[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) logit[rr] = q_ok ? acc[rr] * lscale : kNegInf;
+
+  // ---- PV code loads now (their latency overlaps the softmax): lane (n16, g) takes
+  //      channels cw0 + kCPL n16 + [0, kCPL) of entries 32 ks + 8 g + [0, 8)
+  const int cw0 = wave * (D / kWinWaves);
+  constexpr int kKS = kWinMax / 32;
+  uint32_t pw[kKS][8];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (!act) {
+        pw[ks][jj] = 0u;
+        continue;
+      }
+      const int e = 32 * ks + 8 * g + jj;
+      const uint8_t* src = wb + (int64_t)(e < nw ? e : 0) * D + cw0 + kCPL * n16;
+      uint32_t v;
+      if (kCPL == 4) v = *reinterpret_cast<const uint32_t*>(src);
+      else if (kCPL == 2) v = *reinterpret_cast<const uint16_t*>(src);
+      else v = *src;
+      pw[ks][jj] = e < nw ? v : 0u;
+    }
+  }
+
+  // ---- softmax statistics; the row scales' largest power of two
+  if (act) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float v = row16_max(logit[rr]);
+      if (n16 == 0) s_red[wave][4 * g + rr] = v;
+    }
+    const float smx = wave_max(sq);
+    if (lane == 0) s_smax[wave] = smx;
+  }
+  __syncthreads();
+  if (tid < kAttHeads) {
+    float m = s_red[0][tid];
+#pragma unroll
+    for (int w2 = 1; w2 < kWinWaves; ++w2) m = fmaxf(m, s_red[w2][tid]);
+    s_m[tid] = m;
+  }
+  float smax = s_smax[0];
+#pragma unroll
+  for (int w2 = 1; w2 < kWinWaves; ++w2) smax = fmaxf(smax, s_smax[w2]);
+  // 2^pk with smax * 2^pk in [1, 2): p * s * 2^pk <= 2 (p <= 1)
+  const int sexp = smax > 0.0f ? (int)((__float_as_uint(smax) >> 23) & 255u) - 127 : 0;
+  const float pup = __uint_as_float((uint32_t)(127 - sexp) << 23);
+  const float pdown = __uint_as_float((uint32_t)(127 + sexp) << 23);
+  __syncthreads();
+  if (act) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int h = 4 * g + rr;
+      const float m = s_m[h];
+      const float p = (m == kNegInf || !q_ok) ? 0.0f : __expf(logit[rr] - m);
+      sP[h * kPpad + eq] = __builtin_bit_cast(uint16_t, (_Float16)(p * sq * pup));
+      const float v = row16_sum(p);
+      if (n16 == 0) s_red[wave][h] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < kAttHeads) {
+    float l = s_red[0][tid];
+#pragma unroll
+    for (int w2 = 1; w2 < kWinWaves; ++w2) l += s_red[w2][tid];
+    s_l[tid] = l;
+  }
+
+  // ---- PV: o[h][c] = sum_e p'[h][e] E4M3(code[e][c]) over this wave's channels
+  v4f o[kCPL];
+#pragma unroll
+  for (int m = 0; m < kCPL; ++m) o[m] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    if (!act || 32 * ks >= nw) break;
+    const v8h pa = *reinterpret_cast<const v8h*>(&sP[n16 * kPpad + 32 * ks + 8 * g]);
+#pragma unroll
+    for (int m = 0; m < kCPL; m += 2) {
+      // bytes m, m + 1 of entries (2 p2, 2 p2 + 1): (e0[m], e1[m], e0[m+1], e1[m+1])
+      uint32_t bx[4], by[4];
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2) {
+        const uint32_t t = __builtin_amdgcn_perm(pw[ks][2 * p2 + 1], pw[ks][2 * p2],
+                                                 (uint32_t)m | (uint32_t)(m + 4) << 8 | (uint32_t)(m + 1) << 16 |
+                                                     (uint32_t)(m + 5) << 24);
+        bx[p2] = e4m3x2_f16(t);          // channel m
+        by[p2] = e4m3x2_f16(t >> 16);    // channel m + 1
+      }
+      o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(v8h, make_uint4(bx[0], bx[1], bx[2], bx[3])),
+                                                    o[m], 0, 0, 0);
+      if (m + 1 < kCPL)
+        o[m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            pa, __builtin_bit_cast(v8h, make_uint4(by[0], by[1], by[2], by[3])), o[m + 1], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // s_l
+  // lane (n16, g) holds o[h = 4 g + rr][channel cw0 + kCPL n16 + m]
+#pragma unroll
+  for (int rr = 0; rr < (act ? 4 : 0); ++rr) {
+    const int h = 4 * g + rr;
+    const float l = s_l[h];
+    const float sc = (l > 0.0f) ? pdown / l : 0.0f;
+    float* dst = po + (int64_t)h * D + cw0 + kCPL * n16;
+#pragma unroll
+    for (int m = 0; m < kCPL; ++m) dst[m] = o[m][rr] * sc;
+  }
+  if (tid < kAttHeads) {
+    ml[2 * tid] = s_m[tid];
+    ml[2 * tid + 1] = s_l[tid];
+  }
+}
+
 template <int D, int WPT, bool G16>
 struct AttLds {
   static constexpr int kApad = D + 8;           // fp16 per A row (padding against bank conflicts)
@@ -75,25 +337,27 @@ struct AttLds {
   static constexpr size_t kO = (size_t)WPT * kAttHeads * D * 4;  // per entry group, after sA/sP/sS are dead
   static constexpr size_t kAP = kA + kP + kS;
   static constexpr size_t kWork = kAP > kO ? kAP : kO;
-  static constexpr size_t kUnion = kWork > sizeof(FinalizeSmem) ? kWork : sizeof(FinalizeSmem);
+  static constexpr size_t kUnion0 = kWork > sizeof(FinalizeSmem) ? kWork : sizeof(FinalizeSmem);
+  static constexpr size_t kUnion = kUnion0 > WinLds<D>::kBytes ? kUnion0 : WinLds<D>::kBytes;
 };
 
 // One block = one query row x 16 heads x one split of up to kAttSplit selected entries.
 // FROM_CAND: the block first derives the row's whole Top-K from the candidate list (every
 // block of the row does this identically; block (split 0, head group 0) writes idx_out).
-// With one split the block writes the final output; otherwise it writes its partial
-// (normalised output, running max, sum) for k_attend_combine.
+// With one partial in all (P == 1) the block writes the final output; otherwise it writes
+// its partial (normalised output, running max, sum) for k_attend_combine.
 // G16: the cache holds one E4M3 scale per 16 channels of each entry (the pages' layout).
 // The scale no longer factors out of the contractions; instead the split's scales are
 // staged in LDS as fp16, [group][entry], and multiply the fp16 key / value operands after
 // the E2M1 conversion (E2M1 * E4M3 is exact in fp16, so the operands stay exact).
 template <int D, bool FROM_CAND, bool G16>
 __global__ __launch_bounds__(kAttThreads) void k_attend_part(
-    int T, int Hq, int K, int S, const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
+    int T, int Hq, int K, int S, int P, const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const void* __restrict__ scales_v, int64_t n_max, const int32_t* __restrict__ idx, const RowCtl* __restrict__ ctl,
     const uint32_t* __restrict__ hist2, const uint2* __restrict__ candbuf, const uint32_t* __restrict__ cnt, int nreg,
     int32_t* __restrict__ idx_out, float softmax_scale, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
-    float* __restrict__ part, float* __restrict__ part_ml) {
+    float* __restrict__ part, float* __restrict__ part_ml, const uint8_t* __restrict__ wcodes,
+    const float* __restrict__ wscales, int64_t wn_max, const int32_t* __restrict__ wend, int window) {
   constexpr int kRowBytes = D / 2;
   constexpr int kCT = D / 128;                 // 128-channel tiles
   constexpr int kWPT = (kAttWaves / kCT < kAttSplit / 32) ? kAttWaves / kCT : kAttSplit / 32;  // waves per tile in PV
@@ -113,6 +377,11 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   const float* scales = static_cast<const float*>(scales_v);
 
   const int split = blockIdx.x, hg = blockIdx.y, r = blockIdx.z;
+  if (split == S) {  // the sliding window's block (grid.x = S + 1 with a window)
+    attend_window_block<D>(hg, r, T, Hq, q, wcodes, wscales, wn_max, wend, window, softmax_scale, P, S, part, part_ml,
+                           s_u);
+    return;
+  }
   const int b = r / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, g = lane >> 4;
@@ -405,11 +674,11 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
 #pragma unroll
     for (int m = 0; m < 8; ++m) o[m] *= inv_l;
     const int h = hg * kAttHeads + hl;
-    if (S == 1) {
-      if (!G16) {
+    if (!G16) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) o[m] *= s_scale[c + m];
-      }
+      for (int m = 0; m < 8; ++m) o[m] *= s_scale[c + m];
+    }
+    if (P == 1) {
       const int64_t oi = ((int64_t)r * Hq + h) * D + c;
       if (out_bf16) {
         uint32_t w4[4];
@@ -422,17 +691,17 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
         dst[1] = make_float4(o[4], o[5], o[6], o[7]);
       }
     } else {
-      float4* dst = reinterpret_cast<float4*>(part + (((int64_t)r * S + split) * Hq + h) * D + c);
+      float4* dst = reinterpret_cast<float4*>(part + (((int64_t)r * P + split) * Hq + h) * D + c);
       dst[0] = make_float4(o[0], o[1], o[2], o[3]);
       dst[1] = make_float4(o[4], o[5], o[6], o[7]);
     }
   }
   if (tid < kAttHeads) {
     const float l = s_l[tid];
-    if (S == 1) {
+    if (P == 1) {
       if (lse) lse[(int64_t)r * Hq + hg * kAttHeads + tid] = (l > 0.0f) ? s_m[tid] + __logf(l) : kNegInf;
     } else {
-      float* ml = part_ml + (((int64_t)r * S + split) * Hq + hg * kAttHeads + tid) * 2;
+      float* ml = part_ml + (((int64_t)r * P + split) * Hq + hg * kAttHeads + tid) * 2;
       ml[0] = s_m[tid];
       ml[1] = l;
     }
@@ -441,66 +710,57 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     for (int i = tid; i < K; i += kAttThreads) idx_out[(int64_t)r * K + i] = s_idx[i];
 }
 
-// Merge the splits of (row, head group, channel tile) by log-sum-exp and scale by s_c
-// (scales null: the G16 layout, whose scales were applied inside the splits).
-// Thread t: head t / 16 of the group, channels 128 ct + 8 (t % 16) + [0, 8); all split
-// loads are issued before any is used.
+// Merge the P partials of (row, head group, channel tile) by log-sum-exp.  Thread t: head
+// t / 16 of the group, channels 128 ct + 8 (t % 16) + [0, 8); all partial loads are issued
+// before any is used.
 template <int D>
-__global__ __launch_bounds__(256) void k_attend_combine(int T, int Hq, int S, const float* __restrict__ scales,
-                                                        const float* __restrict__ part,
+__global__ __launch_bounds__(256) void k_attend_combine(int T, int Hq, int P, const float* __restrict__ part,
                                                         const float* __restrict__ part_ml, void* __restrict__ out,
                                                         int out_bf16, float* __restrict__ lse) {
   constexpr int kCT = D / 128;
-  constexpr int kMaxS = CSA2_MAX_K_DEV / kAttSplit;
-  __shared__ float s_w[kMaxS][kAttHeads];
+  constexpr int kMaxP = CSA2_MAX_K_DEV / kAttSplit + 1;
+  __shared__ float s_w[kMaxP][kAttHeads];
   const int hg = blockIdx.x / kCT, ct = blockIdx.x % kCT, r = blockIdx.y;
-  const int b = r / T;
   const int tid = threadIdx.x;
   const int hl = tid >> 4, c = 128 * ct + 8 * (tid & 15);
   const int h = hg * kAttHeads + hl;
-  // issue the partial loads first (up to kMaxS splits, 2 x 16 B each)
-  float4 pv[kMaxS][2];
+  float4 pv[kMaxP][2];
 #pragma unroll
-  for (int s = 0; s < kMaxS; ++s) {
-    if (s < S) {
-      const float4* src = reinterpret_cast<const float4*>(part + (((int64_t)r * S + s) * Hq + h) * D + c);
+  for (int s = 0; s < kMaxP; ++s) {
+    if (s < P) {
+      const float4* src = reinterpret_cast<const float4*>(part + (((int64_t)r * P + s) * Hq + h) * D + c);
       pv[s][0] = src[0];
       pv[s][1] = src[1];
     }
   }
-  float4 sc0 = make_float4(1.f, 1.f, 1.f, 1.f), sc1 = sc0;
-  if (scales) {
-    sc0 = *reinterpret_cast<const float4*>(scales + (int64_t)b * D + c);
-    sc1 = *reinterpret_cast<const float4*>(scales + (int64_t)b * D + c + 4);
-  }
   if (tid < kAttHeads) {
-    const float* ml = part_ml + ((int64_t)r * S) * Hq * 2;
+    const float* ml = part_ml + ((int64_t)r * P) * Hq * 2;
     const int hh = hg * kAttHeads + tid;
-    float mv[kMaxS], lv[kMaxS];
+    float mv[kMaxP], lv[kMaxP];
     float M = kNegInf;
 #pragma unroll
-    for (int s = 0; s < kMaxS; ++s) {
-      mv[s] = (s < S) ? ml[((int64_t)s * Hq + hh) * 2] : kNegInf;
-      lv[s] = (s < S) ? ml[((int64_t)s * Hq + hh) * 2 + 1] : 0.0f;
+    for (int s = 0; s < kMaxP; ++s) {
+      mv[s] = (s < P) ? ml[((int64_t)s * Hq + hh) * 2] : kNegInf;
+      lv[s] = (s < P) ? ml[((int64_t)s * Hq + hh) * 2 + 1] : 0.0f;
       if (lv[s] > 0.0f) M = fmaxf(M, mv[s]);
     }
     float Z = 0.0f;
 #pragma unroll
-    for (int s = 0; s < kMaxS; ++s) {
+    for (int s = 0; s < kMaxP; ++s) {
       const float wgt = (lv[s] > 0.0f) ? lv[s] * __expf(mv[s] - M) : 0.0f;
       s_w[s][tid] = wgt;
       Z += wgt;
     }
     const float inv = (Z > 0.0f) ? 1.0f / Z : 0.0f;
 #pragma unroll
-    for (int s = 0; s < kMaxS; ++s) s_w[s][tid] *= inv;
+    for (int s = 0; s < kMaxP; ++s) s_w[s][tid] *= inv;
     if (lse && ct == 0) lse[(int64_t)r * Hq + hh] = (Z > 0.0f) ? M + __logf(Z) : kNegInf;
   }
   __syncthreads();
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < kMaxS; ++s) {
-    if (s < S) {
+  for (int s = 0; s < kMaxP; ++s) {
+    if (s < P) {
       const float wgt = s_w[s][hl];
       o[0] = fmaf(wgt, pv[s][0].x, o[0]); o[1] = fmaf(wgt, pv[s][0].y, o[1]);
       o[2] = fmaf(wgt, pv[s][0].z, o[2]); o[3] = fmaf(wgt, pv[s][0].w, o[3]);
@@ -508,8 +768,6 @@ __global__ __launch_bounds__(256) void k_attend_combine(int T, int Hq, int S, co
       o[6] = fmaf(wgt, pv[s][1].z, o[6]); o[7] = fmaf(wgt, pv[s][1].w, o[7]);
     }
   }
-  o[0] *= sc0.x; o[1] *= sc0.y; o[2] *= sc0.z; o[3] *= sc0.w;
-  o[4] *= sc1.x; o[5] *= sc1.y; o[6] *= sc1.z; o[7] *= sc1.w;
   const int64_t oi = ((int64_t)r * Hq + h) * D + c;
   if (out_bf16) {
     uint32_t w4[4];
@@ -533,20 +791,33 @@ __device__ __forceinline__ float deq_f32(const uint8_t* cb, const uint8_t* gsb, 
   return G16 ? e * e4m3_value(gsb[(int64_t)j * (D / 16) + c / 16]) : e * s_scale[c];
 }
 
+// Entries 0 .. K-1 come from the selection (FP4 cache), entries K .. K+nw-1 from the
+// sliding window (E4M3 rows with one fp32 scale each: E4M3 * s_row).
 template <bool G16>
 __global__ __launch_bounds__(256) void k_attend_f32(int T, int Hq, int D, int K, const float* __restrict__ q,
                                                     const uint8_t* __restrict__ codes,
                                                     const void* __restrict__ scales_v, int64_t n_max,
-                                                    const int32_t* __restrict__ idx, float softmax_scale,
+                                                    const int32_t* __restrict__ idx, const uint8_t* __restrict__ wcodes,
+                                                    const float* __restrict__ wscales, int64_t wn_max,
+                                                    const int32_t* __restrict__ wend, int window, float softmax_scale,
                                                     float* __restrict__ out, float* __restrict__ lse) {
   __shared__ float s_q[CSA2_MAX_D_DEV];
   __shared__ float s_scale[CSA2_MAX_D_DEV];
-  __shared__ float s_logit[CSA2_MAX_K_DEV];
+  __shared__ float s_logit[CSA2_MAX_K_DEV + CSA2_MAX_WINDOW_DEV];
   __shared__ int32_t s_idx[CSA2_MAX_K_DEV];
   __shared__ float s_red[8];
   const int h = blockIdx.x, r = blockIdx.y, b = r / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* qh = q + ((int64_t)r * Hq + h) * D;
+  int64_t w_end = 0, w_start = 0;
+  if (wcodes) {
+    w_end = wend[r] < wn_max ? wend[r] : wn_max;
+    w_start = w_end - window > 0 ? w_end - window : 0;
+  }
+  const int nw = w_end > w_start ? (int)(w_end - w_start) : 0;
+  const int E = K + nw;
+  const uint8_t* wrow = wcodes ? wcodes + ((int64_t)b * wn_max + w_start) * D : nullptr;
+  const float* wsc = wcodes ? wscales + (int64_t)b * wn_max + w_start : nullptr;
   for (int c = tid; c < D; c += 256) {
     s_q[c] = qh[c];
     if (!G16) s_scale[c] = static_cast<const float*>(scales_v)[(int64_t)b * D + c];
@@ -558,25 +829,33 @@ __global__ __launch_bounds__(256) void k_attend_f32(int T, int Hq, int D, int K,
   __syncthreads();
   const uint8_t* cb = codes + (int64_t)b * n_max * (D / 2);
   const uint8_t* gsb = G16 ? static_cast<const uint8_t*>(scales_v) + (int64_t)b * n_max * (D / 16) : nullptr;
-  for (int e = wave; e < K; e += 4) {
-    const int32_t j = s_idx[e];
+  for (int e = wave; e < E; e += 4) {
     float dot = 0.0f;
-    if (j >= 0) {
-      for (int c = lane; c < D; c += 64) dot = fmaf(s_q[c], deq_f32<G16>(cb, gsb, s_scale, D, j, c), dot);
+    bool ok;
+    if (e < K) {
+      const int32_t j = s_idx[e];
+      ok = j >= 0;
+      if (ok)
+        for (int c = lane; c < D; c += 64) dot = fmaf(s_q[c], deq_f32<G16>(cb, gsb, s_scale, D, j, c), dot);
+    } else {
+      ok = true;
+      const uint8_t* row = wrow + (int64_t)(e - K) * D;
+      for (int c = lane; c < D; c += 64) dot = fmaf(s_q[c], e4m3_value(row[c]), dot);
+      dot *= wsc[e - K];
     }
     dot = wave_sum(dot);
-    if (lane == 0) s_logit[e] = (j >= 0) ? dot * softmax_scale : kNegInf;
+    if (lane == 0) s_logit[e] = ok ? dot * softmax_scale : kNegInf;
   }
   __syncthreads();
   float m = kNegInf;
-  for (int e = tid; e < K; e += 256) m = fmaxf(m, s_logit[e]);
+  for (int e = tid; e < E; e += 256) m = fmaxf(m, s_logit[e]);
   m = wave_max(m);
   if (lane == 0) s_red[wave] = m;
   __syncthreads();
   m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   __syncthreads();
   float z = 0.0f;
-  for (int e = tid; e < K; e += 256) {
+  for (int e = tid; e < E; e += 256) {
     const float p = (m == kNegInf) ? 0.0f : expf(s_logit[e] - m);
     s_logit[e] = p;
     z += p;
@@ -593,6 +872,7 @@ __global__ __launch_bounds__(256) void k_attend_f32(int T, int Hq, int D, int K,
       if (j < 0) continue;
       o = fmaf(s_logit[e], deq_f32<G16>(cb, gsb, s_scale, D, j, c), o);
     }
+    for (int e = 0; e < nw; ++e) o = fmaf(s_logit[K + e], e4m3_value(wrow[(int64_t)e * D + c]) * wsc[e], o);
     out[((int64_t)r * Hq + h) * D + c] = o * inv;
   }
   if (lse && tid == 0) lse[(int64_t)r * Hq + h] = (z > 0.0f) ? m + logf(z) : kNegInf;
@@ -600,54 +880,60 @@ __global__ __launch_bounds__(256) void k_attend_f32(int T, int Hq, int D, int K,
 
 int attend_splits(int K) { return (K + kAttSplit - 1) / kAttSplit; }
 
-size_t attend_ws_floats(int R, int Hq, int D, int K) {
-  const int S = attend_splits(K);
-  if (S <= 1) return 0;
-  return (size_t)R * S * Hq * D + (size_t)R * S * Hq * 2;
+// partial slots: the selection's splits, plus one for the sliding window
+static int attend_parts(int K, bool window) { return attend_splits(K) + (window ? 1 : 0); }
+
+size_t attend_ws_floats(int R, int Hq, int D, int K, int window) {
+  const int P = attend_parts(K, window > 0);
+  if (P <= 1) return 0;
+  return (size_t)R * P * Hq * D + (size_t)R * P * Hq * 2;
 }
 
 template <int D, bool FC, bool G16>
-static void launch_mfma(const AttendArgs& a, int S, hipStream_t st) {
-  dim3 g(S, a.Hq / kAttHeads, a.B * a.T);
-  float* part_ml = a.part ? a.part + (size_t)a.B * a.T * S * a.Hq * D : nullptr;
-  hipLaunchKernelGGL((k_attend_part<D, FC, G16>), g, dim3(kAttThreads), 0, st, a.T, a.Hq, a.K, S,
+static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
+  // the window (if any) is one more block column, run beside the selection's splits
+  dim3 g(S + (a.swa_codes ? 1 : 0), a.Hq / kAttHeads, a.B * a.T);
+  float* part_ml = a.part ? a.part + (size_t)a.B * a.T * P * a.Hq * D : nullptr;
+  hipLaunchKernelGGL((k_attend_part<D, FC, G16>), g, dim3(kAttThreads), 0, st, a.T, a.Hq, a.K, S, P,
                      (const uint16_t*)a.q, a.codes, a.scales, a.n_max, a.idx, a.ctl, a.hist2, a.candbuf, a.cnt,
-                     a.nreg, a.idx_out, a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml);
-  if (S > 1)
+                     a.nreg, a.idx_out, a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml, a.swa_codes,
+                     a.swa_scales, a.swa_n_max, a.swa_end, a.window);
+  if (P > 1)
     hipLaunchKernelGGL(k_attend_combine<D>, dim3(a.Hq / kAttHeads * (D / 128), a.B * a.T), dim3(256), 0, st, a.T,
-                       a.Hq, S, G16 ? nullptr : static_cast<const float*>(a.scales), (const float*)a.part,
-                       (const float*)part_ml, a.out, (int)a.out_bf16, a.lse);
+                       a.Hq, P, (const float*)a.part, (const float*)part_ml, a.out, (int)a.out_bf16, a.lse);
 }
 
 template <int D>
-static void launch_mfma_d(const AttendArgs& a, int S, hipStream_t st) {
+static void launch_mfma_d(const AttendArgs& a, int S, int P, hipStream_t st) {
   const bool fc = a.candbuf != nullptr;
   if (a.g16)
-    fc ? launch_mfma<D, true, true>(a, S, st) : launch_mfma<D, false, true>(a, S, st);
+    fc ? launch_mfma<D, true, true>(a, S, P, st) : launch_mfma<D, false, true>(a, S, P, st);
   else
-    fc ? launch_mfma<D, true, false>(a, S, st) : launch_mfma<D, false, false>(a, S, st);
+    fc ? launch_mfma<D, true, false>(a, S, P, st) : launch_mfma<D, false, false>(a, S, P, st);
 }
 
 int launch_attend(const AttendArgs& a, hipStream_t st) {
   const int R = a.B * a.T;
+  if (a.swa_codes && (a.window < 1 || a.window > kWinMax)) return -1;
   if (!a.q_bf16) {
     if (a.candbuf) return -1;  // the fp32 path takes given indices
     if (a.g16)
       hipLaunchKernelGGL(k_attend_f32<true>, dim3(a.Hq, R), dim3(256), 0, st, a.T, a.Hq, a.D, a.K,
-                         (const float*)a.q, a.codes, a.scales, a.n_max, a.idx, a.softmax_scale, (float*)a.out,
-                         a.lse);
+                         (const float*)a.q, a.codes, a.scales, a.n_max, a.idx, a.swa_codes, a.swa_scales,
+                         a.swa_n_max, a.swa_end, a.window, a.softmax_scale, (float*)a.out, a.lse);
     else
       hipLaunchKernelGGL(k_attend_f32<false>, dim3(a.Hq, R), dim3(256), 0, st, a.T, a.Hq, a.D, a.K,
-                         (const float*)a.q, a.codes, a.scales, a.n_max, a.idx, a.softmax_scale, (float*)a.out,
-                         a.lse);
+                         (const float*)a.q, a.codes, a.scales, a.n_max, a.idx, a.swa_codes, a.swa_scales,
+                         a.swa_n_max, a.swa_end, a.window, a.softmax_scale, (float*)a.out, a.lse);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   const int S = attend_splits(a.K);
-  if (S > 1 && !a.part) return -1;
+  const int P = attend_parts(a.K, a.swa_codes != nullptr);
+  if (P > 1 && !a.part) return -1;
   switch (a.D) {
-    case 128: launch_mfma_d<128>(a, S, st); break;
-    case 256: launch_mfma_d<256>(a, S, st); break;
-    case 512: launch_mfma_d<512>(a, S, st); break;
+    case 128: launch_mfma_d<128>(a, S, P, st); break;
+    case 256: launch_mfma_d<256>(a, S, P, st); break;
+    case 512: launch_mfma_d<512>(a, S, P, st); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

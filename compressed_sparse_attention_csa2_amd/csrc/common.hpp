@@ -21,6 +21,7 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 #define CSA2_MAX_D_DEV 512
+#define CSA2_MAX_WINDOW_DEV 128
 #define CSA2_MAX_K_DEV 2048
 #define CSA2_MAX_DK_DEV 256
 constexpr float kNegInf = -__builtin_inff();

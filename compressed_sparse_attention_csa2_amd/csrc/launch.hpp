@@ -89,11 +89,17 @@ struct AttendArgs {
   const uint32_t* cnt;    // [R][nreg]
   int nreg;
   int32_t* idx_out;   // written when taking the Top-K from candidates (nullable)
-  float* part;        // MFMA path with more than one entry split: partial results (attend_ws_floats)
+  float* part;        // MFMA path with more than one partial: partial results (attend_ws_floats)
+  // sliding window (swa_codes null: none): E4M3 rows [B][swa_n_max][D], scales [B][swa_n_max]
+  const uint8_t* swa_codes;
+  const float* swa_scales;
+  int64_t swa_n_max;
+  const int32_t* swa_end;  // [B][T]
+  int window;
 };
 int launch_attend(const AttendArgs& a, hipStream_t st);
 int attend_splits(int K);
-size_t attend_ws_floats(int R, int Hq, int D, int K);
+size_t attend_ws_floats(int R, int Hq, int D, int K, int window);
 
 int launch_gather_dequant(bool g16, int B, int T, int K, int D, const uint8_t* codes, const void* scales,
                           int64_t n_max, const int32_t* idx, float* out, hipStream_t st);

@@ -67,6 +67,7 @@ typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
 #define CSA2_MAX_HQ 128      /* attention heads */
 #define CSA2_MAX_DK 256      /* indexer dim (fp32 indexer); the fp8 indexer needs dk == 64 */
 #define CSA2_MAX_H 64        /* indexer heads (fp32 indexer); the fp8 indexer needs H == 32 */
+#define CSA2_MAX_WINDOW 128  /* sliding-window entries per query */
 
 /* Human-readable name of a csa2_status (static string). */
 const char* csa2_status_string(int status);
@@ -165,6 +166,25 @@ int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_
 size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int K);
 
 /*
+ * A layer's own sliding-window cache ("CSA2 In Simple Terms": every layer also attends to
+ * the most recent tokens; window 128 in "Model Setup Numbers"; the window cache stays
+ * 8-bit in "FP4 Main KV Cache To Halve Storage Again"; each layer keeps its own, 3.3 of
+ * the Chinese reading).  codes [B][n_max][D] E4M3 with one fp32 scale per row, scales
+ * [B][n_max] (the layout csa2_quantize_kv writes with CSA2_FMT_FP8_PER_TOKEN).  Query row
+ * (b, t) attends to window rows [max(0, e - window), e), e = min(end[b][t], n_max), in the
+ * same softmax as its selected entries (a ring buffer that holds exactly the window may
+ * pass end = its fill count: the order of rows does not matter).  1 <= window <=
+ * CSA2_MAX_WINDOW.
+ */
+typedef struct {
+  const uint8_t* codes;
+  const float* scales;
+  int64_t n_max;
+  const int32_t* end;    /* [B][T] */
+  int window;
+} csa2_swa;
+
+/*
  * Sparse softmax attention over the selected FP4 entries.  Sources: "Compressed Sparse
  * Attention 2 Or CSA2 In Simple Terms" (attend to the selected entries), "FP4 Main KV
  * Cache To Halve Storage Again" (dequantise before attention), "Model Setup Numbers"
@@ -182,13 +202,16 @@ size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int K);
  *   power-of-two prescale) and into the output; per-16-channel scales multiply the fp16
  *   key/value operands (E2M1 * E4M3 is exact in fp16).  Entries are processed in groups of
  *   512 whose partial softmax results are merged by log-sum-exp.
- *   ws: csa2_sparse_attend_workspace_size() bytes (0 when K <= 512 or q is fp32; then ws
- *   may be NULL).
+ *   swa (nullable): the layer's sliding-window entries, joining the same softmax (the
+ *   window's partial result is merged with the selected entries' by log-sum-exp).
+ *   ws: csa2_sparse_attend_workspace_size() bytes (0 when K <= 512 without a window, or q
+ *   is fp32; then ws may be NULL); `window` there is swa->window, or 0 without a window.
  */
 int csa2_sparse_attend(int B, int T, int Hq, int D, const void* q, int q_dtype, int kv_fmt, const uint8_t* kv_codes,
-                       const void* kv_scales, int64_t n_max, const int32_t* idx, int K, float softmax_scale,
-                       void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
-size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype);
+                       const void* kv_scales, int64_t n_max, const int32_t* idx, int K, const csa2_swa* swa,
+                       float softmax_scale, void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes,
+                       void* stream);
+size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int q_dtype, int window);
 
 /*
  * Layer group: Full / Reindex / Reuse layers over one shared cache, run strictly in order.
@@ -203,7 +226,9 @@ size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int
  * FULL or REINDEX; otherwise CSA2_ERR_MODE.  Per-layer pointers: q_idx [B][1][H][dk]
  * (q_dtype), w [B][1][H], q_attn [B][1][Hq][D] (q_dtype), out [B][1][Hq][D] (out_dtype),
  * lse [B][1][Hq] (nullable), idx [B][1][K] written by FULL/REINDEX, ignored by REUSE
- * (may be NULL there).  Decode only (one query token per sequence).
+ * (may be NULL there), swa (nullable): the layer's own sliding-window cache (never shared;
+ * its window must not exceed csa2_group_cache.window).  Decode only (one query token per
+ * sequence).
  * With a candidate pool (csa2_group_cache.pool_blocks > 0), a REINDEX layer after a FULL
  * layer scores only the pool that the most recent FULL layer left; pool [B][pool_blocks *
  * pool_block] (nullable, FULL only) receives that pool's positions: selected blocks
@@ -219,6 +244,7 @@ typedef struct {
   float* lse;
   int32_t* idx;          /* FULL/REINDEX: output; REUSE: ignored */
   int32_t* pool;         /* FULL with a pool: optional output; otherwise ignored */
+  const csa2_swa* swa;   /* nullable */
 } csa2_layer;
 
 typedef struct {
@@ -240,6 +266,7 @@ typedef struct {
   int pool_block;
   int pool_blocks;
   int kv_fmt;              /* CSA2_FMT_FP4_PER_CHANNEL (0) or CSA2_FMT_FP4_G16 */
+  int window;              /* largest sliding window of the layers (0: no layer has one) */
 } csa2_group_cache;
 
 int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_cache* cache, void* ws,

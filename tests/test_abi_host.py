@@ -63,20 +63,27 @@ def test_errors_before_any_launch():
     assert L.csa2_index_score(7, 1, 1, 32, 64, _p(), 1, _p(), _p(), _p(), 100, _p(), None, None, 0, _p(), None, 0,
                               None) == -3
     # attention: bf16 path needs Hq % 16 == 0 and D in {128, 256, 512}; fp32 query needs fp32 output
-    assert L.csa2_sparse_attend(1, 1, 8, 512, _p(), 1, 0, _p(), _p(), 10, _p(), 8, 1.0, _p(), 1, None, None, 0,
+    assert L.csa2_sparse_attend(1, 1, 8, 512, _p(), 1, 0, _p(), _p(), 10, _p(), 8, None, 1.0, _p(), 1, None, None, 0,
                                 None) == -6
-    assert L.csa2_sparse_attend(1, 1, 16, 384, _p(), 1, 0, _p(), _p(), 10, _p(), 8, 1.0, _p(), 1, None, None, 0,
+    assert L.csa2_sparse_attend(1, 1, 16, 384, _p(), 1, 0, _p(), _p(), 10, _p(), 8, None, 1.0, _p(), 1, None, None, 0,
                                 None) == -6
-    assert L.csa2_sparse_attend(1, 1, 8, 128, _p(), 0, 0, _p(), _p(), 10, _p(), 8, 1.0, _p(), 1, None, None, 0,
+    assert L.csa2_sparse_attend(1, 1, 8, 128, _p(), 0, 0, _p(), _p(), 10, _p(), 8, None, 1.0, _p(), 1, None, None, 0,
                                 None) == -3
-    assert L.csa2_sparse_attend(1, 1, 16, 512, _p(), 1, 0, _p(), _p(), 10, _p(), 4096, 1.0, _p(), 1, None, None, 0,
+    assert L.csa2_sparse_attend(1, 1, 16, 512, _p(), 1, 0, _p(), _p(), 10, _p(), 4096, None, 1.0, _p(), 1, None, None, 0,
                                 None) == -2
     # main-KV layouts: per channel (0) or one E4M3 scale per 16 channels (2, D % 16 == 0); the
     # E4M3 per-token format (1) is not a main-KV layout
-    assert L.csa2_sparse_attend(1, 1, 16, 512, _p(), 1, 1, _p(), _p(), 10, _p(), 8, 1.0, _p(), 1, None, None, 0,
+    assert L.csa2_sparse_attend(1, 1, 16, 512, _p(), 1, 1, _p(), _p(), 10, _p(), 8, None, 1.0, _p(), 1, None, None, 0,
                                 None) == -3
-    assert L.csa2_sparse_attend(1, 1, 8, 40, _p(), 0, 2, _p(), _p(), 10, _p(), 8, 1.0, _p(), 0, None, None, 0,
+    assert L.csa2_sparse_attend(1, 1, 8, 40, _p(), 0, 2, _p(), _p(), 10, _p(), 8, None, 1.0, _p(), 0, None, None, 0,
                                 None) == -2
+    # sliding window: 1 <= window <= 128, every pointer given
+    for win, ptrs, code in [(0, True, -2), (129, True, -2), (16, False, -1)]:
+        sw = csa2._Swa(_p() if ptrs else None, _p(), 100, _p(), win)
+        assert L.csa2_sparse_attend(1, 1, 16, 512, _p(), 1, 0, _p(), _p(), 10, _p(), 8, ctypes.byref(sw), 1.0, _p(),
+                                    1, None, None, 0, None) == code
+    assert L.csa2_sparse_attend_workspace_size(2, 1, 64, 512, 512, 1, 0) == 0
+    assert L.csa2_sparse_attend_workspace_size(2, 1, 64, 512, 512, 1, 128) >= 2 * 2 * 64 * 512 * 4
     assert L.csa2_gather_dequant(2, 1, 1, 8, 24, _p(), _p(), 10, _p(), _p(), None) == -2
     assert L.csa2_gather_dequant(5, 1, 1, 8, 32, _p(), _p(), 10, _p(), _p(), None) == -3
     assert L.csa2_quantize_kv(2, 0, 1, 1, 24, _p(), 0, 24, 24, None, 4, _p(), _p(), None) == -2
