@@ -28,7 +28,7 @@ _SRC = os.path.join(_HERE, "csa2_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libcsa2_oracle.so")
 _lib = None
 
-PREC_FP32, PREC_FP8 = 0, 1
+PREC_FP32, PREC_FP8, PREC_FP4 = 0, 1, 2
 FMT_FP4_PER_CHANNEL, FMT_FP4_G16 = 0, 2
 
 
@@ -53,6 +53,7 @@ def _load():
         L.orc_e4m3_encode.argtypes, L.orc_e4m3_encode.restype = [f], i
         L.orc_quantize_fp4.argtypes = [i, i, i, p, i64, i64, p, i64, p, p, i]
         L.orc_quantize_fp8.argtypes = [i, i, i, p, i64, i64, p, i64, p, p]
+        L.orc_quantize_fp4_rows.argtypes = [i, i, i, p, i64, i64, p, i64, p, p]
         L.orc_quantize_index_query.argtypes = [i, i, p, p, p]
         L.orc_quantize_fp4_g16.argtypes = [i, i, i, p, i64, i64, p, i64, p, p]
         L.orc_gather_dequant.argtypes = [i, i, i, i, i, p, p, i64, p, p]
@@ -61,7 +62,8 @@ def _load():
         L.orc_sparse_attend.argtypes = [i, i, i, i, i, p, p, p, i64, p, i, p, p, i64, p, i, d, p, p]
         L.orc_coarse_keys.argtypes = [i, i64, p, i, i, p, p, p, p]
         L.orc_num_threads.argtypes, L.orc_num_threads.restype = [], i
-        for fn in ("orc_quantize_fp4", "orc_quantize_fp4_g16", "orc_quantize_fp8", "orc_quantize_index_query",
+        for fn in ("orc_quantize_fp4", "orc_quantize_fp4_g16", "orc_quantize_fp8", "orc_quantize_fp4_rows",
+                   "orc_quantize_index_query",
                    "orc_gather_dequant", "orc_index_score", "orc_topk", "orc_sparse_attend", "orc_coarse_keys"):
             getattr(L, fn).restype = None
         _lib = L
@@ -138,6 +140,21 @@ def _kv_scales(scales):
     return FMT_FP4_PER_CHANNEL, _c(a, np.float32)
 
 
+def quantize_fp4_rows(x, n_max=None, n0=None, codes=None, scales=None):
+    """x [B][T][D] -> (codes [B][n_max][D/2] u8, scales [B][n_max] f32): E2M1 with one
+    absmax/6 scale per row (the 4-bit indexer keys, orc_quantize_fp4_rows)."""
+    x = _c(x, np.float32)
+    B, T, D = x.shape
+    assert D % 2 == 0
+    n_max = T if n_max is None else n_max
+    codes = np.zeros((B, n_max, D // 2), np.uint8) if codes is None else codes
+    scales = np.zeros((B, n_max), np.float32) if scales is None else scales
+    assert codes.flags["C_CONTIGUOUS"] and scales.flags["C_CONTIGUOUS"]
+    n0a = None if n0 is None else _c(n0, np.int32)
+    _load().orc_quantize_fp4_rows(B, T, D, _p(x), T * D, D, _p(n0a), n_max, _p(codes), _p(scales))
+    return codes, scales
+
+
 def quantize_fp8(x, n_max=None, n0=None, codes=None, scales=None):
     """x [B][T][D] -> (codes [B][n_max][D] u8, scales [B][n_max] f32); per-row absmax/448."""
     x = _c(x, np.float32)
@@ -176,7 +193,8 @@ def gather_dequant(codes, scales, idx):
 def index_score(prec, q, w, k, k_scale, n_keys, q_limit=None, cand=None):
     """Scores [B][T][ncols] float64 (-inf where not visible).
 
-    prec PREC_FP32: k is [B][n_max][dk] f32; PREC_FP8: k is E4M3 codes + k_scale [B][n_max]."""
+    prec PREC_FP32: k is [B][n_max][dk] f32; PREC_FP8: k is E4M3 codes + k_scale [B][n_max];
+    PREC_FP4: k is packed E2M1 codes [B][n_max][dk/2] + k_scale [B][n_max]."""
     q = _c(q, np.float32)
     B, T, H, dk = q.shape
     w = _c(w, np.float32)

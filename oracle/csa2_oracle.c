@@ -191,6 +191,34 @@ void orc_quantize_fp8(int B, int T, int D, const float* x, int64_t xsb, int64_t 
   }
 }
 
+/* FP4 (E2M1) quantisation with one fp32 scale per row: the 4-bit indexer keys.
+ * [N] "FP4 Main KV Cache To Halve Storage Again": the indexer queries and keys were already
+ * 4-bit in the earlier model.  Reading (the pages give no layout): E2M1 with one fp32
+ * scale per row, s = fl32(max_d |x_d| / 6), code = E2M1(fl32(x_d / s)) (s == 0 gives code
+ * +0), two codes per byte with the even dim in the low nibble; codes [B][n_max][D/2],
+ * scales [B][n_max]. */
+void orc_quantize_fp4_rows(int B, int T, int D, const float* x, int64_t xsb, int64_t xst, const int32_t* n0,
+                           int64_t n_max, uint8_t* codes, float* scales) {
+  for (int b = 0; b < B; ++b) {
+    int64_t base = n0 ? n0[b] : 0;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+      const float* xr = x + b * xsb + t * xst;
+      float amax = 0.0f;
+      for (int d = 0; d < D; ++d)
+        if (fabsf(xr[d]) > amax) amax = fabsf(xr[d]);
+      float s = amax / 6.0f;
+      int64_t row = (int64_t)b * n_max + base + t;
+      scales[row] = s;
+      for (int d = 0; d < D; d += 2) {
+        int lo = s != 0.0f ? orc_e2m1_encode(xr[d] / s) : 0;
+        int hi = s != 0.0f ? orc_e2m1_encode(xr[d + 1] / s) : 0;
+        codes[row * (D / 2) + d / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}
+
 /* Main-KV formats: 0 = one fp32 scale per (sequence, channel), scales [B][D];
  *                  2 = one E4M3 scale per 16 channels of each entry, scales [B][n_max][D/16]. */
 enum { ORC_FMT_FP4_PER_CHANNEL = 0, ORC_FMT_FP4_G16 = 2 };
@@ -235,7 +263,9 @@ void orc_gather_dequant(int fmt, int B, int T, int K, int D, const uint8_t* code
  *   prec 1 (fp8): the query is quantised per (token, head) to E4M3 with its own absmax/448
  *     scale sq_h (part of the definition; the pages keep indexer q and k low-bit), so
  *     score_j = sk_j * sum_h w_h * sq_h * sum_d E4M3(q8_hd) * E4M3(k8_jd).
- * q8 / sq are the pre-quantised query (prec 1) or NULL; qf the fp32 query (prec 0). */
+ *   prec 2 (fp4): the same with E2M1 in place of E4M3 on both sides: the query quantised
+ *     per (token, head) with sq_h = absmax/6, the keys from orc_quantize_fp4_rows.
+ * q8 / sq are the pre-quantised query (prec 1, 2) or NULL; qf the fp32 query (prec 0). */
 static double score_one(int prec, int H, int dk, const float* qf, const uint8_t* q8, const float* sq,
                         const float* w, const void* k, const float* k_scale, int64_t row) {
   double total = 0.0;
@@ -246,7 +276,7 @@ static double score_one(int prec, int H, int dk, const float* qf, const uint8_t*
       for (int d = 0; d < dk; ++d) dot += (double)qf[h * dk + d] * (double)kr[d];
       total += (double)w[h] * dot;
     }
-  } else {
+  } else if (prec == 1) {
     const uint8_t* kr = (const uint8_t*)k + row * dk;
     for (int h = 0; h < H; ++h) {
       double dot = 0.0;
@@ -254,8 +284,34 @@ static double score_one(int prec, int H, int dk, const float* qf, const uint8_t*
       total += (double)w[h] * (double)sq[h] * dot;
     }
     total *= (double)k_scale[row];
+  } else {
+    /* prec 2: E2M1 query codes (one per byte here) against packed E2M1 key codes */
+    const uint8_t* kr = (const uint8_t*)k + row * (dk / 2);
+    for (int h = 0; h < H; ++h) {
+      double dot = 0.0;
+      for (int d = 0; d < dk; ++d) {
+        int kc = (d & 1) ? (kr[d / 2] >> 4) : (kr[d / 2] & 15);
+        dot += orc_e2m1_value(q8[h * dk + d]) * orc_e2m1_value(kc);
+      }
+      total += (double)w[h] * (double)sq[h] * dot;
+    }
+    total *= (double)k_scale[row];
   }
   return total;
+}
+
+/* Per-(token, head) E2M1 quantisation of the indexer query (prec 2): sq = fl32(absmax/6),
+ * code = E2M1(fl32(q / sq)), one code per byte. */
+static void quantize_index_query_fp4(int rows, int dk, const float* q, uint8_t* q4, float* sq) {
+  for (int r = 0; r < rows; ++r) {
+    const float* qr = q + (int64_t)r * dk;
+    float amax = 0.0f;
+    for (int d = 0; d < dk; ++d)
+      if (fabsf(qr[d]) > amax) amax = fabsf(qr[d]);
+    float s = amax / 6.0f;
+    sq[r] = s;
+    for (int d = 0; d < dk; ++d) q4[(int64_t)r * dk + d] = (uint8_t)(s != 0.0f ? orc_e2m1_encode(qr[d] / s) : 0);
+  }
 }
 
 /* Per-(token, head) E4M3 quantisation of the indexer query (prec 1). */
@@ -276,6 +332,7 @@ void orc_index_score(int prec, int B, int T, int H, int dk, const float* q, cons
   uint8_t* q8 = (uint8_t*)malloc((size_t)B * T * H * dk + 1);
   float* sq = (float*)malloc(sizeof(float) * ((size_t)B * T * H + 1));
   if (prec == 1) orc_quantize_index_query(B * T * H, dk, q, q8, sq);
+  if (prec == 2) quantize_index_query_fp4(B * T * H, dk, q, q8, sq);
   for (int64_t r = 0; r < (int64_t)B * T; ++r) {
     int b = (int)(r / T);
     int64_t limit = n_keys[b] - 1;
