@@ -41,23 +41,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_device_cache(wl, copies, kv_fmt=csa2.FMT_FP4_PER_CHANNEL):
+def build_device_cache(wl, copies, kv_fmt=csa2.FMT_FP4_PER_CHANNEL, key_fmt=csa2.FMT_FP8_PER_TOKEN):
     """Quantise the workload's cache on the GPU (one sequence at a time) and clone it.  The
     main KV takes one fp32 scale per channel, or (FMT_FP4_G16) one E4M3 scale per 16
-    channels of each entry."""
+    channels of each entry; the indexer keys are E4M3, or (FMT_FP4_PER_TOKEN) E2M1, with
+    one scale per row."""
     B, N, D, dk = wl.B, wl.N, wl.D, wl.dk
     codes = torch.empty((B, N, D // 2), dtype=torch.uint8, device="cuda")
     if kv_fmt == csa2.FMT_FP4_G16:
         scales = torch.empty((B, N, D // 16), dtype=torch.uint8, device="cuda")
     else:
         scales = torch.empty((B, D), dtype=torch.float32, device="cuda")
-    k8 = torch.empty((B, N, dk), dtype=torch.uint8, device="cuda")
+    k8 = torch.empty((B, N, dk if key_fmt == csa2.FMT_FP8_PER_TOKEN else dk // 2), dtype=torch.uint8, device="cuda")
     ks = torch.empty((B, N), dtype=torch.float32, device="cuda")
     for b in range(B):
         x = torch.from_numpy(wl.main_kv(b)).to("cuda")
         csa2.quantize_kv(kv_fmt, x[None], codes[b:b + 1], scales[b:b + 1])
         kf = torch.from_numpy(wl.index_keys(b)).to("cuda")
-        csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, kf[None], k8[b:b + 1], ks[b:b + 1])
+        csa2.quantize_kv(key_fmt, kf[None], k8[b:b + 1], ks[b:b + 1])
         torch.cuda.synchronize()
         del x, kf
     n_keys = torch.full((B,), N, dtype=torch.int32, device="cuda")
@@ -432,6 +433,42 @@ def run_group128k_swa(args):
         "step_pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
 
 
+def run_group128k_fp4idx(args):
+    """The 128K decode group (Full -> Reindex -> Reuse, 16 x 131072, Top-512) with the 4-bit
+    indexer: E2M1 keys with one fp32 scale per row (36 B per key instead of 68) and the
+    query quantised to E2M1 per head, scored on the FP4 form of the MFMA."""
+    wl = workloads.WORKLOADS["group128k"]
+    log("building cache (%d copies) ..." % args.copies)
+    caches = build_device_cache(wl, args.copies, key_fmt=csa2.FMT_FP4_PER_TOKEN)
+    layers = layer_inputs(wl)
+    plans = [csa2.GroupPlan([dict(L) for L in layers],
+                            csa2.GroupCache(c["n_keys"], c["codes"], c["scales"], c["k8"], c["ks"], wl.K,
+                                            wl.softmax_scale, prec=csa2.PREC_FP4), out_dtype=torch.bfloat16)
+             for c in caches]
+    for s in range(args.warmup):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    B, N = wl.B, wl.N
+    n_index = sum(1 for m in wl.modes if m != "reuse")
+    alg = algorithmic_bytes(wl) - n_index * B * N * (wl.dk // 2)    # 32 of the 64 key bytes
+    gbs = alg / (ms_step / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "CSA2 decode queries/s at 128K context (4-bit indexer)", "value": round(B / (ms_step / 1e3), 1),
+        "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4+bf16", "data": "synthetic",
+        "config": {"workload": "group128k_fp4idx: Full->Reindex->Reuse decode, B=16, N=131072, indexer 32x64 E2M1 "
+                               "(per-row scale), Top-512, FP4 E2M1 main KV D=512, 64 heads bf16",
+                   "global_batch": B, "seq_len": N, "layers": list(wl.modes), "cache_copies": args.copies},
+        "step_algorithmic_bytes": alg, "step_achieved_GBps": round(gbs, 1),
+        "step_pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
+
+
 def run_hier1m(args):
     """The 1M-entry two-level configuration (one sequence): coarse keys (64-entry block
     means, built once, not timed) -> score 16384 coarse keys -> top-256 blocks -> exact
@@ -515,12 +552,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="group128k",
                     choices=["group128k", "prefill", "full64k", "hier1m", "decoder128k", "group128k_g16",
-                             "group128k_swa"],
+                             "group128k_swa", "group128k_fp4idx"],
                     help="group128k: the 128K decode group (the headline; default); prefill: the chunked-prefill "
                          "path; full64k: one Full layer at 64K; hier1m: the two-level indexer at 1M; decoder128k: "
                          "the 20-layer decoder schedule at 128K with the candidate pool; group128k_g16: the 128K group with "
                          "the per-16-channel E4M3-scaled FP4 layout; group128k_swa: the 128K group with a 128-token sliding "
-                         "window per layer")
+                         "window per layer; group128k_fp4idx: the 128K group with the 4-bit indexer")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -552,6 +589,9 @@ def main():
         return
     if args.workload == "group128k_swa":
         run_group128k_swa(args)
+        return
+    if args.workload == "group128k_fp4idx":
+        run_group128k_fp4idx(args)
         return
     wl = workloads.WORKLOADS["group128k"]
     log("building cache (%d copies) ..." % args.copies)

@@ -25,9 +25,9 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 # enums of include/csa2.h
 OK = 0
 F32, BF16 = 0, 1
-FMT_FP4_PER_CHANNEL, FMT_FP8_PER_TOKEN, FMT_FP4_G16 = 0, 1, 2
+FMT_FP4_PER_CHANNEL, FMT_FP8_PER_TOKEN, FMT_FP4_G16, FMT_FP4_PER_TOKEN = 0, 1, 2, 3
 SCALE_COMPUTE, SCALE_GIVEN = 0, 1
-PREC_FP32, PREC_FP8 = 0, 1
+PREC_FP32, PREC_FP8, PREC_FP4 = 0, 1, 2
 FULL, REINDEX, REUSE = 0, 1, 2
 MODE_NAMES = {"full": FULL, "reindex": REINDEX, "reuse": REUSE}
 

@@ -161,7 +161,7 @@ int check_index_shape(int prec, int B, int T, int H, int dk, int q_dtype, const 
   if (prec == CSA2_PREC_FP32) {
     if (q_dtype != CSA2_F32) return CSA2_ERR_DTYPE;
     if (H < 1 || H > CSA2_MAX_H || dk < 1 || dk > CSA2_MAX_DK || (int64_t)H * dk > 8192) return CSA2_ERR_SHAPE;
-  } else if (prec == CSA2_PREC_FP8) {
+  } else if (prec == CSA2_PREC_FP8 || prec == CSA2_PREC_FP4) {
     if (H != 32 || dk != 64) return CSA2_ERR_UNSUPPORTED;
     if (!k_scale) return CSA2_ERR_NULL;
   } else {
@@ -234,6 +234,14 @@ int csa2_quantize_kv(int fmt, int scale_policy, int B, int T, int D, const void*
     if (rc) return rc;
     return dev_status(launch_quantize_fp8(bf16, B, T, D, x, x_stride_b, x_stride_t, n0, n_max, codes, scales,
                                           S(stream)));
+  }
+  if (fmt == CSA2_FMT_FP4_PER_TOKEN) {
+    if (scale_policy != CSA2_SCALE_COMPUTE) return CSA2_ERR_DTYPE;
+    if (D % 2 || D > 4096) return CSA2_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return dev_status(launch_quantize_fp4_rows(bf16, B, T, D, x, x_stride_b, x_stride_t, n0, n_max, codes, scales,
+                                               S(stream)));
   }
   if (fmt == CSA2_FMT_FP4_G16) {
     if (D % 16) return CSA2_ERR_SHAPE;

@@ -22,11 +22,14 @@ int launch_quantize_fp4(bool compute, bool bf16, int B, int T, int D, const void
 // the pages' layout: codes [B][n_max][D/2], gscales [B][n_max][D/16] E4M3 bytes (D % 16 == 0)
 int launch_quantize_fp4_g16(bool bf16, int B, int T, int D, const void* x, int64_t xsb, int64_t xst,
                             const int32_t* n0, int64_t n_max, uint8_t* codes, uint8_t* gscales, hipStream_t st);
+// E2M1 with one absmax/6 scale per row (4-bit indexer keys): codes [B][n_max][D/2]
+int launch_quantize_fp4_rows(bool bf16, int B, int T, int D, const void* x, int64_t xsb, int64_t xst,
+                             const int32_t* n0, int64_t n_max, uint8_t* codes, float* scales, hipStream_t st);
 int launch_quantize_fp8(bool bf16, int B, int T, int D, const void* x, int64_t xsb, int64_t xst, const int32_t* n0,
                         int64_t n_max, uint8_t* codes, float* scales, hipStream_t st);
 
 struct ScoreArgs {
-  int prec;           // 0 fp32, 1 fp8
+  int prec;           // 0 fp32, 1 fp8, 2 fp4
   bool q_bf16;
   int B, T, H, dk;
   const void* q;

@@ -136,6 +136,44 @@ __global__ __launch_bounds__(256) void k_fp8_rows(int T, int D, const XT* __rest
   if (lane == 0) scales[(int64_t)b * n_max + row] = s;
 }
 
+// E2M1 per row (4-bit indexer keys): one wave per row; s = absmax/6, lanes take pairs of
+// dims and write one byte each (the lower dim in the low nibble).
+template <typename XT>
+__global__ __launch_bounds__(256) void k_fp4_rows(int T, int D, const XT* __restrict__ x, int64_t xsb, int64_t xst,
+                                                  const int32_t* __restrict__ n0, int64_t n_max,
+                                                  uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (t >= T) return;
+  const int64_t row = (int64_t)(n0 ? n0[b] : 0) + t;
+  if (row < 0 || row >= n_max) return;
+  const XT* xr = x + b * xsb + t * xst;
+  float m = 0.0f;
+  for (int d = lane; d < D; d += 64) m = fmaxf(m, fabsf(load_as_f32(xr + d)));
+  m = wave_max(m);
+  const float s = m / 6.0f;
+  uint8_t* out = codes + ((int64_t)b * n_max + row) * (D / 2);
+  for (int i = lane; i < D / 2; i += 64) {
+    const uint32_t lo = s != 0.0f ? e2m1_encode(load_as_f32(xr + 2 * i) / s) : 0u;
+    const uint32_t hi = s != 0.0f ? e2m1_encode(load_as_f32(xr + 2 * i + 1) / s) : 0u;
+    out[i] = (uint8_t)(lo | hi << 4);
+  }
+  if (lane == 0) scales[(int64_t)b * n_max + row] = s;
+}
+
+int launch_quantize_fp4_rows(bool bf16, int B, int T, int D, const void* x, int64_t xsb, int64_t xst,
+                             const int32_t* n0, int64_t n_max, uint8_t* codes, float* scales, hipStream_t st) {
+  dim3 g((T + 3) / 4, B);
+  if (bf16)
+    hipLaunchKernelGGL(k_fp4_rows<uint16_t>, g, dim3(256), 0, st, T, D, (const uint16_t*)x, xsb, xst, n0, n_max,
+                       codes, scales);
+  else
+    hipLaunchKernelGGL(k_fp4_rows<float>, g, dim3(256), 0, st, T, D, (const float*)x, xsb, xst, n0, n_max, codes,
+                       scales);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st) {
   if (n <= 0) return 0;
   int64_t blocks = (n + 255) / 256;

@@ -109,13 +109,42 @@ __device__ __forceinline__ v8i quantize_query_operand(const QT* __restrict__ qro
   return a;
 }
 
+// The 4-bit variant: the head's 32 values of this lane as E2M1 (sq = absmax/6), packed
+// two per byte with the lower dim in the low nibble, in the first four operand dwords
+// (an FP4 operand of the 32x32x64 MFMA takes 16 bytes per lane).
+template <typename QT>
+__device__ __forceinline__ v8i quantize_query_operand_fp4(const QT* __restrict__ qrow, int lane, float& sq_out) {
+  const int hq = lane & 31, half = lane >> 5;
+  const QT* p = qrow + hq * 64 + half * 32;
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(load_as_f32(p + i)));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  const float sq = amax / 6.0f;
+  v8i a = {};
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const uint32_t code = (sq != 0.0f) ? e2m1_encode(load_as_f32(p + wd * 8 + nb) / sq) : 0u;
+      word |= code << (4 * nb);
+    }
+    a[wd] = (int)word;
+  }
+  sq_out = sq;
+  return a;
+}
+
 // One block streams a contiguous chunk of 4 * TPW 32-key tiles; wave w takes tiles
 // w, w+4, ... so that the block's loads sweep the chunk in order.  Order of issue matters
 // because the vector-memory counter retires loads in order: the query row and head
 // weights are loaded first (one 16-byte load per thread, staged in LDS), then kPrefetch
 // key tiles per wave, so the query quantisation overlaps the first key loads.  The tile
 // loop is fully unrolled so that every wait names exactly the tile it needs.
-template <typename QT, bool CAND, int TPW>
+// F4: the 4-bit indexer (E2M1 keys, 32 B per key plus the fp32 scale; the query quantised
+// to E2M1 per head); the same MFMA takes FP4 operands.
+template <typename QT, bool CAND, int TPW, bool F4 = false>
 __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const QT* __restrict__ q,
                                                    const float* __restrict__ w, const uint8_t* __restrict__ k8,
                                                    const float* __restrict__ ks, int64_t n_max,
@@ -144,7 +173,8 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
   const int64_t lim = visible_limit(b, r, n_max, n_keys, q_limit, key_div);
   const int64_t c0 = (int64_t)blockIdx.x * (kScoreWaves * TPW * 32);
   const int64_t c1 = (c0 + kScoreWaves * TPW * 32 < ncols) ? c0 + kScoreWaves * TPW * 32 : ncols;
-  const uint8_t* kb = k8 + (int64_t)b * n_max * 64 + half * 32;
+  constexpr int kKeyBytes = F4 ? 32 : 64;      // bytes per key row
+  const uint8_t* kb = k8 + (int64_t)b * n_max * kKeyBytes + half * (kKeyBytes / 2);
   const float* ksb = ks + (int64_t)b * n_max;
   const int32_t* crow = CAND ? cand + (int64_t)r * ncols : nullptr;
   v4i ka[P], kc[P];
@@ -157,9 +187,10 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
     vis[slot] = row >= 0 && row <= lim;
     // branch-free: invisible columns read row 0 (always valid) and are masked later
     const int64_t rr = vis[slot] ? row : 0;
-    const v4i* src = reinterpret_cast<const v4i*>(kb + rr * 64);
+    const v4i* src = reinterpret_cast<const v4i*>(kb + rr * kKeyBytes);
     ka[slot] = __builtin_nontemporal_load(src);
-    kc[slot] = __builtin_nontemporal_load(src + 1);
+    if (F4) kc[slot] = (v4i){0, 0, 0, 0};
+    else kc[slot] = __builtin_nontemporal_load(src + 1);
     skv[slot] = __builtin_nontemporal_load(ksb + rr);
   };
 #pragma unroll
@@ -172,7 +203,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
     for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0;
   __syncthreads();
   float sq;
-  const v8i A = quantize_query_operand(s_q, lane, sq);
+  const v8i A = F4 ? quantize_query_operand_fp4(s_q, lane, sq) : quantize_query_operand(s_q, lane, sq);
   if (wave == 0 && lane < 32) s_c[lane] = sq;
   __syncthreads();
   if (tid < 32) s_c[tid] = wv * s_c[tid];
@@ -194,7 +225,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
     const float skl = skv[u];
     if (i + P < TPW) issue(i + P, u);
     v16f acc = {};
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, 0, 0, 0, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, F4 ? 4 : 0, F4 ? 4 : 0, 0, 0, 0, 0);
     float part = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) part = fmaf(cvec[j], acc[j], part);
@@ -414,22 +445,31 @@ int score_cols_per_block(int64_t rows, int64_t ncols) {
   return kScoreWaves * 2 * 32;
 }
 
-template <typename QT, bool CAND, int TPW>
+template <typename QT, bool CAND, int TPW, bool F4>
 static void launch_fp8(const ScoreArgs& a, hipStream_t st) {
   const int cpb = kScoreWaves * TPW * 32;
   dim3 g((unsigned)((a.ncols + cpb - 1) / cpb), a.B * a.T);
-  hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q, a.w,
+  hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q, a.w,
                      (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,
                      a.key_div);
 }
 
-template <typename QT, bool CAND>
+template <typename QT, bool CAND, bool F4>
 static void launch_fp8_tpw(const ScoreArgs& a, hipStream_t st) {
   const int cpb = score_cols_per_block((int64_t)a.B * a.T, a.ncols);
-  if (cpb == kScoreWaves * 16 * 32) launch_fp8<QT, CAND, 16>(a, st);
-  else if (cpb == kScoreWaves * 8 * 32) launch_fp8<QT, CAND, 8>(a, st);
-  else if (cpb == kScoreWaves * 4 * 32) launch_fp8<QT, CAND, 4>(a, st);
-  else launch_fp8<QT, CAND, 2>(a, st);
+  if (cpb == kScoreWaves * 16 * 32) launch_fp8<QT, CAND, 16, F4>(a, st);
+  else if (cpb == kScoreWaves * 8 * 32) launch_fp8<QT, CAND, 8, F4>(a, st);
+  else if (cpb == kScoreWaves * 4 * 32) launch_fp8<QT, CAND, 4, F4>(a, st);
+  else launch_fp8<QT, CAND, 2, F4>(a, st);
+}
+
+template <typename QT>
+static void launch_lowbit(const ScoreArgs& a, hipStream_t st) {
+  if (a.prec == 2) {
+    if (a.cand) launch_fp8_tpw<QT, true, true>(a, st); else launch_fp8_tpw<QT, false, true>(a, st);
+  } else {
+    if (a.cand) launch_fp8_tpw<QT, true, false>(a, st); else launch_fp8_tpw<QT, false, false>(a, st);
+  }
 }
 
 int launch_score(const ScoreArgs& a, hipStream_t st) {
@@ -456,9 +496,9 @@ int launch_score(const ScoreArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(k_score_f32<false>, g, dim3(256), sh, st, a.T, a.H, a.dk, a.ncols, (const float*)a.q, a.w,
                          (const float*)a.k, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist, a.key_div);
   } else if (a.q_bf16) {
-    if (a.cand) launch_fp8_tpw<uint16_t, true>(a, st); else launch_fp8_tpw<uint16_t, false>(a, st);
+    launch_lowbit<uint16_t>(a, st);
   } else {
-    if (a.cand) launch_fp8_tpw<float, true>(a, st); else launch_fp8_tpw<float, false>(a, st);
+    launch_lowbit<float>(a, st);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

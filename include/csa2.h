@@ -56,9 +56,14 @@ typedef enum {
 } csa2_status;
 
 typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
-typedef enum { CSA2_FMT_FP4_PER_CHANNEL = 0, CSA2_FMT_FP8_PER_TOKEN = 1, CSA2_FMT_FP4_G16 = 2 } csa2_fmt;
+typedef enum {
+  CSA2_FMT_FP4_PER_CHANNEL = 0,
+  CSA2_FMT_FP8_PER_TOKEN = 1,
+  CSA2_FMT_FP4_G16 = 2,
+  CSA2_FMT_FP4_PER_TOKEN = 3
+} csa2_fmt;
 typedef enum { CSA2_SCALE_COMPUTE = 0, CSA2_SCALE_GIVEN = 1 } csa2_scale_policy;
-typedef enum { CSA2_PREC_FP32 = 0, CSA2_PREC_FP8 = 1 } csa2_index_prec;
+typedef enum { CSA2_PREC_FP32 = 0, CSA2_PREC_FP8 = 1, CSA2_PREC_FP4 = 2 } csa2_index_prec;
 typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
 
 /* Limits of this build. */
@@ -99,6 +104,10 @@ int csa2_device_check(void);
  *     E2M1(fl32(x / value(sc))) (values beyond 6 after the division saturate; sc = 0 gives
  *     code +0).  Every entry's scales come from the entry itself, so scale_policy is
  *     ignored.  D % 16 == 0.  288 B per entry at D = 512.
+ *   CSA2_FMT_FP4_PER_TOKEN (4-bit indexer keys; the pages' indexer q/k are 4-bit, "FP4 Main
+ *     KV Cache To Halve Storage Again"): codes [B][n_max][D/2] (E2M1 pairs, lower dim in the
+ *     low nibble), scales [B][n_max] fp32: s = fl32(max_c |x| / 6), code = E2M1(fl32(x / s))
+ *     (scale_policy must be COMPUTE).  D even, D <= 4096.
  */
 int csa2_quantize_kv(int fmt, int scale_policy, int B, int T, int D, const void* x, int x_dtype,
                      int64_t x_stride_b, int64_t x_stride_t, const int32_t* n0, int64_t n_max, uint8_t* codes,
@@ -126,6 +135,10 @@ int csa2_gather_dequant(int kv_fmt, int B, int T, int K, int D, const uint8_t* c
  *                   score = k_scale[b][j] * sum_h w_h * sq_h * (q8_h . k8[b][j])
  *                   (k: E4M3 codes, k_scale fp32 per row; contraction on fp8 MFMA;
  *                   requires H == 32, dk == 64).
+ *   CSA2_PREC_FP4 : the same with E2M1 on both sides: the query quantised per (b,t,h) with
+ *                   sq = max|q_h|/6, k the packed E2M1 codes [B][n_max][dk/2] of
+ *                   CSA2_FMT_FP4_PER_TOKEN with k_scale; contraction on the FP4 form of the
+ *                   same MFMA; H == 32, dk == 64.  Not with csa2_hier_select.
  *   q: [B][T][H][dk] of q_dtype; w: [B][T][H] fp32; k: [B][n_max][dk]; k_scale:
  *   [B][n_max] (FP8) or NULL (FP32).
  * Visible columns: cand == NULL -> column j is cache row j (ncols = n_max); cand != NULL

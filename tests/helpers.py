@@ -32,6 +32,24 @@ def fp8_score_bound(q, w, k8, ks, n_keys=None):
     return np.einsum("btd,bjd->btj", qs, kd) * ks.astype(np.float64)[:, None, :]
 
 
+def e2m1_unpack_f64(codes):
+    """Packed E2M1 codes [..][n/2] -> values [..][n] (lower index in the low nibble)."""
+    tab = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    c = np.stack([codes & 15, codes >> 4], axis=-1).reshape(*codes.shape[:-1], -1).astype(np.int64)
+    return np.where(c & 8, -1.0, 1.0) * tab[c & 7]
+
+
+def fp4_score_bound(q, w, k4, ks):
+    """As fp8_score_bound for the 4-bit indexer: sk_j * sum_h |w_h sq_h| sum_d |q4_hd| |k4_jd|,
+    the query quantised per (token, head) to E2M1 with absmax/6 ([B][T][n])."""
+    B, T, H, dk = q.shape
+    qc, sq = oracle.quantize_fp4_rows(np.ascontiguousarray(q, np.float32).reshape(1, B * T * H, dk))
+    q4 = np.abs(e2m1_unpack_f64(qc)).reshape(B, T, H, dk)
+    qd = q4 * (np.abs(w.astype(np.float64)) * sq.reshape(B, T, H).astype(np.float64))[..., None]
+    kd = np.abs(e2m1_unpack_f64(k4))
+    return np.einsum("btd,bjd->btj", qd.sum(axis=2), kd) * ks.astype(np.float64)[:, None, :]
+
+
 def check_topk_near_tie(gpu_idx, ref_scores, K, rel=1e-3, n_vis=None):
     """Survey rule: with tau the reference K-th score and delta = rel*|tau|, the GPU set G
     must have min(K, n_vis) members, contain every j with s_j > tau + delta and lie inside
