@@ -302,21 +302,30 @@ def layer_group(layers, cache, prec, K, softmax_scale, pool=None):
     Every mode then attends over the shared main KV with its own attention query.
     pool = (block, pool_blocks): every Full layer also leaves the pool of its best blocks
     (pool_positions) and the Reindex layers after it score only the pool's positions.
+    T query tokens per sequence (the second dim of q_attn; T > 1 for draft verification, as
+    DSpark's five parallel drafts need in "Detailed Notes", DSpark section): their own
+    entries are the cache's last T, so token t sees positions < n_keys - (T - 1 - t).
     Returns a list of dicts {idx, out, lse} (plus 'pool' for Full layers with a pool)."""
     modes = [L["mode"] for L in layers]
     if not check_schedule(modes):
         raise ValueError("invalid mode schedule %r" % (modes,))
+    nk = _c(cache["n_keys"], np.int32)
+    T = np.asarray(layers[0]["q_attn"]).shape[1]
+    q_limit = None
+    if T > 1:
+        q_limit = (nk[:, None] - T + np.arange(T, dtype=np.int32)[None, :]).astype(np.int32)
     results, last_idx, cand = [], None, None
     for L in layers:
         res = {}
         if L["mode"] == FULL or (L["mode"] == REINDEX and cand is None):
-            s = index_score(prec, L["q_idx"], L["w"], cache["k"], cache["k_scale"], cache["n_keys"])
+            s = index_score(prec, L["q_idx"], L["w"], cache["k"], cache["k_scale"], nk, q_limit=q_limit)
             last_idx = topk(s, K)
             if L["mode"] == FULL and pool is not None:
-                cand = pool_positions(s, pool[0], pool[1], cache["n_keys"])
+                # a row's pool holds only positions it can see
+                cand = pool_positions(s, pool[0], pool[1], nk if q_limit is None else q_limit + 1)
                 res["pool"] = cand
         elif L["mode"] == REINDEX:
-            s = index_score(prec, L["q_idx"], L["w"], cache["k"], cache["k_scale"], cache["n_keys"], cand=cand)
+            s = index_score(prec, L["q_idx"], L["w"], cache["k"], cache["k_scale"], nk, q_limit=q_limit, cand=cand)
             last_idx = topk(s, K, cand=cand)
         out, lse = sparse_attend(L["q_attn"], cache["codes"], cache["scales"], last_idx, softmax_scale,
                                  swa=L.get("swa"))
@@ -338,17 +347,20 @@ def coarse_keys(k8, k_scale, n_keys, block):
 
 def expand_blocks(block_idx, block, n_keys):
     """Candidate positions of the selected blocks: block ascending, then position
-    ascending; positions at or past n_keys and padded blocks become -1."""
+    ascending; positions at or past n_keys ([B], or [B][T] per query row) and padded
+    blocks become -1."""
     B, T, KB = block_idx.shape
     cand = np.full((B, T, KB * block), -1, np.int32)
     off = np.arange(block, dtype=np.int64)
+    nk = np.asarray(n_keys)
     for b in range(B):
         for t in range(T):
+            lim = nk[b, t] if nk.ndim == 2 else nk[b]
             for i, blk in enumerate(block_idx[b, t]):
                 if blk < 0:
                     continue
                 pos = blk * block + off
-                pos[pos >= n_keys[b]] = -1
+                pos[pos >= lim] = -1
                 cand[b, t, i * block:(i + 1) * block] = pos
     return cand
 
