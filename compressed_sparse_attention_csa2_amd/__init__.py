@@ -63,7 +63,8 @@ class _GroupCache(ctypes.Structure):
                 ("kv_codes", ctypes.c_void_p), ("kv_scales", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("prec", ctypes.c_int), ("q_dtype", ctypes.c_int),
                 ("out_dtype", ctypes.c_int), ("softmax_scale", ctypes.c_float), ("pool_block", ctypes.c_int),
-                ("pool_blocks", ctypes.c_int), ("kv_fmt", ctypes.c_int), ("window", ctypes.c_int)]
+                ("pool_blocks", ctypes.c_int), ("kv_fmt", ctypes.c_int), ("window", ctypes.c_int),
+                ("T", ctypes.c_int)]
 
 
 _lib = None
@@ -279,12 +280,12 @@ class GroupCache:
         self.K, self.softmax_scale, self.prec = K, softmax_scale, prec
         self.pool = pool
 
-    def struct(self, H, dk, Hq, q_dtype, out_dtype, window=0):
+    def struct(self, H, dk, Hq, q_dtype, out_dtype, window=0, T=1):
         B, n_max, Dh = self.kv_codes.shape
         pb, pn = self.pool if self.pool else (0, 0)
         return _GroupCache(B, H, dk, Hq, 2 * Dh, self.K, n_max, _ptr(self.n_keys), _ptr(self.kv_codes),
                            _ptr(self.kv_scales), _ptr(self.k), _ptr(self.k_scale), self.prec, q_dtype, out_dtype,
-                           float(self.softmax_scale), pb, pn, kv_format(self.kv_scales), window)
+                           float(self.softmax_scale), pb, pn, kv_format(self.kv_scales), window, T)
 
 
 class GroupPlan:
@@ -303,8 +304,10 @@ class GroupPlan:
 def layer_group(layers: Sequence[dict], cache: GroupCache, out_dtype: Optional[torch.dtype] = None):
     """Run Full/Reindex/Reuse layers in order over one shared cache.
 
-    layers: dicts with mode ('full'|'reindex'|'reuse'), q_idx [B][1][H][dk], w [B][1][H],
-    q_attn [B][1][Hq][D] and optionally out, lse, idx tensors, 'swa' (the layer's own
+    layers: dicts with mode ('full'|'reindex'|'reuse'), q_idx [B][T][H][dk], w [B][T][H],
+    q_attn [B][T][Hq][D] (T query tokens per sequence, 1 for plain decode; with T > 1 their
+    own entries are the cache's last T and token t sees positions < n_keys - (T - 1 - t))
+    and optionally out, lse, idx tensors, 'swa' (the layer's own
     sliding-window cache, a Swa), and for Full layers of a cache with a pool a 'pool' int32
     tensor [B][blocks*block] that receives the pool's positions.  Returns the layer dicts with 'out', 'lse' and (Full/Reindex) 'idx' filled."""
     return GroupPlan(layers, cache, out_dtype).run()
@@ -313,7 +316,7 @@ def layer_group(layers: Sequence[dict], cache: GroupCache, out_dtype: Optional[t
 def _marshal_group(layers, cache, out_dtype):
     first = layers[0]
     q_attn = first["q_attn"]
-    B, _, Hq, D = q_attn.shape
+    B, T, Hq, D = q_attn.shape
     H, dk = (first["q_idx"].shape[2], first["q_idx"].shape[3]) if first.get("q_idx") is not None else (32, 64)
     odt = out_dtype or q_attn.dtype
     arr = (_Layer * len(layers))()
@@ -321,24 +324,26 @@ def _marshal_group(layers, cache, out_dtype):
     window = max([sw.window for sw in swas if sw is not None], default=0)
     for i, L in enumerate(layers):
         mode = MODE_NAMES[L["mode"]] if isinstance(L["mode"], str) else int(L["mode"])
+        if tuple(L["q_attn"].shape[:2]) != (B, T):
+            raise ValueError("every layer's q_attn must be [B][T][Hq][D] with the same B and T")
         if L.get("out") is None:
-            L["out"] = torch.empty((B, 1, Hq, D), dtype=odt, device=q_attn.device)
+            L["out"] = torch.empty((B, T, Hq, D), dtype=odt, device=q_attn.device)
         if L.get("lse") is None:
-            L["lse"] = torch.empty((B, 1, Hq), dtype=torch.float32, device=q_attn.device)
+            L["lse"] = torch.empty((B, T, Hq), dtype=torch.float32, device=q_attn.device)
         if mode != REUSE and L.get("idx") is None:
-            L["idx"] = torch.empty((B, 1, cache.K), dtype=torch.int32, device=q_attn.device)
+            L["idx"] = torch.empty((B, T, cache.K), dtype=torch.int32, device=q_attn.device)
         p = L.get("pool")
         if p is not None and mode == FULL:
             if not cache.pool:
                 raise ValueError("a pool output was given but the cache has no pool")
-            if p.dtype != torch.int32 or not p.is_contiguous() or p.numel() != B * cache.pool[0] * cache.pool[1]:
-                raise ValueError("pool must be a contiguous int32 tensor of B * block * blocks elements")
+            if p.dtype != torch.int32 or not p.is_contiguous() or p.numel() != B * T * cache.pool[0] * cache.pool[1]:
+                raise ValueError("pool must be a contiguous int32 tensor of B * T * block * blocks elements")
         arr[i] = _Layer(mode, _ptr(L.get("q_idx")), _ptr(L.get("w")), _ptr(L["q_attn"]), _ptr(L["out"]),
                         _ptr(L["lse"]), _ptr(L.get("idx")) if mode != REUSE else None,
                         _ptr(L.get("pool")) if mode == FULL else None,
                         ctypes.pointer(swas[i]) if swas[i] is not None else None)
     qd = _dtype_code(q_attn)
-    gc = cache.struct(H, dk, Hq, qd, _dtype_code(torch.empty(0, dtype=odt)), window)
+    gc = cache.struct(H, dk, Hq, qd, _dtype_code(torch.empty(0, dtype=odt)), window, T)
     nb = lib().csa2_layer_group_workspace_size(ctypes.byref(gc), len(layers))
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=q_attn.device)
     return arr, gc, ws, nb, swas

@@ -397,6 +397,9 @@ static int64_t pool_cols(const csa2_group_cache* c) { return pool_on(c) ? (int64
 static int64_t pool_nb(const csa2_group_cache* c) {
   return pool_on(c) ? (c->n_max + c->pool_block - 1) / c->pool_block : 0;
 }
+// query tokens per sequence (multi-token decode)
+static int group_T(const csa2_group_cache* c) { return c->T > 1 ? c->T : 1; }
+
 // columns the scores and candidate regions are sized for (the full scan or the pool)
 static int64_t group_cols(const csa2_group_cache* c) {
   const int64_t pc = pool_cols(c);
@@ -407,14 +410,15 @@ static int64_t group_cols(const csa2_group_cache* c) {
 //            [candidates] [attention partials] [pool positions, block maxima]
 size_t csa2_layer_group_workspace_size(const csa2_group_cache* c, int n_layers) {
   if (!c || n_layers < 1) return 0;
-  const int64_t R = c->B;
+  const int64_t R = (int64_t)c->B * group_T(c);
   const int sel = pool_on(c) ? 2 * n_layers : n_layers;  // a pooled Full layer makes two selections
   const int slots = sel < 64 ? sel : 64;
   const size_t att =
       (c->q_dtype == CSA2_BF16) ? align256(attend_ws_floats((int)R, c->Hq, c->D, c->K, c->window) * 4) : 0;
   const size_t pool = pool_on(c) ? align256((size_t)R * pool_cols(c) * 4) + align256((size_t)R * pool_nb(c) * 4) : 0;
+  const size_t lim = group_T(c) > 1 ? align256((size_t)R * 4) : 0;
   return topk_zero_bytes(R) * (size_t)slots + align256((size_t)R * group_cols(c) * 4) + cand_bytes(R, group_cols(c)) +
-         att + pool;
+         att + pool + lim;
 }
 
 int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_cache* c, void* ws, size_t ws_bytes,
@@ -427,12 +431,14 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   if (c->n_max < 1 || c->n_max > kMaxTopkCols || c->K < 1 || c->K > CSA2_MAX_K) return CSA2_ERR_SHAPE;
   if (c->pool_blocks < 0 || c->pool_blocks > CSA2_MAX_K || (pool_on(c) && c->pool_block < 1)) return CSA2_ERR_SHAPE;
   if (c->window < 0 || c->window > CSA2_MAX_WINDOW) return CSA2_ERR_SHAPE;
+  if (c->T < 0 || c->T > CSA2_MAX_GROUP_T) return CSA2_ERR_SHAPE;
   if (pool_cols(c) > kMaxTopkCols || c->n_max > INT32_MAX) return CSA2_ERR_SHAPE;
-  rc = check_index_shape(c->prec, c->B, 1, c->H, c->dk, c->q_dtype, c->k_scale, c->n_max);
+  const int T = group_T(c);
+  rc = check_index_shape(c->prec, c->B, T, c->H, c->dk, c->q_dtype, c->k_scale, c->n_max);
   if (rc) return rc;
   rc = check_kv_fmt(c->kv_fmt, c->D);
   if (rc) return rc;
-  rc = check_attend_shape(c->B, 1, c->Hq, c->D, c->K, c->q_dtype, c->out_dtype);
+  rc = check_attend_shape(c->B, T, c->Hq, c->D, c->K, c->q_dtype, c->out_dtype);
   if (rc) return rc;
   for (int i = 0; i < n_layers; ++i) {
     const csa2_layer& L = layers[i];
@@ -445,7 +451,7 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   rc = check_device();
   if (rc) return rc;
 
-  const int64_t R = c->B;
+  const int64_t R = (int64_t)c->B * T;
   const bool pooled = pool_on(c);
   int n_sel = count_index_layers(layers, n_layers);
   if (pooled)
@@ -462,7 +468,9 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   const int64_t pc = pool_cols(c), nb = pool_nb(c);
   int32_t* pool = pooled ? cv.take<int32_t>((size_t)R * pc) : nullptr;
   float* bmax = pooled ? cv.take<float>((size_t)R * nb) : nullptr;
+  int32_t* q_limit = T > 1 ? cv.take<int32_t>((size_t)R) : nullptr;
   hipStream_t st = S(stream);
+  if (q_limit && launch_causal_limits(c->B, T, c->n_keys, q_limit, st)) return CSA2_ERR_DEVICE;
   // one fill clears every selection's histograms and control words (more than 64 selections
   // reuse the last slot, cleared again before each reuse)
   if (slots > 0 && launch_fill_u32(tz[0].hist, (int64_t)(zero_bytes / 4), 0u, st)) return CSA2_ERR_DEVICE;
@@ -475,7 +483,7 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   };
   const int32_t* cur_pool = nullptr;  // the pool of the most recent Full layer
 
-  AttendArgs a = attend_args(c->B, 1, c->Hq, c->D, c->K, nullptr, c->q_dtype, c->kv_fmt, c->kv_codes, c->kv_scales,
+  AttendArgs a = attend_args(c->B, T, c->Hq, c->D, c->K, nullptr, c->q_dtype, c->kv_fmt, c->kv_codes, c->kv_scales,
                              c->n_max,
                              nullptr, c->softmax_scale, nullptr, c->out_dtype, nullptr);
   a.part = part;
@@ -495,8 +503,8 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
       const bool use_pool = (L.mode == CSA2_REINDEX) && cur_pool;
       const int64_t ncols = use_pool ? pc : c->n_max;
       const int32_t* cand = use_pool ? cur_pool : nullptr;
-      ScoreArgs sa = score_args(c->prec, c->B, 1, c->H, c->dk, L.q_idx, c->q_dtype, L.w, c->k, c->k_scale, c->n_max,
-                                c->n_keys, nullptr, cand, ncols, scores, t.hist, 1);
+      ScoreArgs sa = score_args(c->prec, c->B, T, c->H, c->dk, L.q_idx, c->q_dtype, L.w, c->k, c->k_scale, c->n_max,
+                                c->n_keys, q_limit, cand, ncols, scores, t.hist, 1);
       if (launch_score(sa, st)) return CSA2_ERR_DEVICE;
       if (launch_topk_filter((int)R, ncols, scores, cand, c->K, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st))
         return CSA2_ERR_DEVICE;
@@ -522,7 +530,7 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
       if (launch_topk_filter((int)R, nb, bmax, nullptr, c->pool_blocks, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st))
         return CSA2_ERR_DEVICE;
       if (launch_topk_finalize((int)R, nb, c->pool_blocks, true, t.ctl, t.hist2, cw.cand, cw.cnt, nullptr, nullptr, st,
-                               c->pool_block, c->n_keys, dst))
+                               c->pool_block, c->n_keys, dst, T))
         return CSA2_ERR_DEVICE;
       cur_pool = dst;
     }

@@ -70,7 +70,8 @@ int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t*
 // positions per selected column, -1 past n_keys[r] or for padding), [R][K * block]
 int launch_topk_finalize(int R, int64_t ncols, int K, bool sorted, const RowCtl* ctl, const uint32_t* hist2,
                          const uint2* candbuf, const uint32_t* cnt, int32_t* idx_out, float* val_out, hipStream_t st,
-                         int block = 0, const int32_t* n_keys = nullptr, int32_t* expand_out = nullptr);
+                         int block = 0, const int32_t* n_keys = nullptr, int32_t* expand_out = nullptr,
+                         int rps = 1);
 
 struct AttendArgs {
   int B, T, Hq, D, K;
@@ -106,6 +107,9 @@ size_t attend_ws_floats(int R, int Hq, int D, int K, int window);
 
 int launch_gather_dequant(bool g16, int B, int T, int K, int D, const uint8_t* codes, const void* scales,
                           int64_t n_max, const int32_t* idx, float* out, hipStream_t st);
+// q_limit[b * T + t] = n_keys[b] - T + t: the causal limit of T decode tokens whose own
+// entries are the cache's last T
+int launch_causal_limits(int B, int T, const int32_t* n_keys, int32_t* q_limit, hipStream_t st);
 int launch_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int block, const uint8_t* k8,
                        const float* k_scale, uint8_t* kb8, float* kb_scale, hipStream_t st);
 }  // namespace csa2

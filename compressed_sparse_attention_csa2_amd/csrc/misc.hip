@@ -99,6 +99,17 @@ int launch_gather_dequant(bool g16, int B, int T, int K, int D, const uint8_t* c
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+__global__ void k_causal_limits(int R, int T, const int32_t* __restrict__ n_keys, int32_t* __restrict__ q_limit) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < R) q_limit[r] = n_keys[r / T] - T + r % T;
+}
+
+int launch_causal_limits(int B, int T, const int32_t* n_keys, int32_t* q_limit, hipStream_t st) {
+  const int R = B * T;
+  hipLaunchKernelGGL(k_causal_limits, dim3((R + 255) / 256), dim3(256), 0, st, R, T, n_keys, q_limit);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int block, const uint8_t* k8,
                        const float* k_scale, uint8_t* kb8, float* kb_scale, hipStream_t st) {
   const int64_t nb = (n_max + block - 1) / block;

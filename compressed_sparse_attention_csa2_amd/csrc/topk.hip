@@ -210,7 +210,8 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
 // EXPAND (two-level select, candidate pool): the selected columns are blocks of `block`
 // positions; the kernel also writes the blocks' positions in order, -1 past a sequence's
 // n_keys or for padding (the candidate list of the fine stage).  idx_out and val_out may be
-// null.
+// null.  With rps > 1 query rows per sequence, row t of a sequence stops at n_keys - (rps -
+// 1 - t).
 template <bool SORTED, bool EXPAND>
 __global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, const RowCtl* __restrict__ ctl,
                                                                const uint32_t* __restrict__ hist2,
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, 
                                                                int32_t* __restrict__ idx_out,
                                                                float* __restrict__ val_out, int block,
                                                                const int32_t* __restrict__ n_keys,
-                                                               int32_t* __restrict__ expand_out) {
+                                                               int32_t* __restrict__ expand_out, int rps) {
   __shared__ FinalizeSmem sm;
   __shared__ int32_t s_pos[CSA2_MAX_K_DEV];
   __shared__ uint32_t s_key[CSA2_MAX_K_DEV];
@@ -234,7 +235,9 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, 
     if (val_out) val_out[(int64_t)r * K + i] = have ? key_to_float(s_key[i]) : kNegInf;
   }
   if (EXPAND) {
-    const int64_t nk = n_keys[r];
+    // rows_per_seq (rps) query rows share a sequence; row t of it sees its first
+    // n_keys - (rps - 1 - t) positions (multi-token decode)
+    const int64_t nk = (int64_t)n_keys[r / rps] - (rps - 1 - r % rps);
     for (int64_t i = threadIdx.x; i < (int64_t)K * block; i += kFinThreads) {
       const int e = (int)(i / block);
       const int64_t pos = (e < keff) ? (int64_t)s_pos[e] * block + i % block : -1;
@@ -311,11 +314,11 @@ int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t*
 
 int launch_topk_finalize(int R, int64_t ncols, int K, bool sorted, const RowCtl* ctl, const uint32_t* hist2,
                          const uint2* candbuf, const uint32_t* cnt, int32_t* idx_out, float* val_out, hipStream_t st,
-                         int block, const int32_t* n_keys, int32_t* expand_out) {
+                         int block, const int32_t* n_keys, int32_t* expand_out, int rps) {
   const int nreg = topk_regions(ncols);
 #define CSA2_FIN(S, E)                                                                                          \
   hipLaunchKernelGGL((k_topk_finalize<S, E>), dim3(R), dim3(kFinThreads), 0, st, nreg, K, ctl, hist2, candbuf, cnt, \
-                     idx_out, val_out, block, n_keys, expand_out)
+                     idx_out, val_out, block, n_keys, expand_out, rps)
   if (expand_out) {
     if (!sorted) return -1;  // block selections come from a list without a candidate map
     CSA2_FIN(true, true);

@@ -73,6 +73,7 @@ typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
 #define CSA2_MAX_DK 256      /* indexer dim (fp32 indexer); the fp8 indexer needs dk == 64 */
 #define CSA2_MAX_H 64        /* indexer heads (fp32 indexer); the fp8 indexer needs H == 32 */
 #define CSA2_MAX_WINDOW 128  /* sliding-window entries per query */
+#define CSA2_MAX_GROUP_T 16  /* query tokens per sequence in a layer group */
 
 /* Human-readable name of a csa2_status (static string). */
 const char* csa2_status_string(int status);
@@ -236,17 +237,18 @@ size_t csa2_sparse_attend_workspace_size(int B, int T, int Hq, int D, int K, int
  *   REUSE   - borrows main KV and the most recent indexing layer's Top-K unchanged.
  *   Every layer attends with its own attention query.
  * Schedule rule: layer 0 is FULL; REINDEX needs an earlier FULL; REUSE needs an earlier
- * FULL or REINDEX; otherwise CSA2_ERR_MODE.  Per-layer pointers: q_idx [B][1][H][dk]
- * (q_dtype), w [B][1][H], q_attn [B][1][Hq][D] (q_dtype), out [B][1][Hq][D] (out_dtype),
- * lse [B][1][Hq] (nullable), idx [B][1][K] written by FULL/REINDEX, ignored by REUSE
- * (may be NULL there), swa (nullable): the layer's own sliding-window cache (never shared;
- * its window must not exceed csa2_group_cache.window).  Decode only (one query token per
- * sequence).
+ * FULL or REINDEX; otherwise CSA2_ERR_MODE.  Per-layer pointers (T = the group cache's
+ * query tokens per sequence, 1 for plain decode): q_idx [B][T][H][dk] (q_dtype), w
+ * [B][T][H], q_attn [B][T][Hq][D] (q_dtype), out [B][T][Hq][D] (out_dtype), lse [B][T][Hq]
+ * (nullable), idx [B][T][K] written by FULL/REINDEX, ignored by REUSE (may be NULL there),
+ * swa (nullable): the layer's own sliding-window cache (never shared; its window must not
+ * exceed csa2_group_cache.window; its end is per query row).
  * With a candidate pool (csa2_group_cache.pool_blocks > 0), a REINDEX layer after a FULL
- * layer scores only the pool that the most recent FULL layer left; pool [B][pool_blocks *
- * pool_block] (nullable, FULL only) receives that pool's positions: selected blocks
- * ascending, positions ascending inside a block, -1 at or past n_keys and for blocks
- * missing when fewer than pool_blocks blocks hold a visible position.
+ * layer scores only the pool that the most recent FULL layer left; pool [B][T][pool_blocks
+ * * pool_block] (nullable, FULL only) receives that pool's positions: selected blocks
+ * ascending, positions ascending inside a block, -1 at or past the row's visible end
+ * (n_keys, less T - 1 - t for row t) and for blocks missing when fewer than pool_blocks
+ * blocks hold a visible position.
  */
 typedef struct {
   int mode;              /* csa2_mode */
@@ -280,6 +282,11 @@ typedef struct {
   int pool_blocks;
   int kv_fmt;              /* CSA2_FMT_FP4_PER_CHANNEL (0) or CSA2_FMT_FP4_G16 */
   int window;              /* largest sliding window of the layers (0: no layer has one) */
+  /* Query tokens per sequence, 0 or 1 = plain decode.  T > 1 (draft verification: DSpark
+   * proposes several tokens at once, "Detailed Notes", DSpark section): the T tokens' own
+   * entries are the cache's last T, token t sees positions < n_keys[b] - (T - 1 - t), and
+   * every per-layer tensor has T rows per sequence ([B][T][...]).  T <= CSA2_MAX_GROUP_T. */
+  int T;
 } csa2_group_cache;
 
 int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_cache* cache, void* ws,
