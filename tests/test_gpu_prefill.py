@@ -106,3 +106,41 @@ def test_many_row_scores_equal_single_row_scores():
         one = csa2.index_score(csa2.PREC_FP8, qd[:, t:t + 1].contiguous(), wd[:, t:t + 1].contiguous(), c["k8"],
                                c["ks"], nk, q_limit=ql[:, t:t + 1].contiguous())
         assert torch.equal(one[:, 0], many[:, t]), t
+
+
+def test_prefill_with_compressed_entries_m2():
+    """Encoder-style compression m = 2 ("CSA2 In Simple Terms": two tokens share one stored
+    entry in the encoder): entry j covers tokens 2j and 2j + 1, so the new token at position
+    p sees the entries whose tokens are all at or before p, j <= (p + 1) / 2 - 1.  4096
+    cached entries (8192 tokens), 64 new tokens forming 32 new entries."""
+    wl = workloads.workload("prefill", N=4096, T=64)
+    Nc, T, dk = wl.N, wl.T, wl.dk
+    n_new = T // 2
+    n_max = Nc + n_new
+    kf = wl.index_keys(0, rows=n_max)[None]                      # cached and new entries' keys
+    x = wl.main_kv(0, rows=n_max)[None]
+    k8r, ksr = oracle.quantize_fp8(kf)
+    cr, sr = oracle.quantize_fp4(x)
+    k8 = torch.empty((1, n_max, dk), dtype=torch.uint8, device=DEV)
+    ks = torch.empty((1, n_max), dtype=torch.float32, device=DEV)
+    codes = torch.empty((1, n_max, wl.D // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((1, wl.D), dtype=torch.float32, device=DEV)
+    csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(kf), k8, ks)
+    csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, to_dev(x), codes, scales)
+    pos = 2 * Nc + np.arange(T)                                  # token positions of the new rows
+    q_limit = ((pos + 1) // 2 - 1).astype(np.int32)[None]
+    nk = np.array([n_max], np.int32)
+    q, w, qa = wl.index_query(), wl.head_weights(), wl.attn_query()
+    ref = oracle.index_score(oracle.PREC_FP8, q, w, k8r, ksr, nk, q_limit=q_limit)
+    idx = csa2.index_topk(csa2.PREC_FP8, to_dev(q, torch.bfloat16), to_dev(w), k8, ks, to_dev(nk), wl.K,
+                          q_limit=to_dev(q_limit))
+    g = idx.cpu().numpy()
+    check_topk_near_tie(g, ref, wl.K)
+    assert np.all(g <= q_limit[..., None])
+    for t in range(T):                                           # entry j's tokens 2j, 2j+1 all <= p
+        sel = g[0, t][g[0, t] >= 0]
+        assert np.all(2 * sel + 1 <= pos[t])
+    out, _ = csa2.sparse_attend(to_dev(qa, torch.bfloat16), codes, scales, idx, wl.softmax_scale,
+                                out_dtype=torch.float32)
+    ro, _ = oracle.sparse_attend(qa, cr, sr, g, wl.softmax_scale)
+    assert max_abs_rel(out.cpu().numpy(), ro) <= 2e-3
