@@ -45,6 +45,7 @@ struct ScoreArgs {
   uint32_t* hist;     // nullable: [R][kHistBins], must be zero on entry
   int key_div;        // 1, or the coarse block size when columns are blocks
   uint8_t* qstage;    // nullable: score_stage_bytes(R) of scratch for the many-row fp8 path
+  bool keep;          // decode scan whose keys a later layer reads again: cached loads
 };
 int launch_score(const ScoreArgs& a, hipStream_t st);
 // Many-row fp8 scoring (chunked prefill) stages the quantised query rows: E4M3 codes and

@@ -17,6 +17,12 @@ __global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
     p[i] = v;
 }
 
+// 16-byte stores (p 16-byte aligned, n a multiple of 4)
+__global__ void k_fill_u32x4(uint4* p, int64_t n4, uint32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(v, v, v, v);
+}
+
 // absmax over rows of each channel: grid (ceil(D/256), row chunks, B)
 template <typename XT>
 __global__ __launch_bounds__(256) void k_fp4_absmax(int T, int D, const XT* __restrict__ x, int64_t xsb, int64_t xst,
@@ -176,6 +182,12 @@ int launch_quantize_fp4_rows(bool bf16, int B, int T, int D, const void* x, int6
 
 int launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st) {
   if (n <= 0) return 0;
+  if ((reinterpret_cast<uintptr_t>(p) & 15) == 0 && n % 4 == 0) {
+    int64_t blocks = (n / 4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_fill_u32x4, dim3((unsigned)blocks), dim3(256), 0, st, reinterpret_cast<uint4*>(p), n / 4, v);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);

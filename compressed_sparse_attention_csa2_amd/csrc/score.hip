@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
                                                    const int32_t* __restrict__ n_keys,
                                                    const int32_t* __restrict__ q_limit,
                                                    const int32_t* __restrict__ cand, float* __restrict__ scores,
-                                                   uint32_t* __restrict__ hist, int key_div) {
+                                                   uint32_t* __restrict__ hist, int key_div, int keep) {
   constexpr int P = (kPrefetch < TPW) ? kPrefetch : TPW;
   constexpr int kQBytes = 32 * 64 * (int)sizeof(QT);           // 4 KB (bf16) or 8 KB (fp32)
   constexpr int kQLoads = kQBytes / (16 * 256);                 // 16-byte loads per thread
@@ -188,10 +188,16 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
     // branch-free: invisible columns read row 0 (always valid) and are masked later
     const int64_t rr = vis[slot] ? row : 0;
     const v4i* src = reinterpret_cast<const v4i*>(kb + rr * kKeyBytes);
-    ka[slot] = __builtin_nontemporal_load(src);
-    if (F4) kc[slot] = (v4i){0, 0, 0, 0};
-    else kc[slot] = __builtin_nontemporal_load(src + 1);
-    skv[slot] = __builtin_nontemporal_load(ksb + rr);
+    if (keep) {  // a later layer rescans these keys: ordinary loads, which leave them in the MALL
+      ka[slot] = *src;
+      kc[slot] = F4 ? (v4i){0, 0, 0, 0} : *(src + 1);
+      skv[slot] = ksb[rr];
+    } else {
+      ka[slot] = __builtin_nontemporal_load(src);
+      if (F4) kc[slot] = (v4i){0, 0, 0, 0};
+      else kc[slot] = __builtin_nontemporal_load(src + 1);
+      skv[slot] = __builtin_nontemporal_load(ksb + rr);
+    }
   };
 #pragma unroll
   for (int i = 0; i < P; ++i) issue(i, i);
@@ -451,7 +457,7 @@ static void launch_fp8(const ScoreArgs& a, hipStream_t st) {
   dim3 g((unsigned)((a.ncols + cpb - 1) / cpb), a.B * a.T);
   hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q, a.w,
                      (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,
-                     a.key_div);
+                     a.key_div, (int)a.keep);
 }
 
 template <typename QT, bool CAND, bool F4>
