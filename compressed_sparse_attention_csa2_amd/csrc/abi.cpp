@@ -515,10 +515,11 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
       const int32_t* cand = use_pool ? cur_pool : nullptr;
       ScoreArgs sa = score_args(c->prec, c->B, T, c->H, c->dk, L.q_idx, c->q_dtype, L.w, c->k, c->k_scale, c->n_max,
                                 c->n_keys, q_limit, cand, ncols, scores, t.hist, 1);
-      // a Full layer whose keys a later Reindex layer of this call reads again scans them
-      // with cached loads, so that the rescan finds them in the Infinity Cache (measured:
-      // the rescan 23.6 us instead of 29 us at 16 x 131072)
-      sa.keep = (L.mode == CSA2_FULL) && reindex_after(layers, n_layers, i);
+      // a Full layer whose keys a later Reindex layer of this call rescans in full reads
+      // them with cached loads, so that the rescan finds them in the Infinity Cache
+      // (measured: the rescan 23.6 us instead of 29 us at 16 x 131072).  With a pool the
+      // Reindex layers read only the pool's positions and the cached scan measured slower.
+      sa.keep = (L.mode == CSA2_FULL) && !pooled && reindex_after(layers, n_layers, i);
       if (launch_score(sa, st)) return CSA2_ERR_DEVICE;
       if (launch_topk_filter((int)R, ncols, scores, cand, c->K, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st))
         return CSA2_ERR_DEVICE;

@@ -144,14 +144,14 @@ __device__ __forceinline__ v8i quantize_query_operand_fp4(const QT* __restrict__
 // loop is fully unrolled so that every wait names exactly the tile it needs.
 // F4: the 4-bit indexer (E2M1 keys, 32 B per key plus the fp32 scale; the query quantised
 // to E2M1 per head); the same MFMA takes FP4 operands.
-template <typename QT, bool CAND, int TPW, bool F4 = false>
+template <typename QT, bool CAND, int TPW, bool F4 = false, bool KEEP = false>
 __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const QT* __restrict__ q,
                                                    const float* __restrict__ w, const uint8_t* __restrict__ k8,
                                                    const float* __restrict__ ks, int64_t n_max,
                                                    const int32_t* __restrict__ n_keys,
                                                    const int32_t* __restrict__ q_limit,
                                                    const int32_t* __restrict__ cand, float* __restrict__ scores,
-                                                   uint32_t* __restrict__ hist, int key_div, int keep) {
+                                                   uint32_t* __restrict__ hist, int key_div) {
   constexpr int P = (kPrefetch < TPW) ? kPrefetch : TPW;
   constexpr int kQBytes = 32 * 64 * (int)sizeof(QT);           // 4 KB (bf16) or 8 KB (fp32)
   constexpr int kQLoads = kQBytes / (16 * 256);                 // 16-byte loads per thread
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
     // branch-free: invisible columns read row 0 (always valid) and are masked later
     const int64_t rr = vis[slot] ? row : 0;
     const v4i* src = reinterpret_cast<const v4i*>(kb + rr * kKeyBytes);
-    if (keep) {  // a later layer rescans these keys: ordinary loads, which leave them in the MALL
+    if (KEEP) {  // a later layer rescans these keys: ordinary loads, which leave them in the MALL
       ka[slot] = *src;
       kc[slot] = F4 ? (v4i){0, 0, 0, 0} : *(src + 1);
       skv[slot] = ksb[rr];
@@ -455,9 +455,14 @@ template <typename QT, bool CAND, int TPW, bool F4>
 static void launch_fp8(const ScoreArgs& a, hipStream_t st) {
   const int cpb = kScoreWaves * TPW * 32;
   dim3 g((unsigned)((a.ncols + cpb - 1) / cpb), a.B * a.T);
-  hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q, a.w,
-                     (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,
-                     a.key_div, (int)a.keep);
+  if (!CAND && a.keep)
+    hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4, true>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q,
+                       a.w, (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,
+                       a.key_div);
+  else
+    hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q, a.w,
+                       (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,
+                       a.key_div);
 }
 
 template <typename QT, bool CAND, bool F4>

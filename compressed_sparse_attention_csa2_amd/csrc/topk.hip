@@ -236,34 +236,62 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, 
   }
   if (EXPAND) {
     // rows_per_seq (rps) query rows share a sequence; row t of it sees its first
-    // n_keys - (rps - 1 - t) positions (multi-token decode)
+    // n_keys - (rps - 1 - t) positions (multi-token decode).  K * block fits in int32 (the
+    // expansion is bounded by the Top-K column limit); four positions per store when the
+    // block size allows.
     const int64_t nk = (int64_t)n_keys[r / rps] - (rps - 1 - r % rps);
-    for (int64_t i = threadIdx.x; i < (int64_t)K * block; i += kFinThreads) {
-      const int e = (int)(i / block);
-      const int64_t pos = (e < keff) ? (int64_t)s_pos[e] * block + i % block : -1;
-      expand_out[(int64_t)r * K * block + i] = (pos >= 0 && pos < nk) ? (int32_t)pos : -1;
+    const int total = K * block;
+    int32_t* dst = expand_out + (int64_t)r * total;
+    auto pos_of = [&](int i) -> int32_t {
+      const int e = i / block;
+      const int64_t pos = (e < keff) ? (int64_t)s_pos[e] * block + (i - e * block) : -1;
+      return (pos >= 0 && pos < nk) ? (int32_t)pos : -1;
+    };
+    if (block % 4 == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      for (int i = 4 * threadIdx.x; i < total; i += 4 * kFinThreads)
+        *reinterpret_cast<int4*>(dst + i) = make_int4(pos_of(i), pos_of(i + 1), pos_of(i + 2), pos_of(i + 3));
+    } else {
+      for (int i = threadIdx.x; i < total; i += kFinThreads) dst[i] = pos_of(i);
     }
   }
 }
 
 // Candidate pool of a Full layer: the largest score of every block of `block` consecutive
 // positions (-inf where none is visible), plus the first-level histogram of those maxima
-// for the pool's Top-K.  One thread per block of positions, 256 blocks per workgroup.
+// for the pool's Top-K.  kBmPer blocks of positions per thread, 256 threads per workgroup;
+// blocks of 8 positions (the pages' size) read each block with two 16-byte loads.
+constexpr int kBmPer = 4;
+
+template <bool B8>
 __global__ __launch_bounds__(256) void k_block_max(int64_t ncols, int block, int64_t nb,
                                                    const float* __restrict__ scores, float* __restrict__ bmax,
                                                    uint32_t* __restrict__ hist) {
   __shared__ uint32_t lhist[kHistBins];
   const int r = blockIdx.y;
   for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
+  const float* srow = scores + (int64_t)r * ncols;
+  float m[kBmPer];
+#pragma unroll
+  for (int j = 0; j < kBmPer; ++j) {
+    const int64_t k = (blockIdx.x * (int64_t)kBmPer + j) * 256 + threadIdx.x;
+    m[j] = kNegInf;
+    if (k >= nb) continue;
+    if (B8 && k * 8 + 8 <= ncols) {
+      const float4 a = *reinterpret_cast<const float4*>(srow + k * 8);
+      const float4 c = *reinterpret_cast<const float4*>(srow + k * 8 + 4);
+      m[j] = fmaxf(fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)), fmaxf(fmaxf(c.x, c.y), fmaxf(c.z, c.w)));
+    } else {
+      const int64_t n = (ncols - k * block < block) ? ncols - k * block : block;
+      for (int64_t i = 0; i < n; ++i) m[j] = fmaxf(m[j], srow[k * block + i]);  // scores are never NaN
+    }
+  }
   __syncthreads();
-  const int64_t k = blockIdx.x * 256LL + threadIdx.x;
-  if (k < nb) {
-    const float* s = scores + (int64_t)r * ncols + k * block;
-    const int64_t n = (ncols - k * block < block) ? ncols - k * block : block;
-    float m = kNegInf;
-    for (int64_t i = 0; i < n; ++i) m = fmaxf(m, s[i]);  // -inf stays -inf; scores are never NaN
-    bmax[(int64_t)r * nb + k] = m;
-    if (visible(m)) atomicAdd(&lhist[hist_bin(order_key(m))], 1u);
+#pragma unroll
+  for (int j = 0; j < kBmPer; ++j) {
+    const int64_t k = (blockIdx.x * (int64_t)kBmPer + j) * 256 + threadIdx.x;
+    if (k >= nb) continue;
+    bmax[(int64_t)r * nb + k] = m[j];
+    if (visible(m[j])) atomicAdd(&lhist[hist_bin(order_key(m[j]))], 1u);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < kHistBins; i += 256) {
@@ -275,8 +303,12 @@ __global__ __launch_bounds__(256) void k_block_max(int64_t ncols, int block, int
 int launch_block_max(int R, int64_t ncols, int block, const float* scores, float* bmax, uint32_t* hist,
                      hipStream_t st) {
   const int64_t nb = (ncols + block - 1) / block;
-  hipLaunchKernelGGL(k_block_max, dim3((unsigned)((nb + 255) / 256), R), dim3(256), 0, st, ncols, block, nb, scores,
-                     bmax, hist);
+  const dim3 g((unsigned)((nb + 256 * kBmPer - 1) / (256 * kBmPer)), R);
+  // 16-byte loads need 16-byte aligned rows
+  if (block == 8 && ncols % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0)
+    hipLaunchKernelGGL(k_block_max<true>, g, dim3(256), 0, st, ncols, block, nb, scores, bmax, hist);
+  else
+    hipLaunchKernelGGL(k_block_max<false>, g, dim3(256), 0, st, ncols, block, nb, scores, bmax, hist);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
