@@ -177,13 +177,24 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
   const uint8_t* kb = k8 + (int64_t)b * n_max * kKeyBytes + half * (kKeyBytes / 2);
   const float* ksb = ks + (int64_t)b * n_max;
   const int32_t* crow = CAND ? cand + (int64_t)r * ncols : nullptr;
+  // candidate positions of all this wave's tiles, loaded together up front: a position
+  // loaded just before the key load that needs it would make every tile wait for all the
+  // loads issued before it (the vector-memory counter retires in order)
+  int32_t cpos[CAND ? TPW : 1];
+  if (CAND) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int64_t col = c0 + (int64_t)(wave + kScoreWaves * i) * 32 + (lane & 31);
+      cpos[i] = col < c1 ? crow[col] : -1;
+    }
+  }
   v4i ka[P], kc[P];
   float skv[P];
   bool vis[P];
   auto issue = [&](int i, int slot) {
     const int64_t col = c0 + (int64_t)(wave + kScoreWaves * i) * 32 + (lane & 31);
     int64_t row = -1;
-    if (col < c1) row = CAND ? (int64_t)crow[col] : col;
+    if (col < c1) row = CAND ? (int64_t)cpos[i] : col;
     vis[slot] = row >= 0 && row <= lim;
     // branch-free: invisible columns read row 0 (always valid) and are masked later
     const int64_t rr = vis[slot] ? row : 0;
