@@ -64,6 +64,43 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return code | sign;
 }
 
+// The same code with both cases computed and one selected (no branch; the subnormal case
+// adds 2^14, whose fp32 ulp is 2^-9, so the hardware add rounds |y| to a multiple of 2^-9
+// ties-to-even and the low bits of the sum are the code).  Cheaper where a wave's values
+// fall on both sides of 2^-6, dearer where they do not; equal to e4m3_encode for every
+// fp32 input.
+__device__ __forceinline__ uint32_t e4m3_encode_select(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t nrm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  const uint32_t sub = __float_as_uint(a + 16384.0f) - 0x46800000u;  // 0x46800000 = 2^14
+  uint32_t code = a < 0.015625f ? sub : nrm;
+  code = a <= 448.0f ? code : 0x7Eu;
+  return code | sign;
+}
+
+// x / s correctly rounded (round to nearest even) for many x and one divisor s > 0, finite
+// inputs: r = 1/s correctly rounded once, then per quotient q0 = x r and one exact-residual
+// correction q = q0 + (x - q0 s) r with fused multiply-adds (P. Markstein, "Computation of
+// elementary functions on the IBM RISC System/6000 processor", IBM J. Res. Dev. 1990: with
+// r the rounded reciprocal, the corrected quotient is the rounded quotient).  The residual
+// must not underflow, so a divisor below 2^-92 is scaled with x by 2^64 first (exact).  The
+// sign is taken from x, which also keeps the sign of a zero quotient.
+struct ExactQuotient {
+  float k, s, r;
+  __device__ __forceinline__ explicit ExactQuotient(float div) {
+    k = div < 0x1p-92f ? 0x1p64f : 1.0f;
+    s = div * k;
+    r = 1.0f / s;
+  }
+  __device__ __forceinline__ float operator()(float x) const {
+    const float xs = x * k;
+    const float q0 = xs * r;
+    return copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, xs), r, q0), x);
+  }
+};
+
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
   float mag = (e == 0u) ? (float)m * 0.001953125f : __uint_as_float((e + 120u) << 23 | m << 20);

@@ -82,8 +82,10 @@ constexpr int kPrefetch = 4;  // 32-key tiles in flight per wave (16 x 16 B nont
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 // Quantise lane's half of head (lane%32) of the query row to E4M3 and return the MFMA
-// A operand (byte j of the 32 = dim 32*(lane/32) + j), plus sq for that head.
-template <typename QT>
+// A operand (byte j of the 32 = dim 32*(lane/32) + j), plus sq for that head.  SEL picks
+// the branch-free encoder: short candidate scans wait on this prologue and run faster with
+// it, long streaming scans hide it behind their loads and run faster without.
+template <typename QT, bool SEL>
 __device__ __forceinline__ v8i quantize_query_operand(const QT* __restrict__ qrow, int lane, float& sq_out) {
   // two passes over the (cache-resident) 32 values so that few registers are live while
   // the first key tiles are in flight: absmax, then encode
@@ -94,16 +96,18 @@ __device__ __forceinline__ v8i quantize_query_operand(const QT* __restrict__ qro
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(load_as_f32(p + i)));
   amax = fmaxf(amax, __shfl_xor(amax, 32));
   const float sq = amax / 448.0f;
+  const ExactQuotient div(sq);
+  const uint32_t keep = sq != 0.0f ? ~0u : 0u;  // an all-zero head encodes to zero bytes
   v8i a;
 #pragma unroll
   for (int wd = 0; wd < 8; ++wd) {
     uint32_t word = 0;
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
-      const uint32_t code = (sq != 0.0f) ? e4m3_encode(load_as_f32(p + wd * 4 + bb) / sq) : 0u;
-      word |= code << (8 * bb);
+      const float y = div(load_as_f32(p + wd * 4 + bb));
+      word |= (SEL ? e4m3_encode_select(y) : e4m3_encode(y)) << (8 * bb);
     }
-    a[wd] = (int)word;
+    a[wd] = (int)(word & keep);
   }
   sq_out = sq;
   return a;
@@ -121,16 +125,15 @@ __device__ __forceinline__ v8i quantize_query_operand_fp4(const QT* __restrict__
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(load_as_f32(p + i)));
   amax = fmaxf(amax, __shfl_xor(amax, 32));
   const float sq = amax / 6.0f;
+  const ExactQuotient div(sq);
+  const uint32_t keep = sq != 0.0f ? ~0u : 0u;
   v8i a = {};
 #pragma unroll
   for (int wd = 0; wd < 4; ++wd) {
     uint32_t word = 0;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const uint32_t code = (sq != 0.0f) ? e2m1_encode(load_as_f32(p + wd * 8 + nb) / sq) : 0u;
-      word |= code << (4 * nb);
-    }
-    a[wd] = (int)word;
+    for (int nb = 0; nb < 8; ++nb) word |= e2m1_encode(div(load_as_f32(p + wd * 8 + nb))) << (4 * nb);
+    a[wd] = (int)(word & keep);
   }
   sq_out = sq;
   return a;
@@ -180,12 +183,19 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
   // candidate positions of all this wave's tiles, loaded together up front: a position
   // loaded just before the key load that needs it would make every tile wait for all the
   // loads issued before it (the vector-memory counter retires in order)
+  // (unconditional loads from a clamped column, masked afterwards: a load behind a branch
+  // is waited for before the branch joins)
   int32_t cpos[CAND ? TPW : 1];
   if (CAND) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int64_t col = c0 + (int64_t)(wave + kScoreWaves * i) * 32 + (lane & 31);
-      cpos[i] = col < c1 ? crow[col] : -1;
+      cpos[i] = crow[col < c1 ? col : c1 - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int64_t col = c0 + (int64_t)(wave + kScoreWaves * i) * 32 + (lane & 31);
+      if (col >= c1) cpos[i] = -1;
     }
   }
   v4i ka[P], kc[P];
@@ -220,7 +230,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
     for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0;
   __syncthreads();
   float sq;
-  const v8i A = F4 ? quantize_query_operand_fp4(s_q, lane, sq) : quantize_query_operand(s_q, lane, sq);
+  const v8i A = F4 ? quantize_query_operand_fp4(s_q, lane, sq) : quantize_query_operand<QT, CAND>(s_q, lane, sq);
   if (wave == 0 && lane < 32) s_c[lane] = sq;
   __syncthreads();
   if (tid < 32) s_c[tid] = wv * s_c[tid];
@@ -292,12 +302,13 @@ __global__ __launch_bounds__(256) void k_quant_query(const QT* __restrict__ q, c
   amax = fmaxf(amax, __shfl_xor(amax, 2));
   amax = fmaxf(amax, __shfl_xor(amax, 4));
   const float sq = amax / 448.0f;
+  const ExactQuotient div(sq);
+  const uint32_t keep = sq != 0.0f ? ~0u : 0u;
   uint32_t wd[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t code = (sq != 0.0f) ? e4m3_encode(v[i] / sq) : 0u;
-    wd[i >> 2] |= code << (8 * (i & 3));
-  }
+  for (int i = 0; i < 8; ++i) wd[i >> 2] |= e4m3_encode(div(v[i])) << (8 * (i & 3));
+  wd[0] &= keep;
+  wd[1] &= keep;
   *reinterpret_cast<uint2*>(q8 + ((int64_t)r * 32 + h) * 64 + d0) = make_uint2(wd[0], wd[1]);
   if ((tid & 7) == 0) c[(int64_t)r * 32 + h] = w[(int64_t)r * 32 + h] * sq;
 }
@@ -466,14 +477,17 @@ template <typename QT, bool CAND, int TPW, bool F4>
 static void launch_fp8(const ScoreArgs& a, hipStream_t st) {
   const int cpb = kScoreWaves * TPW * 32;
   dim3 g((unsigned)((a.ncols + cpb - 1) / cpb), a.B * a.T);
-  if (!CAND && a.keep)
-    hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4, true>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q,
-                       a.w, (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,
-                       a.key_div);
-  else
-    hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q, a.w,
-                       (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,
-                       a.key_div);
+  if constexpr (!CAND) {
+    if (a.keep) {
+      hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4, true>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q,
+                         a.w, (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,
+                         a.key_div);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q, a.w,
+                     (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,
+                     a.key_div);
 }
 
 template <typename QT, bool CAND, bool F4>

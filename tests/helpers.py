@@ -143,3 +143,33 @@ def check_pooled_reindex(g_idx, q, w, k8, ks, nk, gpool, K):
     for b in range(len(nk)):
         sel = g_idx[b, 0]
         assert np.all(np.isin(sel[sel >= 0], gpool[b])), b
+
+
+def single_head_edge_queries(q):
+    """Index queries [B][T][32][64] where row r = (b, t) keeps only head r % 32, bf16-exact,
+    scaled by kind r % 4: 1e-27 (a per-head scale below 2^-92), spread over six decades
+    (many E4M3 subnormal codes), 1e30, or as drawn.  Every other head is zero."""
+    rng = np.random.default_rng(21)
+    B, T, H, dk = q.shape
+    out = np.zeros((B, T, H, dk), np.float32)
+    for r in range(B * T):
+        b, t, h = r // T, r % T, r % H
+        v = q[b, t, h].astype(np.float32)
+        kind = r % 4
+        if kind == 0:
+            v = v * np.float32(1e-27)
+        elif kind == 1:
+            v = v * (10.0 ** rng.uniform(-6, 0, size=dk)).astype(np.float32)
+        elif kind == 2:
+            v = v * np.float32(1e30)
+        out[b, t, h] = v
+    return torch.from_numpy(out).to(torch.bfloat16).float().numpy()
+
+
+def one_hot_keys(B, n, dk=64):
+    """Keys [B][n][dk] with key j = unit vector along dim j % dk: each score of a one-head
+    query is then a single product, exact up to the rounding of the final scaling."""
+    k = np.zeros((B, n, dk), np.float32)
+    j = np.arange(n)
+    k[:, j, j % dk] = 1.0
+    return k

@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import workloads
-from helpers import DEV, build_cache, check_topk_near_tie, fp4_score_bound, max_abs_rel, to_dev
+from helpers import (DEV, build_cache, check_topk_near_tie, fp4_score_bound, max_abs_rel, one_hot_keys,
+                     single_head_edge_queries, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +72,32 @@ def test_index_score_fp4(T, causal):
     idx = csa2.index_topk(csa2.PREC_FP4, to_dev(q, torch.bfloat16), to_dev(w), codes, scales, to_dev(nk), 512,
                           q_limit=None if ql is None else to_dev(ql))
     check_topk_near_tie(idx.cpu().numpy(), ref, 512)
+
+
+@pytest.mark.parametrize("with_cand", [False, True])
+def test_index_query_codes_exact_fp4(with_cand):
+    """The E2M1 query quantisation inside the 4-bit scoring kernel, code for code: one-hot
+    keys and one-head queries make every score a single product of one query code's value
+    and the scales (a differing code moves it by at least 1/4 of itself); bar 1e-6 relative.
+    Heads cover scales below 2^-92, six decades inside a head, 1e30 and all-zero heads."""
+    B = 32
+    wl = workloads.workload("full64k", B=B)
+    n = 128
+    codes, scales, cr, sr = fp4_keys(one_hot_keys(B, n))
+    q, w = single_head_edge_queries(wl.index_query()), wl.head_weights()
+    nk = np.full(B, n, np.int32)
+    cand = None
+    if with_cand:
+        rng = np.random.default_rng(6)
+        cand = np.stack([rng.permutation(np.concatenate([np.arange(n), np.full(30, -1)])) for _ in range(B)])
+        cand = cand[:, None].astype(np.int32)
+    ref = oracle.index_score(oracle.PREC_FP4, q, w, cr, sr, nk, cand=cand)
+    got = csa2.index_score(csa2.PREC_FP4, to_dev(q, torch.bfloat16), to_dev(w), codes, scales, to_dev(nk),
+                           cand=None if cand is None else to_dev(cand)).cpu().numpy()
+    vis = np.isfinite(ref)
+    assert np.array_equal(vis, np.isfinite(got))
+    assert np.all(np.abs(got[vis] - ref[vis]) <= 1e-6 * np.abs(ref[vis]))
+    assert np.count_nonzero(ref[vis]) > vis.sum() // 3
 
 
 def test_index_score_fp4_candidates_and_fp32_query():

@@ -14,7 +14,8 @@ import torch
 
 import oracle
 import workloads
-from helpers import (DEV, build_cache, check_topk_near_tie, e4m3_to_f64, fp8_score_bound, max_abs_rel, to_dev)
+from helpers import (DEV, build_cache, check_topk_near_tie, e4m3_to_f64, fp8_score_bound, max_abs_rel, one_hot_keys,
+                     single_head_edge_queries, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -140,6 +141,38 @@ def test_index_score_fp8_candidates():
     assert np.array_equal(np.isinf(got), np.isinf(ref))
     fin = np.isfinite(ref)
     assert np.allclose(got[fin], ref[fin], rtol=1e-4, atol=1e-4 * np.abs(ref[fin]).max())
+
+
+@pytest.mark.parametrize("path", ["stream", "candidates", "row_tiles"])
+def test_index_query_codes_exact(path):
+    """The query quantisation inside each fp8 scoring kernel, code for code: with one-hot keys
+    and one-head queries every score is a single product of one query code's value and the
+    scales, so a code that differs from the oracle's moves its score by at least 1/16 of
+    itself; the bar is 1e-6 relative (the rounding of the scale products).  The heads cover
+    scales below 2^-92, E4M3 subnormal codes, 1e30 and all-zero heads."""
+    T = 8 if path == "row_tiles" else 1
+    B = 32 // T
+    wl = workloads.workload("full64k", B=B, T=T)
+    n = 192
+    k = one_hot_keys(B, n)
+    k8_ref, ks_ref = oracle.quantize_fp8(k)
+    k8 = torch.empty((B, n, 64), dtype=torch.uint8, device=DEV)
+    ks = torch.empty((B, n), dtype=torch.float32, device=DEV)
+    csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(k), k8, ks)
+    q, w = single_head_edge_queries(wl.index_query()), wl.head_weights()
+    nk = np.full(B, n, np.int32)
+    cand = None
+    if path == "candidates":
+        rng = np.random.default_rng(5)
+        cand = np.stack([rng.permutation(np.concatenate([np.arange(n), np.full(40, -1)])) for _ in range(B)])
+        cand = cand[:, None].astype(np.int32)
+    ref = oracle.index_score(oracle.PREC_FP8, q, w, k8_ref, ks_ref, nk, cand=cand)
+    got = csa2.index_score(csa2.PREC_FP8, to_dev(q, torch.bfloat16), to_dev(w), k8, ks, to_dev(nk),
+                           cand=None if cand is None else to_dev(cand)).cpu().numpy()
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    assert np.all(np.abs(got[fin] - ref[fin]) <= 1e-6 * np.abs(ref[fin]))
+    assert np.count_nonzero(ref[fin]) > fin.sum() // 2
 
 
 # ------------------------------------------------------------------------------ Top-K
