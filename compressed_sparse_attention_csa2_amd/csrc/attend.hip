@@ -335,7 +335,14 @@ struct AttLds {
   static constexpr size_t kP = (size_t)kAttHeads * kPpad * 2;
   static constexpr size_t kS = G16 ? (size_t)(D / 16) * kSpad * 2 : 0;  // [group][entry] fp16 scales
   static constexpr size_t kO = (size_t)WPT * kAttHeads * D * 4;  // per entry group, after sA/sP/sS are dead
-  static constexpr size_t kAP = kA + kP + kS;
+  // per-channel layout: the split's FP4 rows are staged in LDS ([entry][D/2 bytes], 16-byte
+  // chunks XOR-swizzled), followed by sA; sP takes sA's place once QK is done.  G16: sA,
+  // sP, sS side by side (its rows are read from global memory).
+  static constexpr size_t kRows = G16 ? 0 : (size_t)kAttSplit * (D / 2);
+  static constexpr size_t kOffA = kRows;
+  static constexpr size_t kOffP = G16 ? kA : kRows;
+  static constexpr size_t kOffS = kA + kP;
+  static constexpr size_t kAP = G16 ? kA + kP + kS : kRows + (kA > kP ? kA : kP);
   static constexpr size_t kWork = kAP > kO ? kAP : kO;
   static constexpr size_t kUnion0 = kWork > sizeof(FinalizeSmem) ? kWork : sizeof(FinalizeSmem);
   static constexpr size_t kUnion = kUnion0 > WinLds<D>::kBytes ? kUnion0 : WinLds<D>::kBytes;
@@ -361,6 +368,16 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   constexpr int kRowBytes = D / 2;
   constexpr int kCT = D / 128;                 // 128-channel tiles
   constexpr int kWPT = (kAttWaves / kCT < kAttSplit / 32) ? kAttWaves / kCT : kAttSplit / 32;  // waves per tile in PV
+  // per-channel layout: the split's rows are gathered whole (a wave instruction reads
+  // kRPI complete rows, 16 bytes per lane) and staged in LDS; chunk c of entry e sits in
+  // chunk slot c ^ swz(e), so that the 16 entries of an MFMA operand read spread over
+  // all banks.  (Gathering 64-byte row pieces of 16 entries per instruction straight into
+  // operand layout measured about 3x slower per byte when the rows are cached.)
+  constexpr int kNC = kRowBytes / 16;          // 16-byte chunks per row: 4, 8 or 16
+  constexpr int kRPI = 64 / kNC;               // rows per gather instruction
+  constexpr int kGI = kAttSplit / (kRPI * kAttWaves);  // gather instructions per wave
+  static_assert(kGI * kRPI * kAttWaves == kAttSplit, "the gather covers the split");
+  auto swz = [](int e) { return (e / (16 / kNC)) & (kNC - 1); };
   constexpr int kEPW = kAttSplit / kWPT;       // entries per wave in PV (a multiple of 32)
   using L = AttLds<D, kWPT, G16>;
   constexpr int kNG = D / 16;                  // scale groups per entry (G16)
@@ -370,10 +387,11 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   __shared__ float s_m[kAttHeads], s_l[kAttHeads];
   __shared__ float s_qmax[kAttWaves];
   __shared__ __align__(16) unsigned char s_u[L::kUnion];
-  uint16_t* sA = reinterpret_cast<uint16_t*>(s_u);
-  uint16_t* sP = reinterpret_cast<uint16_t*>(s_u + L::kA);
-  uint16_t* sS = reinterpret_cast<uint16_t*>(s_u + L::kA + L::kP);  // G16: [kNG][kSpad] fp16
-  float* sO = reinterpret_cast<float*>(s_u);  // [kWPT][16][D], used once sA, sP, sS are dead
+  uint16_t* sA = reinterpret_cast<uint16_t*>(s_u + L::kOffA);
+  uint16_t* sP = reinterpret_cast<uint16_t*>(s_u + L::kOffP);
+  uint16_t* sS = reinterpret_cast<uint16_t*>(s_u + L::kOffS);  // G16: [kNG][kSpad] fp16
+  unsigned char* s_rows = s_u;                 // per-channel: the split's rows (see AttLds)
+  float* sO = reinterpret_cast<float*>(s_u);  // [kWPT][16][D], used once the rows, sA, sP, sS are dead
   const float* scales = static_cast<const float*>(scales_v);
 
   const int split = blockIdx.x, hg = blockIdx.y, r = blockIdx.z;
@@ -457,9 +475,11 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   for (int t = 0; t < kAttTPW; ++t) {
     const int e = (wave * kAttTPW + t) * 16 + n16;
     jt[t] = sel[e];  // -1 past K
-    const uint8_t* rowp = cb + (int64_t)(jt[t] >= 0 ? jt[t] : 0) * kRowBytes + 16 * g;
+    if constexpr (G16) {
+      const uint8_t* rowp = cb + (int64_t)(jt[t] >= 0 ? jt[t] : 0) * kRowBytes + 16 * g;
 #pragma unroll
-    for (int i = 0; i < kCT; ++i) kw[t][i] = *reinterpret_cast<const uint4*>(rowp + 64 * i);
+      for (int i = 0; i < kCT; ++i) kw[t][i] = *reinterpret_cast<const uint4*>(rowp + 64 * i);
+    }
   }
 
   // ---- phase 0b: q'' = q * s * 2^k in fp16 into LDS (A operand of QK)
@@ -494,6 +514,22 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   const float up = __uint_as_float((uint32_t)(127 + 15 - qexp) << 23);
   const float down = __uint_as_float((uint32_t)(127 - 15 + qexp) << 23);
   const float lscale = softmax_scale * down;
+  // per-channel: gather instruction j of a wave loads rows r0 .. r0 + kRPI - 1 (r0 =
+  // (wave kGI + j) kRPI) straight into LDS, lane l's 16 bytes landing in chunk slot l % kNC of
+  // row r0 + l / kNC; the lane reads logical chunk (l % kNC) ^ swz(row), which swizzles the
+  // staged row.  Issued once the query's block maximum is known: the loads stay in flight through
+  // the query's conversion and stores (LDS reads while they are in flight would wait for them).
+  if constexpr (!G16) {
+#pragma unroll
+    for (int j = 0; j < kGI; ++j) {
+      const int r0 = (wave * kGI + j) * kRPI;
+      const int row = r0 + lane / kNC;
+      const int32_t jr = sel[row];
+      const uint8_t* src = cb + (int64_t)(jr >= 0 ? jr : 0) * kRowBytes + 16 * ((lane % kNC) ^ swz(row));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(s_rows + r0 * kRowBytes), 16, 0, 0);
+    }
+  }
 #pragma unroll
   for (int it = 0; it < kQPer; ++it) {
     const int i = tid + it * kAttThreads;
@@ -522,6 +558,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
       }
     }
   }
+  if constexpr (!G16) __builtin_amdgcn_s_waitcnt(0);  // this wave's row loads have landed in LDS
   __syncthreads();
 
   // ---- phase 1b: logits of this wave's kAttTPW tiles of 16 entries
@@ -532,7 +569,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     const int el = (wave * kAttTPW + t) * 16 + n16;  // this lane's entry in the split
 #pragma unroll
     for (int i = 0; i < kCT; ++i) {
-      const uint32_t wd[4] = {kw[t][i].x, kw[t][i].y, kw[t][i].z, kw[t][i].w};
+      uint4 kv;
+      if constexpr (G16) kv = kw[t][i];
+      else kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
+      const uint32_t wd[4] = {kv.x, kv.y, kv.z, kv.w};
       _Float16 gs[2] = {(_Float16)1.0f, (_Float16)1.0f};
       if (G16) {  // channels 128 i + 32 g + [0, 32): groups 8 i + 2 g and 8 i + 2 g + 1
         gs[0] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g) * L::kSpad + el]);
@@ -550,10 +590,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (jt[t] >= 0) ? a[rr] * lscale : kNegInf;
   }
 
-  // ---- phase 3a: issue the PV code-word loads (cache hits: the rows were just read) so
-  //      that they are in flight during the softmax.  Wave (channel tile ct, entry group
-  //      eq); lane (channel block n16, group g) takes one 32-bit word (8 channels) of each
-  //      of the 8 entries el..el+7 of every 32-entry k-step.
+  // ---- phase 3a: read the PV code words now (staged rows in LDS; G16: global loads, cache
+  //      hits since the rows were just read) so that they arrive during the softmax.  Wave
+  //      (channel tile ct, entry group eq); lane (channel block n16, group g) takes one
+  //      32-bit word (8 channels) of each of the 8 entries el..el+7 of every 32-entry k-step.
   const int ct = wave % kCT, eq = wave / kCT;
   const bool pv_active = eq < kWPT;
   uint32_t pw[kEPW / 32][8];
@@ -563,9 +603,14 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const int e = el + jj;
-      const int32_t j = sel[e];  // -1 past K (read unconditionally: no branch per load)
-      // p is 0 for skipped entries, so any valid row may stand in for them
-      pw[ks][jj] = *reinterpret_cast<const uint32_t*>(cb + (int64_t)(j >= 0 ? j : 0) * kRowBytes + 64 * ct + 4 * n16);
+      if constexpr (G16) {
+        const int32_t j = sel[e];  // -1 past K (read unconditionally: no branch per load)
+        // p is 0 for skipped entries, so any valid row may stand in for them
+        pw[ks][jj] = *reinterpret_cast<const uint32_t*>(cb + (int64_t)(j >= 0 ? j : 0) * kRowBytes + 64 * ct + 4 * n16);
+      } else {  // word 16 ct + n16 of the staged row
+        pw[ks][jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes +
+                                                         16 * ((4 * ct + (n16 >> 2)) ^ swz(e)) + 4 * (n16 & 3));
+      }
     }
   }
 
