@@ -561,34 +561,45 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   if constexpr (!G16) __builtin_amdgcn_s_waitcnt(0);  // this wave's row loads have landed in LDS
   __syncthreads();
 
-  // ---- phase 1b: logits of this wave's kAttTPW tiles of 16 entries
+  // ---- phase 1b: logits of this wave's kAttTPW tiles of 16 entries.  The channel loop is
+  //      outside the tile loop, so each A operand (16 B of q'' per lane) is read from LDS once
+  //      for all of the wave's tiles.
   float logit[kAttTPW][4];
+  v4f a[kAttTPW];
 #pragma unroll
-  for (int t = 0; t < kAttTPW; ++t) {
-    v4f a = {0.f, 0.f, 0.f, 0.f};
-    const int el = (wave * kAttTPW + t) * 16 + n16;  // this lane's entry in the split
+  for (int t = 0; t < kAttTPW; ++t) a[t] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kCT; ++i) {
+  for (int i = 0; i < kCT; ++i) {
+    uint32_t wd[kAttTPW][4];
+    _Float16 gs[kAttTPW][2];
+#pragma unroll
+    for (int t = 0; t < kAttTPW; ++t) {
+      const int el = (wave * kAttTPW + t) * 16 + n16;  // this lane's entry in the split
       uint4 kv;
       if constexpr (G16) kv = kw[t][i];
       else kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
-      const uint32_t wd[4] = {kv.x, kv.y, kv.z, kv.w};
-      _Float16 gs[2] = {(_Float16)1.0f, (_Float16)1.0f};
+      wd[t][0] = kv.x; wd[t][1] = kv.y; wd[t][2] = kv.z; wd[t][3] = kv.w;
+      gs[t][0] = gs[t][1] = (_Float16)1.0f;
       if (G16) {  // channels 128 i + 32 g + [0, 32): groups 8 i + 2 g and 8 i + 2 g + 1
-        gs[0] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g) * L::kSpad + el]);
-        gs[1] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g + 1) * L::kSpad + el]);
-      }
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        v8h bv = decode8_f16(wd[sub]);
-        if (G16) bv = bv * gs[sub >> 1];
-        const v8h av = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, a, 0, 0, 0);
+        gs[t][0] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g) * L::kSpad + el]);
+        gs[t][1] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g + 1) * L::kSpad + el]);
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (jt[t] >= 0) ? a[rr] * lscale : kNegInf;
+    for (int sub = 0; sub < 4; ++sub) {
+      const v8h av = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
+#pragma unroll
+      for (int t = 0; t < kAttTPW; ++t) {
+        v8h bv = decode8_f16(wd[t][sub]);
+        if (G16) bv = bv * gs[t][sub >> 1];
+        a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, a[t], 0, 0, 0);
+      }
+    }
   }
+#pragma unroll
+  for (int t = 0; t < kAttTPW; ++t)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (jt[t] >= 0) ? a[t][rr] * lscale : kNegInf;
 
   // ---- phase 3a: read the PV code words now (staged rows in LDS; G16: global loads, cache
   //      hits since the rows were just read) so that they arrive during the softmax.  Wave
