@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   __shared__ int32_t s_idx[FROM_CAND ? CSA2_MAX_K_DEV : kAttSplit];
   __shared__ float s_red[kAttWaves][kAttHeads];
   __shared__ float s_m[kAttHeads], s_l[kAttHeads];
-  __shared__ float s_qmax[kAttWaves];
+  __shared__ float s_down[kAttHeads];          // per head: softmax scale / the query prescale
   __shared__ __align__(16) unsigned char s_u[L::kUnion];
   uint16_t* sA = reinterpret_cast<uint16_t*>(s_u + L::kOffA);
   uint16_t* sP = reinterpret_cast<uint16_t*>(s_u + L::kOffP);
@@ -482,43 +482,32 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     }
   }
 
-  // ---- phase 0b: q'' = q * s * 2^k in fp16 into LDS (A operand of QK)
-  float qv[kQPer][8];
+  // ---- phase 0b: q'' = q * s * 2^k_h in fp16 into LDS (A operand of QK), with one exact
+  //      power-of-two prescale per head (|q''| < 2^15, the fp16 range), undone in that head's
+  //      logits.  A head's D/8 items sit in one wave, so its maximum needs no block barrier.
+  static_assert(kQPer == 1, "one query item per thread");
+  constexpr int kLPH = D / 8;                  // lanes per head
+  const bool q_act = tid < kQItems;
+  const int qh = tid / kLPH, qc = (tid % kLPH) * 8;
+  float qv[8];
   float qmax = 0.0f;
-#pragma unroll
-  for (int it = 0; it < kQPer; ++it) {
-    const int i = tid + it * kAttThreads;
-    const int ic = i < kQItems ? i : kQItems - 1;
-    const int c = (ic % (D / 8)) * 8;
-    const uint32_t wds[4] = {qraw[it].x, qraw[it].y, qraw[it].z, qraw[it].w};
+  {
+    const uint32_t wds[4] = {qraw[0].x, qraw[0].y, qraw[0].z, qraw[0].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      qv[it][e] = bf16_to_f32((uint16_t)(wds[e >> 1] >> (16 * (e & 1)))) * (G16 ? 1.0f : s_scale[c + e]);
-      qmax = fmaxf(qmax, fabsf(qv[it][e]));
+      qv[e] = bf16_to_f32((uint16_t)(wds[e >> 1] >> (16 * (e & 1)))) * (G16 || !q_act ? 1.0f : s_scale[qc + e]);
+      qmax = fmaxf(qmax, fabsf(qv[e]));
     }
   }
-  qmax = wave_max(qmax);
-  if (lane == 0) s_qmax[wave] = qmax;
-  __syncthreads();
-  {
-    float t4[kAttWaves];
-#pragma unroll
-    for (int w2 = 0; w2 < kAttWaves; ++w2) t4[w2] = s_qmax[w2];
-    qmax = t4[0];
-#pragma unroll
-    for (int w2 = 1; w2 < kAttWaves; ++w2) qmax = fmaxf(qmax, t4[w2]);
-  }
-  // power-of-two prescale so that |q''| < 2^15 (fp16 max 65504); exact, undone in the logits
-  int qexp = 0;
-  if (qmax > 0.0f) qexp = (int)((__float_as_uint(qmax) >> 23) & 255u) - 126;
-  const float up = __uint_as_float((uint32_t)(127 + 15 - qexp) << 23);
-  const float down = __uint_as_float((uint32_t)(127 - 15 + qexp) << 23);
-  const float lscale = softmax_scale * down;
+  // keep the query reads above the row loads (a wait for the query after them would also
+  // wait for the rows)
+  __builtin_amdgcn_sched_barrier(0);
   // per-channel: gather instruction j of a wave loads rows r0 .. r0 + kRPI - 1 (r0 =
   // (wave kGI + j) kRPI) straight into LDS, lane l's 16 bytes landing in chunk slot l % kNC of
   // row r0 + l / kNC; the lane reads logical chunk (l % kNC) ^ swz(row), which swizzles the
-  // staged row.  Issued once the query's block maximum is known: the loads stay in flight through
-  // the query's conversion and stores (LDS reads while they are in flight would wait for them).
+  // staged row.  Issued after the last LDS read of the query preparation: the loads stay in
+  // flight through the query's conversion and stores (an LDS read while they are in flight
+  // would wait for them).
   if constexpr (!G16) {
 #pragma unroll
     for (int j = 0; j < kGI; ++j) {
@@ -530,18 +519,25 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
                                        (__attribute__((address_space(3))) void*)(s_rows + r0 * kRowBytes), 16, 0, 0);
     }
   }
-#pragma unroll
-  for (int it = 0; it < kQPer; ++it) {
-    const int i = tid + it * kAttThreads;
-    if (i >= kQItems) break;
-    const int h = i / (D / 8), c = (i % (D / 8)) * 8;
+  {  // the head's maximum over its kLPH lanes (16-lane rows, then rows of one head)
+    float hm = row16_max(qmax);
+    const float m0 = lane_read(hm, 0), m1 = lane_read(hm, 16), m2 = lane_read(hm, 32), m3 = lane_read(hm, 48);
+    if (kLPH == 64) hm = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+    else if (kLPH == 32) hm = (lane < 32) ? fmaxf(m0, m1) : fmaxf(m2, m3);
+    qmax = hm;
+  }
+  int qexp = 0;
+  if (qmax > 0.0f) qexp = (int)((__float_as_uint(qmax) >> 23) & 255u) - 126;
+  const float up = __uint_as_float((uint32_t)(127 + 15 - qexp) << 23);
+  if (q_act) {
     uint32_t wv[4];
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
-      const _Float16 a0 = (_Float16)(qv[it][2 * k2] * up), a1 = (_Float16)(qv[it][2 * k2 + 1] * up);
+      const _Float16 a0 = (_Float16)(qv[2 * k2] * up), a1 = (_Float16)(qv[2 * k2 + 1] * up);
       wv[k2] = pack2(__builtin_bit_cast(uint16_t, a0), __builtin_bit_cast(uint16_t, a1));
     }
-    *reinterpret_cast<uint4*>(&sA[h * L::kApad + c]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    *reinterpret_cast<uint4*>(&sA[qh * L::kApad + qc]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    if (qc == 0) s_down[qh] = softmax_scale * __uint_as_float((uint32_t)(127 - 15 + qexp) << 23);
   }
   if (G16) {  // the scales as fp16, [group][entry]
 #pragma unroll
@@ -599,7 +595,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
 #pragma unroll
   for (int t = 0; t < kAttTPW; ++t)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (jt[t] >= 0) ? a[t][rr] * lscale : kNegInf;
+    for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (jt[t] >= 0) ? a[t][rr] * s_down[4 * g + rr] : kNegInf;
 
   // ---- phase 3a: read the PV code words now (staged rows in LDS; G16: global loads, cache
   //      hits since the rows were just read) so that they arrive during the softmax.  Wave
