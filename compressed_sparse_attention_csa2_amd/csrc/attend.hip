@@ -11,15 +11,18 @@
 // row x 16 heads (the MFMA M dimension) x one split of up to 512 selected entries, 16
 // waves, so the pages' Top-512 needs no merge; larger K runs several splits and a second
 // kernel merges their partial softmaxes by log-sum-exp (a kernel boundary: merging inside
-// the kernel would need a device-scope release fence, which costs more here).  The per-channel scale s_c factors out of both
-// contractions: logits use q'' = q * s * 2^k in fp16 (2^k an exact prescale keeping
-// |q''| below 2^15, undone in the softmax scale; ~2^-12 relative error) against the exact
-// E2M1 values e in fp16; the output is s_c * sum_j p_j e_jc / l with p in fp16.  FP4
-// rows go straight from HBM into MFMA operand layout (no LDS staging): for QK lane
-// (entry n, group g) reads 16 contiguous bytes per 128 channels; for PV lane (channel
-// block n, entry group g) reads one 32-bit word (8 channels) of each of 8 entries.  PV is
-// split over waves by (channel tile, entry group) and the entry groups are summed in LDS
-// in a fixed order (deterministic).
+// the kernel would need a device-scope release fence, which costs more here).  The
+// per-channel scale s_c factors out of both contractions: logits use q'' = q * s * 2^k_h in
+// fp16 (2^k_h an exact per-head prescale keeping |q''| below 2^15, undone in that head's
+// logits; ~2^-12 relative error) against the exact E2M1 values e in fp16; the output is
+// s_c * sum_j p_j e_jc / l with p in fp16.  Per-channel layout: the split's FP4 rows are
+// gathered whole into LDS (one wave instruction loads complete rows, 16 bytes per lane,
+// straight into LDS) and both contractions read their operands from there: for QK lane
+// (entry n, group g) reads 16 bytes per 128 channels, for PV lane (channel block n, entry
+// group g) one 32-bit word (8 channels) of each of 8 entries.  G16 layout: the same
+// operands are loaded from global memory directly.  PV is split over waves by (channel
+// tile, entry group) and the entry groups are summed in LDS in a fixed order
+// (deterministic).
 //
 // fp32 path (fp32 queries): plain VALU, one block per (row, head), fp32 throughout.
 #include "common.hpp"
