@@ -237,21 +237,21 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, 
   if (EXPAND) {
     // rows_per_seq (rps) query rows share a sequence; row t of it sees its first
     // n_keys - (rps - 1 - t) positions (multi-token decode).  K * block fits in int32 (the
-    // expansion is bounded by the Top-K column limit); four positions per store when the
-    // block size allows.
+    // expansion is bounded by the Top-K column limit).
     const int64_t nk = (int64_t)n_keys[r / rps] - (rps - 1 - r % rps);
-    const int total = K * block;
-    int32_t* dst = expand_out + (int64_t)r * total;
-    auto pos_of = [&](int i) -> int32_t {
-      const int e = i / block;
-      const int64_t pos = (e < keff) ? (int64_t)s_pos[e] * block + (i - e * block) : -1;
-      return (pos >= 0 && pos < nk) ? (int32_t)pos : -1;
-    };
-    if (block % 4 == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-      for (int i = 4 * threadIdx.x; i < total; i += 4 * kFinThreads)
-        *reinterpret_cast<int4*>(dst + i) = make_int4(pos_of(i), pos_of(i + 1), pos_of(i + 2), pos_of(i + 3));
-    } else {
-      for (int i = threadIdx.x; i < total; i += kFinThreads) dst[i] = pos_of(i);
+    int32_t* dst = expand_out + (int64_t)r * K * block;
+    // one selected block per thread and pass: its `block` positions, four per store when
+    // the block size allows
+    const bool vec = block % 4 == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+    for (int e = threadIdx.x; e < K; e += kFinThreads) {
+      const int64_t base = (e < keff) ? (int64_t)s_pos[e] * block : -1;
+      auto pos = [&](int k) -> int32_t { return (base >= 0 && base + k < nk) ? (int32_t)(base + k) : -1; };
+      int32_t* d = dst + (int64_t)e * block;
+      if (vec) {
+        for (int k = 0; k < block; k += 4) *reinterpret_cast<int4*>(d + k) = make_int4(pos(k), pos(k + 1), pos(k + 2), pos(k + 3));
+      } else {
+        for (int k = 0; k < block; ++k) d[k] = pos(k);
+      }
     }
   }
 }
