@@ -153,9 +153,18 @@ __device__ int finalize_row(const uint2* __restrict__ regions, const uint32_t* _
   uint32_t hb[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) hb[i] = (tid < kT) ? h2row[tid * kPer + i] : 0u;
-  // 0. region starts: exclusive prefix of the per-region counts (one load per thread per
-  //    pass; nreg <= kFinMaxRegions)
-  {
+  // 0. region starts: exclusive prefix of the per-region counts (one wave when there are
+  //    at most 64 regions, else one load per thread per pass; nreg <= kFinMaxRegions)
+  if (nreg <= 64) {
+    if (wave == 0) {
+      const uint32_t v = (lane < nreg) ? cnt[lane] : 0u;
+      const uint32_t sfx = wave_suffix(v);  // counts of regions >= lane
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 0);
+      if (lane < nreg) sm.start[lane] = tot - sfx;
+      if (lane == 0) sm.misc[4] = tot;
+    }
+    __syncthreads();
+  } else {
     uint32_t carry = 0;
     for (int base = 0; base < nreg; base += NT) {
       const int rg = base + tid;
