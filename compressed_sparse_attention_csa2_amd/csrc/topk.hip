@@ -56,16 +56,12 @@ __global__ __launch_bounds__(256) void k_topk_hist(int64_t ncols, const float* _
 // above it, keff = min(K, visible).  Block-wide (256 threads, thread t owns bins 8t..8t+7);
 // result in s_misc[0] (visible total), [1] (beta; kHistBins if nothing is visible),
 // [4] (above).
-__device__ __forceinline__ void row_threshold(const uint32_t* __restrict__ hrow, int K, uint32_t* sh4,
-                                              uint32_t* s_misc) {
+// The same from this thread's bins hb = hrow[8 tid .. 8 tid + 7], already loaded.
+__device__ __forceinline__ void row_threshold_of(const uint32_t (&hb)[8], int K, uint32_t* sh4, uint32_t* s_misc) {
   const int tid = threadIdx.x;
-  uint32_t hb[8];
   uint32_t local = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    hb[i] = hrow[tid * 8 + i];
-    local += hb[i];
-  }
+  for (int i = 0; i < 8; ++i) local += hb[i];
   const uint32_t suf = block_suffix_sum(local, sh4);  // visible scores in bins >= 8*tid
   if (tid == 0) {
     s_misc[0] = suf;
@@ -87,6 +83,21 @@ __device__ __forceinline__ void row_threshold(const uint32_t* __restrict__ hrow,
     }
   }
   __syncthreads();
+}
+
+// 16-byte loads of this thread's 8 bins (a row's histogram is 8 KB, 16-byte aligned)
+__device__ __forceinline__ void load_bins(const uint32_t* __restrict__ hrow, uint32_t (&hb)[8]) {
+  const uint4 a = reinterpret_cast<const uint4*>(hrow)[2 * threadIdx.x];
+  const uint4 b = reinterpret_cast<const uint4*>(hrow)[2 * threadIdx.x + 1];
+  hb[0] = a.x; hb[1] = a.y; hb[2] = a.z; hb[3] = a.w;
+  hb[4] = b.x; hb[5] = b.y; hb[6] = b.z; hb[7] = b.w;
+}
+
+__device__ __forceinline__ void row_threshold(const uint32_t* __restrict__ hrow, int K, uint32_t* sh4,
+                                              uint32_t* s_misc) {
+  uint32_t hb[8];
+  load_bins(hrow, hb);
+  row_threshold_of(hb, K, sh4, s_misc);
 }
 
 // Many rows (chunked prefill): one block per row derives the row's threshold once, so
@@ -128,6 +139,10 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
   const int64_t c0 = (int64_t)blockIdx.x * kFilterColsPerBlock;
   const float* srow = scores + (int64_t)r * ncols;
   const int32_t* prow = CAND ? cand + (int64_t)r * ncols : nullptr;
+  // the row's histogram bins first: the threshold is derived while the scores are in flight
+  uint32_t hb[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  if (!CTL) load_bins(hist + (int64_t)r * kHistBins, hb);
+  __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the score loads (the counter retires in order)
   float sv[kPer];
   int32_t pv[kPer];
 #pragma unroll
@@ -146,7 +161,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
     beta = ctl[r].beta;
     __syncthreads();  // lhist2 zeroed before any block thread adds to it
   } else {
-    row_threshold(hist + (int64_t)r * kHistBins, K, sh4, s_misc);
+    row_threshold_of(hb, K, sh4, s_misc);
     beta = s_misc[1];
     if (blockIdx.x == 0 && tid == 0) {
       const uint32_t total = s_misc[0];
