@@ -420,8 +420,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     const int ic = i < kQItems ? i : kQItems - 1;
     qraw[it] = *reinterpret_cast<const uint4*>(qb + (int64_t)(ic / (D / 8)) * D + (ic % (D / 8)) * 8);
   }
-  if (!G16)
-    for (int i = tid; i < D; i += kAttThreads) s_scale[i] = scales[(int64_t)b * D + i];
+  // the channel scales: loaded now, stored to LDS once the entry selection is done (a store
+  // now would wait for them, and with them for the query loads, before the selection starts)
+  static_assert(CSA2_MAX_D_DEV <= kAttThreads, "one channel scale per thread");
+  const float sc_reg = (!G16 && tid < D) ? scales[(int64_t)b * D + tid] : 0.0f;
   const int32_t* sel;                           // the split's entries (LDS)
   if (FROM_CAND) {
     FinalizeSmem& fs = *reinterpret_cast<FinalizeSmem*>(s_u);
@@ -440,6 +442,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     }
     sel = s_idx;
   }
+  if (!G16 && tid < D) s_scale[tid] = sc_reg;
   __syncthreads();  // s_scale, s_idx
 
   // ---- phase 1a: issue this wave's QK row loads now, so that their latency overlaps the

@@ -139,20 +139,21 @@ __device__ uint64_t tied_threshold(const SRC& src, uint32_t n, uint32_t need, ui
 // The candidates are in `nreg` regions of kFilterColsPerBlock pairs (counts in cnt);
 // SORTED: the list is in ascending position order (no candidate map).
 template <int NT, bool SORTED>
-__device__ int finalize_row(const uint2* __restrict__ regions, const uint32_t* __restrict__ cnt, int nreg,
+__device__ __forceinline__ int finalize_row(const uint2* __restrict__ regions, const uint32_t* __restrict__ cnt, int nreg,
                             const uint32_t* __restrict__ h2row, uint32_t beta, uint32_t above, uint32_t keff,
                             FinalizeSmem& sm, int32_t* out_pos, uint32_t* out_key) {
   constexpr int kWaves = NT / 64;
   constexpr int kCompPer = 64 / kWaves;  // list items per thread and compaction pass
   static_assert(kCompPer * kWaves == 64 && kCompPer >= 1, "one wave scans the (pass, wave) counts");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (keff == 0) return 0;
-  // the second-level histogram is loaded first: its latency overlaps the count prefix
+  // the second-level histogram is loaded first (before anything waits for the row's
+  // control values): its latency overlaps the count prefix
   constexpr int kPer = (kHistBins / NT > 0) ? kHistBins / NT : 1;  // bins per thread
   constexpr int kT = kHistBins / kPer;                               // threads holding bins
   uint32_t hb[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) hb[i] = (tid < kT) ? h2row[tid * kPer + i] : 0u;
+  if (keff == 0) return 0;
   // 0. region starts: exclusive prefix of the per-region counts (one wave when there are
   //    at most 64 regions, else one load per thread per pass; nreg <= kFinMaxRegions)
   if (nreg <= 64) {
