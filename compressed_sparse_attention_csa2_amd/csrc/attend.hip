@@ -35,8 +35,10 @@ constexpr int kAttHeads = 16;      // heads per block (MFMA M)
 constexpr int kAttWaves = 16;      // four waves per SIMD
 constexpr int kAttThreads = 64 * kAttWaves;
 constexpr int kAttSplit = 512;     // entries per block: the pages' Top-512 in one block, no merge
-constexpr int kAttTPW = kAttSplit / 16 / kAttWaves;  // 16-entry QK tiles per wave
-static_assert(kAttTPW * 16 * kAttWaves == kAttSplit, "QK tiles cover the split");
+constexpr int kQKW = 8;            // waves that compute logits (each reads the whole query
+                                   // operand from LDS once, so fewer, longer waves read less)
+constexpr int kAttTPW = kAttSplit / 16 / kQKW;  // 16-entry QK tiles per QK wave
+static_assert(kAttTPW * 16 * kQKW == kAttSplit, "QK tiles cover the split");
 
 // partials: part_o [R][P][Hq][D] normalised outputs, part_ml [R][P][Hq][2] (max, sum); P
 // = the splits of the selected entries, plus one slot for the sliding window
@@ -475,11 +477,13 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
       if (j < 0) gsw[it] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
+  const bool qk_wave = wave < kQKW;            // wave-uniform
+  const int qw = wave % kQKW;
   uint4 kw[kAttTPW][kCT];
   int32_t jt[kAttTPW];
 #pragma unroll
   for (int t = 0; t < kAttTPW; ++t) {
-    const int e = (wave * kAttTPW + t) * 16 + n16;
+    const int e = (qw * kAttTPW + t) * 16 + n16;
     jt[t] = sel[e];  // -1 past K
     if constexpr (G16) {
       const uint8_t* rowp = cb + (int64_t)(jt[t] >= 0 ? jt[t] : 0) * kRowBytes + 16 * g;
@@ -571,12 +575,12 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
 #pragma unroll
   for (int t = 0; t < kAttTPW; ++t) a[t] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < kCT; ++i) {
+  for (int i = 0; i < (qk_wave ? kCT : 0); ++i) {
     uint32_t wd[kAttTPW][4];
     _Float16 gs[kAttTPW][2];
 #pragma unroll
     for (int t = 0; t < kAttTPW; ++t) {
-      const int el = (wave * kAttTPW + t) * 16 + n16;  // this lane's entry in the split
+      const int el = (qw * kAttTPW + t) * 16 + n16;  // this lane's entry in the split
       uint4 kv;
       if constexpr (G16) kv = kw[t][i];
       else kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
@@ -601,7 +605,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
 #pragma unroll
   for (int t = 0; t < kAttTPW; ++t)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (jt[t] >= 0) ? a[t][rr] * s_down[4 * g + rr] : kNegInf;
+    for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (qk_wave && jt[t] >= 0) ? a[t][rr] * s_down[4 * g + rr] : kNegInf;
 
   // ---- phase 3a: read the PV code words now (staged rows in LDS; G16: global loads, cache
   //      hits since the rows were just read) so that they arrive during the softmax.  Wave
@@ -650,10 +654,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     const float m = s_m[h];
     float v = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kAttTPW; ++t) {
+    for (int t = 0; t < (qk_wave ? kAttTPW : 0); ++t) {
       const float p = (m == kNegInf) ? 0.0f : __expf(logit[t][rr] - m);
       const _Float16 ph = (_Float16)p;
-      sP[h * L::kPpad + (wave * kAttTPW + t) * 16 + n16] = __builtin_bit_cast(uint16_t, ph);
+      sP[h * L::kPpad + (qw * kAttTPW + t) * 16 + n16] = __builtin_bit_cast(uint16_t, ph);
       v += p;
     }
     v = row16_sum(v);
