@@ -21,7 +21,7 @@
 
 namespace csa2 {
 
-constexpr int kFinStage = 4096;   // candidates staged in LDS; longer lists are read from global memory
+constexpr int kFinStage = 8192;   // candidates staged in LDS; longer lists are read from global memory
 constexpr int kFinCap = 1024;     // tied candidates held in LDS; more are re-read from the list
 constexpr int kFinRankMax = 256;  // tied sets up to this size are resolved by rank counting
 constexpr int kFinMaxRegions = 4096;
