@@ -35,10 +35,6 @@ constexpr int kAttHeads = 16;      // heads per block (MFMA M)
 constexpr int kAttWaves = 16;      // four waves per SIMD
 constexpr int kAttThreads = 64 * kAttWaves;
 constexpr int kAttSplit = 512;     // entries per block: the pages' Top-512 in one block, no merge
-constexpr int kQKW = 8;            // waves that compute logits (each reads the whole query
-                                   // operand from LDS once, so fewer, longer waves read less)
-constexpr int kAttTPW = kAttSplit / 16 / kQKW;  // 16-entry QK tiles per QK wave
-static_assert(kAttTPW * 16 * kQKW == kAttSplit, "QK tiles cover the split");
 
 // partials: part_o [R][P][Hq][D] normalised outputs, part_ml [R][P][Hq][2] (max, sum); P
 // = the splits of the selected entries, plus one slot for the sliding window
@@ -372,6 +368,12 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     const float* __restrict__ wscales, int64_t wn_max, const int32_t* __restrict__ wend, int window) {
   constexpr int kRowBytes = D / 2;
   constexpr int kCT = D / 128;                 // 128-channel tiles
+  // waves that compute logits: per-channel, 8 waves of 4 tiles (each QK wave reads the whole
+  // query operand from LDS once, so fewer, longer waves read less); G16, all 16 waves (its
+  // operands come from global memory, and more waves issue those loads faster)
+  constexpr int kQKW = G16 ? kAttWaves : 8;
+  constexpr int kAttTPW = kAttSplit / 16 / kQKW;  // 16-entry QK tiles per QK wave
+  static_assert(kAttTPW * 16 * kQKW == kAttSplit, "QK tiles cover the split");
   constexpr int kWPT = (kAttWaves / kCT < kAttSplit / 32) ? kAttWaves / kCT : kAttSplit / 32;  // waves per tile in PV
   // per-channel layout: the split's rows are gathered whole (a wave instruction reads
   // kRPI complete rows, 16 bytes per lane) and staged in LDS; chunk c of entry e sits in
