@@ -125,12 +125,12 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
                                                      RowCtl* __restrict__ ctl, uint2* __restrict__ candbuf,
                                                      uint32_t* __restrict__ cnt) {
   constexpr int kWaves = kSelThreads / 64;
-  constexpr int kPer = kFilterColsPerBlock / kSelThreads;  // 16 columns per thread
+  constexpr int kPer = kFilterColsPerBlock / kSelThreads;  // 8 columns per thread
   __shared__ uint32_t lhist2[kHistBins];
   __shared__ uint32_t sh4[kWaves];
   __shared__ uint32_t s_misc[8];
   __shared__ uint32_t s_off[kPer * kWaves];  // candidates before (column pass i, wave w)
-  static_assert(kPer * kWaves == 64, "one wave scans the (pass, wave) counts");
+  static_assert(kPer * kWaves <= 64, "one wave scans the (pass, wave) counts");
   const int r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -197,11 +197,11 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
     s_off[lane * kWaves + wave] = n;
   }
   __syncthreads();
-  if (wave == 0) {  // exclusive scan over the kPer * kWaves (= 64) counts in (pass, wave) order
-    const uint32_t v = s_off[lane];
+  if (wave == 0) {  // exclusive scan over the kPer * kWaves (= 32) counts in (pass, wave) order
+    const uint32_t v = (lane < kPer * kWaves) ? s_off[lane] : 0u;
     const uint32_t sfx = wave_suffix(v);
     const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 0);
-    s_off[lane] = tot - sfx;
+    if (lane < kPer * kWaves) s_off[lane] = tot - sfx;
     if (lane == 0) s_misc[2] = tot;
   }
   __syncthreads();

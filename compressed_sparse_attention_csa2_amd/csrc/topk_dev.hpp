@@ -24,8 +24,8 @@ namespace csa2 {
 constexpr int kFinStage = 8192;   // candidates staged in LDS; longer lists are read from global memory
 constexpr int kFinCap = 1024;     // tied candidates held in LDS; more are re-read from the list
 constexpr int kFinRankMax = 256;  // tied sets up to this size are resolved by rank counting
-constexpr int kFinMaxRegions = 4096;
-constexpr int kFilterColsPerBlock = 4096;  // columns (and candidate slots) per filter block
+constexpr int kFinMaxRegions = 8192;
+constexpr int kFilterColsPerBlock = 2048;  // columns (and candidate slots) per filter block
 
 __device__ __forceinline__ uint32_t hist2_bin(uint32_t key) { return (key >> (32 - 2 * kHistBits)) & (kHistBins - 1); }
 
