@@ -37,7 +37,7 @@ inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int dev_status(int rc) { return rc ? CSA2_ERR_DEVICE : CSA2_OK; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Top-K columns per row this build handles (the finaliser keeps per-region counts in LDS)
-constexpr int64_t kMaxTopkCols = (int64_t)kFinMaxRegions * kFilterColsPerBlock;
+constexpr int64_t kMaxTopkCols = (int64_t)kFinMaxRegions * kFilterColsNarrow;
 
 // Bump allocator over the caller's workspace.
 struct Carve {
@@ -58,8 +58,8 @@ size_t topk_zero_bytes(int64_t R) {
   return 2 * align256((size_t)R * kHistBins * 4) + align256((size_t)R * sizeof(RowCtl));
 }
 size_t cand_bytes(int64_t R, int64_t ncols) {
-  const int64_t nreg = topk_regions(ncols);
-  return align256((size_t)R * nreg * kFilterColsPerBlock * sizeof(uint2)) + align256((size_t)R * nreg * 4);
+  const int64_t nreg = topk_regions((int)R, ncols);
+  return align256((size_t)R * nreg * topk_region_cols((int)R) * sizeof(uint2)) + align256((size_t)R * nreg * 4);
 }
 size_t topk_ws(int64_t R, int64_t ncols) { return topk_zero_bytes(R) + cand_bytes(R, ncols); }
 struct TopkWs {
@@ -74,9 +74,9 @@ struct CandWs {
   uint32_t* cnt;
 };
 CandWs carve_cand(Carve& c, int64_t R, int64_t ncols) {
-  const int64_t nreg = topk_regions(ncols);
+  const int64_t nreg = topk_regions((int)R, ncols);
   CandWs w;
-  w.cand = c.take<uint2>((size_t)R * nreg * kFilterColsPerBlock);
+  w.cand = c.take<uint2>((size_t)R * nreg * topk_region_cols((int)R));
   w.cnt = c.take<uint32_t>((size_t)R * nreg);
   return w;
 }
@@ -132,7 +132,8 @@ AttendArgs attend_args(int B, int T, int Hq, int D, int K, const void* q, int q_
   a.q = q; a.q_bf16 = (q_dtype == CSA2_BF16);
   a.codes = codes; a.scales = scales; a.g16 = (kv_fmt == CSA2_FMT_FP4_G16); a.n_max = n_max; a.idx = idx;
   a.softmax_scale = softmax_scale; a.out = out; a.out_bf16 = (out_dtype == CSA2_BF16); a.lse = lse;
-  a.ctl = nullptr; a.hist2 = nullptr; a.candbuf = nullptr; a.cnt = nullptr; a.nreg = 0; a.idx_out = nullptr;
+  a.ctl = nullptr; a.hist2 = nullptr; a.candbuf = nullptr; a.cnt = nullptr; a.nreg = 0; a.rstride = 0;
+  a.idx_out = nullptr;
   a.part = nullptr;
   a.swa_codes = nullptr; a.swa_scales = nullptr; a.swa_n_max = 0; a.swa_end = nullptr; a.window = 0;
   return a;
@@ -524,7 +525,8 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
       if (launch_topk_filter((int)R, ncols, scores, cand, c->K, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st))
         return CSA2_ERR_DEVICE;
       if (a.q_bf16) {
-        a.ctl = t.ctl; a.hist2 = t.hist2; a.candbuf = cw.cand; a.cnt = cw.cnt; a.nreg = topk_regions(ncols);
+        a.ctl = t.ctl; a.hist2 = t.hist2; a.candbuf = cw.cand; a.cnt = cw.cnt; a.nreg = topk_regions((int)R, ncols);
+        a.rstride = topk_region_cols((int)R);
         a.idx_out = L.idx;
       } else {
         if (launch_topk_finalize((int)R, ncols, c->K, true, t.ctl, t.hist2, cw.cand, cw.cnt, L.idx, nullptr, st))

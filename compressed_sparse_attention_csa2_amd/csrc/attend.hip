@@ -363,7 +363,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     int T, int Hq, int K, int S, int P, const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const void* __restrict__ scales_v, int64_t n_max, const int32_t* __restrict__ idx, const RowCtl* __restrict__ ctl,
     const uint32_t* __restrict__ hist2, const uint2* __restrict__ candbuf, const uint32_t* __restrict__ cnt, int nreg,
-    int32_t* __restrict__ idx_out, float softmax_scale, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
+    int rstride, int32_t* __restrict__ idx_out, float softmax_scale, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
     float* __restrict__ part, float* __restrict__ part_ml, const uint8_t* __restrict__ wcodes,
     const float* __restrict__ wscales, int64_t wn_max, const int32_t* __restrict__ wend, int window) {
   constexpr int kRowBytes = D / 2;
@@ -432,8 +432,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   if (FROM_CAND) {
     FinalizeSmem& fs = *reinterpret_cast<FinalizeSmem*>(s_u);
     const RowCtl c = ctl[r];
-    const int keff = finalize_row<kAttThreads, true>(candbuf + (int64_t)r * nreg * kFilterColsPerBlock,
-                                               cnt + (int64_t)r * nreg, nreg, hist2 + (int64_t)r * kHistBins, c.beta,
+    const int keff = finalize_row<kAttThreads, true>(candbuf + (int64_t)r * nreg * rstride,
+                                               cnt + (int64_t)r * nreg, nreg, rstride, hist2 + (int64_t)r * kHistBins, c.beta,
                                                c.above, c.keff, fs, s_idx, nullptr);
     for (int i = keff + tid; i < S * kAttSplit; i += kAttThreads) s_idx[i] = -1;  // pad to whole splits
     sel = s_idx + e0;  // the row's indices are stored at the end (a global store before a
@@ -960,7 +960,7 @@ static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
   float* part_ml = a.part ? a.part + (size_t)a.B * a.T * P * a.Hq * D : nullptr;
   hipLaunchKernelGGL((k_attend_part<D, FC, G16>), g, dim3(kAttThreads), 0, st, a.T, a.Hq, a.K, S, P,
                      (const uint16_t*)a.q, a.codes, a.scales, a.n_max, a.idx, a.ctl, a.hist2, a.candbuf, a.cnt,
-                     a.nreg, a.idx_out, a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml, a.swa_codes,
+                     a.nreg, a.rstride, a.idx_out, a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml, a.swa_codes,
                      a.swa_scales, a.swa_n_max, a.swa_end, a.window);
   if (P > 1)
     hipLaunchKernelGGL(k_attend_combine<D>, dim3(a.Hq / kAttHeads * (D / 128), a.B * a.T), dim3(256), 0, st, a.T,

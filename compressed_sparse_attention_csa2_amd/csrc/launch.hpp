@@ -62,8 +62,9 @@ int launch_topk_hist(int R, int64_t ncols, const float* scores, const int32_t* c
 int launch_block_max(int R, int64_t ncols, int block, const float* scores, float* bmax, uint32_t* hist,
                      hipStream_t st);
 // hist2 [R][kHistBins]: second-level histogram of the threshold bin (zeroed on entry).
-// candbuf [R][regions][kFilterColsPerBlock] and cnt [R][regions], regions = topk_regions.
-int topk_regions(int64_t ncols);
+// candbuf [R][regions][topk_region_cols(R)] and cnt [R][regions], regions = topk_regions.
+int topk_region_cols(int R);
+int topk_regions(int R, int64_t ncols);
 int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const uint32_t* hist,
                        uint32_t* hist2, RowCtl* ctl, uint2* candbuf, uint32_t* cnt, hipStream_t st);
 // sorted: the candidates were filtered without a candidate map (list in position order)
@@ -90,9 +91,10 @@ struct AttendArgs {
   // MFMA path only: take the Top-K from the candidate list (candbuf != nullptr) instead of idx
   const RowCtl* ctl;
   const uint32_t* hist2;
-  const uint2* candbuf;   // [R][nreg][kFilterColsPerBlock]
+  const uint2* candbuf;   // [R][nreg][rstride]
   const uint32_t* cnt;    // [R][nreg]
   int nreg;
+  int rstride;            // columns (candidate slots) per region
   int32_t* idx_out;   // written when taking the Top-K from candidates (nullable)
   float* part;        // MFMA path with more than one partial: partial results (attend_ws_floats)
   // sliding window (swa_codes null: none): E4M3 rows [B][swa_n_max][D], scales [B][swa_n_max]

@@ -118,6 +118,8 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_threshold(int K, const uin
 
 // CTL: the row's threshold was computed by k_topk_threshold (read ctl); otherwise every
 // block derives it from the histogram and block 0 of the row writes ctl.
+// Regions: kFilterColsPerBlock columns with CTL (many rows), kFilterColsNarrow otherwise
+// (twice the blocks for the few rows of a decode step).
 template <bool CAND, bool CTL>
 __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float* __restrict__ scores,
                                                      const int32_t* __restrict__ cand, int K,
@@ -125,7 +127,8 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
                                                      RowCtl* __restrict__ ctl, uint2* __restrict__ candbuf,
                                                      uint32_t* __restrict__ cnt) {
   constexpr int kWaves = kSelThreads / 64;
-  constexpr int kPer = kFilterColsPerBlock / kSelThreads;  // 8 columns per thread
+  constexpr int kCols = CTL ? kFilterColsPerBlock : kFilterColsNarrow;
+  constexpr int kPer = kCols / kSelThreads;  // 16 or 8 columns per thread
   __shared__ uint32_t lhist2[kHistBins];
   __shared__ uint32_t sh4[kWaves];
   __shared__ uint32_t s_misc[8];
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
 
   // the scores of this block's columns (all loads first, branch-free, clamped); pass i,
   // wave w, lane l holds column c0 + 256 i + 64 w + l, so (i, w, l) order is column order
-  const int64_t c0 = (int64_t)blockIdx.x * kFilterColsPerBlock;
+  const int64_t c0 = (int64_t)blockIdx.x * kCols;
   const float* srow = scores + (int64_t)r * ncols;
   const int32_t* prow = CAND ? cand + (int64_t)r * ncols : nullptr;
   // the row's histogram bins first: the threshold is derived while the scores are in flight
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
     s_off[lane * kWaves + wave] = n;
   }
   __syncthreads();
-  if (wave == 0) {  // exclusive scan over the kPer * kWaves (= 32) counts in (pass, wave) order
+  if (wave == 0) {  // exclusive scan over the kPer * kWaves (64 or 32) counts in (pass, wave) order
     const uint32_t v = (lane < kPer * kWaves) ? s_off[lane] : 0u;
     const uint32_t sfx = wave_suffix(v);
     const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 0);
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
   const uint32_t nloc = s_misc[2];
   if (tid == 0) cnt[(int64_t)r * nreg + blockIdx.x] = nloc;
   if (nloc == 0) return;
-  uint2* creg = candbuf + ((int64_t)r * nreg + blockIdx.x) * kFilterColsPerBlock;
+  uint2* creg = candbuf + ((int64_t)r * nreg + blockIdx.x) * kCols;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if ((bal[i] >> lane) & 1ull) {
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
 // null.  With rps > 1 query rows per sequence, row t of a sequence stops at n_keys - (rps -
 // 1 - t).
 template <bool SORTED, bool EXPAND>
-__global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, const RowCtl* __restrict__ ctl,
+__global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int rstride, int K, const RowCtl* __restrict__ ctl,
                                                                const uint32_t* __restrict__ hist2,
                                                                const uint2* __restrict__ candbuf,
                                                                const uint32_t* __restrict__ cnt,
@@ -241,8 +244,8 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_finalize(int nreg, int K, 
   __shared__ uint32_t s_key[CSA2_MAX_K_DEV];
   const int r = blockIdx.x;
   const RowCtl c = ctl[r];
-  const int keff = finalize_row<kFinThreads, SORTED>(candbuf + (int64_t)r * nreg * kFilterColsPerBlock,
-                                                     cnt + (int64_t)r * nreg, nreg, hist2 + (int64_t)r * kHistBins,
+  const int keff = finalize_row<kFinThreads, SORTED>(candbuf + (int64_t)r * nreg * rstride,
+                                                     cnt + (int64_t)r * nreg, nreg, rstride, hist2 + (int64_t)r * kHistBins,
                                                      c.beta, c.above, c.keff, sm, s_pos, s_key);
   for (int i = threadIdx.x; i < K; i += kFinThreads) {
     const bool have = i < keff;
@@ -336,15 +339,20 @@ int launch_topk_hist(int R, int64_t ncols, const float* scores, const int32_t* c
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int topk_regions(int64_t ncols) { return (int)((ncols + kFilterColsPerBlock - 1) / kFilterColsPerBlock); }
-
 // Rows from which the threshold is computed once per row in its own kernel rather than
-// in every filter block (many rows: the histogram re-reads would cost more than a launch).
+// in every filter block (many rows: the histogram re-reads would cost more than a launch);
+// those filter blocks also take the wider regions.
 constexpr int kThresholdKernelRows = 64;
+
+int topk_region_cols(int R) { return R >= kThresholdKernelRows ? kFilterColsPerBlock : kFilterColsNarrow; }
+int topk_regions(int R, int64_t ncols) {
+  const int c = topk_region_cols(R);
+  return (int)((ncols + c - 1) / c);
+}
 
 int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const uint32_t* hist,
                        uint32_t* hist2, RowCtl* ctl, uint2* candbuf, uint32_t* cnt, hipStream_t st) {
-  dim3 g((unsigned)topk_regions(ncols), R);
+  dim3 g((unsigned)topk_regions(R, ncols), R);
   const bool pre = R >= kThresholdKernelRows;
   if (pre) hipLaunchKernelGGL(k_topk_threshold, dim3(R), dim3(kSelThreads), 0, st, K, hist, ctl);
 #define CSA2_FILTER(C, P)                                                                                      \
@@ -362,9 +370,10 @@ int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t*
 int launch_topk_finalize(int R, int64_t ncols, int K, bool sorted, const RowCtl* ctl, const uint32_t* hist2,
                          const uint2* candbuf, const uint32_t* cnt, int32_t* idx_out, float* val_out, hipStream_t st,
                          int block, const int32_t* n_keys, int32_t* expand_out, int rps) {
-  const int nreg = topk_regions(ncols);
+  const int nreg = topk_regions(R, ncols);
 #define CSA2_FIN(S, E)                                                                                          \
-  hipLaunchKernelGGL((k_topk_finalize<S, E>), dim3(R), dim3(kFinThreads), 0, st, nreg, K, ctl, hist2, candbuf, cnt, \
+  hipLaunchKernelGGL((k_topk_finalize<S, E>), dim3(R), dim3(kFinThreads), 0, st, nreg, topk_region_cols(R), K, ctl, \
+                     hist2, candbuf, cnt,                                                                        \
                      idx_out, val_out, block, n_keys, expand_out, rps)
   if (expand_out) {
     if (!sorted) return -1;  // block selections come from a list without a candidate map

@@ -25,7 +25,8 @@ constexpr int kFinStage = 8192;   // candidates staged in LDS; longer lists are 
 constexpr int kFinCap = 1024;     // tied candidates held in LDS; more are re-read from the list
 constexpr int kFinRankMax = 256;  // tied sets up to this size are resolved by rank counting
 constexpr int kFinMaxRegions = 8192;
-constexpr int kFilterColsPerBlock = 2048;  // columns (and candidate slots) per filter block
+constexpr int kFilterColsPerBlock = 4096;  // columns (and candidate slots) per filter block, many rows
+constexpr int kFilterColsNarrow = 2048;    // the same for a few (decode) rows: twice the blocks
 
 __device__ __forceinline__ uint32_t hist2_bin(uint32_t key) { return (key >> (32 - 2 * kHistBits)) & (kHistBins - 1); }
 
@@ -41,18 +42,20 @@ struct FinalizeSmem {
 };
 
 // A row's candidates: the filter block b of the row wrote cnt[b] pairs at regions +
-// b * kFilterColsPerBlock; `start` (LDS) is the exclusive prefix of the counts.
+// b * stride (the columns a filter block covers); `start` (LDS) is the exclusive prefix of
+// the counts.
 struct CandList {
   const uint2* regions;
   const uint32_t* start;
   int nreg;
+  int stride;
   __device__ __forceinline__ uint2 get(uint32_t i) const {
     int lo = 0, hi = nreg - 1;  // last region whose start <= i
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (start[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    return regions[(int64_t)lo * kFilterColsPerBlock + (i - start[lo])];
+    return regions[(int64_t)lo * stride + (i - start[lo])];
   }
 };
 
@@ -136,11 +139,11 @@ __device__ uint64_t tied_threshold(const SRC& src, uint32_t n, uint32_t need, ui
 
 // Writes the keff winners' positions (ascending) to out_pos[0..keff) and, if out_key !=
 // nullptr, their order keys; returns keff.  All threads of the block must call it.
-// The candidates are in `nreg` regions of kFilterColsPerBlock pairs (counts in cnt);
+// The candidates are in `nreg` regions of `rstride` pairs (counts in cnt);
 // SORTED: the list is in ascending position order (no candidate map).
 template <int NT, bool SORTED>
 __device__ __forceinline__ int finalize_row(const uint2* __restrict__ regions, const uint32_t* __restrict__ cnt, int nreg,
-                            const uint32_t* __restrict__ h2row, uint32_t beta, uint32_t above, uint32_t keff,
+                            int rstride, const uint32_t* __restrict__ h2row, uint32_t beta, uint32_t above, uint32_t keff,
                             FinalizeSmem& sm, int32_t* out_pos, uint32_t* out_key) {
   constexpr int kWaves = NT / 64;
   constexpr int kCompPer = 64 / kWaves;  // list items per thread and compaction pass
@@ -182,7 +185,7 @@ __device__ __forceinline__ int finalize_row(const uint2* __restrict__ regions, c
     __syncthreads();
   }
   const uint32_t M = sm.misc[4];
-  const CandList list{regions, sm.start, nreg};
+  const CandList list{regions, sm.start, nreg, rstride};
   // 1. issue the loads that stage the candidates in LDS (all in flight, clamped,
   //    branch-free); they are stored after the second-level scan, which hides them
   constexpr int kStagePer = kFinStage / NT;
