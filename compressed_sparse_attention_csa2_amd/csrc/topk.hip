@@ -5,7 +5,8 @@
 //
 // Distributed radix select over three launches, no fence or grid-wide wait inside a
 // kernel (on MI355X an agent-scope release writes back the XCD's whole L2, which made
-// in-kernel hand-offs between blocks cost tens of microseconds):
+// in-kernel hand-offs between blocks cost tens of microseconds, and blocks polling a
+// counter with device-scope loads slowed the score blocks still streaming up to 4x):
 //   1. the score kernel (or k_topk_hist) adds every visible score's top 11 key bits to a
 //      per-row histogram (LDS histogram per block, then one atomic per non-empty bin);
 //   2. k_topk_filter: every block derives from the complete histogram the bin holding the
