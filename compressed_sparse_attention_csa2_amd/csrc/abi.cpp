@@ -471,7 +471,6 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   Carve cv(ws);
   TopkWs tz[64];
   for (int i = 0; i < slots; ++i) tz[i] = carve_topk_zero(cv, R);
-  const size_t zero_bytes = cv.off;
   float* scores = cv.take<float>((size_t)R * group_cols(c));
   CandWs cw = carve_cand(cv, R, group_cols(c));
   float* part =
@@ -482,13 +481,17 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   int32_t* q_limit = T > 1 ? cv.take<int32_t>((size_t)R) : nullptr;
   hipStream_t st = S(stream);
   if (q_limit && launch_causal_limits(c->B, T, c->n_keys, q_limit, st)) return CSA2_ERR_DEVICE;
-  // one fill clears every selection's histograms and control words (more than 64 selections
-  // reuse the last slot, cleared again before each reuse)
-  if (slots > 0 && launch_fill_u32(tz[0].hist, (int64_t)(zero_bytes / 4), 0u, st)) return CSA2_ERR_DEVICE;
+  // the first selection's histograms and control words are cleared here; the filter of
+  // each selection clears the slot the next one takes (more than 64 selections reuse the
+  // last slot, cleared again before each reuse)
+  const int64_t slot_words = (int64_t)(topk_zero_bytes(R) / 4);
+  if (slots > 0 && launch_fill_u32(tz[0].hist, slot_words, 0u, st)) return CSA2_ERR_DEVICE;
   int si = 0;
+  uint32_t* next_clear = nullptr;  // the slot after the one handed out last (nullptr: none)
   auto next_slot = [&](TopkWs& t) -> int {
     t = tz[si < slots ? si : slots - 1];
     const bool reuse = si >= slots;
+    next_clear = (si + 1 < slots) ? tz[si + 1].hist : nullptr;
     ++si;
     return reuse ? zero_topk(t, R, st) : 0;
   };
@@ -522,7 +525,8 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
       // Reindex layers read only the pool's positions and the cached scan measured slower.
       sa.keep = (L.mode == CSA2_FULL) && !pooled && reindex_after(layers, n_layers, i);
       if (launch_score(sa, st)) return CSA2_ERR_DEVICE;
-      if (launch_topk_filter((int)R, ncols, scores, cand, c->K, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st))
+      if (launch_topk_filter((int)R, ncols, scores, cand, c->K, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st,
+                             next_clear, next_clear ? slot_words : 0))
         return CSA2_ERR_DEVICE;
       if (a.q_bf16) {
         a.ctl = t.ctl; a.hist2 = t.hist2; a.candbuf = cw.cand; a.cnt = cw.cnt; a.nreg = topk_regions((int)R, ncols);
@@ -544,7 +548,8 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
       if (next_slot(t)) return CSA2_ERR_DEVICE;
       int32_t* dst = L.pool ? L.pool : pool;
       if (launch_block_max((int)R, c->n_max, c->pool_block, scores, bmax, t.hist, st)) return CSA2_ERR_DEVICE;
-      if (launch_topk_filter((int)R, nb, bmax, nullptr, c->pool_blocks, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st))
+      if (launch_topk_filter((int)R, nb, bmax, nullptr, c->pool_blocks, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st,
+                             next_clear, next_clear ? slot_words : 0))
         return CSA2_ERR_DEVICE;
       if (launch_topk_finalize((int)R, nb, c->pool_blocks, true, t.ctl, t.hist2, cw.cand, cw.cnt, nullptr, nullptr, st,
                                c->pool_block, c->n_keys, dst, T))

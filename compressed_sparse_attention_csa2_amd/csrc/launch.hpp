@@ -65,8 +65,11 @@ int launch_block_max(int R, int64_t ncols, int block, const float* scores, float
 // candbuf [R][regions][topk_region_cols(R)] and cnt [R][regions], regions = topk_regions.
 int topk_region_cols(int R);
 int topk_regions(int R, int64_t ncols);
+// clear (nullable, 16-byte aligned, clear_words a multiple of 4): words the filter blocks
+// zero on the side (the next selection's histograms and control words)
 int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const uint32_t* hist,
-                       uint32_t* hist2, RowCtl* ctl, uint2* candbuf, uint32_t* cnt, hipStream_t st);
+                       uint32_t* hist2, RowCtl* ctl, uint2* candbuf, uint32_t* cnt, hipStream_t st,
+                       uint32_t* clear = nullptr, int64_t clear_words = 0);
 // sorted: the candidates were filtered without a candidate map (list in position order)
 // expand_out (nullable, needs sorted): also write the selected blocks' positions (block
 // positions per selected column, -1 past n_keys[r] or for padding), [R][K * block]

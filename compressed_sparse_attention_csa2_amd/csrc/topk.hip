@@ -126,7 +126,8 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
                                                      const int32_t* __restrict__ cand, int K,
                                                      const uint32_t* __restrict__ hist, uint32_t* __restrict__ hist2,
                                                      RowCtl* __restrict__ ctl, uint2* __restrict__ candbuf,
-                                                     uint32_t* __restrict__ cnt) {
+                                                     uint32_t* __restrict__ cnt, uint4* __restrict__ clear,
+                                                     int64_t clear_n4) {
   constexpr int kWaves = kSelThreads / 64;
   constexpr int kCols = CTL ? kFilterColsPerBlock : kFilterColsNarrow;
   constexpr int kPer = kCols / kSelThreads;  // 16 or 8 columns per thread
@@ -137,6 +138,11 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
   static_assert(kPer * kWaves <= 64, "one wave scans the (pass, wave) counts");
   const int r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the next selection's histograms and control words, idle until then, are cleared here
+  // (saves the clearing kernel a launch per selection)
+  for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kSelThreads + tid; i < clear_n4;
+       i += (int64_t)gridDim.x * gridDim.y * kSelThreads)
+    clear[i] = make_uint4(0u, 0u, 0u, 0u);
 
   // the scores of this block's columns (all loads first, branch-free, clamped); pass i,
   // wave w, lane l holds column c0 + 256 i + 64 w + l, so (i, w, l) order is column order
@@ -352,13 +358,17 @@ int topk_regions(int R, int64_t ncols) {
 }
 
 int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t* cand, int K, const uint32_t* hist,
-                       uint32_t* hist2, RowCtl* ctl, uint2* candbuf, uint32_t* cnt, hipStream_t st) {
+                       uint32_t* hist2, RowCtl* ctl, uint2* candbuf, uint32_t* cnt, hipStream_t st,
+                       uint32_t* clear, int64_t clear_words) {
+  if (clear && ((reinterpret_cast<uintptr_t>(clear) & 15) || clear_words % 4)) return -1;
+  uint4* clear4 = clear ? reinterpret_cast<uint4*>(clear) : nullptr;
+  const int64_t clear_n4 = clear ? clear_words / 4 : 0;
   dim3 g((unsigned)topk_regions(R, ncols), R);
   const bool pre = R >= kThresholdKernelRows;
   if (pre) hipLaunchKernelGGL(k_topk_threshold, dim3(R), dim3(kSelThreads), 0, st, K, hist, ctl);
 #define CSA2_FILTER(C, P)                                                                                      \
   hipLaunchKernelGGL((k_topk_filter<C, P>), g, dim3(kSelThreads), 0, st, ncols, scores, cand, K, hist, hist2, ctl, \
-                     candbuf, cnt)
+                     candbuf, cnt, clear4, clear_n4)
   if (cand) {
     if (pre) CSA2_FILTER(true, true); else CSA2_FILTER(true, false);
   } else {
