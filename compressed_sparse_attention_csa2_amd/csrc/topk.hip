@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
   const int r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the next selection's histograms and control words, idle until then, are cleared here
-  // (saves the clearing kernel a launch per selection)
+  // (the caller's fill then clears only the first selection's)
   for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kSelThreads + tid; i < clear_n4;
        i += (int64_t)gridDim.x * gridDim.y * kSelThreads)
     clear[i] = make_uint4(0u, 0u, 0u, 0u);
