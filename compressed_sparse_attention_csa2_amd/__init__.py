@@ -141,10 +141,12 @@ _ws_cache: dict = {}
 
 
 def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
-    """A device byte buffer of at least nbytes (reused across calls on one stream)."""
+    """A device byte buffer of at least nbytes, one per (device, stream): calls on one
+    stream are ordered, so they may share it; a buffer that grows is released to torch's
+    allocator, which hands it out again only in that stream's order."""
     if nbytes == 0:
         return None
-    key = (str(device),)
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(nbytes, dtype=torch.uint8, device=device)

@@ -6,8 +6,8 @@ namespace csa2 {
 
 // out[r][k][c] = fl32(E2M1(code) * s_c) of cache row idx[r][k] (G16: the scale of the
 // entry's 16-channel group, E4M3); 0 for rows outside [0, n_max).  One thread per 8
-// channels.  ("values are dequantized back before attention": "FP4 Main KV Cache To
-// Halve Storage Again", paper notes.)
+// channels.  (The stored FP4 entries are turned back into real values before the
+// attention uses them: "FP4 Main KV Cache To Halve Storage Again", paper notes.)
 template <bool G16>
 __global__ __launch_bounds__(256) void k_gather_dequant(int T, int K, int D, const uint8_t* __restrict__ codes,
                                                         const void* __restrict__ scales_v, int64_t n_max,

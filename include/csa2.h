@@ -115,8 +115,9 @@ int csa2_quantize_kv(int fmt, int scale_policy, int B, int T, int D, const void*
                      void* scales, void* stream);
 
 /*
- * Gather + dequantise selected FP4 rows (the step before attention; "values are
- * dequantized back before attention" in "FP4 Main KV Cache To Halve Storage Again").
+ * Gather + dequantise selected FP4 rows (the step before attention: the stored FP4 entries
+ * are turned back into real values before attention, "FP4 Main KV Cache To Halve Storage
+ * Again").
  *   kv_fmt CSA2_FMT_FP4_PER_CHANNEL: out[b][t][k][c] = fl32(E2M1(code) * scales[b][c]),
  *     scales fp32 [B][D];
  *   kv_fmt CSA2_FMT_FP4_G16: out = E2M1(code) * E4M3(scales[b][j][c / 16]) (exact), scales

@@ -53,22 +53,27 @@ def _device_cache_with_samples(wl, sample):
 
 
 def _check_group_against_oracle(wl, modes, dev_layers, ref_cache, sample, q_in):
-    ref_layers = [dict(mode=m, q_idx=q_in[i][0][sample], w=q_in[i][1][sample], q_attn=q_in[i][2][sample])
-                  for i, m in enumerate(modes)]
-    R = oracle.layer_group(ref_layers, ref_cache, oracle.PREC_FP8, wl.K, wl.softmax_scale)
+    """Every layer of the sampled sequences: an indexing layer's selection by the near-tie
+    rule on the oracle's scores; every layer's output and log-sum-exp against the oracle's
+    attention over the index tensor the GPU layer attended (its own selection, or for
+    Reuse the last indexing layer's), so the outputs are always compared."""
     idx_last = None
-    exact = 0
-    for i, (L, Rl) in enumerate(zip(dev_layers, R)):
-        if L["mode"] != "reuse":
-            s = oracle.index_score(oracle.PREC_FP8, ref_layers[i]["q_idx"], ref_layers[i]["w"], ref_cache["k"],
-                                   ref_cache["k_scale"], ref_cache["n_keys"])
+    checked = 0
+    for i, (L, m) in enumerate(zip(dev_layers, modes)):
+        qi, w, qa = (x[sample] for x in q_in[i])
+        if m != "reuse":
+            s = oracle.index_score(oracle.PREC_FP8, qi, w, ref_cache["k"], ref_cache["k_scale"], ref_cache["n_keys"])
             idx_last = L["idx"].cpu().numpy()[sample]
-            exact += check_topk_near_tie(idx_last, s, wl.K)
+            check_topk_near_tie(idx_last, s, wl.K)
+        ro, rl = oracle.sparse_attend(qa, ref_cache["codes"], ref_cache["scales"], idx_last, wl.softmax_scale)
         out = L["out"].float().cpu().numpy()[sample]
+        lse = L["lse"].cpu().numpy()[sample]
         for j in range(len(sample)):
-            if np.array_equal(idx_last[j], Rl["idx"][j]):
-                assert _bf16_ok(out[j], Rl["out"][j]), (i, sample[j])
-    return exact
+            assert _bf16_ok(out[j], ro[j]), (i, sample[j])
+            assert np.allclose(lse[j], rl[j], rtol=0, atol=2e-3 * max(1.0, np.abs(rl[j]).max())), (i, sample[j])
+            checked += 1
+    assert checked == len(modes) * len(sample)
+    return checked
 
 
 def test_group128k_full_size_sampled_sequences():
@@ -236,15 +241,16 @@ def test_hier1m_full_size():
                                 wl.coarse_topk, wl.K, want_blocks=True)
     cs = oracle.index_score(oracle.PREC_FP8, q, w, kb_ref, kbs_ref, (nk + wl.coarse_block - 1) // wl.coarse_block)
     check_topk_near_tie(blk.cpu().numpy(), cs, wl.coarse_topk)
-    ref_idx, ref_blk = oracle.hier_select(q, w, kr, ksr, kb_ref, kbs_ref, nk, wl.coarse_block, wl.coarse_topk, wl.K)
     g_idx = idx.cpu().numpy()
-    if np.array_equal(blk.cpu().numpy(), ref_blk):
-        cand = oracle.expand_blocks(ref_blk, wl.coarse_block, nk)
-        fs = oracle.index_score(oracle.PREC_FP8, q, w, kr, ksr, nk, cand=cand)
-        full = np.full((1, 1, n), -np.inf)
-        c0 = cand[0, 0]
-        full[0, 0, c0[c0 >= 0]] = fs[0, 0][c0 >= 0]
-        check_topk_near_tie(g_idx, full, wl.K)
+    # the fine stage on the GPU's own block list (whatever blocks it kept within the near-tie
+    # band): near-tie rule on the oracle's scores of exactly those candidates, all inside them
+    cand = oracle.expand_blocks(blk.cpu().numpy(), wl.coarse_block, nk)
+    fs = oracle.index_score(oracle.PREC_FP8, q, w, kr, ksr, nk, cand=cand)
+    full = np.full((1, 1, n), -np.inf)
+    c0 = cand[0, 0]
+    full[0, 0, c0[c0 >= 0]] = fs[0, 0][c0 >= 0]
+    check_topk_near_tie(g_idx, full, wl.K)
+    assert np.all(np.isin(g_idx[g_idx >= 0], c0[c0 >= 0]))
     # attention over the GPU's selection on both sides
     qa = wl.attn_query()
     cr, sr = oracle.quantize_fp4(x[None])
