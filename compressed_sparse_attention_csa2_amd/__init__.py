@@ -36,8 +36,11 @@ EXPORTS = [
     "csa2_index_score_workspace_size", "csa2_topk", "csa2_topk_workspace_size", "csa2_index_topk",
     "csa2_index_topk_workspace_size", "csa2_sparse_attend", "csa2_sparse_attend_workspace_size",
     "csa2_layer_group", "csa2_layer_group_workspace_size", "csa2_coarse_keys", "csa2_hier_select",
-    "csa2_hier_select_workspace_size",
+    "csa2_hier_select_workspace_size", "csa2_layer_group_noalloc",
 ]
+
+# bytes of the library-held scratch array of csa2_layer_group_noalloc (one per GPU)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class Csa2Error(RuntimeError):
@@ -94,6 +97,7 @@ def lib() -> ctypes.CDLL:
             "csa2_sparse_attend_workspace_size": ([i, i, i, i, i, i, i], sz),
             "csa2_layer_group": ([p, i, p, p, sz, p], i),
             "csa2_layer_group_workspace_size": ([p, i], sz),
+            "csa2_layer_group_noalloc": ([p, i, p, p], i),
             "csa2_coarse_keys": ([i, i64, p, i, i, p, p, p, p, p], i),
             "csa2_hier_select": ([i, i, i, p, i, p, p, p, p, p, i64, p, i, i, i, p, p, p, sz, p], i),
             "csa2_hier_select_workspace_size": ([i, i64, i, i, i], sz),
@@ -315,7 +319,17 @@ def layer_group(layers: Sequence[dict], cache: GroupCache, out_dtype: Optional[t
     return GroupPlan(layers, cache, out_dtype).run()
 
 
-def _marshal_group(layers, cache, out_dtype):
+def layer_group_noalloc(layers: Sequence[dict], cache: GroupCache, out_dtype: Optional[torch.dtype] = None):
+    """layer_group through csa2_layer_group_noalloc: the library's own scratch array serves
+    as the workspace, so the call itself allocates no device memory (outputs missing from
+    the layer dicts are still created here, before the call)."""
+    arr, gc, _, _, swas = _marshal_group(layers, cache, out_dtype, workspace=False)
+    _check(lib().csa2_layer_group_noalloc(arr, len(layers), ctypes.byref(gc), _stream()), "csa2_layer_group_noalloc")
+    del swas  # the window structs stay alive until the call has returned
+    return layers
+
+
+def _marshal_group(layers, cache, out_dtype, workspace=True):
     first = layers[0]
     q_attn = first["q_attn"]
     B, T, Hq, D = q_attn.shape
@@ -347,7 +361,7 @@ def _marshal_group(layers, cache, out_dtype):
     qd = _dtype_code(q_attn)
     gc = cache.struct(H, dk, Hq, qd, _dtype_code(torch.empty(0, dtype=odt)), window, T)
     nb = lib().csa2_layer_group_workspace_size(ctypes.byref(gc), len(layers))
-    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=q_attn.device)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=q_attn.device) if workspace else None
     return arr, gc, ws, nb, swas
 
 

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["quant.hip", "score.hip", "topk.hip", "attend.hip", "misc.hip", "abi.cpp"]
+SOURCES = ["quant.hip", "score.hip", "topk.hip", "attend.hip", "misc.hip", "abi.cpp", "noalloc.hip"]
 HEADERS = ["common.hpp", "launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

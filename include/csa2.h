@@ -16,7 +16,8 @@
  * Conventions shared by every call:
  *   - Every pointer argument is a DEVICE pointer unless marked "host".  All calls are
  *     asynchronous on `stream` (a hipStream_t; NULL = the null stream).
- *   - The caller owns every buffer.  No call allocates, frees or retains device memory.
+ *   - The caller owns every buffer.  No call allocates, frees or retains device memory
+ *     (csa2_layer_group_noalloc uses a scratch array the library itself holds).
  *     Calls that take `ws` need a device workspace of at least the size the matching
  *     *_workspace_size() function reports; it needs no initialisation and its contents
  *     are undefined afterwards.  Calls that share one `ws` must be ordered on a stream.
@@ -293,6 +294,22 @@ typedef struct {
 int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_cache* cache, void* ws,
                      size_t ws_bytes, void* stream);
 size_t csa2_layer_group_workspace_size(const csa2_group_cache* cache, int n_layers);
+
+/*
+ * Layer group that allocates nothing, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments (less the workspace), validation and results as csa2_layer_group; the
+ * workspace is a device array of CSA2_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU the library runs on, held until the process ends (its address is looked up on the
+ * first call on each device).  No hipMalloc, hipFree or allocating library call is made.
+ * Errors: those of csa2_layer_group; CSA2_ERR_WORKSPACE when
+ * csa2_layer_group_workspace_size(cache, n_layers) exceeds CSA2_NOALLOC_SCRATCH_BYTES
+ * (nothing is launched).  All calls on one GPU share that GPU's array, which keeps the
+ * last call's contents (the call clears what must start at zero itself): calls that
+ * overlap on one GPU (other streams, other threads) race on it and must be ordered.
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES (64u << 20)
+int csa2_layer_group_noalloc(const csa2_layer* layers, int n_layers, const csa2_group_cache* cache, void* stream);
 
 /*
  * Two-level indexer, coarse keys: the mean of each `block` consecutive dequantised E4M3

@@ -139,6 +139,23 @@ def test_layer_group_pool_workspace_grows():
     assert L.csa2_layer_group_workspace_size(ctypes.byref(big), 4) >= 4 * 32768 * 4 * 2
 
 
+def test_layer_group_noalloc_validates_and_rejects_shapes_beyond_its_scratch():
+    """The no-allocation layer group returns csa2_layer_group's argument errors, and
+    CSA2_ERR_WORKSPACE for a shape whose workspace exceeds the library's scratch array,
+    both before any device call (so this runs without a GPU)."""
+    L = csa2.lib()
+    assert L.csa2_layer_group_noalloc(None, 1, None, None) == -1
+    arr = (csa2._Layer * 2)()
+    arr[0] = csa2._Layer(2, _p(), _p(), _p(), _p(), None, _p())  # Reuse first: invalid schedule
+    arr[1] = csa2._Layer(0, _p(), _p(), _p(), _p(), None, _p())
+    gc = csa2._GroupCache(16, 32, 64, 64, 512, 512, 1 << 22, _p(), _p(), _p(), _p(), _p(), 1, 1, 1, 0.04)
+    assert L.csa2_layer_group_noalloc(arr, 2, ctypes.byref(gc), None) == -4
+    arr[0] = csa2._Layer(0, _p(), _p(), _p(), _p(), None, _p())
+    arr[1] = csa2._Layer(2, _p(), _p(), _p(), _p(), None, _p())
+    assert L.csa2_layer_group_workspace_size(ctypes.byref(gc), 2) > csa2.NOALLOC_SCRATCH_BYTES
+    assert L.csa2_layer_group_noalloc(arr, 2, ctypes.byref(gc), None) == -5
+
+
 def test_product_path_does_not_import_oracle():
     pkg = os.path.join(ROOT, "compressed_sparse_attention_csa2_amd")
     for dirpath, _, files in os.walk(pkg):
