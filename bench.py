@@ -8,10 +8,14 @@ keys with a per-token fp32 scale, bf16 queries, head weights U(0,1); Top-512; ma
 64 attention heads, bf16 query and output.  Every layer draws its own queries/weights.
 
 A step is one pass of the whole decode path of the group (indexer scores, Top-K, gather +
-FP4 dequant + attention, for all three layers) through `csa2_layer_group`.  The cache is
-built once (FP4 / E4M3 quantisation on the GPU) and several copies are rotated between
-steps so that every step starts with its cache in HBM rather than in the 256 MB
-Infinity Cache.  Prints one JSON line.
+FP4 dequant + attention, for all three layers).  Two protocols are timed:
+
+* flushed (the headline): every layer is its own C-ABI call, a 512 MiB buffer is written
+  before each layer (evicting the 256 MB Infinity Cache and the L2s, as the other layers of
+  a real model would), and the step time is the sum of the per-layer HIP-event times.
+* warm: the whole group as one csa2_layer_group call, cache copies rotated between steps.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -31,6 +35,7 @@ import compressed_sparse_attention_csa2_amd as csa2  # noqa: E402
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 512 << 20  # written before every flushed layer: twice the 256 MB Infinity Cache
 SCORE_SOURCES = ("compressed_sparse_attention_csa2_amd/csrc/score.hip", "compressed_sparse_attention_csa2_amd/csrc/common.hpp",
                  "compressed_sparse_attention_csa2_amd/csrc/launch.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_fp8_group128k_hbm_traffic.md")
@@ -39,6 +44,155 @@ METRIC = "CSA2 decode queries/s + achieved HBM GB/s (% of peak) at 128K context"
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+class Flusher:
+    """Writes a 512 MiB device buffer (a plain fill): afterwards neither the Infinity Cache
+    nor any L2 holds the data of the layer before."""
+
+    def __init__(self):
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(1 + self.n % 200)
+
+
+def host_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return dict(cpu_model=model, nproc=os.cpu_count(), affinity_cpus=affinity)
+
+
+def layer_calls(wl, c, layers, out_dtype=torch.bfloat16):
+    """One C-ABI call per layer of the group, for the flushed protocol: a Full or Reindex
+    layer is a one-layer csa2_layer_group (without a candidate pool a Reindex layer takes
+    exactly the steps of a Full layer over the shared cache: every entry scored with its own
+    query, a fresh Top-K, attention); a Reuse layer is csa2_sparse_attend on the indices of
+    the most recent indexing layer, unchanged."""
+    calls, last_idx = [], None
+    for L in layers:
+        if L["mode"] != "reuse":
+            d = dict(mode="full", q_idx=L["q_idx"], w=L["w"], q_attn=L["q_attn"])
+            plan = csa2.GroupPlan([d], csa2.GroupCache(c["n_keys"], c["codes"], c["scales"], c["k8"], c["ks"], wl.K,
+                                                       wl.softmax_scale), out_dtype=out_dtype)
+            calls.append(plan.run)
+            last_idx = d["idx"]
+        else:
+            out = torch.empty((wl.B, 1, wl.Hq, wl.D), dtype=out_dtype, device="cuda")
+            lse = torch.empty((wl.B, 1, wl.Hq), dtype=torch.float32, device="cuda")
+
+            def reuse(q=L["q_attn"], idx=last_idx, out=out, lse=lse):
+                csa2.sparse_attend(q, c["codes"], c["scales"], idx, wl.softmax_scale, out=out, lse=lse)
+            calls.append(reuse)
+    return calls
+
+
+def time_flushed(calls, steps, warmup, flush):
+    """Flushed protocol: before every layer the flush buffer is written; each layer's call
+    is bracketed by HIP events on the launching stream (torch's current stream, which the
+    library launches on).  Returns (mean step ms = mean over steps of the summed layer
+    times, per-layer mean ms, wall seconds of the whole timed loop incl. the flushes)."""
+    n = len(calls)
+    for _ in range(warmup):
+        for f in calls:
+            flush()
+            f()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for i, f in enumerate(calls):
+            flush()
+            evs[s][i][0].record()
+            f()
+            evs[s][i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[a.elapsed_time(b) for a, b in row] for row in evs])  # [steps][layers] ms
+    return float(per.sum(axis=1).mean()), [float(x) for x in per.mean(axis=0)], wall
+
+
+def time_warm(plans, steps, warmup):
+    for s in range(warmup):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        plans[s % len(plans)].run()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def stream_ceiling(buf, flush, reps=5):
+    """Read rate (GB/s) of the library's streaming probe over `buf` from HBM (a flush before
+    every read), best over a few grid sizes: the practical ceiling for a kernel that reads
+    these bytes once."""
+    best = 0.0
+    sink = torch.empty(1, dtype=torch.int32, device="cuda")
+    nbytes = buf.numel() * buf.element_size()
+    for blocks in (1024, 2048, 4096):
+        ms = []
+        for _ in range(reps):
+            flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            csa2.stream_probe(buf, blocks, sink)
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        best = max(best, nbytes / (float(np.median(ms)) / 1e3) / 1e9)
+    return best
+
+
+def score_roofline(wl, c, L, reps, flush):
+    """The decode score kernel (one launch per csa2_index_score call) on a cold cache: a
+    flush before every launch, each launch bracketed by HIP events on the launching stream.
+    Algorithmic bytes per launch: every key's 64 code bytes and 4-byte scale read once, plus
+    the query and head weights (the kernel also writes one fp32 score per key, which is
+    traffic beyond the algorithm and shows in the counted traffic instead)."""
+    out = torch.empty((wl.B, 1, wl.N), dtype=torch.float32, device="cuda")
+
+    def launch():
+        csa2.index_score(csa2.PREC_FP8, L["q_idx"], L["w"], c["k8"], c["ks"], c["n_keys"], scores=out)
+
+    for _ in range(3):
+        flush()
+        launch()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    # the same kernel back to back without a flush (its keys partly in the Infinity Cache)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        launch()
+    b.record()
+    torch.cuda.synchronize()
+    warm_ms = a.elapsed_time(b) / reps
+    nbytes = wl.B * wl.N * (wl.dk + 4) + wl.B * wl.H * (wl.dk * 2 + 4)
+    mean_ms = float(np.mean(ms))
+    return dict(bytes_per_launch=nbytes, kernel_ms_mean=mean_ms, kernel_ms_median=float(np.median(ms)),
+                warm_kernel_ms_mean=float(warm_ms), achieved=nbytes / (mean_ms / 1e3) / 1e9)
 
 
 def build_device_cache(wl, copies, kv_fmt=csa2.FMT_FP4_PER_CHANNEL, key_fmt=csa2.FMT_FP8_PER_TOKEN):
@@ -88,43 +242,6 @@ def algorithmic_bytes(wl):
     q_idx = B * wl.H * wl.dk * 2 + B * wl.H * 4
     per_layer_attend = B * K * (D // 2) + B * D * 4 + B * Hq * D * 2 * 2 + B * K * 4 + B * Hq * 4
     return n_index * (scan + q_idx + B * K * 4) + len(wl.modes) * per_layer_attend
-
-
-def time_score_kernel(wl, caches, layers, reps):
-    """Average duration of the indexer-score kernel (one launch per csa2_index_score call),
-    from HIP events on the launching stream around `reps` back-to-back launches (so the
-    per-event overhead is not counted); launches alternate over the rotated caches and the
-    indexing layers' queries exactly as the timed steps do.  Also returns the median of
-    single launches each bracketed by its own events."""
-    idx_layers = [L for L in layers if L["mode"] != "reuse"]
-    out = torch.empty((wl.B, 1, wl.N), dtype=torch.float32, device="cuda")
-    seq = []
-    for r in range(reps):
-        c = caches[(r // len(idx_layers)) % len(caches)]
-        L = idx_layers[r % len(idx_layers)]
-        seq.append((c, L))
-
-    def launch(c, L):
-        csa2.index_score(csa2.PREC_FP8, L["q_idx"], L["w"], c["k8"], c["ks"], c["n_keys"], scores=out)
-
-    for c, L in seq[: min(4, reps)]:  # warm-up
-        launch(c, L)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for c, L in seq:
-        launch(c, L)
-    e1.record()
-    torch.cuda.synchronize()
-    mean_ms = e0.elapsed_time(e1) / reps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for (c, L), (a, b) in zip(seq, evs):
-        a.record()
-        launch(c, L)
-        b.record()
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
-    return float(mean_ms), float(np.median(ms))
 
 
 def score_sources_sha256():
@@ -187,9 +304,11 @@ def cpu_baseline(wl, seqs):
     t0 = time.perf_counter()
     oracle.layer_group(layers, cache, oracle.PREC_FP8, sub.K, sub.softmax_scale)
     dt = time.perf_counter() - t0
-    return dict(value=seqs / dt, unit="queries/s", cores=oracle.num_threads(), kind="oracle",
-                sample="%d of %d sequences of the same workload (N=%d, all %d layers); %.2f s" %
-                       (seqs, wl.B, wl.N, len(wl.modes), dt))
+    res = dict(value=seqs / dt, unit="queries/s", cores=oracle.num_threads(), kind="oracle",
+               sample="%d of %d sequences of the same workload (N=%d, all %d layers); %.2f s" %
+                      (seqs, wl.B, wl.N, len(wl.modes), dt))
+    res.update(host_info())
+    return res
 
 
 def run_prefill(args):
@@ -260,37 +379,80 @@ def run_prefill(args):
                      "kernel": "k_quant_query + k_score_fp8_rows (one csa2_index_score call)",
                      "kernel_ms_mean": round(score_ms, 4), "flops_per_launch": flops},
     }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline_prefill(wl, args.cpu_rows)
     print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_prefill(wl, rows):
+    """The CPU oracle on a bounded sample of the chunked-prefill step: the append of all
+    4096 new tokens (FP4 with the cache's scales, E4M3 keys), then for `rows` new tokens
+    spread over the chunk the causal score against every visible entry, Top-512 and the
+    attention; reported as new tokens per second of those rows."""
+    import oracle
+    Nc, T = wl.N, wl.T
+    n_max = Nc + T
+    pick = np.linspace(0, T - 1, rows).astype(np.int64)
+    cr, sr = oracle.quantize_fp4(wl.main_kv(0)[None], n_max=n_max)
+    kr, ksr = oracle.quantize_fp8(wl.index_keys(0)[None], n_max=n_max)
+    t0 = time.perf_counter()
+    oracle.quantize_fp4(wl.new_kv(), n_max=n_max, n0=np.array([Nc], np.int32), scales=sr, codes=cr)
+    oracle.quantize_fp8(wl.new_index_keys(), n_max=n_max, n0=np.array([Nc], np.int32), codes=kr, scales=ksr)
+    t_append = time.perf_counter() - t0
+    q, w, qa = wl.index_query()[:, pick], wl.head_weights()[:, pick], wl.attn_query()[:, pick]
+    ql = (Nc + pick).astype(np.int32)[None]
+    t1 = time.perf_counter()
+    s = oracle.index_score(oracle.PREC_FP8, q, w, kr, ksr, np.array([n_max], np.int32), q_limit=ql)
+    idx = oracle.topk(s, wl.K)
+    oracle.sparse_attend(qa, cr, sr, idx, wl.softmax_scale)
+    t_rows = time.perf_counter() - t1
+    dt = t_rows + t_append * rows / T
+    res = dict(value=rows / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+               sample="%d of the %d new tokens (rows spread over the chunk: causal score against every visible "
+                      "entry, Top-%d, attention; %.2f s) plus the append of the whole chunk (%.2f s) counted "
+                      "pro rata" % (rows, T, wl.K, t_rows, t_append))
+    res.update(host_info())
+    return res
 
 
 def run_full64k(args):
     """The single-layer 64K decode configuration: a Full layer over 16 sequences x 65536
-    entries (score, Top-512, FP4 gather + attention), with 3 rotated cache copies."""
+    entries (score, Top-512, FP4 gather + attention).  Flushed protocol as the headline (the
+    512 MiB flush before every step); the warm number (3 rotated cache copies) beside it."""
     wl = workloads.WORKLOADS["full64k"]
     log("building cache (%d copies) ..." % args.copies)
     caches = build_device_cache(wl, args.copies)
     layers = layer_inputs(wl)
+    flush = Flusher()
+    ms_step, per_layer, wall = time_flushed(layer_calls(wl, caches[0], layers), args.steps, args.warmup, flush)
     plans = [csa2.GroupPlan([dict(L) for L in layers],
                             csa2.GroupCache(c["n_keys"], c["codes"], c["scales"], c["k8"], c["ks"], wl.K,
                                             wl.softmax_scale), out_dtype=torch.bfloat16) for c in caches]
-    for s in range(args.warmup):
-        plans[s % len(plans)].run()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        plans[s % len(plans)].run()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    warm_ms = time_warm(plans, args.steps, args.warmup)
     alg = algorithmic_bytes(wl)
     gbs = alg / (ms_step / 1e3) / 1e9
-    print(json.dumps({
+    rf = score_roofline(wl, caches[0], layers[0], args.score_reps, flush)
+    ceil = stream_ceiling(caches[0]["k8"], flush)
+    res = {
         "metric": "CSA2 decode queries/s at 64K context (single Full layer)", "value": round(wl.B / (ms_step / 1e3), 1),
         "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
         "config": {"workload": "full64k: Full decode, B=16, N=65536, indexer 32x64 E4M3, Top-512, FP4 E2M1 main KV "
-                               "D=512, 64 heads bf16", "global_batch": wl.B, "seq_len": wl.N},
+                               "D=512, 64 heads bf16", "global_batch": wl.B, "seq_len": wl.N,
+                   "protocol": "flushed: 512 MiB written before the layer, HIP-event time of the call"},
         "step_algorithmic_bytes": alg, "step_achieved_GBps": round(gbs, 1),
-        "step_pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
+        "step_pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "step_pct_stream_ceiling": round(100 * gbs / ceil, 2),
+        "warm_ms_per_step": round(warm_ms, 5), "stream_ceiling_GBps": round(ceil, 1),
+        "roofline": {"bound": "hbm", "achieved": round(rf["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(rf["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac_of_stream_ceiling": round(rf["achieved"] / ceil, 4),
+                     "kernel": "k_score_fp8 (cold: flushed before each launch)",
+                     "kernel_ms_mean": round(rf["kernel_ms_mean"], 5), "bytes_per_launch": rf["bytes_per_launch"]}}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seqs)
+    print(json.dumps(res), flush=True)
 
 
 DECODER_MODES = ["full"] + ["reuse"] * 3 + (["reindex"] + ["reuse"] * 3) * 4
@@ -531,14 +693,52 @@ def run_hier1m(args):
     nb = n // wl.coarse_block
     alg = nb * (wl.dk + 4) + wl.coarse_topk * wl.coarse_block * (wl.dk + 4) + wl.K * (wl.D // 2 + 4) + \
         wl.Hq * wl.D * 2 * 2
-    print(json.dumps({
+    # the step's largest kernel is the attention over the 1024 selected entries: its time on
+    # a flushed cache (one csa2_sparse_attend call, HIP events) against its bytes (the
+    # gathered rows and their indices, the per-channel scales, the query and the output)
+    flush = Flusher()
+    idx = csa2.hier_select(q, w, k8, ks, kb, kbs, nk, wl.coarse_block, wl.coarse_topk, wl.K)
+    att_ms = []
+    for r in range(args.score_reps):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        csa2.sparse_attend(qa, codes, scales, idx, wl.softmax_scale, out=out, lse=lse)
+        b.record()
+        torch.cuda.synchronize()
+        att_ms.append(a.elapsed_time(b))
+    att_bytes = wl.K * (wl.D // 2 + 4) + wl.D * 4 + wl.Hq * wl.D * 2 * 2 + wl.Hq * 4
+    att_mean = float(np.mean(att_ms))
+    att_gbs = att_bytes / (att_mean / 1e3) / 1e9
+    res = {
         "metric": "CSA2 decode queries/s at 1M context (two-level indexer)", "value": round(1.0 / (ms_step / 1e3), 1),
         "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
         "config": {"workload": "hier1m: B=1, N=2^20, coarse blocks of 64, top-256 blocks, Top-1024, FP4 E2M1 main KV "
                                "D=512, 64 heads bf16", "global_batch": 1, "seq_len": n, "launch": "hip graph replay"},
         "step_algorithmic_bytes": alg, "flat_full_layer_ms_per_step": round(flat_ms, 5),
-        "flat_scan_at_hbm_peak_ms": round(n * (wl.dk + 4) / (HBM_PEAK_GBS * 1e9) * 1e3, 5)}), flush=True)
+        "flat_scan_at_hbm_peak_ms": round(n * (wl.dk + 4) / (HBM_PEAK_GBS * 1e9) * 1e3, 5),
+        "roofline": {"bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(att_gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                     "kernel": "sparse attention over the 1024 selected entries (cold: flushed before each call; "
+                               "latency-bound)", "kernel_ms_mean": round(att_mean, 5), "bytes_per_launch": att_bytes}}
+    if not args.no_cpu_baseline:
+        import oracle
+        kr, ksr = oracle.quantize_fp8(wl.index_keys(0)[None])
+        cr, sr = oracle.quantize_fp4(wl.main_kv(0)[None])
+        nka = np.array([n], np.int32)
+        kbr, kbsr = oracle.coarse_keys(kr, ksr, nka, wl.coarse_block)
+        qn, wn, qan = wl.index_query(), wl.head_weights(), wl.attn_query()
+        t0 = time.perf_counter()
+        ridx, _ = oracle.hier_select(qn, wn, kr, ksr, kbr, kbsr, nka, wl.coarse_block, wl.coarse_topk, wl.K)
+        oracle.sparse_attend(qan, cr, sr, ridx, wl.softmax_scale)
+        dt = time.perf_counter() - t0
+        cb = dict(value=1.0 / dt, unit="queries/s", cores=oracle.num_threads(), kind="oracle",
+                  sample="the whole step for the one sequence (coarse scores, top-256 blocks, fine scores, Top-1024, "
+                         "attention; coarse keys built beforehand, as on the GPU); %.3f s" % dt)
+        cb.update(host_info())
+        res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -560,6 +760,10 @@ def main():
                          "window per layer; group128k_fp4idx: the 128K group with the 4-bit indexer")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--stream-probe", type=int, default=0, metavar="BYTES",
+                    help="only measure the read-stream ceiling over a buffer of BYTES (flushed before every read) "
+                         "and exit")
+    ap.add_argument("--cpu-rows", type=int, default=16, help="prefill: new tokens the CPU oracle baseline computes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the CSA2 decode path runs per sequence with no exchange between GPUs, "
@@ -571,6 +775,12 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.stream_probe:
+        buf = torch.empty(args.stream_probe // 16 * 16, dtype=torch.uint8, device="cuda").fill_(3)
+        gbs = stream_ceiling(buf, Flusher())
+        print(json.dumps({"stream_probe_bytes": buf.numel(), "read_GBps": round(gbs, 1),
+                          "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
         return
     if args.workload == "prefill":
         run_prefill(args)
@@ -593,52 +803,57 @@ def main():
     if args.workload == "group128k_fp4idx":
         run_group128k_fp4idx(args)
         return
+    run_group128k(args)
+
+
+def run_group128k(args):
     wl = workloads.WORKLOADS["group128k"]
     log("building cache (%d copies) ..." % args.copies)
     caches = build_device_cache(wl, args.copies)
     layers = layer_inputs(wl)
-    plans = []
-    for c in caches:
-        cache = csa2.GroupCache(c["n_keys"], c["codes"], c["scales"], c["k8"], c["ks"], wl.K, wl.softmax_scale)
-        ls = [dict(L) for L in layers]
-        plans.append(csa2.GroupPlan(ls, cache, out_dtype=torch.bfloat16))
-    log("warmup %d steps" % args.warmup)
-    for s in range(args.warmup):
-        plans[s % len(plans)].run()
+    flush = Flusher()
+    # headline: flushed, layer by layer
+    calls = layer_calls(wl, caches[0], layers)
+    log("flushed protocol: warmup %d, timing %d steps" % (args.warmup, args.steps))
     torch.cuda.synchronize()
-    log("timing %d steps" % args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        plans[s % len(plans)].run()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_step = dt / args.steps * 1e3
-    qps = wl.B / (ms_step / 1e3)
+    ms_step, per_layer, wall = time_flushed(calls, args.steps, args.warmup, flush)
+    # warm protocol: the whole group in one call
+    plans = [csa2.GroupPlan([dict(L) for L in layers],
+                            csa2.GroupCache(c["n_keys"], c["codes"], c["scales"], c["k8"], c["ks"], wl.K,
+                                            wl.softmax_scale), out_dtype=torch.bfloat16) for c in caches]
+    log("warm protocol: timing %d steps" % args.steps)
+    warm_ms = time_warm(plans, args.steps, args.warmup)
     alg = algorithmic_bytes(wl)
-    step_gbs = alg / (ms_step / 1e3) / 1e9
-
-    log("timing the score kernel")
-    mean_ms, med_ms = time_score_kernel(wl, caches, layers, args.score_reps)
-    # algorithmic bytes of one score launch: per scored key 64 B key + 4 B scale read and
-    # 4 B score written; plus the query and weights
-    score_bytes = wl.B * wl.N * (wl.dk + 4 + 4) + wl.B * wl.H * (wl.dk * 2 + 4)
-    achieved = score_bytes / (mean_ms / 1e3) / 1e9
-
+    gbs = alg / (ms_step / 1e3) / 1e9
+    log("score kernel (cold) and stream ceiling")
+    rf = score_roofline(wl, caches[0], layers[0], args.score_reps, flush)
+    ceil = stream_ceiling(caches[0]["k8"], flush)
     res = {
-        "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
+        "metric": METRIC, "value": round(wl.B / (ms_step / 1e3), 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
         "config": {"workload": "group128k: Full->Reindex->Reuse decode, B=16, N=131072, indexer 32x64 E4M3, "
                                "Top-512, FP4 E2M1 main KV D=512, 64 heads bf16",
-                   "global_batch": wl.B, "seq_len": wl.N, "layers": list(wl.modes), "cache_copies": args.copies},
-        "step_algorithmic_bytes": alg, "step_achieved_GBps": round(step_gbs, 1),
-        "step_pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counted_traffic(),
-                     "kernel": "k_score_fp8 (indexer score, one launch per indexing layer)",
-                     "kernel_ms_mean": round(mean_ms, 5), "kernel_ms_median": round(med_ms, 5),
-                     "bytes_per_launch": score_bytes, "traffic_unit": "bytes per launch"},
+                   "global_batch": wl.B, "seq_len": wl.N, "layers": list(wl.modes),
+                   "protocol": "flushed: 512 MiB written before each layer, one C-ABI call per layer, step = sum "
+                               "of per-layer HIP-event times"},
+        "step_algorithmic_bytes": alg, "step_achieved_GBps": round(gbs, 1),
+        "step_pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "step_pct_stream_ceiling": round(100 * gbs / ceil, 2),
+        "per_layer_ms": [round(x, 5) for x in per_layer],
+        "flushed_loop_wall_s": round(wall, 4),
+        "warm_ms_per_step": round(warm_ms, 5), "warm_value": round(wl.B / (warm_ms / 1e3), 1),
+        "warm_protocol": "the group in one csa2_layer_group call (the Full scan keeps its keys for the Reindex "
+                         "rescan in the Infinity Cache), %d cache copies rotated between steps" % args.copies,
+        "stream_ceiling_GBps": round(ceil, 1),
+        "roofline": {"bound": "hbm", "achieved": round(rf["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(rf["achieved"] / HBM_PEAK_GBS, 4), "traffic": counted_traffic(),
+                     "frac_of_stream_ceiling": round(rf["achieved"] / ceil, 4),
+                     "kernel": "k_score_fp8 (indexer score over every cached key, cold: flushed before each launch)",
+                     "kernel_ms_mean": round(rf["kernel_ms_mean"], 5),
+                     "kernel_ms_median": round(rf["kernel_ms_median"], 5),
+                     "warm_kernel_ms_mean": round(rf["warm_kernel_ms_mean"], 5),
+                     "bytes_per_launch": rf["bytes_per_launch"], "traffic_unit": "bytes per launch"},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -36,7 +36,7 @@ EXPORTS = [
     "csa2_index_score_workspace_size", "csa2_topk", "csa2_topk_workspace_size", "csa2_index_topk",
     "csa2_index_topk_workspace_size", "csa2_sparse_attend", "csa2_sparse_attend_workspace_size",
     "csa2_layer_group", "csa2_layer_group_workspace_size", "csa2_coarse_keys", "csa2_hier_select",
-    "csa2_hier_select_workspace_size", "csa2_layer_group_noalloc",
+    "csa2_hier_select_workspace_size", "csa2_layer_group_noalloc", "csa2_stream_probe",
 ]
 
 # bytes of the library-held scratch array of csa2_layer_group_noalloc (one per GPU)
@@ -98,6 +98,7 @@ def lib() -> ctypes.CDLL:
             "csa2_layer_group": ([p, i, p, p, sz, p], i),
             "csa2_layer_group_workspace_size": ([p, i], sz),
             "csa2_layer_group_noalloc": ([p, i, p, p], i),
+            "csa2_stream_probe": ([p, i64, i, p, p], i),
             "csa2_coarse_keys": ([i, i64, p, i, i, p, p, p, p, p], i),
             "csa2_hier_select": ([i, i, i, p, i, p, p, p, p, p, i64, p, i, i, i, p, p, p, sz, p], i),
             "csa2_hier_select_workspace_size": ([i, i64, i, i, i], sz),
@@ -391,3 +392,13 @@ def hier_select(q: torch.Tensor, w: torch.Tensor, k8: torch.Tensor, k_scale: tor
                                   _ptr(kb_scale), n_max, _ptr(n_keys), block, block_topk, K, _ptr(idx), _ptr(blk),
                                   _ptr(ws), nb, _stream()), "csa2_hier_select")
     return (idx, blk) if want_blocks else idx
+
+
+# ------------------------------------------------------------------------------ measurement
+def stream_probe(buf: torch.Tensor, blocks: int = 2048, sink: Optional[torch.Tensor] = None) -> None:
+    """One read of the whole of `buf` by the library's streaming probe kernel (a ceiling for
+    the key scan's HBM rate; it computes nothing)."""
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device=buf.device)
+    _check(lib().csa2_stream_probe(_ptr(buf), buf.numel() * buf.element_size(), blocks, _ptr(sink), _stream()),
+           "csa2_stream_probe")

@@ -560,6 +560,15 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   return CSA2_OK;
 }
 
+int csa2_stream_probe(const void* src, int64_t bytes, int blocks, uint32_t* sink, void* stream) {
+  if (!src || !sink) return CSA2_ERR_NULL;
+  if (bytes < 16 || bytes % 16 || (reinterpret_cast<uintptr_t>(src) & 15) || blocks < 1 || blocks > (1 << 20))
+    return CSA2_ERR_SHAPE;
+  int rc = check_device();
+  if (rc) return rc;
+  return dev_status(launch_stream_read(src, bytes, blocks, sink, S(stream)));
+}
+
 // ---------------------------------------------------------------------------- two-level indexer
 int csa2_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int block, const uint8_t* k8,
                      const float* k_scale, uint8_t* kb8, float* kb_scale, void* stream) {

@@ -118,4 +118,6 @@ int launch_gather_dequant(bool g16, int B, int T, int K, int D, const uint8_t* c
 int launch_causal_limits(int B, int T, const int32_t* n_keys, int32_t* q_limit, hipStream_t st);
 int launch_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int block, const uint8_t* k8,
                        const float* k_scale, uint8_t* kb8, float* kb_scale, hipStream_t st);
+// read-stream probe: `bytes` (a multiple of 16, 16-byte aligned) read once by `blocks` blocks
+int launch_stream_read(const void* p, int64_t bytes, int blocks, uint32_t* sink, hipStream_t st);
 }  // namespace csa2

@@ -4,6 +4,8 @@
 
 namespace csa2 {
 
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+
 // out[r][k][c] = fl32(E2M1(code) * s_c) of cache row idx[r][k] (G16: the scale of the
 // entry's 16-channel group, E4M3); 0 for rows outside [0, n_max).  One thread per 8
 // channels.  (The stored FP4 entries are turned back into real values before the
@@ -115,6 +117,36 @@ int launch_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int 
   const int64_t nb = (n_max + block - 1) / block;
   hipLaunchKernelGGL(k_coarse_keys, dim3((unsigned)((nb + 3) / 4), B), dim3(256), 0, st, n_max, n_keys, dk, block, nb,
                      k8, k_scale, kb8, kb_scale);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Read-stream ceiling probe: the grid sweeps `n16` 16-byte chunks with nontemporal loads,
+// four in flight per lane, and folds them into one word per thread.  The word is stored
+// only when it equals a value the caller's data never produces, so the kernel's memory
+// traffic is the read alone.
+__global__ __launch_bounds__(256) void k_stream_read(const v4i_t* __restrict__ p, int64_t n16, uint32_t never,
+                                                     uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = blockIdx.x * 256LL + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const v4i_t a = __builtin_nontemporal_load(p + i);
+    const v4i_t b = __builtin_nontemporal_load(p + i + stride);
+    const v4i_t c = __builtin_nontemporal_load(p + i + 2 * stride);
+    const v4i_t d = __builtin_nontemporal_load(p + i + 3 * stride);
+    acc ^= (uint32_t)(a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3]);
+    acc ^= (uint32_t)(c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3]);
+  }
+  for (; i < n16; i += stride) {
+    const v4i_t a = __builtin_nontemporal_load(p + i);
+    acc ^= (uint32_t)(a[0] ^ a[1] ^ a[2] ^ a[3]);
+  }
+  if (acc == never) sink[0] = acc;
+}
+
+int launch_stream_read(const void* p, int64_t bytes, int blocks, uint32_t* sink, hipStream_t st) {
+  hipLaunchKernelGGL(k_stream_read, dim3(blocks), dim3(256), 0, st, static_cast<const v4i_t*>(p), bytes / 16,
+                     0x9E3779B9u, sink);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

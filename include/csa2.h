@@ -338,6 +338,15 @@ int csa2_hier_select(int B, int H, int dk, const void* q, int q_dtype, const flo
                      void* ws, size_t ws_bytes, void* stream);
 size_t csa2_hier_select_workspace_size(int B, int64_t n_max, int block, int block_topk, int K);
 
+/*
+ * Measurement utility (not a step of the method): reads `bytes` of device memory at `src`
+ * once with 16-byte nontemporal loads, `blocks` workgroups of 256 threads sweeping it, and
+ * computes nothing the caller sees (sink [1] uint32 is written only in an impossible case).
+ * Timing it gives the read bandwidth a streaming kernel reaches on this GPU, the ceiling
+ * the indexer's key scan is compared with.  bytes a multiple of 16, src 16-byte aligned.
+ */
+int csa2_stream_probe(const void* src, int64_t bytes, int blocks, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
