@@ -101,6 +101,38 @@ int zero_topk(const TopkWs& t, int64_t R, hipStream_t st) {
   return launch_fill_u32(t.hist, (int64_t)(topk_zero_bytes(R) / 4), 0u, st);
 }
 
+// ---- candidate lists of LOCAL decode scans: pairs [R][nreg][stride] | cnt, cut, vis [R][nreg]
+size_t local_pairs(int64_t R, int64_t ncols) {
+  return (size_t)R * score_blocks(R, ncols) * score_cols_per_block(R, ncols);
+}
+size_t local_regions(int64_t R, int64_t ncols) { return (size_t)R * score_blocks(R, ncols); }
+size_t local_ws(size_t pairs, size_t regions) {
+  return align256(pairs * sizeof(uint2)) + 3 * align256(regions * 4);
+}
+size_t local_ws(int64_t R, int64_t ncols) { return local_ws(local_pairs(R, ncols), local_regions(R, ncols)); }
+LocalCand carve_local(Carve& c, size_t pairs, size_t regions) {
+  LocalCand l;
+  l.cand = c.take<uint2>(pairs);
+  l.cnt = c.take<uint32_t>(regions);
+  l.cut = c.take<int32_t>(regions);
+  l.vis = c.take<uint32_t>(regions);
+  l.stride = 0;
+  l.K = 0;
+  return l;
+}
+// the same storage set up for a scan of ncols columns
+LocalCand local_for(LocalCand l, int64_t R, int64_t ncols, int K) {
+  l.stride = score_cols_per_block(R, ncols);
+  l.K = K;
+  return l;
+}
+// decode scans (the fp8 / fp4 indexer's k_score_fp8; the many-row tiled kernel of chunked
+// prefill is not one) list their candidates for k_topk_select
+bool local_scan(int prec, int T, const int32_t* cand) {
+  const bool tiled = prec == CSA2_PREC_FP8 && !cand && T >= score_tiled_min_rows();
+  return prec != CSA2_PREC_FP32 && !tiled;
+}
+
 bool valid_dtype(int d) { return d == CSA2_F32 || d == CSA2_BF16; }
 
 // main-KV layouts the attention reads
@@ -132,8 +164,6 @@ AttendArgs attend_args(int B, int T, int Hq, int D, int K, const void* q, int q_
   a.q = q; a.q_bf16 = (q_dtype == CSA2_BF16);
   a.codes = codes; a.scales = scales; a.g16 = (kv_fmt == CSA2_FMT_FP4_G16); a.n_max = n_max; a.idx = idx;
   a.softmax_scale = softmax_scale; a.out = out; a.out_bf16 = (out_dtype == CSA2_BF16); a.lse = lse;
-  a.ctl = nullptr; a.hist2 = nullptr; a.candbuf = nullptr; a.cnt = nullptr; a.nreg = 0; a.rstride = 0;
-  a.idx_out = nullptr;
   a.part = nullptr;
   a.swa_codes = nullptr; a.swa_scales = nullptr; a.swa_n_max = 0; a.swa_end = nullptr; a.window = 0;
   return a;
@@ -183,6 +213,8 @@ ScoreArgs score_args(int prec, int B, int T, int H, int dk, const void* q, int q
   a.ncols = ncols; a.scores = scores; a.hist = hist; a.key_div = key_div;
   a.qstage = nullptr;
   a.keep = false;
+  a.local = false;
+  a.lc = LocalCand{nullptr, nullptr, nullptr, nullptr, 0, 0};
   return a;
 }
 
@@ -310,7 +342,9 @@ int csa2_topk(int B, int T, int64_t ncols, const float* scores, const int32_t* c
 
 size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int) {
   const int64_t R = (int64_t)B * T;
-  return align256((size_t)R * ncols * 4) + topk_ws(R, ncols) + csa2_index_score_workspace_size(B, T, ncols);
+  // the candidate lists of a decode scan (fp8 / fp4), or the histogram filter's regions
+  const size_t sel = local_ws(R, ncols) > topk_ws(R, ncols) ? local_ws(R, ncols) : topk_ws(R, ncols);
+  return align256((size_t)R * ncols * 4) + sel + csa2_index_score_workspace_size(B, T, ncols);
 }
 
 int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_dtype, const float* w, const void* k,
@@ -329,10 +363,22 @@ int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_
   if (rc) return rc;
   Carve c(ws);
   float* scores = c.take<float>((size_t)R * ncols);
+  hipStream_t st = S(stream);
+  if (local_scan(prec, T, cand)) {
+    // decode rows: the score blocks list their candidates, one select workgroup per row
+    // finishes the exact Top-K (a candidate map in arbitrary order needs the ranked output)
+    const LocalCand lc = local_for(carve_local(c, local_pairs(R, ncols), local_regions(R, ncols)), R, ncols, K);
+    ScoreArgs a = score_args(prec, B, T, H, dk, q, q_dtype, w, k, k_scale, n_max, n_keys, q_limit, cand, ncols,
+                             scores, nullptr, 1);
+    a.local = true;
+    a.lc = lc;
+    if (launch_score(a, st)) return CSA2_ERR_DEVICE;
+    return dev_status(launch_topk_select((int)R, ncols, K, cand == nullptr, lc, score_blocks(R, ncols), scores, cand,
+                                         idx_out, val_out, st));
+  }
   TopkWs t = carve_topk(c, R, ncols);
   const size_t stage = csa2_index_score_workspace_size(B, T, ncols);
   uint8_t* qstage = stage ? c.take<uint8_t>(stage) : nullptr;
-  hipStream_t st = S(stream);
   if (zero_topk(t, R, st)) return CSA2_ERR_DEVICE;
   ScoreArgs a = score_args(prec, B, T, H, dk, q, q_dtype, w, k, k_scale, n_max, n_keys, q_limit, cand, ncols, scores,
                            t.hist, 1);
@@ -417,19 +463,46 @@ static int64_t group_cols(const csa2_group_cache* c) {
   return pc > c->n_max ? pc : c->n_max;
 }
 
-// workspace: [hist, hist2, ctl per Top-K selection (zeroed once per call)] [scores]
-//            [candidates] [attention partials] [pool positions, block maxima]
+// Selections that use a histogram slot (hist, hist2, ctl; zeroed before use): with the fp8 /
+// fp4 indexer only the candidate pools' block selections, with the fp32 indexer every one.
+static bool group_local(const csa2_group_cache* c) { return c->prec != CSA2_PREC_FP32; }
+static int group_slot_selections(const csa2_group_cache* c, int n_index, int n_full) {
+  const int pool_sel = pool_on(c) ? n_full : 0;
+  return group_local(c) ? pool_sel : n_index + pool_sel;
+}
+// storage of the decode scans' candidate lists: the larger of the full scan's and the pool's
+static void group_local_sizes(const csa2_group_cache* c, int64_t R, size_t& pairs, size_t& regions) {
+  pairs = local_pairs(R, c->n_max);
+  regions = local_regions(R, c->n_max);
+  if (pool_on(c)) {
+    const size_t p2 = local_pairs(R, pool_cols(c)), r2 = local_regions(R, pool_cols(c));
+    if (p2 > pairs) pairs = p2;
+    if (r2 > regions) regions = r2;
+  }
+}
+// candidate regions of the histogram filter (fp32 indexer: every selection; else the pools')
+static int64_t group_filter_cols(const csa2_group_cache* c) {
+  if (!group_local(c)) return group_cols(c);
+  return pool_on(c) ? pool_nb(c) : 0;
+}
+
+// workspace: [hist, hist2, ctl per slot selection (the first zeroed per call, each later one
+//            by the filter before it)] [scores] [filter regions] [candidate lists]
+//            [attention partials] [pool positions, block maxima] [causal limits]
 size_t csa2_layer_group_workspace_size(const csa2_group_cache* c, int n_layers) {
   if (!c || n_layers < 1) return 0;
   const int64_t R = (int64_t)c->B * group_T(c);
-  const int sel = pool_on(c) ? 2 * n_layers : n_layers;  // a pooled Full layer makes two selections
+  const int sel = group_slot_selections(c, n_layers, n_layers);
   const int slots = sel < 64 ? sel : 64;
   const size_t att =
       (c->q_dtype == CSA2_BF16) ? align256(attend_ws_floats((int)R, c->Hq, c->D, c->K, c->window) * 4) : 0;
   const size_t pool = pool_on(c) ? align256((size_t)R * pool_cols(c) * 4) + align256((size_t)R * pool_nb(c) * 4) : 0;
   const size_t lim = group_T(c) > 1 ? align256((size_t)R * 4) : 0;
-  return topk_zero_bytes(R) * (size_t)slots + align256((size_t)R * group_cols(c) * 4) + cand_bytes(R, group_cols(c)) +
-         att + pool + lim;
+  size_t lp = 0, lr = 0;
+  if (group_local(c)) group_local_sizes(c, R, lp, lr);
+  const int64_t fc = group_filter_cols(c);
+  return topk_zero_bytes(R) * (size_t)slots + align256((size_t)R * group_cols(c) * 4) + (fc ? cand_bytes(R, fc) : 0) +
+         (group_local(c) ? local_ws(lp, lr) : 0) + att + pool + lim;
 }
 
 int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_cache* c, void* ws, size_t ws_bytes,
@@ -464,15 +537,23 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
 
   const int64_t R = (int64_t)c->B * T;
   const bool pooled = pool_on(c);
-  int n_sel = count_index_layers(layers, n_layers);
-  if (pooled)
-    for (int i = 0; i < n_layers; ++i) n_sel += (layers[i].mode == CSA2_FULL);
+  const bool local = group_local(c);
+  int n_full = 0;
+  for (int i = 0; i < n_layers; ++i) n_full += (layers[i].mode == CSA2_FULL);
+  const int n_sel = group_slot_selections(c, count_index_layers(layers, n_layers), n_full);
   const int slots = n_sel < 64 ? n_sel : 64;
   Carve cv(ws);
   TopkWs tz[64];
   for (int i = 0; i < slots; ++i) tz[i] = carve_topk_zero(cv, R);
   float* scores = cv.take<float>((size_t)R * group_cols(c));
-  CandWs cw = carve_cand(cv, R, group_cols(c));
+  const int64_t fc = group_filter_cols(c);
+  CandWs cw = fc ? carve_cand(cv, R, fc) : CandWs{nullptr, nullptr};
+  LocalCand lbase{nullptr, nullptr, nullptr, nullptr, 0, 0};
+  if (local) {
+    size_t lp = 0, lr = 0;
+    group_local_sizes(c, R, lp, lr);
+    lbase = carve_local(cv, lp, lr);
+  }
   float* part =
       (c->q_dtype == CSA2_BF16) ? cv.take<float>(attend_ws_floats((int)R, c->Hq, c->D, c->K, c->window)) : nullptr;
   const int64_t pc = pool_cols(c), nb = pool_nb(c);
@@ -481,9 +562,9 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   int32_t* q_limit = T > 1 ? cv.take<int32_t>((size_t)R) : nullptr;
   hipStream_t st = S(stream);
   if (q_limit && launch_causal_limits(c->B, T, c->n_keys, q_limit, st)) return CSA2_ERR_DEVICE;
-  // the first selection's histograms and control words are cleared here; the filter of
-  // each selection clears the slot the next one takes (more than 64 selections reuse the
-  // last slot, cleared again before each reuse)
+  // the first slot selection's histograms and control words are cleared here; the filter of
+  // each slot selection clears the slot the next one takes (more than 64 selections reuse
+  // the last slot, cleared again before each reuse)
   const int64_t slot_words = (int64_t)(topk_zero_bytes(R) / 4);
   if (slots > 0 && launch_fill_u32(tz[0].hist, slot_words, 0u, st)) return CSA2_ERR_DEVICE;
   int si = 0;
@@ -498,8 +579,7 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
   const int32_t* cur_pool = nullptr;  // the pool of the most recent Full layer
 
   AttendArgs a = attend_args(c->B, T, c->Hq, c->D, c->K, nullptr, c->q_dtype, c->kv_fmt, c->kv_codes, c->kv_scales,
-                             c->n_max,
-                             nullptr, c->softmax_scale, nullptr, c->out_dtype, nullptr);
+                             c->n_max, nullptr, c->softmax_scale, nullptr, c->out_dtype, nullptr);
   a.part = part;
   const int32_t* last_idx = nullptr;
   for (int i = 0; i < n_layers; ++i) {
@@ -508,42 +588,46 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
     a.out = L.out;
     a.lse = L.lse;
     set_swa(a, L.swa);
-    a.ctl = nullptr; a.hist2 = nullptr; a.candbuf = nullptr; a.idx_out = nullptr; a.idx = last_idx;
     if (L.mode != CSA2_REUSE) {
-      TopkWs t;
-      if (next_slot(t)) return CSA2_ERR_DEVICE;
       // a Reindex layer after a pooled Full layer scores only the pool's positions; the pool
-      // ascends, so its filtered candidates are in position order like a full scan's
+      // ascends, so its candidates are in position order like a full scan's
       const bool use_pool = (L.mode == CSA2_REINDEX) && cur_pool;
       const int64_t ncols = use_pool ? pc : c->n_max;
       const int32_t* cand = use_pool ? cur_pool : nullptr;
       ScoreArgs sa = score_args(c->prec, c->B, T, c->H, c->dk, L.q_idx, c->q_dtype, L.w, c->k, c->k_scale, c->n_max,
-                                c->n_keys, q_limit, cand, ncols, scores, t.hist, 1);
+                                c->n_keys, q_limit, cand, ncols, scores, nullptr, 1);
       // a Full layer whose keys a later Reindex layer of this call rescans in full reads
       // them with cached loads, so that the rescan finds them in the Infinity Cache
       // (measured: the rescan 23.6 us instead of 29 us at 16 x 131072).  With a pool the
       // Reindex layers read only the pool's positions and the cached scan measured slower.
       sa.keep = (L.mode == CSA2_FULL) && !pooled && reindex_after(layers, n_layers, i);
-      if (launch_score(sa, st)) return CSA2_ERR_DEVICE;
-      if (launch_topk_filter((int)R, ncols, scores, cand, c->K, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st,
-                             next_clear, next_clear ? slot_words : 0))
-        return CSA2_ERR_DEVICE;
-      if (a.q_bf16) {
-        a.ctl = t.ctl; a.hist2 = t.hist2; a.candbuf = cw.cand; a.cnt = cw.cnt; a.nreg = topk_regions((int)R, ncols);
-        a.rstride = topk_region_cols((int)R);
-        a.idx_out = L.idx;
+      if (local) {
+        // the score blocks list their candidates; one select workgroup per row finishes the
+        // exact Top-K straight into the layer's idx
+        sa.local = true;
+        sa.lc = local_for(lbase, R, ncols, c->K);
+        if (launch_score(sa, st)) return CSA2_ERR_DEVICE;
+        if (launch_topk_select((int)R, ncols, c->K, true, sa.lc, score_blocks(R, ncols), scores, cand, L.idx, nullptr,
+                               st))
+          return CSA2_ERR_DEVICE;
       } else {
+        TopkWs t;
+        if (next_slot(t)) return CSA2_ERR_DEVICE;
+        sa.hist = t.hist;
+        if (launch_score(sa, st)) return CSA2_ERR_DEVICE;
+        if (launch_topk_filter((int)R, ncols, scores, cand, c->K, t.hist, t.hist2, t.ctl, cw.cand, cw.cnt, st,
+                               next_clear, next_clear ? slot_words : 0))
+          return CSA2_ERR_DEVICE;
         if (launch_topk_finalize((int)R, ncols, c->K, true, t.ctl, t.hist2, cw.cand, cw.cnt, L.idx, nullptr, st))
           return CSA2_ERR_DEVICE;
-        a.idx = L.idx;
       }
       last_idx = L.idx;
     }
+    a.idx = last_idx;
     if (launch_attend(a, st)) return CSA2_ERR_DEVICE;
     if (pooled && L.mode == CSA2_FULL) {
       // the pool: block maxima of this layer's scores, their best pool_blocks blocks (lowest
-      // block on ties), expanded to positions (-1 past n_keys).  Runs after the attention,
-      // which has finished reading the candidate regions this selection reuses.
+      // block on ties), expanded to positions (-1 past n_keys)
       TopkWs t;
       if (next_slot(t)) return CSA2_ERR_DEVICE;
       int32_t* dst = L.pool ? L.pool : pool;

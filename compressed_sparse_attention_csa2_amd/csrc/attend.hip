@@ -27,7 +27,6 @@
 // fp32 path (fp32 queries): plain VALU, one block per (row, head), fp32 throughout.
 #include "common.hpp"
 #include "launch.hpp"
-#include "topk_dev.hpp"
 
 namespace csa2 {
 
@@ -345,25 +344,20 @@ struct AttLds {
   static constexpr size_t kOffS = kA + kP;
   static constexpr size_t kAP = G16 ? kA + kP + kS : kRows + (kA > kP ? kA : kP);
   static constexpr size_t kWork = kAP > kO ? kAP : kO;
-  static constexpr size_t kUnion0 = kWork > sizeof(FinalizeSmem) ? kWork : sizeof(FinalizeSmem);
-  static constexpr size_t kUnion = kUnion0 > WinLds<D>::kBytes ? kUnion0 : WinLds<D>::kBytes;
+  static constexpr size_t kUnion = kWork > WinLds<D>::kBytes ? kWork : WinLds<D>::kBytes;
 };
 
 // One block = one query row x 16 heads x one split of up to kAttSplit selected entries.
-// FROM_CAND: the block first derives the row's whole Top-K from the candidate list (every
-// block of the row does this identically; block (split 0, head group 0) writes idx_out).
 // With one partial in all (P == 1) the block writes the final output; otherwise it writes
 // its partial (normalised output, running max, sum) for k_attend_combine.
 // G16: the cache holds one E4M3 scale per 16 channels of each entry (the pages' layout).
 // The scale no longer factors out of the contractions; instead the split's scales are
 // staged in LDS as fp16, [group][entry], and multiply the fp16 key / value operands after
 // the E2M1 conversion (E2M1 * E4M3 is exact in fp16, so the operands stay exact).
-template <int D, bool FROM_CAND, bool G16>
+template <int D, bool G16>
 __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     int T, int Hq, int K, int S, int P, const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
-    const void* __restrict__ scales_v, int64_t n_max, const int32_t* __restrict__ idx, const RowCtl* __restrict__ ctl,
-    const uint32_t* __restrict__ hist2, const uint2* __restrict__ candbuf, const uint32_t* __restrict__ cnt, int nreg,
-    int rstride, int32_t* __restrict__ idx_out, float softmax_scale, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
+    const void* __restrict__ scales_v, int64_t n_max, const int32_t* __restrict__ idx, float softmax_scale, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
     float* __restrict__ part, float* __restrict__ part_ml, const uint8_t* __restrict__ wcodes,
     const float* __restrict__ wscales, int64_t wn_max, const int32_t* __restrict__ wend, int window) {
   constexpr int kRowBytes = D / 2;
@@ -389,7 +383,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   using L = AttLds<D, kWPT, G16>;
   constexpr int kNG = D / 16;                  // scale groups per entry (G16)
   __shared__ float s_scale[G16 ? 1 : D];
-  __shared__ int32_t s_idx[FROM_CAND ? CSA2_MAX_K_DEV : kAttSplit];
+  __shared__ int32_t s_idx[kAttSplit];
   __shared__ float s_red[kAttWaves][kAttHeads];
   __shared__ float s_m[kAttHeads], s_l[kAttHeads];
   __shared__ float s_down[kAttHeads];          // per head: softmax scale / the query prescale
@@ -428,24 +422,12 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   // now would wait for them, and with them for the query loads, before the selection starts)
   static_assert(CSA2_MAX_D_DEV <= kAttThreads, "one channel scale per thread");
   const float sc_reg = (!G16 && tid < D) ? scales[(int64_t)b * D + tid] : 0.0f;
-  const int32_t* sel;                           // the split's entries (LDS)
-  if (FROM_CAND) {
-    FinalizeSmem& fs = *reinterpret_cast<FinalizeSmem*>(s_u);
-    const RowCtl c = ctl[r];
-    const int keff = finalize_row<kAttThreads, true>(candbuf + (int64_t)r * nreg * rstride,
-                                               cnt + (int64_t)r * nreg, nreg, rstride, hist2 + (int64_t)r * kHistBins, c.beta,
-                                               c.above, c.keff, fs, s_idx, nullptr);
-    for (int i = keff + tid; i < S * kAttSplit; i += kAttThreads) s_idx[i] = -1;  // pad to whole splits
-    sel = s_idx + e0;  // the row's indices are stored at the end (a global store before a
-                       // barrier would make that barrier wait for every load in flight)
-  } else {
-    for (int i = tid; i < kAttSplit; i += kAttThreads) {
-      const int e = e0 + i;
-      const int32_t j = (e < K) ? idx[(int64_t)r * K + e] : -1;
-      s_idx[i] = (j >= 0 && j < n_max) ? j : -1;
-    }
-    sel = s_idx;
+  for (int i = tid; i < kAttSplit; i += kAttThreads) {
+    const int e = e0 + i;
+    const int32_t j = (e < K) ? idx[(int64_t)r * K + e] : -1;
+    s_idx[i] = (j >= 0 && j < n_max) ? j : -1;
   }
+  const int32_t* sel = s_idx;                    // the split's entries (LDS)
   if (!G16 && tid < D) s_scale[tid] = sc_reg;
   __syncthreads();  // s_scale, s_idx
 
@@ -770,8 +752,6 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
       ml[1] = l;
     }
   }
-  if (FROM_CAND && split == 0 && hg == 0 && idx_out)
-    for (int i = tid; i < K; i += kAttThreads) idx_out[(int64_t)r * K + i] = s_idx[i];
 }
 
 // Merge the P partials of (row, head group, channel tile) by log-sum-exp.  Thread t: head
@@ -953,14 +933,13 @@ size_t attend_ws_floats(int R, int Hq, int D, int K, int window) {
   return (size_t)R * P * Hq * D + (size_t)R * P * Hq * 2;
 }
 
-template <int D, bool FC, bool G16>
+template <int D, bool G16>
 static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
   // the window (if any) is one more block column, run beside the selection's splits
   dim3 g(S + (a.swa_codes ? 1 : 0), a.Hq / kAttHeads, a.B * a.T);
   float* part_ml = a.part ? a.part + (size_t)a.B * a.T * P * a.Hq * D : nullptr;
-  hipLaunchKernelGGL((k_attend_part<D, FC, G16>), g, dim3(kAttThreads), 0, st, a.T, a.Hq, a.K, S, P,
-                     (const uint16_t*)a.q, a.codes, a.scales, a.n_max, a.idx, a.ctl, a.hist2, a.candbuf, a.cnt,
-                     a.nreg, a.rstride, a.idx_out, a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml, a.swa_codes,
+  hipLaunchKernelGGL((k_attend_part<D, G16>), g, dim3(kAttThreads), 0, st, a.T, a.Hq, a.K, S, P,
+                     (const uint16_t*)a.q, a.codes, a.scales, a.n_max, a.idx, a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml, a.swa_codes,
                      a.swa_scales, a.swa_n_max, a.swa_end, a.window);
   if (P > 1)
     hipLaunchKernelGGL(k_attend_combine<D>, dim3(a.Hq / kAttHeads * (D / 128), a.B * a.T), dim3(256), 0, st, a.T,
@@ -969,18 +948,16 @@ static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
 
 template <int D>
 static void launch_mfma_d(const AttendArgs& a, int S, int P, hipStream_t st) {
-  const bool fc = a.candbuf != nullptr;
   if (a.g16)
-    fc ? launch_mfma<D, true, true>(a, S, P, st) : launch_mfma<D, false, true>(a, S, P, st);
+    launch_mfma<D, true>(a, S, P, st);
   else
-    fc ? launch_mfma<D, true, false>(a, S, P, st) : launch_mfma<D, false, false>(a, S, P, st);
+    launch_mfma<D, false>(a, S, P, st);
 }
 
 int launch_attend(const AttendArgs& a, hipStream_t st) {
   const int R = a.B * a.T;
   if (a.swa_codes && (a.window < 1 || a.window > kWinMax)) return -1;
   if (!a.q_bf16) {
-    if (a.candbuf) return -1;  // the fp32 path takes given indices
     if (a.g16)
       hipLaunchKernelGGL(k_attend_f32<true>, dim3(a.Hq, R), dim3(256), 0, st, a.T, a.Hq, a.D, a.K,
                          (const float*)a.q, a.codes, a.scales, a.n_max, a.idx, a.swa_codes, a.swa_scales,

@@ -28,6 +28,19 @@ int launch_quantize_fp4_rows(bool bf16, int B, int T, int D, const void* x, int6
 int launch_quantize_fp8(bool bf16, int B, int T, int D, const void* x, int64_t xsb, int64_t xst, const int32_t* n0,
                         int64_t n_max, uint8_t* codes, float* scales, hipStream_t st);
 
+// Candidate lists a LOCAL score kernel writes for k_topk_select: per row and score block
+// (nreg blocks of `stride` columns), the visible scores above the block's cut as (order
+// key, position) pairs in column order, their count, the cut (-1: every visible score
+// listed) and the block's visible count.
+struct LocalCand {
+  uint2* cand;      // [R][nreg][stride]
+  uint32_t* cnt;    // [R][nreg]
+  int32_t* cut;     // [R][nreg]
+  uint32_t* vis;    // [R][nreg]
+  int stride;       // columns per score block (and slots per region)
+  int K;            // the Top-K the lists serve (sizes the per-block cap)
+};
+
 struct ScoreArgs {
   int prec;           // 0 fp32, 1 fp8, 2 fp4
   bool q_bf16;
@@ -46,6 +59,8 @@ struct ScoreArgs {
   int key_div;        // 1, or the coarse block size when columns are blocks
   uint8_t* qstage;    // nullable: score_stage_bytes(R) of scratch for the many-row fp8 path
   bool keep;          // decode scan whose keys a later layer reads again: cached loads
+  bool local;         // decode fp8/fp4 scan that also writes candidate lists (lc)
+  LocalCand lc;
 };
 int launch_score(const ScoreArgs& a, hipStream_t st);
 // Many-row fp8 scoring (chunked prefill) stages the quantised query rows: E4M3 codes and
@@ -53,6 +68,17 @@ int launch_score(const ScoreArgs& a, hipStream_t st);
 inline size_t score_stage_bytes(int64_t R) { return (size_t)R * (32 * 64 + 32 * 4); }
 inline int score_tiled_min_rows() { return 8; }
 int score_cols_per_block(int64_t rows, int64_t ncols);
+// score blocks per row of a decode scan (= candidate regions of a LOCAL scan)
+inline int score_blocks(int64_t rows, int64_t ncols) {
+  const int cpb = score_cols_per_block(rows, ncols);
+  return (int)((ncols + cpb - 1) / cpb);
+}
+// The exact Top-K from a LOCAL scan's candidate lists (nreg regions per row; sorted: the
+// candidate positions ascend with the column, so the winners come out ascending).  Falls
+// back to the scores of a block whose list may miss winners.
+int launch_topk_select(int R, int64_t ncols, int K, bool sorted, const LocalCand& lc, int nreg, const float* scores,
+                       const int32_t* cand, int32_t* idx_out, float* val_out, hipStream_t st,
+                       uint32_t* clear = nullptr, int64_t clear_words = 0);
 
 // Top-K: histogram (zeroed on entry) -> filter into candidates (ctl zeroed on entry)
 // -> finalize (here, or fused into the attention kernel).
@@ -91,14 +117,6 @@ struct AttendArgs {
   void* out;
   bool out_bf16;
   float* lse;
-  // MFMA path only: take the Top-K from the candidate list (candbuf != nullptr) instead of idx
-  const RowCtl* ctl;
-  const uint32_t* hist2;
-  const uint2* candbuf;   // [R][nreg][rstride]
-  const uint32_t* cnt;    // [R][nreg]
-  int nreg;
-  int rstride;            // columns (candidate slots) per region
-  int32_t* idx_out;   // written when taking the Top-K from candidates (nullable)
   float* part;        // MFMA path with more than one partial: partial results (attend_ws_floats)
   // sliding window (swa_codes null: none): E4M3 rows [B][swa_n_max][D], scales [B][swa_n_max]
   const uint8_t* swa_codes;

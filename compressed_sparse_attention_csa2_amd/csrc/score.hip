@@ -13,6 +13,7 @@
 // scores' top bits for the Top-K select that follows.
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_dev.hpp"
 
 namespace csa2 {
 
@@ -139,6 +140,93 @@ __device__ __forceinline__ v8i quantize_query_operand_fp4(const QT* __restrict__
   return a;
 }
 
+// The block's candidate list for k_topk_select (LOCAL score kernels; 256 threads, kCols
+// columns whose order keys are in s_key, 0 where not visible, and whose first-level
+// histogram is in lhist).  Listed: the visible keys in bins above `cut`, where cut is the
+// lowest bin such that the bins above it hold at most `cap` keys (-1: every visible key
+// fits, the block is complete).  They are written in column order (ballot counts per
+// (pass, wave), one exclusive scan), so a full scan's list is sorted by position.
+template <int kCols>
+__device__ __forceinline__ void list_block_candidates(const uint32_t* lhist, const uint32_t* s_key,
+                                                      const int32_t* s_pos, bool cand, int64_t c0, int64_t lim,
+                                                      int64_t ncols, const LocalCand& lc, int r, int blk, int nblk,
+                                                      uint32_t* s_sh4, uint32_t* s_misc, uint32_t* s_off) {
+  constexpr int kPer = kCols / 256;  // column passes
+  static_assert(kPer * 4 <= 32, "one wave scans the (pass, wave) counts");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // cap: four times the winners a block of this row holds on average (K spread over the
+  // visible columns), plus 32, rounded up to a multiple of 32.  The cut falls on a whole
+  // first-level bin (a quarter octave of the score), and the bin holding the K-th score can
+  // hold a few times the winners above it, all of which must be listed.
+  const int64_t nvis = cand ? ncols : (lim + 1 < ncols ? lim + 1 : ncols);
+  const int64_t mu2 = nvis > 0 ? (4 * (int64_t)lc.K * kCols + nvis - 1) / nvis : kCols;
+  int64_t cap = ((mu2 + 32 + 31) / 32) * 32;
+  if (cap > kCols) cap = kCols;
+  uint32_t hb[8], local = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hb[i] = lhist[8 * tid + i];
+    local += hb[i];
+  }
+  const uint32_t suf = block_suffix<256, 256>(local, s_sh4);  // visible keys in bins >= 8 tid
+  if (tid == 0) {
+    s_misc[0] = suf;                 // the block's visible keys
+    s_misc[1] = 0xFFFFFFFFu;         // cut (none)
+    s_misc[2] = suf;                 // listed
+  }
+  __syncthreads();
+  const uint32_t total = s_misc[0];
+  if (total > (uint32_t)cap && suf > (uint32_t)cap && suf - local <= (uint32_t)cap) {
+    uint32_t acc = suf - local;      // keys in bins above this thread's
+    for (int i = 7; i >= 0; --i) {
+      if (acc + hb[i] > (uint32_t)cap) {
+        s_misc[1] = 8 * tid + i;
+        s_misc[2] = acc;
+        break;
+      }
+      acc += hb[i];
+    }
+  }
+  __syncthreads();
+  const uint32_t cut = s_misc[1];
+  uint64_t bal[kPer];
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const uint32_t key = s_key[p * 256 + tid];
+    bal[p] = __ballot(key != 0u && (cut == 0xFFFFFFFFu || hist_bin(key) > cut));
+  }
+  if (lane < kPer) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int p = 0; p < kPer; ++p)
+      if (p == lane) n = (uint32_t)__builtin_popcountll(bal[p]);
+    s_off[lane * 4 + wave] = n;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t v = (lane < kPer * 4) ? s_off[lane] : 0u;
+    const uint32_t sfx = wave_suffix(v);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 0);
+    if (lane < kPer * 4) s_off[lane] = tot - sfx;
+  }
+  __syncthreads();
+  uint2* creg = lc.cand + ((int64_t)r * nblk + blk) * lc.stride;
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    if ((bal[p] >> lane) & 1ull) {
+      const int j = p * 256 + tid;
+      const uint32_t slot = s_off[p * 4 + wave] + lanes_below(bal[p]);
+      creg[slot] = make_uint2(s_key[j], (uint32_t)(cand ? s_pos[j] : (int32_t)(c0 + j)));
+    }
+  }
+  if (tid == 0) {
+    const int64_t o = (int64_t)r * nblk + blk;
+    lc.cnt[o] = s_misc[2];
+    lc.cut[o] = (int32_t)cut;
+    lc.vis[o] = total;
+  }
+}
+
 // One block streams a contiguous chunk of 4 * TPW 32-key tiles; wave w takes tiles
 // w, w+4, ... so that the block's loads sweep the chunk in order.  Order of issue matters
 // because the vector-memory counter retires loads in order: the query row and head
@@ -147,20 +235,33 @@ __device__ __forceinline__ v8i quantize_query_operand_fp4(const QT* __restrict__
 // loop is fully unrolled so that every wait names exactly the tile it needs.
 // F4: the 4-bit indexer (E2M1 keys, 32 B per key plus the fp32 scale; the query quantised
 // to E2M1 per head); the same MFMA takes FP4 operands.
-template <typename QT, bool CAND, int TPW, bool F4 = false, bool KEEP = false>
+// LOCAL: the block also lists its Top-K candidates for k_topk_select (LocalCand): it keeps
+// its scores' order keys in LDS, finds the lowest first-level bin `cut` such that the bins
+// above it hold at most `cap` visible scores (cap from K and the row's visible count, about
+// four times the winners a block holds on average, plus a margin), and writes those scores'
+// (key, position) pairs in column order, their count, the cut and its visible count.  The
+// scores themselves still go to `scores` (nontemporal stores: they are read again only if
+// the selection has to fall back to them).
+template <typename QT, bool CAND, int TPW, bool F4 = false, bool KEEP = false, bool LOCAL = false>
 __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const QT* __restrict__ q,
                                                    const float* __restrict__ w, const uint8_t* __restrict__ k8,
                                                    const float* __restrict__ ks, int64_t n_max,
                                                    const int32_t* __restrict__ n_keys,
                                                    const int32_t* __restrict__ q_limit,
                                                    const int32_t* __restrict__ cand, float* __restrict__ scores,
-                                                   uint32_t* __restrict__ hist, int key_div) {
+                                                   uint32_t* __restrict__ hist, int key_div, LocalCand lc) {
   constexpr int P = (kPrefetch < TPW) ? kPrefetch : TPW;
   constexpr int kQBytes = 32 * 64 * (int)sizeof(QT);           // 4 KB (bf16) or 8 KB (fp32)
   constexpr int kQLoads = kQBytes / (16 * 256);                 // 16-byte loads per thread
+  constexpr int kCols = kScoreWaves * TPW * 32;                 // columns of one block
   __shared__ uint32_t lhist[kHistBins];
   __shared__ __align__(16) QT s_q[32 * 64];
   __shared__ float s_c[32];
+  __shared__ uint32_t s_key[LOCAL ? kCols : 1];                // order keys, 0 = not visible
+  __shared__ int32_t s_pos[LOCAL && CAND ? kCols : 1];         // candidate positions
+  __shared__ uint32_t s_sh4[4];
+  __shared__ uint32_t s_misc[4];
+  __shared__ uint32_t s_off[32];
   const int r = blockIdx.y, b = r / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5;
@@ -226,7 +327,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
   // 3. quantise the query from LDS while the key tiles are in flight
 #pragma unroll
   for (int i = 0; i < kQLoads; ++i) reinterpret_cast<v4i*>(s_q)[tid + 256 * i] = qraw[i];
-  if (hist)
+  if (hist || LOCAL)
     for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0;
   __syncthreads();
   float sq;
@@ -258,12 +359,25 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
     for (int j = 0; j < 16; ++j) part = fmaf(cvec[j], acc[j], part);
     const float total = part + __shfl_xor(part, 32);
     const float sc = v ? total * skl : kNegInf;
-    if (half == 0 && col < c1) {
+    if (LOCAL) {
+      const int j = (wave + kScoreWaves * i) * 32 + (lane & 31);  // column within the block
+      if (half == 0) {
+        const bool vv = col < c1 && visible(sc);
+        if (col < c1) __builtin_nontemporal_store(sc, srow + col);
+        s_key[j] = vv ? order_key(sc) : 0u;
+        if (CAND) s_pos[j] = cpos[i];
+        if (vv) atomicAdd(&lhist[hist_bin(order_key(sc))], 1u);
+      }
+    } else if (half == 0 && col < c1) {
       srow[col] = sc;
       if (hist && visible(sc)) atomicAdd(&lhist[hist_bin(order_key(sc))], 1u);
     }
   }
-  if (hist) {
+  if (LOCAL) {
+    __syncthreads();
+    list_block_candidates<kCols>(lhist, s_key, s_pos, CAND, c0, lim, ncols, lc, r, (int)blockIdx.x, (int)gridDim.x,
+                                 s_sh4, s_misc, s_off);
+  } else if (hist) {
     __syncthreads();
     for (int i = tid; i < kHistBins; i += 256) {
       const uint32_t vv = lhist[i];
@@ -477,17 +591,28 @@ template <typename QT, bool CAND, int TPW, bool F4>
 static void launch_fp8(const ScoreArgs& a, hipStream_t st) {
   const int cpb = kScoreWaves * TPW * 32;
   dim3 g((unsigned)((a.ncols + cpb - 1) / cpb), a.B * a.T);
+#define CSA2_SCORE(KEEP, LOC)                                                                                     \
+  hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4, KEEP, LOC>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q, \
+                     a.w, (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,   \
+                     a.key_div, a.lc)
+  if (a.local) {
+    if constexpr (!CAND) {
+      if (a.keep) {
+        CSA2_SCORE(true, true);
+        return;
+      }
+    }
+    CSA2_SCORE(false, true);
+    return;
+  }
   if constexpr (!CAND) {
     if (a.keep) {
-      hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4, true>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q,
-                         a.w, (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,
-                         a.key_div);
+      CSA2_SCORE(true, false);
       return;
     }
   }
-  hipLaunchKernelGGL((k_score_fp8<QT, CAND, TPW, F4>), g, dim3(256), 0, st, a.T, a.ncols, (const QT*)a.q, a.w,
-                     (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.cand, a.scores, a.hist,
-                     a.key_div);
+  CSA2_SCORE(false, false);
+#undef CSA2_SCORE
 }
 
 template <typename QT, bool CAND, bool F4>

@@ -1,0 +1,464 @@
+// Exact Top-K of one query row from the candidate lists its score blocks wrote (one
+// workgroup per row, k_topk_select).
+//
+// Every score block of a row lists the visible scores of its columns that lie in first-level
+// bins (top 11 order-key bits) above a block-local cut, the lowest bin such that the bins
+// above hold at most a few times the winners a block holds on average; it also records its
+// cut and how many visible scores it has (all of them listed: a complete block).  Let tau be
+// the K-th largest (score, lower position first) among the listed candidates and beta its
+// bin.  If every incomplete block's cut lies below beta, every unlisted score is in a bin
+// below beta, hence below tau, and the listed candidates hold the whole Top-K: the K-th of
+// the candidates is the K-th overall.  Otherwise (clustered scores, many equal scores, a
+// block holding more winners than it listed) the failing blocks are re-read whole from the
+// row's scores and the selection runs again over the enlarged list, in which no block can
+// fail any more (enlarging the list only raises tau).
+//
+// The selection itself is a radix select on the composite (key << 32 | ~position): the
+// threshold bin beta from the first-level histogram, the second-level bin inside it (the
+// next 11 key bits), the few candidates tied at both, their exact composite threshold
+// (rank counting, or an 8-bit-digit radix select), then an ordered compaction.  Lists are in
+// column order, so without a candidate map the winners come out by ascending position.
+#pragma once
+
+#include "topk_dev.hpp"
+
+namespace csa2 {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelMaxRegions = 8192;
+
+struct SelectSmem {
+  // h1 and h2 (16 KB, contiguous) also hold the staging owner map (uint16 region of each
+  // list item) before the histograms are built
+  alignas(16) uint32_t h1[kHistBins];  // read 16 bytes at a time
+  alignas(16) uint32_t h2[kHistBins];
+  uint32_t h256[256];
+  uint32_t misc[16];
+  uint32_t wsum[16];
+  uint32_t start[kSelMaxRegions + 1];  // exclusive prefix of the region sizes
+  uint32_t raw[kSelMaxRegions / 32];   // bit per region: re-read whole from the scores (fallback)
+  uint2 stage[kFinStage];
+  uint2 tied[kFinCap];
+  alignas(16) uint32_t win_pos[CSA2_MAX_K_DEV];
+  uint32_t win_key[CSA2_MAX_K_DEV];
+};
+
+// A row's candidates as one list in column order: region b holds start[b+1] - start[b]
+// items, either its listed (key, position) pairs, or (raw[b]) its whole column range read
+// from the row's scores (key 0 = not visible).
+struct RowList {
+  const uint2* regions;   // [nreg][stride]
+  const uint32_t* start;  // LDS
+  const uint32_t* raw;    // LDS bit mask
+  int nreg;
+  int stride;             // slots per region = columns per region
+  const float* srow;      // the row's scores (raw regions)
+  const int32_t* prow;    // the row's candidate positions (nullable: position = column)
+  // item k of region b
+  __device__ __forceinline__ uint2 get_in(int b, uint32_t k) const {
+    if (!((raw[b >> 5] >> (b & 31)) & 1u)) return regions[(int64_t)b * stride + k];
+    const int64_t col = (int64_t)b * stride + k;
+    const float sc = srow[col];
+    const int32_t pos = prow ? prow[col] : (int32_t)col;
+    return make_uint2((visible(sc) && pos >= 0) ? order_key(sc) : 0u, (uint32_t)pos);
+  }
+  __device__ __forceinline__ uint2 get(uint32_t i) const {
+    int lo = 0, hi = nreg - 1;  // last region whose start <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (start[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return get_in(lo, i - start[lo]);
+  }
+};
+
+// Wave 0 finds the bin of a 2048-bin LDS histogram that holds the need-th largest item (bins
+// scanned from the top, lane l summing bins 32 l .. 32 l + 31) and writes it to *bin_out
+// (kHistBins if the histogram holds fewer than need) and the items in higher bins to
+// *above_out.  One wave's scan instead of block-wide ones: the other waves only meet it at
+// the caller's next barrier.
+__device__ __forceinline__ void wave0_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* bin_out,
+                                                    uint32_t* above_out) {
+  if ((threadIdx.x >> 6) != 0) return;
+  const int lane = threadIdx.x & 63;
+  uint32_t hb[32], local = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint4 v = *reinterpret_cast<const uint4*>(&h[32 * lane + 4 * q]);
+    hb[4 * q] = v.x; hb[4 * q + 1] = v.y; hb[4 * q + 2] = v.z; hb[4 * q + 3] = v.w;
+    local += v.x + v.y + v.z + v.w;
+  }
+  const uint32_t suf = wave_suffix(local);  // items in bins >= 32 lane
+  if (lane == 0) {
+    *bin_out = kHistBins;
+    *above_out = 0;
+  }
+  if (need > 0 && suf >= need && suf - local < need) {  // one lane
+    uint32_t acc = suf - local;
+    for (int i = 31; i >= 0; --i) {
+      if (acc + hb[i] >= need) {
+        *bin_out = 32 * lane + i;
+        *above_out = acc;
+        break;
+      }
+      acc += hb[i];
+    }
+  }
+}
+
+// The first-level threshold over the list: sm.misc[0] = beta (kHistBins if fewer than keff
+// visible items), sm.misc[1] = visible items in bins above beta.  BUILD: count the list into
+// sm.h1 here (cleared here); otherwise the caller did, cleared h1 and h2 and synchronised.
+// Also clears sm.h2 for select_winners (BUILD) and resets the tied count.  src(i) gives item i.
+template <int NT, bool BUILD, typename SRC>
+__device__ __forceinline__ void select_first_level(const SRC& src, uint32_t M, uint32_t keff, SelectSmem& sm) {
+  const int tid = threadIdx.x;
+  if (BUILD) {
+    for (int i = tid; i < kHistBins; i += NT) {
+      sm.h1[i] = 0;
+      sm.h2[i] = 0;
+    }
+    __syncthreads();
+    for (uint32_t i = tid; i < M; i += NT) {
+      const uint32_t key = src(i).x;
+      if (key) atomicAdd(&sm.h1[hist_bin(key)], 1u);
+    }
+    __syncthreads();
+  }
+  wave0_threshold_bin(sm.h1, keff, &sm.misc[0], &sm.misc[1]);
+  if (tid == 0) sm.misc[4] = 0;  // tied count
+  __syncthreads();
+}
+
+// Given the first-level threshold (beta, above) of the list, the keff winners' positions in
+// list order (SORTED: ascending) to out_pos and, if out_key != nullptr, their order keys.
+template <int NT, bool SORTED, typename SRC>
+__device__ __forceinline__ void select_winners(const SRC& src, uint32_t M, uint32_t keff, uint32_t beta, uint32_t above,
+                               SelectSmem& sm, int32_t* out_pos, uint32_t* out_key) {
+  constexpr int kWaves = NT / 64;
+  constexpr int kCompPer = 64 / kWaves;  // list items per thread and compaction pass
+  static_assert(kCompPer * kWaves == 64 && kCompPer >= 1, "one wave scans the (pass, wave) counts");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // 1. second-level histogram of bin beta (h2 cleared before the first-level barrier) and
+  //    its threshold
+  for (uint32_t i = tid; i < M; i += NT) {
+    const uint32_t key = src(i).x;
+    if (key && hist_bin(key) == beta) atomicAdd(&sm.h2[hist2_bin(key)], 1u);
+  }
+  __syncthreads();
+  const uint32_t need1 = keff - above;
+  wave0_threshold_bin(sm.h2, need1, &sm.misc[2], &sm.misc[3]);
+  __syncthreads();
+  const uint32_t beta2 = sm.misc[2];
+  const uint32_t need3 = need1 - sm.misc[3];  // >= 1: bin (beta, beta2) holds the K-th
+  // 2. the candidates tied at (beta, beta2)
+  for (uint32_t base = 0; base < M; base += NT) {  // uniform trip count: wave_reserve needs every lane
+    const uint32_t i = base + tid;
+    const bool valid = i < M;
+    const uint2 c = valid ? src(i) : make_uint2(0u, 0u);
+    const bool tie = valid && c.x && is_tied(c.x, beta, beta2);
+    const uint32_t ts = wave_reserve(&sm.misc[4], tie);
+    if (tie && ts < (uint32_t)kFinCap) sm.tied[ts] = c;
+  }
+  __syncthreads();
+  // 3. their composite threshold (held in LDS, or - many equal scores - picked out of the
+  //    whole list again)
+  const uint32_t ntied = sm.misc[4];
+  uint64_t thr;
+  if (ntied <= (uint32_t)kFinCap) {
+    const uint2* tl = sm.tied;
+    thr = tied_threshold<NT, false>([tl](uint32_t i) { return tl[i]; }, ntied, need3, beta, beta2, sm);
+  } else {
+    thr = tied_threshold<NT, true>(src, M, need3, beta, beta2, sm);
+  }
+  // 4. the winners in list order: item base + 64 (kWaves u + wave) + lane goes to its
+  //    (pass u, wave) count's exclusive prefix plus its rank in the ballot
+  int32_t* dst_pos = SORTED ? out_pos : reinterpret_cast<int32_t*>(sm.win_pos);
+  uint32_t* dst_key = SORTED ? out_key : sm.win_key;
+  uint32_t carry = 0;
+  for (uint32_t base = 0; base < M; base += 64 * 64) {
+    uint64_t bal[kCompPer];
+    uint2 cv[kCompPer];
+#pragma unroll
+    for (int u = 0; u < kCompPer; ++u) {
+      const uint32_t i = base + 64 * (kWaves * u + wave) + lane;
+      const bool valid = i < M;
+      const uint2 c = valid ? src(i) : make_uint2(0u, 0u);
+      const uint32_t b1 = hist_bin(c.x), b2 = hist2_bin(c.x);
+      const uint64_t comp = ((uint64_t)c.x << 32) | (uint32_t)(~c.y);
+      const bool win = valid && c.x && (b1 > beta || (b1 == beta && (b2 > beta2 || (b2 == beta2 && comp >= thr))));
+      bal[u] = __ballot(win);
+      cv[u] = c;
+    }
+    if (lane < kCompPer) {
+      uint32_t n = 0;
+#pragma unroll
+      for (int u = 0; u < kCompPer; ++u)
+        if (u == lane) n = (uint32_t)__builtin_popcountll(bal[u]);
+      sm.h256[lane * kWaves + wave] = n;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t v = sm.h256[lane];
+      const uint32_t sfx = wave_suffix(v);
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 0);
+      sm.h256[64 + lane] = carry + tot - sfx;
+      if (lane == 0) sm.misc[5] = tot;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kCompPer; ++u) {
+      if ((bal[u] >> lane) & 1ull) {
+        const uint32_t slot = sm.h256[64 + u * kWaves + wave] + lanes_below(bal[u]);
+        if (slot < (uint32_t)CSA2_MAX_K_DEV) {
+          dst_pos[slot] = (int32_t)cv[u].y;
+          if (!SORTED || out_key) dst_key[slot] = cv[u].x;
+        }
+      }
+    }
+    carry += sm.misc[5];
+    __syncthreads();
+  }
+  if (!SORTED) {
+    // rank the winners by position (distinct positions): each counts the smaller ones
+    for (uint32_t i = tid; i < keff; i += NT) {
+      const uint32_t p = sm.win_pos[i];
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < keff; ++j) rank += (sm.win_pos[j] < p) ? 1u : 0u;
+      out_pos[rank] = (int32_t)p;
+      if (out_key) out_key[rank] = sm.win_key[i];
+    }
+    __syncthreads();
+  }
+}
+
+// The exact Top-K of row r from its score blocks' candidate lists (LocalCand), by the NT
+// threads of a workgroup (rows of at most MAXREG regions): the region counts' prefix, the
+// candidates staged in LDS, the first-level threshold and the check that every incomplete
+// block's cut lies below it (else those blocks are re-read from the scores and the selection
+// runs on the enlarged list), then the winners in list order.  Writes the keff = min(K,
+// visible) winners' positions to out_pos (ascending with SORTED, else ranked by position)
+// and, if out_key != nullptr, their order keys; returns keff.  Every thread must call it.
+// Fast path (at most 64 regions of at most 64 listed candidates, the decode rows): the
+// region counts and the first 64 slots of every region are loaded in one round, their
+// prefix is one wave's scan and the first-level histogram is counted from registers.
+struct SelectIn {
+  int nreg, stride;
+  int64_t ncols;
+  int K;
+  const uint2* candbuf;   // [R][nreg][stride]
+  const uint32_t* cnt;    // [R][nreg]
+  const int32_t* cut;
+  const uint32_t* vis;
+  const float* scores;    // [R][ncols]: the fallback's re-read
+  const int32_t* cand;    // [R][ncols] candidate positions, or nullptr (position = column)
+};
+
+template <bool SORTED, int NT, int MAXREG>
+__device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, SelectSmem& sm, int32_t* out_pos,
+                                               uint32_t* out_key) {
+  static_assert(MAXREG <= kSelMaxRegions && MAXREG >= 64, "region bound");
+  constexpr int kRP = (MAXREG + NT - 1) / NT;  // regions per thread (region tid + NT j)
+  constexpr int kSP = kFinStage / NT;         // staged items per thread
+  constexpr int kWaves = NT / 64;
+  constexpr int kFastRegions = 64;            // fast path: one wave's scan of the region counts
+  constexpr int kFastSlots = 64;              //   and at most 64 listed per region,
+  constexpr int kFastPer = kFastRegions * kFastSlots / NT;  // loaded with the counts (4 per thread)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nreg = in.nreg, stride = in.stride, K = in.K;
+  const int64_t ncols = in.ncols;
+  const uint2* __restrict__ candbuf = in.candbuf;
+  const uint32_t* __restrict__ cnt = in.cnt;
+  const int32_t* __restrict__ cut = in.cut;
+  const uint32_t* __restrict__ vis = in.vis;
+  const float* __restrict__ scores = in.scores;
+  const int32_t* __restrict__ cand = in.cand;
+  const bool few = nreg <= kFastRegions && stride >= kFastSlots;
+  // 0. every load issued together: the region counts, cuts and visible counts, and (few
+  //    regions) the first 64 slots of every region, whatever their counts turn out to be
+  uint32_t rcv[kRP], rvv[kRP];
+  int32_t rcutv[kRP];
+  // (unconditional loads from clamped addresses, masked afterwards: a load behind a branch
+  // is waited for where the branch joins)
+#pragma unroll
+  for (int j = 0; j < kRP; ++j) {
+    const int rg = tid + NT * j;
+    if (NT * j >= nreg) {  // uniform
+      rcv[j] = rvv[j] = 0u;
+      rcutv[j] = -1;
+      continue;
+    }
+    const int64_t o = (int64_t)r * nreg + (rg < nreg ? rg : nreg - 1);
+    rcv[j] = cnt[o];
+    rvv[j] = vis[o];
+    rcutv[j] = cut[o];
+    if (rg >= nreg) {
+      rcv[j] = rvv[j] = 0u;
+      rcutv[j] = -1;
+    }
+  }
+  const int fb = tid / (kFastSlots / kFastPer);            // this thread's region (fast path)
+  const int fk = tid % (kFastSlots / kFastPer);            // and its first slot
+  uint2 fv[kFastPer];
+  if (few) {  // uniform
+    const int64_t rb = (int64_t)r * nreg + (fb < nreg ? fb : nreg - 1);
+#pragma unroll
+    for (int u = 0; u < kFastPer; ++u) fv[u] = candbuf[rb * stride + fk + (kFastSlots / kFastPer) * u];
+  }
+  for (int i = tid; i < kSelMaxRegions / 32; i += NT) sm.raw[i] = 0u;
+  for (int i = tid; i < kHistBins; i += NT) {
+    sm.h1[i] = 0u;
+    sm.h2[i] = 0u;
+  }
+  // region starts (exclusive prefix of the sizes: the listed count, or the region's columns
+  // when it is re-read whole); sm.start[nreg] = the total
+  auto prefix = [&](bool with_raw) -> uint32_t {
+    uint32_t carry = 0;
+#pragma unroll
+    for (int j = 0; j < kRP; ++j) {
+      if (NT * j >= nreg) break;  // uniform
+      const int rg = tid + NT * j;
+      uint32_t v = rcv[j];
+      if (with_raw && rg < nreg && ((sm.raw[rg >> 5] >> (rg & 31)) & 1u)) {
+        const int64_t left = ncols - (int64_t)rg * stride;
+        v = (uint32_t)(left < stride ? left : stride);
+      }
+      const uint32_t suf = block_suffix<NT, NT>(v, sm.wsum);
+      if (tid == 0) sm.misc[8] = suf;
+      __syncthreads();
+      const uint32_t tot = sm.misc[8];
+      if (rg < nreg) sm.start[rg] = carry + tot - suf;
+      carry += tot;
+      __syncthreads();
+    }
+    if (tid == 0) sm.start[nreg] = carry;
+    return carry;
+  };
+  // 1. visible total, starts, and whether every region fits the fast path
+  uint32_t V, M = 0;
+  bool fast = false;
+  if (few) {
+    if (wave == 0) {  // regions are lanes: one wave's scans
+      const uint32_t c = rcv[0];
+      const uint32_t sfx = wave_suffix(c);
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 0);
+      const uint32_t vsfx = wave_suffix(rvv[0]);
+      if (lane < nreg) sm.start[lane] = tot - sfx;
+      if (lane == 0) {
+        sm.start[nreg] = tot;
+        sm.misc[9] = (uint32_t)__builtin_amdgcn_readlane((int)vsfx, 0);
+        sm.misc[11] = __ballot(c > (uint32_t)kFastSlots) ? 0u : 1u;
+      }
+    }
+    __syncthreads();
+    V = sm.misc[9];
+    fast = sm.misc[11] != 0;
+    M = sm.start[nreg];
+  } else {
+    uint32_t vloc = 0;
+#pragma unroll
+    for (int j = 0; j < kRP; ++j) vloc += rvv[j];
+    const uint32_t vsuf = block_suffix<NT, NT>(vloc, sm.wsum);
+    if (tid == 0) sm.misc[9] = vsuf;
+    __syncthreads();
+    V = sm.misc[9];
+  }
+  const uint32_t keff = V < (uint32_t)K ? V : (uint32_t)K;
+  RowList L{candbuf + (int64_t)r * nreg * stride, sm.start, sm.raw, nreg, stride, scores + (int64_t)r * ncols,
+            cand ? cand + (int64_t)r * ncols : nullptr};
+  const uint2* st = sm.stage;
+  int pass = 0;
+  if (keff > 0 && fast) {
+    // 2. stage the listed candidates from registers and count them into the first-level
+    //    histogram on the way (h1 was cleared before the barrier above)
+    if (fb < nreg) {
+      const uint32_t s0 = sm.start[fb], n = sm.start[fb + 1] - s0;
+#pragma unroll
+      for (int u = 0; u < kFastPer; ++u) {
+        const uint32_t k = fk + (kFastSlots / kFastPer) * u;
+        if (k < n) {
+          sm.stage[s0 + k] = fv[u];
+          atomicAdd(&sm.h1[hist_bin(fv[u].x)], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    auto src = [&](uint32_t i) -> uint2 { return st[i]; };
+    select_first_level<NT, false>(src, M, keff, sm);
+    const uint32_t beta = sm.misc[0], above = sm.misc[1];
+    // 3. the check (regions are lanes of wave 0)
+    if (wave == 0) {
+      const bool bad = lane < nreg && rvv[0] > rcv[0] && (beta >= (uint32_t)kHistBins || rcutv[0] >= (int32_t)beta);
+      const uint64_t bal = __ballot(bad);
+      if (lane < kSelMaxRegions / 32 && lane < 2) sm.raw[lane] = (uint32_t)(bal >> (32 * lane));
+      if (lane == 0) sm.misc[10] = bal ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!sm.misc[10]) {
+      select_winners<NT, SORTED>(src, M, keff, beta, above, sm, out_pos, out_key);
+      pass = 2;  // done
+    } else {
+      M = prefix(true);
+      __syncthreads();
+      pass = 1;  // the fallback over the enlarged list
+    }
+  } else if (keff > 0) {
+    M = prefix(false);
+    __syncthreads();
+  }
+  for (; pass < 2 && keff > 0; ++pass) {  // generic path; pass 1: the fallback over the enlarged list
+    const bool staged = M <= (uint32_t)kFinStage;
+    if (staged) {
+      // owner map (the region of every item), then every item's load in flight at once
+      uint16_t* owner = reinterpret_cast<uint16_t*>(sm.h1);
+      for (int b = wave; b < nreg; b += kWaves) {
+        const uint32_t s0 = sm.start[b], n = sm.start[b + 1] - s0;
+        for (uint32_t k = lane; k < n; k += 64) owner[s0 + k] = (uint16_t)b;
+      }
+      __syncthreads();
+      uint2 v[kSP];
+#pragma unroll
+      for (int u = 0; u < kSP; ++u) {
+        const uint32_t i = tid + NT * u;
+        if (i < M) {
+          const int b = owner[i];
+          v[u] = L.get_in(b, i - sm.start[b]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kSP; ++u) {
+        const uint32_t i = tid + NT * u;
+        if (i < M) sm.stage[i] = v[u];
+      }
+      __syncthreads();
+    }
+    auto src = [&](uint32_t i) -> uint2 { return staged ? st[i] : L.get(i); };
+    select_first_level<NT, true>(src, M, keff, sm);
+    const uint32_t beta = sm.misc[0], above = sm.misc[1];
+    if (pass == 0) {
+      // the check: an incomplete block whose cut is not below beta may hold unlisted winners
+      if (tid == 0) sm.misc[10] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kRP; ++j) {
+        const int rg = tid + NT * j;
+        if (rg < nreg && rvv[j] > rcv[j] && (beta >= (uint32_t)kHistBins || rcutv[j] >= (int32_t)beta)) {
+          atomicOr(&sm.raw[rg >> 5], 1u << (rg & 31));
+          sm.misc[10] = 1;
+        }
+      }
+      __syncthreads();
+      if (sm.misc[10]) {
+        M = prefix(true);
+        __syncthreads();
+        continue;
+      }
+    }
+    select_winners<NT, SORTED>(src, M, keff, beta, above, sm, out_pos, out_key);
+    break;
+  }
+  __syncthreads();
+  return keff;
+}
+
+}  // namespace csa2

@@ -20,17 +20,18 @@
 // scores degrade to every visible column (correct, slower).
 #include "common.hpp"
 #include "launch.hpp"
+#include "select_dev.hpp"
 #include "topk_dev.hpp"
 
 namespace csa2 {
 
-constexpr int kSelThreads = 256;
+constexpr int kFiltThreads = 256;
 constexpr int kHistColsPerBlock = 2048;
 constexpr int kFinThreads = 1024;
 
 // inclusive suffix sum over the 256 threads of a block: sum of v over threads >= tid
 __device__ __forceinline__ uint32_t block_suffix_sum(uint32_t v, uint32_t* sh4) {
-  return block_suffix<kSelThreads, kSelThreads>(v, sh4);
+  return block_suffix<kFiltThreads, kFiltThreads>(v, sh4);
 }
 
 template <bool CAND>
@@ -103,7 +104,7 @@ __device__ __forceinline__ void row_threshold(const uint32_t* __restrict__ hrow,
 
 // Many rows (chunked prefill): one block per row derives the row's threshold once, so
 // that the filter blocks read 16 bytes of it instead of the 8 KB histogram each.
-__global__ __launch_bounds__(kSelThreads) void k_topk_threshold(int K, const uint32_t* __restrict__ hist,
+__global__ __launch_bounds__(kFiltThreads) void k_topk_threshold(int K, const uint32_t* __restrict__ hist,
                                                                 RowCtl* __restrict__ ctl) {
   __shared__ uint32_t sh4[4];
   __shared__ uint32_t s_misc[8];
@@ -128,9 +129,9 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
                                                      RowCtl* __restrict__ ctl, uint2* __restrict__ candbuf,
                                                      uint32_t* __restrict__ cnt, uint4* __restrict__ clear,
                                                      int64_t clear_n4) {
-  constexpr int kWaves = kSelThreads / 64;
+  constexpr int kWaves = kFiltThreads / 64;
   constexpr int kCols = CTL ? kFilterColsPerBlock : kFilterColsNarrow;
-  constexpr int kPer = kCols / kSelThreads;  // 16 or 8 columns per thread
+  constexpr int kPer = kCols / kFiltThreads;  // 16 or 8 columns per thread
   __shared__ uint32_t lhist2[kHistBins];
   __shared__ uint32_t sh4[kWaves];
   __shared__ uint32_t s_misc[8];
@@ -140,8 +141,8 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the next selection's histograms and control words, idle until then, are cleared here
   // (the caller's fill then clears only the first selection's)
-  for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kSelThreads + tid; i < clear_n4;
-       i += (int64_t)gridDim.x * gridDim.y * kSelThreads)
+  for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kFiltThreads + tid; i < clear_n4;
+       i += (int64_t)gridDim.x * gridDim.y * kFiltThreads)
     clear[i] = make_uint4(0u, 0u, 0u, 0u);
 
   // the scores of this block's columns (all loads first, branch-free, clamped); pass i,
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
   int32_t pv[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int64_t c = c0 + tid + (int64_t)i * kSelThreads;
+    const int64_t c = c0 + tid + (int64_t)i * kFiltThreads;
     const int64_t cc = c < ncols ? c : ncols - 1;
     sv[i] = srow[cc];
     pv[i] = CAND ? prow[cc] : (int32_t)cc;
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
   }
 
   // threshold bin
-  for (int i = tid; i < kHistBins; i += kSelThreads) lhist2[i] = 0;
+  for (int i = tid; i < kHistBins; i += kFiltThreads) lhist2[i] = 0;
   uint32_t beta;
   if (CTL) {
     beta = ctl[r].beta;
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(int64_t ncols, const float*
       creg[slot] = make_uint2(order_key(sv[i]), (uint32_t)pv[i]);
     }
   }
-  for (int i = tid; i < kHistBins; i += kSelThreads) {
+  for (int i = tid; i < kHistBins; i += kFiltThreads) {
     const uint32_t v = lhist2[i];
     if (v) atomicAdd(&hist2[(int64_t)r * kHistBins + i], v);
   }
@@ -346,6 +347,43 @@ int launch_topk_hist(int R, int64_t ncols, const float* scores, const int32_t* c
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// One workgroup per row (select_row): idx_out [R][K] ascending (SORTED; otherwise ranked by
+// position), -1 padded; val_out (nullable) their scores.  clear: as in k_topk_filter (words of
+// a later selection zeroed on the side).
+template <bool SORTED, int NT, int MAXREG>
+__global__ __launch_bounds__(NT) void k_topk_select(SelectIn in, int32_t* __restrict__ idx_out,
+                                                    float* __restrict__ val_out, uint4* __restrict__ clear,
+                                                    int64_t clear_n4) {
+  __shared__ SelectSmem sm;
+  __shared__ int32_t s_pos[CSA2_MAX_K_DEV];
+  __shared__ uint32_t s_key[CSA2_MAX_K_DEV];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  for (int64_t i = (int64_t)r * NT + tid; i < clear_n4; i += (int64_t)gridDim.x * NT)
+    clear[i] = make_uint4(0u, 0u, 0u, 0u);
+  const int keff = (int)select_row<SORTED, NT, MAXREG>(in, r, sm, s_pos, s_key);
+  const int K = in.K;
+  for (int i = tid; i < K; i += NT) {
+    const bool have = i < keff;
+    idx_out[(int64_t)r * K + i] = have ? s_pos[i] : -1;
+    if (val_out) val_out[(int64_t)r * K + i] = have ? key_to_float(s_key[i]) : kNegInf;
+  }
+}
+
+int launch_topk_select(int R, int64_t ncols, int K, bool sorted, const LocalCand& lc, int nreg, const float* scores,
+                       const int32_t* cand, int32_t* idx_out, float* val_out, hipStream_t st, uint32_t* clear,
+                       int64_t clear_words) {
+  if (nreg > kSelMaxRegions) return -1;
+  if (clear && ((reinterpret_cast<uintptr_t>(clear) & 15) || clear_words % 4)) return -1;
+  uint4* clear4 = clear ? reinterpret_cast<uint4*>(clear) : nullptr;
+  const int64_t clear_n4 = clear ? clear_words / 4 : 0;
+  const SelectIn in{nreg, lc.stride, ncols, K, lc.cand, lc.cnt, lc.cut, lc.vis, scores, cand};
+#define CSA2_SELECT(S, NT, MR) \
+  hipLaunchKernelGGL((k_topk_select<S, NT, MR>), dim3(R), dim3(NT), 0, st, in, idx_out, val_out, clear4, clear_n4)
+  if (sorted) CSA2_SELECT(true, kSelThreads, kSelMaxRegions); else CSA2_SELECT(false, kSelThreads, kSelMaxRegions);
+#undef CSA2_SELECT
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 // Rows from which the threshold is computed once per row in its own kernel rather than
 // in every filter block (many rows: the histogram re-reads would cost more than a launch);
 // those filter blocks also take the wider regions.
@@ -365,9 +403,9 @@ int launch_topk_filter(int R, int64_t ncols, const float* scores, const int32_t*
   const int64_t clear_n4 = clear ? clear_words / 4 : 0;
   dim3 g((unsigned)topk_regions(R, ncols), R);
   const bool pre = R >= kThresholdKernelRows;
-  if (pre) hipLaunchKernelGGL(k_topk_threshold, dim3(R), dim3(kSelThreads), 0, st, K, hist, ctl);
+  if (pre) hipLaunchKernelGGL(k_topk_threshold, dim3(R), dim3(kFiltThreads), 0, st, K, hist, ctl);
 #define CSA2_FILTER(C, P)                                                                                      \
-  hipLaunchKernelGGL((k_topk_filter<C, P>), g, dim3(kSelThreads), 0, st, ncols, scores, cand, K, hist, hist2, ctl, \
+  hipLaunchKernelGGL((k_topk_filter<C, P>), g, dim3(kFiltThreads), 0, st, ncols, scores, cand, K, hist, hist2, ctl, \
                      candbuf, cnt, clear4, clear_n4)
   if (cand) {
     if (pre) CSA2_FILTER(true, true); else CSA2_FILTER(true, false);

@@ -83,9 +83,8 @@ __device__ __forceinline__ bool is_tied(uint32_t key, uint32_t beta, uint32_t be
 // composite >= the returned value.  src[0..n) holds the tied candidates (FILTERED =
 // false), or is the row's whole candidate list from which the tied ones are picked by
 // is_tied.  Ends with a block barrier; every thread gets the value.
-template <int NT, bool FILTERED, typename SRC>
-__device__ uint64_t tied_threshold(const SRC& src, uint32_t n, uint32_t need, uint32_t beta, uint32_t beta2,
-                                   FinalizeSmem& sm) {
+template <int NT, bool FILTERED, typename SRC, typename SM>
+__device__ __forceinline__ uint64_t tied_threshold(const SRC& src, uint32_t n, uint32_t need, uint32_t beta, uint32_t beta2, SM& sm) {
   const int tid = threadIdx.x;
   if (!FILTERED && n <= (uint32_t)kFinRankMax) {
     for (uint32_t i = tid; i < n; i += NT) {  // ranks are distinct: positions are
