@@ -89,6 +89,7 @@ __device__ __forceinline__ uint32_t e4m3_encode_select(float y) {
 // sign is taken from x, which also keeps the sign of a zero quotient.
 struct ExactQuotient {
   float k, s, r;
+  ExactQuotient() = default;
   __device__ __forceinline__ explicit ExactQuotient(float div) {
     k = div < 0x1p-92f ? 0x1p64f : 1.0f;
     s = div * k;

@@ -4,9 +4,13 @@
 // the main KV is stored as E2M1 and dequantised before attention.  The per-channel scale
 // is the absmax over the sequence's rows divided by 6 (the largest E2M1 magnitude).
 //
-// HBM-bound streaming kernels: coalesced row reads, one 32-bit word of packed codes per
-// thread, absmax by an order-preserving atomicMax on the fp32 bit pattern (abs values
-// are non-negative, so unsigned order == float order; the max does not depend on order).
+// HBM-bound streaming kernels: 16-byte coalesced row reads where the shape allows (else one
+// 32-bit word or one byte of codes per thread), absmax by an order-preserving atomicMax on
+// the fp32 bit pattern (abs values are non-negative, so unsigned order == float order; the
+// max does not depend on order).
+#include <algorithm>
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -67,6 +71,156 @@ __global__ __launch_bounds__(256) void k_fp4_pack(int T, int D, const XT* __rest
   *reinterpret_cast<uint32_t*>(codes + ((int64_t)b * n_max + row) * (D / 2) + w8 * 4) = word;
 }
 
+// One 16-byte chunk of x as fp32: 4 channels of fp32 input, 8 of bf16.
+template <typename XT>
+struct Chunk;
+template <>
+struct Chunk<float> {
+  static constexpr int C = 4;
+  template <bool NT>
+  __device__ __forceinline__ static void load(const float* p, float (&v)[C]) {
+    const v4f a = NT ? __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p)) : *reinterpret_cast<const v4f*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+};
+template <>
+struct Chunk<uint16_t> {
+  static constexpr int C = 8;
+  template <bool NT>
+  __device__ __forceinline__ static void load(const uint16_t* p, float (&v)[C]) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u a = NT ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p)) : *reinterpret_cast<const v4u*>(p);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
+  }
+};
+
+// Vector forms for rows of D channels in 16-byte chunks, where the chunks per row divide 256
+// and rows start 16-byte aligned.  Thread i of a 256-thread block reads chunk i % chunks of
+// rows r + i / chunks, stepping 256 / chunks rows, so every wave load is one contiguous
+// kilobyte.  absmax: each block walks a run of `rpb` rows with kAbsUnroll loads in flight
+// and few blocks (each adds one atomic per channel); pack: groups of kPackUnroll steps are
+// dealt to the blocks round robin.
+constexpr int kAbsUnroll = 8, kPackUnroll = 4;
+
+// absmax: per-thread maxima, reduced per channel in LDS (as unsigned: the bits of
+// non-negative fp32 values order like the values), then one global atomic per channel and block.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_fp4_absmax_v(int T, int D, const XT* __restrict__ x, int64_t xsb, int64_t xst,
+                                                      int rpb, uint32_t* __restrict__ amax_bits) {
+  constexpr int C = Chunk<XT>::C;
+  __shared__ uint32_t s_m[CSA2_MAX_D_DEV];
+  const int chunks = D / C, lanes_r = 256 / chunks;
+  const int w = threadIdx.x % chunks, rl = threadIdx.x / chunks;
+  const int b = blockIdx.y;
+  for (int i = threadIdx.x; i < D; i += 256) s_m[i] = 0u;
+  float m[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) m[i] = 0.0f;
+  const int t0 = blockIdx.x * rpb, t1 = min(T, t0 + rpb);
+  const XT* xb = x + b * xsb + C * w;
+  int t = t0 + rl;
+  for (; t + (kAbsUnroll - 1) * lanes_r < t1; t += kAbsUnroll * lanes_r) {
+    float v[kAbsUnroll][C];
+#pragma unroll
+    for (int u = 0; u < kAbsUnroll; ++u) Chunk<XT>::template load<false>(xb + (int64_t)(t + u * lanes_r) * xst, v[u]);
+#pragma unroll
+    for (int u = 0; u < kAbsUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < C; ++i) m[i] = fmaxf(m[i], fabsf(v[u][i]));
+  }
+  for (; t < t1; t += lanes_r) {
+    float v[C];
+    Chunk<XT>::template load<false>(xb + (int64_t)t * xst, v);
+#pragma unroll
+    for (int i = 0; i < C; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < C; ++i) atomicMax(&s_m[C * w + i], __float_as_uint(m[i]));
+  __syncthreads();
+  for (int i = threadIdx.x; i < D; i += 256) {
+    const uint32_t v = s_m[i];
+    if (v) atomicMax(&amax_bits[(int64_t)b * D + i], v);
+  }
+}
+
+// Codes of one chunk: C / 2 bytes (fp32 input: 16 bits, bf16: 32 bits).
+template <int C>
+struct ChunkCodes;
+template <>
+struct ChunkCodes<4> {
+  using T = uint16_t;
+};
+template <>
+struct ChunkCodes<8> {
+  using T = uint32_t;
+};
+
+// pack: each thread quantises its chunk's channels for every row it visits.  The quotient
+// x / s_c is one correctly rounded reciprocal per channel plus a fused-multiply-add
+// correction per value (ExactQuotient: the same value as the division); a scale that is not
+// positive and finite, or a quotient that overflows, takes the division itself.  The loads
+// are the last use of x, so they bypass the caches' retention.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_fp4_pack_v(int T, int D, const XT* __restrict__ x, int64_t xsb, int64_t xst,
+                                                    const int32_t* __restrict__ n0, int64_t n_max,
+                                                    uint8_t* __restrict__ codes, const float* __restrict__ scales) {
+  constexpr int C = Chunk<XT>::C;
+  using CT = typename ChunkCodes<C>::T;
+  const int chunks = D / C, lanes_r = 256 / chunks;
+  const int w = threadIdx.x % chunks, rl = threadIdx.x / chunks;
+  const int b = blockIdx.y;
+  float sc[C];
+  bool fast[C];
+  ExactQuotient eq[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    sc[i] = scales[(int64_t)b * D + C * w + i];
+    fast[i] = sc[i] > 0.0f && sc[i] <= 3.0e38f;
+    eq[i] = ExactQuotient(fast[i] ? sc[i] : 1.0f);
+  }
+  const int64_t base = n0 ? n0[b] : 0;
+  const XT* xb = x + b * xsb + C * w;
+  uint8_t* cb = codes + (int64_t)b * n_max * (D / 2) + (C / 2) * w;
+  auto encode = [&](const float (&v)[C]) -> CT {
+    CT word = 0;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      uint32_t code = 0u;
+      if (sc[i] != 0.0f) {
+        float y = fast[i] ? eq[i](v[i]) : v[i] / sc[i];
+        if (!(fabsf(y) <= 3.4e38f)) y = v[i] / sc[i];
+        code = e2m1_encode(y);
+      }
+      word |= (CT)(code << (4 * i));
+    }
+    return word;
+  };
+  auto store = [&](int tt, CT word) {
+    const int64_t row = base + tt;
+    if (row >= 0 && row < n_max) *reinterpret_cast<CT*>(cb + row * (D / 2)) = word;
+  };
+  const int R = kPackUnroll * lanes_r;  // rows per group
+  for (int g = blockIdx.x; (int64_t)g * R < T; g += gridDim.x) {
+    int t = g * R + rl;
+    if ((g + 1) * (int64_t)R <= T) {
+      float v[kPackUnroll][C];
+#pragma unroll
+      for (int u = 0; u < kPackUnroll; ++u) Chunk<XT>::template load<true>(xb + (int64_t)(t + u * lanes_r) * xst, v[u]);
+#pragma unroll
+      for (int u = 0; u < kPackUnroll; ++u) store(t + u * lanes_r, encode(v[u]));
+    } else {
+      for (; t < T; t += lanes_r) {
+        float v[C];
+        Chunk<XT>::template load<true>(xb + (int64_t)t * xst, v);
+        store(t, encode(v));
+      }
+    }
+  }
+}
+
 // pack for D not a multiple of 8: one thread per byte (two channels)
 template <typename XT>
 __global__ __launch_bounds__(256) void k_fp4_pack_bytes(int T, int D, const XT* __restrict__ x, int64_t xsb,
@@ -122,6 +276,61 @@ __global__ __launch_bounds__(256) void k_fp4g16_pack(int T, int D, const XT* __r
 }
 
 // E4M3 per row: one wave per row, lanes stride over the row's D values.
+// Vector form of the per-row E4M3 quantise for rows of D channels in 16-byte chunks whose
+// count per row divides 64: the chunks of one row sit in adjacent lanes of one wave, so the
+// row absmax is a butterfly over those lanes.  Groups of kPackUnroll block steps are dealt
+// to the blocks round robin; rows past T load a clamped row and store nothing, so every
+// lane takes part in every butterfly.  One ExactQuotient per row replaces the per-value
+// division (same quotient), with the division kept for scales it does not cover.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_fp8_rows_v(int T, int D, const XT* __restrict__ x, int64_t xsb, int64_t xst,
+                                                    const int32_t* __restrict__ n0, int64_t n_max,
+                                                    uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  constexpr int C = Chunk<XT>::C;
+  using CT = typename std::conditional<C == 4, uint32_t, uint64_t>::type;
+  const int chunks = D / C, lanes_r = 256 / chunks;
+  const int w = threadIdx.x % chunks, rl = threadIdx.x / chunks;
+  const int b = blockIdx.y;
+  const int64_t base = n0 ? n0[b] : 0;
+  const XT* xb = x + b * xsb + C * w;
+  const int R = kPackUnroll * lanes_r;
+  for (int g = blockIdx.x; (int64_t)g * R < T; g += gridDim.x) {
+    float v[kPackUnroll][C];
+#pragma unroll
+    for (int u = 0; u < kPackUnroll; ++u) {
+      const int t = min(g * R + rl + u * lanes_r, T - 1);
+      Chunk<XT>::template load<true>(xb + (int64_t)t * xst, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kPackUnroll; ++u) {
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < C; ++i) m = fmaxf(m, fabsf(v[u][i]));
+      for (int off = chunks >> 1; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const float sc = m / 448.0f;
+      const bool fast = sc > 0.0f && sc <= 3.0e38f;
+      const ExactQuotient eq(fast ? sc : 1.0f);
+      CT word = 0;
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        uint32_t code = 0u;
+        if (sc != 0.0f) {
+          float y = fast ? eq(v[u][i]) : v[u][i] / sc;
+          if (!(fabsf(y) <= 3.4e38f)) y = v[u][i] / sc;
+          code = e4m3_encode(y);
+        }
+        word |= (CT)code << (8 * i);
+      }
+      const int t = g * R + rl + u * lanes_r;
+      const int64_t row = base + t;
+      if (t < T && row >= 0 && row < n_max) {
+        *reinterpret_cast<CT*>(codes + ((int64_t)b * n_max + row) * D + C * w) = word;
+        if (w == 0) scales[(int64_t)b * n_max + row] = sc;
+      }
+    }
+  }
+}
+
 template <typename XT>
 __global__ __launch_bounds__(256) void k_fp8_rows(int T, int D, const XT* __restrict__ x, int64_t xsb, int64_t xst,
                                                   const int32_t* __restrict__ n0, int64_t n_max,
@@ -197,6 +406,32 @@ int launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st) {
 template <typename XT>
 static int quantize_fp4_t(bool compute, int B, int T, int D, const XT* x, int64_t xsb, int64_t xst, const int32_t* n0,
                           int64_t n_max, uint8_t* codes, float* scales, hipStream_t st) {
+  // vector kernels: 16-byte chunks whose count per row divides 256, 16-byte aligned rows
+  constexpr int C = Chunk<XT>::C;
+  const int chunks = D / C;
+  const bool vec = D % C == 0 && D <= CSA2_MAX_D_DEV && 256 % chunks == 0 &&
+                   (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (xst * sizeof(XT)) % 16 == 0 &&
+                   (xsb * sizeof(XT)) % 16 == 0;
+  if (vec) {
+    // absmax: about 512 blocks in all, runs of at least 4 unrolled steps
+    const int lanes_r = 256 / chunks;
+    int64_t rpb = ((int64_t)T * B + 511) / 512;
+    rpb = ((rpb + lanes_r - 1) / lanes_r) * lanes_r;
+    if (rpb < 4 * kAbsUnroll * lanes_r) rpb = 4 * kAbsUnroll * lanes_r;
+    if (compute) {
+      if (launch_fill_u32(reinterpret_cast<uint32_t*>(scales), (int64_t)B * D, 0u, st)) return -1;
+      hipLaunchKernelGGL(k_fp4_absmax_v<XT>, dim3((unsigned)((T + rpb - 1) / rpb), B), dim3(256), 0, st, T, D, x, xsb,
+                         xst, (int)rpb, reinterpret_cast<uint32_t*>(scales));
+      const int64_t n = (int64_t)B * D;
+      hipLaunchKernelGGL(k_fp4_finalize_scales, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n, scales);
+    }
+    // pack: about 8192 blocks in all, at most one per group of rows
+    const int64_t groups = ((int64_t)T + kPackUnroll * lanes_r - 1) / (kPackUnroll * lanes_r);
+    const int64_t per_seq = std::max<int64_t>(1, 8192 / B);
+    hipLaunchKernelGGL(k_fp4_pack_v<XT>, dim3((unsigned)std::min(groups, per_seq), B), dim3(256), 0, st, T, D, x, xsb,
+                       xst, n0, n_max, codes, scales);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   if (compute) {
     if (launch_fill_u32(reinterpret_cast<uint32_t*>(scales), (int64_t)B * D, 0u, st)) return -1;
     const int rows_per_block = 256;
@@ -240,6 +475,22 @@ int launch_quantize_fp4_g16(bool bf16, int B, int T, int D, const void* x, int64
 
 int launch_quantize_fp8(bool bf16, int B, int T, int D, const void* x, int64_t xsb, int64_t xst, const int32_t* n0,
                         int64_t n_max, uint8_t* codes, float* scales, hipStream_t st) {
+  const int C = bf16 ? Chunk<uint16_t>::C : Chunk<float>::C;
+  const int esz = bf16 ? 2 : 4;
+  const int chunks = D / C;
+  if (D % C == 0 && 64 % chunks == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (xst * esz) % 16 == 0 &&
+      (xsb * esz) % 16 == 0 && (reinterpret_cast<uintptr_t>(codes) & 7) == 0) {
+    // about 8192 blocks in all, at most one per group of rows
+    const int64_t groups = ((int64_t)T + kPackUnroll * (256 / chunks) - 1) / (kPackUnroll * (256 / chunks));
+    const dim3 gv((unsigned)std::min<int64_t>(groups, std::max(1, 8192 / B)), B);
+    if (bf16)
+      hipLaunchKernelGGL(k_fp8_rows_v<uint16_t>, gv, dim3(256), 0, st, T, D, (const uint16_t*)x, xsb, xst, n0, n_max,
+                         codes, scales);
+    else
+      hipLaunchKernelGGL(k_fp8_rows_v<float>, gv, dim3(256), 0, st, T, D, (const float*)x, xsb, xst, n0, n_max, codes,
+                         scales);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   dim3 g((T + 3) / 4, B);
   if (bf16)
     hipLaunchKernelGGL(k_fp8_rows<uint16_t>, g, dim3(256), 0, st, T, D, (const uint16_t*)x, xsb, xst, n0, n_max,

@@ -53,6 +53,22 @@ def test_quantize_fp4_bf16_input_and_append_given_scales():
     assert np.array_equal(codes.cpu().numpy(), codes_ref)
 
 
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_quantize_fp4_many_sequences(dt):
+    # eight sequences of 20001 rows: every pack block handles several row groups, the last
+    # group of each sequence is partial, and the absmax runs span many blocks per sequence
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((8, 20001, 512)).astype(np.float32)
+    x *= np.exp2(rng.integers(-6, 7, size=(1, 1, 512))).astype(np.float32)
+    xin = torch.from_numpy(x).to(dt).float().numpy()
+    codes_ref, s_ref = oracle.quantize_fp4(xin)
+    codes = torch.empty((8, 20001, 256), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((8, 512), dtype=torch.float32, device=DEV)
+    csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, to_dev(x, dt), codes, scales)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), codes_ref)
+
+
 def test_quantize_fp4_strided_and_special_values():
     x = np.zeros((1, 6, 64), np.float32)
     x[0, 0, :16] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, -0.1, -0.0, 1e-30, -6.0, 3.0, 0.5, 1e4, -1e4]
@@ -70,6 +86,27 @@ def test_quantize_fp4_strided_and_special_values():
     assert np.array_equal(codes.cpu().numpy(), ref)
 
 
+def test_quantize_fp4_extreme_given_scales():
+    # given scales far from absmax/6: tiny (below 2^-92), subnormal, negative, huge and
+    # infinite, with values over the whole fp32 exponent range, so that quotients underflow,
+    # overflow and change sign; the codes must match the oracle's fp32 division bit for bit
+    rng = np.random.default_rng(11)
+    T, D = 97, 64
+    mag = np.exp2(rng.uniform(-149, 127, size=(1, T, D)))
+    x = (np.where(rng.random((1, T, D)) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
+    x[0, :3] = 0.0
+    x[0, 1] = -0.0
+    s = np.array([1e-30, 1e-40, -0.5, 3e38, np.inf, -np.inf, 2.0 ** -92, 0.0,
+                  1.0, 7.5e-39, 1e30, -1e-35, 0.1, 2.0 ** 126, 6.0, 1e-20], np.float32)
+    s = np.tile(s, D // len(s))[None]
+    for dt in (torch.float32, torch.bfloat16):
+        xin = torch.from_numpy(x).to(dt).float().numpy()         # the values the kernel reads
+        ref_dt, _ = oracle.quantize_fp4(xin, scales=s)
+        codes = torch.empty((1, T, D // 2), dtype=torch.uint8, device=DEV)
+        csa2.quantize_kv(csa2.FMT_FP4_PER_CHANNEL, to_dev(x, dt), codes, to_dev(s), scale_policy=csa2.SCALE_GIVEN)
+        assert np.array_equal(codes.cpu().numpy(), ref_dt), dt
+
+
 def test_quantize_fp8_bitexact_and_special_values():
     wl = workloads.workload("full64k")
     k = np.stack([wl.index_keys(b, rows=2500) for b in range(2)])
@@ -79,6 +116,26 @@ def test_quantize_fp8_bitexact_and_special_values():
     k8 = torch.empty((2, 2500, 64), dtype=torch.uint8, device=DEV)
     ks = torch.empty((2, 2500), dtype=torch.float32, device=DEV)
     csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(k), k8, ks)
+    assert np.array_equal(ks.cpu().numpy(), ks_ref)
+    assert np.array_equal(k8.cpu().numpy(), k8_ref)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_quantize_fp8_many_sequences_append(dt):
+    # eight sequences appended at different offsets (one ending exactly at n_max); rows
+    # with a zero, a huge and a tiny absmax
+    rng = np.random.default_rng(29)
+    T, n_max = 20001, 24000
+    k = rng.standard_normal((8, T, 64)).astype(np.float32)
+    k[0, 5] = 0.0
+    k[1, 7] *= 1e30
+    k[2, 9] *= 1e-30
+    n0 = np.array([0, 17, 3999, 100, 5, 1, 2, 3990], np.int32)
+    kin = torch.from_numpy(k).to(dt).float().numpy()
+    k8_ref, ks_ref = oracle.quantize_fp8(kin, n_max=n_max, n0=n0)
+    k8 = torch.zeros((8, n_max, 64), dtype=torch.uint8, device=DEV)
+    ks = torch.zeros((8, n_max), dtype=torch.float32, device=DEV)
+    csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(k, dt), k8, ks, n0=to_dev(n0))
     assert np.array_equal(ks.cpu().numpy(), ks_ref)
     assert np.array_equal(k8.cpu().numpy(), k8_ref)
 
