@@ -143,7 +143,7 @@ def stream_ceiling(buf, flush, reps=5):
     best = 0.0
     sink = torch.empty(1, dtype=torch.int32, device="cuda")
     nbytes = buf.numel() * buf.element_size()
-    for blocks in (1024, 2048, 4096):
+    for blocks in (256, 512, 1024, 2048):
         ms = []
         for _ in range(reps):
             flush()

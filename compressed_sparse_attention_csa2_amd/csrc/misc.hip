@@ -121,21 +121,21 @@ int launch_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int 
 }
 
 // Read-stream ceiling probe: the grid sweeps `n16` 16-byte chunks with nontemporal loads,
-// four in flight per lane, and folds them into one word per thread.  The word is stored
+// eight in flight per lane, and folds them into one word per thread.  The word is stored
 // only when it equals a value the caller's data never produces, so the kernel's memory
 // traffic is the read alone.
 __global__ __launch_bounds__(256) void k_stream_read(const v4i_t* __restrict__ p, int64_t n16, uint32_t never,
                                                      uint32_t* __restrict__ sink) {
+  constexpr int U = 8;  // 16-byte loads in flight per lane
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t i = blockIdx.x * 256LL + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const v4i_t a = __builtin_nontemporal_load(p + i);
-    const v4i_t b = __builtin_nontemporal_load(p + i + stride);
-    const v4i_t c = __builtin_nontemporal_load(p + i + 2 * stride);
-    const v4i_t d = __builtin_nontemporal_load(p + i + 3 * stride);
-    acc ^= (uint32_t)(a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3]);
-    acc ^= (uint32_t)(c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3]);
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    v4i_t a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= (uint32_t)(a[u][0] ^ a[u][1] ^ a[u][2] ^ a[u][3]);
   }
   for (; i < n16; i += stride) {
     const v4i_t a = __builtin_nontemporal_load(p + i);

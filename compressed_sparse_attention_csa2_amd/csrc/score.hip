@@ -278,7 +278,13 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
   const int64_t c0 = (int64_t)blockIdx.x * (kScoreWaves * TPW * 32);
   const int64_t c1 = (c0 + kScoreWaves * TPW * 32 < ncols) ? c0 + kScoreWaves * TPW * 32 : ncols;
   constexpr int kKeyBytes = F4 ? 32 : 64;      // bytes per key row
-  const uint8_t* kb = k8 + (int64_t)b * n_max * kKeyBytes + half * (kKeyBytes / 2);
+  // fp8 keys: a tile's two 16-byte loads per lane each cover 16 whole keys (one kilobyte,
+  // every cache line fully used): load 0 gives lane l chunk l / 16 of key l % 16, load 1 the
+  // same chunk of key 16 + l % 16.  One row swap (v_permlane16_swap) then leaves lane
+  // (n, half) with bytes 32 half .. 32 half + 31 of key n, the MFMA operand layout.  FP4
+  // keys (32 bytes) are read in operand layout directly: lane (n, half) loads 16 bytes at
+  // 16 half, and the 64 lanes cover the tile's kilobyte whole.
+  const uint8_t* kb = k8 + (int64_t)b * n_max * kKeyBytes + (F4 ? half * 16 : 16 * (lane >> 4));
   const float* ksb = ks + (int64_t)b * n_max;
   const int32_t* crow = CAND ? cand + (int64_t)r * ncols : nullptr;
   // candidate positions of all this wave's tiles, loaded together up front: a position
@@ -286,38 +292,67 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
   // loads issued before it (the vector-memory counter retires in order)
   // (unconditional loads from a clamped column, masked afterwards: a load behind a branch
   // is waited for before the branch joins)
-  int32_t cpos[CAND ? TPW : 1];
+  // (fp8 keys also need the positions of the two keys this lane loads: cpos of key
+  // lane % 16 and 16 + lane % 16; the lane's own key lane % 32 is one of them)
+  int32_t cpos[CAND ? TPW : 1], cpos_lo[CAND && !F4 ? TPW : 1], cpos_hi[CAND && !F4 ? TPW : 1];
   if (CAND) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int64_t col = c0 + (int64_t)(wave + kScoreWaves * i) * 32 + (lane & 31);
-      cpos[i] = crow[col < c1 ? col : c1 - 1];
+      const int64_t t0 = c0 + (int64_t)(wave + kScoreWaves * i) * 32;
+      if constexpr (F4) {
+        const int64_t col = t0 + (lane & 31);
+        cpos[i] = crow[col < c1 ? col : c1 - 1];
+      } else {
+        const int64_t cl = t0 + (lane & 15), ch = cl + 16;
+        cpos_lo[i] = crow[cl < c1 ? cl : c1 - 1];
+        cpos_hi[i] = crow[ch < c1 ? ch : c1 - 1];
+      }
     }
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int64_t col = c0 + (int64_t)(wave + kScoreWaves * i) * 32 + (lane & 31);
-      if (col >= c1) cpos[i] = -1;
+      const int64_t t0 = c0 + (int64_t)(wave + kScoreWaves * i) * 32;
+      if constexpr (F4) {
+        if (t0 + (lane & 31) >= c1) cpos[i] = -1;
+      } else {
+        if (t0 + (lane & 15) >= c1) cpos_lo[i] = -1;
+        if (t0 + (lane & 15) + 16 >= c1) cpos_hi[i] = -1;
+        cpos[i] = (lane & 16) ? cpos_hi[i] : cpos_lo[i];
+      }
     }
   }
   v4i ka[P], kc[P];
   float skv[P];
   bool vis[P];
-  auto issue = [&](int i, int slot) {
-    const int64_t col = c0 + (int64_t)(wave + kScoreWaves * i) * 32 + (lane & 31);
+  // the row of column `col` when it is visible, else row 0 (always valid; masked later):
+  // branch-free loads
+  auto row_of = [&](int64_t col, int32_t cp, bool& v) -> int64_t {
     int64_t row = -1;
-    if (col < c1) row = CAND ? (int64_t)cpos[i] : col;
-    vis[slot] = row >= 0 && row <= lim;
-    // branch-free: invisible columns read row 0 (always valid) and are masked later
-    const int64_t rr = vis[slot] ? row : 0;
-    const v4i* src = reinterpret_cast<const v4i*>(kb + rr * kKeyBytes);
+    if (col < c1) row = CAND ? (int64_t)cp : col;
+    v = row >= 0 && row <= lim;
+    return v ? row : 0;
+  };
+  auto issue = [&](int i, int slot) {
+    const int64_t t0 = c0 + (int64_t)(wave + kScoreWaves * i) * 32;
+    const int64_t rr = row_of(t0 + (lane & 31), CAND ? cpos[i] : 0, vis[slot]);
+    const v4i* src;
+    const v4i* src2 = nullptr;
+    if constexpr (F4) {
+      src = reinterpret_cast<const v4i*>(kb + rr * kKeyBytes);
+    } else {
+      bool vl, vh;
+      const int64_t rl = row_of(t0 + (lane & 15), CAND ? cpos_lo[i] : 0, vl);
+      const int64_t rh = row_of(t0 + (lane & 15) + 16, CAND ? cpos_hi[i] : 0, vh);
+      src = reinterpret_cast<const v4i*>(kb + rl * kKeyBytes);
+      src2 = reinterpret_cast<const v4i*>(kb + rh * kKeyBytes);
+    }
     if (KEEP) {  // a later layer rescans these keys: ordinary loads, which leave them in the MALL
       ka[slot] = *src;
-      kc[slot] = F4 ? (v4i){0, 0, 0, 0} : *(src + 1);
+      kc[slot] = F4 ? (v4i){0, 0, 0, 0} : *src2;
       skv[slot] = ksb[rr];
     } else {
       ka[slot] = __builtin_nontemporal_load(src);
       if (F4) kc[slot] = (v4i){0, 0, 0, 0};
-      else kc[slot] = __builtin_nontemporal_load(src + 1);
+      else kc[slot] = __builtin_nontemporal_load(src2);
       skv[slot] = __builtin_nontemporal_load(ksb + rr);
     }
   };
@@ -347,8 +382,17 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
     const int u = i % P;
     const int64_t col = c0 + (int64_t)(wave + kScoreWaves * i) * 32 + (lane & 31);
     v8i B;
-    B[0] = ka[u][0]; B[1] = ka[u][1]; B[2] = ka[u][2]; B[3] = ka[u][3];
-    B[4] = kc[u][0]; B[5] = kc[u][1]; B[6] = kc[u][2]; B[7] = kc[u][3];
+    if constexpr (F4) {
+      B[0] = ka[u][0]; B[1] = ka[u][1]; B[2] = ka[u][2]; B[3] = ka[u][3];
+      B[4] = 0; B[5] = 0; B[6] = 0; B[7] = 0;
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const auto sw = __builtin_amdgcn_permlane16_swap((uint32_t)ka[u][d], (uint32_t)kc[u][d], false, false);
+        B[d] = (int)sw[0];
+        B[4 + d] = (int)sw[1];
+      }
+    }
     const bool v = vis[u];
     const float skl = skv[u];
     if (i + P < TPW) issue(i + P, u);

@@ -73,36 +73,40 @@ struct RowList {
 };
 
 // Wave 0 finds the bin of a 2048-bin LDS histogram that holds the need-th largest item (bins
-// scanned from the top, lane l summing bins 32 l .. 32 l + 31) and writes it to *bin_out
-// (kHistBins if the histogram holds fewer than need) and the items in higher bins to
-// *above_out.  One wave's scan instead of block-wide ones: the other waves only meet it at
-// the caller's next barrier.
+// counted from the top) and writes it to *bin_out (kHistBins if the histogram holds fewer
+// than need), the items in higher bins to *above_out and, if count_out != nullptr, the items
+// in that bin to *count_out (0 without one).  Lane l sums bins 32 l .. 32 l + 31;
+// one suffix scan finds the group of 32 bins, a second one (a bin per lane) the bin.  One
+// wave's scans instead of block-wide ones: the other waves only meet it at the caller's next
+// barrier.
 __device__ __forceinline__ void wave0_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* bin_out,
-                                                    uint32_t* above_out) {
+                                                    uint32_t* above_out, uint32_t* count_out = nullptr) {
   if ((threadIdx.x >> 6) != 0) return;
   const int lane = threadIdx.x & 63;
-  uint32_t hb[32], local = 0;
+  uint32_t local = 0;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const uint4 v = *reinterpret_cast<const uint4*>(&h[32 * lane + 4 * q]);
-    hb[4 * q] = v.x; hb[4 * q + 1] = v.y; hb[4 * q + 2] = v.z; hb[4 * q + 3] = v.w;
     local += v.x + v.y + v.z + v.w;
   }
   const uint32_t suf = wave_suffix(local);  // items in bins >= 32 lane
-  if (lane == 0) {
-    *bin_out = kHistBins;
-    *above_out = 0;
-  }
-  if (need > 0 && suf >= need && suf - local < need) {  // one lane
-    uint32_t acc = suf - local;
-    for (int i = 31; i >= 0; --i) {
-      if (acc + hb[i] >= need) {
-        *bin_out = 32 * lane + i;
-        *above_out = acc;
-        break;
-      }
-      acc += hb[i];
+  const uint64_t grp = __ballot(need > 0 && suf >= need && suf - local < need);
+  if (grp == 0) {
+    if (lane == 0) {
+      *bin_out = kHistBins;
+      *above_out = 0;
+      if (count_out) *count_out = 0;
     }
+    return;
+  }
+  const int g = __builtin_ctzll(grp);
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(suf - local), g);  // items above group g
+  const uint32_t hv = lane < 32 ? h[32 * g + lane] : 0u;
+  const uint32_t s2 = base + wave_suffix(hv);  // lane < 32: items in bins >= 32 g + lane
+  if (lane < 32 && s2 >= need && s2 - hv < need) {  // one lane (hv > 0 there)
+    *bin_out = 32 * g + lane;
+    *above_out = s2 - hv;
+    if (count_out) *count_out = hv;
   }
 }
 
@@ -130,49 +134,17 @@ __device__ __forceinline__ void select_first_level(const SRC& src, uint32_t M, u
   __syncthreads();
 }
 
-// Given the first-level threshold (beta, above) of the list, the keff winners' positions in
-// list order (SORTED: ascending) to out_pos and, if out_key != nullptr, their order keys.
+// The winners (composite >= thr: exactly keff items) of the list in list order, their
+// positions to out_pos (SORTED: ascending) and, if out_key != nullptr, their order keys.
+// Item base + 64 (kWaves u + wave) + lane goes to its (pass u, wave) count's exclusive
+// prefix plus its rank in the ballot.  Without SORTED the winners are then ranked by position.
 template <int NT, bool SORTED, typename SRC>
-__device__ __forceinline__ void select_winners(const SRC& src, uint32_t M, uint32_t keff, uint32_t beta, uint32_t above,
-                               SelectSmem& sm, int32_t* out_pos, uint32_t* out_key) {
+__device__ __forceinline__ void compact_winners(const SRC& src, uint32_t M, uint32_t keff, uint64_t thr,
+                                                SelectSmem& sm, int32_t* out_pos, uint32_t* out_key) {
   constexpr int kWaves = NT / 64;
   constexpr int kCompPer = 64 / kWaves;  // list items per thread and compaction pass
   static_assert(kCompPer * kWaves == 64 && kCompPer >= 1, "one wave scans the (pass, wave) counts");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // 1. second-level histogram of bin beta (h2 cleared before the first-level barrier) and
-  //    its threshold
-  for (uint32_t i = tid; i < M; i += NT) {
-    const uint32_t key = src(i).x;
-    if (key && hist_bin(key) == beta) atomicAdd(&sm.h2[hist2_bin(key)], 1u);
-  }
-  __syncthreads();
-  const uint32_t need1 = keff - above;
-  wave0_threshold_bin(sm.h2, need1, &sm.misc[2], &sm.misc[3]);
-  __syncthreads();
-  const uint32_t beta2 = sm.misc[2];
-  const uint32_t need3 = need1 - sm.misc[3];  // >= 1: bin (beta, beta2) holds the K-th
-  // 2. the candidates tied at (beta, beta2)
-  for (uint32_t base = 0; base < M; base += NT) {  // uniform trip count: wave_reserve needs every lane
-    const uint32_t i = base + tid;
-    const bool valid = i < M;
-    const uint2 c = valid ? src(i) : make_uint2(0u, 0u);
-    const bool tie = valid && c.x && is_tied(c.x, beta, beta2);
-    const uint32_t ts = wave_reserve(&sm.misc[4], tie);
-    if (tie && ts < (uint32_t)kFinCap) sm.tied[ts] = c;
-  }
-  __syncthreads();
-  // 3. their composite threshold (held in LDS, or - many equal scores - picked out of the
-  //    whole list again)
-  const uint32_t ntied = sm.misc[4];
-  uint64_t thr;
-  if (ntied <= (uint32_t)kFinCap) {
-    const uint2* tl = sm.tied;
-    thr = tied_threshold<NT, false>([tl](uint32_t i) { return tl[i]; }, ntied, need3, beta, beta2, sm);
-  } else {
-    thr = tied_threshold<NT, true>(src, M, need3, beta, beta2, sm);
-  }
-  // 4. the winners in list order: item base + 64 (kWaves u + wave) + lane goes to its
-  //    (pass u, wave) count's exclusive prefix plus its rank in the ballot
   int32_t* dst_pos = SORTED ? out_pos : reinterpret_cast<int32_t*>(sm.win_pos);
   uint32_t* dst_key = SORTED ? out_key : sm.win_key;
   uint32_t carry = 0;
@@ -184,10 +156,8 @@ __device__ __forceinline__ void select_winners(const SRC& src, uint32_t M, uint3
       const uint32_t i = base + 64 * (kWaves * u + wave) + lane;
       const bool valid = i < M;
       const uint2 c = valid ? src(i) : make_uint2(0u, 0u);
-      const uint32_t b1 = hist_bin(c.x), b2 = hist2_bin(c.x);
       const uint64_t comp = ((uint64_t)c.x << 32) | (uint32_t)(~c.y);
-      const bool win = valid && c.x && (b1 > beta || (b1 == beta && (b2 > beta2 || (b2 == beta2 && comp >= thr))));
-      bal[u] = __ballot(win);
+      bal[u] = __ballot(valid && c.x && comp >= thr);
       cv[u] = c;
     }
     if (lane < kCompPer) {
@@ -230,6 +200,47 @@ __device__ __forceinline__ void select_winners(const SRC& src, uint32_t M, uint3
     }
     __syncthreads();
   }
+}
+
+// Given the first-level threshold (beta, above) of the list, the keff winners' positions in
+// list order (SORTED: ascending) to out_pos and, if out_key != nullptr, their order keys.
+template <int NT, bool SORTED, typename SRC>
+__device__ __forceinline__ void select_winners(const SRC& src, uint32_t M, uint32_t keff, uint32_t beta, uint32_t above,
+                               SelectSmem& sm, int32_t* out_pos, uint32_t* out_key) {
+  const int tid = threadIdx.x;
+  // 1. second-level histogram of bin beta (h2 cleared before the first-level barrier) and
+  //    its threshold
+  for (uint32_t i = tid; i < M; i += NT) {
+    const uint32_t key = src(i).x;
+    if (key && hist_bin(key) == beta) atomicAdd(&sm.h2[hist2_bin(key)], 1u);
+  }
+  __syncthreads();
+  const uint32_t need1 = keff - above;
+  wave0_threshold_bin(sm.h2, need1, &sm.misc[2], &sm.misc[3]);
+  __syncthreads();
+  const uint32_t beta2 = sm.misc[2];
+  const uint32_t need3 = need1 - sm.misc[3];  // >= 1: bin (beta, beta2) holds the K-th
+  // 2. the candidates tied at (beta, beta2)
+  for (uint32_t base = 0; base < M; base += NT) {  // uniform trip count: wave_reserve needs every lane
+    const uint32_t i = base + tid;
+    const bool valid = i < M;
+    const uint2 c = valid ? src(i) : make_uint2(0u, 0u);
+    const bool tie = valid && c.x && is_tied(c.x, beta, beta2);
+    const uint32_t ts = wave_reserve(&sm.misc[4], tie);
+    if (tie && ts < (uint32_t)kFinCap) sm.tied[ts] = c;
+  }
+  __syncthreads();
+  // 3. their composite threshold (held in LDS, or - many equal scores - picked out of the
+  //    whole list again)
+  const uint32_t ntied = sm.misc[4];
+  uint64_t thr;
+  if (ntied <= (uint32_t)kFinCap) {
+    const uint2* tl = sm.tied;
+    thr = tied_threshold<NT, false>([tl](uint32_t i) { return tl[i]; }, ntied, need3, beta, beta2, sm);
+  } else {
+    thr = tied_threshold<NT, true>(src, M, need3, beta, beta2, sm);
+  }
+  compact_winners<NT, SORTED>(src, M, keff, thr, sm, out_pos, out_key);
 }
 
 // The exact Top-K of row r from its score blocks' candidate lists (LocalCand), by the NT
@@ -369,38 +380,107 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
   const uint2* st = sm.stage;
   int pass = 0;
   if (keff > 0 && fast) {
-    // 2. stage the listed candidates from registers and count them into the first-level
-    //    histogram on the way (h1 was cleared before the barrier above)
-    if (fb < nreg) {
-      const uint32_t s0 = sm.start[fb], n = sm.start[fb + 1] - s0;
+    // 2. stage the listed candidates from registers, and the range [lo, hi] of their keys
+    //    over the row
+    bool have[kFastPer];
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+    {
+      const uint32_t s0 = fb < nreg ? sm.start[fb] : 0u;
+      const uint32_t n = fb < nreg ? sm.start[fb + 1] - s0 : 0u;
 #pragma unroll
       for (int u = 0; u < kFastPer; ++u) {
         const uint32_t k = fk + (kFastSlots / kFastPer) * u;
-        if (k < n) {
+        have[u] = k < n;
+        if (have[u]) {
           sm.stage[s0 + k] = fv[u];
-          atomicAdd(&sm.h1[hist_bin(fv[u].x)], 1u);
+          kmn = min(kmn, fv[u].x);
+          kmx = max(kmx, fv[u].x);
         }
       }
     }
-    __syncthreads();
-    auto src = [&](uint32_t i) -> uint2 { return st[i]; };
-    select_first_level<NT, false>(src, M, keff, sm);
-    const uint32_t beta = sm.misc[0], above = sm.misc[1];
-    // 3. the check (regions are lanes of wave 0)
-    if (wave == 0) {
-      const bool bad = lane < nreg && rvv[0] > rcv[0] && (beta >= (uint32_t)kHistBins || rcutv[0] >= (int32_t)beta);
-      const uint64_t bal = __ballot(bad);
-      if (lane < kSelMaxRegions / 32 && lane < 2) sm.raw[lane] = (uint32_t)(bal >> (32 * lane));
-      if (lane == 0) sm.misc[10] = bal ? 1u : 0u;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o));
+      kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o));
+    }
+    if (lane == 0) {
+      sm.h256[wave] = kmn;
+      sm.h256[kWaves + wave] = kmx;
     }
     __syncthreads();
-    if (!sm.misc[10]) {
-      select_winners<NT, SORTED>(src, M, keff, beta, above, sm, out_pos, out_key);
-      pass = 2;  // done
+    // 3. a histogram over the keys' own range, bins of 2^sh keys (at most 2048 bins): the
+    //    listed keys sit in a few first-level bins, so counting them there would make every
+    //    atomic of a bin wait for the others; spread over their range they rarely collide
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      lo = min(lo, sm.h256[w]);
+      hi = max(hi, sm.h256[kWaves + w]);
+    }
+    const uint32_t span = hi - lo;  // M >= keff >= 1 items, so lo <= hi
+    const int bits = span ? 32 - __builtin_clz(span) : 0;
+    const int sh = bits > kHistBits ? bits - kHistBits : 0;
+#pragma unroll
+    for (int u = 0; u < kFastPer; ++u)
+      if (have[u]) atomicAdd(&sm.h1[(fv[u].x - lo) >> sh], 1u);
+    __syncthreads();
+    wave0_threshold_bin(sm.h1, keff, &sm.misc[0], &sm.misc[1], &sm.misc[2]);
+    if (tid == 0) sm.misc[4] = 0;  // tied count
+    __syncthreads();
+    const uint32_t tb = sm.misc[0], above = sm.misc[1], ntied = sm.misc[2];
+    if (tb >= (uint32_t)kHistBins) {  // uniform: fewer listed than keff, every incomplete block is re-read
+      if (wave == 0) {
+        const uint64_t bal = __ballot(lane < nreg && rvv[0] > rcv[0]);
+        if (lane < 2) sm.raw[lane] = (uint32_t)(bal >> (32 * lane));
+      }
+      __syncthreads();
+      pass = 1;
+    } else if (ntied <= (uint32_t)kFinCap) {  // uniform
+      // 4. the candidates in bin tb (the K-th among them), their exact composite threshold
+#pragma unroll
+      for (int u = 0; u < kFastPer; ++u) {
+        const bool tie = have[u] && ((fv[u].x - lo) >> sh) == tb;
+        const uint32_t ts = wave_reserve(&sm.misc[4], tie);
+        if (tie) sm.tied[ts] = fv[u];
+      }
+      __syncthreads();
+      const uint2* tl = sm.tied;
+      const uint64_t thr = tied_threshold<NT, false>([tl](uint32_t i) { return tl[i]; }, ntied, keff - above, 0u, 0u, sm);
+      // 5. the check (regions are lanes of wave 0): every incomplete block's cut must lie
+      //    below the first-level bin of the K-th score; the flag is read after the
+      //    compaction's barriers
+      const uint32_t beta = hist_bin((uint32_t)(thr >> 32));
+      if (wave == 0) {
+        const bool bad = lane < nreg && rvv[0] > rcv[0] && rcutv[0] >= (int32_t)beta;
+        const uint64_t bal = __ballot(bad);
+        if (lane < 2) sm.raw[lane] = (uint32_t)(bal >> (32 * lane));
+        if (lane == 0) sm.misc[14] = bal ? 1u : 0u;
+      }
+      auto src = [&](uint32_t i) -> uint2 { return st[i]; };
+      compact_winners<NT, SORTED>(src, M, keff, thr, sm, out_pos, out_key);
+      pass = sm.misc[14] ? 1 : 2;
     } else {
+      // many equal keys: the first-level selection over the staged list
+      auto src = [&](uint32_t i) -> uint2 { return st[i]; };
+      select_first_level<NT, true>(src, M, keff, sm);
+      const uint32_t beta = sm.misc[0], ab = sm.misc[1];
+      if (wave == 0) {
+        const bool bad = lane < nreg && rvv[0] > rcv[0] && (beta >= (uint32_t)kHistBins || rcutv[0] >= (int32_t)beta);
+        const uint64_t bal = __ballot(bad);
+        if (lane < 2) sm.raw[lane] = (uint32_t)(bal >> (32 * lane));
+        if (lane == 0) sm.misc[14] = bal ? 1u : 0u;
+      }
+      __syncthreads();
+      if (!sm.misc[14]) {
+        select_winners<NT, SORTED>(src, M, keff, beta, ab, sm, out_pos, out_key);
+        pass = 2;
+      } else {
+        pass = 1;
+      }
+    }
+    if (pass == 1) {  // the fallback over the enlarged list
       M = prefix(true);
       __syncthreads();
-      pass = 1;  // the fallback over the enlarged list
     }
   } else if (keff > 0) {
     M = prefix(false);
