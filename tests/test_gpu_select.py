@@ -143,3 +143,38 @@ def test_index_topk_short_visible_prefix(nk0):
     idx = csa2.index_topk(csa2.PREC_FP8, qd, wd, c["k8"], c["ks"], to_dev(nk), wl.K)
     ref = oracle.index_score(oracle.PREC_FP8, q, w, c["k8_ref"], c["ks_ref"], nk)
     check_topk_near_tie(idx.cpu().numpy(), ref, wl.K)
+
+
+@pytest.mark.parametrize("copies", [300, 1500])
+def test_index_topk_many_keys_tied_at_the_top(copies):
+    """The best key of each row copied to `copies` further random positions: that many keys
+    share the largest score (same codes, same scale), spread over the score blocks so that
+    each block lists its share.  With 1500 copies more than a thousand listed candidates hold
+    one key value, the selection's equal-key branch; the K winners are then the lowest
+    positions among the tied keys, exactly."""
+    wl = workloads.workload("group128k", B=2, N=131072, K=512)
+    n = wl.N
+    rng = np.random.default_rng(31)
+    kf = np.stack([wl.index_keys(b) for b in range(2)])
+    q, w = wl.index_query(), wl.head_weights()
+    k8r, ksr = oracle.quantize_fp8(kf)
+    nk = np.array([n, 100000], np.int32)
+    ref = oracle.index_score(oracle.PREC_FP8, q, w, k8r, ksr, nk)
+    for b in range(2):
+        best = int(np.argmax(ref[b, 0, :nk[b]]))
+        dst = rng.choice(nk[b], size=copies, replace=False)
+        kf[b, dst] = kf[b, best]
+    k8, ks = _keys_device(kf)
+    qd, wd = to_dev(q, torch.bfloat16), to_dev(w)
+    s = csa2.index_score(csa2.PREC_FP8, qd, wd, k8, ks, to_dev(nk)).cpu().numpy()
+    g = csa2.index_topk(csa2.PREC_FP8, qd, wd, k8, ks, to_dev(nk), wl.K).cpu().numpy()
+    for b in range(2):
+        row = s[b, 0, :nk[b]]
+        tied = np.flatnonzero(row == row.max())
+        assert tied.size >= copies + 1, b  # the premise: the copies tie with the best key
+        if tied.size >= wl.K:  # the lowest positions among the tied keys, exactly
+            assert np.array_equal(g[b, 0], tied[:wl.K]), b
+        else:                  # every tied key wins
+            assert np.all(np.isin(tied, g[b, 0])), b
+    k8r2, ksr2 = oracle.quantize_fp8(kf)
+    check_topk_near_tie(g, oracle.index_score(oracle.PREC_FP8, q, w, k8r2, ksr2, nk), wl.K)
