@@ -356,7 +356,7 @@ struct AttLds {
 // the E2M1 conversion (E2M1 * E4M3 is exact in fp16, so the operands stay exact).
 template <int D, bool G16>
 __global__ __launch_bounds__(kAttThreads) void k_attend_part(
-    int T, int Hq, int K, int S, int P, const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
+    int R, int T, int Hq, int K, int S, int P, const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const void* __restrict__ scales_v, int64_t n_max, const int32_t* __restrict__ idx, float softmax_scale, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
     float* __restrict__ part, float* __restrict__ part_ml, const uint8_t* __restrict__ wcodes,
     const float* __restrict__ wscales, int64_t wn_max, const int32_t* __restrict__ wend, int window) {
@@ -395,7 +395,15 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   float* sO = reinterpret_cast<float*>(s_u);  // [kWPT][16][D], used once the rows, sA, sP, sS are dead
   const float* scales = static_cast<const float*>(scales_v);
 
-  const int split = blockIdx.x, hg = blockIdx.y, r = blockIdx.z;
+  // XCD-aware order: workgroups are dealt to the 8 XCDs in turn (L2 per XCD), so a unit
+  // (row, split) takes workgroups wg with the same wg % 8 for all its head groups, which then
+  // gather the same rows through one L2.  Units past the last (grid rounded up) exit.
+  const int X = S + (wcodes ? 1 : 0);            // splits, plus the window's block
+  const int G = Hq / kAttHeads;                  // head groups
+  const int wg = blockIdx.x, slot = wg >> 3;
+  const int unit = (slot / G) * 8 + (wg & 7), hg = slot % G;
+  if (unit >= X * R) return;
+  const int split = unit % X, r = unit / X;
   if (split == S) {  // the sliding window's block (grid.x = S + 1 with a window)
     attend_window_block<D>(hg, r, T, Hq, q, wcodes, wscales, wn_max, wend, window, softmax_scale, P, S, part, part_ml,
                            s_u);
@@ -936,9 +944,11 @@ size_t attend_ws_floats(int R, int Hq, int D, int K, int window) {
 template <int D, bool G16>
 static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
   // the window (if any) is one more block column, run beside the selection's splits
-  dim3 g(S + (a.swa_codes ? 1 : 0), a.Hq / kAttHeads, a.B * a.T);
+  // one block per (unit = (row, split or window), head group), dealt in XCD-aware order
+  const int units = (S + (a.swa_codes ? 1 : 0)) * a.B * a.T;
+  const dim3 g((unsigned)(8 * (a.Hq / kAttHeads) * ((units + 7) / 8)));
   float* part_ml = a.part ? a.part + (size_t)a.B * a.T * P * a.Hq * D : nullptr;
-  hipLaunchKernelGGL((k_attend_part<D, G16>), g, dim3(kAttThreads), 0, st, a.T, a.Hq, a.K, S, P,
+  hipLaunchKernelGGL((k_attend_part<D, G16>), g, dim3(kAttThreads), 0, st, a.B * a.T, a.T, a.Hq, a.K, S, P,
                      (const uint16_t*)a.q, a.codes, a.scales, a.n_max, a.idx, a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml, a.swa_codes,
                      a.swa_scales, a.swa_n_max, a.swa_end, a.window);
   if (P > 1)

@@ -166,6 +166,26 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_mov<kDppHalfMirror>(v);
   return v + dpp_mov<kDppMirror>(v);
 }
+// unsigned minimum / maximum over the 64 lanes of the wave (DPP within rows, then the
+// four row results by readlane)
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+  v = min(v, dpp_mov_u<kDppXor1>(v));
+  v = min(v, dpp_mov_u<kDppXor2>(v));
+  v = min(v, dpp_mov_u<kDppHalfMirror>(v));
+  v = min(v, dpp_mov_u<kDppMirror>(v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return min(min(a, b), min(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  v = max(v, dpp_mov_u<kDppXor1>(v));
+  v = max(v, dpp_mov_u<kDppXor2>(v));
+  v = max(v, dpp_mov_u<kDppHalfMirror>(v));
+  v = max(v, dpp_mov_u<kDppMirror>(v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
 // inclusive suffix sum within each 16-lane row (lane i: lanes i..15 of its row), by
 // Hillis-Steele steps with DPP row shifts toward lower lanes (lanes past the row end add 0)
 template <int CTRL>

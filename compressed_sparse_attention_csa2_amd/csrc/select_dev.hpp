@@ -398,11 +398,8 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
         }
       }
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o));
-      kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o));
-    }
+    kmn = wave_min_u(kmn);
+    kmx = wave_max_u(kmx);
     if (lane == 0) {
       sm.h256[wave] = kmn;
       sm.h256[kWaves + wave] = kmx;
