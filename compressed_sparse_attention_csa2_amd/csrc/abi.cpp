@@ -118,6 +118,7 @@ LocalCand carve_local(Carve& c, size_t pairs, size_t regions) {
   l.vis = c.take<uint32_t>(regions);
   l.stride = 0;
   l.K = 0;
+  l.store = 0;
   return l;
 }
 // the same storage set up for a scan of ncols columns
@@ -214,7 +215,7 @@ ScoreArgs score_args(int prec, int B, int T, int H, int dk, const void* q, int q
   a.qstage = nullptr;
   a.keep = false;
   a.local = false;
-  a.lc = LocalCand{nullptr, nullptr, nullptr, nullptr, 0, 0};
+  a.lc = LocalCand{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
   return a;
 }
 
@@ -373,8 +374,7 @@ int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_
     a.local = true;
     a.lc = lc;
     if (launch_score(a, st)) return CSA2_ERR_DEVICE;
-    return dev_status(launch_topk_select((int)R, ncols, K, cand == nullptr, lc, score_blocks(R, ncols), scores, cand,
-                                         idx_out, val_out, st));
+    return dev_status(launch_topk_select(a, K, cand == nullptr, score_blocks(R, ncols), idx_out, val_out, st));
   }
   TopkWs t = carve_topk(c, R, ncols);
   const size_t stage = csa2_index_score_workspace_size(B, T, ncols);
@@ -606,9 +606,9 @@ int csa2_layer_group(const csa2_layer* layers, int n_layers, const csa2_group_ca
         // exact Top-K straight into the layer's idx
         sa.local = true;
         sa.lc = local_for(lbase, R, ncols, c->K);
+        sa.lc.store = pooled && L.mode == CSA2_FULL;  // the pool's block maxima read every score
         if (launch_score(sa, st)) return CSA2_ERR_DEVICE;
-        if (launch_topk_select((int)R, ncols, c->K, true, sa.lc, score_blocks(R, ncols), scores, cand, L.idx, nullptr,
-                               st))
+        if (launch_topk_select(sa, c->K, true, score_blocks(R, ncols), L.idx, nullptr, st))
           return CSA2_ERR_DEVICE;
       } else {
         TopkWs t;

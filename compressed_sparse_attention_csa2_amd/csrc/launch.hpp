@@ -39,6 +39,7 @@ struct LocalCand {
   uint32_t* vis;    // [R][nreg]
   int stride;       // columns per score block (and slots per region)
   int K;            // the Top-K the lists serve (sizes the per-block cap)
+  int store;        // also write every score (a later step reads them all)
 };
 
 struct ScoreArgs {
@@ -73,12 +74,13 @@ inline int score_blocks(int64_t rows, int64_t ncols) {
   const int cpb = score_cols_per_block(rows, ncols);
   return (int)((ncols + cpb - 1) / cpb);
 }
-// The exact Top-K from a LOCAL scan's candidate lists (nreg regions per row; sorted: the
-// candidate positions ascend with the column, so the winners come out ascending).  Falls
-// back to the scores of a block whose list may miss winners.
-int launch_topk_select(int R, int64_t ncols, int K, bool sorted, const LocalCand& lc, int nreg, const float* scores,
-                       const int32_t* cand, int32_t* idx_out, float* val_out, hipStream_t st,
-                       uint32_t* clear = nullptr, int64_t clear_words = 0);
+// The exact Top-K from a LOCAL scan's candidate lists (a = the scan's arguments: rows, its
+// lc, nreg = score_blocks regions per row; sorted: the candidate positions ascend with the
+// column, so the winners come out ascending).  A block whose list may miss winners is
+// re-scored by the select workgroup with the scan's arithmetic into a.scores ([R][ncols],
+// written only there) and re-read whole.
+int launch_topk_select(const ScoreArgs& a, int K, bool sorted, int nreg, int32_t* idx_out, float* val_out,
+                       hipStream_t st, uint32_t* clear = nullptr, int64_t clear_words = 0);
 
 // Top-K: histogram (zeroed on entry) -> filter into candidates (ctl zeroed on entry)
 // -> finalize (here, or fused into the attention kernel).

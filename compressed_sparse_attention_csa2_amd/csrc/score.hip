@@ -13,21 +13,10 @@
 // scores' top bits for the Top-K select that follows.
 #include "common.hpp"
 #include "launch.hpp"
+#include "score_dev.hpp"
 #include "topk_dev.hpp"
 
 namespace csa2 {
-
-// Visible rows of query row r: [0, lim].  n_keys counts cache rows; with key_div > 1 the
-// columns are blocks of key_div rows (coarse keys) and a block is visible iff it holds at
-// least one visible row.
-__device__ __forceinline__ int64_t visible_limit(int b, int r, int64_t n_max, const int32_t* n_keys,
-                                                 const int32_t* q_limit, int key_div) {
-  int64_t nk = n_keys[b];
-  if (key_div > 1) nk = (nk + key_div - 1) / key_div;
-  int64_t lim = (nk < n_max ? nk : n_max) - 1;
-  if (q_limit && q_limit[r] < lim) lim = q_limit[r];
-  return lim;
-}
 
 // ---------------------------------------------------------------------------- fp32 path
 // One thread per column; the query row is staged in LDS.  score = sum_h w_h (q_h . k_j),
@@ -80,65 +69,6 @@ __global__ __launch_bounds__(256) void k_score_f32(int T, int H, int dk, int64_t
 constexpr int kScoreWaves = 4;
 constexpr int kPrefetch = 4;  // 32-key tiles in flight per wave (16 x 16 B nontemporal loads per lane)
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-
-// Quantise lane's half of head (lane%32) of the query row to E4M3 and return the MFMA
-// A operand (byte j of the 32 = dim 32*(lane/32) + j), plus sq for that head.  SEL picks
-// the branch-free encoder: short candidate scans wait on this prologue and run faster with
-// it, long streaming scans hide it behind their loads and run faster without.
-template <typename QT, bool SEL>
-__device__ __forceinline__ v8i quantize_query_operand(const QT* __restrict__ qrow, int lane, float& sq_out) {
-  // two passes over the (cache-resident) 32 values so that few registers are live while
-  // the first key tiles are in flight: absmax, then encode
-  const int hq = lane & 31, half = lane >> 5;
-  const QT* p = qrow + hq * 64 + half * 32;
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(load_as_f32(p + i)));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
-  const float sq = amax / 448.0f;
-  const ExactQuotient div(sq);
-  const uint32_t keep = sq != 0.0f ? ~0u : 0u;  // an all-zero head encodes to zero bytes
-  v8i a;
-#pragma unroll
-  for (int wd = 0; wd < 8; ++wd) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const float y = div(load_as_f32(p + wd * 4 + bb));
-      word |= (SEL ? e4m3_encode_select(y) : e4m3_encode(y)) << (8 * bb);
-    }
-    a[wd] = (int)(word & keep);
-  }
-  sq_out = sq;
-  return a;
-}
-
-// The 4-bit variant: the head's 32 values of this lane as E2M1 (sq = absmax/6), packed
-// two per byte with the lower dim in the low nibble, in the first four operand dwords
-// (an FP4 operand of the 32x32x64 MFMA takes 16 bytes per lane).
-template <typename QT>
-__device__ __forceinline__ v8i quantize_query_operand_fp4(const QT* __restrict__ qrow, int lane, float& sq_out) {
-  const int hq = lane & 31, half = lane >> 5;
-  const QT* p = qrow + hq * 64 + half * 32;
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(load_as_f32(p + i)));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
-  const float sq = amax / 6.0f;
-  const ExactQuotient div(sq);
-  const uint32_t keep = sq != 0.0f ? ~0u : 0u;
-  v8i a = {};
-#pragma unroll
-  for (int wd = 0; wd < 4; ++wd) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) word |= e2m1_encode(div(load_as_f32(p + wd * 8 + nb))) << (4 * nb);
-    a[wd] = (int)(word & keep);
-  }
-  sq_out = sq;
-  return a;
-}
 
 // The block's candidate list for k_topk_select (LOCAL score kernels; 256 threads, kCols
 // columns whose order keys are in s_key, 0 where not visible, and whose first-level
@@ -240,8 +170,9 @@ __device__ __forceinline__ void list_block_candidates(const uint32_t* lhist, con
 // above it hold at most `cap` visible scores (cap from K and the row's visible count, about
 // four times the winners a block holds on average, plus a margin), and writes those scores'
 // (key, position) pairs in column order, their count, the cut and its visible count.  The
-// scores themselves still go to `scores` (nontemporal stores: they are read again only if
-// the selection has to fall back to them).
+// scores themselves are written only when a later step reads them all (lc.store: a Full
+// layer's candidate pool takes the block maxima); a selection that cannot trust a block's
+// list re-scores that block's columns itself (k_topk_select, with this kernel's arithmetic).
 template <typename QT, bool CAND, int TPW, bool F4 = false, bool KEEP = false, bool LOCAL = false>
 __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const QT* __restrict__ q,
                                                    const float* __restrict__ w, const uint8_t* __restrict__ k8,
@@ -372,8 +303,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
   if (tid < 32) s_c[tid] = wv * s_c[tid];
   __syncthreads();
   float cvec[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) cvec[i] = s_c[8 * (i >> 2) + 4 * half + (i & 3)];
+  tile_head_factors(s_c, half, cvec);
   float* srow = scores + (int64_t)r * ncols;
 
   // 4. stream the tiles
@@ -396,18 +326,12 @@ __global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const Q
     const bool v = vis[u];
     const float skl = skv[u];
     if (i + P < TPW) issue(i + P, u);
-    v16f acc = {};
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, F4 ? 4 : 0, F4 ? 4 : 0, 0, 0, 0, 0);
-    float part = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) part = fmaf(cvec[j], acc[j], part);
-    const float total = part + __shfl_xor(part, 32);
-    const float sc = v ? total * skl : kNegInf;
+    const float sc = tile_score<F4>(A, B, cvec, v, skl);
     if (LOCAL) {
       const int j = (wave + kScoreWaves * i) * 32 + (lane & 31);  // column within the block
       if (half == 0) {
         const bool vv = col < c1 && visible(sc);
-        if (col < c1) __builtin_nontemporal_store(sc, srow + col);
+        if (lc.store && col < c1) __builtin_nontemporal_store(sc, srow + col);
         s_key[j] = vv ? order_key(sc) : 0u;
         if (CAND) s_pos[j] = cpos[i];
         if (vv) atomicAdd(&lhist[hist_bin(order_key(sc))], 1u);

@@ -20,6 +20,7 @@
 // column order, so without a candidate map the winners come out by ascending position.
 #pragma once
 
+#include "score_dev.hpp"
 #include "topk_dev.hpp"
 
 namespace csa2 {
@@ -52,13 +53,13 @@ struct RowList {
   const uint32_t* raw;    // LDS bit mask
   int nreg;
   int stride;             // slots per region = columns per region
-  const float* srow;      // the row's scores (raw regions)
+  const float* srow;      // the row's re-scored scores (raw regions)
   const int32_t* prow;    // the row's candidate positions (nullable: position = column)
   // item k of region b
   __device__ __forceinline__ uint2 get_in(int b, uint32_t k) const {
     if (!((raw[b >> 5] >> (b & 31)) & 1u)) return regions[(int64_t)b * stride + k];
     const int64_t col = (int64_t)b * stride + k;
-    const float sc = srow[col];
+    const float sc = __builtin_nontemporal_load(srow + col);  // written by this workgroup (re-score)
     const int32_t pos = prow ? prow[col] : (int32_t)col;
     return make_uint2((visible(sc) && pos >= 0) ? order_key(sc) : 0u, (uint32_t)pos);
   }
@@ -254,16 +255,89 @@ __device__ __forceinline__ void select_winners(const SRC& src, uint32_t M, uint3
 // region counts and the first 64 slots of every region are loaded in one round, their
 // prefix is one wave's scan and the first-level histogram is counted from registers.
 struct SelectIn {
-  int nreg, stride;
+  int nreg, stride;       // regions per row; columns per region (= slots per region)
   int64_t ncols;
   int K;
   const uint2* candbuf;   // [R][nreg][stride]
   const uint32_t* cnt;    // [R][nreg]
   const int32_t* cut;
   const uint32_t* vis;
-  const float* scores;    // [R][ncols]: the fallback's re-read
+  float* scores;          // [R][ncols]: a re-scored region's scores (written and read only there)
   const int32_t* cand;    // [R][ncols] candidate positions, or nullptr (position = column)
+  // the scan's inputs, for the re-score (32 heads x 64 dims)
+  const void* q;          // [R][32][64] bf16 (q_bf16) or fp32
+  int q_bf16, f4;         // f4: the FP4 indexer (32-byte keys), else E4M3 (64-byte keys)
+  const float* w;         // [R][32]
+  const uint8_t* k;       // [B][n_max][64 or 32]
+  const float* ks;        // [B][n_max]
+  int64_t n_max;
+  const int32_t* n_keys;
+  const int32_t* q_limit;
+  int key_div, T;
 };
+
+// Re-score every region of row r marked in sm.raw into in.scores, with the score kernel's
+// arithmetic (score_dev.hpp: the same query operand, MFMA and epilogue order, so each score
+// is bit-identical to the one the scan computed), then make the stores visible to the
+// workgroup.  Uses sm.h2 (the query row) and sm.h256 (the head factors), which the
+// selection rebuilds afterwards.  Every thread must call it.
+template <int NT>
+__device__ __forceinline__ void rescore_raw_regions(const SelectIn& in, int r, SelectSmem& sm) {
+  constexpr int kWaves = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int b = r / in.T;
+  // the query row into LDS, the head weights into registers
+  const int qbytes = in.q_bf16 ? 32 * 64 * 2 : 32 * 64 * 4;
+  for (int i = tid; i < qbytes / 16; i += NT)
+    reinterpret_cast<uint4*>(sm.h2)[i] =
+        reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(in.q) + (int64_t)r * qbytes)[i];
+  const float wv = tid < 32 ? in.w[(int64_t)r * 32 + tid] : 0.0f;
+  __syncthreads();
+  float sq;
+  v8i A;
+  if (in.f4) {
+    A = in.q_bf16 ? quantize_query_operand_fp4(reinterpret_cast<const uint16_t*>(sm.h2), lane, sq)
+                  : quantize_query_operand_fp4(reinterpret_cast<const float*>(sm.h2), lane, sq);
+  } else {
+    A = in.q_bf16 ? quantize_query_operand<uint16_t, false>(reinterpret_cast<const uint16_t*>(sm.h2), lane, sq)
+                  : quantize_query_operand<float, false>(reinterpret_cast<const float*>(sm.h2), lane, sq);
+  }
+  float* s_c = reinterpret_cast<float*>(sm.h256);
+  if (wave == 0 && lane < 32) s_c[lane] = sq;
+  __syncthreads();
+  if (tid < 32) s_c[tid] = wv * s_c[tid];
+  __syncthreads();
+  float cvec[16];
+  tile_head_factors(s_c, half, cvec);
+  const int64_t lim = visible_limit(b, r, in.n_max, in.n_keys, in.q_limit, in.key_div);
+  const int kb = in.f4 ? 32 : 64;  // key bytes
+  const uint8_t* kbase = in.k + (int64_t)b * in.n_max * kb + (in.f4 ? 16 : 32) * half;
+  const float* ksb = in.ks + (int64_t)b * in.n_max;
+  const int32_t* crow = in.cand ? in.cand + (int64_t)r * in.ncols : nullptr;
+  float* srow = in.scores + (int64_t)r * in.ncols;
+  const int tiles = in.stride / 32;
+  for (int rg = 0; rg < in.nreg; ++rg) {
+    if (!((sm.raw[rg >> 5] >> (rg & 31)) & 1u)) continue;  // uniform
+    for (int t = wave; t < tiles; t += kWaves) {             // uniform per wave
+      const int64_t col = (int64_t)rg * in.stride + (int64_t)t * 32 + (lane & 31);
+      int64_t pos = -1;
+      if (col < in.ncols) pos = crow ? (int64_t)crow[col] : col;
+      const bool v = pos >= 0 && pos <= lim;
+      const int64_t rr = v ? pos : 0;
+      const v4i* src = reinterpret_cast<const v4i*>(kbase + rr * kb);
+      const v4i x0 = src[0];
+      v4i x1 = {0, 0, 0, 0};
+      if (!in.f4) x1 = src[1];
+      const v8i B = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      const float skl = ksb[rr];
+      const float sc = in.f4 ? tile_score<true>(A, B, cvec, v, skl) : tile_score<false>(A, B, cvec, v, skl);
+      if (half == 0 && col < in.ncols) srow[col] = sc;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 template <bool SORTED, int NT, int MAXREG>
 __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, SelectSmem& sm, int32_t* out_pos,
@@ -282,7 +356,7 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
   const uint32_t* __restrict__ cnt = in.cnt;
   const int32_t* __restrict__ cut = in.cut;
   const uint32_t* __restrict__ vis = in.vis;
-  const float* __restrict__ scores = in.scores;
+  const float* scores = in.scores;  // written by the re-score, read after it
   const int32_t* __restrict__ cand = in.cand;
   const bool few = nreg <= kFastRegions && stride >= kFastSlots;
   // 0. every load issued together: the region counts, cuts and visible counts, and (few
@@ -476,6 +550,7 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
       }
     }
     if (pass == 1) {  // the fallback over the enlarged list
+      rescore_raw_regions<NT>(in, r, sm);
       M = prefix(true);
       __syncthreads();
     }
@@ -526,6 +601,7 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
       }
       __syncthreads();
       if (sm.misc[10]) {
+        rescore_raw_regions<NT>(in, r, sm);
         M = prefix(true);
         __syncthreads();
         continue;

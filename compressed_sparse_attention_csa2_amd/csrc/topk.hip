@@ -369,17 +369,47 @@ __global__ __launch_bounds__(NT) void k_topk_select(SelectIn in, int32_t* __rest
   }
 }
 
-int launch_topk_select(int R, int64_t ncols, int K, bool sorted, const LocalCand& lc, int nreg, const float* scores,
-                       const int32_t* cand, int32_t* idx_out, float* val_out, hipStream_t st, uint32_t* clear,
-                       int64_t clear_words) {
+int launch_topk_select(const ScoreArgs& a, int K, bool sorted, int nreg, int32_t* idx_out, float* val_out,
+                       hipStream_t st, uint32_t* clear, int64_t clear_words) {
   if (nreg > kSelMaxRegions) return -1;
+  if (a.prec != 1 && a.prec != 2) return -1;  // the re-score covers the fp8 and FP4 indexers
+  if (a.H != 32 || a.dk != 64) return -1;
   if (clear && ((reinterpret_cast<uintptr_t>(clear) & 15) || clear_words % 4)) return -1;
   uint4* clear4 = clear ? reinterpret_cast<uint4*>(clear) : nullptr;
   const int64_t clear_n4 = clear ? clear_words / 4 : 0;
-  const SelectIn in{nreg, lc.stride, ncols, K, lc.cand, lc.cnt, lc.cut, lc.vis, scores, cand};
+  const int R = a.B * a.T;
+  const LocalCand& lc = a.lc;
+  SelectIn in{};
+  in.nreg = nreg;
+  in.stride = lc.stride;
+  in.ncols = a.ncols;
+  in.K = K;
+  in.candbuf = lc.cand;
+  in.cnt = lc.cnt;
+  in.cut = lc.cut;
+  in.vis = lc.vis;
+  in.scores = a.scores;
+  in.cand = a.cand;
+  in.q = a.q;
+  in.q_bf16 = a.q_bf16 ? 1 : 0;
+  in.f4 = a.prec == 2 ? 1 : 0;
+  in.w = a.w;
+  in.k = static_cast<const uint8_t*>(a.k);
+  in.ks = a.k_scale;
+  in.n_max = a.n_max;
+  in.n_keys = a.n_keys;
+  in.q_limit = a.q_limit;
+  in.key_div = a.key_div;
+  in.T = a.T;
 #define CSA2_SELECT(S, NT, MR) \
   hipLaunchKernelGGL((k_topk_select<S, NT, MR>), dim3(R), dim3(NT), 0, st, in, idx_out, val_out, clear4, clear_n4)
-  if (sorted) CSA2_SELECT(true, kSelThreads, kSelMaxRegions); else CSA2_SELECT(false, kSelThreads, kSelMaxRegions);
+  // one region count per thread covers rows of up to kSelThreads regions (2M columns at
+  // 2048 per region) and keeps the per-thread region state in few registers
+  if (nreg <= kSelThreads) {
+    if (sorted) CSA2_SELECT(true, kSelThreads, kSelThreads); else CSA2_SELECT(false, kSelThreads, kSelThreads);
+  } else {
+    if (sorted) CSA2_SELECT(true, kSelThreads, kSelMaxRegions); else CSA2_SELECT(false, kSelThreads, kSelMaxRegions);
+  }
 #undef CSA2_SELECT
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
