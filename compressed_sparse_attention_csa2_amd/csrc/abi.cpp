@@ -117,6 +117,7 @@ LocalCand carve_local(Carve& c, size_t pairs, size_t regions) {
   l.cut = c.take<int32_t>(regions);
   l.vis = c.take<uint32_t>(regions);
   l.stride = 0;
+  l.rcols = 0;
   l.K = 0;
   l.store = 0;
   return l;
@@ -124,14 +125,24 @@ LocalCand carve_local(Carve& c, size_t pairs, size_t regions) {
 // the same storage set up for a scan of ncols columns
 LocalCand local_for(LocalCand l, int64_t R, int64_t ncols, int K) {
   l.stride = score_cols_per_block(R, ncols);
+  l.rcols = l.stride;
   l.K = K;
   return l;
 }
-// decode scans (the fp8 / fp4 indexer's k_score_fp8; the many-row tiled kernel of chunked
-// prefill is not one) list their candidates for k_topk_select
-bool local_scan(int prec, int T, const int32_t* cand) {
-  const bool tiled = prec == CSA2_PREC_FP8 && !cand && T >= score_tiled_min_rows();
-  return prec != CSA2_PREC_FP32 && !tiled;
+// the many-row fp8 kernel of chunked prefill (no candidate map, T >= 8 rows per sequence)
+bool rows_scan(int prec, int T, const int32_t* cand) {
+  return prec == CSA2_PREC_FP8 && !cand && T >= score_tiled_min_rows();
+}
+// decode scans (the fp8 / fp4 indexer's k_score_fp8) list their candidates for k_topk_select
+bool local_scan(int prec, int T, const int32_t* cand) { return prec != CSA2_PREC_FP32 && !rows_scan(prec, T, cand); }
+// candidate lists of the many-row kernel: regions of rows_list_cols() columns, each listing
+// at most kRowsSlots candidates (its cap: four times a region's expected winners plus 32,
+// about 40 at 4096 x 262144; a region needing more is re-scored by the selection)
+constexpr int kRowsSlots = 128;
+int rows_regions(int64_t ncols) { return (int)((ncols + rows_list_cols() - 1) / rows_list_cols()); }
+size_t rows_local_ws(int64_t R, int64_t ncols) {
+  const size_t regions = (size_t)R * rows_regions(ncols);
+  return local_ws(regions * kRowsSlots, regions);
 }
 
 bool valid_dtype(int d) { return d == CSA2_F32 || d == CSA2_BF16; }
@@ -215,7 +226,7 @@ ScoreArgs score_args(int prec, int B, int T, int H, int dk, const void* q, int q
   a.qstage = nullptr;
   a.keep = false;
   a.local = false;
-  a.lc = LocalCand{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
+  a.lc = LocalCand{nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0};
   return a;
 }
 
@@ -343,8 +354,11 @@ int csa2_topk(int B, int T, int64_t ncols, const float* scores, const int32_t* c
 
 size_t csa2_index_topk_workspace_size(int B, int T, int64_t ncols, int) {
   const int64_t R = (int64_t)B * T;
-  // the candidate lists of a decode scan (fp8 / fp4), or the histogram filter's regions
-  const size_t sel = local_ws(R, ncols) > topk_ws(R, ncols) ? local_ws(R, ncols) : topk_ws(R, ncols);
+  // the candidate lists of a decode scan (fp8 / fp4) or of the many-row scan, or the
+  // histogram filter's regions; the scores (written by the fp32 scan, or where the selection
+  // re-scores a region); the many-row scan's staged query
+  size_t sel = local_ws(R, ncols) > topk_ws(R, ncols) ? local_ws(R, ncols) : topk_ws(R, ncols);
+  if (T >= score_tiled_min_rows() && rows_local_ws(R, ncols) > sel) sel = rows_local_ws(R, ncols);
   return align256((size_t)R * ncols * 4) + sel + csa2_index_score_workspace_size(B, T, ncols);
 }
 
@@ -375,6 +389,23 @@ int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_
     a.lc = lc;
     if (launch_score(a, st)) return CSA2_ERR_DEVICE;
     return dev_status(launch_topk_select(a, K, cand == nullptr, score_blocks(R, ncols), idx_out, val_out, st));
+  }
+  if (rows_scan(prec, T, cand)) {
+    // chunked prefill: the many-row blocks list their candidates per (row, region), one
+    // select workgroup per row finishes the exact Top-K
+    const int nreg = rows_regions(ncols);
+    LocalCand lc = carve_local(c, (size_t)R * nreg * kRowsSlots, (size_t)R * nreg);
+    lc.stride = kRowsSlots;
+    lc.rcols = rows_list_cols();
+    lc.K = K;
+    uint8_t* qstage = c.take<uint8_t>(csa2_index_score_workspace_size(B, T, ncols));
+    ScoreArgs a = score_args(prec, B, T, H, dk, q, q_dtype, w, k, k_scale, n_max, n_keys, q_limit, cand, ncols,
+                             scores, nullptr, 1);
+    a.qstage = qstage;
+    a.local = true;
+    a.lc = lc;
+    if (launch_score(a, st)) return CSA2_ERR_DEVICE;
+    return dev_status(launch_topk_select(a, K, true, nreg, idx_out, val_out, st));
   }
   TopkWs t = carve_topk(c, R, ncols);
   const size_t stage = csa2_index_score_workspace_size(B, T, ncols);

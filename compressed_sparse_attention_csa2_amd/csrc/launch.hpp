@@ -37,7 +37,8 @@ struct LocalCand {
   uint32_t* cnt;    // [R][nreg]
   int32_t* cut;     // [R][nreg]
   uint32_t* vis;    // [R][nreg]
-  int stride;       // columns per score block (and slots per region)
+  int stride;       // candidate slots per region (a block lists at most this many)
+  int rcols;        // columns per score block (region)
   int K;            // the Top-K the lists serve (sizes the per-block cap)
   int store;        // also write every score (a later step reads them all)
 };
@@ -69,6 +70,7 @@ int launch_score(const ScoreArgs& a, hipStream_t st);
 inline size_t score_stage_bytes(int64_t R) { return (size_t)R * (32 * 64 + 32 * 4); }
 inline int score_tiled_min_rows() { return 8; }
 int score_cols_per_block(int64_t rows, int64_t ncols);
+int rows_list_cols();  // columns per region of the many-row kernel's candidate lists
 // score blocks per row of a decode scan (= candidate regions of a LOCAL scan)
 inline int score_blocks(int64_t rows, int64_t ncols) {
   const int cpb = score_cols_per_block(rows, ncols);

@@ -92,6 +92,7 @@ __device__ __forceinline__ void list_block_candidates(const uint32_t* lhist, con
   const int64_t mu2 = nvis > 0 ? (4 * (int64_t)lc.K * kCols + nvis - 1) / nvis : kCols;
   int64_t cap = ((mu2 + 32 + 31) / 32) * 32;
   if (cap > kCols) cap = kCols;
+  if (cap > lc.stride) cap = lc.stride;  // the region's slots
   uint32_t hb[8], local = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -532,6 +533,214 @@ __global__ __launch_bounds__(64 * NW) void k_score_fp8_rows(int T, int64_t ncols
   }
 }
 
+// The many-row kernel with candidate lists instead of stored scores (chunked prefill's
+// Top-K): a block takes TT rows and RPB consecutive regions of NW x NKT x 32 columns, one
+// region at a time.  Per region it scores the TT rows, keeping each score in a register
+// (lane half h keeps tiles u with u % 2 == h: both halves hold a tile's totals after the
+// half exchange), and counts the rows' first-level histograms in LDS; then per row (rows
+// dealt to the waves) the cut, the lowest bin such that the bins above hold at most `cap`
+// visible scores (cap as for the decode lists, at most lc.stride slots), and the listing of
+// those scores' (key, position) pairs in column order (per-tile ballot counts, one wave scan
+// per row) into the row's region of lc, with its count, cut and visible count.
+template <int TT, int NW, int NKT, int RPB>
+__global__ __launch_bounds__(64 * NW) void k_score_fp8_rows_list(int T, int64_t ncols, int nblk,
+                                                                 const uint8_t* __restrict__ q8,
+                                                                 const float* __restrict__ cst,
+                                                                 const uint8_t* __restrict__ k8,
+                                                                 const float* __restrict__ ks, int64_t n_max,
+                                                                 const int32_t* __restrict__ n_keys,
+                                                                 const int32_t* __restrict__ q_limit, LocalCand lc) {
+  static_assert(NKT % 4 == 0, "key tiles come in groups of 4");
+  static_assert(TT % NW == 0, "whole rows per wave in the cut search");
+  constexpr int kRPW = TT / NW;          // rows per wave in the cut search
+  constexpr int NT = 64 * NW;
+  constexpr int kCols = NW * NKT * 32;   // columns of a region
+  constexpr int kTiles = NW * NKT;       // 32-column tiles of a region
+  static_assert(kTiles <= 64, "one wave scans a row's tile counts");
+  constexpr int kKept = NKT / 2;         // scores kept per lane and row
+  constexpr int kQRow = 80;
+  __shared__ __align__(16) uint8_t s_q8[TT * 32 * kQRow];
+  __shared__ __align__(16) float s_c[TT * 32];
+  __shared__ int64_t s_lim[TT];
+  __shared__ __align__(16) uint32_t s_h[TT * kHistBins / 2];
+  __shared__ uint32_t s_cnt[TT * kTiles];  // listed per (row, tile), then their exclusive offsets
+  __shared__ uint32_t s_cut[TT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int tiles_per_seq = (T + TT - 1) / TT;
+  const int b = blockIdx.x / tiles_per_seq;
+  const int t0 = (blockIdx.x % tiles_per_seq) * TT;
+  const int nrows = (T - t0 < TT) ? T - t0 : TT;
+  const int64_t r0 = (int64_t)b * T + t0;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(q8 + r0 * 32 * 64);
+    for (int i = tid; i < TT * 32 * 64 / 16; i += NT) {
+      const int hr = i >> 2, part = i & 3;
+      reinterpret_cast<uint4*>(s_q8 + hr * kQRow)[part] =
+          (i < nrows * 32 * 64 / 16) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    for (int i = tid; i < TT * 32; i += NT) s_c[i] = (i < nrows * 32) ? cst[r0 * 32 + i] : 0.0f;
+    if (tid < TT && tid >= nrows) s_lim[tid] = -1;
+    if (tid < nrows) {
+      int64_t nk = n_keys[b];
+      int64_t lim = (nk < n_max ? nk : n_max) - 1;
+      if (q_limit && q_limit[r0 + tid] < lim) lim = q_limit[r0 + tid];
+      s_lim[tid] = lim;
+    }
+  }
+  // whole-line key loads (as in k_score_fp8): load 0 gives lane l chunk l / 16 of key l % 16,
+  // load 1 the same chunk of key 16 + l % 16; one row swap makes the MFMA operand
+  const uint8_t* kb = k8 + (int64_t)b * n_max * 64 + 16 * (lane >> 4);
+  const float* ksb = ks + (int64_t)b * n_max;
+
+  for (int rg = 0; rg < RPB; ++rg) {
+    const int blk = blockIdx.y * RPB + rg;
+    if (blk >= nblk) break;  // uniform
+    const int64_t c0 = (int64_t)blk * kCols;
+    for (int i = tid; i < TT * kHistBins / 2; i += NT) s_h[i] = 0;
+    __syncthreads();
+
+    float keep[TT][kKept];
+#pragma unroll
+    for (int g = 0; g < NKT / 4; ++g) {
+      v8i B[4];
+      float sk[4];
+      int64_t col[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t tbase = c0 + (int64_t)(wave + NW * (4 * g + u)) * 32;
+        col[u] = tbase + (lane & 31);
+        const int64_t rr = col[u] < ncols ? col[u] : 0;  // clamped, masked below
+        const int64_t rl = tbase + (lane & 15) < ncols ? tbase + (lane & 15) : 0;
+        const int64_t rh = tbase + (lane & 15) + 16 < ncols ? tbase + (lane & 15) + 16 : 0;
+        const v4i x0 = *reinterpret_cast<const v4i*>(kb + rl * 64);
+        const v4i x1 = *reinterpret_cast<const v4i*>(kb + rh * 64);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const auto sw = __builtin_amdgcn_permlane16_swap((uint32_t)x0[d], (uint32_t)x1[d], false, false);
+          B[u][d] = (int)sw[0];
+          B[u][4 + d] = (int)sw[1];
+        }
+        sk[u] = ksb[rr];
+      }
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        const uint4* qa = reinterpret_cast<const uint4*>(s_q8 + (t * 32 + (lane & 31)) * kQRow + half * 32);
+        const uint4 a0 = qa[0], a1 = qa[1];
+        const v8i A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        float cvec[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 cc = *reinterpret_cast<const float4*>(&s_c[t * 32 + 8 * j + 4 * half]);
+          cvec[4 * j] = cc.x; cvec[4 * j + 1] = cc.y; cvec[4 * j + 2] = cc.z; cvec[4 * j + 3] = cc.w;
+        }
+        const int64_t lim = s_lim[t];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float sc = tile_score<false>(A, B[u], cvec, col[u] <= lim, sk[u]);
+          if (half == 0 && col[u] < ncols && visible(sc)) {
+            const uint32_t bin = hist_bin(order_key(sc));
+            atomicAdd(&s_h[t * (kHistBins / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
+          }
+          if ((u & 1) == half) keep[t][2 * g + (u >> 1)] = sc;  // col[u] > lim (incl. past ncols): -inf
+        }
+      }
+    }
+    __syncthreads();
+
+    // the cut of rows wave + NW rr: lane l holds bins 32 l .. 32 l + 31
+#pragma unroll
+    for (int rr = 0; rr < kRPW; ++rr) {
+      const int t = wave + NW * rr;
+      const int64_t lim = s_lim[t];
+      const int64_t nvis = lim + 1 < ncols ? lim + 1 : ncols;
+      const int64_t mu2 = nvis > 0 ? (4 * (int64_t)lc.K * kCols + nvis - 1) / nvis : kCols;
+      int64_t cap = ((mu2 + 32 + 31) / 32) * 32;
+      if (cap > kCols) cap = kCols;
+      if (cap > lc.stride) cap = lc.stride;
+      uint32_t local = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 w4 = *reinterpret_cast<const uint4*>(&s_h[t * (kHistBins / 2) + 16 * lane + 4 * q]);
+        local += (w4.x & 0xFFFFu) + (w4.x >> 16) + (w4.y & 0xFFFFu) + (w4.y >> 16) + (w4.z & 0xFFFFu) +
+                 (w4.z >> 16) + (w4.w & 0xFFFFu) + (w4.w >> 16);
+      }
+      const uint32_t suf = wave_suffix(local);  // visible scores in bins >= 32 lane
+      const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)suf, 0);
+      uint32_t cut = 0xFFFFFFFFu, listed = total;
+      const uint32_t need = (uint32_t)cap + 1;
+      if (total >= need) {  // uniform: the cut bin holds the (cap + 1)-th largest
+        const uint64_t grp = __ballot(suf >= need && suf - local < need);
+        const int gl = __builtin_ctzll(grp);
+        const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(suf - local), gl);
+        const uint32_t w2 = s_h[t * (kHistBins / 2) + 16 * gl + ((lane & 31) >> 1)];
+        const uint32_t hvv = lane < 32 ? ((lane & 1) ? w2 >> 16 : w2 & 0xFFFFu) : 0u;
+        const uint32_t s2 = base + wave_suffix(hvv);
+        const uint64_t hit = __ballot(lane < 32 && s2 >= need && s2 - hvv < need);
+        const int hl = __builtin_ctzll(hit);
+        cut = (uint32_t)(32 * gl + hl);
+        listed = (uint32_t)__builtin_amdgcn_readlane((int)(s2 - hvv), hl);
+      }
+      if (lane == 0) {
+        s_cut[t] = cut;
+        if (t < nrows) {
+          const int64_t o = (r0 + t) * nblk + blk;
+          lc.cnt[o] = listed;
+          lc.cut[o] = (int32_t)cut;
+          lc.vis[o] = total;
+        }
+      }
+    }
+    __syncthreads();
+    // per (row, tile) counts of the listed scores: kept slot k of lane (h, key) is tile
+    // wave + NW (4 (k / 2) + 2 (k % 2) + h); one ballot covers both halves' tiles
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const uint32_t cut = s_cut[t];
+#pragma unroll
+      for (int k = 0; k < kKept; ++k) {
+        const float sc = keep[t][k];
+        const bool pred = visible(sc) && (cut == 0xFFFFFFFFu || hist_bin(order_key(sc)) > cut);
+        const uint64_t bal = __ballot(pred);
+        if (lane == 0) {
+          const int tile0 = wave + NW * (4 * (k >> 1) + 2 * (k & 1));
+          s_cnt[t * kTiles + tile0] = (uint32_t)__builtin_popcountll(bal & 0xFFFFFFFFull);
+          s_cnt[t * kTiles + tile0 + NW] = (uint32_t)__builtin_popcountll(bal >> 32);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < kRPW; ++rr) {  // exclusive offsets in tile (= column) order
+      const int t = wave + NW * rr;
+      const uint32_t v = lane < kTiles ? s_cnt[t * kTiles + lane] : 0u;
+      const uint32_t sfx = wave_suffix(v);
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 0);
+      if (lane < kTiles) s_cnt[t * kTiles + lane] = tot - sfx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      if (t >= nrows) break;  // uniform
+      const uint32_t cut = s_cut[t];
+      uint2* creg = lc.cand + ((r0 + t) * nblk + blk) * lc.stride;
+#pragma unroll
+      for (int k = 0; k < kKept; ++k) {
+        const float sc = keep[t][k];
+        const uint32_t key = order_key(sc);
+        const bool pred = visible(sc) && (cut == 0xFFFFFFFFu || hist_bin(key) > cut);
+        const uint64_t bal = __ballot(pred);
+        const int tile = wave + NW * (4 * (k >> 1) + 2 * (k & 1) + half);
+        if (pred) {
+          const uint64_t mine = half ? (bal >> 32) : (bal & 0xFFFFFFFFull);
+          const uint32_t below = (uint32_t)__builtin_popcountll(mine & ((1ull << (lane & 31)) - 1ull));
+          const uint32_t slot = s_cnt[t * kTiles + tile] + below;
+          creg[slot] = make_uint2(key, (uint32_t)(c0 + (int64_t)tile * 32 + (lane & 31)));
+        }
+      }
+    }
+  }
+}
+
 template <int TT, int NW, int NKT, bool DB>
 static void launch_rows(const ScoreArgs& a, const uint8_t* q8, const float* cst, hipStream_t st) {
   const int64_t cpb = NW * NKT * 32;
@@ -539,6 +748,11 @@ static void launch_rows(const ScoreArgs& a, const uint8_t* q8, const float* cst,
   hipLaunchKernelGGL((k_score_fp8_rows<TT, NW, NKT, DB>), g, dim3(64 * NW), 0, st, a.T, a.ncols, q8, cst,
                      (const uint8_t*)a.k, a.k_scale, a.n_max, a.n_keys, a.q_limit, a.scores, a.hist);
 }
+
+// chunked prefill with candidate lists: 8 rows x one region of 1024 columns per block (measured
+// fastest: more regions per block, or wider regions, ran slower)
+constexpr int kRowsListWaves = 8, kRowsListTiles = 4, kRowsListRegions = 1;
+int rows_list_cols() { return kRowsListWaves * kRowsListTiles * 32; }
 
 int score_rows_tiled(const ScoreArgs& a) {
   return a.prec == 1 && a.cand == nullptr && a.key_div == 1 && a.T >= kRowTile && a.qstage != nullptr;
@@ -610,6 +824,15 @@ int launch_score(const ScoreArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(k_quant_query<uint16_t>, dim3(R), dim3(256), 0, st, (const uint16_t*)a.q, a.w, q8, cst);
     else
       hipLaunchKernelGGL(k_quant_query<float>, dim3(R), dim3(256), 0, st, (const float*)a.q, a.w, q8, cst);
+    if (a.local) {
+      const int nblk = (int)((a.ncols + rows_list_cols() - 1) / rows_list_cols());
+      const dim3 g((unsigned)(a.B * ((a.T + kRowTile - 1) / kRowTile)),
+                   (unsigned)((nblk + kRowsListRegions - 1) / kRowsListRegions));
+      hipLaunchKernelGGL((k_score_fp8_rows_list<kRowTile, kRowsListWaves, kRowsListTiles, kRowsListRegions>), g,
+                         dim3(64 * kRowsListWaves), 0, st, a.T, a.ncols, nblk, q8, cst, (const uint8_t*)a.k,
+                         a.k_scale, a.n_max, a.n_keys, a.q_limit, a.lc);
+      return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
     // 8 rows x 4096 keys per block, single-buffered key groups: the variant measured
     // fastest (double buffering or 16-row tiles cost occupancy and ran slower)
     launch_rows<kRowTile, 4, 32, false>(a, q8, cst, st);

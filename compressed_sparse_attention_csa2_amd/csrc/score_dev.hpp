@@ -84,16 +84,24 @@ __device__ __forceinline__ v8i quantize_query_operand_fp4(const QT* __restrict__
 // operand B (lane l: key l % 32, bytes 32 (l / 32) .. + 31 of fp8 keys, or 16 (l / 32) .. + 15
 // of FP4 keys), then the head-weighted sum: 16 in-lane FMAs over this lane's heads (cvec =
 // their c_h = w_h sq_h) in a fixed order, plus lane l ^ 32's 16.  Invisible keys score -inf.
+// tile_mfma and tile_epilogue split it so that several tiles' MFMAs can issue back to back.
 template <bool F4>
-__device__ __forceinline__ float tile_score(const v8i& A, const v8i& B, const float (&cvec)[16], bool visible_key,
-                                            float key_scale) {
+__device__ __forceinline__ v16f tile_mfma(const v8i& A, const v8i& B) {
   v16f acc = {};
-  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, F4 ? 4 : 0, F4 ? 4 : 0, 0, 0, 0, 0);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, F4 ? 4 : 0, F4 ? 4 : 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ float tile_epilogue(const v16f& acc, const float (&cvec)[16], bool visible_key,
+                                               float key_scale) {
   float part = 0.0f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) part = fmaf(cvec[j], acc[j], part);
   const float total = part + __shfl_xor(part, 32);
   return visible_key ? total * key_scale : kNegInf;
+}
+template <bool F4>
+__device__ __forceinline__ float tile_score(const v8i& A, const v8i& B, const float (&cvec)[16], bool visible_key,
+                                            float key_scale) {
+  return tile_epilogue(tile_mfma<F4>(A, B), cvec, visible_key, key_scale);
 }
 
 // c_h of the 16 heads whose results lane l holds in a tile's accumulator (s_c: the 32 c_h)

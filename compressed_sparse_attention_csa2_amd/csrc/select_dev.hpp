@@ -52,13 +52,14 @@ struct RowList {
   const uint32_t* start;  // LDS
   const uint32_t* raw;    // LDS bit mask
   int nreg;
-  int stride;             // slots per region = columns per region
+  int stride;             // slots per region
+  int rcols;              // columns per region
   const float* srow;      // the row's re-scored scores (raw regions)
   const int32_t* prow;    // the row's candidate positions (nullable: position = column)
   // item k of region b
   __device__ __forceinline__ uint2 get_in(int b, uint32_t k) const {
     if (!((raw[b >> 5] >> (b & 31)) & 1u)) return regions[(int64_t)b * stride + k];
-    const int64_t col = (int64_t)b * stride + k;
+    const int64_t col = (int64_t)b * rcols + k;
     const float sc = __builtin_nontemporal_load(srow + col);  // written by this workgroup (re-score)
     const int32_t pos = prow ? prow[col] : (int32_t)col;
     return make_uint2((visible(sc) && pos >= 0) ? order_key(sc) : 0u, (uint32_t)pos);
@@ -255,7 +256,8 @@ __device__ __forceinline__ void select_winners(const SRC& src, uint32_t M, uint3
 // region counts and the first 64 slots of every region are loaded in one round, their
 // prefix is one wave's scan and the first-level histogram is counted from registers.
 struct SelectIn {
-  int nreg, stride;       // regions per row; columns per region (= slots per region)
+  int nreg, stride;       // regions per row; candidate slots per region
+  int rcols;              // columns per region (a score block's columns)
   int64_t ncols;
   int K;
   const uint2* candbuf;   // [R][nreg][stride]
@@ -315,11 +317,11 @@ __device__ __forceinline__ void rescore_raw_regions(const SelectIn& in, int r, S
   const float* ksb = in.ks + (int64_t)b * in.n_max;
   const int32_t* crow = in.cand ? in.cand + (int64_t)r * in.ncols : nullptr;
   float* srow = in.scores + (int64_t)r * in.ncols;
-  const int tiles = in.stride / 32;
+  const int tiles = in.rcols / 32;
   for (int rg = 0; rg < in.nreg; ++rg) {
     if (!((sm.raw[rg >> 5] >> (rg & 31)) & 1u)) continue;  // uniform
     for (int t = wave; t < tiles; t += kWaves) {             // uniform per wave
-      const int64_t col = (int64_t)rg * in.stride + (int64_t)t * 32 + (lane & 31);
+      const int64_t col = (int64_t)rg * in.rcols + (int64_t)t * 32 + (lane & 31);
       int64_t pos = -1;
       if (col < in.ncols) pos = crow ? (int64_t)crow[col] : col;
       const bool v = pos >= 0 && pos <= lim;
@@ -350,7 +352,7 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
   constexpr int kFastSlots = 64;              //   and at most 64 listed per region,
   constexpr int kFastPer = kFastRegions * kFastSlots / NT;  // loaded with the counts (4 per thread)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nreg = in.nreg, stride = in.stride, K = in.K;
+  const int nreg = in.nreg, stride = in.stride, rcols = in.rcols, K = in.K;
   const int64_t ncols = in.ncols;
   const uint2* __restrict__ candbuf = in.candbuf;
   const uint32_t* __restrict__ cnt = in.cnt;
@@ -405,8 +407,8 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
       const int rg = tid + NT * j;
       uint32_t v = rcv[j];
       if (with_raw && rg < nreg && ((sm.raw[rg >> 5] >> (rg & 31)) & 1u)) {
-        const int64_t left = ncols - (int64_t)rg * stride;
-        v = (uint32_t)(left < stride ? left : stride);
+        const int64_t left = ncols - (int64_t)rg * rcols;
+        v = (uint32_t)(left < rcols ? left : rcols);
       }
       const uint32_t suf = block_suffix<NT, NT>(v, sm.wsum);
       if (tid == 0) sm.misc[8] = suf;
@@ -449,7 +451,7 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
     V = sm.misc[9];
   }
   const uint32_t keff = V < (uint32_t)K ? V : (uint32_t)K;
-  RowList L{candbuf + (int64_t)r * nreg * stride, sm.start, sm.raw, nreg, stride, scores + (int64_t)r * ncols,
+  RowList L{candbuf + (int64_t)r * nreg * stride, sm.start, sm.raw, nreg, stride, rcols, scores + (int64_t)r * ncols,
             cand ? cand + (int64_t)r * ncols : nullptr};
   const uint2* st = sm.stage;
   int pass = 0;

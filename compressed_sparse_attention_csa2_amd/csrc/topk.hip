@@ -382,6 +382,7 @@ int launch_topk_select(const ScoreArgs& a, int K, bool sorted, int nreg, int32_t
   SelectIn in{};
   in.nreg = nreg;
   in.stride = lc.stride;
+  in.rcols = lc.rcols;
   in.ncols = a.ncols;
   in.K = K;
   in.candbuf = lc.cand;

@@ -178,3 +178,36 @@ def test_index_topk_many_keys_tied_at_the_top(copies):
             assert np.all(np.isin(tied, g[b, 0])), b
     k8r2, ksr2 = oracle.quantize_fp8(kf)
     check_topk_near_tie(g, oracle.index_score(oracle.PREC_FP8, q, w, k8r2, ksr2, nk), wl.K)
+
+
+@pytest.mark.parametrize("kind", ["equal", "growing"])
+def test_many_row_topk_fallback(kind):
+    """The many-row (chunked prefill) selection on keys that defeat its candidate lists:
+    every score equal (nothing is listed; the lowest positions win) or scores growing with
+    the position (the winners are each row's last K visible positions, more than a region
+    lists).  16 rows with causal limits, so that rows see different prefixes."""
+    K = 512
+    wl = workloads.workload("prefill", N=20000, T=16, K=K)
+    n = wl.N + wl.T
+    if kind == "equal":
+        kf = np.broadcast_to(wl.index_keys(0, rows=1)[None], (1, n, wl.dk)).astype(np.float32).copy()
+    else:
+        kf = _scaled_direction_keys(1, n)
+    k8, ks = _keys_device(kf)
+    nk = np.array([n], np.int32)
+    ql = (wl.N + np.arange(wl.T, dtype=np.int32))[None]
+    q, w = wl.index_query(), wl.head_weights()
+    qd, wd = to_dev(q, torch.bfloat16), to_dev(w)
+    s = csa2.index_score(csa2.PREC_FP8, qd, wd, k8, ks, to_dev(nk), q_limit=to_dev(ql)).cpu().numpy()
+    g = csa2.index_topk(csa2.PREC_FP8, qd, wd, k8, ks, to_dev(nk), K, q_limit=to_dev(ql)).cpu().numpy()
+    for t in range(wl.T):
+        row = s[0, t, :ql[0, t] + 1]
+        if kind == "equal":
+            assert np.unique(row).size == 1, t
+            want = np.arange(K)
+        else:
+            assert np.all(np.diff(row) > 0) or np.all(np.diff(row) < 0), t
+            want = np.arange(ql[0, t] + 1 - K, ql[0, t] + 1) if row[-1] > row[0] else np.arange(K)
+        assert np.array_equal(g[0, t], want), t
+    k8r, ksr = oracle.quantize_fp8(kf)
+    check_topk_near_tie(g, oracle.index_score(oracle.PREC_FP8, q, w, k8r, ksr, nk, q_limit=ql), K)
