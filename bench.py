@@ -37,7 +37,8 @@ import workloads  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20  # written before every flushed layer: twice the 256 MB Infinity Cache
 SCORE_SOURCES = ("compressed_sparse_attention_csa2_amd/csrc/score.hip", "compressed_sparse_attention_csa2_amd/csrc/common.hpp",
-                 "compressed_sparse_attention_csa2_amd/csrc/launch.hpp")
+                 "compressed_sparse_attention_csa2_amd/csrc/launch.hpp",
+                 "compressed_sparse_attention_csa2_amd/csrc/score_dev.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_fp8_group128k_hbm_traffic.md")
 METRIC = "CSA2 decode queries/s + achieved HBM GB/s (% of peak) at 128K context"
 

@@ -539,7 +539,7 @@ __global__ __launch_bounds__(64 * NW) void k_score_fp8_rows(int T, int64_t ncols
 // (lane half h keeps tiles u with u % 2 == h: both halves hold a tile's totals after the
 // half exchange), and counts the rows' first-level histograms in LDS; then per row (rows
 // dealt to the waves) the cut, the lowest bin such that the bins above hold at most `cap`
-// visible scores (cap as for the decode lists, at most lc.stride slots), and the listing of
+// visible scores (cap as for the decode lists with a smaller margin, at most lc.stride slots), and the listing of
 // those scores' (key, position) pairs in column order (per-tile ballot counts, one wave scan
 // per row) into the row's region of lc, with its count, cut and visible count.
 template <int TT, int NW, int NKT, int RPB>
@@ -653,8 +653,10 @@ __global__ __launch_bounds__(64 * NW) void k_score_fp8_rows_list(int T, int64_t 
       const int t = wave + NW * rr;
       const int64_t lim = s_lim[t];
       const int64_t nvis = lim + 1 < ncols ? lim + 1 : ncols;
+      // (a margin of 16 rather than the decode lists' 32: with hundreds of regions per row
+      // the row's whole list must still fit the selection's staging)
       const int64_t mu2 = nvis > 0 ? (4 * (int64_t)lc.K * kCols + nvis - 1) / nvis : kCols;
-      int64_t cap = ((mu2 + 32 + 31) / 32) * 32;
+      int64_t cap = ((mu2 + 16 + 31) / 32) * 32;
       if (cap > kCols) cap = kCols;
       if (cap > lc.stride) cap = lc.stride;
       uint32_t local = 0;
