@@ -134,7 +134,14 @@ bool rows_scan(int prec, int T, const int32_t* cand) {
   return prec == CSA2_PREC_FP8 && !cand && T >= score_tiled_min_rows();
 }
 // decode scans (the fp8 / fp4 indexer's k_score_fp8) list their candidates for k_topk_select
-bool local_scan(int prec, int T, const int32_t* cand) { return prec != CSA2_PREC_FP32 && !rows_scan(prec, T, cand); }
+// rows whose candidate lists fit the selection's staging: at most kLocalMaxRegions score
+// blocks per row (262144 columns at 2048 per block); longer rows (a flat scan of a million
+// entries) take the histogram filter, whose candidates do fit
+constexpr int kLocalMaxRegions = 128;
+bool local_fits(int64_t R, int64_t ncols) { return score_blocks(R, ncols) <= kLocalMaxRegions; }
+bool local_scan(int prec, int T, const int32_t* cand, int64_t R, int64_t ncols) {
+  return prec != CSA2_PREC_FP32 && !rows_scan(prec, T, cand) && local_fits(R, ncols);
+}
 // candidate lists of the many-row kernel: regions of rows_list_cols() columns, each listing
 // at most kRowsSlots candidates (its cap: four times a region's expected winners plus 32,
 // about 40 at 4096 x 262144; a region needing more is re-scored by the selection)
@@ -379,7 +386,7 @@ int csa2_index_topk(int prec, int B, int T, int H, int dk, const void* q, int q_
   Carve c(ws);
   float* scores = c.take<float>((size_t)R * ncols);
   hipStream_t st = S(stream);
-  if (local_scan(prec, T, cand)) {
+  if (local_scan(prec, T, cand, R, ncols)) {
     // decode rows: the score blocks list their candidates, one select workgroup per row
     // finishes the exact Top-K (a candidate map in arbitrary order needs the ranked output)
     const LocalCand lc = local_for(carve_local(c, local_pairs(R, ncols), local_regions(R, ncols)), R, ncols, K);
@@ -496,7 +503,9 @@ static int64_t group_cols(const csa2_group_cache* c) {
 
 // Selections that use a histogram slot (hist, hist2, ctl; zeroed before use): with the fp8 /
 // fp4 indexer only the candidate pools' block selections, with the fp32 indexer every one.
-static bool group_local(const csa2_group_cache* c) { return c->prec != CSA2_PREC_FP32; }
+static bool group_local(const csa2_group_cache* c) {
+  return c->prec != CSA2_PREC_FP32 && local_fits((int64_t)c->B * c->T, c->n_max);
+}
 static int group_slot_selections(const csa2_group_cache* c, int n_index, int n_full) {
   const int pool_sel = pool_on(c) ? n_full : 0;
   return group_local(c) ? pool_sel : n_index + pool_sel;
