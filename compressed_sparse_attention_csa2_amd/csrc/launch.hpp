@@ -81,8 +81,25 @@ inline int score_blocks(int64_t rows, int64_t ncols) {
 // column, so the winners come out ascending).  A block whose list may miss winners is
 // re-scored by the select workgroup with the scan's arithmetic into a.scores ([R][ncols],
 // written only there) and re-read whole.
+// The candidate-list cap of one score block of kcols columns in a row of nvis visible
+// columns: four times the Top-K winners such a block holds on average plus a margin, in
+// multiples of 32, at most the block's columns and its slots.  The cut falls on a whole
+// first-level bin (a quarter octave of the score), and the bin holding the K-th score can
+// hold a few times the winners above it, all of which must be listed.
+// margins: 32 for the decode scans' lists; 16 for the many-row prefill kernel, whose rows of
+// hundreds of regions must still fit the selection's staging
+constexpr int64_t kListMargin = 32, kRowsListMargin = 16;
+__host__ __device__ inline int64_t list_cap(int64_t K, int64_t kcols, int64_t nvis, int64_t margin, int64_t slots) {
+  const int64_t mu2 = nvis > 0 ? (4 * K * kcols + nvis - 1) / nvis : kcols;
+  int64_t cap = ((mu2 + margin + 31) / 32) * 32;
+  if (cap > kcols) cap = kcols;
+  return cap < slots ? cap : slots;
+}
+// expand_out (nullable): the winners are blocks of expand_block positions; their positions
+// ([R][K * expand_block], -1 past n_keys or for padding) are written there as well.
 int launch_topk_select(const ScoreArgs& a, int K, bool sorted, int nreg, int32_t* idx_out, float* val_out,
-                       hipStream_t st, uint32_t* clear = nullptr, int64_t clear_words = 0);
+                       hipStream_t st, uint32_t* clear = nullptr, int64_t clear_words = 0, int expand_block = 0,
+                       int32_t* expand_out = nullptr);
 
 // Top-K: histogram (zeroed on entry) -> filter into candidates (ctl zeroed on entry)
 // -> finalize (here, or fused into the attention kernel).

@@ -85,14 +85,9 @@ __device__ __forceinline__ void list_block_candidates(const uint32_t* lhist, con
   static_assert(kPer * 4 <= 32, "one wave scans the (pass, wave) counts");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // cap: four times the winners a block of this row holds on average (K spread over the
-  // visible columns), plus 32, rounded up to a multiple of 32.  The cut falls on a whole
-  // first-level bin (a quarter octave of the score), and the bin holding the K-th score can
-  // hold a few times the winners above it, all of which must be listed.
+  // visible columns), plus 32
   const int64_t nvis = cand ? ncols : (lim + 1 < ncols ? lim + 1 : ncols);
-  const int64_t mu2 = nvis > 0 ? (4 * (int64_t)lc.K * kCols + nvis - 1) / nvis : kCols;
-  int64_t cap = ((mu2 + 32 + 31) / 32) * 32;
-  if (cap > kCols) cap = kCols;
-  if (cap > lc.stride) cap = lc.stride;  // the region's slots
+  const int64_t cap = list_cap(lc.K, kCols, nvis, kListMargin, lc.stride);
   uint32_t hb[8], local = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -653,12 +648,7 @@ __global__ __launch_bounds__(64 * NW) void k_score_fp8_rows_list(int T, int64_t 
       const int t = wave + NW * rr;
       const int64_t lim = s_lim[t];
       const int64_t nvis = lim + 1 < ncols ? lim + 1 : ncols;
-      // (a margin of 16 rather than the decode lists' 32: with hundreds of regions per row
-      // the row's whole list must still fit the selection's staging)
-      const int64_t mu2 = nvis > 0 ? (4 * (int64_t)lc.K * kCols + nvis - 1) / nvis : kCols;
-      int64_t cap = ((mu2 + 16 + 31) / 32) * 32;
-      if (cap > kCols) cap = kCols;
-      if (cap > lc.stride) cap = lc.stride;
+      const int64_t cap = list_cap(lc.K, kCols, nvis, kRowsListMargin, lc.stride);
       uint32_t local = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

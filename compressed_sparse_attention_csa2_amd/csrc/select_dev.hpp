@@ -252,11 +252,14 @@ __device__ __forceinline__ void select_winners(const SRC& src, uint32_t M, uint3
 // runs on the enlarged list), then the winners in list order.  Writes the keff = min(K,
 // visible) winners' positions to out_pos (ascending with SORTED, else ranked by position)
 // and, if out_key != nullptr, their order keys; returns keff.  Every thread must call it.
-// Fast path (at most 64 regions of at most 64 listed candidates, the decode rows): the
-// region counts and the first 64 slots of every region are loaded in one round, their
-// prefix is one wave's scan and the first-level histogram is counted from registers.
+// Fast path (at most 64 regions whose slots fit the LDS staging: the decode rows and both
+// stages of the two-level select): the region counts and every slot of every region are
+// loaded in one round, their prefix is one wave's scan and a histogram over the listed
+// keys' own range is counted from registers.
 struct SelectIn {
   int nreg, stride;       // regions per row; candidate slots per region
+  int spec;               // slots per region loaded with the counts (a power of two): the lists'
+                          // expected cap, rounded up
   int rcols;              // columns per region (a score block's columns)
   int64_t ncols;
   int K;
@@ -276,6 +279,10 @@ struct SelectIn {
   const int32_t* n_keys;
   const int32_t* q_limit;
   int key_div, T;
+  // optional expansion of the winners (columns = blocks of expand_block positions) into
+  // their positions, [R][K * expand_block], -1 past the sequence's n_keys or for padding
+  int32_t* expand_out;
+  int expand_block;
 };
 
 // Re-score every region of row r marked in sm.raw into in.scores, with the score kernel's
@@ -348,9 +355,8 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
   constexpr int kRP = (MAXREG + NT - 1) / NT;  // regions per thread (region tid + NT j)
   constexpr int kSP = kFinStage / NT;         // staged items per thread
   constexpr int kWaves = NT / 64;
-  constexpr int kFastRegions = 64;            // fast path: one wave's scan of the region counts
-  constexpr int kFastSlots = 64;              //   and at most 64 listed per region,
-  constexpr int kFastPer = kFastRegions * kFastSlots / NT;  // loaded with the counts (4 per thread)
+  constexpr int kFastRegions = 64;            // fast path: one wave's scan of the region counts,
+  constexpr int kFastPer = kFinStage / NT;    //   every slot of every region loaded with the counts
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nreg = in.nreg, stride = in.stride, rcols = in.rcols, K = in.K;
   const int64_t ncols = in.ncols;
@@ -360,7 +366,9 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
   const uint32_t* __restrict__ vis = in.vis;
   const float* scores = in.scores;  // written by the re-score, read after it
   const int32_t* __restrict__ cand = in.cand;
-  const bool few = nreg <= kFastRegions && stride >= kFastSlots;
+  const int spec = in.spec, ssh = __builtin_ctz((unsigned)spec);
+  const int slots = nreg * spec;  // < kFinStage on the fast path
+  const bool few = nreg <= kFastRegions && nreg * (int64_t)spec <= kFinStage;
   // 0. every load issued together: the region counts, cuts and visible counts, and (few
   //    regions) the first 64 slots of every region, whatever their counts turn out to be
   uint32_t rcv[kRP], rvv[kRP];
@@ -384,13 +392,15 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
       rcutv[j] = -1;
     }
   }
-  const int fb = tid / (kFastSlots / kFastPer);            // this thread's region (fast path)
-  const int fk = tid % (kFastSlots / kFastPer);            // and its first slot
-  uint2 fv[kFastPer];
+  uint2 fv[kFastPer];  // fast path: item tid + NT u = slot (i & (spec - 1)) of region (i >> ssh)
   if (few) {  // uniform
-    const int64_t rb = (int64_t)r * nreg + (fb < nreg ? fb : nreg - 1);
+    const uint2* crow = candbuf + (int64_t)r * nreg * stride;
 #pragma unroll
-    for (int u = 0; u < kFastPer; ++u) fv[u] = candbuf[rb * stride + fk + (kFastSlots / kFastPer) * u];
+    for (int u = 0; u < kFastPer; ++u) {
+      const int i = tid + NT * u;
+      const int ic = i < slots ? i : slots - 1;
+      if (NT * u < slots) fv[u] = crow[(int64_t)(ic >> ssh) * stride + (ic & (spec - 1))];  // uniform bound
+    }
   }
   for (int i = tid; i < kSelMaxRegions / 32; i += NT) sm.raw[i] = 0u;
   for (int i = tid; i < kHistBins; i += NT) {
@@ -421,7 +431,7 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
     if (tid == 0) sm.start[nreg] = carry;
     return carry;
   };
-  // 1. visible total, starts, and whether every region fits the fast path
+  // 1. visible total and starts
   uint32_t V, M = 0;
   bool fast = false;
   if (few) {
@@ -434,12 +444,12 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
       if (lane == 0) {
         sm.start[nreg] = tot;
         sm.misc[9] = (uint32_t)__builtin_amdgcn_readlane((int)vsfx, 0);
-        sm.misc[11] = __ballot(c > (uint32_t)kFastSlots) ? 0u : 1u;
+        sm.misc[11] = __ballot(c > (uint32_t)spec) ? 0u : 1u;
       }
     }
     __syncthreads();
     V = sm.misc[9];
-    fast = sm.misc[11] != 0;
+    fast = sm.misc[11] != 0;  // every listed candidate was loaded
     M = sm.start[nreg];
   } else {
     uint32_t vloc = 0;
@@ -460,13 +470,14 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
     //    over the row
     bool have[kFastPer];
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-    {
-      const uint32_t s0 = fb < nreg ? sm.start[fb] : 0u;
-      const uint32_t n = fb < nreg ? sm.start[fb + 1] - s0 : 0u;
 #pragma unroll
-      for (int u = 0; u < kFastPer; ++u) {
-        const uint32_t k = fk + (kFastSlots / kFastPer) * u;
-        have[u] = k < n;
+    for (int u = 0; u < kFastPer; ++u) {
+      const int i = tid + NT * u;
+      have[u] = false;
+      if (NT * u < slots && i < slots) {
+        const int b = i >> ssh, k = i & (spec - 1);
+        const uint32_t s0 = sm.start[b];
+        have[u] = (uint32_t)k < sm.start[b + 1] - s0;
         if (have[u]) {
           sm.stage[s0 + k] = fv[u];
           kmn = min(kmn, fv[u].x);

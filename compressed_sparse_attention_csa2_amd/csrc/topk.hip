@@ -364,13 +364,24 @@ __global__ __launch_bounds__(NT) void k_topk_select(SelectIn in, int32_t* __rest
   const int K = in.K;
   for (int i = tid; i < K; i += NT) {
     const bool have = i < keff;
-    idx_out[(int64_t)r * K + i] = have ? s_pos[i] : -1;
+    if (idx_out) idx_out[(int64_t)r * K + i] = have ? s_pos[i] : -1;
     if (val_out) val_out[(int64_t)r * K + i] = have ? key_to_float(s_key[i]) : kNegInf;
+  }
+  if (in.expand_out) {  // the winners are blocks: write their positions (the fine candidates)
+    const int blk = in.expand_block;
+    const int64_t nk = in.n_keys[r / in.T];
+    int32_t* dst = in.expand_out + (int64_t)r * K * blk;
+    for (int64_t i = tid; i < (int64_t)K * blk; i += NT) {
+      const int e = (int)(i / blk);
+      const int64_t p = e < keff ? (int64_t)s_pos[e] * blk + i % blk : -1;
+      dst[i] = (p >= 0 && p < nk) ? (int32_t)p : -1;
+    }
   }
 }
 
 int launch_topk_select(const ScoreArgs& a, int K, bool sorted, int nreg, int32_t* idx_out, float* val_out,
-                       hipStream_t st, uint32_t* clear, int64_t clear_words) {
+                       hipStream_t st, uint32_t* clear, int64_t clear_words, int expand_block,
+                       int32_t* expand_out) {
   if (nreg > kSelMaxRegions) return -1;
   if (a.prec != 1 && a.prec != 2) return -1;  // the re-score covers the fp8 and FP4 indexers
   if (a.H != 32 || a.dk != 64) return -1;
@@ -402,6 +413,14 @@ int launch_topk_select(const ScoreArgs& a, int K, bool sorted, int nreg, int32_t
   in.q_limit = a.q_limit;
   in.key_div = a.key_div;
   in.T = a.T;
+  // the lists' cap for a row whose columns are all visible (shorter rows list more per
+  // region and, past spec, take the general path), rounded up to a power of two
+  const int64_t cap = list_cap(a.lc.K, a.lc.rcols, a.ncols, kListMargin, a.lc.stride);
+  int spec = 1;
+  while (spec < cap && 2 * spec <= a.lc.stride) spec *= 2;
+  in.spec = spec;
+  in.expand_out = expand_out;
+  in.expand_block = expand_block;
 #define CSA2_SELECT(S, NT, MR) \
   hipLaunchKernelGGL((k_topk_select<S, NT, MR>), dim3(R), dim3(NT), 0, st, in, idx_out, val_out, clear4, clear_n4)
   // one region count per thread covers rows of up to kSelThreads regions (2M columns at
