@@ -11,6 +11,8 @@
 // once; keeping them out of L2 measured ~15 % faster than cached loads on MI355X) and
 // each wave keeps 16 KB in flight.  Optionally it also builds a per-row histogram of the
 // scores' top bits for the Top-K select that follows.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "score_dev.hpp"
@@ -536,9 +538,10 @@ __global__ __launch_bounds__(64 * NW) void k_score_fp8_rows(int T, int64_t ncols
 // dealt to the waves) the cut, the lowest bin such that the bins above hold at most `cap`
 // visible scores (cap as for the decode lists with a smaller margin, at most lc.stride slots), and the listing of
 // those scores' (key, position) pairs in column order (per-tile ballot counts, one wave scan
-// per row) into the row's region of lc, with its count, cut and visible count.
+// per row) into the row's region of lc, with its count, cut and visible count.  Launch
+// bound: four waves per SIMD (at most 128 VGPRs; the two region variants would take 130).
 template <int TT, int NW, int NKT, int RPB>
-__global__ __launch_bounds__(64 * NW) void k_score_fp8_rows_list(int T, int64_t ncols, int nblk,
+__global__ __launch_bounds__(64 * NW, 4) void k_score_fp8_rows_list(int T, int64_t ncols, int nblk,
                                                                  const uint8_t* __restrict__ q8,
                                                                  const float* __restrict__ cst,
                                                                  const uint8_t* __restrict__ k8,
@@ -594,52 +597,81 @@ __global__ __launch_bounds__(64 * NW) void k_score_fp8_rows_list(int T, int64_t 
     for (int i = tid; i < TT * kHistBins / 2; i += NT) s_h[i] = 0;
     __syncthreads();
 
-    float keep[TT][kKept];
+    // every column of the region visible to every row of the block (all regions but the
+    // causal tail and the last): no clamped addresses, no visibility tests
+    bool full = c0 + kCols <= ncols;
 #pragma unroll
-    for (int g = 0; g < NKT / 4; ++g) {
-      v8i B[4];
-      float sk[4];
-      int64_t col[4];
+    for (int t = 0; t < TT; ++t) full = full && c0 + kCols - 1 <= s_lim[t];
+    // kept order keys (0: not visible, never the key of a visible score): slot k of lane
+    // (half h, key l) is tile wave + NW (4 (k / 2) + 2 (k % 2) + h), column l of it
+    uint32_t keep[TT][kKept];
+    auto scan = [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
+      const uint8_t* kw = kb + (c0 + wave * 32 + (lane & 15)) * 64;  // FULL: this lane's first key
+      const float* skw = ksb + c0 + wave * 32 + (lane & 31);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t tbase = c0 + (int64_t)(wave + NW * (4 * g + u)) * 32;
-        col[u] = tbase + (lane & 31);
-        const int64_t rr = col[u] < ncols ? col[u] : 0;  // clamped, masked below
-        const int64_t rl = tbase + (lane & 15) < ncols ? tbase + (lane & 15) : 0;
-        const int64_t rh = tbase + (lane & 15) + 16 < ncols ? tbase + (lane & 15) + 16 : 0;
-        const v4i x0 = *reinterpret_cast<const v4i*>(kb + rl * 64);
-        const v4i x1 = *reinterpret_cast<const v4i*>(kb + rh * 64);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const auto sw = __builtin_amdgcn_permlane16_swap((uint32_t)x0[d], (uint32_t)x1[d], false, false);
-          B[u][d] = (int)sw[0];
-          B[u][4 + d] = (int)sw[1];
-        }
-        sk[u] = ksb[rr];
-      }
-#pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        const uint4* qa = reinterpret_cast<const uint4*>(s_q8 + (t * 32 + (lane & 31)) * kQRow + half * 32);
-        const uint4 a0 = qa[0], a1 = qa[1];
-        const v8i A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        float cvec[16];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 cc = *reinterpret_cast<const float4*>(&s_c[t * 32 + 8 * j + 4 * half]);
-          cvec[4 * j] = cc.x; cvec[4 * j + 1] = cc.y; cvec[4 * j + 2] = cc.z; cvec[4 * j + 3] = cc.w;
-        }
-        const int64_t lim = s_lim[t];
+      for (int g = 0; g < NKT / 4; ++g) {
+        v8i B[4];
+        float sk[4];
+        int64_t col[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float sc = tile_score<false>(A, B[u], cvec, col[u] <= lim, sk[u]);
-          if (half == 0 && col[u] < ncols && visible(sc)) {
-            const uint32_t bin = hist_bin(order_key(sc));
-            atomicAdd(&s_h[t * (kHistBins / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
+          const int64_t tbase = c0 + (int64_t)(wave + NW * (4 * g + u)) * 32;
+          col[u] = tbase + (lane & 31);
+          v4i x0, x1;
+          if (FULL) {
+            const uint8_t* p = kw + NW * (4 * g + u) * 32 * 64;
+            x0 = *reinterpret_cast<const v4i*>(p);
+            x1 = *reinterpret_cast<const v4i*>(p + 16 * 64);
+            sk[u] = skw[NW * (4 * g + u) * 32];
+          } else {
+            const int64_t rr = col[u] < ncols ? col[u] : 0;  // clamped, masked below
+            const int64_t rl = tbase + (lane & 15) < ncols ? tbase + (lane & 15) : 0;
+            const int64_t rh = tbase + (lane & 15) + 16 < ncols ? tbase + (lane & 15) + 16 : 0;
+            x0 = *reinterpret_cast<const v4i*>(kb + rl * 64);
+            x1 = *reinterpret_cast<const v4i*>(kb + rh * 64);
+            sk[u] = ksb[rr];
           }
-          if ((u & 1) == half) keep[t][2 * g + (u >> 1)] = sc;  // col[u] > lim (incl. past ncols): -inf
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const auto sw = __builtin_amdgcn_permlane16_swap((uint32_t)x0[d], (uint32_t)x1[d], false, false);
+            B[u][d] = (int)sw[0];
+            B[u][4 + d] = (int)sw[1];
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          const uint4* qa = reinterpret_cast<const uint4*>(s_q8 + (t * 32 + (lane & 31)) * kQRow + half * 32);
+          const uint4 a0 = qa[0], a1 = qa[1];
+          const v8i A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+          float cvec[16];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float4 cc = *reinterpret_cast<const float4*>(&s_c[t * 32 + 8 * j + 4 * half]);
+            cvec[4 * j] = cc.x; cvec[4 * j + 1] = cc.y; cvec[4 * j + 2] = cc.z; cvec[4 * j + 3] = cc.w;
+          }
+          const int64_t lim = s_lim[t];
+          float sc[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)  // columns past lim (incl. past ncols): -inf
+            sc[u] = tile_score<false>(A, B[u], cvec, FULL || (col[u] <= lim && col[u] < ncols), sk[u]);
+          // each half keeps (and counts in the row's histogram) its own two of the 4 tiles:
+          // one atomic per lane and kept score, no lane idle
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const float kv = half ? sc[2 * p + 1] : sc[2 * p];
+            const uint32_t key = visible(kv) ? order_key(kv) : 0u;
+            keep[t][2 * g + p] = key;
+            const uint32_t bin = hist_bin(key);
+            atomicAdd(&s_h[t * (kHistBins / 2) + (bin >> 1)], key ? 1u << (16 * (bin & 1)) : 0u);
+          }
         }
       }
-    }
+    };
+    if (full)  // uniform
+      scan(std::true_type{});
+    else
+      scan(std::false_type{});
     __syncthreads();
 
     // the cut of rows wave + NW rr: lane l holds bins 32 l .. 32 l + 31
@@ -690,8 +722,8 @@ __global__ __launch_bounds__(64 * NW) void k_score_fp8_rows_list(int T, int64_t 
       const uint32_t cut = s_cut[t];
 #pragma unroll
       for (int k = 0; k < kKept; ++k) {
-        const float sc = keep[t][k];
-        const bool pred = visible(sc) && (cut == 0xFFFFFFFFu || hist_bin(order_key(sc)) > cut);
+        const uint32_t key = keep[t][k];
+        const bool pred = key != 0u && (cut == 0xFFFFFFFFu || hist_bin(key) > cut);
         const uint64_t bal = __ballot(pred);
         if (lane == 0) {
           const int tile0 = wave + NW * (4 * (k >> 1) + 2 * (k & 1));
@@ -717,9 +749,8 @@ __global__ __launch_bounds__(64 * NW) void k_score_fp8_rows_list(int T, int64_t 
       uint2* creg = lc.cand + ((r0 + t) * nblk + blk) * lc.stride;
 #pragma unroll
       for (int k = 0; k < kKept; ++k) {
-        const float sc = keep[t][k];
-        const uint32_t key = order_key(sc);
-        const bool pred = visible(sc) && (cut == 0xFFFFFFFFu || hist_bin(key) > cut);
+        const uint32_t key = keep[t][k];
+        const bool pred = key != 0u && (cut == 0xFFFFFFFFu || hist_bin(key) > cut);
         const uint64_t bal = __ballot(pred);
         const int tile = wave + NW * (4 * (k >> 1) + 2 * (k & 1) + half);
         if (pred) {
