@@ -554,12 +554,14 @@ __global__ __launch_bounds__(64 * NW, 4) void k_score_fp8_rows_list(int T, int64
   constexpr int NT = 64 * NW;
   constexpr int kCols = NW * NKT * 32;   // columns of a region
   constexpr int kTiles = NW * NKT;       // 32-column tiles of a region
+  static_assert(kCols < 65536, "16-bit histogram halves");
   static_assert(kTiles <= 64, "one wave scans a row's tile counts");
   constexpr int kKept = NKT / 2;         // scores kept per lane and row
   constexpr int kQRow = 80;
   __shared__ __align__(16) uint8_t s_q8[TT * 32 * kQRow];
   __shared__ __align__(16) float s_c[TT * 32];
   __shared__ int64_t s_lim[TT];
+  __shared__ uint32_t s_cap[TT];           // the rows' list caps (once per block: a 64-bit division)
   __shared__ __align__(16) uint32_t s_h[TT * kHistBins / 2];
   __shared__ uint32_t s_cnt[TT * kTiles];  // listed per (row, tile), then their exclusive offsets
   __shared__ uint32_t s_cut[TT];
@@ -577,12 +579,17 @@ __global__ __launch_bounds__(64 * NW, 4) void k_score_fp8_rows_list(int T, int64
           (i < nrows * 32 * 64 / 16) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
     }
     for (int i = tid; i < TT * 32; i += NT) s_c[i] = (i < nrows * 32) ? cst[r0 * 32 + i] : 0.0f;
-    if (tid < TT && tid >= nrows) s_lim[tid] = -1;
+    if (tid < TT && tid >= nrows) {
+      s_lim[tid] = -1;
+      s_cap[tid] = 0;
+    }
     if (tid < nrows) {
       int64_t nk = n_keys[b];
       int64_t lim = (nk < n_max ? nk : n_max) - 1;
       if (q_limit && q_limit[r0 + tid] < lim) lim = q_limit[r0 + tid];
       s_lim[tid] = lim;
+      const int64_t nvis = lim + 1 < ncols ? lim + 1 : ncols;
+      s_cap[tid] = (uint32_t)list_cap(lc.K, kCols, nvis, kRowsListMargin, lc.stride);
     }
   }
   // whole-line key loads (as in k_score_fp8): load 0 gives lane l chunk l / 16 of key l % 16,
@@ -678,16 +685,16 @@ __global__ __launch_bounds__(64 * NW, 4) void k_score_fp8_rows_list(int T, int64
 #pragma unroll
     for (int rr = 0; rr < kRPW; ++rr) {
       const int t = wave + NW * rr;
-      const int64_t lim = s_lim[t];
-      const int64_t nvis = lim + 1 < ncols ? lim + 1 : ncols;
-      const int64_t cap = list_cap(lc.K, kCols, nvis, kRowsListMargin, lc.stride);
-      uint32_t local = 0;
+      const uint32_t cap = s_cap[t];
+      // the 32 bins as 16 packed pairs: a row has at most kCols (< 2^16) visible scores, so
+      // the pairs add as whole words without a carry between the halves
+      uint32_t pairs = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint4 w4 = *reinterpret_cast<const uint4*>(&s_h[t * (kHistBins / 2) + 16 * lane + 4 * q]);
-        local += (w4.x & 0xFFFFu) + (w4.x >> 16) + (w4.y & 0xFFFFu) + (w4.y >> 16) + (w4.z & 0xFFFFu) +
-                 (w4.z >> 16) + (w4.w & 0xFFFFu) + (w4.w >> 16);
+        pairs += w4.x + w4.y + w4.z + w4.w;
       }
+      const uint32_t local = (pairs & 0xFFFFu) + (pairs >> 16);
       const uint32_t suf = wave_suffix(local);  // visible scores in bins >= 32 lane
       const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)suf, 0);
       uint32_t cut = 0xFFFFFFFFu, listed = total;
@@ -716,19 +723,20 @@ __global__ __launch_bounds__(64 * NW, 4) void k_score_fp8_rows_list(int T, int64
     }
     __syncthreads();
     // per (row, tile) counts of the listed scores: kept slot k of lane (h, key) is tile
-    // wave + NW (4 (k / 2) + 2 (k % 2) + h); one ballot covers both halves' tiles
+    // wave + NW (4 (k / 2) + 2 (k % 2) + h); one ballot covers both halves' tiles, and the
+    // ballots (wave-uniform) are kept for the listing
+    uint64_t bals[TT][kKept];
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       const uint32_t cut = s_cut[t];
 #pragma unroll
       for (int k = 0; k < kKept; ++k) {
         const uint32_t key = keep[t][k];
-        const bool pred = key != 0u && (cut == 0xFFFFFFFFu || hist_bin(key) > cut);
-        const uint64_t bal = __ballot(pred);
+        bals[t][k] = __ballot(key != 0u && (cut == 0xFFFFFFFFu || hist_bin(key) > cut));
         if (lane == 0) {
           const int tile0 = wave + NW * (4 * (k >> 1) + 2 * (k & 1));
-          s_cnt[t * kTiles + tile0] = (uint32_t)__builtin_popcountll(bal & 0xFFFFFFFFull);
-          s_cnt[t * kTiles + tile0 + NW] = (uint32_t)__builtin_popcountll(bal >> 32);
+          s_cnt[t * kTiles + tile0] = (uint32_t)__builtin_popcountll(bals[t][k] & 0xFFFFFFFFull);
+          s_cnt[t * kTiles + tile0 + NW] = (uint32_t)__builtin_popcountll(bals[t][k] >> 32);
         }
       }
     }
@@ -742,22 +750,23 @@ __global__ __launch_bounds__(64 * NW, 4) void k_score_fp8_rows_list(int T, int64
       if (lane < kTiles) s_cnt[t * kTiles + lane] = tot - sfx;
     }
     __syncthreads();
+    // the listing: a listed score's slot is its tile's offset plus the listed lanes of its
+    // half below it (columns < 2^31, so positions are 32-bit)
+    const uint32_t col0 = (uint32_t)c0 + (uint32_t)(wave * 32 + (lane & 31));
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       if (t >= nrows) break;  // uniform
-      const uint32_t cut = s_cut[t];
       uint2* creg = lc.cand + ((r0 + t) * nblk + blk) * lc.stride;
 #pragma unroll
       for (int k = 0; k < kKept; ++k) {
-        const uint32_t key = keep[t][k];
-        const bool pred = key != 0u && (cut == 0xFFFFFFFFu || hist_bin(key) > cut);
-        const uint64_t bal = __ballot(pred);
-        const int tile = wave + NW * (4 * (k >> 1) + 2 * (k & 1) + half);
-        if (pred) {
-          const uint64_t mine = half ? (bal >> 32) : (bal & 0xFFFFFFFFull);
-          const uint32_t below = (uint32_t)__builtin_popcountll(mine & ((1ull << (lane & 31)) - 1ull));
-          const uint32_t slot = s_cnt[t * kTiles + tile] + below;
-          creg[slot] = make_uint2(key, (uint32_t)(c0 + (int64_t)tile * 32 + (lane & 31)));
+        const uint64_t bal = bals[t][k];
+        if (bal == 0) continue;  // uniform
+        if ((bal >> lane) & 1ull) {
+          const int tile = NW * (4 * (k >> 1) + 2 * (k & 1) + half);  // past this wave's first
+          const uint32_t below = half ? __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), 0u)
+                                      : __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u);
+          const uint32_t slot = s_cnt[t * kTiles + wave + tile] + below;
+          creg[slot] = make_uint2(keep[t][k], col0 + (uint32_t)tile * 32);
         }
       }
     }
