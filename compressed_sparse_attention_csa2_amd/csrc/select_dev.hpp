@@ -170,26 +170,24 @@ __device__ __forceinline__ void compact_winners(const SRC& src, uint32_t M, uint
       sm.h256[lane * kWaves + wave] = n;
     }
     __syncthreads();
-    if (wave == 0) {
-      const uint32_t v = sm.h256[lane];
-      const uint32_t sfx = wave_suffix(v);
-      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 0);
-      sm.h256[64 + lane] = carry + tot - sfx;
-      if (lane == 0) sm.misc[5] = tot;
-    }
-    __syncthreads();
+    // every wave scans the 64 (pass, wave) counts itself (no second barrier): the offset of
+    // (u, wave) is the suffix's complement at lane kWaves u + wave
+    const uint32_t sfx = wave_suffix(sm.h256[lane]);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 0);
+    const uint32_t off = carry + tot - sfx;
 #pragma unroll
     for (int u = 0; u < kCompPer; ++u) {
+      const uint32_t base_u = (uint32_t)__builtin_amdgcn_readlane((int)off, u * kWaves + wave);
       if ((bal[u] >> lane) & 1ull) {
-        const uint32_t slot = sm.h256[64 + u * kWaves + wave] + lanes_below(bal[u]);
+        const uint32_t slot = base_u + lanes_below(bal[u]);
         if (slot < (uint32_t)CSA2_MAX_K_DEV) {
           dst_pos[slot] = (int32_t)cv[u].y;
           if (!SORTED || out_key) dst_key[slot] = cv[u].x;
         }
       }
     }
-    carry += sm.misc[5];
-    __syncthreads();
+    carry += tot;
+    __syncthreads();  // every wave has read the counts before the next pass (or the caller) reuses h256
   }
   if (!SORTED) {
     // rank the winners by position (distinct positions): each counts the smaller ones
