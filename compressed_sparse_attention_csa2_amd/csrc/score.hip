@@ -171,8 +171,11 @@ __device__ __forceinline__ void list_block_candidates(const uint32_t* lhist, con
 // scores themselves are written only when a later step reads them all (lc.store: a Full
 // layer's candidate pool takes the block maxima); a selection that cannot trust a block's
 // list re-scores that block's columns itself (k_topk_select, with this kernel's arithmetic).
+// Launch bound: four waves per SIMD for the full scans (at most 128 VGPRs, so that all four
+// blocks a CU gets at 16 x 131072 are resident at once: at 129 VGPRs a quarter of the
+// blocks ran as a second wave after the first had streamed); the candidate scans keep two.
 template <typename QT, bool CAND, int TPW, bool F4 = false, bool KEEP = false, bool LOCAL = false>
-__global__ __launch_bounds__(256) void k_score_fp8(int T, int64_t ncols, const QT* __restrict__ q,
+__global__ __launch_bounds__(256, CAND ? 2 : 4) void k_score_fp8(int T, int64_t ncols, const QT* __restrict__ q,
                                                    const float* __restrict__ w, const uint8_t* __restrict__ k8,
                                                    const float* __restrict__ ks, int64_t n_max,
                                                    const int32_t* __restrict__ n_keys,
