@@ -703,13 +703,20 @@ int csa2_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int bl
   return dev_status(launch_coarse_keys(B, n_max, n_keys, dk, block, k8, k_scale, kb8, kb_scale, S(stream)));
 }
 
-// Two-level select: [coarse and fine candidate lists] [coarse and fine scores (written only
-// where the selection re-scores a block)] [selected blocks] [their positions]
+// Two-level select.  Rows whose coarse and fine stages both fit the candidate lists (at most
+// kLocalMaxRegions score blocks each): [coarse and fine lists] [coarse and fine scores
+// (written only where the selection re-scores a block)] [selected blocks] [their positions].
+// Larger ones take the histogram selection: [both selections' zeroed state] [their candidate
+// lists] [coarse scores] [selected blocks] [their positions] [fine scores].
+static bool hier_lists(int B, int64_t nb, int64_t C) { return local_fits(B, nb) && local_fits(B, C); }
 size_t csa2_hier_select_workspace_size(int B, int64_t n_max, int block, int block_topk, int) {
   const int64_t nb = (n_max + block - 1) / block;
   const int64_t C = (int64_t)block_topk * block;
-  return local_ws(B, nb) + local_ws(B, C) + align256((size_t)B * nb * 4) + align256((size_t)B * C * 4) +
-         align256((size_t)B * block_topk * 4) + align256((size_t)B * C * 4);
+  if (hier_lists(B, nb, C))
+    return local_ws(B, nb) + local_ws(B, C) + align256((size_t)B * nb * 4) + align256((size_t)B * C * 4) +
+           align256((size_t)B * block_topk * 4) + align256((size_t)B * C * 4);
+  return align256((size_t)B * nb * 4) + topk_ws(B, nb) + align256((size_t)B * block_topk * 4) +
+         align256((size_t)B * C * 4) + align256((size_t)B * C * 4) + topk_ws(B, C);
 }
 int csa2_hier_select(int B, int H, int dk, const void* q, int q_dtype, const float* w, const uint8_t* k8,
                      const float* k_scale, const uint8_t* kb8, const float* kb_scale, int64_t n_max,
@@ -721,39 +728,69 @@ int csa2_hier_select(int B, int H, int dk, const void* q, int q_dtype, const flo
   const int64_t nb = (n_max + block - 1) / block;
   const int64_t C = (int64_t)block_topk * block;
   if (C > kMaxTopkCols || nb > kMaxTopkCols || n_max > INT32_MAX) return CSA2_ERR_SHAPE;
-  // both stages' rows must fit the candidate lists' region bound
-  if (!local_fits(B, nb) || !local_fits(B, C)) return CSA2_ERR_SHAPE;
   int rc = check_index_shape(CSA2_PREC_FP8, B, 1, H, dk, q_dtype, k_scale, nb);
   if (rc) return rc;
   if (!ws || ws_bytes < csa2_hier_select_workspace_size(B, n_max, block, block_topk, K)) return CSA2_ERR_WORKSPACE;
   rc = check_device();
   if (rc) return rc;
   Carve cv(ws);
-  const LocalCand l1 = local_for(carve_local(cv, local_pairs(B, nb), local_regions(B, nb)), B, nb, block_topk);
-  const LocalCand l2 = local_for(carve_local(cv, local_pairs(B, C), local_regions(B, C)), B, C, K);
+  hipStream_t st = S(stream);
+  int32_t* bout = block_out;
+  if (hier_lists(B, nb, C)) {
+    const LocalCand l1 = local_for(carve_local(cv, local_pairs(B, nb), local_regions(B, nb)), B, nb, block_topk);
+    const LocalCand l2 = local_for(carve_local(cv, local_pairs(B, C), local_regions(B, C)), B, C, K);
+    float* cscores = cv.take<float>((size_t)B * nb);
+    float* fscores = cv.take<float>((size_t)B * C);
+    int32_t* blocks = cv.take<int32_t>((size_t)B * block_topk);
+    int32_t* cand = cv.take<int32_t>((size_t)B * C);
+    if (!bout) bout = blocks;
+    // coarse: the block keys' scan lists its candidates; the block selection also writes the
+    // selected blocks' positions (the fine candidates, ascending, -1 past n_keys)
+    ScoreArgs a1 = score_args(CSA2_PREC_FP8, B, 1, H, dk, q, q_dtype, w, kb8, kb_scale, nb, n_keys, nullptr, nullptr,
+                              nb, cscores, nullptr, block);
+    a1.local = true;
+    a1.lc = l1;
+    if (launch_score(a1, st)) return CSA2_ERR_DEVICE;
+    if (launch_topk_select(a1, block_topk, true, score_blocks(B, nb), bout, nullptr, st, nullptr, 0, block, cand))
+      return CSA2_ERR_DEVICE;
+    // fine: the exact score of every candidate position, listed, then the Top-K (the
+    // candidates ascend, so the winners come out in position order)
+    ScoreArgs a2 = score_args(CSA2_PREC_FP8, B, 1, H, dk, q, q_dtype, w, k8, k_scale, n_max, n_keys, nullptr, cand,
+                              C, fscores, nullptr, 1);
+    a2.local = true;
+    a2.lc = l2;
+    if (launch_score(a2, st)) return CSA2_ERR_DEVICE;
+    return dev_status(launch_topk_select(a2, K, true, score_blocks(B, C), idx_out, nullptr, st));
+  }
+  // the histogram selection: both selections' zeroed state first (one fill), then their lists
+  TopkWs t1 = carve_topk_zero(cv, B);
+  TopkWs t2 = carve_topk_zero(cv, B);
+  const CandWs w1 = carve_cand(cv, B, nb);
+  const CandWs w2 = carve_cand(cv, B, C);
+  t1.cand = w1.cand; t1.cnt = w1.cnt;
+  t2.cand = w2.cand; t2.cnt = w2.cnt;
   float* cscores = cv.take<float>((size_t)B * nb);
-  float* fscores = cv.take<float>((size_t)B * C);
   int32_t* blocks = cv.take<int32_t>((size_t)B * block_topk);
   int32_t* cand = cv.take<int32_t>((size_t)B * C);
-  hipStream_t st = S(stream);
-  // coarse: the block keys' scan lists its candidates; the block selection also writes the
-  // selected blocks' positions (the fine candidates, ascending, -1 past n_keys)
+  float* fscores = cv.take<float>((size_t)B * C);
+  if (!bout) bout = blocks;
+  if (launch_fill_u32(t1.hist, (int64_t)(2 * topk_zero_bytes(B) / 4), 0u, st)) return CSA2_ERR_DEVICE;
   ScoreArgs a1 = score_args(CSA2_PREC_FP8, B, 1, H, dk, q, q_dtype, w, kb8, kb_scale, nb, n_keys, nullptr, nullptr,
-                            nb, cscores, nullptr, block);
-  a1.local = true;
-  a1.lc = l1;
+                            nb, cscores, t1.hist, block);
   if (launch_score(a1, st)) return CSA2_ERR_DEVICE;
-  int32_t* bout = block_out ? block_out : blocks;
-  if (launch_topk_select(a1, block_topk, true, score_blocks(B, nb), bout, nullptr, st, nullptr, 0, block, cand))
+  if (launch_topk_filter(B, nb, cscores, nullptr, block_topk, t1.hist, t1.hist2, t1.ctl, t1.cand, t1.cnt, st))
     return CSA2_ERR_DEVICE;
-  // fine: the exact score of every candidate position, listed, then the Top-K (the
-  // candidates ascend, so the winners come out in position order)
+  if (launch_topk_finalize(B, nb, block_topk, true, t1.ctl, t1.hist2, t1.cand, t1.cnt, bout, nullptr, st, block,
+                           n_keys, cand))
+    return CSA2_ERR_DEVICE;
   ScoreArgs a2 = score_args(CSA2_PREC_FP8, B, 1, H, dk, q, q_dtype, w, k8, k_scale, n_max, n_keys, nullptr, cand, C,
-                            fscores, nullptr, 1);
-  a2.local = true;
-  a2.lc = l2;
+                            fscores, t2.hist, 1);
   if (launch_score(a2, st)) return CSA2_ERR_DEVICE;
-  return dev_status(launch_topk_select(a2, K, true, score_blocks(B, C), idx_out, nullptr, st));
+  // the expanded candidates ascend (blocks ascending, positions within a block ascending,
+  // -1 for none), so the filtered list is in position order
+  if (launch_topk_filter(B, C, fscores, cand, K, t2.hist, t2.hist2, t2.ctl, t2.cand, t2.cnt, st))
+    return CSA2_ERR_DEVICE;
+  return dev_status(launch_topk_finalize(B, C, K, true, t2.ctl, t2.hist2, t2.cand, t2.cnt, idx_out, nullptr, st));
 }
 
 }  // extern "C"

@@ -330,7 +330,10 @@ int csa2_coarse_keys(int B, int64_t n_max, const int32_t* n_keys, int dk, int bl
  * the best `block_topk` blocks (ties to the lower block), score every position inside
  * them and keep the best K (ties to the lower position).  idx_out [B][1][K] ascending,
  * -1 padded; block_out [B][1][block_topk] (nullable) the kept blocks ascending.
- * ws: csa2_hier_select_workspace_size() bytes.
+ * ws: csa2_hier_select_workspace_size() bytes.  Each stage's scan lists its candidates for
+ * the selection (four launches) when its rows span at most 128 score blocks; larger stages
+ * (e.g. more than 32768 block keys for a single sequence) take the histogram selection
+ * (seven launches).  Both give the same result.
  */
 int csa2_hier_select(int B, int H, int dk, const void* q, int q_dtype, const float* w, const uint8_t* k8,
                      const float* k_scale, const uint8_t* kb8, const float* kb_scale, int64_t n_max,

@@ -368,27 +368,30 @@ def test_coarse_keys_bitexact():
     assert np.array_equal(kb.cpu().numpy(), kb_ref)
 
 
-def test_hier_select_matches_oracle():
-    wl = workloads.workload("hier1m", N=64 * 2048)
-    n = wl.N
+# (block, N, block_topk, K): both stages on candidate lists; a coarse stage of 65536 block
+# keys, more score blocks than the lists cover, which takes the histogram selection
+@pytest.mark.parametrize("block,n,block_topk,K", [(64, 64 * 2048, 256, 1024), (4, 1 << 18, 512, 512)],
+                         ids=["lists", "histogram"])
+def test_hier_select_matches_oracle(block, n, block_topk, K):
+    wl = workloads.workload("hier1m", N=n)
     k = wl.index_keys(0)[None]
     k8r, ksr = oracle.quantize_fp8(k)
     nk = np.array([n - 100], np.int32)
-    kb_ref, kbs_ref = oracle.coarse_keys(k8r, ksr, nk, 64)
+    kb_ref, kbs_ref = oracle.coarse_keys(k8r, ksr, nk, block)
     q, w = wl.index_query(), wl.head_weights()
     k8 = torch.empty((1, n, 64), dtype=torch.uint8, device=DEV)
     ks = torch.empty((1, n), dtype=torch.float32, device=DEV)
     csa2.quantize_kv(csa2.FMT_FP8_PER_TOKEN, to_dev(k), k8, ks)
-    kb, kbs = csa2.coarse_keys(k8, ks, to_dev(nk), 64)
-    idx, blk = csa2.hier_select(to_dev(q, torch.bfloat16), to_dev(w), k8, ks, kb, kbs, to_dev(nk), 64, 256, 1024,
-                                want_blocks=True)
-    cs = oracle.index_score(oracle.PREC_FP8, q, w, kb_ref, kbs_ref, (nk + 63) // 64)
-    check_topk_near_tie(blk.cpu().numpy(), cs, 256)
+    kb, kbs = csa2.coarse_keys(k8, ks, to_dev(nk), block)
+    idx, blk = csa2.hier_select(to_dev(q, torch.bfloat16), to_dev(w), k8, ks, kb, kbs, to_dev(nk), block, block_topk,
+                                K, want_blocks=True)
+    cs = oracle.index_score(oracle.PREC_FP8, q, w, kb_ref, kbs_ref, (nk + block - 1) // block)
+    check_topk_near_tie(blk.cpu().numpy(), cs, block_topk)
     # the fine stage scored on the GPU's own block list, unconditionally
-    cand = oracle.expand_blocks(blk.cpu().numpy(), 64, nk)
+    cand = oracle.expand_blocks(blk.cpu().numpy(), block, nk)
     fs = oracle.index_score(oracle.PREC_FP8, q, w, k8r, ksr, nk, cand=cand)
     full = np.full((1, 1, n), -np.inf)
     full[0, 0, cand[0, 0][cand[0, 0] >= 0]] = fs[0, 0][cand[0, 0] >= 0]
     g = idx.cpu().numpy()
-    check_topk_near_tie(g, full, 1024)
+    check_topk_near_tie(g, full, K)
     assert np.all(np.isin(g[g >= 0], cand[0, 0][cand[0, 0] >= 0]))
