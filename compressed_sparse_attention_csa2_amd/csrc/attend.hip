@@ -700,14 +700,17 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   // ---- phase 4: every entry group writes its partial sums to its own LDS slice (sA and
   //      sP are dead once all waves are past PV); then each thread sums the kWPT slices of
   //      8 channels of one head in a fixed order (deterministic), normalises and stores.
+  //      Within a head's 128-channel tile, channels 8 n .. 8 n + 3 sit at float4 n and
+  //      8 n + 4 .. 8 n + 7 at float4 16 + n, so that the 16 lanes of a row write (and the
+  //      summing threads read) 256 contiguous bytes: with the channels in order the head
+  //      rows' writes hit the same banks (four-way conflicts, 1.3 us per wave).
   __syncthreads();
   if (pv_active) {
-    const int c = 128 * ct + 8 * n16;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      float4* o = reinterpret_cast<float4*>(&sO[((size_t)eq * kAttHeads + 4 * g + rr) * D + c]);
-      o[0] = make_float4(acc[0][rr], acc[1][rr], acc[2][rr], acc[3][rr]);
-      o[1] = make_float4(acc[4][rr], acc[5][rr], acc[6][rr], acc[7][rr]);
+      float4* o = reinterpret_cast<float4*>(&sO[((size_t)eq * kAttHeads + 4 * g + rr) * D + 128 * ct]);
+      o[n16] = make_float4(acc[0][rr], acc[1][rr], acc[2][rr], acc[3][rr]);
+      o[16 + n16] = make_float4(acc[4][rr], acc[5][rr], acc[6][rr], acc[7][rr]);
     }
   }
   __syncthreads();
@@ -717,8 +720,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
 #pragma unroll
     for (int gq = 0; gq < kWPT; ++gq) {
-      const float4* src = reinterpret_cast<const float4*>(&sO[((size_t)gq * kAttHeads + hl) * D + c]);
-      const float4 a0 = src[0], a1 = src[1];
+      const float4* src = reinterpret_cast<const float4*>(&sO[((size_t)gq * kAttHeads + hl) * D + (c & ~127)]);
+      const float4 a0 = src[(c & 127) >> 3], a1 = src[16 + ((c & 127) >> 3)];
       o0.x += a0.x; o0.y += a0.y; o0.z += a0.z; o0.w += a0.w;
       o1.x += a1.x; o1.y += a1.y; o1.z += a1.z; o1.w += a1.w;
     }
