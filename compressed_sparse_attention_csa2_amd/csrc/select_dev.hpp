@@ -367,8 +367,20 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
   const int spec = in.spec, ssh = __builtin_ctz((unsigned)spec);
   const int slots = nreg * spec;  // < kFinStage on the fast path
   const bool few = nreg <= kFastRegions && nreg * (int64_t)spec <= kFinStage;
-  // 0. every load issued together: the region counts, cuts and visible counts, and (few
-  //    regions) the first 64 slots of every region, whatever their counts turn out to be
+  // 0. every load issued together: (few regions) the first spec slots of every region,
+  //    whatever their counts turn out to be, then the region counts, cuts and visible counts,
+  //    masked only after all are issued (a value used or spilled right after its load is
+  //    waited for there, and with it every load issued before: the slots go first)
+  uint2 fv[kFastPer];  // fast path: item tid + NT u = slot (i & (spec - 1)) of region (i >> ssh)
+  if (few) {  // uniform
+    const uint2* crow = candbuf + (int64_t)r * nreg * stride;
+#pragma unroll
+    for (int u = 0; u < kFastPer; ++u) {
+      const int i = tid + NT * u;
+      const int ic = i < slots ? i : slots - 1;
+      if (NT * u < slots) fv[u] = crow[(int64_t)(ic >> ssh) * stride + (ic & (spec - 1))];  // uniform bound
+    }
+  }
   uint32_t rcv[kRP], rvv[kRP];
   int32_t rcutv[kRP];
   // (unconditional loads from clamped addresses, masked afterwards: a load behind a branch
@@ -385,19 +397,12 @@ __device__ __forceinline__ uint32_t select_row(const SelectIn& in, int r, Select
     rcv[j] = cnt[o];
     rvv[j] = vis[o];
     rcutv[j] = cut[o];
-    if (rg >= nreg) {
+  }
+#pragma unroll
+  for (int j = 0; j < kRP; ++j) {
+    if (tid + NT * j >= nreg) {
       rcv[j] = rvv[j] = 0u;
       rcutv[j] = -1;
-    }
-  }
-  uint2 fv[kFastPer];  // fast path: item tid + NT u = slot (i & (spec - 1)) of region (i >> ssh)
-  if (few) {  // uniform
-    const uint2* crow = candbuf + (int64_t)r * nreg * stride;
-#pragma unroll
-    for (int u = 0; u < kFastPer; ++u) {
-      const int i = tid + NT * u;
-      const int ic = i < slots ? i : slots - 1;
-      if (NT * u < slots) fv[u] = crow[(int64_t)(ic >> ssh) * stride + (ic & (spec - 1))];  // uniform bound
     }
   }
   for (int i = tid; i < kSelMaxRegions / 32; i += NT) sm.raw[i] = 0u;
