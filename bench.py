@@ -126,6 +126,27 @@ def time_flushed(calls, steps, warmup, flush):
     return float(per.sum(axis=1).mean()), [float(x) for x in per.mean(axis=0)], wall
 
 
+def time_flushed_by_difference(calls, steps, flush):
+    """The flushed layers timed by difference (as time_cold): per layer, HIP events around
+    (flush, layer call) and around a flush alone, interleaved; the mean difference is the
+    layer's GPU time without the event pair's own dispatch.  Returns (step ms, per-layer ms)."""
+    n = len(calls)
+    both, alone = np.zeros((steps, n)), np.zeros((steps, n))
+    for s in range(steps):
+        for i, f in enumerate(calls):
+            for sink, run in ((both, f), (alone, None)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                flush()
+                if run is not None:
+                    run()
+                b.record()
+                torch.cuda.synchronize()
+                sink[s, i] = a.elapsed_time(b)
+    per = both.mean(axis=0) - alone.mean(axis=0)
+    return float(per.sum()), [float(x) for x in per]
+
+
 def time_warm(plans, steps, warmup):
     for s in range(warmup):
         plans[s % len(plans)].run()
@@ -825,6 +846,8 @@ def run_group128k(args):
     log("flushed protocol: warmup %d, timing %d steps" % (args.warmup, args.steps))
     torch.cuda.synchronize()
     ms_step, per_layer, wall = time_flushed(calls, args.steps, args.warmup, flush)
+    # the same layers timed by difference (the event pairs' own dispatch cancelled), beside it
+    diff_step, diff_layer = time_flushed_by_difference(calls, min(args.steps, 60), flush)
     # warm protocol: the whole group in one call
     plans = [csa2.GroupPlan([dict(L) for L in layers],
                             csa2.GroupCache(c["n_keys"], c["codes"], c["scales"], c["k8"], c["ks"], wl.K,
@@ -850,6 +873,10 @@ def run_group128k(args):
         "step_pct_stream_ceiling": round(100 * gbs / ceil, 2),
         "per_layer_ms": [round(x, 5) for x in per_layer],
         "flushed_loop_wall_s": round(wall, 4),
+        "by_difference_ms_per_step": round(diff_step, 5),
+        "by_difference_per_layer_ms": [round(x, 5) for x in diff_layer],
+        "by_difference_protocol": "flushed, each layer timed by HIP events around (flush, layer) minus events around "
+                                  "a flush alone: the event pair's own dispatch cancelled, as in the kernel trace",
         "warm_ms_per_step": round(warm_ms, 5), "warm_value": round(wl.B / (warm_ms / 1e3), 1),
         "warm_protocol": "the group in one csa2_layer_group call (the Full scan keeps its keys for the Reindex "
                          "rescan in the Infinity Cache), %d cache copies rotated between steps" % args.copies,
