@@ -9,7 +9,9 @@
 //
 // MFMA path (bf16 queries, Hq % 16 == 0, D in {128, 256, 512}).  One block = one query
 // row x 16 heads (the MFMA M dimension) x one split of up to 512 selected entries, 16
-// waves, so the pages' Top-512 needs no merge; larger K runs several splits and a second
+// waves, so the pages' Top-512 needs no merge; without a sliding window and with the
+// per-channel layout, each such unit runs as D / 128 blocks that all compute the logits and
+// the softmax, each then taking PV and the output of one 128-channel tile; larger K runs several splits and a second
 // kernel merges their partial softmaxes by log-sum-exp (a kernel boundary: merging inside
 // the kernel would need a device-scope release fence, which costs more here).  The
 // per-channel scale s_c factors out of both contractions: logits use q'' = q * s * 2^k_h in
@@ -326,7 +328,7 @@ __device__ __forceinline__ void attend_window_block(
   }
 }
 
-template <int D, int WPT, bool G16>
+template <int D, int WPT, bool G16, int OW = D>
 struct AttLds {
   static constexpr int kApad = D + 8;           // fp16 per A row (padding against bank conflicts)
   static constexpr int kPpad = kAttSplit + 8;
@@ -334,7 +336,7 @@ struct AttLds {
   static constexpr size_t kA = (size_t)kAttHeads * kApad * 2;
   static constexpr size_t kP = (size_t)kAttHeads * kPpad * 2;
   static constexpr size_t kS = G16 ? (size_t)(D / 16) * kSpad * 2 : 0;  // [group][entry] fp16 scales
-  static constexpr size_t kO = (size_t)WPT * kAttHeads * D * 4;  // per entry group, after sA/sP/sS are dead
+  static constexpr size_t kO = (size_t)WPT * kAttHeads * OW * 4;  // per entry group, after sA/sP/sS are dead
   // per-channel layout: the split's FP4 rows are staged in LDS ([entry][D/2 bytes], 16-byte
   // chunks XOR-swizzled), followed by sA; sP takes sA's place once QK is done.  G16: sA,
   // sP, sS side by side (its rows are read from global memory).
@@ -354,7 +356,7 @@ struct AttLds {
 // The scale no longer factors out of the contractions; instead the split's scales are
 // staged in LDS as fp16, [group][entry], and multiply the fp16 key / value operands after
 // the E2M1 conversion (E2M1 * E4M3 is exact in fp16, so the operands stay exact).
-template <int D, bool G16>
+template <int D, bool G16, bool CS>
 __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     int R, int T, int Hq, int K, int S, int P, const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const void* __restrict__ scales_v, int64_t n_max, const int32_t* __restrict__ idx, float softmax_scale, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
@@ -368,7 +370,13 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   constexpr int kQKW = G16 ? kAttWaves : 8;
   constexpr int kAttTPW = kAttSplit / 16 / kQKW;  // 16-entry QK tiles per QK wave
   static_assert(kAttTPW * 16 * kQKW == kAttSplit, "QK tiles cover the split");
-  constexpr int kWPT = (kAttWaves / kCT < kAttSplit / 32) ? kAttWaves / kCT : kAttSplit / 32;  // waves per tile in PV
+  // CS (channel split): the block computes every logit and the softmax of its (row, split, head
+  // group) but PV and the output only for channel tile `cb`; the kCT blocks of a head group
+  // repeat QK and each takes one tile, so the chip runs kCT times as many blocks with a
+  // quarter of the PV each (D = 512) and no merge
+  constexpr int kPVT = CS ? 1 : kCT;           // channel tiles per block in PV
+  constexpr int kOW = 128 * kPVT;              // channels per head row of the partial sums
+  constexpr int kWPT = (kAttWaves / kPVT < kAttSplit / 32) ? kAttWaves / kPVT : kAttSplit / 32;  // waves per tile in PV
   // per-channel layout: the split's rows are gathered whole (a wave instruction reads
   // kRPI complete rows, 16 bytes per lane) and staged in LDS; chunk c of entry e sits in
   // chunk slot c ^ swz(e), so that the 16 entries of an MFMA operand read spread over
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   static_assert(kGI * kRPI * kAttWaves == kAttSplit, "the gather covers the split");
   auto swz = [](int e) { return (e / (16 / kNC)) & (kNC - 1); };
   constexpr int kEPW = kAttSplit / kWPT;       // entries per wave in PV (a multiple of 32)
-  using L = AttLds<D, kWPT, G16>;
+  using L = AttLds<D, kWPT, G16, kOW>;
   constexpr int kNG = D / 16;                  // scale groups per entry (G16)
   __shared__ float s_scale[G16 ? 1 : D];
   __shared__ int32_t s_idx[kAttSplit];
@@ -392,7 +400,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   uint16_t* sP = reinterpret_cast<uint16_t*>(s_u + L::kOffP);
   uint16_t* sS = reinterpret_cast<uint16_t*>(s_u + L::kOffS);  // G16: [kNG][kSpad] fp16
   unsigned char* s_rows = s_u;                 // per-channel: the split's rows (see AttLds)
-  float* sO = reinterpret_cast<float*>(s_u);  // [kWPT][16][D], used once the rows, sA, sP, sS are dead
+  float* sO = reinterpret_cast<float*>(s_u);  // [kWPT][16][kOW], used once the rows, sA, sP, sS are dead
   const float* scales = static_cast<const float*>(scales_v);
 
   // XCD-aware order: workgroups are dealt to the 8 XCDs in turn (L2 per XCD), so a unit
@@ -400,8 +408,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   // gather the same rows through one L2.  Units past the last (grid rounded up) exit.
   const int X = S + (wcodes ? 1 : 0);            // splits, plus the window's block
   const int G = Hq / kAttHeads;                  // head groups
+  constexpr int kNCB = CS ? kCT : 1;             // channel blocks per head group
   const int wg = blockIdx.x, slot = wg >> 3;
-  const int unit = (slot / G) * 8 + (wg & 7), hg = slot % G;
+  const int unit = (slot / (G * kNCB)) * 8 + (wg & 7), hg = (slot % (G * kNCB)) / kNCB;
+  const int ctb = CS ? slot % kNCB : 0;        // CS: this block's channel tile
   if (unit >= X * R) return;
   const int split = unit % X, r = unit / X;
   if (split == S) {  // the sliding window's block (grid.x = S + 1 with a window)
@@ -603,7 +613,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   //      hits since the rows were just read) so that they arrive during the softmax.  Wave
   //      (channel tile ct, entry group eq); lane (channel block n16, group g) takes one
   //      32-bit word (8 channels) of each of the 8 entries el..el+7 of every 32-entry k-step.
-  const int ct = wave % kCT, eq = wave / kCT;
+  const int ct = CS ? ctb : wave % kCT, eq = CS ? wave : wave / kCT;
   const bool pv_active = eq < kWPT;
   uint32_t pw[kEPW / 32][8];
 #pragma unroll
@@ -708,52 +718,46 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   if (pv_active) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      float4* o = reinterpret_cast<float4*>(&sO[((size_t)eq * kAttHeads + 4 * g + rr) * D + 128 * ct]);
+      float4* o = reinterpret_cast<float4*>(&sO[((size_t)eq * kAttHeads + 4 * g + rr) * kOW + 128 * (CS ? 0 : ct)]);
       o[n16] = make_float4(acc[0][rr], acc[1][rr], acc[2][rr], acc[3][rr]);
       o[16 + n16] = make_float4(acc[4][rr], acc[5][rr], acc[6][rr], acc[7][rr]);
     }
   }
   __syncthreads();
-  constexpr int kOItems = kAttHeads * D / 8;
+  // items of 4 channels: 128 c0 + 8 n + 4 hf + [0, 4) of head hl sit at float4 16 hf + n of the
+  // head's tile in every slice
+  constexpr int kOItems = kAttHeads * kOW / 4;
   for (int i = tid; i < kOItems; i += kAttThreads) {
-    const int hl = i / (D / 8), c = (i % (D / 8)) * 8;
-    float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
+    const int hl = i / (kOW / 4), ci = i % (kOW / 4);
+    const int tile = ci >> 5, n = ci & 15, hf = (ci >> 4) & 1;
+    const int c = 128 * (CS ? ctb : tile) + 8 * n + 4 * hf;
+    float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int gq = 0; gq < kWPT; ++gq) {
-      const float4* src = reinterpret_cast<const float4*>(&sO[((size_t)gq * kAttHeads + hl) * D + (c & ~127)]);
-      const float4 a0 = src[(c & 127) >> 3], a1 = src[16 + ((c & 127) >> 3)];
-      o0.x += a0.x; o0.y += a0.y; o0.z += a0.z; o0.w += a0.w;
-      o1.x += a1.x; o1.y += a1.y; o1.z += a1.z; o1.w += a1.w;
+      const float4 a4 = reinterpret_cast<const float4*>(&sO[((size_t)gq * kAttHeads + hl) * kOW + 128 * tile])[16 * hf + n];
+      o4.x += a4.x; o4.y += a4.y; o4.z += a4.z; o4.w += a4.w;
     }
     const float l = s_l[hl];
     const float inv_l = (l > 0.0f) ? 1.0f / l : 0.0f;
-    float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-#pragma unroll
-    for (int m = 0; m < 8; ++m) o[m] *= inv_l;
+    float o[4] = {o4.x * inv_l, o4.y * inv_l, o4.z * inv_l, o4.w * inv_l};
     const int h = hg * kAttHeads + hl;
     if (!G16) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) o[m] *= s_scale[c + m];
+      for (int m = 0; m < 4; ++m) o[m] *= s_scale[c + m];
     }
     if (P == 1) {
       const int64_t oi = ((int64_t)r * Hq + h) * D + c;
       if (out_bf16) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) w4[k2] = pack2(bf16_rne(o[2 * k2]), bf16_rne(o[2 * k2 + 1]));
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + oi) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + oi) =
+            make_uint2(pack2(bf16_rne(o[0]), bf16_rne(o[1])), pack2(bf16_rne(o[2]), bf16_rne(o[3])));
       } else {
-        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi);
-        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi) = make_float4(o[0], o[1], o[2], o[3]);
       }
     } else {
-      float4* dst = reinterpret_cast<float4*>(part + (((int64_t)r * P + split) * Hq + h) * D + c);
-      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+      *reinterpret_cast<float4*>(part + (((int64_t)r * P + split) * Hq + h) * D + c) = make_float4(o[0], o[1], o[2], o[3]);
     }
   }
-  if (tid < kAttHeads) {
+  if (tid < kAttHeads && ctb == 0) {
     const float l = s_l[tid];
     if (P == 1) {
       if (lse) lse[(int64_t)r * Hq + hg * kAttHeads + tid] = (l > 0.0f) ? s_m[tid] + __logf(l) : kNegInf;
@@ -944,14 +948,16 @@ size_t attend_ws_floats(int R, int Hq, int D, int K, int window) {
   return (size_t)R * P * Hq * D + (size_t)R * P * Hq * 2;
 }
 
-template <int D, bool G16>
+template <int D, bool G16, bool CS>
 static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
   // the window (if any) is one more block column, run beside the selection's splits
-  // one block per (unit = (row, split or window), head group), dealt in XCD-aware order
+  // one block per (unit = (row, split or window), head group[, channel tile]), dealt in
+  // XCD-aware order
   const int units = (S + (a.swa_codes ? 1 : 0)) * a.B * a.T;
-  const dim3 g((unsigned)(8 * (a.Hq / kAttHeads) * ((units + 7) / 8)));
+  const int ncb = CS ? D / 128 : 1;
+  const dim3 g((unsigned)(8 * (a.Hq / kAttHeads) * ncb * ((units + 7) / 8)));
   float* part_ml = a.part ? a.part + (size_t)a.B * a.T * P * a.Hq * D : nullptr;
-  hipLaunchKernelGGL((k_attend_part<D, G16>), g, dim3(kAttThreads), 0, st, a.B * a.T, a.T, a.Hq, a.K, S, P,
+  hipLaunchKernelGGL((k_attend_part<D, G16, CS>), g, dim3(kAttThreads), 0, st, a.B * a.T, a.T, a.Hq, a.K, S, P,
                      (const uint16_t*)a.q, a.codes, a.scales, a.n_max, a.idx, a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml, a.swa_codes,
                      a.swa_scales, a.swa_n_max, a.swa_end, a.window);
   if (P > 1)
@@ -962,9 +968,11 @@ static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
 template <int D>
 static void launch_mfma_d(const AttendArgs& a, int S, int P, hipStream_t st) {
   if (a.g16)
-    launch_mfma<D, true>(a, S, P, st);
+    launch_mfma<D, true, false>(a, S, P, st);
+  else if (a.swa_codes)  // the window's block column computes every channel
+    launch_mfma<D, false, false>(a, S, P, st);
   else
-    launch_mfma<D, false>(a, S, P, st);
+    launch_mfma<D, false, true>(a, S, P, st);
 }
 
 int launch_attend(const AttendArgs& a, hipStream_t st) {
