@@ -376,7 +376,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   // quarter of the PV each (D = 512) and no merge
   constexpr int kPVT = CS ? 1 : kCT;           // channel tiles per block in PV
   constexpr int kOW = 128 * kPVT;              // channels per head row of the partial sums
-  constexpr int kWPT = (kAttWaves / kPVT < kAttSplit / 32) ? kAttWaves / kPVT : kAttSplit / 32;  // waves per tile in PV
+  // waves per tile in PV (CS: each logit wave takes PV over its own entries)
+  constexpr int kWPT = CS ? kQKW : ((kAttWaves / kPVT < kAttSplit / 32) ? kAttWaves / kPVT : kAttSplit / 32);
   // per-channel layout: the split's rows are gathered whole (a wave instruction reads
   // kRPI complete rows, 16 bytes per lane) and staged in LDS; chunk c of entry e sits in
   // chunk slot c ^ swz(e), so that the 16 entries of an MFMA operand read spread over
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   using L = AttLds<D, kWPT, G16, kOW>;
   constexpr int kNG = D / 16;                  // scale groups per entry (G16)
   __shared__ float s_scale[G16 ? 1 : D];
-  __shared__ int32_t s_idx[kAttSplit];
+  __shared__ __align__(16) int32_t s_idx[kAttSplit];
   __shared__ float s_red[kAttWaves][kAttHeads];
   __shared__ float s_m[kAttHeads], s_l[kAttHeads];
   __shared__ float s_down[kAttHeads];          // per head: softmax scale / the query prescale
@@ -569,163 +570,295 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   if constexpr (!G16) __builtin_amdgcn_s_waitcnt(0);  // this wave's row loads have landed in LDS
   __syncthreads();
 
-  // ---- phase 1b: logits of this wave's kAttTPW tiles of 16 entries.  The channel loop is
-  //      outside the tile loop, so each A operand (16 B of q'' per lane) is read from LDS once
-  //      for all of the wave's tiles.
-  float logit[kAttTPW][4];
-  v4f a[kAttTPW];
+  if constexpr (CS) {
+    // ---- CS phase 1: the logits transposed (rows x q''^T, the row chunk as the MFMA's A
+    //      operand and q'' as B): lane (head n16, g) holds head n16's logits of the entries
+    //      16 t' + 4 g + rr (t' = qw kAttTPW + t) of this wave's tiles
+    v4f a[kAttTPW];
 #pragma unroll
-  for (int t = 0; t < kAttTPW; ++t) a[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kAttTPW; ++t) a[t] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < (qk_wave ? kCT : 0); ++i) {
-    uint32_t wd[kAttTPW][4];
-    _Float16 gs[kAttTPW][2];
-#pragma unroll
-    for (int t = 0; t < kAttTPW; ++t) {
-      const int el = (qw * kAttTPW + t) * 16 + n16;  // this lane's entry in the split
-      uint4 kv;
-      if constexpr (G16) kv = kw[t][i];
-      else kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
-      wd[t][0] = kv.x; wd[t][1] = kv.y; wd[t][2] = kv.z; wd[t][3] = kv.w;
-      gs[t][0] = gs[t][1] = (_Float16)1.0f;
-      if (G16) {  // channels 128 i + 32 g + [0, 32): groups 8 i + 2 g and 8 i + 2 g + 1
-        gs[t][0] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g) * L::kSpad + el]);
-        gs[t][1] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g + 1) * L::kSpad + el]);
-      }
-    }
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      const v8h av = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
+    for (int i = 0; i < (qk_wave ? kCT : 0); ++i) {
+      uint32_t wd[kAttTPW][4];
 #pragma unroll
       for (int t = 0; t < kAttTPW; ++t) {
-        v8h bv = decode8_f16(wd[t][sub]);
-        if (G16) bv = bv * gs[t][sub >> 1];
-        a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, a[t], 0, 0, 0);
+        const int el = (qw * kAttTPW + t) * 16 + n16;
+        const uint4 kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
+        wd[t][0] = kv.x; wd[t][1] = kv.y; wd[t][2] = kv.z; wd[t][3] = kv.w;
+      }
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const v8h qv8 = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
+#pragma unroll
+        for (int t = 0; t < kAttTPW; ++t)
+          a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode8_f16(wd[t][sub]), qv8, a[t], 0, 0, 0);
       }
     }
-  }
+    // ---- CS phase 2: this wave's softmax statistics per head (no block barrier): the
+    //      maximum and the sum over the lane's 4 kAttTPW logits, then over the 4 lanes of the
+    //      head (g); p = exp(logit - m) stays in registers as PV's A operand
+    const float dn = s_down[n16];
+    float pr[kAttTPW][4];
+    float m = kNegInf;
 #pragma unroll
-  for (int t = 0; t < kAttTPW; ++t)
+    for (int t = 0; t < kAttTPW; ++t) {
+      const int4 sv = *reinterpret_cast<const int4*>(&s_idx[(qw * kAttTPW + t) * 16 + 4 * g]);
+      const int32_t svv[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (qk_wave && jt[t] >= 0) ? a[t][rr] * s_down[4 * g + rr] : kNegInf;
-
-  // ---- phase 3a: read the PV code words now (staged rows in LDS; G16: global loads, cache
-  //      hits since the rows were just read) so that they arrive during the softmax.  Wave
-  //      (channel tile ct, entry group eq); lane (channel block n16, group g) takes one
-  //      32-bit word (8 channels) of each of the 8 entries el..el+7 of every 32-entry k-step.
-  const int ct = CS ? ctb : wave % kCT, eq = CS ? wave : wave / kCT;
-  const bool pv_active = eq < kWPT;
-  uint32_t pw[kEPW / 32][8];
-#pragma unroll
-  for (int ks = 0; ks < kEPW / 32; ++ks) {
-    const int el = eq * kEPW + 32 * ks + 8 * g;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int e = el + jj;
-      if constexpr (G16) {
-        const int32_t j = sel[e];  // -1 past K (read unconditionally: no branch per load)
-        // p is 0 for skipped entries, so any valid row may stand in for them
-        pw[ks][jj] = *reinterpret_cast<const uint32_t*>(cb + (int64_t)(j >= 0 ? j : 0) * kRowBytes + 64 * ct + 4 * n16);
-      } else {  // word 16 ct + n16 of the staged row
-        pw[ks][jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes +
-                                                         16 * ((4 * ct + (n16 >> 2)) ^ swz(e)) + 4 * (n16 & 3));
+      for (int rr = 0; rr < 4; ++rr) {
+        pr[t][rr] = (qk_wave && svv[rr] >= 0) ? a[t][rr] * dn : kNegInf;
+        m = fmaxf(m, pr[t][rr]);
       }
     }
-  }
-
-  // ---- phase 2: softmax statistics of the split (heads 4g + rr of this lane).  Per-wave
-  //      partials go to LDS; 256 threads (one 16-lane row per head) reduce them by DPP.
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float lsum = 0.0f;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    float v = logit[0][rr];
+    for (int t = 0; t < kAttTPW; ++t)
 #pragma unroll
-    for (int t = 1; t < kAttTPW; ++t) v = fmaxf(v, logit[t][rr]);
-    v = row16_max(v);
-    if (n16 == 0) s_red[wave][4 * g + rr] = v;
-  }
-  __syncthreads();
-  static_assert(kAttWaves == 16 && kAttHeads == 16, "one 16-lane row per head reduces the 16 waves");
-  if (tid < 256) {
-    const float v = row16_max(s_red[tid & 15][tid >> 4]);
-    if ((tid & 15) == 0) s_m[tid >> 4] = v;
-  }
-  __syncthreads();
+      for (int rr = 0; rr < 4; ++rr) {
+        pr[t][rr] = (m == kNegInf) ? 0.0f : __expf(pr[t][rr] - m);
+        lsum += pr[t][rr];
+      }
+    lsum += __shfl_xor(lsum, 16);  // the four lanes of a head add the same pairs: equal sums
+    lsum += __shfl_xor(lsum, 32);
+    // ---- CS phase 3: PV over this wave's entries for channel tile ctb.  K step ks takes the
+    //      wave's tiles 2 ks and 2 ks + 1; its K slot 8 g + j is entry 16 t0' + 4 g + j (j < 4)
+    //      or 16 t1' + 4 g + j - 4 (j >= 4), which is where lane (head, g) holds p already;
+    //      lane (channel block n16, g) reads word 16 ctb + n16 (8 channels) of those 8 entries
+    //      and nibble-interleaves pairs of them as in the other path.
+    v4f acc[8];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int h = 4 * g + rr;
-    const float m = s_m[h];
-    float v = 0.0f;
+    for (int mm = 0; mm < 8; ++mm) acc[mm] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < (qk_wave ? kAttTPW : 0); ++t) {
-      const float p = (m == kNegInf) ? 0.0f : __expf(logit[t][rr] - m);
-      const _Float16 ph = (_Float16)p;
-      sP[h * L::kPpad + (qw * kAttTPW + t) * 16 + n16] = __builtin_bit_cast(uint16_t, ph);
-      v += p;
-    }
-    v = row16_sum(v);
-    if (n16 == 0) s_red[wave][h] = v;
-  }
-  __syncthreads();
-  if (tid < 256) {
-    const float v = row16_sum(s_red[tid & 15][tid >> 4]);
-    if ((tid & 15) == 0) s_l[tid >> 4] = v;
-  }
-
-  // ---- phase 3b: o[h][c] = sum_j p[h][j] e[j][c] over this wave's entries and channel
-  //      tile.  For each pair of entries the two code words are nibble-interleaved so that
-  //      one byte holds the same channel of both entries; one fp4->fp16 pair conversion
-  //      then yields the (entry 2p, entry 2p+1) dword the MFMA k-order wants.
-  v4f acc[8];
+    for (int ks = 0; ks < (qk_wave ? kAttTPW / 2 : 0); ++ks) {
+      uint32_t pw[8];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
-  if (pv_active) {
+      for (int jj = 0; jj < 8; ++jj) {
+        const int e = (qw * kAttTPW + 2 * ks + (jj >> 2)) * 16 + 4 * g + (jj & 3);
+        pw[jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes + 16 * ((4 * ctb + (n16 >> 2)) ^ swz(e)) +
+                                                    4 * (n16 & 3));
+      }
+      v8h pa;
 #pragma unroll
-    for (int ks = 0; ks < kEPW / 32; ++ks) {
-      const int el = eq * kEPW + 32 * ks + 8 * g;  // first of this lane's 8 entries
-      const v8h pa = *reinterpret_cast<const v8h*>(&sP[n16 * L::kPpad + el]);
-      // G16: the scales of entries el..el+7 in this lane's group (channels 128 ct + 8 n16 ..)
-      v8h sc = {};
-      if (G16) sc = *reinterpret_cast<const v8h*>(&sS[(8 * ct + (n16 >> 1)) * L::kSpad + el]);
+      for (int rr = 0; rr < 4; ++rr) {
+        pa[rr] = (_Float16)pr[2 * ks][rr];
+        pa[4 + rr] = (_Float16)pr[2 * ks + 1][rr];
+      }
       uint32_t xe[4], xo[4];
 #pragma unroll
       for (int p2 = 0; p2 < 4; ++p2) {
-        const uint32_t w0 = pw[ks][2 * p2], w1 = pw[ks][2 * p2 + 1];
+        const uint32_t w0 = pw[2 * p2], w1 = pw[2 * p2 + 1];
         xe[p2] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);  // channels 0,2,4,6
         xo[p2] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);  // channels 1,3,5,7
       }
-#define CSA2_PV_MFMA(M, X, BS)                                                                                  \
+#define CSA2_CS_MFMA(M, X, BS)                                                                                 \
   {                                                                                                          \
     const uint4 bw = make_uint4(cvt_pair_f16<BS>(X[0]), cvt_pair_f16<BS>(X[1]), cvt_pair_f16<BS>(X[2]),      \
                                 cvt_pair_f16<BS>(X[3]));                                                     \
-    v8h bv = __builtin_bit_cast(v8h, bw);                                                                    \
-    if (G16) bv = bv * sc;                                                                                   \
-    acc[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, acc[M], 0, 0, 0);                                \
+    acc[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(v8h, bw), acc[M], 0, 0, 0);        \
   }
-      CSA2_PV_MFMA(0, xe, 0) CSA2_PV_MFMA(1, xo, 0) CSA2_PV_MFMA(2, xe, 1) CSA2_PV_MFMA(3, xo, 1)
-      CSA2_PV_MFMA(4, xe, 2) CSA2_PV_MFMA(5, xo, 2) CSA2_PV_MFMA(6, xe, 3) CSA2_PV_MFMA(7, xo, 3)
-#undef CSA2_PV_MFMA
+      CSA2_CS_MFMA(0, xe, 0) CSA2_CS_MFMA(1, xo, 0) CSA2_CS_MFMA(2, xe, 1) CSA2_CS_MFMA(3, xo, 1)
+      CSA2_CS_MFMA(4, xe, 2) CSA2_CS_MFMA(5, xo, 2) CSA2_CS_MFMA(6, xe, 3) CSA2_CS_MFMA(7, xo, 3)
+#undef CSA2_CS_MFMA
     }
-  }
-
-  // ---- phase 4: every entry group writes its partial sums to its own LDS slice (sA and
-  //      sP are dead once all waves are past PV); then each thread sums the kWPT slices of
-  //      8 channels of one head in a fixed order (deterministic), normalises and stores.
-  //      Within a head's 128-channel tile, channels 8 n .. 8 n + 3 sit at float4 n and
-  //      8 n + 4 .. 8 n + 7 at float4 16 + n, so that the 16 lanes of a row write (and the
-  //      summing threads read) 256 contiguous bytes: with the channels in order the head
-  //      rows' writes hit the same banks (four-way conflicts, 1.3 us per wave).
-  __syncthreads();
-  if (pv_active) {
+    // ---- CS phase 4: the waves' (m, l) meet in LDS (s_red rows w and kQKW + w); after one
+    //      barrier every logit wave rescales its partial sums by exp(m_w - M) into its slice
+    //      (the rows are dead then) and 16 threads form the block's (M, sum of exp(m_w - M) l_w)
+    //      in a fixed order; the output stage then adds the slices as in the other path.
+    static_assert(2 * kQKW <= kAttWaves, "s_red holds the waves' maxima and sums");
+    if (qk_wave && g == 0) {
+      s_red[qw][n16] = m;
+      s_red[kQKW + qw][n16] = lsum;
+    }
+    __syncthreads();
+    if (tid < kAttHeads) {
+      float mx = kNegInf;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      float4* o = reinterpret_cast<float4*>(&sO[((size_t)eq * kAttHeads + 4 * g + rr) * kOW + 128 * (CS ? 0 : ct)]);
-      o[n16] = make_float4(acc[0][rr], acc[1][rr], acc[2][rr], acc[3][rr]);
-      o[16 + n16] = make_float4(acc[4][rr], acc[5][rr], acc[6][rr], acc[7][rr]);
+      for (int w2 = 0; w2 < kQKW; ++w2) mx = fmaxf(mx, s_red[w2][tid]);
+      float ls = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < kQKW; ++w2) {
+        const float mw = s_red[w2][tid];
+        ls += (mw == kNegInf) ? 0.0f : __expf(mw - mx) * s_red[kQKW + w2][tid];
+      }
+      s_m[tid] = mx;
+      s_l[tid] = ls;
     }
+    if (qk_wave) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int h = 4 * g + rr;
+        float mx = kNegInf;
+#pragma unroll
+        for (int w2 = 0; w2 < kQKW; ++w2) mx = fmaxf(mx, s_red[w2][h]);
+        const float mw = s_red[qw][h];
+        const float f = (mw == kNegInf) ? 0.0f : __expf(mw - mx);
+        float4* o = reinterpret_cast<float4*>(&sO[((size_t)qw * kAttHeads + h) * kOW]);
+        o[n16] = make_float4(acc[0][rr] * f, acc[1][rr] * f, acc[2][rr] * f, acc[3][rr] * f);
+        o[16 + n16] = make_float4(acc[4][rr] * f, acc[5][rr] * f, acc[6][rr] * f, acc[7][rr] * f);
+      }
+    }
+    __syncthreads();
+  } else {
+  // ---- phase 1b: logits of this wave's kAttTPW tiles of 16 entries.  The channel loop is
+    //      outside the tile loop, so each A operand (16 B of q'' per lane) is read from LDS once
+    //      for all of the wave's tiles.
+    float logit[kAttTPW][4];
+    v4f a[kAttTPW];
+  #pragma unroll
+    for (int t = 0; t < kAttTPW; ++t) a[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+    for (int i = 0; i < (qk_wave ? kCT : 0); ++i) {
+      uint32_t wd[kAttTPW][4];
+      _Float16 gs[kAttTPW][2];
+  #pragma unroll
+      for (int t = 0; t < kAttTPW; ++t) {
+        const int el = (qw * kAttTPW + t) * 16 + n16;  // this lane's entry in the split
+        uint4 kv;
+        if constexpr (G16) kv = kw[t][i];
+        else kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
+        wd[t][0] = kv.x; wd[t][1] = kv.y; wd[t][2] = kv.z; wd[t][3] = kv.w;
+        gs[t][0] = gs[t][1] = (_Float16)1.0f;
+        if (G16) {  // channels 128 i + 32 g + [0, 32): groups 8 i + 2 g and 8 i + 2 g + 1
+          gs[t][0] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g) * L::kSpad + el]);
+          gs[t][1] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g + 1) * L::kSpad + el]);
+        }
+      }
+  #pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const v8h av = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
+  #pragma unroll
+        for (int t = 0; t < kAttTPW; ++t) {
+          v8h bv = decode8_f16(wd[t][sub]);
+          if (G16) bv = bv * gs[t][sub >> 1];
+          a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, a[t], 0, 0, 0);
+        }
+      }
+    }
+  #pragma unroll
+    for (int t = 0; t < kAttTPW; ++t)
+  #pragma unroll
+      for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (qk_wave && jt[t] >= 0) ? a[t][rr] * s_down[4 * g + rr] : kNegInf;
+  
+    // ---- phase 3a: read the PV code words now (staged rows in LDS; G16: global loads, cache
+    //      hits since the rows were just read) so that they arrive during the softmax.  Wave
+    //      (channel tile ct, entry group eq); lane (channel block n16, group g) takes one
+    //      32-bit word (8 channels) of each of the 8 entries el..el+7 of every 32-entry k-step.
+    const int ct = CS ? ctb : wave % kCT, eq = CS ? wave : wave / kCT;
+    const bool pv_active = eq < kWPT;
+    uint32_t pw[kEPW / 32][8];
+  #pragma unroll
+    for (int ks = 0; ks < kEPW / 32; ++ks) {
+      const int el = eq * kEPW + 32 * ks + 8 * g;
+  #pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int e = el + jj;
+        if constexpr (G16) {
+          const int32_t j = sel[e];  // -1 past K (read unconditionally: no branch per load)
+          // p is 0 for skipped entries, so any valid row may stand in for them
+          pw[ks][jj] = *reinterpret_cast<const uint32_t*>(cb + (int64_t)(j >= 0 ? j : 0) * kRowBytes + 64 * ct + 4 * n16);
+        } else {  // word 16 ct + n16 of the staged row
+          pw[ks][jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes +
+                                                           16 * ((4 * ct + (n16 >> 2)) ^ swz(e)) + 4 * (n16 & 3));
+        }
+      }
+    }
+  
+    // ---- phase 2: softmax statistics of the split (heads 4g + rr of this lane).  Per-wave
+    //      partials go to LDS; 256 threads (one 16-lane row per head) reduce them by DPP.
+  #pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float v = logit[0][rr];
+  #pragma unroll
+      for (int t = 1; t < kAttTPW; ++t) v = fmaxf(v, logit[t][rr]);
+      v = row16_max(v);
+      if (n16 == 0) s_red[wave][4 * g + rr] = v;
+    }
+    __syncthreads();
+    static_assert(kAttWaves == 16 && kAttHeads == 16, "one 16-lane row per head reduces the 16 waves");
+    if (tid < 256) {
+      const float v = row16_max(s_red[tid & 15][tid >> 4]);
+      if ((tid & 15) == 0) s_m[tid >> 4] = v;
+    }
+    __syncthreads();
+  #pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int h = 4 * g + rr;
+      const float m = s_m[h];
+      float v = 0.0f;
+  #pragma unroll
+      for (int t = 0; t < (qk_wave ? kAttTPW : 0); ++t) {
+        const float p = (m == kNegInf) ? 0.0f : __expf(logit[t][rr] - m);
+        const _Float16 ph = (_Float16)p;
+        sP[h * L::kPpad + (qw * kAttTPW + t) * 16 + n16] = __builtin_bit_cast(uint16_t, ph);
+        v += p;
+      }
+      v = row16_sum(v);
+      if (n16 == 0) s_red[wave][h] = v;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      const float v = row16_sum(s_red[tid & 15][tid >> 4]);
+      if ((tid & 15) == 0) s_l[tid >> 4] = v;
+    }
+  
+    // ---- phase 3b: o[h][c] = sum_j p[h][j] e[j][c] over this wave's entries and channel
+    //      tile.  For each pair of entries the two code words are nibble-interleaved so that
+    //      one byte holds the same channel of both entries; one fp4->fp16 pair conversion
+    //      then yields the (entry 2p, entry 2p+1) dword the MFMA k-order wants.
+    v4f acc[8];
+  #pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
+    if (pv_active) {
+  #pragma unroll
+      for (int ks = 0; ks < kEPW / 32; ++ks) {
+        const int el = eq * kEPW + 32 * ks + 8 * g;  // first of this lane's 8 entries
+        const v8h pa = *reinterpret_cast<const v8h*>(&sP[n16 * L::kPpad + el]);
+        // G16: the scales of entries el..el+7 in this lane's group (channels 128 ct + 8 n16 ..)
+        v8h sc = {};
+        if (G16) sc = *reinterpret_cast<const v8h*>(&sS[(8 * ct + (n16 >> 1)) * L::kSpad + el]);
+        uint32_t xe[4], xo[4];
+  #pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+          const uint32_t w0 = pw[ks][2 * p2], w1 = pw[ks][2 * p2 + 1];
+          xe[p2] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);  // channels 0,2,4,6
+          xo[p2] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);  // channels 1,3,5,7
+        }
+  #define CSA2_PV_MFMA(M, X, BS)                                                                                  \
+    {                                                                                                          \
+      const uint4 bw = make_uint4(cvt_pair_f16<BS>(X[0]), cvt_pair_f16<BS>(X[1]), cvt_pair_f16<BS>(X[2]),      \
+                                  cvt_pair_f16<BS>(X[3]));                                                     \
+      v8h bv = __builtin_bit_cast(v8h, bw);                                                                    \
+      if (G16) bv = bv * sc;                                                                                   \
+      acc[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, acc[M], 0, 0, 0);                                \
+    }
+        CSA2_PV_MFMA(0, xe, 0) CSA2_PV_MFMA(1, xo, 0) CSA2_PV_MFMA(2, xe, 1) CSA2_PV_MFMA(3, xo, 1)
+        CSA2_PV_MFMA(4, xe, 2) CSA2_PV_MFMA(5, xo, 2) CSA2_PV_MFMA(6, xe, 3) CSA2_PV_MFMA(7, xo, 3)
+  #undef CSA2_PV_MFMA
+      }
+    }
+  
+    // ---- phase 4: every entry group writes its partial sums to its own LDS slice (sA and
+    //      sP are dead once all waves are past PV); then each thread sums the kWPT slices of
+    //      8 channels of one head in a fixed order (deterministic), normalises and stores.
+    //      Within a head's 128-channel tile, channels 8 n .. 8 n + 3 sit at float4 n and
+    //      8 n + 4 .. 8 n + 7 at float4 16 + n, so that the 16 lanes of a row write (and the
+    //      summing threads read) 256 contiguous bytes: with the channels in order the head
+    //      rows' writes hit the same banks (four-way conflicts, 1.3 us per wave).
+    __syncthreads();
+    if (pv_active) {
+  #pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float4* o = reinterpret_cast<float4*>(&sO[((size_t)eq * kAttHeads + 4 * g + rr) * kOW + 128 * (CS ? 0 : ct)]);
+        o[n16] = make_float4(acc[0][rr], acc[1][rr], acc[2][rr], acc[3][rr]);
+        o[16 + n16] = make_float4(acc[4][rr], acc[5][rr], acc[6][rr], acc[7][rr]);
+      }
+    }
+    __syncthreads();
+    // items of 4 channels: 128 c0 + 8 n + 4 hf + [0, 4) of head hl sit at float4 16 hf + n of the
+    // head's tile in every slice
   }
-  __syncthreads();
-  // items of 4 channels: 128 c0 + 8 n + 4 hf + [0, 4) of head hl sit at float4 16 hf + n of the
-  // head's tile in every slice
   constexpr int kOItems = kAttHeads * kOW / 4;
   for (int i = tid; i < kOItems; i += kAttThreads) {
     const int hl = i / (kOW / 4), ci = i % (kOW / 4);
