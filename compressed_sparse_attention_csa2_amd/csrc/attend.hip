@@ -36,6 +36,7 @@ constexpr int kAttHeads = 16;      // heads per block (MFMA M)
 constexpr int kAttWaves = 16;      // four waves per SIMD
 constexpr int kAttThreads = 64 * kAttWaves;
 constexpr int kAttSplit = 512;     // entries per block: the pages' Top-512 in one block, no merge
+constexpr int kCSBlocks = 4;       // channel split: blocks per (row, split, head group), at most D / 128
 
 // partials: part_o [R][P][Hq][D] normalised outputs, part_ml [R][P][Hq][2] (max, sum); P
 // = the splits of the selected entries, plus one slot for the sliding window
@@ -374,7 +375,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   // group) but PV and the output only for channel tile `cb`; the kCT blocks of a head group
   // repeat QK and each takes one tile, so the chip runs kCT times as many blocks with a
   // quarter of the PV each (D = 512) and no merge
-  constexpr int kPVT = CS ? 1 : kCT;           // channel tiles per block in PV
+  constexpr int kNCB = CS ? (kCT < kCSBlocks ? kCT : kCSBlocks) : 1;  // channel blocks per head group
+  constexpr int kPVT = kCT / kNCB;             // channel tiles per block in PV
   constexpr int kOW = 128 * kPVT;              // channels per head row of the partial sums
   // waves per tile in PV (CS: each logit wave takes PV over its own entries)
   constexpr int kWPT = CS ? kQKW : ((kAttWaves / kPVT < kAttSplit / 32) ? kAttWaves / kPVT : kAttSplit / 32);
@@ -409,10 +411,9 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   // gather the same rows through one L2.  Units past the last (grid rounded up) exit.
   const int X = S + (wcodes ? 1 : 0);            // splits, plus the window's block
   const int G = Hq / kAttHeads;                  // head groups
-  constexpr int kNCB = CS ? kCT : 1;             // channel blocks per head group
   const int wg = blockIdx.x, slot = wg >> 3;
   const int unit = (slot / (G * kNCB)) * 8 + (wg & 7), hg = (slot % (G * kNCB)) / kNCB;
-  const int ctb = CS ? slot % kNCB : 0;        // CS: this block's channel tile
+  const int ctb = CS ? slot % kNCB : 0;        // CS: this block's channel tiles ctb kPVT + [0, kPVT)
   if (unit >= X * R) return;
   const int split = unit % X, r = unit / X;
   if (split == S) {  // the sliding window's block (grid.x = S + 1 with a window)
@@ -622,28 +623,33 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
       }
     lsum += __shfl_xor(lsum, 16);  // the four lanes of a head add the same pairs: equal sums
     lsum += __shfl_xor(lsum, 32);
-    // ---- CS phase 3: PV over this wave's entries for channel tile ctb.  K step ks takes the
+    // ---- CS phase 3: PV over this wave's entries for the block's channel tiles.  K step ks takes the
     //      wave's tiles 2 ks and 2 ks + 1; its K slot 8 g + j is entry 16 t0' + 4 g + j (j < 4)
     //      or 16 t1' + 4 g + j - 4 (j >= 4), which is where lane (head, g) holds p already;
-    //      lane (channel block n16, g) reads word 16 ctb + n16 (8 channels) of those 8 entries
+    //      lane (channel block n16, g) reads word 16 ct + n16 (8 channels) of those 8 entries
     //      and nibble-interleaves pairs of them as in the other path.
-    v4f acc[8];
+    v4f acc[kPVT][8];
 #pragma unroll
-    for (int mm = 0; mm < 8; ++mm) acc[mm] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int ci = 0; ci < kPVT; ++ci)
+#pragma unroll
+      for (int mm = 0; mm < 8; ++mm) acc[ci][mm] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < (qk_wave ? kAttTPW / 2 : 0); ++ks) {
-      uint32_t pw[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int e = (qw * kAttTPW + 2 * ks + (jj >> 2)) * 16 + 4 * g + (jj & 3);
-        pw[jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes + 16 * ((4 * ctb + (n16 >> 2)) ^ swz(e)) +
-                                                    4 * (n16 & 3));
-      }
       v8h pa;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         pa[rr] = (_Float16)pr[2 * ks][rr];
         pa[4 + rr] = (_Float16)pr[2 * ks + 1][rr];
+      }
+#pragma unroll
+      for (int ci = 0; ci < kPVT; ++ci) {
+      const int ct = ctb * kPVT + ci;
+      uint32_t pw[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int e = (qw * kAttTPW + 2 * ks + (jj >> 2)) * 16 + 4 * g + (jj & 3);
+        pw[jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes + 16 * ((4 * ct + (n16 >> 2)) ^ swz(e)) +
+                                                    4 * (n16 & 3));
       }
       uint32_t xe[4], xo[4];
 #pragma unroll
@@ -656,11 +662,12 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   {                                                                                                          \
     const uint4 bw = make_uint4(cvt_pair_f16<BS>(X[0]), cvt_pair_f16<BS>(X[1]), cvt_pair_f16<BS>(X[2]),      \
                                 cvt_pair_f16<BS>(X[3]));                                                     \
-    acc[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(v8h, bw), acc[M], 0, 0, 0);        \
+    acc[ci][M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(v8h, bw), acc[ci][M], 0, 0, 0);  \
   }
       CSA2_CS_MFMA(0, xe, 0) CSA2_CS_MFMA(1, xo, 0) CSA2_CS_MFMA(2, xe, 1) CSA2_CS_MFMA(3, xo, 1)
       CSA2_CS_MFMA(4, xe, 2) CSA2_CS_MFMA(5, xo, 2) CSA2_CS_MFMA(6, xe, 3) CSA2_CS_MFMA(7, xo, 3)
 #undef CSA2_CS_MFMA
+      }
     }
     // ---- CS phase 4: the waves' (m, l) meet in LDS (s_red rows w and kQKW + w); after one
     //      barrier every logit wave rescales its partial sums by exp(m_w - M) into its slice
@@ -694,9 +701,12 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
         for (int w2 = 0; w2 < kQKW; ++w2) mx = fmaxf(mx, s_red[w2][h]);
         const float mw = s_red[qw][h];
         const float f = (mw == kNegInf) ? 0.0f : __expf(mw - mx);
-        float4* o = reinterpret_cast<float4*>(&sO[((size_t)qw * kAttHeads + h) * kOW]);
-        o[n16] = make_float4(acc[0][rr] * f, acc[1][rr] * f, acc[2][rr] * f, acc[3][rr] * f);
-        o[16 + n16] = make_float4(acc[4][rr] * f, acc[5][rr] * f, acc[6][rr] * f, acc[7][rr] * f);
+#pragma unroll
+        for (int ci = 0; ci < kPVT; ++ci) {
+          float4* o = reinterpret_cast<float4*>(&sO[((size_t)qw * kAttHeads + h) * kOW + 128 * ci]);
+          o[n16] = make_float4(acc[ci][0][rr] * f, acc[ci][1][rr] * f, acc[ci][2][rr] * f, acc[ci][3][rr] * f);
+          o[16 + n16] = make_float4(acc[ci][4][rr] * f, acc[ci][5][rr] * f, acc[ci][6][rr] * f, acc[ci][7][rr] * f);
+        }
       }
     }
     __syncthreads();
@@ -863,7 +873,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   for (int i = tid; i < kOItems; i += kAttThreads) {
     const int hl = i / (kOW / 4), ci = i % (kOW / 4);
     const int tile = ci >> 5, n = ci & 15, hf = (ci >> 4) & 1;
-    const int c = 128 * (CS ? ctb : tile) + 8 * n + 4 * hf;
+    const int c = 128 * (ctb * kPVT + tile) + 8 * n + 4 * hf;
     float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int gq = 0; gq < kWPT; ++gq) {
@@ -1087,7 +1097,7 @@ static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
   // one block per (unit = (row, split or window), head group[, channel tile]), dealt in
   // XCD-aware order
   const int units = (S + (a.swa_codes ? 1 : 0)) * a.B * a.T;
-  const int ncb = CS ? D / 128 : 1;
+  const int ncb = CS ? (D / 128 < kCSBlocks ? D / 128 : kCSBlocks) : 1;
   const dim3 g((unsigned)(8 * (a.Hq / kAttHeads) * ncb * ((units + 7) / 8)));
   float* part_ml = a.part ? a.part + (size_t)a.B * a.T * P * a.Hq * D : nullptr;
   hipLaunchKernelGGL((k_attend_part<D, G16, CS>), g, dim3(kAttThreads), 0, st, a.B * a.T, a.T, a.Hq, a.K, S, P,
