@@ -41,16 +41,16 @@ constexpr int kCSBlocks = 4;       // channel split: blocks per (row, split, hea
 // partials: part_o [R][P][Hq][D] normalised outputs, part_ml [R][P][Hq][2] (max, sum); P
 // = the splits of the selected entries, plus one slot for the sliding window
 
-// Two E4M3 codes (bytes 0 and 1 of w) -> two fp16 values (exact), low byte in the low half.
-// Placing the code's exponent and mantissa bits at the top of an fp16 gives the value times
-// 2^-8 (the exponent biases are 7 and 15), subnormal codes included; one packed multiply
-// by 256 restores it.
+// Two E4M3 codes (bytes 0 and 1 of w) -> two fp16 values (exact), low byte in the low half:
+// gfx950's scaled conversion with scale 1.  Every E4M3 value, subnormals included, is an
+// fp16 value; for all 65536 code pairs the result equals placing the code's exponent and
+// mantissa bits at the top of an fp16 (the value times 2^-8: the biases are 7 and 15) and
+// multiplying by 256, NaN payloads aside.  The _hi form converts bytes 2 and 3.
 __device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
-  const uint32_t sp = (w & 0xFFu) | ((w & 0xFF00u) << 8);
-  const uint32_t bits = ((sp & 0x007F007Fu) << 7) | ((sp & 0x00800080u) << 8);
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const h2 v = __builtin_bit_cast(h2, bits) * (h2){(_Float16)256.0f, (_Float16)256.0f};
-  return __builtin_bit_cast(uint32_t, v);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t e4m3x2_hi_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xFFFFu) | (hi16 << 16); }
@@ -357,7 +357,7 @@ struct AttLds {
 // The scale no longer factors out of the contractions; instead the split's scales are
 // staged in LDS as fp16, [group][entry], and multiply the fp16 key / value operands after
 // the E2M1 conversion (E2M1 * E4M3 is exact in fp16, so the operands stay exact).
-template <int D, bool G16, bool CS>
+template <int D, bool G16, bool CS, bool WIN>
 __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     int R, int T, int Hq, int K, int S, int P, const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const void* __restrict__ scales_v, int64_t n_max, const int32_t* __restrict__ idx, float softmax_scale, void* __restrict__ out, int out_bf16, float* __restrict__ lse,
@@ -379,7 +379,12 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   constexpr int kPVT = kCT / kNCB;             // channel tiles per block in PV
   constexpr int kOW = 128 * kPVT;              // channels per head row of the partial sums
   // waves per tile in PV (CS: each logit wave takes PV over its own entries)
-  constexpr int kWPT = CS ? kQKW : ((kAttWaves / kPVT < kAttSplit / 32) ? kAttWaves / kPVT : kAttSplit / 32);
+  // CS with a sliding window (WIN): kCSWinW more waves attend the window's rows (32 each) in
+  // the same softmax
+  constexpr int kCSWinW = kWinMax / 32;
+  static_assert(!CS || kQKW + kCSWinW <= kAttWaves, "window waves past the logit waves");
+  constexpr int kWPT = CS ? kQKW + (WIN ? kCSWinW : 0)
+                          : ((kAttWaves / kPVT < kAttSplit / 32) ? kAttWaves / kPVT : kAttSplit / 32);
   // per-channel layout: the split's rows are gathered whole (a wave instruction reads
   // kRPI complete rows, 16 bytes per lane) and staged in LDS; chunk c of entry e sits in
   // chunk slot c ^ swz(e), so that the 16 entries of an MFMA operand read spread over
@@ -395,9 +400,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   constexpr int kNG = D / 16;                  // scale groups per entry (G16)
   __shared__ float s_scale[G16 ? 1 : D];
   __shared__ __align__(16) int32_t s_idx[kAttSplit];
-  __shared__ float s_red[kAttWaves][kAttHeads];
+  __shared__ float s_red[2 * kAttWaves][kAttHeads];
   __shared__ float s_m[kAttHeads], s_l[kAttHeads];
   __shared__ float s_down[kAttHeads];          // per head: softmax scale / the query prescale
+  __shared__ float s_wmax[WIN ? kAttHeads : 1];  // WIN: per head, the largest |q| (no channel scales)
   __shared__ __align__(16) unsigned char s_u[L::kUnion];
   uint16_t* sA = reinterpret_cast<uint16_t*>(s_u + L::kOffA);
   uint16_t* sP = reinterpret_cast<uint16_t*>(s_u + L::kOffP);
@@ -409,14 +415,14 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   // XCD-aware order: workgroups are dealt to the 8 XCDs in turn (L2 per XCD), so a unit
   // (row, split) takes workgroups wg with the same wg % 8 for all its head groups, which then
   // gather the same rows through one L2.  Units past the last (grid rounded up) exit.
-  const int X = S + (wcodes ? 1 : 0);            // splits, plus the window's block
+  const int X = S + ((wcodes && !CS) ? 1 : 0);   // splits, plus the window's block (not CS)
   const int G = Hq / kAttHeads;                  // head groups
   const int wg = blockIdx.x, slot = wg >> 3;
   const int unit = (slot / (G * kNCB)) * 8 + (wg & 7), hg = (slot % (G * kNCB)) / kNCB;
   const int ctb = CS ? slot % kNCB : 0;        // CS: this block's channel tiles ctb kPVT + [0, kPVT)
   if (unit >= X * R) return;
   const int split = unit % X, r = unit / X;
-  if (split == S) {  // the sliding window's block (grid.x = S + 1 with a window)
+  if (!CS && split == S) {  // the sliding window's block (grid.x = S + 1 with a window)
     attend_window_block<D>(hg, r, T, Hq, q, wcodes, wscales, wn_max, wend, window, softmax_scale, P, S, part, part_ml,
                            s_u);
     return;
@@ -504,12 +510,14 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   const bool q_act = tid < kQItems;
   const int qh = tid / kLPH, qc = (tid % kLPH) * 8;
   float qv[8];
-  float qmax = 0.0f;
+  float qmax = 0.0f, qrmax = 0.0f;  // qrmax (WIN): without the channel scales
   {
     const uint32_t wds[4] = {qraw[0].x, qraw[0].y, qraw[0].z, qraw[0].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      qv[e] = bf16_to_f32((uint16_t)(wds[e >> 1] >> (16 * (e & 1)))) * (G16 || !q_act ? 1.0f : s_scale[qc + e]);
+      const float qe = bf16_to_f32((uint16_t)(wds[e >> 1] >> (16 * (e & 1))));
+      qrmax = fmaxf(qrmax, fabsf(qe));
+      qv[e] = qe * (G16 || !q_act ? 1.0f : s_scale[qc + e]);
       qmax = fmaxf(qmax, fabsf(qv[e]));
     }
   }
@@ -533,12 +541,53 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
                                        (__attribute__((address_space(3))) void*)(s_rows + r0 * kRowBytes), 16, 0, 0);
     }
   }
+  // WIN: the window waves' row scales and PV bytes (lane (channel block n16, g): channels
+  // 128 ctb + 8 n16 + [0, 8) of the entries in its K slots, see the window waves below),
+  // loaded now so that they arrive with the gathered rows
+  int wnw = 0;
+  const uint8_t* wbp = wcodes;
+  float wsq[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  uint2 wvw[8];
+  if constexpr (WIN) {
+    if (wave >= kQKW && wave < kQKW + kCSWinW) {  // wave-uniform
+      int64_t w_end = wend[r];
+      if (w_end > wn_max) w_end = wn_max;
+      const int64_t w_start = w_end - window > 0 ? w_end - window : 0;
+      wnw = (split == 0 && w_end > w_start) ? (int)(w_end - w_start) : 0;
+      if (wnw > 0) {
+        const int ww = wave - kQKW;
+        wbp = wcodes + ((int64_t)b * wn_max + w_start) * D;
+        const float* wsb = wscales + (int64_t)b * wn_max + w_start;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int e = 32 * ww + 16 * t + 4 * g + rr;
+            const float v = wsb[e < wnw ? e : 0];  // (unconditional loads from a valid row)
+            wsq[t][rr] = e < wnw ? v : 0.0f;
+          }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int e = 32 * ww + 16 * (j >> 2) + 4 * g + (j & 3);
+          const uint2 v = *reinterpret_cast<const uint2*>(wbp + (int64_t)(e < wnw ? e : 0) * D + 128 * ctb + 8 * n16);
+          wvw[j] = e < wnw ? v : make_uint2(0u, 0u);
+        }
+      }
+    }
+  }
   {  // the head's maximum over its kLPH lanes (16-lane rows, then rows of one head)
     float hm = row16_max(qmax);
     const float m0 = lane_read(hm, 0), m1 = lane_read(hm, 16), m2 = lane_read(hm, 32), m3 = lane_read(hm, 48);
     if (kLPH == 64) hm = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
     else if (kLPH == 32) hm = (lane < 32) ? fmaxf(m0, m1) : fmaxf(m2, m3);
     qmax = hm;
+    if constexpr (WIN) {
+      float hr = row16_max(qrmax);
+      const float r0 = lane_read(hr, 0), r1 = lane_read(hr, 16), r2 = lane_read(hr, 32), r3 = lane_read(hr, 48);
+      if (kLPH == 64) hr = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+      else if (kLPH == 32) hr = (lane < 32) ? fmaxf(r0, r1) : fmaxf(r2, r3);
+      if (q_act && qc == 0) s_wmax[qh] = hr;
+    }
   }
   int qexp = 0;
   if (qmax > 0.0f) qexp = (int)((__float_as_uint(qmax) >> 23) & 255u) - 126;
@@ -572,140 +621,268 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   __syncthreads();
 
   if constexpr (CS) {
-    // ---- CS phase 1: the logits transposed (rows x q''^T, the row chunk as the MFMA's A
-    //      operand and q'' as B): lane (head n16, g) holds head n16's logits of the entries
-    //      16 t' + 4 g + rr (t' = qw kAttTPW + t) of this wave's tiles
-    v4f a[kAttTPW];
-#pragma unroll
-    for (int t = 0; t < kAttTPW; ++t) a[t] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < (qk_wave ? kCT : 0); ++i) {
-      uint32_t wd[kAttTPW][4];
-#pragma unroll
-      for (int t = 0; t < kAttTPW; ++t) {
-        const int el = (qw * kAttTPW + t) * 16 + n16;
-        const uint4 kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
-        wd[t][0] = kv.x; wd[t][1] = kv.y; wd[t][2] = kv.z; wd[t][3] = kv.w;
-      }
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        const v8h qv8 = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
-#pragma unroll
-        for (int t = 0; t < kAttTPW; ++t)
-          a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode8_f16(wd[t][sub]), qv8, a[t], 0, 0, 0);
-      }
-    }
-    // ---- CS phase 2: this wave's softmax statistics per head (no block barrier): the
-    //      maximum and the sum over the lane's 4 kAttTPW logits, then over the 4 lanes of the
-    //      head (g); p = exp(logit - m) stays in registers as PV's A operand
-    const float dn = s_down[n16];
-    float pr[kAttTPW][4];
-    float m = kNegInf;
-#pragma unroll
-    for (int t = 0; t < kAttTPW; ++t) {
-      const int4 sv = *reinterpret_cast<const int4*>(&s_idx[(qw * kAttTPW + t) * 16 + 4 * g]);
-      const int32_t svv[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        pr[t][rr] = (qk_wave && svv[rr] >= 0) ? a[t][rr] * dn : kNegInf;
-        m = fmaxf(m, pr[t][rr]);
-      }
-    }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    float lsum = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kAttTPW; ++t)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        pr[t][rr] = (m == kNegInf) ? 0.0f : __expf(pr[t][rr] - m);
-        lsum += pr[t][rr];
-      }
-    lsum += __shfl_xor(lsum, 16);  // the four lanes of a head add the same pairs: equal sums
-    lsum += __shfl_xor(lsum, 32);
-    // ---- CS phase 3: PV over this wave's entries for the block's channel tiles.  K step ks takes the
-    //      wave's tiles 2 ks and 2 ks + 1; its K slot 8 g + j is entry 16 t0' + 4 g + j (j < 4)
-    //      or 16 t1' + 4 g + j - 4 (j >= 4), which is where lane (head, g) holds p already;
-    //      lane (channel block n16, g) reads word 16 ct + n16 (8 channels) of those 8 entries
-    //      and nibble-interleaves pairs of them as in the other path.
+    float m = kNegInf, lsum = 0.0f;
+    float xdown = 1.0f;  // window waves: the power of two taken out of p, put back at the rescale
     v4f acc[kPVT][8];
+    const bool win_wave = WIN && wave >= kQKW && wave < kQKW + kCSWinW;  // wave-uniform
+    // ---- CS window waves (WIN, split 0): the row's sliding window, rows [max(0, end -
+    //      window), end) of the layer's E4M3 cache with one fp32 scale per row, 32 entries per
+    //      wave (kWinMax / 32 waves past the logit waves, idle until now).  The logits need the
+    //      query without the main cache's channel scales: each lane loads its B operand (head
+    //      n16, channels 128 ct + 32 g + 8 sub + [0, 8)) straight from global memory and takes
+    //      the head's own power of two.  The row scale multiplies the logit and, with the
+    //      wave's largest row scale 2^sx taken out (undone at the rescale), p in PV.
+    if (win_wave) {
+      if constexpr (WIN) {
+        static_assert(kPVT == 1, "the window's PV takes one channel tile");
 #pragma unroll
-    for (int ci = 0; ci < kPVT; ++ci)
+        for (int mm = 0; mm < 8; ++mm) acc[0][mm] = (v4f){0.f, 0.f, 0.f, 0.f};
+        const int ww = wave - kQKW;
+        const int nw = wnw;
+        if (nw > 0) {  // (an empty window leaves m = -inf, l = 0 and zero sums)
+        const uint8_t* wb = wbp;
+        const uint16_t* qrow = q + ((int64_t)r * Hq + hg * kAttHeads + n16) * D + 32 * g;
+        const float (&sqv)[2][4] = wsq;  // row scales of this lane's logit entries 32 ww + 16 t + 4 g + rr
+        const float qm = s_wmax[n16];    // the head's largest |q|
+        int wexp = 0;
+        if (qm > 0.0f) wexp = (int)((__float_as_uint(qm) >> 23) & 255u) - 126;
+        wexp = wexp < -100 ? -100 : wexp;
+        const float wup = __uint_as_float((uint32_t)(127 + 15 - wexp) << 23);
+        const float wdn = softmax_scale * __uint_as_float((uint32_t)(127 - 15 + wexp) << 23);
+        v4f a2[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 2
+        for (int i = 0; i < kCT; ++i) {  // (two tiles in flight: the loads of all four spill)
+          v8h qh8[4];  // B operand: the tile's query in fp16 with the head's power of two
 #pragma unroll
-      for (int mm = 0; mm < 8; ++mm) acc[ci][mm] = (v4f){0.f, 0.f, 0.f, 0.f};
+          for (int sub = 0; sub < 4; ++sub) {
+            const uint4 qv4 = *reinterpret_cast<const uint4*>(qrow + 128 * i + 8 * sub);
+            const uint32_t wds[4] = {qv4.x, qv4.y, qv4.z, qv4.w};
 #pragma unroll
-    for (int ks = 0; ks < (qk_wave ? kAttTPW / 2 : 0); ++ks) {
-      v8h pa;
+            for (int e = 0; e < 8; ++e) qh8[sub][e] = (_Float16)(bf16_to_f32((uint16_t)(wds[e >> 1] >> (16 * (e & 1)))) * wup);
+          }
+          uint4 kr[2][2];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        pa[rr] = (_Float16)pr[2 * ks][rr];
-        pa[4 + rr] = (_Float16)pr[2 * ks + 1][rr];
+          for (int t = 0; t < 2; ++t) {
+            const int e = 32 * ww + 16 * t + n16;
+            const uint8_t* src = wb + (int64_t)(e < nw ? e : 0) * D + 128 * i + 32 * g;
+            kr[t][0] = *reinterpret_cast<const uint4*>(src);
+            kr[t][1] = *reinterpret_cast<const uint4*>(src + 16);
+          }
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const uint4 hw = kr[t][sub >> 1];
+              const uint32_t w0 = (sub & 1) ? hw.z : hw.x, w1 = (sub & 1) ? hw.w : hw.y;
+              const uint4 bw = make_uint4(e4m3x2_f16(w0), e4m3x2_hi_to_f16x2(w0), e4m3x2_f16(w1), e4m3x2_hi_to_f16x2(w1));
+              a2[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, bw), qh8[sub], a2[t], 0, 0, 0);
+            }
+        }
+        float p2v[2][4];
+        float wm = kNegInf, smx = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int e = 32 * ww + 16 * t + 4 * g + rr;
+            p2v[t][rr] = e < nw ? a2[t][rr] * wdn * sqv[t][rr] : kNegInf;
+            wm = fmaxf(wm, p2v[t][rr]);
+            smx = fmaxf(smx, sqv[t][rr]);
+          }
+        wm = fmaxf(wm, __shfl_xor(wm, 16));
+        wm = fmaxf(wm, __shfl_xor(wm, 32));
+        smx = fmaxf(smx, __shfl_xor(smx, 16));
+        smx = fmaxf(smx, __shfl_xor(smx, 32));
+        float wl = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            p2v[t][rr] = (wm == kNegInf) ? 0.0f : __expf(p2v[t][rr] - wm);
+            wl += p2v[t][rr];
+          }
+        wl += __shfl_xor(wl, 16);
+        wl += __shfl_xor(wl, 32);
+        // 2^sx with smx 2^-sx in [1, 2): p s 2^-sx <= 2
+        const int sx = smx > 0.0f ? (int)((__float_as_uint(smx) >> 23) & 255u) - 127 : 0;
+        const float sdn = __uint_as_float((uint32_t)(127 - sx) << 23);
+        xdown = __uint_as_float((uint32_t)(127 + sx) << 23);
+        v8h pa;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          pa[rr] = (_Float16)(p2v[0][rr] * sqv[0][rr] * sdn);
+          pa[4 + rr] = (_Float16)(p2v[1][rr] * sqv[1][rr] * sdn);
+        }
+        // PV: lane (channel block n16, g) takes channels 128 ctb + 8 n16 + [0, 8) (8 bytes) of
+        // the entries in K slots 8 g + j (entry 32 ww + 16 (j >> 2) + 4 g + (j & 3)); pairs of
+        // entries are byte-transposed so that one word holds (e0[c], e1[c], e0[c + 1], e1[c + 1])
+        const uint2 (&vw)[8] = wvw;
+#pragma unroll
+        for (int hw = 0; hw < 2; ++hw)
+#pragma unroll
+          for (int mm = 0; mm < 4; mm += 2) {
+            uint32_t bx[4], by[4];
+#pragma unroll
+            for (int p2 = 0; p2 < 4; ++p2) {
+              const uint32_t lo = hw ? vw[2 * p2].y : vw[2 * p2].x, hi = hw ? vw[2 * p2 + 1].y : vw[2 * p2 + 1].x;
+              const uint32_t tw = __builtin_amdgcn_perm(hi, lo, (uint32_t)mm | (uint32_t)(mm + 4) << 8 |
+                                                                    (uint32_t)(mm + 1) << 16 | (uint32_t)(mm + 5) << 24);
+              bx[p2] = e4m3x2_f16(tw);           // channel 4 hw + mm
+              by[p2] = e4m3x2_hi_to_f16x2(tw);   // channel 4 hw + mm + 1
+            }
+            acc[0][4 * hw + mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                pa, __builtin_bit_cast(v8h, make_uint4(bx[0], bx[1], bx[2], bx[3])), acc[0][4 * hw + mm], 0, 0, 0);
+            acc[0][4 * hw + mm + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                pa, __builtin_bit_cast(v8h, make_uint4(by[0], by[1], by[2], by[3])), acc[0][4 * hw + mm + 1], 0, 0, 0);
+          }
+        m = wm;
+        lsum = wl;
+        }
       }
-#pragma unroll
-      for (int ci = 0; ci < kPVT; ++ci) {
-      const int ct = ctb * kPVT + ci;
-      uint32_t pw[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int e = (qw * kAttTPW + 2 * ks + (jj >> 2)) * 16 + 4 * g + (jj & 3);
-        pw[jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes + 16 * ((4 * ct + (n16 >> 2)) ^ swz(e)) +
-                                                    4 * (n16 & 3));
+    } else {
+      // ---- CS phase 1: the logits transposed (rows x q''^T, the row chunk as the MFMA's A
+      //      operand and q'' as B): lane (head n16, g) holds head n16's logits of the entries
+      //      16 t' + 4 g + rr (t' = qw kAttTPW + t) of this wave's tiles
+      v4f a[kAttTPW];
+  #pragma unroll
+      for (int t = 0; t < kAttTPW; ++t) a[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int i = 0; i < (qk_wave ? kCT : 0); ++i) {
+        uint32_t wd[kAttTPW][4];
+  #pragma unroll
+        for (int t = 0; t < kAttTPW; ++t) {
+          const int el = (qw * kAttTPW + t) * 16 + n16;
+          const uint4 kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
+          wd[t][0] = kv.x; wd[t][1] = kv.y; wd[t][2] = kv.z; wd[t][3] = kv.w;
+        }
+  #pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+          const v8h qv8 = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
+  #pragma unroll
+          for (int t = 0; t < kAttTPW; ++t)
+            a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode8_f16(wd[t][sub]), qv8, a[t], 0, 0, 0);
+        }
       }
-      uint32_t xe[4], xo[4];
-#pragma unroll
-      for (int p2 = 0; p2 < 4; ++p2) {
-        const uint32_t w0 = pw[2 * p2], w1 = pw[2 * p2 + 1];
-        xe[p2] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);  // channels 0,2,4,6
-        xo[p2] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);  // channels 1,3,5,7
+      // ---- CS phase 2: this wave's softmax statistics per head (no block barrier): the
+      //      maximum and the sum over the lane's 4 kAttTPW logits, then over the 4 lanes of the
+      //      head (g); p = exp(logit - m) stays in registers as PV's A operand
+      const float dn = s_down[n16];
+      float pr[kAttTPW][4];
+      m = kNegInf;
+  #pragma unroll
+      for (int t = 0; t < kAttTPW; ++t) {
+        const int4 sv = *reinterpret_cast<const int4*>(&s_idx[(qw * kAttTPW + t) * 16 + 4 * g]);
+        const int32_t svv[4] = {sv.x, sv.y, sv.z, sv.w};
+  #pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          pr[t][rr] = (qk_wave && svv[rr] >= 0) ? a[t][rr] * dn : kNegInf;
+          m = fmaxf(m, pr[t][rr]);
+        }
       }
-#define CSA2_CS_MFMA(M, X, BS)                                                                                 \
-  {                                                                                                          \
-    const uint4 bw = make_uint4(cvt_pair_f16<BS>(X[0]), cvt_pair_f16<BS>(X[1]), cvt_pair_f16<BS>(X[2]),      \
-                                cvt_pair_f16<BS>(X[3]));                                                     \
-    acc[ci][M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(v8h, bw), acc[ci][M], 0, 0, 0);  \
-  }
-      CSA2_CS_MFMA(0, xe, 0) CSA2_CS_MFMA(1, xo, 0) CSA2_CS_MFMA(2, xe, 1) CSA2_CS_MFMA(3, xo, 1)
-      CSA2_CS_MFMA(4, xe, 2) CSA2_CS_MFMA(5, xo, 2) CSA2_CS_MFMA(6, xe, 3) CSA2_CS_MFMA(7, xo, 3)
-#undef CSA2_CS_MFMA
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      lsum = 0.0f;
+  #pragma unroll
+      for (int t = 0; t < kAttTPW; ++t)
+  #pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          pr[t][rr] = (m == kNegInf) ? 0.0f : __expf(pr[t][rr] - m);
+          lsum += pr[t][rr];
+        }
+      lsum += __shfl_xor(lsum, 16);  // the four lanes of a head add the same pairs: equal sums
+      lsum += __shfl_xor(lsum, 32);
+      // ---- CS phase 3: PV over this wave's entries for the block's channel tiles.  K step ks takes the
+      //      wave's tiles 2 ks and 2 ks + 1; its K slot 8 g + j is entry 16 t0' + 4 g + j (j < 4)
+      //      or 16 t1' + 4 g + j - 4 (j >= 4), which is where lane (head, g) holds p already;
+      //      lane (channel block n16, g) reads word 16 ct + n16 (8 channels) of those 8 entries
+      //      and nibble-interleaves pairs of them as in the other path.
+  #pragma unroll
+      for (int ci = 0; ci < kPVT; ++ci)
+  #pragma unroll
+        for (int mm = 0; mm < 8; ++mm) acc[ci][mm] = (v4f){0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int ks = 0; ks < (qk_wave ? kAttTPW / 2 : 0); ++ks) {
+        v8h pa;
+  #pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          pa[rr] = (_Float16)pr[2 * ks][rr];
+          pa[4 + rr] = (_Float16)pr[2 * ks + 1][rr];
+        }
+  #pragma unroll
+        for (int ci = 0; ci < kPVT; ++ci) {
+        const int ct = ctb * kPVT + ci;
+        uint32_t pw[8];
+  #pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int e = (qw * kAttTPW + 2 * ks + (jj >> 2)) * 16 + 4 * g + (jj & 3);
+          pw[jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes + 16 * ((4 * ct + (n16 >> 2)) ^ swz(e)) +
+                                                      4 * (n16 & 3));
+        }
+        uint32_t xe[4], xo[4];
+  #pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+          const uint32_t w0 = pw[2 * p2], w1 = pw[2 * p2 + 1];
+          xe[p2] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);  // channels 0,2,4,6
+          xo[p2] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);  // channels 1,3,5,7
+        }
+  #define CSA2_CS_MFMA(M, X, BS)                                                                                 \
+    {                                                                                                          \
+      const uint4 bw = make_uint4(cvt_pair_f16<BS>(X[0]), cvt_pair_f16<BS>(X[1]), cvt_pair_f16<BS>(X[2]),      \
+                                  cvt_pair_f16<BS>(X[3]));                                                     \
+      acc[ci][M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(v8h, bw), acc[ci][M], 0, 0, 0);  \
+    }
+        CSA2_CS_MFMA(0, xe, 0) CSA2_CS_MFMA(1, xo, 0) CSA2_CS_MFMA(2, xe, 1) CSA2_CS_MFMA(3, xo, 1)
+        CSA2_CS_MFMA(4, xe, 2) CSA2_CS_MFMA(5, xo, 2) CSA2_CS_MFMA(6, xe, 3) CSA2_CS_MFMA(7, xo, 3)
+  #undef CSA2_CS_MFMA
+        }
       }
     }
-    // ---- CS phase 4: the waves' (m, l) meet in LDS (s_red rows w and kQKW + w); after one
-    //      barrier every logit wave rescales its partial sums by exp(m_w - M) into its slice
-    //      (the rows are dead then) and 16 threads form the block's (M, sum of exp(m_w - M) l_w)
-    //      in a fixed order; the output stage then adds the slices as in the other path.
-    static_assert(2 * kQKW <= kAttWaves, "s_red holds the waves' maxima and sums");
-    if (qk_wave && g == 0) {
-      s_red[qw][n16] = m;
-      s_red[kQKW + qw][n16] = lsum;
+    // ---- CS phase 4: every wave's (m, l) meets in LDS (s_red rows w and kAttWaves + w; the
+    //      waves without entries hold (-inf, 0)); after one barrier every wave with a slice
+    //      rescales its partial sums by exp(m_w - M) (window waves also by 2^sx; the logit
+    //      waves by the main cache's channel scales) into its slice (the rows are dead then),
+    //      and 16 threads form the block's (M, sum of exp(m_w - M) l_w) in a fixed order; the
+    //      output stage adds the slices.
+    if (g == 0) {
+      s_red[wave][n16] = m;
+      s_red[kAttWaves + wave][n16] = lsum;
     }
     __syncthreads();
     if (tid < kAttHeads) {
       float mx = kNegInf;
 #pragma unroll
-      for (int w2 = 0; w2 < kQKW; ++w2) mx = fmaxf(mx, s_red[w2][tid]);
+      for (int w2 = 0; w2 < kWPT; ++w2) mx = fmaxf(mx, s_red[w2][tid]);
       float ls = 0.0f;
 #pragma unroll
-      for (int w2 = 0; w2 < kQKW; ++w2) {
+      for (int w2 = 0; w2 < kWPT; ++w2) {
         const float mw = s_red[w2][tid];
-        ls += (mw == kNegInf) ? 0.0f : __expf(mw - mx) * s_red[kQKW + w2][tid];
+        ls += (mw == kNegInf) ? 0.0f : __expf(mw - mx) * s_red[kAttWaves + w2][tid];
       }
       s_m[tid] = mx;
       s_l[tid] = ls;
     }
-    if (qk_wave) {
+    if (qk_wave || win_wave) {
+      float csc[kPVT][8];  // logit waves: the channel scales of this lane's output channels
+#pragma unroll
+      for (int ci = 0; ci < kPVT; ++ci)
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) csc[ci][mm] = win_wave ? xdown : s_scale[128 * (ctb * kPVT + ci) + 8 * n16 + mm];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int h = 4 * g + rr;
         float mx = kNegInf;
 #pragma unroll
-        for (int w2 = 0; w2 < kQKW; ++w2) mx = fmaxf(mx, s_red[w2][h]);
-        const float mw = s_red[qw][h];
+        for (int w2 = 0; w2 < kWPT; ++w2) mx = fmaxf(mx, s_red[w2][h]);
+        const float mw = s_red[wave][h];
         const float f = (mw == kNegInf) ? 0.0f : __expf(mw - mx);
 #pragma unroll
         for (int ci = 0; ci < kPVT; ++ci) {
-          float4* o = reinterpret_cast<float4*>(&sO[((size_t)qw * kAttHeads + h) * kOW + 128 * ci]);
-          o[n16] = make_float4(acc[ci][0][rr] * f, acc[ci][1][rr] * f, acc[ci][2][rr] * f, acc[ci][3][rr] * f);
-          o[16 + n16] = make_float4(acc[ci][4][rr] * f, acc[ci][5][rr] * f, acc[ci][6][rr] * f, acc[ci][7][rr] * f);
+          float4* o = reinterpret_cast<float4*>(&sO[((size_t)wave * kAttHeads + h) * kOW + 128 * ci]);
+          const float* c8 = csc[ci];
+          o[n16] = make_float4(acc[ci][0][rr] * f * c8[0], acc[ci][1][rr] * f * c8[1], acc[ci][2][rr] * f * c8[2],
+                               acc[ci][3][rr] * f * c8[3]);
+          o[16 + n16] = make_float4(acc[ci][4][rr] * f * c8[4], acc[ci][5][rr] * f * c8[5],
+                                    acc[ci][6][rr] * f * c8[6], acc[ci][7][rr] * f * c8[7]);
         }
       }
     }
@@ -884,7 +1061,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     const float inv_l = (l > 0.0f) ? 1.0f / l : 0.0f;
     float o[4] = {o4.x * inv_l, o4.y * inv_l, o4.z * inv_l, o4.w * inv_l};
     const int h = hg * kAttHeads + hl;
-    if (!G16) {
+    if (!G16 && !CS) {  // (CS: already in the slices)
 #pragma unroll
       for (int m = 0; m < 4; ++m) o[m] *= s_scale[c + m];
     }
@@ -1091,16 +1268,16 @@ size_t attend_ws_floats(int R, int Hq, int D, int K, int window) {
   return (size_t)R * P * Hq * D + (size_t)R * P * Hq * 2;
 }
 
-template <int D, bool G16, bool CS>
+template <int D, bool G16, bool CS, bool WIN>
 static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
   // the window (if any) is one more block column, run beside the selection's splits
   // one block per (unit = (row, split or window), head group[, channel tile]), dealt in
   // XCD-aware order
-  const int units = (S + (a.swa_codes ? 1 : 0)) * a.B * a.T;
+  const int units = (S + ((a.swa_codes && !CS) ? 1 : 0)) * a.B * a.T;
   const int ncb = CS ? (D / 128 < kCSBlocks ? D / 128 : kCSBlocks) : 1;
   const dim3 g((unsigned)(8 * (a.Hq / kAttHeads) * ncb * ((units + 7) / 8)));
   float* part_ml = a.part ? a.part + (size_t)a.B * a.T * P * a.Hq * D : nullptr;
-  hipLaunchKernelGGL((k_attend_part<D, G16, CS>), g, dim3(kAttThreads), 0, st, a.B * a.T, a.T, a.Hq, a.K, S, P,
+  hipLaunchKernelGGL((k_attend_part<D, G16, CS, WIN>), g, dim3(kAttThreads), 0, st, a.B * a.T, a.T, a.Hq, a.K, S, P,
                      (const uint16_t*)a.q, a.codes, a.scales, a.n_max, a.idx, a.softmax_scale, a.out, (int)a.out_bf16, a.lse, a.part, part_ml, a.swa_codes,
                      a.swa_scales, a.swa_n_max, a.swa_end, a.window);
   if (P > 1)
@@ -1110,12 +1287,12 @@ static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
 
 template <int D>
 static void launch_mfma_d(const AttendArgs& a, int S, int P, hipStream_t st) {
-  if (a.g16)
-    launch_mfma<D, true, false>(a, S, P, st);
-  else if (a.swa_codes)  // the window's block column computes every channel
-    launch_mfma<D, false, false>(a, S, P, st);
+  if (a.g16)  // with a window: one more block column and partial slot, merged by k_attend_combine
+    launch_mfma<D, true, false, false>(a, S, P, st);
+  else if (a.swa_codes)  // the window in the selection's blocks and softmax
+    launch_mfma<D, false, true, true>(a, S, P, st);
   else
-    launch_mfma<D, false, true>(a, S, P, st);
+    launch_mfma<D, false, true, false>(a, S, P, st);
 }
 
 int launch_attend(const AttendArgs& a, hipStream_t st) {
@@ -1133,7 +1310,8 @@ int launch_attend(const AttendArgs& a, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   const int S = attend_splits(a.K);
-  const int P = attend_parts(a.K, a.swa_codes != nullptr);
+  // the window takes a partial slot of its own only with the G16 layout
+  const int P = attend_parts(a.K, a.swa_codes != nullptr && a.g16);
   if (P > 1 && !a.part) return -1;
   switch (a.D) {
     case 128: launch_mfma_d<128>(a, S, P, st); break;
