@@ -37,6 +37,9 @@ constexpr int kAttWaves = 16;      // four waves per SIMD
 constexpr int kAttThreads = 64 * kAttWaves;
 constexpr int kAttSplit = 512;     // entries per block: the pages' Top-512 in one block, no merge
 constexpr int kCSBlocks = 4;       // channel split: blocks per (row, split, head group), at most D / 128
+// The channel split repeats QK in each of its blocks, so it pays only while its whole grid runs
+// in one round of blocks (one per CU: each holds about 150 KB of LDS); MI355X has 256 CUs.
+constexpr long kCSMaxBlocks = 256;
 
 // partials: part_o [R][P][Hq][D] normalised outputs, part_ml [R][P][Hq][2] (max, sum); P
 // = the splits of the selected entries, plus one slot for the sliding window
@@ -1286,13 +1289,21 @@ static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
 }
 
 template <int D>
-static void launch_mfma_d(const AttendArgs& a, int S, int P, hipStream_t st) {
+static void launch_mfma_d(const AttendArgs& a, int S, int P, bool cs, hipStream_t st) {
   if (a.g16)  // with a window: one more block column and partial slot, merged by k_attend_combine
     launch_mfma<D, true, false, false>(a, S, P, st);
+  else if (!cs)  // likewise
+    launch_mfma<D, false, false, false>(a, S, P, st);
   else if (a.swa_codes)  // the window in the selection's blocks and softmax
     launch_mfma<D, false, true, true>(a, S, P, st);
   else
     launch_mfma<D, false, true, false>(a, S, P, st);
+}
+
+// the channel-split kernel (per-channel layout) when its grid fits one round of blocks
+static bool attend_channel_split(const AttendArgs& a, int S) {
+  const long ncb = a.D / 128 < kCSBlocks ? a.D / 128 : kCSBlocks;
+  return !a.g16 && (long)a.B * a.T * S * (a.Hq / kAttHeads) * ncb <= kCSMaxBlocks;
 }
 
 int launch_attend(const AttendArgs& a, hipStream_t st) {
@@ -1310,13 +1321,15 @@ int launch_attend(const AttendArgs& a, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   const int S = attend_splits(a.K);
-  // the window takes a partial slot of its own only with the G16 layout
-  const int P = attend_parts(a.K, a.swa_codes != nullptr && a.g16);
+  // with the channel split the window is attended inside the selection's blocks; otherwise
+  // it takes one more partial slot
+  const bool cs = attend_channel_split(a, S);
+  const int P = attend_parts(a.K, a.swa_codes != nullptr && !cs);
   if (P > 1 && !a.part) return -1;
   switch (a.D) {
-    case 128: launch_mfma_d<128>(a, S, P, st); break;
-    case 256: launch_mfma_d<256>(a, S, P, st); break;
-    case 512: launch_mfma_d<512>(a, S, P, st); break;
+    case 128: launch_mfma_d<128>(a, S, P, cs, st); break;
+    case 256: launch_mfma_d<256>(a, S, P, cs, st); break;
+    case 512: launch_mfma_d<512>(a, S, P, cs, st); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -141,3 +141,24 @@ def test_layer_group_with_a_window_per_layer(pool):
                                       swa=RL["swa"])
         assert max_abs_rel(L["out"].cpu().numpy(), ro) <= 2e-3, i
         assert np.allclose(L["lse"].cpu().numpy(), rl, rtol=2e-3, atol=2e-3), i
+
+
+def test_sparse_attend_with_window_many_rows():
+    """72 rows: more attention blocks than fit one round on the chip, where the window runs as a
+    block column of its own and its partial is merged with the selection's (the decode shapes
+    attend it inside the selection's blocks instead)."""
+    B = 72
+    wl = workloads.workload("full64k", B=B, K=512)
+    c = build_cache(wl, n_rows=1500)
+    q = wl.attn_query()
+    rng = np.random.default_rng(72)
+    idx = np.stack([np.sort(rng.choice(1500, 512, replace=False)) for _ in range(B)]).astype(np.int32)[:, None]
+    idx[5, 0, ::2] = -1
+    wc, ws, wcr, wsr = window_cache(B, 160, 512, seed=72)
+    end = rng.integers(0, 200, size=(B, 1)).astype(np.int32)
+    ref_o, ref_l = oracle.sparse_attend(q, c["codes_ref"], c["scales_ref"], idx, wl.softmax_scale,
+                                        swa=(wcr, wsr, end, 128))
+    out, lse = csa2.sparse_attend(to_dev(q, torch.bfloat16), c["codes"], c["scales"], to_dev(idx), wl.softmax_scale,
+                                  out_dtype=torch.float32, swa=csa2.Swa(wc, ws, to_dev(end), 128))
+    assert max_abs_rel(out.cpu().numpy(), ref_o) <= 2e-3
+    assert np.allclose(lse.cpu().numpy(), ref_l, rtol=2e-3, atol=2e-3)
