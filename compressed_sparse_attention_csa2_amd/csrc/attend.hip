@@ -7,24 +7,29 @@
 // Two main-KV layouts: one fp32 scale per (sequence, channel), and the pages' own one E4M3
 // scale per 16 channels of each entry (G16, see k_attend_part).
 //
-// MFMA path (bf16 queries, Hq % 16 == 0, D in {128, 256, 512}).  One block = one query
-// row x 16 heads (the MFMA M dimension) x one split of up to 512 selected entries, 16
-// waves, so the pages' Top-512 needs no merge; without a sliding window and with the
-// per-channel layout, each such unit runs as D / 128 blocks that all compute the logits and
-// the softmax, each then taking PV and the output of one 128-channel tile; larger K runs several splits and a second
-// kernel merges their partial softmaxes by log-sum-exp (a kernel boundary: merging inside
-// the kernel would need a device-scope release fence, which costs more here).  The
-// per-channel scale s_c factors out of both contractions: logits use q'' = q * s * 2^k_h in
-// fp16 (2^k_h an exact per-head prescale keeping |q''| below 2^15, undone in that head's
-// logits; ~2^-12 relative error) against the exact E2M1 values e in fp16; the output is
-// s_c * sum_j p_j e_jc / l with p in fp16.  Per-channel layout: the split's FP4 rows are
+// MFMA path (bf16 queries, Hq % 16 == 0, D in {128, 256, 512}).  A unit = one query row x 16
+// heads (the MFMA M dimension) x one split of up to 512 selected entries, so the pages'
+// Top-512 needs no merge; larger K runs several splits and a second kernel merges their
+// partial softmaxes by log-sum-exp (a kernel boundary: merging inside the kernel would need a
+// device-scope release fence).  The per-channel scale s_c factors out of both contractions:
+// logits use q'' = q * s * 2^k_h in fp16 (2^k_h an exact per-head prescale keeping |q''| below
+// 2^15, undone in that head's logits; ~2^-12 relative error) against the exact E2M1 values e in
+// fp16; the output is s_c * sum_j p_j e_jc / l with p in fp16.  The split's FP4 rows are
 // gathered whole into LDS (one wave instruction loads complete rows, 16 bytes per lane,
-// straight into LDS) and both contractions read their operands from there: for QK lane
-// (entry n, group g) reads 16 bytes per 128 channels, for PV lane (channel block n, entry
-// group g) one 32-bit word (8 channels) of each of 8 entries.  G16 layout: the same
-// operands are loaded from global memory directly.  PV is split over waves by (channel
-// tile, entry group) and the entry groups are summed in LDS in a fixed order
-// (deterministic).
+// straight into LDS) and both contractions read their operands from there.
+//
+// Channel split (per-channel layout, grids of at most one block per CU: the decode shapes):
+// each unit runs as D / 128 blocks of 16 waves that all compute the logits, each then taking
+// PV and the output of one 128-channel tile.  The logits come out transposed (lane: one head,
+// 16 entries), each of the 8 logit waves takes its softmax statistics over its own 64 entries
+// and feeds p from registers to PV over them; one barrier merges the waves' (m, l), and the
+// waves' rescaled partial sums are added in LDS in a fixed order (deterministic).  With a
+// sliding window, 4 otherwise idle waves attend its 128 rows in the same softmax.
+//
+// Undivided grid (many rows, or the G16 layout): one block per unit, 16 waves, PV split over
+// waves by (channel tile, entry group), the groups summed in LDS in a fixed order; a sliding
+// window is one more block column merged by the second kernel.  G16 layout: the operands are
+// loaded from global memory directly and the group scales staged in LDS.
 //
 // fp32 path (fp32 queries): plain VALU, one block per (row, head), fp32 throughout.
 #include "common.hpp"
