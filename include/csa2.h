@@ -218,10 +218,12 @@ typedef struct {
  *   power-of-two prescale) and into the output; per-16-channel scales multiply the fp16
  *   key/value operands (E2M1 * E4M3 is exact in fp16).  Entries are processed in groups of
  *   512 whose partial softmax results are merged by log-sum-exp.
- *   swa (nullable): the layer's sliding-window entries, joining the same softmax (the
- *   window's partial result is merged with the selected entries' by log-sum-exp).
+ *   swa (nullable): the layer's sliding-window entries, joining the same softmax (attended
+ *   inside the selected entries' blocks when the grid is small, as at decode; otherwise
+ *   the window's partial result is merged with the selected entries' by log-sum-exp).
  *   ws: csa2_sparse_attend_workspace_size() bytes (0 when K <= 512 without a window, or q
  *   is fp32; then ws may be NULL); `window` there is swa->window, or 0 without a window.
+ *   The size covers a window's own partial slot whether or not the call needs it.
  */
 int csa2_sparse_attend(int B, int T, int Hq, int D, const void* q, int q_dtype, int kv_fmt, const uint8_t* kv_codes,
                        const void* kv_scales, int64_t n_max, const int32_t* idx, int K, const csa2_swa* swa,
