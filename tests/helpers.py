@@ -51,7 +51,7 @@ def fp4_score_bound(q, w, k4, ks):
 
 
 def check_topk_near_tie(gpu_idx, ref_scores, K, rel=1e-3, n_vis=None):
-    """Survey rule: with tau the reference K-th score and delta = rel*|tau|, the GPU set G
+    """Near-tie acceptance rule: with tau the reference K-th score and delta = rel*|tau|, the GPU set G
     must have min(K, n_vis) members, contain every j with s_j > tau + delta and lie inside
     {j : s_j >= tau - delta}.  Also: ascending order, -1 padding."""
     B, T, _ = gpu_idx.shape
