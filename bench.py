@@ -796,7 +796,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the CSA2 decode path runs per sequence with no exchange between GPUs, "
-              "and this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+              "and the library has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     if csa2.device_check() != 0:
