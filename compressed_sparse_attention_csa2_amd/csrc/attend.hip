@@ -18,7 +18,7 @@
 // gathered whole into LDS (one wave instruction loads complete rows, 16 bytes per lane,
 // straight into LDS) and both contractions read their operands from there.
 //
-// Channel split (per-channel layout, grids of at most one block per CU: the decode shapes):
+// Channel split (grids of at most one block per CU: the decode shapes; G16 without a window):
 // each unit runs as D / 128 blocks of 16 waves that all compute the logits, each then taking
 // PV and the output of one 128-channel tile.  The logits come out transposed (lane: one head,
 // 16 entries), each of the 8 logit waves takes its softmax statistics over its own 64 entries
@@ -26,10 +26,11 @@
 // waves' rescaled partial sums are added in LDS in a fixed order (deterministic).  With a
 // sliding window, 4 otherwise idle waves attend its 128 rows in the same softmax.
 //
-// Undivided grid (many rows, or the G16 layout): one block per unit, 16 waves, PV split over
-// waves by (channel tile, entry group), the groups summed in LDS in a fixed order; a sliding
-// window is one more block column merged by the second kernel.  G16 layout: the operands are
-// loaded from global memory directly and the group scales staged in LDS.
+// Undivided grid (many rows, or G16 with a window): one block per unit, 16 waves, PV split
+// over waves by (channel tile, entry group), the groups summed in LDS in a fixed order; a
+// sliding window is one more block column merged by the second kernel.  G16 layout (either
+// grid): the row operands are loaded from global memory directly (16 logit waves of 32
+// entries) and the group scales staged in LDS.
 //
 // fp32 path (fp32 queries): plain VALU, one block per (row, head), fp32 throughout.
 #include "common.hpp"
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   // CS with a sliding window (WIN): kCSWinW more waves attend the window's rows (32 each) in
   // the same softmax
   constexpr int kCSWinW = kWinMax / 32;
-  static_assert(!CS || kQKW + kCSWinW <= kAttWaves, "window waves past the logit waves");
+  static_assert(!WIN || kQKW + kCSWinW <= kAttWaves, "window waves past the logit waves");
   constexpr int kWPT = CS ? kQKW + (WIN ? kCSWinW : 0)
                           : ((kAttWaves / kPVT < kAttSplit / 32) ? kAttWaves / kPVT : kAttSplit / 32);
   // per-channel layout: the split's rows are gathered whole (a wave instruction reads
@@ -757,18 +758,29 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   #pragma unroll
       for (int i = 0; i < (qk_wave ? kCT : 0); ++i) {
         uint32_t wd[kAttTPW][4];
+        _Float16 gs[kAttTPW][2];  // G16: groups 8 i + 2 g and 8 i + 2 g + 1 of the lane's entry
   #pragma unroll
         for (int t = 0; t < kAttTPW; ++t) {
           const int el = (qw * kAttTPW + t) * 16 + n16;
-          const uint4 kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
+          uint4 kv;
+          if constexpr (G16) {  // operand-layout rows from global memory, scales staged in LDS
+            kv = kw[t][i];
+            gs[t][0] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g) * L::kSpad + el]);
+            gs[t][1] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g + 1) * L::kSpad + el]);
+          } else {
+            kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
+          }
           wd[t][0] = kv.x; wd[t][1] = kv.y; wd[t][2] = kv.z; wd[t][3] = kv.w;
         }
   #pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
           const v8h qv8 = *reinterpret_cast<const v8h*>(&sA[n16 * L::kApad + 128 * i + 32 * g + 8 * sub]);
   #pragma unroll
-          for (int t = 0; t < kAttTPW; ++t)
-            a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode8_f16(wd[t][sub]), qv8, a[t], 0, 0, 0);
+          for (int t = 0; t < kAttTPW; ++t) {
+            v8h kvh = decode8_f16(wd[t][sub]);
+            if constexpr (G16) kvh = kvh * gs[t][sub >> 1];  // E2M1 x E4M3 is exact in fp16
+            a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kvh, qv8, a[t], 0, 0, 0);
+          }
         }
       }
       // ---- CS phase 2: this wave's softmax statistics per head (no block barrier): the
@@ -820,11 +832,19 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
         for (int ci = 0; ci < kPVT; ++ci) {
         const int ct = ctb * kPVT + ci;
         uint32_t pw[8];
+        v8h sc = {};  // G16: the scales of the 8 K-slot entries, group 8 ct + n16 / 2
   #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           const int e = (qw * kAttTPW + 2 * ks + (jj >> 2)) * 16 + 4 * g + (jj & 3);
-          pw[jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes + 16 * ((4 * ct + (n16 >> 2)) ^ swz(e)) +
-                                                      4 * (n16 & 3));
+          if constexpr (G16) {  // word 16 ct + n16 of the row (global; p is 0 for skipped entries,
+                                // whose staged scale is 0, so row 0 may stand in for them)
+            const int32_t j = sel[e];
+            pw[jj] = *reinterpret_cast<const uint32_t*>(cb + (int64_t)(j >= 0 ? j : 0) * kRowBytes + 64 * ct + 4 * n16);
+            sc[jj] = __builtin_bit_cast(_Float16, sS[(8 * ct + (n16 >> 1)) * L::kSpad + e]);
+          } else {
+            pw[jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes + 16 * ((4 * ct + (n16 >> 2)) ^ swz(e)) +
+                                                        4 * (n16 & 3));
+          }
         }
         uint32_t xe[4], xo[4];
   #pragma unroll
@@ -837,7 +857,9 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     {                                                                                                          \
       const uint4 bw = make_uint4(cvt_pair_f16<BS>(X[0]), cvt_pair_f16<BS>(X[1]), cvt_pair_f16<BS>(X[2]),      \
                                   cvt_pair_f16<BS>(X[3]));                                                     \
-      acc[ci][M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(v8h, bw), acc[ci][M], 0, 0, 0);  \
+      v8h bv = __builtin_bit_cast(v8h, bw);                                                                  \
+      if constexpr (G16) bv = bv * sc;                                                                       \
+      acc[ci][M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, acc[ci][M], 0, 0, 0);                      \
     }
         CSA2_CS_MFMA(0, xe, 0) CSA2_CS_MFMA(1, xo, 0) CSA2_CS_MFMA(2, xe, 1) CSA2_CS_MFMA(3, xo, 1)
         CSA2_CS_MFMA(4, xe, 2) CSA2_CS_MFMA(5, xo, 2) CSA2_CS_MFMA(6, xe, 3) CSA2_CS_MFMA(7, xo, 3)
@@ -874,7 +896,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
 #pragma unroll
       for (int ci = 0; ci < kPVT; ++ci)
 #pragma unroll
-        for (int mm = 0; mm < 8; ++mm) csc[ci][mm] = win_wave ? xdown : s_scale[128 * (ctb * kPVT + ci) + 8 * n16 + mm];
+        for (int mm = 0; mm < 8; ++mm)
+          csc[ci][mm] = win_wave ? xdown : (G16 ? 1.0f : s_scale[G16 ? 0 : 128 * (ctb * kPVT + ci) + 8 * n16 + mm]);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int h = 4 * g + rr;
@@ -1295,7 +1318,9 @@ static void launch_mfma(const AttendArgs& a, int S, int P, hipStream_t st) {
 
 template <int D>
 static void launch_mfma_d(const AttendArgs& a, int S, int P, bool cs, hipStream_t st) {
-  if (a.g16)  // with a window: one more block column and partial slot, merged by k_attend_combine
+  if (a.g16 && cs)
+    launch_mfma<D, true, true, false>(a, S, P, st);
+  else if (a.g16)  // with a window: one more block column and partial slot, merged by k_attend_combine
     launch_mfma<D, true, false, false>(a, S, P, st);
   else if (!cs)  // likewise
     launch_mfma<D, false, false, false>(a, S, P, st);
@@ -1305,10 +1330,10 @@ static void launch_mfma_d(const AttendArgs& a, int S, int P, bool cs, hipStream_
     launch_mfma<D, false, true, false>(a, S, P, st);
 }
 
-// the channel-split kernel (per-channel layout) when its grid fits one round of blocks
+// the channel-split kernel when its grid fits one round of blocks (G16: without a window)
 static bool attend_channel_split(const AttendArgs& a, int S) {
   const long ncb = a.D / 128 < kCSBlocks ? a.D / 128 : kCSBlocks;
-  return !a.g16 && (long)a.B * a.T * S * (a.Hq / kAttHeads) * ncb <= kCSMaxBlocks;
+  return (!a.g16 || !a.swa_codes) && (long)a.B * a.T * S * (a.Hq / kAttHeads) * ncb <= kCSMaxBlocks;
 }
 
 int launch_attend(const AttendArgs& a, hipStream_t st) {
