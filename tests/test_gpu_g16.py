@@ -106,6 +106,24 @@ def test_sparse_attend_g16_bf16(K, D):
     assert np.all(np.abs(ob - ref_o) <= 2e-3 * np.abs(ref_o).max() + np.abs(ref_o) * 2.0 ** -8)
 
 
+def test_sparse_attend_g16_many_rows():
+    """72 rows: more attention blocks than fit one round on the chip, where the G16 layout runs
+    the undivided grid (the decode shapes above take the channel split)."""
+    B = 72
+    wl = workloads.workload("full64k", B=B, K=512)
+    x = np.stack([wl.main_kv(b, rows=900) for b in range(B)])
+    codes, gs, cr, gr = g16_cache(x)
+    q = wl.attn_query()
+    rng = np.random.default_rng(1672)
+    idx = np.stack([np.sort(rng.choice(900, 512, replace=False)) for _ in range(B)]).astype(np.int32)[:, None]
+    idx[7, 0, ::4] = -1
+    ref_o, ref_l = oracle.sparse_attend(q, cr, gr, idx, wl.softmax_scale)
+    out, lse = csa2.sparse_attend(to_dev(q, torch.bfloat16), codes, gs, to_dev(idx), wl.softmax_scale,
+                                  out_dtype=torch.float32)
+    assert max_abs_rel(out.cpu().numpy(), ref_o) <= 2e-3
+    assert np.allclose(lse.cpu().numpy(), ref_l, rtol=2e-3, atol=2e-3)
+
+
 def test_sparse_attend_g16_subnormal_scales():
     """Small entries whose group scales are subnormal E4M3 codes (m * 2^-9): the output is
     built from them alone, so a wrong subnormal decode shows at full relative size."""
