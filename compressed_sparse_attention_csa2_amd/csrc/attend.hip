@@ -28,9 +28,10 @@
 //
 // Undivided grid (many rows, or G16 with a window): one block per unit, 16 waves, PV split
 // over waves by (channel tile, entry group), the groups summed in LDS in a fixed order; a
-// sliding window is one more block column merged by the second kernel.  G16 layout (either
-// grid): the row operands are loaded from global memory directly (16 logit waves of 32
-// entries) and the group scales staged in LDS.
+// sliding window is one more block column merged by the second kernel.  G16 layout: on the
+// channel split its rows are gathered into LDS too (16 logit waves of 32 entries) and each
+// lane loads its scale bytes from global memory; on the undivided grid the row operands are
+// loaded from global memory directly and the group scales staged in LDS.
 //
 // fp32 path (fp32 queries): plain VALU, one block per (row, head), fp32 throughout.
 #include "common.hpp"
@@ -377,6 +378,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   // waves that compute logits: per-channel, 8 waves of 4 tiles (each QK wave reads the whole
   // query operand from LDS once, so fewer, longer waves read less); G16, all 16 waves (its
   // operands come from global memory, and more waves issue those loads faster)
+  // G16 on the channel split gathers its rows into LDS like the per-channel layout and loads
+  // each lane's scale bytes from global memory; the undivided G16 kernel keeps operand-layout
+  // row loads and stages the scales
+  constexpr bool kOpG16 = G16 && !CS;
   constexpr int kQKW = G16 ? kAttWaves : 8;
   constexpr int kAttTPW = kAttSplit / 16 / kQKW;  // 16-entry QK tiles per QK wave
   static_assert(kAttTPW * 16 * kQKW == kAttSplit, "QK tiles cover the split");
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   static_assert(kGI * kRPI * kAttWaves == kAttSplit, "the gather covers the split");
   auto swz = [](int e) { return (e / (16 / kNC)) & (kNC - 1); };
   constexpr int kEPW = kAttSplit / kWPT;       // entries per wave in PV (a multiple of 32)
-  using L = AttLds<D, kWPT, G16, kOW>;
+  using L = AttLds<D, kWPT, kOpG16, kOW>;
   constexpr int kNG = D / 16;                  // scale groups per entry (G16)
   __shared__ float s_scale[G16 ? 1 : D];
   __shared__ __align__(16) int32_t s_idx[kAttSplit];
@@ -479,8 +484,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   constexpr int kScChunks = kAttSplit * kGC;
   constexpr int kScPer = G16 ? (kScChunks + kAttThreads - 1) / kAttThreads : 1;
   uint4 gsw[kScPer];
-  if (G16) {
-    const uint8_t* gsb = static_cast<const uint8_t*>(scales_v) + (int64_t)b * n_max * kNG;
+  const uint8_t* gsb = G16 ? static_cast<const uint8_t*>(scales_v) + (int64_t)b * n_max * kNG : nullptr;
+  if (kOpG16) {
 #pragma unroll
     for (int it = 0; it < kScPer; ++it) {
       const int i = tid + it * kAttThreads;
@@ -504,7 +509,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   for (int t = 0; t < kAttTPW; ++t) {
     const int e = (qw * kAttTPW + t) * 16 + n16;
     jt[t] = sel[e];  // -1 past K
-    if constexpr (G16) {
+    if constexpr (kOpG16) {
       const uint8_t* rowp = cb + (int64_t)(jt[t] >= 0 ? jt[t] : 0) * kRowBytes + 16 * g;
 #pragma unroll
       for (int i = 0; i < kCT; ++i) kw[t][i] = *reinterpret_cast<const uint4*>(rowp + 64 * i);
@@ -539,7 +544,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   // staged row.  Issued after the last LDS read of the query preparation: the loads stay in
   // flight through the query's conversion and stores (an LDS read while they are in flight
   // would wait for them).
-  if constexpr (!G16) {
+  if constexpr (!kOpG16) {
 #pragma unroll
     for (int j = 0; j < kGI; ++j) {
       const int r0 = (wave * kGI + j) * kRPI;
@@ -548,6 +553,33 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
       const uint8_t* src = cb + (int64_t)(jr >= 0 ? jr : 0) * kRowBytes + 16 * ((lane % kNC) ^ swz(row));
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(s_rows + r0 * kRowBytes), 16, 0, 0);
+    }
+  }
+  // G16 on the channel split: this lane's scale bytes, loaded with the gather.  QK: the whole
+  // 32-byte scale row of each of its entries (qw kAttTPW + t) 16 + n16 (it uses groups 8 i + 2 g
+  // and 8 i + 2 g + 1); PV: group 8 ctb + n16 / 2 of the entries of its K slots.  Skipped
+  // entries take scale 0 (their p is 0, and the row standing in for them may hold any byte).
+  uint4 gqk[G16 && CS ? kAttTPW : 1][2];
+  uint32_t gpv[2] = {0u, 0u};
+  if constexpr (G16 && CS) {
+    static_assert(kNG == 32 || kNG == 16 || kNG == 8, "scale row of D / 16 bytes");
+#pragma unroll
+    for (int t = 0; t < kAttTPW; ++t) {
+      const int32_t j = sel[(qw * kAttTPW + t) * 16 + n16];
+      const uint8_t* gp = gsb + (int64_t)(j >= 0 ? j : 0) * kNG;
+      uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
+      if constexpr (kNG >= 16) a0 = *reinterpret_cast<const uint4*>(gp);
+      else a0 = make_uint4(reinterpret_cast<const uint2*>(gp)->x, reinterpret_cast<const uint2*>(gp)->y, 0u, 0u);
+      if constexpr (kNG == 32) a1 = *reinterpret_cast<const uint4*>(gp + 16);
+      gqk[t][0] = j >= 0 ? a0 : make_uint4(0u, 0u, 0u, 0u);
+      gqk[t][1] = j >= 0 ? a1 : make_uint4(0u, 0u, 0u, 0u);
+    }
+    static_assert(kAttTPW == 2, "one PV step of two tiles per logit wave");
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int32_t j = sel[(qw * kAttTPW + (jj >> 2)) * 16 + 4 * g + (jj & 3)];
+      const uint32_t v = gsb[(int64_t)(j >= 0 ? j : 0) * kNG + 8 * ctb + (n16 >> 1)];
+      gpv[jj >> 2] |= (j >= 0 ? v : 0u) << (8 * (jj & 3));
     }
   }
   // WIN: the window waves' row scales and PV bytes (lane (channel block n16, g): channels
@@ -611,7 +643,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
     *reinterpret_cast<uint4*>(&sA[qh * L::kApad + qc]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     if (qc == 0) s_down[qh] = softmax_scale * __uint_as_float((uint32_t)(127 - 15 + qexp) << 23);
   }
-  if (G16) {  // the scales as fp16, [group][entry]
+  if (kOpG16) {  // the scales as fp16, [group][entry]
 #pragma unroll
     for (int it = 0; it < kScPer; ++it) {
       const int i = tid + it * kAttThreads;
@@ -626,7 +658,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
       }
     }
   }
-  if constexpr (!G16) __builtin_amdgcn_s_waitcnt(0);  // this wave's row loads have landed in LDS
+  if constexpr (!kOpG16) __builtin_amdgcn_s_waitcnt(0);  // this wave's row loads have landed in LDS
   __syncthreads();
 
   if constexpr (CS) {
@@ -763,12 +795,14 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
         for (int t = 0; t < kAttTPW; ++t) {
           const int el = (qw * kAttTPW + t) * 16 + n16;
           uint4 kv;
-          if constexpr (G16) {  // operand-layout rows from global memory, scales staged in LDS
-            kv = kw[t][i];
-            gs[t][0] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g) * L::kSpad + el]);
-            gs[t][1] = __builtin_bit_cast(_Float16, sS[(8 * i + 2 * g + 1) * L::kSpad + el]);
-          } else {
-            kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
+          kv = *reinterpret_cast<const uint4*>(s_rows + el * kRowBytes + 16 * ((4 * i + g) ^ swz(el)));
+          if constexpr (G16) {  // bytes 8 i + 2 g, 8 i + 2 g + 1 of the entry's scale row
+            const uint4 hv = gqk[t][(8 * i) >> 4];
+            const int bo = (8 * i + 2 * g) & 15;
+            const uint32_t wsel = (bo >> 2) == 0 ? hv.x : (bo >> 2) == 1 ? hv.y : (bo >> 2) == 2 ? hv.z : hv.w;
+            const uint32_t s2 = e4m3x2_to_f16x2(wsel >> (8 * (bo & 3)));
+            gs[t][0] = __builtin_bit_cast(_Float16, (uint16_t)(s2 & 0xFFFFu));
+            gs[t][1] = __builtin_bit_cast(_Float16, (uint16_t)(s2 >> 16));
           }
           wd[t][0] = kv.x; wd[t][1] = kv.y; wd[t][2] = kv.z; wd[t][3] = kv.w;
         }
@@ -833,18 +867,14 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
         const int ct = ctb * kPVT + ci;
         uint32_t pw[8];
         v8h sc = {};  // G16: the scales of the 8 K-slot entries, group 8 ct + n16 / 2
+        if constexpr (G16)
+          sc = __builtin_bit_cast(v8h, make_uint4(e4m3x2_to_f16x2(gpv[0]), e4m3x2_hi_to_f16x2(gpv[0]),
+                                                  e4m3x2_to_f16x2(gpv[1]), e4m3x2_hi_to_f16x2(gpv[1])));
   #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           const int e = (qw * kAttTPW + 2 * ks + (jj >> 2)) * 16 + 4 * g + (jj & 3);
-          if constexpr (G16) {  // word 16 ct + n16 of the row (global; p is 0 for skipped entries,
-                                // whose staged scale is 0, so row 0 may stand in for them)
-            const int32_t j = sel[e];
-            pw[jj] = *reinterpret_cast<const uint32_t*>(cb + (int64_t)(j >= 0 ? j : 0) * kRowBytes + 64 * ct + 4 * n16);
-            sc[jj] = __builtin_bit_cast(_Float16, sS[(8 * ct + (n16 >> 1)) * L::kSpad + e]);
-          } else {
-            pw[jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes + 16 * ((4 * ct + (n16 >> 2)) ^ swz(e)) +
-                                                        4 * (n16 & 3));
-          }
+          pw[jj] = *reinterpret_cast<const uint32_t*>(s_rows + e * kRowBytes + 16 * ((4 * ct + (n16 >> 2)) ^ swz(e)) +
+                                                      4 * (n16 & 3));
         }
         uint32_t xe[4], xo[4];
   #pragma unroll
