@@ -1,7 +1,7 @@
 // Sparse softmax attention over the selected FP4 entries (gather + dequant + attention).
 // "Compressed Sparse Attention 2 Or CSA2 In Simple Terms": only the selected entries are
-// attended; "FP4 Main KV Cache To Halve Storage Again": entries are dequantised back
-// before attention; "Model Setup Numbers Without Jargon": 64 heads of dim 512.  The whole
+// attended; "FP4 Main KV Cache To Halve Storage Again": the stored FP4 codes are expanded
+// to real values only when attention needs them; "Model Setup Numbers Without Jargon": 64 heads of dim 512.  The whole
 // dequantised entry is both key and value.
 //
 // Two main-KV layouts: one fp32 scale per (sequence, channel), and the pages' own one E4M3

@@ -411,7 +411,7 @@ void orc_topk(int B, int T, int64_t ncols, const double* scores, const int32_t* 
 
 /* Softmax attention of each query row over only its selected entries.
  * [N] "CSA2 In Simple Terms" (attend to the selected top entries), "FP4 Main KV Cache"
- * (entries are dequantised back before attention), "Model Setup Numbers" (64 heads of
+ * (the FP4 codes become real values again only for attention), "Model Setup Numbers" (64 heads of
  * dim 512).  Reading: the whole dequantised entry is both key and value (K = V), so with
  * v_j the dequantised row j and S the selected rows (positions outside [0, n_max)
  * skipped):
