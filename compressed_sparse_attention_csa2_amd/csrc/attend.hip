@@ -989,8 +989,9 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_part(
   #pragma unroll
       for (int rr = 0; rr < 4; ++rr) logit[t][rr] = (qk_wave && jt[t] >= 0) ? a[t][rr] * s_down[4 * g + rr] : kNegInf;
   
-    // ---- phase 3a: read the PV code words now (staged rows in LDS; G16: global loads, cache
-    //      hits since the rows were just read) so that they arrive during the softmax.  Wave
+    // ---- phase 3a: read the PV code words now (staged rows in LDS; G16 on the undivided
+    //      grid: global loads, cache hits since the rows were just read) so that they arrive
+    //      during the softmax.  Wave
     //      (channel tile ct, entry group eq); lane (channel block n16, group g) takes one
     //      32-bit word (8 channels) of each of the 8 entries el..el+7 of every 32-entry k-step.
     const int ct = CS ? ctb : wave % kCT, eq = CS ? wave : wave / kCT;
